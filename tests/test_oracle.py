@@ -1,0 +1,315 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test ties one pass of the oracle to something it cannot agree with by
+construction: exact rational arithmetic, hand-worked fixtures, closed-form
+identities, or an independent library routine (numpy BLAS, scipy, math.erf).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import workloads
+from conftest import GOLDEN
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _bf16_values(bits):
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# GEMM pass
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (8, 8, 8), (2, 9, 4), (7, 1, 9)])
+def test_gemm_exact_integers_match_rational_sum(M, N, K):
+    rng = np.random.default_rng([11, M, N, K])
+    A = rng.integers(-16, 17, size=(M, K)).astype(np.float32)
+    B = rng.integers(-16, 17, size=(K, N)).astype(np.float32)
+    got = oracle.gemm(A, B, "f32", "f32")
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(int(A[m, k])) * Fraction(int(B[k, n])) for k in range(K))
+            assert got[m, n] == float(exact)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 3, 16), (5, 6, 33)])
+def test_gemm_bf16_values_within_fp64_bound_of_exact(M, N, K):
+    A = workloads.normal((M, K), 1.0, "bf16", wid=90, tid=0)
+    B = workloads.normal((K, N), 0.3, "bf16", wid=90, tid=1)
+    got = oracle.gemm(A, B, "bf16", "bf16")
+    Av, Bv = _bf16_values(A), _bf16_values(B)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(Av[m, k])) * Fraction(float(Bv[k, n])) for k in range(K))
+            mag = sum(abs(float(Av[m, k]) * float(Bv[k, n])) for k in range(K))
+            # recursive summation in fp64: |err| <= K * 2^-53 * sum |a_k b_k| (first order)
+            assert abs(got[m, n] - float(exact)) <= K * 2.0 ** -53 * mag * 1.01 + 1e-300
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 53, 129), (64, 64, 128), (1, 300, 17)])
+def test_gemm_matches_numpy_blas(M, N, K):
+    A = workloads.uniform((M, K), -1, 1, "f32", wid=91, tid=0)
+    B = workloads.uniform((K, N), -1, 1, "f32", wid=91, tid=1)
+    got = oracle.gemm(A, B, "f32", "f32")
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * (1 + np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_B_returns_A_bitwise(dtype):
+    K = 48
+    A = workloads.normal((13, K), 1.0, dtype, wid=92, tid=0)
+    eye = np.eye(K, dtype=np.float32)
+    I = eye if dtype == "f32" else workloads.f32_to_bf16_bits(eye)
+    got = oracle.gemm_epilogue(A, I, dtype)
+    Av = A.astype(np.float64) if dtype == "f32" else _bf16_values(A)
+    assert np.array_equal(got, Av)
+    got_nk = oracle.gemm_epilogue(A, I, dtype, b_layout="NK")
+    assert np.array_equal(got_nk, Av)
+
+
+def test_nk_layout_equals_kn_bitwise():
+    A = workloads.normal((9, 40), 1.0, "bf16", wid=93, tid=0)
+    B = workloads.normal((40, 11), 1.0, "bf16", wid=93, tid=1)
+    kn = oracle.gemm(A, B, "bf16", "bf16", "KN")
+    nk = oracle.gemm(A, np.ascontiguousarray(B.T), "bf16", "bf16", "NK")
+    assert np.array_equal(kn, nk)
+
+
+# --------------------------------------------------------------------------
+# epilogue passes against hand-worked cases
+# --------------------------------------------------------------------------
+
+def _floats(s):
+    s = s.strip()
+    return None if s == "-" else np.array([float(v) for v in s.split()], dtype=np.float32)
+
+
+def _golden_cases(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden_cases("epilogue_worked.txt"), ids=lambda r: r[0])
+def test_epilogue_worked_examples(row):
+    name, dims, A, B, ab, C, bias, act, R, D = row
+    M, N, K = (int(v) for v in dims.split())
+    alpha, beta = (float(v) for v in ab.split())
+    A = _floats(A).reshape(M, K)
+    B = _floats(B).reshape(K, N)
+    C = _floats(C)
+    R = _floats(R)
+    got = oracle.gemm_epilogue(A, B, "f32", alpha=alpha, beta=beta,
+                               C=None if C is None else C.reshape(M, N), bias=_floats(bias),
+                               act=act, R=None if R is None else R.reshape(M, N))
+    assert np.array_equal(got, _floats(D).astype(np.float64).reshape(M, N))
+
+
+def test_beta_zero_never_reads_C():
+    A = np.ones((2, 3), np.float32)
+    B = np.ones((3, 2), np.float32)
+    got = oracle.gemm_epilogue(A, B, "f32", beta=0.0, C=np.full((2, 2), np.nan, np.float32))
+    assert np.array_equal(got, np.full((2, 2), 3.0))
+
+
+def test_zero_A_reduces_to_epilogue_of_C_bias_R():
+    # A = 0: D = act(beta*C + bias) + R for any B
+    M, N, K = 5, 7, 9
+    A = np.zeros((M, K), np.float32)
+    B = workloads.uniform((K, N), -1, 1, "f32", wid=94, tid=1)
+    C = np.arange(M * N, dtype=np.float32).reshape(M, N) - 17.0
+    bias = np.linspace(-4, 4, N).astype(np.float32)
+    R = np.full((M, N), 0.25, np.float32)
+    got = oracle.gemm_epilogue(A, B, "f32", alpha=3.0, beta=0.5, C=C, bias=bias, act="relu", R=R)
+    want = np.maximum(0.5 * C.astype(np.float64) + bias.astype(np.float64), 0.0) + 0.25
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# activations
+# --------------------------------------------------------------------------
+
+def test_relu_is_exact():
+    x = np.array([-3.5, -0.0, 0.0, 1e-300, 2.25, -1e300], np.float64)
+    got = oracle.activation(x, "relu")
+    assert list(got) == [0.0, 0.0, 0.0, 1e-300, 2.25, 0.0]
+
+
+def test_gelu_tanh_tracks_exact_gelu_within_published_error():
+    # The tanh form approximates x * Phi(x); its largest deviation is about 4.7e-4
+    # (near |x| = 2.7).  A wrong constant (e.g. 0.04715 or 0.79) pushes it past 1e-3.
+    x = np.linspace(-10, 10, 400001)
+    got = oracle.activation(x, "gelu_tanh")
+    exact = np.array([v * 0.5 * (1.0 + math.erf(v / math.sqrt(2.0))) for v in x[::50]])
+    dev = np.abs(got[::50] - exact)
+    assert dev.max() <= 5.0e-4
+    assert dev.max() >= 4.0e-4  # the approximation is not the exact function
+
+
+def test_gelu_tanh_identities():
+    x = np.linspace(-6, 6, 1201)
+    f = oracle.activation(x, "gelu_tanh")
+    fm = oracle.activation(-x, "gelu_tanh")
+    assert np.max(np.abs((f - fm) - x)) <= 1e-14 * (1 + np.abs(x)).max()
+    assert oracle.activation(np.array([0.0]), "gelu_tanh")[0] == 0.0
+    big = oracle.activation(np.array([12.0, -12.0]), "gelu_tanh")
+    assert big[0] == 12.0 and abs(big[1]) < 1e-300 + 1e-30
+    # slope 1/2 at the origin, curvature sqrt(2/pi)
+    h = 1e-4
+    f_h = oracle.activation(np.array([h, -h]), "gelu_tanh")
+    assert abs((f_h[0] - f_h[1]) / (2 * h) - 0.5) < 1e-9
+    assert abs((f_h[0] + f_h[1]) / h ** 2 - math.sqrt(2 / math.pi)) < 1e-5
+
+
+def test_silu_matches_scipy_expit_and_identities():
+    x = np.linspace(-30, 30, 6001)
+    got = oracle.activation(x, "silu")
+    ref = x * expit(x)
+    assert np.max(np.abs(got - ref) / (1 + np.abs(ref))) <= 4e-16
+    neg = oracle.activation(-x, "silu")
+    assert np.max(np.abs((got - neg) - x)) <= 1e-14 * 31
+    assert oracle.activation(np.array([0.0]), "silu")[0] == 0.0
+
+
+# --------------------------------------------------------------------------
+# SwiGLU
+# --------------------------------------------------------------------------
+
+def test_swiglu_worked_example():
+    (row,) = _golden_cases("swiglu_worked.txt")
+    X, Wg, Wu, out = (_floats(p).reshape(2, 2) for p in row)
+    got = oracle.swiglu(X, Wg, Wu, "f32")
+    assert np.max(np.abs(got - out.astype(np.float64))) <= 1e-6
+    # the fixture's values carry 16 digits; recheck them against scipy directly
+    assert np.max(np.abs(got - Wg * expit(Wg.astype(np.float64)) * Wu)) <= 1e-15 * 6
+
+
+# --------------------------------------------------------------------------
+# int4 unpack + dequant
+# --------------------------------------------------------------------------
+
+def _w4_fixture():
+    rows = []
+    with open(os.path.join(GOLDEN, "w4_unpack.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                b, ce, co, we, wo = line.split()
+                rows.append((int(b, 16), int(ce), int(co), float(we), float(wo)))
+    return rows
+
+
+def test_w4_unpack_and_dequant_hand_computed():
+    rows = _w4_fixture()
+    Wq = np.array([[r[0] for r in rows]], dtype=np.uint8)  # K = 1 row, N = 2 * len
+    N = 2 * len(rows)
+    codes = oracle.w4_unpack(Wq, N)
+    assert list(codes[0, 0::2]) == [r[1] for r in rows]
+    assert list(codes[0, 1::2]) == [r[2] for r in rows]
+    # K = 128 rows (one group), scale 2^-4 everywhere
+    Wq128 = np.repeat(Wq, 128, axis=0)
+    scales = np.full((1, N), 0.0625, np.float64)
+    W = oracle.w4_dequant(Wq128, scales, N, s_dtype="f64")
+    assert list(W[0, 0::2]) == [r[3] for r in rows]
+    assert list(W[0, 1::2]) == [r[4] for r in rows]
+    assert np.array_equal(W, np.repeat(W[:1], 128, axis=0))
+
+
+def test_w4_lo_first_swaps_nibbles():
+    Wq = np.array([[0x8F, 0x07]], np.uint8)
+    assert list(oracle.w4_unpack(Wq, 4, lo_first=True)[0]) == [15, 8, 7, 0]
+
+
+def test_w4_scale_groups_broadcast_along_k():
+    K, N, G = 256, 4, 128
+    Wq = np.full((K, N // 2), 0x9B, np.uint8)  # codes 9 and 11 -> +1 and +3
+    scales = np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 0.125, 0.0625]], np.float64)
+    W = oracle.w4_dequant(Wq, scales, N, group=G, s_dtype="f64")
+    assert np.array_equal(W[:G], np.tile([1.0, 6.0, 4.0, 24.0], (G, 1)))
+    assert np.array_equal(W[G:], np.tile([0.5, 0.75, 0.125, 0.1875], (G, 1)))
+
+
+def test_w4_gemm_one_hot_rows_select_weights_exactly():
+    # X row m is one-hot at k_m, so D[m] = (code[k_m] - 8) * s[k_m // 128] exactly
+    K, N = 256, 16
+    Wq = workloads.uniform_bytes((K, N // 2), wid=95, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = [0, 1, 127, 128, 200, 255]
+    X = np.zeros((len(ks), K), np.float32)
+    for m, k in enumerate(ks):
+        X[m, k] = 1.0
+    Xb = workloads.f32_to_bf16_bits(X)
+    D = oracle.w4_gemm(Xb, Wq, scales, N, "bf16")
+    for m, k in enumerate(ks):
+        hi = (Wq[k] >> 4).astype(np.int64)
+        lo = (Wq[k] & 0xF).astype(np.int64)
+        codes = np.empty(N, np.int64)
+        codes[0::2], codes[1::2] = hi, lo
+        assert np.array_equal(D[m], (codes - 8) * 2.0 ** -6)
+
+
+# --------------------------------------------------------------------------
+# add + RMSNorm
+# --------------------------------------------------------------------------
+
+def test_add_rmsnorm_constant_rows():
+    # a + x = 2 on every element of a row: rms = 2, so with eps = 0 the output is w exactly
+    M, N = 3, 10
+    a = np.full((M, N), 1.5, np.float32)
+    x = np.full((M, N), 0.5, np.float32)
+    w = np.linspace(-1, 1, N).astype(np.float32)
+    resid, out = oracle.add_rmsnorm(a, x, w, "f32", eps=0.0)
+    assert np.array_equal(resid, np.full((M, N), 2.0))
+    assert np.array_equal(out, np.tile(w.astype(np.float64), (M, 1)))
+
+
+def test_add_rmsnorm_unit_rms_after_normalisation():
+    a = workloads.normal((4, 256), 1.0, "f32", wid=96, tid=0)
+    x = workloads.normal((4, 256), 1.0, "f32", wid=96, tid=1)
+    w = np.ones(256, np.float32)
+    resid, out = oracle.add_rmsnorm(a, x, w, "f32", eps=0.0)
+    assert np.array_equal(resid, a.astype(np.float64) + x.astype(np.float64))
+    assert np.allclose(np.sqrt(np.mean(out ** 2, axis=1)), 1.0, rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# composition
+# --------------------------------------------------------------------------
+
+def test_whole_pipeline_against_independent_numpy_scipy_path():
+    w = workloads.WORKLOADS["square_bf16"].with_shape(M=70, N=90, K=200)
+    inp = workloads.make_inputs(w, seed=3)
+    got = oracle.reference(inp)
+    A, B = _bf16_values(inp["A"]), _bf16_values(inp["B"])
+    t = A @ B + _bf16_values(inp["bias"])[None, :]
+    erf = np.vectorize(math.erf)
+    gelu_exact = t * 0.5 * (1 + erf(t / math.sqrt(2)))
+    ref = gelu_exact + _bf16_values(inp["R"])
+    assert np.max(np.abs(got - ref)) <= 5.0e-4 + 1e-12
+
+
+def test_row_subset_equals_full_result_rows():
+    w = workloads.WORKLOADS["skinny_decode"].with_shape(M=16, N=64, K=96)
+    inp = workloads.make_inputs(w)
+    full = oracle.reference(inp)
+    rows = np.array([0, 5, 15])
+    assert np.array_equal(oracle.reference(inp, rows=rows), full[rows])
+
+
+def test_w4_reference_equals_dense_bf16_gemm_on_dequantised_weights():
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=4, N=32, K=256)
+    inp = workloads.make_inputs(w)
+    got = oracle.reference(inp)
+    W = oracle.w4_dequant(inp["Wq"], inp["scales"], w.N)
+    ref = _bf16_values(inp["X"]) @ W + _bf16_values(inp["bias"])[None, :]
+    assert np.max(np.abs(got - ref)) <= 1e-12 * (1 + np.abs(ref).max())
