@@ -1,0 +1,357 @@
+"""Python binding of ``libgemm_epi.so``, the fused GEMM + epilogue engine for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/gemm_epi.h``.  PyTorch
+provides device memory and the current stream; nothing here computes.
+
+The binding raises ``GemmEpiError`` on a nonzero status and
+``RuntimeError`` when the HIP library has not been built -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
+    "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
+    "F32", "BF16", "U4X2", "ACTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libgemm_epi.so")
+
+# status codes, types, layouts, activations, kinds, flags (mirror gemm_epi.h)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_ALIGN = range(6)
+F32, BF16, U4X2 = 0, 1, 2
+LAYOUT_KN, LAYOUT_NK = 0, 1
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
+KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
+FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST = 1, 2, 4, 8
+
+EXPORTS = [
+    "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_run",
+    "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
+    "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "ge_add_rmsnorm_run",
+    "ge_status_string", "ge_last_error", "ge_version",
+]
+
+
+class GemmEpiError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({_status_name(status)}): {detail}")
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``ge_desc``."""
+    _fields_ = [
+        ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("a_type", ctypes.c_int32), ("b_type", ctypes.c_int32),
+        ("c_type", ctypes.c_int32), ("d_type", ctypes.c_int32),
+        ("bias_type", ctypes.c_int32), ("r_type", ctypes.c_int32), ("scale_type", ctypes.c_int32),
+        ("b_layout", ctypes.c_int32),
+        ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+        ("ldd", ctypes.c_int64), ("ldr", ctypes.c_int64),
+        ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+        ("act", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("group_size", ctypes.c_int32), ("zero_point", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """Load the HIP library (raises if it was never built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(lib_path):
+                raise RuntimeError(f"{lib_path} is missing: build it first "
+                                   "(python -c 'import __graft_entry__ as g; g.build()')")
+            L = ctypes.CDLL(lib_path)
+            P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            L.ge_desc_init.argtypes = [ctypes.POINTER(Desc)]
+            L.ge_desc_init.restype = None
+            L.gemm_epi_plan.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(P)]
+            L.gemm_epi_plan.restype = I
+            L.gemm_epi_plan_destroy.argtypes = [P]
+            L.gemm_epi_plan_destroy.restype = I
+            L.gemm_epi_plan_kernel.argtypes = [P]
+            L.gemm_epi_plan_kernel.restype = ctypes.c_char_p
+            L.gemm_epi_run.argtypes = [P] * 8
+            L.gemm_epi_run.restype = I
+            L.gemm_swiglu_run.argtypes = [P] * 6
+            L.gemm_swiglu_run.restype = I
+            L.gemm_w4_run.argtypes = [P] * 9
+            L.gemm_w4_run.restype = I
+            L.gemm_epi_unfused_workspace_bytes.argtypes = [P, ctypes.POINTER(S)]
+            L.gemm_epi_unfused_workspace_bytes.restype = I
+            L.gemm_epi_run_unfused.argtypes = [P] * 9
+            L.gemm_epi_run_unfused.restype = I
+            L.gemm_swiglu_run_unfused.argtypes = [P] * 7
+            L.gemm_swiglu_run_unfused.restype = I
+            L.gemm_w4_run_unfused.argtypes = [P] * 10
+            L.gemm_w4_run_unfused.restype = I
+            L.gemm_w4_dequant_run.argtypes = [P] * 5
+            L.gemm_w4_dequant_run.restype = I
+            L.ge_add_rmsnorm_run.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
+            L.ge_add_rmsnorm_run.restype = I
+            L.ge_status_string.argtypes = [I]
+            L.ge_status_string.restype = ctypes.c_char_p
+            L.ge_last_error.argtypes = []
+            L.ge_last_error.restype = ctypes.c_char_p
+            L.ge_version.argtypes = []
+            L.ge_version.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().ge_status_string(s).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error
+        return str(s)
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise GemmEpiError(status, where, lib().ge_last_error().decode())
+
+
+# --------------------------------------------------------------------------
+# torch marshalling
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch  # plumbing: device memory and streams
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.uint8:
+        return U4X2
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ld(t) -> int:
+    """Leading dimension (row stride in elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+class Plan:
+    """Owner of a ``ge_plan*``."""
+
+    def __init__(self, desc: Desc, kind: int):
+        self.desc = desc
+        self.kind = kind
+        h = ctypes.c_void_p()
+        _check(lib().gemm_epi_plan(ctypes.byref(desc), kind, ctypes.byref(h)), "gemm_epi_plan")
+        self.handle = h
+
+    @property
+    def kernel(self) -> str:
+        return lib().gemm_epi_plan_kernel(self.handle).decode()
+
+    def workspace_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().gemm_epi_unfused_workspace_bytes(self.handle, ctypes.byref(n)),
+               "gemm_epi_unfused_workspace_bytes")
+        return n.value
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.gemm_epi_plan_destroy(h)
+            self.handle = None
+
+
+_plan_cache: dict = {}
+
+
+def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=BF16, c_type=None,
+         bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
+         alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
+         lo_first=False) -> Plan:
+    """Build (or fetch from a cache) the plan of one problem descriptor."""
+    d = Desc()
+    lib().ge_desc_init(ctypes.byref(d))
+    d.M, d.N, d.K = M, N, K
+    d.a_type = a_type
+    d.b_type = a_type if b_type is None else b_type
+    d.d_type = d_type
+    d.c_type = d_type if c_type is None else c_type
+    d.bias_type = d_type if bias_type is None else bias_type
+    d.r_type = d_type if r_type is None else r_type
+    d.b_layout = b_layout
+    d.lda, d.ldb, d.ldc, d.ldd, d.ldr = lda, ldb, ldc, ldd, ldr
+    d.alpha, d.beta = alpha, beta
+    d.act = ACTS[act] if isinstance(act, str) else int(act)
+    d.flags = ((FLAG_BIAS if bias else 0) | (FLAG_C if C else 0) | (FLAG_RESIDUAL if R else 0)
+               | (FLAG_NIBBLE_LO_FIRST if lo_first else 0))
+    d.group_size, d.zero_point = group, zero_point
+    key = (kind, bytes(d))
+    p = _plan_cache.get(key)
+    if p is None:
+        p = Plan(d, kind)
+        _plan_cache[key] = p
+    return p
+
+
+def _out(M, N, dtype, device, out):
+    if out is not None:
+        return out
+    return _torch().empty((M, N), dtype=dtype, device=device)
+
+
+def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act):
+    M, K = A.shape
+    N = B.shape[1] if b_layout == LAYOUT_KN else B.shape[0]
+    return plan(KIND_GENERIC, M, N, K, a_type=_dtype_code(A), b_type=_dtype_code(B),
+                d_type=_dtype_code(out), c_type=_dtype_code(C) if C is not None else None,
+                bias_type=_dtype_code(bias) if bias is not None else None,
+                r_type=_dtype_code(R) if R is not None else None, b_layout=b_layout,
+                lda=_ld(A), ldb=_ld(B), ldc=_ld(C) if C is not None else 0, ldd=_ld(out),
+                ldr=_ld(R) if R is not None else 0, alpha=alpha, beta=beta, act=act,
+                bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None)
+
+
+def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                  b_layout="KN", out=None, out_dtype=None, stream=None):
+    """D = act(alpha * A @ B + beta * C + bias) + R on the GPU (fused kernel)."""
+    lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
+    M = A.shape[0]
+    N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]
+    out = _out(M, N, out_dtype or A.dtype, A.device, out)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    _check(lib().gemm_epi_run(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
+                              _stream(stream)), "gemm_epi_run")
+    return out
+
+
+def gemm_epilogue_unfused(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                          b_layout="KN", out=None, out_dtype=None, workspace=None, stream=None):
+    """Same result as ``gemm_epilogue`` from the unfused chain of kernels."""
+    lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
+    M = A.shape[0]
+    N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]
+    out = _out(M, N, out_dtype or A.dtype, A.device, out)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    ws = workspace if workspace is not None else _workspace(p, A.device)
+    _check(lib().gemm_epi_run_unfused(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
+                                      _ptr(ws), _stream(stream)), "gemm_epi_run_unfused")
+    return out
+
+
+def _workspace(p: Plan, device):
+    torch = _torch()
+    return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
+
+
+def _swiglu_plan(X, Wg, out):
+    M, K = X.shape
+    N = Wg.shape[1]
+    return plan(KIND_SWIGLU, M, N, K, a_type=BF16, b_type=BF16, d_type=BF16, lda=_ld(X), ldb=_ld(Wg),
+                ldd=_ld(out))
+
+
+def swiglu(X, Wg, Wu, *, out=None, stream=None):
+    """D = silu(X @ Wg) * (X @ Wu) (fused dual GEMM)."""
+    if Wg.stride() != Wu.stride() or Wg.shape != Wu.shape:
+        raise ValueError("Wg and Wu must have the same shape and strides")
+    out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
+    p = _swiglu_plan(X, Wg, out)
+    _check(lib().gemm_swiglu_run(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream)),
+           "gemm_swiglu_run")
+    return out
+
+
+def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, stream=None):
+    out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
+    p = _swiglu_plan(X, Wg, out)
+    ws = workspace if workspace is not None else _workspace(p, X.device)
+    _check(lib().gemm_swiglu_run_unfused(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _ptr(ws),
+                                         _stream(stream)), "gemm_swiglu_run_unfused")
+    return out
+
+
+def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first):
+    M, K = X.shape
+    N = Wq.shape[1] * 2
+    return plan(KIND_W4, M, N, K, a_type=BF16, b_type=U4X2, d_type=_dtype_code(out),
+                c_type=_dtype_code(C) if C is not None else None,
+                bias_type=_dtype_code(bias) if bias is not None else None,
+                r_type=_dtype_code(R) if R is not None else None, lda=_ld(X), ldb=_ld(Wq),
+                ldc=_ld(C) if C is not None else 0, ldd=_ld(out), ldr=_ld(R) if R is not None else 0,
+                alpha=alpha, beta=beta, act=act, bias=bias is not None, C=C is not None and beta != 0.0,
+                R=R is not None, group=group, zero_point=zero_point, lo_first=lo_first)
+
+
+def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none", group=128,
+            zero_point=8, lo_first=False, out=None, out_dtype=None, stream=None):
+    """D = act(alpha * X @ deq(Wq, scales) + beta * C + bias) + R with int4 weights (fused)."""
+    out = _out(X.shape[0], Wq.shape[1] * 2, out_dtype or X.dtype, X.device, out)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first)
+    _check(lib().gemm_w4_run(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R),
+                             _ptr(out), _stream(stream)), "gemm_w4_run")
+    return out
+
+
+def w4_gemm_unfused(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                    group=128, zero_point=8, lo_first=False, out=None, out_dtype=None, workspace=None,
+                    stream=None):
+    out = _out(X.shape[0], Wq.shape[1] * 2, out_dtype or X.dtype, X.device, out)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first)
+    ws = workspace if workspace is not None else _workspace(p, X.device)
+    _check(lib().gemm_w4_run_unfused(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias),
+                                     _ptr(R), _ptr(out), _ptr(ws), _stream(stream)), "gemm_w4_run_unfused")
+    return out
+
+
+def w4_dequant(Wq, scales, *, M=1, group=128, zero_point=8, lo_first=False, out=None, stream=None):
+    """bf16 W[k][n] = rne((code - zero_point) * s[k // group][n]) (the unfused chain's first step)."""
+    torch = _torch()
+    K, N = Wq.shape[0], Wq.shape[1] * 2
+    out = out if out is not None else torch.empty((K, N), dtype=torch.bfloat16, device=Wq.device)
+    p = plan(KIND_W4, M, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), group=group,
+             zero_point=zero_point, lo_first=lo_first)
+    _check(lib().gemm_w4_dequant_run(p.handle, _ptr(Wq), _ptr(scales), _ptr(out), _stream(stream)),
+           "gemm_w4_dequant_run")
+    return out
+
+
+def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
+    """resid = a + x; out = resid * rsqrt(mean(resid^2) + eps) * w (fused row kernel, bf16)."""
+    torch = _torch()
+    M, N = a.shape
+    resid = resid if resid is not None else torch.empty_like(a)
+    out = out if out is not None else torch.empty_like(a)
+    for t in (a, x, resid, out):
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("add_rmsnorm takes dense bf16 rows")
+    _check(lib().ge_add_rmsnorm_run(M, N, _ptr(a), _ptr(x), _ptr(w), float(eps), _ptr(resid), _ptr(out),
+                                    _stream(stream)), "ge_add_rmsnorm_run")
+    return resid, out

@@ -1,0 +1,544 @@
+// ge_api.cpp -- the C ABI: descriptor validation, planning (kernel choice),
+// and the run entry points.  Host code only; kernels live in the .hip units.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "gemm_epi.h"
+#include "ge_launch.hpp"
+
+using namespace ge;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ge_status fail(ge_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+ge_status ok() {
+    g_last_error.clear();
+    return GE_OK;
+}
+
+ge_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(GE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_float_type(int32_t t) { return t == GE_F32 || t == GE_BF16; }
+size_t type_size(int32_t t) { return t == GE_F32 ? 4 : 2; }
+
+}  // namespace
+
+struct ge_plan {
+    ge_desc d;
+    int32_t kind;
+    int device;
+    int cu_count;
+    int64_t lda, ldb, ldc, ldd, ldr, ld_s;
+    int32_t group;
+    const char *kernel;  // fused kernel chosen for aligned inputs
+};
+
+namespace {
+
+// Fill a Problem from a plan and the run's pointers.
+Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void *B2, const void *scales,
+                     const void *C, const void *bias, const void *R, void *D) {
+    const ge_desc &d = pl->d;
+    Problem p{};
+    p.M = d.M;
+    p.N = d.N;
+    p.K = d.K;
+    p.mode = pl->kind == GE_KIND_SWIGLU ? MODE_SWIGLU : pl->kind == GE_KIND_W4 ? MODE_W4 : MODE_GENERIC;
+    p.ab_type = d.a_type;
+    p.b_layout = pl->kind == GE_KIND_GENERIC ? d.b_layout : GE_LAYOUT_KN;
+    p.A = A;
+    p.B = B;
+    p.B2 = B2;
+    p.scales = scales;
+    p.lda = pl->lda;
+    p.ldb = pl->ldb;
+    p.ld_s = pl->ld_s;
+    p.group = pl->group;
+    p.zero_point = d.zero_point;
+    p.lo_first = (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0;
+    EpiArgs &e = p.epi;
+    e.alpha = d.alpha;
+    e.beta = d.beta;
+    e.C = C;
+    e.bias = bias;
+    e.R = R;
+    e.D = D;
+    e.ldc = pl->ldc;
+    e.ldr = pl->ldr;
+    e.ldd = pl->ldd;
+    e.c_type = d.c_type;
+    e.bias_type = d.bias_type;
+    e.r_type = d.r_type;
+    e.d_type = d.d_type;
+    e.act = pl->kind == GE_KIND_SWIGLU ? GE_ACT_NONE : d.act;
+    uint32_t f = 0;
+    if (pl->kind != GE_KIND_SWIGLU) {
+        if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
+        if (d.flags & GE_FLAG_BIAS) f |= GE_FLAG_BIAS;
+        if (d.flags & GE_FLAG_RESIDUAL) f |= GE_FLAG_RESIDUAL;
+    }
+    e.flags = f;
+    return p;
+}
+
+// Launch the fused kernel for p: the specialised kernels when their
+// preconditions (shape, alignment) hold, the general kernel otherwise.
+hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
+    if (skinny_supported(p)) return launch_skinny(p, pl->cu_count, s);
+    if (tile_supported(p)) return launch_tile(p, pl->cu_count, s);
+    return launch_general(p, s);
+}
+
+const char *fused_name(const Problem &p) {
+    if (skinny_supported(p)) return skinny_kernel_name(p);
+    if (tile_supported(p)) return tile_kernel_name(p);
+    return "general_64x64";
+}
+
+ge_status check_device(const ge_plan *pl) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev != pl->device)
+        return fail(GE_ERR_INVALID_ARG, "plan was made on device %d but device %d is current", pl->device, dev);
+    return GE_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// D may alias C or R only exactly; A and B must not overlap D at all.
+ge_status check_alias(const ge_plan *pl, const void *A, size_t nA, const void *B, size_t nB,
+                      const void *C, const void *R, const void *D) {
+    const ge_desc &d = pl->d;
+    const size_t nD = ((size_t)(d.M - 1) * pl->ldd + d.N) * type_size(d.d_type);
+    if (overlaps(A, nA, D, nD) || overlaps(B, nB, D, nD))
+        return fail(GE_ERR_INVALID_ARG, "D overlaps an operand of the product");
+    if (C && C != D && (d.flags & GE_FLAG_C) && d.beta != 0.0f) {
+        const size_t nC = ((size_t)(d.M - 1) * pl->ldc + d.N) * type_size(d.c_type);
+        if (overlaps(C, nC, D, nD)) return fail(GE_ERR_INVALID_ARG, "D partially overlaps C");
+    }
+    if (C && C == D && pl->ldc != pl->ldd) return fail(GE_ERR_INVALID_ARG, "D aliases C with another stride");
+    if (R && R != D && (d.flags & GE_FLAG_RESIDUAL)) {
+        const size_t nR = ((size_t)(d.M - 1) * pl->ldr + d.N) * type_size(d.r_type);
+        if (overlaps(R, nR, D, nD)) return fail(GE_ERR_INVALID_ARG, "D partially overlaps R");
+    }
+    if (R && R == D && pl->ldr != pl->ldd) return fail(GE_ERR_INVALID_ARG, "D aliases R with another stride");
+    return GE_OK;
+}
+
+ge_status check_epi_ptrs(const ge_plan *pl, const void *C, const void *bias, const void *R, const void *D) {
+    const ge_desc &d = pl->d;
+    if (!D) return fail(GE_ERR_INVALID_ARG, "D is NULL");
+    if ((d.flags & GE_FLAG_C) && d.beta != 0.0f && !C) return fail(GE_ERR_INVALID_ARG, "C is NULL");
+    if ((d.flags & GE_FLAG_BIAS) && !bias) return fail(GE_ERR_INVALID_ARG, "bias is NULL");
+    if ((d.flags & GE_FLAG_RESIDUAL) && !R) return fail(GE_ERR_INVALID_ARG, "R is NULL");
+    return GE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+void ge_desc_init(ge_desc *d) {
+    if (!d) return;
+    std::memset(d, 0, sizeof *d);
+    d->alpha = 1.0f;
+    d->b_layout = GE_LAYOUT_KN;
+    d->a_type = d->b_type = d->c_type = d->d_type = d->bias_type = d->r_type = GE_BF16;
+    d->scale_type = GE_BF16;
+    d->group_size = 128;
+    d->zero_point = 8;
+}
+
+const char *ge_status_string(ge_status s) {
+    switch (s) {
+    case GE_OK: return "GE_OK";
+    case GE_ERR_INVALID_ARG: return "GE_ERR_INVALID_ARG";
+    case GE_ERR_UNSUPPORTED: return "GE_ERR_UNSUPPORTED";
+    case GE_ERR_NO_DEVICE: return "GE_ERR_NO_DEVICE";
+    case GE_ERR_HIP: return "GE_ERR_HIP";
+    case GE_ERR_ALIGN: return "GE_ERR_ALIGN";
+    default: return "GE_ERR_UNKNOWN";
+    }
+}
+
+const char *ge_last_error(void) { return g_last_error.c_str(); }
+
+const char *ge_version(void) { return "0.1.0"; }
+
+ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
+    if (!dp || !out) return fail(GE_ERR_INVALID_ARG, "descriptor or output pointer is NULL");
+    *out = nullptr;
+    const ge_desc d = *dp;
+    if (kind != GE_KIND_GENERIC && kind != GE_KIND_SWIGLU && kind != GE_KIND_W4)
+        return fail(GE_ERR_INVALID_ARG, "unknown kind %d", kind);
+    if (d.M <= 0 || d.N <= 0 || d.K <= 0) return fail(GE_ERR_INVALID_ARG, "M, N, K must be positive");
+    if ((int64_t)d.M * d.N >= (1ll << 31) || (int64_t)d.K * d.N >= (1ll << 31) ||
+        (int64_t)d.M * d.K >= (1ll << 31))
+        return fail(GE_ERR_UNSUPPORTED, "matrix with 2^31 or more elements");
+    if (d.act < GE_ACT_NONE || d.act > GE_ACT_SILU) return fail(GE_ERR_INVALID_ARG, "unknown activation %d", d.act);
+    if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST))
+        return fail(GE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags);
+    if (d.b_layout != GE_LAYOUT_KN && d.b_layout != GE_LAYOUT_NK)
+        return fail(GE_ERR_INVALID_ARG, "unknown b_layout %d", d.b_layout);
+    if (!is_float_type(d.d_type)) return fail(GE_ERR_INVALID_ARG, "d_type must be F32 or BF16");
+    if ((d.flags & GE_FLAG_C) && d.beta != 0.0f && !is_float_type(d.c_type))
+        return fail(GE_ERR_INVALID_ARG, "c_type must be F32 or BF16");
+    if ((d.flags & GE_FLAG_BIAS) && !is_float_type(d.bias_type))
+        return fail(GE_ERR_INVALID_ARG, "bias_type must be F32 or BF16");
+    if ((d.flags & GE_FLAG_RESIDUAL) && !is_float_type(d.r_type))
+        return fail(GE_ERR_INVALID_ARG, "r_type must be F32 or BF16");
+
+    ge_plan pl{};
+    pl.d = d;
+    pl.kind = kind;
+    pl.group = d.group_size ? d.group_size : 128;
+    pl.lda = d.lda ? d.lda : d.K;
+    pl.ldc = d.ldc ? d.ldc : d.N;
+    pl.ldd = d.ldd ? d.ldd : d.N;
+    pl.ldr = d.ldr ? d.ldr : d.N;
+    if (d.lda < 0 || d.ldb < 0 || d.ldc < 0 || d.ldd < 0 || d.ldr < 0)
+        return fail(GE_ERR_INVALID_ARG, "negative leading dimension");
+    if (pl.lda < d.K) return fail(GE_ERR_INVALID_ARG, "lda < K");
+    if (pl.ldd < d.N) return fail(GE_ERR_INVALID_ARG, "ldd < N");
+    if ((d.flags & GE_FLAG_C) && d.beta != 0.0f && pl.ldc < d.N) return fail(GE_ERR_INVALID_ARG, "ldc < N");
+    if ((d.flags & GE_FLAG_RESIDUAL) && pl.ldr < d.N) return fail(GE_ERR_INVALID_ARG, "ldr < N");
+
+    if (kind == GE_KIND_GENERIC) {
+        if (d.a_type != d.b_type || !is_float_type(d.a_type))
+            return fail(GE_ERR_UNSUPPORTED, "generic kind needs a_type == b_type in {F32, BF16}");
+        if (d.flags & GE_FLAG_NIBBLE_LO_FIRST) return fail(GE_ERR_INVALID_ARG, "nibble flag on a dense product");
+        pl.ldb = d.ldb ? d.ldb : (d.b_layout == GE_LAYOUT_KN ? d.N : d.K);
+        if (pl.ldb < (d.b_layout == GE_LAYOUT_KN ? d.N : d.K)) return fail(GE_ERR_INVALID_ARG, "ldb too small");
+    } else if (kind == GE_KIND_SWIGLU) {
+        if (d.a_type != GE_BF16 || d.b_type != GE_BF16 || d.d_type != GE_BF16)
+            return fail(GE_ERR_UNSUPPORTED, "swiglu needs bf16 X, W and D");
+        if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "swiglu needs KN weights");
+        if (d.act != GE_ACT_NONE || d.flags != 0 || d.alpha != 1.0f)
+            return fail(GE_ERR_UNSUPPORTED, "swiglu takes no extra epilogue");
+        pl.ldb = d.ldb ? d.ldb : d.N;
+        if (pl.ldb < d.N) return fail(GE_ERR_INVALID_ARG, "ldb < N");
+    } else {
+        if (d.a_type != GE_BF16 || d.b_type != GE_U4X2 || d.scale_type != GE_BF16)
+            return fail(GE_ERR_UNSUPPORTED, "w4 needs bf16 X, U4X2 weights and bf16 scales");
+        if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "w4 weights are [K, N/2]");
+        if (d.N % 2) return fail(GE_ERR_INVALID_ARG, "w4 needs an even N");
+        if (pl.group != 32 && pl.group != 64 && pl.group != 128 && pl.group != 256)
+            return fail(GE_ERR_UNSUPPORTED, "group size %d not in {32, 64, 128, 256}", pl.group);
+        if (d.K % pl.group) return fail(GE_ERR_INVALID_ARG, "K %% group != 0");
+        if (d.zero_point < 0 || d.zero_point > 15) return fail(GE_ERR_INVALID_ARG, "zero_point outside [0, 15]");
+        pl.ldb = d.ldb ? d.ldb : d.N / 2;
+        if (pl.ldb < d.N / 2) return fail(GE_ERR_INVALID_ARG, "ldb < N/2 bytes");
+        pl.ld_s = d.N;
+    }
+
+    // device
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        return fail(GE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GE_ERR_NO_DEVICE, "hipGetDevice failed");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(GE_ERR_NO_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(GE_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+    pl.device = dev;
+    pl.cu_count = prop.multiProcessorCount;
+
+    // name of the fused kernel for aligned pointers
+    Problem p = make_problem(&pl, (const void *)256, (const void *)256, (const void *)256, (const void *)256,
+                             (const void *)256, (const void *)256, (const void *)256, (void *)256);
+    pl.kernel = fused_name(p);
+
+    ge_plan *h = new (std::nothrow) ge_plan(pl);
+    if (!h) return fail(GE_ERR_INVALID_ARG, "out of host memory");
+    *out = h;
+    return ok();
+}
+
+ge_status gemm_epi_plan_destroy(ge_plan *plan) {
+    delete plan;
+    return ok();
+}
+
+const char *gemm_epi_plan_kernel(const ge_plan *plan) { return plan ? plan->kernel : ""; }
+
+ge_status gemm_epi_run(const ge_plan *pl, const void *A, const void *B, const void *C, const void *bias,
+                       const void *R, void *D, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (!A || !B) return fail(GE_ERR_INVALID_ARG, "A or B is NULL");
+    ge_status st = check_epi_ptrs(pl, C, bias, R, D);
+    if (st) return st;
+    const ge_desc &d = pl->d;
+    const size_t es = type_size(d.a_type);
+    const size_t nA = ((size_t)(d.M - 1) * pl->lda + d.K) * es;
+    const size_t nB = (d.b_layout == GE_LAYOUT_KN ? (size_t)(d.K - 1) * pl->ldb + d.N
+                                                  : (size_t)(d.N - 1) * pl->ldb + d.K) * es;
+    if ((st = check_alias(pl, A, nA, B, nB, C, R, D))) return st;
+    if ((st = check_device(pl))) return st;
+    const Problem p = make_problem(pl, A, B, nullptr, nullptr, C, bias, R, D);
+    return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_epi_run launch");
+}
+
+ge_status gemm_swiglu_run(const ge_plan *pl, const void *X, const void *Wg, const void *Wu, void *D,
+                          void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_SWIGLU) return fail(GE_ERR_INVALID_ARG, "plan is not a swiglu plan");
+    if (!X || !Wg || !Wu || !D) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    const ge_desc &d = pl->d;
+    const size_t nX = ((size_t)(d.M - 1) * pl->lda + d.K) * 2;
+    const size_t nW = ((size_t)(d.K - 1) * pl->ldb + d.N) * 2;
+    const size_t nD = ((size_t)(d.M - 1) * pl->ldd + d.N) * 2;
+    if (overlaps(X, nX, D, nD) || overlaps(Wg, nW, D, nD) || overlaps(Wu, nW, D, nD))
+        return fail(GE_ERR_INVALID_ARG, "D overlaps an input");
+    ge_status st;
+    if ((st = check_device(pl))) return st;
+    const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
+    return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_swiglu_run launch");
+}
+
+ge_status gemm_w4_run(const ge_plan *pl, const void *X, const uint8_t *Wq, const void *scales, const void *C,
+                      const void *bias, const void *R, void *D, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (!X || !Wq || !scales) return fail(GE_ERR_INVALID_ARG, "X, Wq or scales is NULL");
+    ge_status st = check_epi_ptrs(pl, C, bias, R, D);
+    if (st) return st;
+    const ge_desc &d = pl->d;
+    const size_t nX = ((size_t)(d.M - 1) * pl->lda + d.K) * 2;
+    const size_t nW = (size_t)(d.K - 1) * pl->ldb + d.N / 2;
+    if ((st = check_alias(pl, X, nX, Wq, nW, C, R, D))) return st;
+    const size_t nS = (size_t)(d.K / pl->group) * d.N * 2;
+    const size_t nD = ((size_t)(d.M - 1) * pl->ldd + d.N) * type_size(d.d_type);
+    if (overlaps(scales, nS, D, nD)) return fail(GE_ERR_INVALID_ARG, "D overlaps the scales");
+    if ((st = check_device(pl))) return st;
+    const Problem p = make_problem(pl, X, Wq, nullptr, scales, C, bias, R, D);
+    return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_w4_run launch");
+}
+
+// ---------------------------------------------------------------------------
+// unfused chains
+// ---------------------------------------------------------------------------
+
+ge_status gemm_epi_unfused_workspace_bytes(const ge_plan *pl, size_t *bytes) {
+    if (!pl || !bytes) return fail(GE_ERR_INVALID_ARG, "NULL argument");
+    const ge_desc &d = pl->d;
+    const size_t mn = (size_t)d.M * d.N;
+    size_t b = 0;
+    if (pl->kind == GE_KIND_SWIGLU) {
+        b = 3 * align256(mn * 2);
+    } else {
+        b = 2 * align256(mn * type_size(d.d_type));
+        if (pl->kind == GE_KIND_W4) b += align256((size_t)d.K * d.N * 2);
+    }
+    *bytes = b;
+    return ok();
+}
+
+namespace {
+
+// The epilogue of a generic / w4 plan as separate kernels.  T0 holds the plain
+// product (d_type, dense); each step reads its input buffer and writes the
+// next one; the last step writes D.
+hipError_t run_epilogue_chain(const ge_plan *pl, const void *C, const void *bias, const void *R, void *D,
+                              void *T0, void *T1, hipStream_t s) {
+    const ge_desc &d = pl->d;
+    const int32_t t = d.d_type;
+    const bool use_scale = d.alpha != 1.0f;
+    const bool use_c = (d.flags & GE_FLAG_C) && d.beta != 0.0f;
+    const bool use_bias = (d.flags & GE_FLAG_BIAS) != 0;
+    const bool use_act = d.act != GE_ACT_NONE;
+    const bool use_r = (d.flags & GE_FLAG_RESIDUAL) != 0;
+    const int steps = use_scale + use_c + use_bias + use_act + use_r;
+    void *bufs[2] = {T0, T1};
+    int cur = 0, done = 0;
+    auto dst = [&]() -> void * { return ++done == steps ? D : bufs[cur ^ 1]; };
+    hipError_t e = hipSuccess;
+    if (steps == 0) return launch_ew_copy(d.M, d.N, T0, t, D, t, d.N, s);
+    if (use_scale) {
+        void *y = dst();
+        e = launch_ew_axpby(d.M, d.N, d.alpha, bufs[cur], t, 0.0f, nullptr, t, 0, y, t, s);
+        cur ^= 1;
+        if (e) return e;
+    }
+    if (use_c) {
+        void *y = dst();
+        e = launch_ew_axpby(d.M, d.N, 1.0f, bufs[cur], t, d.beta, C, d.c_type, pl->ldc, y, t, s);
+        cur ^= 1;
+        if (e) return e;
+    }
+    if (use_bias) {
+        void *y = dst();
+        e = launch_ew_bias(d.M, d.N, bufs[cur], t, bias, d.bias_type, y, t, s);
+        cur ^= 1;
+        if (e) return e;
+    }
+    if (use_act) {
+        void *y = dst();
+        e = launch_ew_act(d.M, d.N, d.act, bufs[cur], t, y, t, s);
+        cur ^= 1;
+        if (e) return e;
+    }
+    if (use_r) {
+        void *y = dst();
+        e = launch_ew_add(d.M, d.N, bufs[cur], t, R, d.r_type, pl->ldr, y, t, d.N, s);
+        cur ^= 1;
+    }
+    return e;
+}
+
+// plain product into a dense buffer of the output type
+Problem plain_problem(const ge_plan *pl, const void *A, const void *B, const void *B2, const void *scales,
+                      void *out, int32_t out_type) {
+    Problem p = make_problem(pl, A, B, B2, scales, nullptr, nullptr, nullptr, out);
+    p.epi.alpha = 1.0f;
+    p.epi.beta = 0.0f;
+    p.epi.flags = 0;
+    p.epi.act = GE_ACT_NONE;
+    p.epi.ldd = pl->d.N;
+    p.epi.d_type = out_type;
+    return p;
+}
+
+ge_status check_ws(const ge_plan *pl, void *ws) {
+    if (!ws) return fail(GE_ERR_INVALID_ARG, "workspace is NULL");
+    if ((uintptr_t)ws & 255) return fail(GE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (pl->ldd != pl->d.N) return fail(GE_ERR_UNSUPPORTED, "unfused chains write a dense D (ldd == N)");
+    return GE_OK;
+}
+
+}  // namespace
+
+ge_status gemm_epi_run_unfused(const ge_plan *pl, const void *A, const void *B, const void *C,
+                               const void *bias, const void *R, void *D, void *ws, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (!A || !B) return fail(GE_ERR_INVALID_ARG, "A or B is NULL");
+    ge_status st = check_epi_ptrs(pl, C, bias, R, D);
+    if (st || (st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
+    const ge_desc &d = pl->d;
+    const size_t mnb = align256((size_t)d.M * d.N * type_size(d.d_type));
+    void *T0 = ws, *T1 = (char *)ws + mnb;
+    hipStream_t s = (hipStream_t)stream;
+    Problem p = plain_problem(pl, A, B, nullptr, nullptr, T0, d.d_type);
+    hipError_t e = launch_fused(pl, p, s);
+    if (e == hipSuccess) e = run_epilogue_chain(pl, C, bias, R, D, T0, T1, s);
+    return hip_status(e, "gemm_epi_run_unfused");
+}
+
+ge_status gemm_swiglu_run_unfused(const ge_plan *pl, const void *X, const void *Wg, const void *Wu, void *D,
+                                  void *ws, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_SWIGLU) return fail(GE_ERR_INVALID_ARG, "plan is not a swiglu plan");
+    if (!X || !Wg || !Wu || !D) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    ge_status st;
+    if ((st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
+    const ge_desc &d = pl->d;
+    const int64_t mn = (int64_t)d.M * d.N;
+    const size_t mnb = align256((size_t)mn * 2);
+    void *G = ws, *U = (char *)ws + mnb, *S = (char *)ws + 2 * mnb;
+    hipStream_t s = (hipStream_t)stream;
+    // gate and up products as two plain GEMMs (generic kind, bf16 out)
+    ge_plan gp = *pl;
+    gp.kind = GE_KIND_GENERIC;
+    gp.d.b_layout = GE_LAYOUT_KN;
+    Problem pg = plain_problem(&gp, X, Wg, nullptr, nullptr, G, GE_BF16);
+    Problem pu = plain_problem(&gp, X, Wu, nullptr, nullptr, U, GE_BF16);
+    hipError_t e = launch_fused(&gp, pg, s);
+    if (!e) e = launch_fused(&gp, pu, s);
+    if (!e) e = launch_ew_sigmoid(mn, G, S, s);   // s = sigmoid(g)
+    if (!e) e = launch_ew_mul(mn, G, S, S, s);    // h = g * s  (silu)
+    if (!e) e = launch_ew_mul(mn, S, U, D, s);    // out = h * u
+    return hip_status(e, "gemm_swiglu_run_unfused");
+}
+
+ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *Wq, const void *scales,
+                              const void *C, const void *bias, const void *R, void *D, void *ws, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (!X || !Wq || !scales) return fail(GE_ERR_INVALID_ARG, "X, Wq or scales is NULL");
+    ge_status st = check_epi_ptrs(pl, C, bias, R, D);
+    if (st || (st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
+    const ge_desc &d = pl->d;
+    const size_t mnb = align256((size_t)d.M * d.N * type_size(d.d_type));
+    void *W = ws;
+    void *T0 = (char *)ws + align256((size_t)d.K * d.N * 2);
+    void *T1 = (char *)T0 + mnb;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_w4_dequant(d.K, d.N, Wq, pl->ldb, scales, pl->ld_s, pl->group, d.zero_point,
+                                     (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, s);
+    if (!e) {
+        ge_plan gp = *pl;
+        gp.kind = GE_KIND_GENERIC;
+        gp.d.b_type = GE_BF16;
+        gp.d.b_layout = GE_LAYOUT_KN;
+        gp.ldb = d.N;
+        Problem p = plain_problem(&gp, X, W, nullptr, nullptr, T0, d.d_type);
+        e = launch_fused(&gp, p, s);
+    }
+    if (!e) e = run_epilogue_chain(pl, C, bias, R, D, T0, T1, s);
+    return hip_status(e, "gemm_w4_run_unfused");
+}
+
+ge_status gemm_w4_dequant_run(const ge_plan *pl, const uint8_t *Wq, const void *scales, void *W, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (!Wq || !scales || !W) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    ge_status st;
+    if ((st = check_device(pl))) return st;
+    const ge_desc &d = pl->d;
+    return hip_status(launch_w4_dequant(d.K, d.N, Wq, pl->ldb, scales, pl->ld_s, pl->group, d.zero_point,
+                                        (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, (hipStream_t)stream),
+                      "gemm_w4_dequant_run");
+}
+
+ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,
+                             void *resid, void *out, void *stream) {
+    if (M <= 0 || N <= 0) return fail(GE_ERR_INVALID_ARG, "M and N must be positive");
+    if (N > 16384) return fail(GE_ERR_UNSUPPORTED, "rows longer than 16384 elements");
+    if (!a || !x || !w || !resid || !out) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    if (!(eps >= 0.0f)) return fail(GE_ERR_INVALID_ARG, "eps must be >= 0");
+    const size_t nb = (size_t)M * N * 2;
+    if (overlaps(out, nb, a, nb) || overlaps(out, nb, x, nb) || overlaps(out, nb, resid, nb))
+        return fail(GE_ERR_INVALID_ARG, "out overlaps an input or resid");
+    if ((resid != a && overlaps(resid, nb, a, nb)) || (resid != x && overlaps(resid, nb, x, nb)))
+        return fail(GE_ERR_INVALID_ARG, "resid partially overlaps an input");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        return fail(GE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    return hip_status(launch_add_rmsnorm(M, N, a, x, w, eps, resid, out, (hipStream_t)stream),
+                      "ge_add_rmsnorm_run");
+}
+
+}  // extern "C"

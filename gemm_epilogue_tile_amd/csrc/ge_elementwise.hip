@@ -1,0 +1,319 @@
+// ge_elementwise.hip -- one-op-per-kernel building blocks of the deliberately
+// unfused chains (each reads its inputs from memory and writes its output
+// back, as an eager framework would), the standalone int4 dequant kernel, and
+// the fused residual-add + RMSNorm row kernel.
+//
+// All of them are bandwidth-bound: rows are walked in 8-element chunks with
+// 16-byte vector accesses when the row is aligned, element by element
+// otherwise.
+
+#include "ge_launch.hpp"
+
+namespace ge {
+namespace {
+
+constexpr int EW_THREADS = 256;
+
+__device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// Walk an M x N index space in 8-column chunks: f(m, n, vec) where vec says the
+// whole chunk n..n+7 is inside the row.
+template <typename F>
+__device__ __forceinline__ void for_chunks(int64_t M, int64_t N, F &&f) {
+    const int64_t chunks = (N + 7) / 8;
+    const int64_t total = M * chunks;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = c / chunks;
+        const int64_t n = (c - m * chunks) * 8;
+        f(m, n, n + 8 <= N);
+    }
+}
+
+dim3 ew_grid(int64_t M, int64_t N) {
+    const int64_t chunks = M * ((N + 7) / 8);
+    int64_t blocks = (chunks + EW_THREADS - 1) / EW_THREADS;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    return dim3((unsigned)blocks);
+}
+
+// read 8 (or the remaining) elements of row m, columns n.., as fp32
+__device__ __forceinline__ void rd(const void *p, int32_t t, int64_t ld, int64_t m, int64_t n,
+                                   int64_t N, bool vec, bool al, float v[8]) {
+    const int64_t off = m * ld + n;
+    if (vec && al) {
+        load8(p, t, off, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (n + i < N) ? load_elem(p, t, off + i) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void wr(void *p, int32_t t, int64_t ld, int64_t m, int64_t n, int64_t N,
+                                   bool vec, bool al, const float v[8]) {
+    const int64_t off = m * ld + n;
+    if (vec && al) {
+        store8(p, t, off, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (n + i < N) store_elem(p, t, off + i, v[i]);
+    }
+}
+
+// rows of a dense or strided matrix are 16-byte aligned when base and stride are
+__device__ __forceinline__ bool rows_aligned(const void *p, int32_t t, int64_t ld) {
+    const int64_t es = t == GE_BF16 ? 2 : 4;
+    return aligned16(p) && ((ld * es) & 15) == 0;
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_axpby(int64_t M, int64_t N, float alpha,
+                                                     const void *X, int32_t xt, float beta,
+                                                     const void *C, int32_t ct, int64_t ldc,
+                                                     void *Y, int32_t yt) {
+    const bool ax = rows_aligned(X, xt, N), ay = rows_aligned(Y, yt, N);
+    const bool ac = C ? rows_aligned(C, ct, ldc) : true;
+    for_chunks(M, N, [&](int64_t m, int64_t n, bool vec) {
+        float x[8], c[8];
+        rd(X, xt, N, m, n, N, vec, ax, x);
+        if (C) {
+            rd(C, ct, ldc, m, n, N, vec, ac, c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = fmaf(beta, c[i], alpha * x[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = alpha * x[i];
+        }
+        wr(Y, yt, N, m, n, N, vec, ay, x);
+    });
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_bias(int64_t M, int64_t N, const void *X, int32_t xt,
+                                                    const void *bias, int32_t bt, void *Y, int32_t yt) {
+    const bool ax = rows_aligned(X, xt, N), ay = rows_aligned(Y, yt, N), ab = aligned16(bias);
+    for_chunks(M, N, [&](int64_t m, int64_t n, bool vec) {
+        float x[8], b[8];
+        rd(X, xt, N, m, n, N, vec, ax, x);
+        rd(bias, bt, 0, 0, n, N, vec, ab, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] += b[i];
+        wr(Y, yt, N, m, n, N, vec, ay, x);
+    });
+}
+
+template <int ACT>
+__global__ __launch_bounds__(EW_THREADS) void k_act(int64_t M, int64_t N, const void *X, int32_t xt,
+                                                   void *Y, int32_t yt) {
+    const bool ax = rows_aligned(X, xt, N), ay = rows_aligned(Y, yt, N);
+    for_chunks(M, N, [&](int64_t m, int64_t n, bool vec) {
+        float x[8];
+        rd(X, xt, N, m, n, N, vec, ax, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = activate<ACT>(x[i]);
+        wr(Y, yt, N, m, n, N, vec, ay, x);
+    });
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_add(int64_t M, int64_t N, const void *X, int32_t xt,
+                                                   const void *R, int32_t rt, int64_t ldr, void *Y,
+                                                   int32_t yt, int64_t ldy) {
+    const bool ax = rows_aligned(X, xt, N), ar = rows_aligned(R, rt, ldr), ay = rows_aligned(Y, yt, ldy);
+    for_chunks(M, N, [&](int64_t m, int64_t n, bool vec) {
+        float x[8], r[8];
+        rd(X, xt, N, m, n, N, vec, ax, x);
+        rd(R, rt, ldr, m, n, N, vec, ar, r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] += r[i];
+        wr(Y, yt, ldy, m, n, N, vec, ay, x);
+    });
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_copy(int64_t M, int64_t N, const void *X, int32_t xt,
+                                                    void *Y, int32_t yt, int64_t ldy) {
+    const bool ax = rows_aligned(X, xt, N), ay = rows_aligned(Y, yt, ldy);
+    for_chunks(M, N, [&](int64_t m, int64_t n, bool vec) {
+        float x[8];
+        rd(X, xt, N, m, n, N, vec, ax, x);
+        wr(Y, yt, ldy, m, n, N, vec, ay, x);
+    });
+}
+
+// bf16 sigmoid and product, treated as flat arrays of `count` elements
+__global__ __launch_bounds__(EW_THREADS) void k_sigmoid(int64_t count, const void *X, void *Y) {
+    const bool al = aligned16(X) && aligned16(Y);
+    for_chunks(1, count, [&](int64_t, int64_t n, bool vec) {
+        float x[8];
+        rd(X, GE_BF16, 0, 0, n, count, vec, al, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fast_sigmoid(x[i]);
+        wr(Y, GE_BF16, 0, 0, n, count, vec, al, x);
+    });
+}
+
+__global__ __launch_bounds__(EW_THREADS) void k_mul(int64_t count, const void *X, const void *Z, void *Y) {
+    const bool al = aligned16(X) && aligned16(Z) && aligned16(Y);
+    for_chunks(1, count, [&](int64_t, int64_t n, bool vec) {
+        float x[8], z[8];
+        rd(X, GE_BF16, 0, 0, n, count, vec, al, x);
+        rd(Z, GE_BF16, 0, 0, n, count, vec, al, z);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= z[i];
+        wr(Y, GE_BF16, 0, 0, n, count, vec, al, x);
+    });
+}
+
+// W[k][n] = bf16((code - zp) * s[k / group][n]); 8 columns (4 bytes) per step
+__global__ __launch_bounds__(EW_THREADS) void k_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq,
+                                                          int64_t ldq, const uint16_t *scales,
+                                                          int64_t lds, int32_t group, int32_t zp,
+                                                          int32_t lo_first, uint16_t *W) {
+    const bool al = aligned16(W) && ((N & 7) == 0) && aligned16(scales) && ((lds & 7) == 0);
+    for_chunks(K, N, [&](int64_t k, int64_t n, bool vec) {
+        float w[8];
+        const uint16_t *srow = scales + (k / group) * lds;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t c = n + i;
+            if (c < N) {
+                const uint8_t b = Wq[k * ldq + (c >> 1)];
+                const bool even = (c & 1) == 0;
+                const int code = (even != (lo_first != 0)) ? (b >> 4) : (b & 0xF);
+                w[i] = (float)(code - zp) * bf16_to_f32(srow[c]);
+            } else {
+                w[i] = 0.0f;
+            }
+        }
+        wr(W, GE_BF16, N, k, n, N, vec, al, w);
+    });
+}
+
+// One workgroup per row.  r = a + x in fp32 is kept in registers (at most
+// RMS_MAX_CHUNKS 8-element chunks per thread, so N <= 256 * 8 * 8 = 16384);
+// resid = bf16(r) is written; rrms = 1 / sqrt(sum(r^2) / N + eps) over the
+// fp32 r; out = bf16(r * rrms * w).  Every input element is read before the
+// same thread writes resid at that position, so resid may alias a or x.
+constexpr int RMS_MAX_CHUNKS = 8;
+
+__global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm(int32_t M, int32_t N, const uint16_t *a,
+                                                           const uint16_t *x, const uint16_t *w,
+                                                           float eps, uint16_t *resid, uint16_t *out) {
+    __shared__ float red[EW_THREADS / 64];
+    const bool al = aligned16(a) && aligned16(x) && aligned16(w) && aligned16(resid) &&
+                    aligned16(out) && (N & 7) == 0;
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        float r[RMS_MAX_CHUNKS][8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < RMS_MAX_CHUNKS; ++c) {
+            const int64_t n = ((int64_t)c * EW_THREADS + threadIdx.x) * 8;
+            if (n < N) {
+                const bool vec = n + 8 <= N;
+                float vx[8];
+                rd(a, GE_BF16, N, m, n, N, vec, al, r[c]);
+                rd(x, GE_BF16, N, m, n, N, vec, al, vx);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    r[c][i] += vx[i];
+                    ss = fmaf(r[c][i], r[c][i], ss);
+                }
+                wr(resid, GE_BF16, N, m, n, N, vec, al, r[c]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EW_THREADS / 64; ++i) tot += red[i];
+        const float rrms = 1.0f / sqrtf(tot / (float)N + eps);
+#pragma unroll
+        for (int c = 0; c < RMS_MAX_CHUNKS; ++c) {
+            const int64_t n = ((int64_t)c * EW_THREADS + threadIdx.x) * 8;
+            if (n < N) {
+                const bool vec = n + 8 <= N;
+                float vw[8];
+                rd(w, GE_BF16, 0, 0, n, N, vec, al, vw);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vw[i] = r[c][i] * rrms * vw[i];
+                wr(out, GE_BF16, N, m, n, N, vec, al, vw);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ew_axpby(int64_t M, int64_t N, float alpha, const void *X, int32_t x_type,
+                           float beta, const void *C, int32_t c_type, int64_t ldc, void *Y,
+                           int32_t y_type, hipStream_t s) {
+    hipLaunchKernelGGL(k_axpby, ew_grid(M, N), dim3(EW_THREADS), 0, s, M, N, alpha, X, x_type, beta,
+                       C, c_type, ldc, Y, y_type);
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_bias(int64_t M, int64_t N, const void *X, int32_t x_type, const void *bias,
+                          int32_t bias_type, void *Y, int32_t y_type, hipStream_t s) {
+    hipLaunchKernelGGL(k_bias, ew_grid(M, N), dim3(EW_THREADS), 0, s, M, N, X, x_type, bias, bias_type,
+                       Y, y_type);
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_act(int64_t M, int64_t N, int32_t act, const void *X, int32_t x_type, void *Y,
+                         int32_t y_type, hipStream_t s) {
+    const dim3 g = ew_grid(M, N), b(EW_THREADS);
+    switch (act) {
+    case GE_ACT_RELU: hipLaunchKernelGGL(k_act<GE_ACT_RELU>, g, b, 0, s, M, N, X, x_type, Y, y_type); break;
+    case GE_ACT_GELU_TANH:
+        hipLaunchKernelGGL(k_act<GE_ACT_GELU_TANH>, g, b, 0, s, M, N, X, x_type, Y, y_type);
+        break;
+    case GE_ACT_SILU: hipLaunchKernelGGL(k_act<GE_ACT_SILU>, g, b, 0, s, M, N, X, x_type, Y, y_type); break;
+    default: hipLaunchKernelGGL(k_act<GE_ACT_NONE>, g, b, 0, s, M, N, X, x_type, Y, y_type); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_add(int64_t M, int64_t N, const void *X, int32_t x_type, const void *R,
+                         int32_t r_type, int64_t ldr, void *Y, int32_t y_type, int64_t ldy,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(k_add, ew_grid(M, N), dim3(EW_THREADS), 0, s, M, N, X, x_type, R, r_type, ldr, Y,
+                       y_type, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_copy(int64_t M, int64_t N, const void *X, int32_t x_type, void *Y,
+                          int32_t y_type, int64_t ldy, hipStream_t s) {
+    hipLaunchKernelGGL(k_copy, ew_grid(M, N), dim3(EW_THREADS), 0, s, M, N, X, x_type, Y, y_type, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_sigmoid(int64_t count, const void *X, void *Y, hipStream_t s) {
+    hipLaunchKernelGGL(k_sigmoid, ew_grid(1, count), dim3(EW_THREADS), 0, s, count, X, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_ew_mul(int64_t count, const void *X, const void *Z, void *Y, hipStream_t s) {
+    hipLaunchKernelGGL(k_mul, ew_grid(1, count), dim3(EW_THREADS), 0, s, count, X, Z, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
+                             const void *scales, int64_t ld_s, int32_t group, int32_t zero_point,
+                             int32_t lo_first, void *W, hipStream_t s) {
+    hipLaunchKernelGGL(k_w4_dequant, ew_grid(K, N), dim3(EW_THREADS), 0, s, K, N, Wq, ldq,
+                       (const uint16_t *)scales, ld_s, group, zero_point, lo_first, (uint16_t *)W);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                              float eps, void *resid, void *out, hipStream_t s) {
+    const unsigned blocks = (unsigned)(M < 65536 ? M : 65536);
+    hipLaunchKernelGGL(k_add_rmsnorm, dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
+                       (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
+                       (uint16_t *)resid, (uint16_t *)out);
+    return hipGetLastError();
+}
+
+}  // namespace ge

@@ -1,0 +1,67 @@
+// ge_launch.hpp -- internal interface between the host planner (ge_api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ge_device.hpp"
+
+namespace ge {
+
+enum Mode : int32_t { MODE_GENERIC = 0, MODE_SWIGLU = 1, MODE_W4 = 2 };
+
+// A fully described product + epilogue, pointers included.
+struct Problem {
+    int32_t M, N, K;
+    int32_t mode;       // Mode
+    int32_t ab_type;    // GE_F32 / GE_BF16 storage of A (and of dense B)
+    int32_t b_layout;   // GE_LAYOUT_KN / GE_LAYOUT_NK (dense B only)
+    const void *A;
+    const void *B;      // dense B, Wg (swiglu) or Wq (w4)
+    const void *B2;     // Wu (swiglu)
+    const void *scales; // w4 scales (bf16)
+    int64_t lda, ldb, ld_s;
+    int32_t group, zero_point, lo_first;
+    EpiArgs epi;
+};
+
+// Fallback tile kernel: any shape, stride and alignment.
+hipError_t launch_general(const Problem &p, hipStream_t s);
+
+// Large-tile bf16 MFMA kernel (M large).  Returns hipErrorInvalidValue when
+// the problem does not meet its preconditions (see tile_supported()).
+bool tile_supported(const Problem &p);
+hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s);
+const char *tile_kernel_name(const Problem &p);
+
+// Small-M weight-streaming kernel (decode shapes).
+bool skinny_supported(const Problem &p);
+hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);
+const char *skinny_kernel_name(const Problem &p);
+
+// Elementwise kernels of the unfused chain.  All tensors dense [M, N] of the
+// given storage type unless noted.
+hipError_t launch_ew_axpby(int64_t M, int64_t N, float alpha, const void *X, int32_t x_type,
+                           float beta, const void *C, int32_t c_type, int64_t ldc, void *Y,
+                           int32_t y_type, hipStream_t s);
+hipError_t launch_ew_bias(int64_t M, int64_t N, const void *X, int32_t x_type, const void *bias,
+                          int32_t bias_type, void *Y, int32_t y_type, hipStream_t s);
+hipError_t launch_ew_act(int64_t M, int64_t N, int32_t act, const void *X, int32_t x_type, void *Y,
+                         int32_t y_type, hipStream_t s);
+hipError_t launch_ew_add(int64_t M, int64_t N, const void *X, int32_t x_type, const void *R,
+                         int32_t r_type, int64_t ldr, void *Y, int32_t y_type, int64_t ldy,
+                         hipStream_t s);
+hipError_t launch_ew_sigmoid(int64_t count, const void *X, void *Y, hipStream_t s);   // bf16
+hipError_t launch_ew_mul(int64_t count, const void *X, const void *Z, void *Y, hipStream_t s);  // bf16
+hipError_t launch_ew_copy(int64_t M, int64_t N, const void *X, int32_t x_type, void *Y,
+                          int32_t y_type, int64_t ldy, hipStream_t s);
+hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
+                             const void *scales, int64_t ld_s, int32_t group, int32_t zero_point,
+                             int32_t lo_first, void *W, hipStream_t s);
+
+// Fused residual add + RMSNorm (bf16 rows).
+hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                              float eps, void *resid, void *out, hipStream_t s);
+
+}  // namespace ge

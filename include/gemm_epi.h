@@ -1,0 +1,216 @@
+/*
+ * gemm_epi.h -- C ABI of the fused GEMM + epilogue engine for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * What is computed (pages "Fusion and Epilogues" (Epilogue fusion), "Kernel
+ * fusion" (Concept, Check yourself) and "Fusion Thinking" (Patterns 2 and 3)):
+ *
+ *   generic   D = act(alpha * A.B + beta * C + bias) + R
+ *   swiglu    D = silu(X.Wg) * (X.Wu)
+ *   w4        D = act(alpha * X.deq(Wq, s) + beta * C + bias) + R,
+ *             deq(Wq, s)[k][n] = (code[k][n] - zero_point) * s[k / group][n]
+ *
+ * The whole epilogue is applied to the fp32 accumulator tile while it is
+ * still on chip, so D is written to memory exactly once.  The unfused entry
+ * points compute the same results as a chain of separate kernels (one memory
+ * round trip per step); they exist to measure what fusion saves.
+ *
+ * Conventions common to every entry point
+ *   - Matrices are row-major.  Element (i, j) of a matrix with leading
+ *     dimension ld lives at base[i * ld + j]; ld is counted in elements
+ *     (bytes for packed int4), 0 means dense.
+ *   - A is [M, K].  B is [K, N] (GE_LAYOUT_KN) or stored transposed as [N, K]
+ *     (GE_LAYOUT_NK).  C, R and D are [M, N]; bias is [N].
+ *   - Packed int4 weights Wq are [K, N/2] bytes: byte j of row k holds the
+ *     codes of columns 2j and 2j+1, high nibble first unless the flag
+ *     GE_FLAG_NIBBLE_LO_FIRST is set.  Scales are [K / group, N].
+ *   - All device pointers belong to the caller and must be device memory of
+ *     the device that was current when the plan was made.  The library never
+ *     allocates, frees or synchronises in a run call: runs are asynchronous on
+ *     the given stream (a hipStream_t passed as void*, NULL = null stream) and
+ *     may be captured into a HIP graph.
+ *   - D may alias C or R exactly (same pointer, same leading dimension); any
+ *     other overlap between D and an input is undefined.
+ *   - Arithmetic: products in bf16 x bf16 (or fp32 x fp32) with fp32
+ *     accumulation, epilogue in fp32, one round-to-nearest-even conversion to
+ *     the output type.
+ *   - Errors: every function returns a ge_status; nothing is thrown across the
+ *     ABI.  On an error no work has been queued; a thread-local message is
+ *     available from ge_last_error().
+ *
+ * Plans are immutable once made: one plan may be used from several threads
+ * and streams at once.
+ */
+#ifndef GEMM_EPI_H
+#define GEMM_EPI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GE_API __attribute__((visibility("default")))
+#else
+#define GE_API
+#endif
+
+typedef int32_t ge_status;
+#define GE_OK 0
+#define GE_ERR_INVALID_ARG 1 /* bad shape, stride, pointer or enum value */
+#define GE_ERR_UNSUPPORTED 2 /* valid request that no kernel instance covers */
+#define GE_ERR_NO_DEVICE 3   /* no usable HIP device (or not a gfx950) */
+#define GE_ERR_HIP 4         /* HIP runtime or launch error; see ge_last_error() */
+#define GE_ERR_ALIGN 5       /* a pointer / stride breaks the alignment the kernel needs */
+
+/* storage types */
+#define GE_F32 0
+#define GE_BF16 1
+#define GE_U4X2 2 /* two 4-bit codes per byte (packed int4 weights) */
+
+/* layout of the second operand */
+#define GE_LAYOUT_KN 0 /* B[k][n] at B[k * ldb + n] */
+#define GE_LAYOUT_NK 1 /* B[k][n] at B[n * ldb + k] */
+
+/* activations (applied after alpha, beta * C and bias; before R) */
+#define GE_ACT_NONE 0
+#define GE_ACT_RELU 1      /* max(t, 0) */
+#define GE_ACT_GELU_TANH 2 /* 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))) */
+#define GE_ACT_SILU 3      /* t / (1 + exp(-t)) */
+
+/* plan kinds */
+#define GE_KIND_GENERIC 0
+#define GE_KIND_SWIGLU 1
+#define GE_KIND_W4 2
+
+/* flags */
+#define GE_FLAG_BIAS 1u            /* add bias[n] */
+#define GE_FLAG_C 2u               /* add beta * C (ignored when beta == 0) */
+#define GE_FLAG_RESIDUAL 4u        /* add R after the activation */
+#define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
+
+/*
+ * Problem descriptor.  Unused fields must be zero.  dtype fields take
+ * GE_F32 / GE_BF16 (b_type may be GE_U4X2 for GE_KIND_W4).
+ *
+ * Supported combinations:
+ *   GENERIC  a_type == b_type in {F32, BF16}; c/bias/r/d types in {F32, BF16};
+ *            b_layout KN or NK; any act; any flags except NIBBLE_LO_FIRST.
+ *   SWIGLU   a, b, d = BF16, b_layout KN, act = NONE, alpha = 1, no flags
+ *            other than none; Wg and Wu share ldb.
+ *   W4       a = BF16, b = U4X2, scale_type = BF16, d/bias/c/r in {F32, BF16},
+ *            K % group == 0, N even, group in {32, 64, 128, 256},
+ *            zero_point in [0, 15].
+ */
+typedef struct ge_desc {
+    int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */
+    int32_t a_type, b_type;  /* operand storage types */
+    int32_t c_type, d_type;  /* C and D storage types */
+    int32_t bias_type, r_type, scale_type;
+    int32_t b_layout;        /* GE_LAYOUT_KN or GE_LAYOUT_NK */
+    int64_t lda, ldb, ldc, ldd, ldr; /* leading dimensions (elements; bytes for Wq); 0 = dense */
+    float alpha, beta;
+    int32_t act;             /* GE_ACT_* */
+    uint32_t flags;          /* GE_FLAG_* */
+    int32_t group_size;      /* W4 scale group along K (0 = 128) */
+    int32_t zero_point;      /* W4 code offset (the pages use 8) */
+} ge_desc;
+
+typedef struct ge_plan ge_plan;
+
+/* Fill *d with the defaults: alpha 1, everything else 0 / dense / KN. */
+GE_API void ge_desc_init(ge_desc *d);
+
+/*
+ * Validate d for the given kind and choose a kernel instance.  On success
+ * *out receives a library-owned plan that the caller releases with
+ * gemm_epi_plan_destroy().  Queries the current device (architecture and
+ * compute-unit count); allocates host memory only.
+ * Errors: INVALID_ARG (bad descriptor or null out), UNSUPPORTED, NO_DEVICE.
+ */
+GE_API ge_status gemm_epi_plan(const ge_desc *d, int32_t kind, ge_plan **out);
+
+/* Release a plan (NULL is accepted). */
+GE_API ge_status gemm_epi_plan_destroy(ge_plan *plan);
+
+/* Name of the fused kernel instance a plan launches (static string). */
+GE_API const char *gemm_epi_plan_kernel(const ge_plan *plan);
+
+/*
+ * Fused generic GEMM + epilogue:  D = act(alpha * A.B + beta * C + bias) + R.
+ * C is read only when GE_FLAG_C is set and beta != 0; bias only with
+ * GE_FLAG_BIAS; R only with GE_FLAG_RESIDUAL (pointers that are not read may
+ * be NULL).  Fast paths need 16-byte aligned bases and leading dimensions
+ * that are multiples of 8 elements; other inputs run a general kernel.
+ */
+GE_API ge_status gemm_epi_run(const ge_plan *plan, const void *A, const void *B, const void *C,
+                       const void *bias, const void *R, void *D, void *stream);
+
+/*
+ * Fused SwiGLU dual GEMM:  D = silu(X.Wg) * (X.Wu).  X is [M, K]; Wg and Wu
+ * are [K, N] with the plan's ldb.  Each X tile is read once and feeds both
+ * products (page "Fusion Thinking", Pattern 2, Level 2).
+ */
+GE_API ge_status gemm_swiglu_run(const ge_plan *plan, const void *X, const void *Wg, const void *Wu,
+                          void *D, void *stream);
+
+/*
+ * Fused W4A16 GEMM: the packed int4 weights are unpacked and dequantised
+ * inside the K loop and never exist in memory as bf16 (page "Fusion
+ * Thinking", Pattern 3).  D = act(alpha * X.deq(Wq, s) + beta*C + bias) + R.
+ */
+GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *Wq, const void *scales,
+                      const void *C, const void *bias, const void *R, void *D, void *stream);
+
+/*
+ * Deliberately unfused chains, for measurement only: the plain GEMM writes
+ * its fp32-accumulated result to the workspace in the output type (bf16 or
+ * fp32), then one elementwise kernel per epilogue step reads and writes
+ * memory (generic: scale / C, bias, activation, residual; swiglu: gate GEMM,
+ * up GEMM, then sigmoid, multiply, multiply, as separate kernels; w4: a
+ * dequant kernel writes the bf16 weights to the workspace first).  The
+ * caller owns the workspace, of at least gemm_epi_unfused_workspace_bytes()
+ * bytes, 256-byte aligned.
+ */
+GE_API ge_status gemm_epi_unfused_workspace_bytes(const ge_plan *plan, size_t *bytes);
+GE_API ge_status gemm_epi_run_unfused(const ge_plan *plan, const void *A, const void *B, const void *C,
+                               const void *bias, const void *R, void *D, void *workspace,
+                               void *stream);
+GE_API ge_status gemm_swiglu_run_unfused(const ge_plan *plan, const void *X, const void *Wg,
+                                  const void *Wu, void *D, void *workspace, void *stream);
+GE_API ge_status gemm_w4_run_unfused(const ge_plan *plan, const void *X, const uint8_t *Wq,
+                              const void *scales, const void *C, const void *bias, const void *R,
+                              void *D, void *workspace, void *stream);
+
+/*
+ * First step of the unfused W4 chain on its own: W[k][n] =
+ * bf16_rne((code[k][n] - zero_point) * s[k / group][n]), W dense [K, N] bf16.
+ */
+GE_API ge_status gemm_w4_dequant_run(const ge_plan *plan, const uint8_t *Wq, const void *scales, void *W,
+                              void *stream);
+
+/*
+ * Fused residual add + RMSNorm over rows of length N (page "Fusion
+ * Thinking", Pattern 1): resid = a + x; out = resid / sqrt(mean(resid^2) +
+ * eps) * w.  a, x, resid, out are [M, N] bf16 (dense), w is [N] bf16.  resid
+ * may alias a or x exactly.
+ */
+GE_API ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                             float eps, void *resid, void *out, void *stream);
+
+/* Static text for a status code. */
+GE_API const char *ge_status_string(ge_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+GE_API const char *ge_last_error(void);
+
+/* Library version, "major.minor.patch". */
+GE_API const char *ge_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPI_H */

@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU test modules (moving seeded host arrays to the
+device and comparing device results with the oracle)."""
+import numpy as np
+import torch
+
+import workloads
+
+DEV = torch.device("cuda:0")
+
+TOL_BF16 = 1e-2   # max |gpu - ref| / (1 + |ref|) for bf16 outputs
+TOL_F32 = 1e-4    # ... for fp32 outputs
+
+
+def to_dev(a, dtype=None):
+    """numpy (bf16 as uint16 bits, f32, uint8) -> device tensor of the storage type."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16 or dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t) -> np.ndarray:
+    """device tensor -> float64 numpy (exact widening of bf16 / fp32)."""
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    return np.abs(gpu - ref) / (1.0 + np.abs(ref))
+
+
+def assert_close(gpu_t, ref, tol, what=""):
+    g = to_host(gpu_t) if isinstance(gpu_t, torch.Tensor) else gpu_t
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    e = rel_err(g, ref)
+    i = np.unravel_index(np.argmax(e), e.shape)
+    assert e[i] <= tol, f"{what}: max err {e[i]:.3e} at {i}: gpu {g[i]!r} ref {ref[i]!r} (tol {tol})"
+    return float(e[i])
+
+
+def dev_inputs(inp: dict) -> dict:
+    """Device copies of every array in a workloads.make_inputs dict."""
+    out = {}
+    for k, v in inp.items():
+        if isinstance(v, np.ndarray):
+            out[k] = to_dev(v)
+    return out

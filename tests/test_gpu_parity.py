@@ -1,0 +1,297 @@
+"""GPU parity: every fused entry point against the CPU oracle, element by
+element, on seeded inputs (small and ragged shapes spanning several tiles,
+edge cases, strides, aliasing, misalignment, the unfused chains)."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_epilogue_tile_amd as ge
+import oracle
+import workloads
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, dev_inputs, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SQ = workloads.WORKLOADS["square_bf16"]
+
+
+def _generic(inp, act=None, **kw):
+    d = dev_inputs(inp)
+    return ge.gemm_epilogue(d["A"], d["B"], bias=d.get("bias"), C=d.get("C"), R=d.get("R"),
+                            alpha=inp["alpha"], beta=inp["beta"], act=act or inp["act"], **kw)
+
+
+def test_tiny_fp32_config():
+    w = workloads.WORKLOADS["tiny_fp32"]
+    inp = workloads.make_inputs(w)
+    out = _generic(inp)
+    assert out.dtype == torch.float32
+    assert_close(out, oracle.reference(inp), TOL_F32, "tiny_fp32")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (1, 8, 8), (7, 13, 5), (64, 64, 32), (65, 63, 33),
+                                   (128, 256, 512), (200, 136, 264), (257, 520, 96), (16, 1000, 776),
+                                   (300, 17, 1024), (513, 264, 136)])
+def test_bf16_gelu_bias_residual_ragged(M, N, K):
+    w = SQ.with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M * 7 + N)
+    assert_close(_generic(inp), oracle.reference(inp), TOL_BF16, f"bf16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "silu"])
+@pytest.mark.parametrize("flags", ["", "b", "c", "r", "bcr"])
+def test_bf16_every_activation_and_flag(act, flags):
+    import dataclasses
+    w = dataclasses.replace(SQ, M=192, N=264, K=320, alpha=0.75 if "c" in flags else 1.0,
+                            beta=-0.5 if "c" in flags else 0.0, act=act, bias="b" in flags,
+                            C="c" in flags, R="r" in flags)
+    inp = workloads.make_inputs(w, seed=5)
+    assert_close(_generic(inp), oracle.reference(inp), TOL_BF16, f"{act}/{flags}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (33, 71, 130), (256, 256, 256)])
+def test_fp32_operands_all_epilogue_terms(M, N, K):
+    w = workloads.WORKLOADS["tiny_fp32"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=2)
+    assert_close(_generic(inp), oracle.reference(inp), TOL_F32, f"fp32 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (100, 72, 200), (512, 512, 1024)])
+def test_nk_layout(M, N, K):
+    w = SQ.with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=4)
+    d = dev_inputs(inp)
+    Bt = to_dev(np.ascontiguousarray(inp["B"].T))
+    out = ge.gemm_epilogue(d["A"], Bt, bias=d["bias"], R=d["R"], act="gelu_tanh", b_layout="NK")
+    assert_close(out, oracle.reference(inp), TOL_BF16, "NK")
+
+
+def test_fp32_output_with_mixed_epilogue_types():
+    w = SQ.with_shape(M=130, N=200, K=256)
+    inp = workloads.make_inputs(w, seed=6)
+    d = dev_inputs(inp)
+    bias32 = d["bias"].float()
+    out = ge.gemm_epilogue(d["A"], d["B"], bias=bias32, R=d["R"], act="gelu_tanh", out_dtype=torch.float32)
+    # the product is bf16 x bf16 with fp32 accumulation: fp32-level agreement
+    assert_close(out, oracle.reference(inp), TOL_F32, "fp32 out")
+
+
+def test_strided_operands_and_output():
+    M, N, K = 96, 136, 200
+    w = SQ.with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=8)
+    d = dev_inputs(inp)
+    Abig = torch.zeros((M, K + 24), dtype=torch.bfloat16, device=DEV)
+    Abig[:, :K] = d["A"]
+    Bbig = torch.zeros((K, N + 8), dtype=torch.bfloat16, device=DEV)
+    Bbig[:, :N] = d["B"]
+    Rbig = torch.zeros((M, N + 16), dtype=torch.bfloat16, device=DEV)
+    Rbig[:, :N] = d["R"]
+    Dbig = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device=DEV)
+    ge.gemm_epilogue(Abig[:, :K], Bbig[:, :N], bias=d["bias"], R=Rbig[:, :N], act="gelu_tanh",
+                     out=Dbig[:, :N])
+    assert_close(Dbig[:, :N], oracle.reference(inp), TOL_BF16, "strided")
+    assert torch.all(Dbig[:, N:] == 7.0), "wrote outside the output view"
+
+
+def test_misaligned_pointers_take_the_general_kernel():
+    M, N, K = 70, 90, 101
+    w = SQ.with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=9)
+    d = dev_inputs(inp)
+    flatA = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+    flatA[1:] = d["A"].reshape(-1)
+    A = flatA[1:].view(M, K)
+    assert A.data_ptr() % 16 != 0
+    out = ge.gemm_epilogue(A, d["B"], bias=d["bias"], R=d["R"], act="gelu_tanh")
+    assert_close(out, oracle.reference(inp), TOL_BF16, "misaligned")
+
+
+def test_output_aliases_residual():
+    w = SQ.with_shape(M=128, N=128, K=256)
+    inp = workloads.make_inputs(w, seed=10)
+    d = dev_inputs(inp)
+    R = d["R"].clone()
+    ge.gemm_epilogue(d["A"], d["B"], bias=d["bias"], R=R, act="gelu_tanh", out=R)
+    assert_close(R, oracle.reference(inp), TOL_BF16, "D == R")
+
+
+def test_output_aliases_C():
+    w = workloads.WORKLOADS["tiny_fp32"]
+    inp = workloads.make_inputs(w)
+    d = dev_inputs(inp)
+    C = d["C"].clone()
+    ge.gemm_epilogue(d["A"], d["B"], C=C, bias=d["bias"], alpha=w.alpha, beta=w.beta, act="relu", out=C)
+    assert_close(C, oracle.reference(inp), TOL_F32, "D == C")
+
+
+def test_identity_B_returns_A():
+    K = 256
+    A = workloads.normal((96, K), 1.0, "bf16", wid=97, tid=0)
+    I = workloads.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    out = ge.gemm_epilogue(to_dev(A), to_dev(I))
+    assert np.array_equal(to_host(out), workloads.bf16_bits_to_f32(A).astype(np.float64))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = SQ.with_shape(M=512, N=384, K=640)
+    inp = workloads.make_inputs(w, seed=11)
+    a = _generic(inp)
+    b = _generic(inp)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# SwiGLU
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (16, 64, 64), (64, 128, 256), (130, 200, 264),
+                                   (256, 512, 512), (512, 1024, 640)])
+def test_swiglu_ragged(M, N, K):
+    w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N)
+    d = dev_inputs(inp)
+    out = ge.swiglu(d["X"], d["Wg"], d["Wu"])
+    assert_close(out, oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
+
+
+# --------------------------------------------------------------------------
+# W4A16
+# --------------------------------------------------------------------------
+
+def _w4(inp, **kw):
+    d = dev_inputs(inp)
+    return ge.w4_gemm(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"], bias=d.get("bias"),
+                      group=inp["group"], zero_point=inp["zero_point"], **kw)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 2, 128), (16, 256, 512), (16, 1000, 1024), (33, 264, 384),
+                                   (128, 512, 1024), (512, 512, 256), (200, 136, 640)])
+def test_w4_ragged(M, N, K):
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + K)
+    assert_close(_w4(inp), oracle.reference(inp), TOL_BF16, f"w4 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("group", [32, 64, 256])
+def test_w4_group_sizes(group):
+    import dataclasses
+    w = dataclasses.replace(workloads.WORKLOADS["w4a16_m16"], M=32, N=256, K=512, group=group)
+    inp = workloads.make_inputs(w, seed=group)
+    assert_close(_w4(inp), oracle.reference(inp), TOL_BF16, f"group {group}")
+
+
+def test_w4_lo_first_and_zero_point():
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=16, N=128, K=256)
+    inp = workloads.make_inputs(w, seed=3)
+    ref = oracle.w4_gemm(inp["X"], inp["Wq"], inp["scales"], w.N, "bf16", zero_point=5, lo_first=True,
+                         bias=inp["bias"])
+    d = dev_inputs(inp)
+    out = ge.w4_gemm(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"], bias=d["bias"],
+                     zero_point=5, lo_first=True)
+    assert_close(out, ref, TOL_BF16, "lo_first zp5")
+
+
+@pytest.mark.parametrize("M", [16, 512])
+def test_w4_unpack_bit_exact_with_one_hot_rows(M):
+    # X row m is one-hot at k_m and scales are 2^-6: D[m][n] = (code - 8) * 2^-6 exactly
+    K, N = 1024, 512
+    Wq = workloads.uniform_bytes((K, N // 2), wid=98, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = np.arange(M) * 37 % K
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), ks] = 1.0
+    Xb = workloads.f32_to_bf16_bits(X)
+    out = to_host(ge.w4_gemm(to_dev(Xb), torch.from_numpy(Wq).to(DEV), to_dev(scales)))
+    codes = oracle.w4_unpack(Wq, N).astype(np.int64)
+    want = (codes[ks] - 8) * 2.0 ** -6
+    assert np.array_equal(out, want)
+
+
+def test_w4_dequant_kernel_bit_exact():
+    K, N = 256, 384
+    Wq = workloads.uniform_bytes((K, N // 2), wid=99, tid=1)
+    scales = workloads.uniform((K // 128, N), 0.005, 0.02, "bf16", wid=99, tid=2)
+    W = ge.w4_dequant(torch.from_numpy(Wq).to(DEV), to_dev(scales))
+    exact = oracle.w4_dequant(Wq, scales, N)  # products of <= 12 significant bits: exact in fp32
+    want = workloads.f32_to_bf16_bits(exact.astype(np.float32))
+    got = W.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# unfused chains (measurement baselines)
+# --------------------------------------------------------------------------
+
+def _unfused_tol(ref_t, ref, extra_roundings):
+    # each extra bf16 rounding of an intermediate of size |t| adds <= 2^-9 |t|
+    return TOL_BF16 * (1 + np.abs(ref)) + extra_roundings * 2.0 ** -9 * (1 + np.abs(ref_t)) * 1.2
+
+
+def test_unfused_generic_matches_oracle():
+    w = SQ.with_shape(M=256, N=264, K=320)
+    inp = workloads.make_inputs(w, seed=12)
+    d = dev_inputs(inp)
+    out = to_host(ge.gemm_epilogue_unfused(d["A"], d["B"], bias=d["bias"], R=d["R"], act="gelu_tanh"))
+    ref = oracle.reference(inp)
+    t = oracle.gemm(inp["A"], inp["B"], "bf16", "bf16")
+    assert np.all(np.abs(out - ref) <= _unfused_tol(t, ref, 3))
+
+
+def test_unfused_fp32_alpha_beta_chain():
+    w = workloads.WORKLOADS["tiny_fp32"]
+    inp = workloads.make_inputs(w)
+    d = dev_inputs(inp)
+    out = ge.gemm_epilogue_unfused(d["A"], d["B"], C=d["C"], bias=d["bias"], alpha=w.alpha, beta=w.beta,
+                                   act="relu")
+    assert_close(out, oracle.reference(inp), TOL_F32, "unfused fp32")
+
+
+def test_unfused_swiglu_matches_oracle():
+    w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=128, N=256, K=512)
+    inp = workloads.make_inputs(w, seed=13)
+    d = dev_inputs(inp)
+    out = to_host(ge.swiglu_unfused(d["X"], d["Wg"], d["Wu"]))
+    ref = oracle.reference(inp)
+    assert np.all(np.abs(out - ref) <= TOL_BF16 * (1 + np.abs(ref)) + 5 * 2.0 ** -9 * np.abs(ref))
+
+
+def test_unfused_w4_matches_oracle():
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=16, N=512, K=1024)
+    inp = workloads.make_inputs(w, seed=14)
+    d = dev_inputs(inp)
+    out = to_host(ge.w4_gemm_unfused(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"],
+                                     bias=d["bias"]))
+    ref = oracle.reference(inp)
+    # the chain rounds every dequantised weight to bf16: random error per product <= 2^-9 |x w|
+    X = workloads.bf16_bits_to_f32(inp["X"]).astype(np.float64)
+    W = oracle.w4_dequant(inp["Wq"], inp["scales"], w.N)
+    spread = np.sqrt((X ** 2) @ (W ** 2))
+    tol = TOL_BF16 * (1 + np.abs(ref)) + 6 * 2.0 ** -9 * spread / np.sqrt(3) + 2 * 2.0 ** -9 * np.abs(ref)
+    assert np.all(np.abs(out - ref) <= tol)
+
+
+# --------------------------------------------------------------------------
+# fused residual add + RMSNorm
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N", [(1, 8), (4, 100), (16, 4096), (33, 8192), (7, 16384)])
+def test_add_rmsnorm(M, N):
+    a = workloads.normal((M, N), 1.0, "bf16", wid=100, tid=0, seed=N)
+    x = workloads.normal((M, N), 1.0, "bf16", wid=100, tid=1, seed=N)
+    wt = workloads.normal((N,), 1.0, "bf16", wid=100, tid=2, seed=N)
+    resid, out = ge.add_rmsnorm(to_dev(a), to_dev(x), to_dev(wt), eps=1e-6)
+    rr, ro = oracle.add_rmsnorm(a, x, wt, "bf16", eps=1e-6)
+    assert_close(resid, rr, TOL_BF16, "resid")
+    assert_close(out, ro, TOL_BF16, "normed")
+
+
+def test_add_rmsnorm_in_place_residual():
+    M, N = 8, 2048
+    a = workloads.normal((M, N), 1.0, "bf16", wid=101, tid=0)
+    x = workloads.normal((M, N), 1.0, "bf16", wid=101, tid=1)
+    wt = workloads.normal((N,), 1.0, "bf16", wid=101, tid=2)
+    ad = to_dev(a)
+    ge.add_rmsnorm(ad, to_dev(x), to_dev(wt), resid=ad)
+    rr, _ = oracle.add_rmsnorm(a, x, wt, "bf16")
+    assert_close(ad, rr, TOL_BF16, "resid in place")
