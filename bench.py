@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM + epilogue engine on one MI355X.
+
+One step = one fused call of the headline workload: the 4096^3 bf16 GEMM
+with bias, tanh-GELU and residual add in the epilogue (fp32 accumulation,
+bf16 output).  W untimed warmup steps, then exactly K timed steps bracketed by
+device synchronisation; HIP events around every launch on the launch stream
+give the kernel's average duration for the roofline object.
+
+Also reported (same JSON line): the deliberately unfused chain of the same
+workload, the other workloads (tiny fp32, SwiGLU dual GEMM, 16-row decode
+GEMM, W4A16 at M=16 and M=512) fused and unfused, and the CPU oracle timed
+on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--main-only]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20      # Infinity Cache: HBM-bound rows rotate past it
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--main-only", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size in rows (0 = auto)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
+def time_launches(fn_list, steps, warmup):
+    """Run fn_list[i % len] for warmup + steps iterations; return (total_ms, per_launch_ms list).
+
+    Every timed launch is bracketed by its own pair of HIP events on the
+    current stream (the one the library launches on)."""
+    import torch
+    s = torch.cuda.current_stream()
+    n = len(fn_list)
+    for i in range(warmup):
+        fn_list[i % n]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(s)
+    for i in range(steps):
+        ev[i][0].record(s)
+        fn_list[i % n]()
+        ev[i][1].record(s)
+    t_all1.record(s)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return t_all0.elapsed_time(t_all1), per
+
+
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+# --------------------------------------------------------------------------
+# workloads on the device
+# --------------------------------------------------------------------------
+
+def _dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _rotations(set_bytes, hbm_bound):
+    if not hbm_bound:
+        return 1
+    return max(1, min(8, -(-(2 * MALL_BYTES) // max(set_bytes, 1))))
+
+
+def build_calls(name, w, inp):
+    """Return (fused_calls, unfused_calls, meta) for one workload; each call list
+    rotates over enough copies of the weights to defeat the Infinity Cache
+    when the workload is HBM-bound."""
+    import torch
+    import gemm_epilogue_tile_amd as ge
+    from gemm_epilogue_tile_amd import accounting
+
+    acc = accounting.work(w)
+    d = {k: _dev(v) for k, v in inp.items() if hasattr(v, "dtype")}
+    hbm = acc["bound"] == "hbm"
+    wkey = {"generic": "B", "swiglu": None, "w4": "Wq"}[w.kind]
+    set_bytes = acc["bytes"]
+    nrot = _rotations(set_bytes, hbm)
+    sets = [d]
+    for _ in range(nrot - 1):
+        c = dict(d)
+        for k in (["Wg", "Wu"] if w.kind == "swiglu" else [wkey] + (["scales"] if w.kind == "w4" else [])):
+            c[k] = d[k].clone()
+        sets.append(c)
+    out_dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    outs = [torch.empty((w.M, w.N), dtype=out_dtype, device="cuda") for _ in sets]
+    fused, unfused = [], []
+    ws = None
+    for s, o in zip(sets, outs):
+        if w.kind == "generic":
+            kw = dict(bias=s.get("bias"), C=s.get("C"), R=s.get("R"), alpha=w.alpha, beta=w.beta, act=w.act,
+                      out=o)
+            fused.append(lambda s=s, kw=kw: ge.gemm_epilogue(s["A"], s["B"], **kw))
+            p = ge._generic_plan(s["A"], s["B"], ge.LAYOUT_KN, kw["C"], kw["bias"], kw["R"], o, w.alpha, w.beta,
+                                 w.act)
+            ws = ws if ws is not None else ge._workspace(p, "cuda")
+            unfused.append(lambda s=s, kw=kw: ge.gemm_epilogue_unfused(s["A"], s["B"], workspace=ws, **kw))
+            kernel = p.kernel
+        elif w.kind == "swiglu":
+            fused.append(lambda s=s, o=o: ge.swiglu(s["X"], s["Wg"], s["Wu"], out=o))
+            p = ge._swiglu_plan(s["X"], s["Wg"], o)
+            ws = ws if ws is not None else ge._workspace(p, "cuda")
+            unfused.append(lambda s=s, o=o: ge.swiglu_unfused(s["X"], s["Wg"], s["Wu"], out=o, workspace=ws))
+            kernel = p.kernel
+        else:
+            kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o)
+            fused.append(lambda s=s, kw=kw: ge.w4_gemm(s["X"], s["Wq"], s["scales"], **kw))
+            p = ge._w4_plan(s["X"], s["Wq"], s["scales"], None, s.get("bias"), None, o, 1.0, 0.0, "none",
+                            w.group, w.zero_point, False)
+            ws = ws if ws is not None else ge._workspace(p, "cuda")
+            unfused.append(lambda s=s, kw=kw: ge.w4_gemm_unfused(s["X"], s["Wq"], s["scales"], workspace=ws,
+                                                                 **kw))
+            kernel = p.kernel
+    return fused, unfused, dict(acc, kernel=kernel, rotations=nrot)
+
+
+def measure(name, steps, warmup):
+    import workloads
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    fused, unfused, meta = build_calls(name, w, inp)
+    tot_f, per_f = time_launches(fused, steps, warmup)
+    tot_u, per_u = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2))
+    fused_ms = tot_f / steps
+    kern_ms = sum(per_f) / len(per_f)
+    unfused_ms = tot_u / max(steps // 2, 5)
+    r = dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
+             flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"],
+             ms_per_step=fused_ms, kernel_ms_avg=kern_ms, kernel_ms_median=median(per_f),
+             unfused_ms=unfused_ms, unfused_bytes=meta["unfused_bytes"],
+             speedup_vs_unfused=unfused_ms / fused_ms)
+    r["tflops"] = meta["flops"] / (kern_ms * 1e-3) / 1e12
+    r["gbps"] = meta["bytes"] / (kern_ms * 1e-3) / 1e9
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    r["mfma_frac"] = r["tflops"] / peak
+    r["hbm_frac"] = r["gbps"] / PEAK_HBM_GBPS
+    return r
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+
+def cpu_baseline(rows_req):
+    import numpy as np
+    import oracle
+    import workloads
+    w = workloads.WORKLOADS["square_bf16"]
+    inp = workloads.make_inputs(w)
+    oracle.build()
+    # calibrate on 16 rows, then size the sample for about 15 s of CPU work
+    t0 = time.perf_counter()
+    oracle.reference(inp, rows=np.arange(16))
+    t16 = time.perf_counter() - t0
+    rows = rows_req or int(max(16, min(w.M, 16 * 15.0 / max(t16, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.reference(inp, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} of 4096 output rows of the 4096x4096x4096 bf16 GELU+bias+residual "
+                      f"workload ({rows}x4096x4096 fp64 products + epilogue passes), {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# traffic from the committed rocprofv3 counter summary
+# --------------------------------------------------------------------------
+
+def kernel_source_hash():
+    import glob
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gemm_epilogue_tile_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_name):
+    """HBM bytes per launch of the headline kernel from profiles/counters_square_bf16.json,
+    or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "counters_square_bf16.json")
+    try:
+        with open(path) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_hash") != kernel_source_hash() or c.get("kernel") != kernel_name:
+        return None
+    return c.get("bytes_per_launch")
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the engine is a single-GPU "
+              "kernel library and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gemm_epilogue_tile_amd as ge
+    ge.lib()  # fails loudly when the HIP library is missing
+
+    main_r = measure("square_bf16", a.steps, a.warmup)
+    others = {}
+    if not a.main_only:
+        for name in ["tiny_fp32", "swiglu_8b", "skinny_decode", "w4a16_m16", "w4a16_m512"]:
+            r = measure(name, max(a.steps // 2, 10), max(a.warmup // 2, 3))
+            torch.cuda.empty_cache()
+            others[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
+                            if k not in ("name",)}
+
+    achieved = main_r["tflops"]
+    traffic = traffic_for(main_r["kernel"])
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s (% bf16 MFMA peak); skinny/int4 HBM GB/s (% peak)",
+        "value": round(main_r["flops"] / (main_r["ms_per_step"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "square_bf16: D = gelu_tanh(A@B + bias) + R, M=N=K=4096, bf16 in/out, "
+                               "fp32 accumulation",
+                   "M": 4096, "N": 4096, "K": 4096, "kernel": main_r["kernel"],
+                   "pct_bf16_peak": round(100 * main_r["flops"] / (main_r["ms_per_step"] * 1e-3) / 1e12
+                                          / PEAK_BF16_TFLOPS, 2),
+                   "unfused_ms": round(main_r["unfused_ms"], 5),
+                   "speedup_vs_unfused": round(main_r["speedup_vs_unfused"], 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": main_r["kernel"], "kernel_ms_avg": round(main_r["kernel_ms_avg"], 5),
+                     "algorithmic_flops_per_launch": main_r["flops"]},
+    }
+    if others:
+        line["workloads"] = others
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
