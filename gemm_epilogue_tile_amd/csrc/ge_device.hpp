@@ -203,6 +203,17 @@ __device__ __forceinline__ void with_act(int32_t act, F &&f) {
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// In-place form for hot loops: the accumulator is tied to the destination in
+// AGPRs, so it never moves between registers from one step to the next (the
+// builtin form lets the register allocator rotate accumulators through
+// copies, which halves the MFMA issue rate of a lone wave).  The hazard
+// between the last MFMA and a later read of the accumulator is covered by
+// mfma_drain().
+__device__ __forceinline__ void mfma_bf16_acc(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states after the last in-place MFMA before its accumulators are read.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::); }
 // fp32 16x16x4: lane l supplies row / column l % 16 at reduction index l / 16.
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -1,26 +1,28 @@
 // ge_tile.hip -- large-tile bf16 MFMA kernel with the epilogue in the store path.
 //
-// One 256-thread workgroup (four waves) owns a BM x BN output tile and its
-// whole K reduction, so the epilogue needs nothing from other workgroups
+// One 256-thread workgroup (four waves, 2 x 2) owns a BM x BN output tile and
+// its whole K reduction, so the epilogue needs nothing from other workgroups
 // (page "kernel fusion" wiki: the activation is applied to each output tile
 // before it leaves the compute unit; page "Fusion and Epilogues": the ending
 // is applied to the accumulators on the way to their single store).
 //
-// Main loop, per 64-deep K step:
-//   global -> registers  128-bit buffer loads (out-of-range rows/chunks read 0)
-//                        of the NEXT step, issued before this step's MFMAs;
-//   registers -> LDS     A rows stored as-is; B ([K, N] row-major) is
-//                        transposed 8x8 in registers so that LDS holds B^T
-//                        with the reduction index contiguous, like A;
-//                        16-byte chunks XOR-swizzled (chunk ^ f(row),
-//                        f(row) = (row ^ row >> 3) & 7) so that both the
-//                        128-bit writes and the fragment reads are free of
-//                        bank conflicts;
-//   LDS -> MFMA          ds_read_b128 fragments, v_mfma_f32_16x16x32_bf16
-//                        with fp32 accumulators.  B is the first MFMA
-//                        operand, so each lane ends up holding four
-//                        consecutive output columns of one row.
-// Two LDS stages (double buffering), one barrier per K step.
+// Data path, per 32-deep K stage:
+//   memory -> LDS   buffer_load ... lds (16 bytes per lane, straight into LDS,
+//                   no registers); lanes past the end of a matrix read zeros.
+//                   Four LDS stages: the loads of stage s+4 are issued while
+//                   stage s is multiplied, three stages ahead of their use.
+//   A in LDS        [BM][32] bf16, 16-byte chunk c of row r at c ^ ((r>>1)&3):
+//                   conflict-free 128-bit fragment reads.
+//   B in LDS        KN layout: [32][BN] as stored in memory, 16-byte chunk c of
+//                   row k at c ^ ((k&3)<<1); fragments come from the gfx950
+//                   transposing read ds_read_b64_tr_b16, which turns four
+//                   rows x sixteen columns into one k-vector per column.
+//                   NK layout: [BN][32] like A.
+//   LDS -> MFMA     v_mfma_f32_16x16x32_bf16, fp32 accumulators (AGPRs).  B is
+//                   the first operand, so each lane ends up holding four
+//                   consecutive output columns of one row.  The fragments of
+//                   stage s+1 are read while the MFMAs of stage s run.
+//   One barrier per stage.
 //
 // Epilogue: alpha*acc + beta*C + bias -> activation -> + R (or silu(g)*u for
 // the dual product), 4 consecutive columns per lane, one rounding to the
@@ -37,23 +39,45 @@
 namespace ge {
 namespace {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define AS3 __attribute__((address_space(3)))
+
 constexpr int T_THREADS = 256;
-constexpr int T_BK = 64;
+constexpr int T_BK = 32;   // K depth of one stage
+constexpr int T_NS = 4;    // LDS stages
 constexpr int GROUP_M = 4;
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-
 constexpr uint32_t OOB = 0x80000000u;  // beyond any buffer this kernel builds (< 2^31 bytes)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (base, size in bytes, stride 0): lanes whose offset is
+// at or past `bytes` read zeros.  The fields are wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
+    const uint32_t n = bytes > 0 ? (uint32_t)bytes : 0u;
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from memory straight into LDS at lds + 16 * lane.  Issued
+// as inline assembly so the compiler does not track it: its LDS writes are
+// ordered by the explicit vmcnt waits and barriers of the main loop.  (The
+// tracked builtin makes the compiler wait for every outstanding direct load
+// before any LDS read, which would undo the prefetch.)
+__device__ __forceinline__ void load_lds16(const i32x4 &r, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// [rows][32] tiles (64-byte rows): 16-byte chunk c of row r lives at c ^ ((r >> 1) & 3)
+__device__ __forceinline__ int swz_a(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// [32][BN] tiles: 16-byte chunk c of row k lives at c ^ ((k & 3) << 1)
+template <int BN>
+__device__ __forceinline__ int swz_b(int k, int chunk) { return k * (BN * 2) + ((chunk ^ ((k & 3) << 1)) << 4); }
 
 // 4 consecutive elements as fp32 (8-byte bf16 or 16-byte fp32 access)
 __device__ __forceinline__ void load4(const void *p, int32_t type, int64_t off, float v[4]) {
@@ -110,35 +134,38 @@ __device__ __forceinline__ void epi4(const EpiArgs &e, float v[4], int64_t m, in
     store4(e.D, e.d_type, m * e.ldd + n, v);
 }
 
-// even / odd bf16 halves of two dwords, packed (x supplies the low half)
-__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xffff0000u); }
-
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 struct Cfg {
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
     static constexpr int MT = WTM / 16, NT = WTN / 16;   // 16x16 MFMA tiles per wave
     static constexpr int NB = DUAL ? 2 : 1;
-    static constexpr int A_BYTES = BM * T_BK * 2;
-    static constexpr int B_BYTES = BN * T_BK * 2;
-    static constexpr int STAGE = A_BYTES + NB * B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int A_LOADS = A_BYTES / 16 / T_THREADS;  // 16-byte loads per thread
-    static constexpr int B_LOADS = B_BYTES / 16 / T_THREADS;
-    static constexpr int KB_ROWS = BN / 32;                   // KN: k rows per thread block (8 or 4)
+    static constexpr int A_STAGE = BM * T_BK * 2;        // bytes of one stage
+    static constexpr int B_STAGE = BN * T_BK * 2;
+    static constexpr int B_BASE = T_NS * A_STAGE;        // LDS: all A stages, then all B stages
+    static constexpr int LDS = T_NS * (A_STAGE + NB * B_STAGE);
+    static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // 1 KB direct loads per wave per stage
+    static constexpr int B_INSTR = B_STAGE / 1024 / 4;
+    static constexpr int LOADS = A_INSTR + NB * B_INSTR; // per wave per stage
+    static constexpr int B_ROWS_PER_INSTR = 1024 / (BN * 2);  // KN: k rows one load instruction fills
     static_assert(WM * WN == 4, "four waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(BM % 32 == 0 && A_LOADS * T_THREADS * 16 == A_BYTES, "A loads");
-    static_assert(B_NK || BN == 256 || BN == 128, "KN transpose blocks");
+    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 4096 == A_STAGE && B_INSTR * 4096 == B_STAGE, "loads");
+    static_assert(B_NK || BN == 256 || BN == 128 || BN == 512, "KN row width");
+    static_assert((T_NS - 1) * A_STAGE + (MT - 1) * 1024 + 64 < 65536, "A fragment offsets fit the ds offset field");
+    static_assert((NB * T_NS - 1) * B_STAGE < 65536, "B stage offsets fit the ds offset field");
 };
 
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 __global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(1, 1)))
 void tile_kernel(Problem p) {
     using C = Cfg<BM, BN, WM, WN, DUAL, B_NK>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    // LDS: the T_NS A stages, then the T_NS B stages (then the B2 stages).  Every
+    // fragment address is a per-lane base plus a compile-time offset below 64 KiB.
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(AS3 void *)smem;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
     // ---- tile selection (XCD-aware) ----
@@ -153,97 +180,114 @@ void tile_kernel(Problem p) {
     const int tn = (t % per_group) / gsize;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // ---- per-thread load assignment ----
-    // A (and B^T when B_NK): thread -> 16-byte chunk tid%8 of rows tid/8 + 32 i
-    const int a_chunk = tid & 7, a_row = tid >> 3;
-    // B [K, N]: thread -> column block nb (8 columns) and KB_ROWS k rows starting kb * KB_ROWS
-    const int b_nb = tid % (BN / 8), b_kb = tid / (BN / 8);
+    // ---- direct-load lane offsets (constant across stages; k advances in the resource base) ----
+    // A / B^T stage: [rows][32] = 16 rows x 4 chunks per 1 KB instruction; lane -> row lane/4,
+    // LDS slot lane%4, which holds logical chunk (lane%4) ^ ((row>>1)&3).
+    const int arow_l = lane >> 2;
+    const int achunk = (lane & 3) ^ ((arow_l >> 1) & 3);
+    uint32_t a_off[C::A_INSTR];
+#pragma unroll
+    for (int q = 0; q < C::A_INSTR; ++q) {
+        const int row = (wave * C::A_INSTR + q) * 16 + arow_l;
+        a_off[q] = (uint32_t)(row * p.lda * 2) + achunk * 16;
+    }
+    // B stage: KN -> [32][BN], an instruction fills B_ROWS_PER_INSTR k rows; NK -> like A.
+    uint32_t b_off[C::B_INSTR];
+    if constexpr (B_NK) {
+#pragma unroll
+        for (int q = 0; q < C::B_INSTR; ++q) {
+            const int row = (wave * C::B_INSTR + q) * 16 + arow_l;
+            b_off[q] = (uint32_t)(row * p.ldb * 2) + achunk * 16;
+        }
+    } else {
+        constexpr int CPR = BN / 8;  // 16-byte chunks per k row
+        const int krow_l = lane / CPR;
+        const int slot = lane % CPR;
+#pragma unroll
+        for (int q = 0; q < C::B_INSTR; ++q) {
+            const int k = (wave * C::B_INSTR + q) * C::B_ROWS_PER_INSTR + krow_l;
+            const int chunk = slot ^ ((k & 3) << 1);
+            // columns past N read zeros (fixed per lane, so folded in once)
+            b_off[q] = n0 + chunk * 8 < p.N ? (uint32_t)(k * p.ldb * 2) + chunk * 16 : OOB;
+        }
+    }
 
-    const int nk = (p.K + T_BK - 1) / T_BK;
-    const int64_t lda_b = p.lda * 2, ldb_b = p.ldb * 2;
-
-    u32x4 ra[C::A_LOADS];
-    u32x4 rb[C::NB][C::B_LOADS];
-
-    auto load_stage = [&](int ks) {
-        const int k0 = ks * T_BK;
+    // issue the direct loads of stage s (K offset s * 32) into LDS buffer s % T_NS
+    auto load_stage = [&](int s) {
+        const int k0 = s * T_BK;
+        const int buf = s & (T_NS - 1);
         {
             const char *base = (const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2;
-            const int64_t rem = ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(base, rem > 0 ? (uint32_t)rem : 0u);
-            const bool kin = k0 + a_chunk * 8 < p.K;
+            const i32x4 r = make_rsrc(base, ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
+            const bool kin = k0 + achunk * 8 < p.K;
+            const uint32_t dst = lds0 + buf * C::A_STAGE + wave * C::A_INSTR * 1024;
 #pragma unroll
-            for (int i = 0; i < C::A_LOADS; ++i) {
-                const uint32_t off = (uint32_t)((a_row + 32 * i) * lda_b) + a_chunk * 16;
-                ra[i] = bload(r, kin ? off : OOB);
-            }
+            for (int q = 0; q < C::A_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? a_off[q] : OOB);
         }
 #pragma unroll
         for (int d = 0; d < C::NB; ++d) {
             const void *B = d == 0 ? p.B : p.B2;
+            const uint32_t dst = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE +
+                                 wave * C::B_INSTR * 1024;
             if constexpr (B_NK) {
                 const char *base = (const char *)B + ((int64_t)n0 * p.ldb + k0) * 2;
-                const int64_t rem = ((int64_t)(p.N - 1 - n0) * p.ldb + (p.K - k0)) * 2;
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(base, rem > 0 ? (uint32_t)rem : 0u);
-                const bool kin = k0 + a_chunk * 8 < p.K;
+                const i32x4 r = make_rsrc(base, ((int64_t)(p.N - 1 - n0) * p.ldb + (p.K - k0)) * 2);
+                const bool kin = k0 + achunk * 8 < p.K;
 #pragma unroll
-                for (int i = 0; i < C::B_LOADS; ++i) {
-                    const uint32_t off = (uint32_t)((a_row + 32 * i) * ldb_b) + a_chunk * 16;
-                    rb[d][i] = bload(r, kin ? off : OOB);
-                }
+                for (int q = 0; q < C::B_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? b_off[q] : OOB);
             } else {
                 const char *base = (const char *)B + ((int64_t)k0 * p.ldb + n0) * 2;
-                const int64_t rem = ((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2;
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(base, rem > 0 ? (uint32_t)rem : 0u);
-                const bool nin = n0 + b_nb * 8 < p.N;
+                const i32x4 r = make_rsrc(base, ((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
 #pragma unroll
-                for (int i = 0; i < C::B_LOADS; ++i) {
-                    const uint32_t off = (uint32_t)((b_kb * C::KB_ROWS + i) * ldb_b) + b_nb * 16;
-                    rb[d][i] = bload(r, nin ? off : OOB);
-                }
+                for (int q = 0; q < C::B_INSTR; ++q) load_lds16(r, dst + q * 1024, b_off[q]);
             }
         }
     };
 
-    auto store_stage = [&](int buf) {
-        char *sA = smem + buf * C::STAGE;
+    // ---- fragment addresses (stage 0; other stages add a compile-time offset) ----
+    const int frow = lane & 15, fgrp = lane >> 4;
+    // A fragment i: rows wm*WTM + 16 i + frow, chunk fgrp (k = 8 fgrp .. 8 fgrp + 7)
+    const int a_frag = swz_a(wm * C::WTM + frow, fgrp);
+    // B fragment j:
+    //   NK: like A;
+    //   KN: two transposing reads r = 0, 1: lane (g, jj) points at k = 8 g + 4 r + jj/4 and
+    //       columns 16 j + 4 (jj % 4) .. + 3; the read hands lane jj the k-vector of column jj.
+    int b_frag[C::NT][2];
 #pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) *(u32x4 *)(sA + swz(a_row + 32 * i, a_chunk)) = ra[i];
+    for (int j = 0; j < C::NT; ++j) {
+        if constexpr (B_NK) {
+            b_frag[j][0] = C::B_BASE + swz_a(wn * C::WTN + j * 16 + frow, fgrp);
+            b_frag[j][1] = 0;
+        } else {
 #pragma unroll
-        for (int d = 0; d < C::NB; ++d) {
-            char *sB = sA + C::A_BYTES + d * C::B_BYTES;
-            if constexpr (B_NK) {
-#pragma unroll
-                for (int i = 0; i < C::B_LOADS; ++i) *(u32x4 *)(sB + swz(a_row + 32 * i, a_chunk)) = rb[d][i];
-            } else if constexpr (C::KB_ROWS == 8) {
-                // 8 k rows x 8 columns -> for each column, its 8 k values (one 16-byte chunk)
-#pragma unroll
-                for (int dw = 0; dw < 4; ++dw) {
-                    u32x4 lo, hi;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        lo[q] = pack_lo(rb[d][2 * q][dw], rb[d][2 * q + 1][dw]);
-                        hi[q] = pack_hi(rb[d][2 * q][dw], rb[d][2 * q + 1][dw]);
-                    }
-                    *(u32x4 *)(sB + swz(b_nb * 8 + 2 * dw, b_kb)) = lo;
-                    *(u32x4 *)(sB + swz(b_nb * 8 + 2 * dw + 1, b_kb)) = hi;
-                }
-            } else {
-                // 4 k rows x 8 columns -> for each column, 4 k values (half a chunk)
-#pragma unroll
-                for (int dw = 0; dw < 4; ++dw) {
-                    u32x2 lo, hi;
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        lo[q] = pack_lo(rb[d][2 * q][dw], rb[d][2 * q + 1][dw]);
-                        hi[q] = pack_hi(rb[d][2 * q][dw], rb[d][2 * q + 1][dw]);
-                    }
-                    const int half = (b_kb & 1) * 8;
-                    *(u32x2 *)(sB + swz(b_nb * 8 + 2 * dw, b_kb >> 1) + half) = lo;
-                    *(u32x2 *)(sB + swz(b_nb * 8 + 2 * dw + 1, b_kb >> 1) + half) = hi;
-                }
+            for (int r = 0; r < 2; ++r) {
+                const int k = 8 * fgrp + 4 * r + (frow >> 2);
+                const int n = wn * C::WTN + j * 16 + 4 * (frow & 3);
+                b_frag[j][r] = C::B_BASE + swz_b<BN>(k, n >> 3) + ((n >> 2) & 1) * 8;
             }
         }
+    }
+
+    bf16x8 fa[2][C::MT], fb[2][C::NB][C::NT];
+    auto read_frags = [&](int buf, bf16x8 (&a)[C::MT], bf16x8 (&b)[C::NB][C::NT]) {
+        const AS3 char *s3 = (const AS3 char *)smem;
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+            a[i] = *(const AS3 bf16x8 *)(s3 + a_frag + buf * C::A_STAGE + i * 1024);
+#pragma unroll
+        for (int d = 0; d < C::NB; ++d)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) {
+                const int off = d * T_NS * C::B_STAGE + buf * C::B_STAGE;
+                if constexpr (B_NK) {
+                    b[d][j] = *(const AS3 bf16x8 *)(s3 + b_frag[j][0] + off);
+                } else {
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][0] + off));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][1] + off));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    b[d][j] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                }
+            }
     };
 
     f32x4 acc[C::NB][C::MT][C::NT];
@@ -254,41 +298,65 @@ void tile_kernel(Problem p) {
 #pragma unroll
             for (int j = 0; j < C::NT; ++j) acc[d][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int frow = lane & 15, fchunk = lane >> 4;
+    auto mfma_stage = [&](const bf16x8 (&a)[C::MT], const bf16x8 (&b)[C::NB][C::NT]) {
+#pragma unroll
+        for (int d = 0; d < C::NB; ++d)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j)
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i) mfma_bf16_acc(acc[d][i][j], b[d][j], a[i]);
+    };
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+    // LDS-only barrier: orders this workgroup's LDS traffic without waiting for prefetches
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
 
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) load_stage(ks + 1);
-        const char *sA = smem + buf * C::STAGE;
+    // wait until at most n of this wave's direct loads are outstanding
+    // (vmcnt counts them in issue order; lgkm / exp counters left at their maximum)
+#define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
+
+    const int nk = (p.K + T_BK - 1) / T_BK;
+    const int nsteps = (nk + T_NS - 1) / T_NS * T_NS;  // whole rounds of T_NS stages (extra stages read zeros)
+
+    // prologue: stages 0..3 in flight, stage 0 landed, its fragments read
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 af[C::MT];
+    for (int s = 0; s < T_NS; ++s) load_stage(s);
+    GE_WAIT_VM((T_NS - 1) * C::LOADS);
+    lds_barrier();
+    read_frags(0, fa[0], fb[0]);
+
+    for (int s0 = 0; s0 < nsteps; s0 += T_NS) {
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-                af[i] = *(const bf16x8 *)(sA + swz(wm * C::WTM + i * 16 + frow, kk * 4 + fchunk));
-#pragma unroll
-            for (int d = 0; d < C::NB; ++d) {
-                const char *sB = sA + C::A_BYTES + d * C::B_BYTES;
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j) {
-                    const bf16x8 bfr = *(const bf16x8 *)(sB + swz(wn * C::WTN + j * 16 + frow, kk * 4 + fchunk));
-#pragma unroll
-                    for (int i = 0; i < C::MT; ++i) acc[d][i][j] = mfma_bf16(bfr, af[i], acc[d][i][j]);
-                }
-            }
+        for (int b = 0; b < T_NS; ++b) {
+            const int s = s0 + b;
+            // stage s+1 landed (own loads), visible to all; every wave is done reading stage s
+            GE_WAIT_VM((T_NS - 2) * C::LOADS);
+            lds_barrier();
+            load_stage(s + T_NS);                                  // into buffer b, three stages ahead
+            read_frags((b + 1) & (T_NS - 1), fa[(b + 1) & 1], fb[(b + 1) & 1]);  // stage s+1
+            mfma_stage(fa[b & 1], fb[b & 1]);                     // stage s
         }
-        if (ks + 1 < nk) store_stage(buf ^ 1);
-        __syncthreads();
     }
+#undef GE_WAIT_VM
+    // drain the (zero-reading) prefetches past the end before the workgroup can exit,
+    // and let the last MFMAs retire before their accumulators are read
+    __builtin_amdgcn_s_waitcnt(0);
+    mfma_drain();
+    // tie every accumulator to the drain so no read of it is scheduled above the wait
+#pragma unroll
+    for (int d = 0; d < C::NB; ++d)
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) asm volatile("" : "+a"(acc[d][i][j]));
 
-    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 tile ----
+    // ---- epilogue: lane holds row m, columns n..n+3 of each 16x16 tile ----
     const EpiArgs &e = p.epi;
     const int mbase = m0 + wm * C::WTM + frow;
-    const int nbase = n0 + wn * C::WTN + fchunk * 4;
+    const int nbase = n0 + wn * C::WTN + fgrp * 4;
     if constexpr (DUAL) {
 #pragma unroll
         for (int i = 0; i < C::MT; ++i)
@@ -323,7 +391,7 @@ template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     using C = Cfg<BM, BN, WM, WN, DUAL, B_NK>;
     auto k = tile_kernel<BM, BN, WM, WN, DUAL, B_NK>;
-    static bool attr_set = false;  // benign race: every thread sets the same value
+    static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
         if (e != hipSuccess) return e;
@@ -365,8 +433,8 @@ bool tile_supported(const Problem &p) {
 }
 
 const char *tile_kernel_name(const Problem &p) {
-    if (p.mode == MODE_SWIGLU) return "tile_swiglu_256x128x64";
-    return p.b_layout == GE_LAYOUT_NK ? "tile_nk_256x256x64" : "tile_kn_256x256x64";
+    if (p.mode == MODE_SWIGLU) return "tile_swiglu_256x128x32";
+    return p.b_layout == GE_LAYOUT_NK ? "tile_nk_256x256x32" : "tile_kn_256x256x32";
 }
 
 hipError_t launch_tile(const Problem &p, int, hipStream_t s) {
