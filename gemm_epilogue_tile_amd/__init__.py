@@ -17,7 +17,8 @@ import threading
 __all__ = [
     "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
-    "F32", "BF16", "U4X2", "ACTS",
+    "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
+    "w4_prepack",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,12 +30,13 @@ F32, BF16, U4X2 = 0, 1, 2
 LAYOUT_KN, LAYOUT_NK = 0, 1
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
-FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST = 1, 2, 4, 8
+FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED = 1, 2, 4, 8, 16
 
 EXPORTS = [
     "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_run",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
-    "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "ge_add_rmsnorm_run",
+    "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack",
+    "ge_add_rmsnorm_run",
     "ge_status_string", "ge_last_error", "ge_version",
 ]
 
@@ -99,6 +101,8 @@ def lib():
             L.gemm_w4_run_unfused.restype = I
             L.gemm_w4_dequant_run.argtypes = [P] * 5
             L.gemm_w4_dequant_run.restype = I
+            L.gemm_w4_prepack.argtypes = [P] * 4
+            L.gemm_w4_prepack.restype = I
             L.ge_add_rmsnorm_run.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
             L.ge_add_rmsnorm_run.restype = I
             L.ge_status_string.argtypes = [I]
@@ -189,13 +193,32 @@ class Plan:
             self.handle = None
 
 
+class Prepared:
+    """A run call with every argument already converted: ``call()`` only crosses
+    the C ABI.  For timing loops and graph capture, where per-call Python work
+    would otherwise dominate small kernels.  The tensors passed at preparation
+    must stay alive (they are referenced here)."""
+
+    def __init__(self, fn, where, plan_obj, tensors, args):
+        self._fn = fn
+        self._where = where
+        self._plan = plan_obj
+        self._tensors = tensors
+        self._args = args
+
+    def __call__(self):
+        s = self._fn(*self._args)
+        if s != OK:
+            raise GemmEpiError(s, self._where, lib().ge_last_error().decode())
+
+
 _plan_cache: dict = {}
 
 
 def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=BF16, c_type=None,
          bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
          alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
-         lo_first=False) -> Plan:
+         lo_first=False, prepacked=False) -> Plan:
     """Build (or fetch from a cache) the plan of one problem descriptor."""
     d = Desc()
     lib().ge_desc_init(ctypes.byref(d))
@@ -211,7 +234,7 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
     d.alpha, d.beta = alpha, beta
     d.act = ACTS[act] if isinstance(act, str) else int(act)
     d.flags = ((FLAG_BIAS if bias else 0) | (FLAG_C if C else 0) | (FLAG_RESIDUAL if R else 0)
-               | (FLAG_NIBBLE_LO_FIRST if lo_first else 0))
+               | (FLAG_NIBBLE_LO_FIRST if lo_first else 0) | (FLAG_W4_PREPACKED if prepacked else 0))
     d.group_size, d.zero_point = group, zero_point
     key = (kind, bytes(d))
     p = _plan_cache.get(key)
@@ -298,33 +321,36 @@ def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, stream=None):
     return out
 
 
-def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first):
+def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked=False):
     M, K = X.shape
-    N = Wq.shape[1] * 2
+    N = scales.shape[1]
     return plan(KIND_W4, M, N, K, a_type=BF16, b_type=U4X2, d_type=_dtype_code(out),
                 c_type=_dtype_code(C) if C is not None else None,
                 bias_type=_dtype_code(bias) if bias is not None else None,
-                r_type=_dtype_code(R) if R is not None else None, lda=_ld(X), ldb=_ld(Wq),
+                r_type=_dtype_code(R) if R is not None else None, lda=_ld(X),
+                ldb=_ld(Wq) if Wq.dim() == 2 else 0,
                 ldc=_ld(C) if C is not None else 0, ldd=_ld(out), ldr=_ld(R) if R is not None else 0,
                 alpha=alpha, beta=beta, act=act, bias=bias is not None, C=C is not None and beta != 0.0,
-                R=R is not None, group=group, zero_point=zero_point, lo_first=lo_first)
+                R=R is not None, group=group, zero_point=zero_point, lo_first=lo_first, prepacked=prepacked)
 
 
 def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none", group=128,
-            zero_point=8, lo_first=False, out=None, out_dtype=None, stream=None):
-    """D = act(alpha * X @ deq(Wq, scales) + beta * C + bias) + R with int4 weights (fused)."""
-    out = _out(X.shape[0], Wq.shape[1] * 2, out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first)
+            zero_point=8, lo_first=False, prepacked=False, out=None, out_dtype=None, stream=None):
+    """D = act(alpha * X @ deq(Wq, scales) + beta * C + bias) + R with int4 weights (fused).
+
+    ``prepacked``: Wq came from ``w4_prepack`` (kernel-native layout, same byte count)."""
+    out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
     _check(lib().gemm_w4_run(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R),
                              _ptr(out), _stream(stream)), "gemm_w4_run")
     return out
 
 
 def w4_gemm_unfused(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
-                    group=128, zero_point=8, lo_first=False, out=None, out_dtype=None, workspace=None,
-                    stream=None):
-    out = _out(X.shape[0], Wq.shape[1] * 2, out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first)
+                    group=128, zero_point=8, lo_first=False, prepacked=False, out=None, out_dtype=None,
+                    workspace=None, stream=None):
+    out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
     ws = workspace if workspace is not None else _workspace(p, X.device)
     _check(lib().gemm_w4_run_unfused(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias),
                                      _ptr(R), _ptr(out), _ptr(ws), _stream(stream)), "gemm_w4_run_unfused")
@@ -355,3 +381,55 @@ def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
     _check(lib().ge_add_rmsnorm_run(M, N, _ptr(a), _ptr(x), _ptr(w), float(eps), _ptr(resid), _ptr(out),
                                     _stream(stream)), "ge_add_rmsnorm_run")
     return resid, out
+
+
+def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                          b_layout="KN", unfused=False, workspace=None, stream=None) -> Prepared:
+    """Bind one fused (or unfused) generic call to fixed tensors and stream."""
+    lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    ts = [A, B, C, bias, R, out]
+    if unfused:
+        ws = workspace if workspace is not None else _workspace(p, A.device)
+        ts.append(ws)
+        args = (p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out), _ptr(ws), _stream(stream))
+        return Prepared(lib().gemm_epi_run_unfused, "gemm_epi_run_unfused", p, ts, args)
+    args = (p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out), _stream(stream))
+    return Prepared(lib().gemm_epi_run, "gemm_epi_run", p, ts, args)
+
+
+def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, stream=None) -> Prepared:
+    p = _swiglu_plan(X, Wg, out)
+    ts = [X, Wg, Wu, out]
+    if unfused:
+        ws = workspace if workspace is not None else _workspace(p, X.device)
+        ts.append(ws)
+        args = (p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _ptr(ws), _stream(stream))
+        return Prepared(lib().gemm_swiglu_run_unfused, "gemm_swiglu_run_unfused", p, ts, args)
+    args = (p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream))
+    return Prepared(lib().gemm_swiglu_run, "gemm_swiglu_run", p, ts, args)
+
+
+def prepare_w4_gemm(X, Wq, scales, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                    group=128, zero_point=8, lo_first=False, prepacked=False, unfused=False, workspace=None,
+                    stream=None) -> Prepared:
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
+    ts = [X, Wq, scales, C, bias, R, out]
+    if unfused:
+        ws = workspace if workspace is not None else _workspace(p, X.device)
+        ts.append(ws)
+        args = (p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R), _ptr(out), _ptr(ws),
+                _stream(stream))
+        return Prepared(lib().gemm_w4_run_unfused, "gemm_w4_run_unfused", p, ts, args)
+    args = (p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R), _ptr(out), _stream(stream))
+    return Prepared(lib().gemm_w4_run, "gemm_w4_run", p, ts, args)
+
+
+def w4_prepack(Wq, *, lo_first=False, out=None, stream=None):
+    """Raw packed int4 weights [K, N/2] -> the fused kernels' layout (same bytes, one-time)."""
+    torch = _torch()
+    K, N = Wq.shape[0], Wq.shape[1] * 2
+    out = out if out is not None else torch.empty(K * N // 2, dtype=torch.uint8, device=Wq.device)
+    p = plan(KIND_W4, 1, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), lo_first=lo_first)
+    _check(lib().gemm_w4_prepack(p.handle, _ptr(Wq), _ptr(out), _stream(stream)), "gemm_w4_prepack")
+    return out

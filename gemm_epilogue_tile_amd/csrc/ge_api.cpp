@@ -92,6 +92,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     e.d_type = d.d_type;
     e.act = pl->kind == GE_KIND_SWIGLU ? GE_ACT_NONE : d.act;
     uint32_t f = 0;
+    p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
         if (d.flags & GE_FLAG_BIAS) f |= GE_FLAG_BIAS;
@@ -105,6 +106,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
 // preconditions (shape, alignment) hold, the general kernel otherwise.
 hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     if (skinny_supported(p)) return launch_skinny(p, pl->cu_count, s);
+    if (p.w4_packed) return hipErrorInvalidValue;  // only the specialised kernels read the packed layout
     if (tile_supported(p)) return launch_tile(p, pl->cu_count, s);
     return launch_general(p, s);
 }
@@ -203,7 +205,7 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         (int64_t)d.M * d.K >= (1ll << 31))
         return fail(GE_ERR_UNSUPPORTED, "matrix with 2^31 or more elements");
     if (d.act < GE_ACT_NONE || d.act > GE_ACT_SILU) return fail(GE_ERR_INVALID_ARG, "unknown activation %d", d.act);
-    if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST))
+    if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED))
         return fail(GE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags);
     if (d.b_layout != GE_LAYOUT_KN && d.b_layout != GE_LAYOUT_NK)
         return fail(GE_ERR_INVALID_ARG, "unknown b_layout %d", d.b_layout);
@@ -233,7 +235,8 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     if (kind == GE_KIND_GENERIC) {
         if (d.a_type != d.b_type || !is_float_type(d.a_type))
             return fail(GE_ERR_UNSUPPORTED, "generic kind needs a_type == b_type in {F32, BF16}");
-        if (d.flags & GE_FLAG_NIBBLE_LO_FIRST) return fail(GE_ERR_INVALID_ARG, "nibble flag on a dense product");
+        if (d.flags & (GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED))
+            return fail(GE_ERR_INVALID_ARG, "int4 flag on a dense product");
         pl.ldb = d.ldb ? d.ldb : (d.b_layout == GE_LAYOUT_KN ? d.N : d.K);
         if (pl.ldb < (d.b_layout == GE_LAYOUT_KN ? d.N : d.K)) return fail(GE_ERR_INVALID_ARG, "ldb too small");
     } else if (kind == GE_KIND_SWIGLU) {
@@ -256,6 +259,11 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         pl.ldb = d.ldb ? d.ldb : d.N / 2;
         if (pl.ldb < d.N / 2) return fail(GE_ERR_INVALID_ARG, "ldb < N/2 bytes");
         pl.ld_s = d.N;
+        if (d.flags & GE_FLAG_W4_PREPACKED) {
+            if (d.M > 16 || d.N % 16 || d.K % 128 || pl.group > 128)
+                return fail(GE_ERR_UNSUPPORTED,
+                            "prepacked int4 weights need M <= 16, N %% 16 == 0, K %% 128 == 0, group <= 128");
+        }
     }
 
     // device
@@ -342,6 +350,8 @@ ge_status gemm_w4_run(const ge_plan *pl, const void *X, const uint8_t *Wq, const
     if (overlaps(scales, nS, D, nD)) return fail(GE_ERR_INVALID_ARG, "D overlaps the scales");
     if ((st = check_device(pl))) return st;
     const Problem p = make_problem(pl, X, Wq, nullptr, scales, C, bias, R, D);
+    if (p.w4_packed && !skinny_supported(p))
+        return fail(GE_ERR_ALIGN, "prepacked int4 path needs 16-byte aligned X and Wq and lda %% 8 == 0");
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_w4_run launch");
 }
 
@@ -485,6 +495,7 @@ ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *W
                               const void *C, const void *bias, const void *R, void *D, void *ws, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw int4 weights");
     if (!X || !Wq || !scales) return fail(GE_ERR_INVALID_ARG, "X, Wq or scales is NULL");
     ge_status st = check_epi_ptrs(pl, C, bias, R, D);
     if (st || (st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
@@ -512,6 +523,7 @@ ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *W
 ge_status gemm_w4_dequant_run(const ge_plan *pl, const uint8_t *Wq, const void *scales, void *W, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw int4 weights");
     if (!Wq || !scales || !W) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     ge_status st;
     if ((st = check_device(pl))) return st;
@@ -519,6 +531,22 @@ ge_status gemm_w4_dequant_run(const ge_plan *pl, const uint8_t *Wq, const void *
     return hip_status(launch_w4_dequant(d.K, d.N, Wq, pl->ldb, scales, pl->ld_s, pl->group, d.zero_point,
                                         (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, (hipStream_t)stream),
                       "gemm_w4_dequant_run");
+}
+
+ge_status gemm_w4_prepack(const ge_plan *pl, const uint8_t *Wq, uint8_t *Wp, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
+    if (!Wq || !Wp) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    const ge_desc &d = pl->d;
+    if (d.N % 16 || d.K % 128) return fail(GE_ERR_UNSUPPORTED, "prepack needs N %% 16 == 0 and K %% 128 == 0");
+    if ((uintptr_t)Wp & 15) return fail(GE_ERR_ALIGN, "Wp must be 16-byte aligned");
+    const size_t nq = (size_t)(d.K - 1) * pl->ldb + d.N / 2, np = (size_t)d.K * d.N / 2;
+    if (overlaps(Wq, nq, Wp, np)) return fail(GE_ERR_INVALID_ARG, "Wp overlaps Wq");
+    ge_status st;
+    if ((st = check_device(pl))) return st;
+    return hip_status(launch_w4_prepack(d.K, d.N, Wq, pl->ldb, (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, Wp,
+                                        (hipStream_t)stream),
+                      "gemm_w4_prepack");
 }
 
 ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,

@@ -23,6 +23,7 @@ struct Problem {
     const void *scales; // w4 scales (bf16)
     int64_t lda, ldb, ld_s;
     int32_t group, zero_point, lo_first;
+    int32_t w4_packed;  // B holds int4 weights in the prepacked layout
     EpiArgs epi;
 };
 
@@ -34,6 +35,10 @@ hipError_t launch_general(const Problem &p, hipStream_t s);
 bool tile_supported(const Problem &p);
 hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s);
 const char *tile_kernel_name(const Problem &p);
+
+// One-time conversion of raw [K, N/2] int4 weights to the prepacked layout.
+hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,
+                             hipStream_t s);
 
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);

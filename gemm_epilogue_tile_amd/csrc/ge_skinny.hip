@@ -1,8 +1,360 @@
-// ge_skinny.hip -- small-M weight-streaming kernel (placeholder until written).
+// ge_skinny.hip -- small-M (decode) kernels: the weights are streamed from
+// memory once, straight into MFMA fragments, and the epilogue runs after an
+// in-LDS reduction over the workgroup's K split.
+//
+// Shape of the work: M <= 32 rows of activations X (tiny, re-read from L2),
+// weights W with K x N entries (the whole cost: the kernel is bound by HBM).
+// One workgroup (8 waves) owns a block of output columns and the full K; its
+// waves split K, so every weight byte is read once and there is no
+// cross-workgroup reduction.
+//
+// bf16 weights, KN layout ([K, N], N contiguous):
+//   a lane loads 8 rows x 16 bytes (8 columns) of one 32-deep K block and
+//   transposes them in registers into 8 B fragments (8 k values of one
+//   column each); MFMA tile t then covers the columns 8 c + t of the lanes'
+//   16 column chunks c, i.e. a wave covers 128 consecutive columns.
+//
+// int4 weights, prepacked (see gemm_w4_prepack): for each 16-column tile and
+// each 128-row K group, lane l's 16 bytes are its four B fragments (one per
+// 32-deep block), 8 codes per dword.  A code c becomes the bf16 value 128 + c
+// by OR-ing it into the mantissa of 0x4300; a second MFMA against a constant
+// -(128 + z) fragment folds in -(128 + z) * sum(x), so the product is
+// sum x * (c - z) for zero point z (8 on the pages),
+// exact in fp32 before the per-group scale (page "Fusion Thinking",
+// Pattern 3: zero point 8, per-group scales, dequantisation in registers).
+
 #include "ge_launch.hpp"
 
 namespace ge {
-bool skinny_supported(const Problem &) { return false; }
-hipError_t launch_skinny(const Problem &, int, hipStream_t) { return hipErrorInvalidValue; }
-const char *skinny_kernel_name(const Problem &) { return "none"; }
+namespace {
+
+constexpr int S_WAVES = 8;
+constexpr int S_THREADS = 64 * S_WAVES;
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint32_t n = bytes > 0 ? (bytes >= (1ll << 31) ? 0x7fffffffu : (uint32_t)bytes) : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// even / odd bf16 halves of two dwords (x supplies the low half)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) { return (x & 0xffffu) | (y << 16); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return (x >> 16) | (y & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// shared tail: reduce the waves' partial tiles in LDS, then the epilogue on
+// 8-column row chunks (16-byte accesses where aligned)
+// ---------------------------------------------------------------------------
+
+// red: [S_WAVES][MR][NC] fp32 partials in LDS (MR rows, NC columns)
+template <int MR, int NC>
+__device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *red, int n0) {
+    const EpiArgs &e = p.epi;
+    constexpr int CH = NC / 8;  // 8-column chunks per row
+    const bool vec_ok = ((p.N & 7) == 0) && (((uintptr_t)e.D & 15) == 0) && ((e.ldd & 7) == 0) &&
+                        (!(e.flags & GE_FLAG_RESIDUAL) || ((((uintptr_t)e.R & 15) == 0) && ((e.ldr & 7) == 0))) &&
+                        (!(e.flags & GE_FLAG_C) || ((((uintptr_t)e.C & 15) == 0) && ((e.ldc & 7) == 0))) &&
+                        (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) &&
+                        e.d_type == GE_BF16 && (!(e.flags & GE_FLAG_RESIDUAL) || e.r_type == GE_BF16) &&
+                        (!(e.flags & GE_FLAG_C) || e.c_type == GE_BF16) &&
+                        (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
+    with_act(e.act, [&](auto ACTC) {
+        constexpr int ACT = decltype(ACTC)::value;
+        for (int item = threadIdx.x; item < MR * CH; item += S_THREADS) {
+            const int r = item / CH, c = item % CH;
+            const int m = r, n = n0 + c * 8;
+            if (m >= p.M || n >= p.N) continue;
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = 0.0f;
+#pragma unroll
+            for (int w = 0; w < S_WAVES; ++w) {
+                const f32x4 a = *(const f32x4 *)&red[(w * MR + r) * NC + c * 8];
+                const f32x4 b = *(const f32x4 *)&red[(w * MR + r) * NC + c * 8 + 4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    v[q] += a[q];
+                    v[4 + q] += b[q];
+                }
+            }
+            if (vec_ok && n + 8 <= p.N) {
+                epi_row8<ACT>(e, v, m, n);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (n + q < p.N) store_elem(e.D, e.d_type, (int64_t)m * e.ldd + n + q, epi_scalar<ACT>(e, v[q], m, n + q));
+            }
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// bf16 weights
+// ---------------------------------------------------------------------------
+
+// MT: 16-row tiles of X (M <= 16 MT).  WG: 128 columns, 8 waves splitting K.
+template <int MT>
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
+    constexpr int NC = 128;
+    constexpr int MR = 16 * MT;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int n0 = blockIdx.x * NC;
+
+    const int nkb = (p.K + 31) / 32;
+    const int per = (nkb + S_WAVES - 1) / S_WAVES;
+    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+
+    // W: lane -> rows 8 g + r of the block, 16-byte column chunk i (columns n0 + 8 i ..)
+    const bool nin = n0 + 8 * i < p.N;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, ((int64_t)(p.K - 1) * p.ldb + p.N) * 2);
+    // X: lane -> row mt*16 + i, k = 8 g .. 8 g + 7 of the block
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_w = [&](int kb, u32x4 (&w)[8]) {
+        const int k = kb * 32 + 8 * g;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t off = (uint32_t)(((int64_t)(k + r) * p.ldb + n0 + 8 * i) * 2);
+            w[r] = bload16(rw, (nin && k + r < p.K) ? off : OOB);
+        }
+    };
+    auto load_x = [&](int kb, bf16x8 (&x)[MT]) {
+        const int k = kb * 32 + 8 * g;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + i;
+            const uint32_t off = (uint32_t)(((int64_t)m * p.lda + k) * 2);
+            x[mt] = __builtin_bit_cast(bf16x8, bload16(rx, (m < p.M && k < p.K) ? off : OOB));
+        }
+    };
+
+    u32x4 wcur[8], wnxt[8];
+    if (kb0 < kb1) load_w(kb0, wcur);
+    for (int kb = kb0; kb < kb1; ++kb) {
+        if (kb + 1 < kb1) load_w(kb + 1, wnxt);
+        bf16x8 x[MT];
+        load_x(kb, x);
+        // 8 rows x 8 columns -> 8 fragments (k-vectors of one column each)
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+            u32x4 lo, hi;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                lo[q] = pack_lo(wcur[2 * q][dw], wcur[2 * q + 1][dw]);
+                hi[q] = pack_hi(wcur[2 * q][dw], wcur[2 * q + 1][dw]);
+            }
+            const bf16x8 f0 = __builtin_bit_cast(bf16x8, lo), f1 = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[mt][2 * dw] = mfma_bf16(x[mt], f0, acc[mt][2 * dw]);
+                acc[mt][2 * dw + 1] = mfma_bf16(x[mt], f1, acc[mt][2 * dw + 1]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) wcur[r] = wnxt[r];
+    }
+
+    // partial tile -> LDS: lane (g, i) holds rows mt*16 + 4 g + e, columns 8 i + t
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            float *dst = &red[(wave * MR + mt * 16 + 4 * g + e4) * NC + 8 * i];
+            *(f32x4 *)dst = f32x4{acc[mt][0][e4], acc[mt][1][e4], acc[mt][2][e4], acc[mt][3][e4]};
+            *(f32x4 *)(dst + 4) = f32x4{acc[mt][4][e4], acc[mt][5][e4], acc[mt][6][e4], acc[mt][7][e4]};
+        }
+    __syncthreads();
+    reduce_epilogue<MR, NC>(p, red, n0);
+}
+
+// ---------------------------------------------------------------------------
+// int4 weights, prepacked
+// ---------------------------------------------------------------------------
+
+// Four bf16 pairs (a B fragment, k in order) from one packed dword of 8 codes:
+// pair q = (code at nibble q, code at nibble q + 4), each as bf16 128 + code.
+__device__ __forceinline__ bf16x8 unpack_w4(uint32_t w) {
+    u32x4 f;
+    f[0] = (w & 0x000f000fu) | 0x43004300u;
+    f[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
+    f[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
+    f[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, f);
+}
+
+// NTW 16-column tiles per workgroup; 8 waves split the 128-row packing
+// groups.  SPG: 32-deep blocks per scale group (group size / 32 = 1, 2 or 4).
+template <int NTW, int SPG>
+__global__ __launch_bounds__(S_THREADS) void skinny_w4_kernel(Problem p) {
+    constexpr int NC = 16 * NTW;
+    constexpr int MR = 16;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int nt0 = blockIdx.x * NTW;  // first 16-column tile
+    const int n0 = nt0 * 16;
+    const int ntiles = p.N / 16;
+    const int ngroups = p.K / 128;
+    const int per = (ngroups + S_WAVES - 1) / S_WAVES;
+    const int g0 = wave * per, g1 = min(ngroups, g0 + per);
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+    const uint16_t *sc = (const uint16_t *)p.scales;
+
+    // constant fragment -(128 + zero point) (exact in bf16) for the zero-point correction
+    const uint32_t nz = f32_to_bf16(-(128.0f + (float)p.zero_point));
+    const uint32_t nz2 = nz | (nz << 16);
+    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
+
+    f32x4 tot[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int gi = g0; gi < g1; ++gi) {
+        u32x4 w[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const bool tin = nt0 + t < ntiles;
+            w[t] = bload16(rw, tin ? (uint32_t)((((int64_t)(nt0 + t) * ngroups + gi) * 64 + lane) * 16) : OOB);
+        }
+        bf16x8 x[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int k = gi * 128 + kb * 32 + 8 * g;
+            const uint32_t off = (uint32_t)(((int64_t)i * p.lda + k) * 2);
+            x[kb] = __builtin_bit_cast(bf16x8, bload16(rx, i < p.M ? off : OOB));
+        }
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const int n = n0 + 16 * t + i;
+#pragma unroll
+            for (int sg = 0; sg < 4; sg += SPG) {
+                // sum over one scale group of x * (c - 8), then scale
+                f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = sg; kb < sg + SPG; ++kb) {
+                    u = mfma_bf16(x[kb], unpack_w4(w[t][kb]), u);
+                    u = mfma_bf16(x[kb], neg136, u);
+                }
+                const int grp = (gi * 128 + sg * 32) / (SPG * 32);
+                const float s = n < p.N ? bf16_to_f32(sc[(int64_t)grp * p.ld_s + n]) : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tot[t][q] = fmaf(s, u[q], tot[t][q]);
+            }
+        }
+    }
+
+    // partial tile -> LDS: lane (g, i) holds rows 4 g + e, column 16 t + i
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) red[(wave * MR + 4 * g + e4) * NC + 16 * t + i] = tot[t][e4];
+    __syncthreads();
+    reduce_epilogue<MR, NC>(p, red, n0);
+}
+
+// Prepack: raw [K, N/2] bytes (two codes per byte, order per lo_first) ->
+// per (16-column tile, 128-row group): 64 lanes x 16 bytes; lane l, dword kb
+// holds the 8 codes of column 16 tile + l % 16 at k = 128 group + 32 kb +
+// 8 (l / 16) + j: code j at bits 4 (j/2) + 16 (j%2) ... i.e. even j in the
+// low half, odd j in the high half, so that unpack_w4 yields k in order.
+__global__ __launch_bounds__(256) void w4_prepack_kernel(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
+                                                         int32_t lo_first, uint8_t *Wp) {
+    const int64_t ngroups = K / 128, ntiles = N / 16;
+    const int64_t total = ntiles * ngroups * 64;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(u & 63);
+        const int64_t tg = u >> 6;
+        const int64_t gi = tg % ngroups, nt = tg / ngroups;
+        const int64_t n = nt * 16 + (l & 15);
+        const bool even = (n & 1) == 0;
+        const bool hi = even != (lo_first != 0);
+        u32x4 out;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            uint32_t d = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t k = gi * 128 + kb * 32 + 8 * (l >> 4) + j;
+                const uint8_t b = Wq[k * ldq + (n >> 1)];
+                const uint32_t code = hi ? (b >> 4) : (b & 0xF);
+                d |= code << (4 * (j >> 1) + 16 * (j & 1));
+            }
+            out[kb] = d;
+        }
+        *(u32x4 *)(Wp + ((nt * ngroups + gi) * 64 + l) * 16) = out;
+    }
+}
+
+bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
+
+}  // namespace
+
+hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,
+                             hipStream_t s) {
+    const int64_t total = (int64_t)(N / 16) * (K / 128) * 64;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(w4_prepack_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s, K, N, Wq, ldq,
+                       lo_first, Wp);
+    return hipGetLastError();
+}
+
+bool skinny_supported(const Problem &p) {
+    if (p.ab_type != GE_BF16 || p.M > 32) return false;
+    if (p.mode == MODE_SWIGLU) return false;
+    if (!al16(p.A) || (p.lda & 7) || (p.K & 7)) return false;
+    if (p.mode == MODE_W4) {
+        return p.w4_packed && p.M <= 16 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
+               (p.group == 32 || p.group == 64 || p.group == 128);
+    }
+    if (p.b_layout != GE_LAYOUT_KN || !al16(p.B) || (p.ldb & 7) || (p.N & 7)) return false;
+    const int64_t b_bytes = ((int64_t)(p.K - 1) * p.ldb + p.N) * 2;
+    const int64_t a_bytes = ((int64_t)(p.M - 1) * p.lda + p.K) * 2;
+    return b_bytes < (1ll << 31) && a_bytes < (1ll << 31);
+}
+
+const char *skinny_kernel_name(const Problem &p) {
+    if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
+    return p.M <= 16 ? "skinny_bf16_m16_128col" : "skinny_bf16_m32_128col";
+}
+
+hipError_t launch_skinny(const Problem &p, int, hipStream_t s) {
+    if (!skinny_supported(p)) return hipErrorInvalidValue;
+    if (p.mode == MODE_W4) {
+        constexpr int NTW = 2;
+        const int blocks = (p.N / 16 + NTW - 1) / NTW;
+        if (p.group == 32)
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 1>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+        else if (p.group == 64)
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+        return hipGetLastError();
+    }
+    const int blocks = (p.N + 127) / 128;
+    if (p.M <= 16)
+        hipLaunchKernelGGL(skinny_bf16_kernel<1>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL(skinny_bf16_kernel<2>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace ge

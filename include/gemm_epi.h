@@ -90,6 +90,7 @@ typedef int32_t ge_status;
 #define GE_FLAG_C 2u               /* add beta * C (ignored when beta == 0) */
 #define GE_FLAG_RESIDUAL 4u        /* add R after the activation */
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
+#define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
 
 /*
  * Problem descriptor.  Unused fields must be zero.  dtype fields take
@@ -103,6 +104,9 @@ typedef int32_t ge_status;
  *   W4       a = BF16, b = U4X2, scale_type = BF16, d/bias/c/r in {F32, BF16},
  *            K % group == 0, N even, group in {32, 64, 128, 256},
  *            zero_point in [0, 15].
+ *            With GE_FLAG_W4_PREPACKED additionally: M <= 16, N % 16 == 0,
+ *            K % 128 == 0, group in {32, 64, 128}; the unfused entry points
+ *            take raw weights and reject such plans.
  */
 typedef struct ge_desc {
     int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */
@@ -163,6 +167,19 @@ GE_API ge_status gemm_swiglu_run(const ge_plan *plan, const void *X, const void 
  */
 GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *Wq, const void *scales,
                       const void *C, const void *bias, const void *R, void *D, void *stream);
+
+/*
+ * One-time weight conversion for the fused W4 kernels (the way a weight
+ * loader would store quantised weights): reads raw packed int4 weights Wq
+ * [K, N/2] (nibble order from the plan's flags, row stride = the plan's ldb)
+ * and writes the same K*N/2 bytes to Wp in the kernel-native layout: for each
+ * 16-column tile (outer) and 128-row K group (inner), 64 lanes x 16 bytes,
+ * lane l holding the codes of column 16*tile + l%16 for k = 128*group +
+ * 32*b + 8*(l/16) + j (b = 0..3, one dword per b; code j at bit
+ * 4*(j/2) + 16*(j%2)).  Needs N % 16 == 0, K % 128 == 0 and a 16-byte aligned
+ * Wp that does not overlap Wq.  Asynchronous on the stream.
+ */
+GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t *Wp, void *stream);
 
 /*
  * Deliberately unfused chains, for measurement only: the plain GEMM writes

@@ -26,8 +26,10 @@ def _run(name, inp):
                                 alpha=inp["alpha"], beta=inp["beta"], act=inp["act"])
     if inp["kind"] == "swiglu":
         return ge.swiglu(d["X"], d["Wg"], d["Wu"])
-    return ge.w4_gemm(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"], bias=d.get("bias"),
-                      group=inp["group"], zero_point=inp["zero_point"])
+    Wq = torch.from_numpy(inp["Wq"]).to(DEV)
+    packed = inp["M"] <= 16  # the decode shape takes the prepacked streaming kernel, as in the benchmark
+    return ge.w4_gemm(d["X"], ge.w4_prepack(Wq) if packed else Wq, d["scales"], bias=d.get("bias"),
+                      group=inp["group"], zero_point=inp["zero_point"], prepacked=packed)
 
 
 @pytest.mark.parametrize("name,nrows", [("tiny_fp32", 64), ("square_bf16", 24), ("swiglu_8b", 8),

@@ -295,3 +295,80 @@ def test_add_rmsnorm_in_place_residual():
     ge.add_rmsnorm(ad, to_dev(x), to_dev(wt), resid=ad)
     rr, _ = oracle.add_rmsnorm(a, x, wt, "bf16")
     assert_close(ad, rr, TOL_BF16, "resid in place")
+
+
+# --------------------------------------------------------------------------
+# small-M weight-streaming kernels
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (3, 136, 96), (16, 1000, 1000), (16, 2048, 4096),
+                                   (17, 264, 520), (32, 512, 2048), (5, 4104, 136)])
+def test_skinny_bf16_bias_residual_gelu(M, N, K):
+    w = workloads.WORKLOADS["skinny_decode"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N + K)
+    d = dev_inputs(inp)
+    out = ge.gemm_epilogue(d["A"], d["B"], bias=d["bias"], R=d["R"], act="gelu_tanh")
+    ref = oracle.gemm_epilogue(inp["A"], inp["B"], "bf16", bias=inp["bias"], act="gelu_tanh", R=inp["R"])
+    assert_close(out, ref, TOL_BF16, f"skinny {M}x{N}x{K}")
+
+
+def test_skinny_plan_picks_the_streaming_kernel():
+    p = ge.plan(ge.KIND_GENERIC, 16, 28672, 8192, bias=True, R=True)
+    assert p.kernel.startswith("skinny_bf16")
+    q = ge.plan(ge.KIND_W4, 16, 8192, 8192, b_type=ge.U4X2, bias=True, prepacked=True)
+    assert q.kernel.startswith("skinny_w4")
+
+
+def _w4_packed(inp, **kw):
+    d = dev_inputs(inp)
+    Wq = torch.from_numpy(inp["Wq"]).to(DEV)
+    Wp = ge.w4_prepack(Wq, lo_first=kw.get("lo_first", False))
+    return ge.w4_gemm(d["X"], Wp, d["scales"], bias=d.get("bias"), group=inp["group"],
+                      zero_point=inp["zero_point"], prepacked=True, **kw)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (7, 256, 512), (16, 1008, 1024), (16, 4096, 2048)])
+def test_w4_prepacked_ragged(M, N, K):
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N)
+    assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_w4_prepacked_group_sizes(group):
+    import dataclasses
+    w = dataclasses.replace(workloads.WORKLOADS["w4a16_m16"], M=16, N=256, K=512, group=group)
+    inp = workloads.make_inputs(w, seed=group)
+    assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed group {group}")
+
+
+def test_w4_prepacked_lo_first_and_zero_point():
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=16, N=128, K=256)
+    inp = workloads.make_inputs(w, seed=7)
+    ref = oracle.w4_gemm(inp["X"], inp["Wq"], inp["scales"], w.N, "bf16", zero_point=3, lo_first=True,
+                         bias=inp["bias"])
+    inp["zero_point"] = 3
+    assert_close(_w4_packed(inp, lo_first=True), ref, TOL_BF16, "packed lo_first zp3")
+
+
+def test_w4_prepacked_one_hot_rows_bit_exact():
+    K, N, M = 1024, 512, 16
+    Wq = workloads.uniform_bytes((K, N // 2), wid=102, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = np.arange(M) * 61 % K
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), ks] = 1.0
+    Wp = ge.w4_prepack(torch.from_numpy(Wq).to(DEV))
+    out = to_host(ge.w4_gemm(to_dev(workloads.f32_to_bf16_bits(X)), Wp, to_dev(scales), prepacked=True))
+    codes = oracle.w4_unpack(Wq, N).astype(np.int64)
+    assert np.array_equal(out, (codes[ks] - 8) * 2.0 ** -6)
+
+
+def test_w4_prepacked_rejected_by_unfused_chain():
+    p = ge.plan(ge.KIND_W4, 16, 256, 256, b_type=ge.U4X2, prepacked=True)
+    n = ge.ctypes.c_size_t()
+    assert ge.lib().gemm_epi_unfused_workspace_bytes(p.handle, ge.ctypes.byref(n)) == 0
+    with pytest.raises(ge.GemmEpiError):
+        X = torch.zeros((16, 256), dtype=torch.bfloat16, device=DEV)
+        ge.w4_gemm_unfused(X, torch.zeros(256 * 128, dtype=torch.uint8, device=DEV),
+                           torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV), prepacked=True)
