@@ -134,12 +134,9 @@ def build_calls(name, w, inp):
             u = ge.prepare_swiglu(s["X"], s["Wg"], s["Wu"], out=o, unfused=True, workspace=ws)
         else:
             kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o)
-            if w.M <= 16:
-                # fused decode path: weights converted once to the kernel layout (a load-time step)
-                wp = ge.w4_prepack(s["Wq"])
-                f = ge.prepare_w4_gemm(s["X"], wp, s["scales"], prepacked=True, **kw)
-            else:
-                f = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], **kw)
+            # fused path: weights converted once to the kernel layout (a load-time step)
+            wp = ge.w4_prepack(s["Wq"])
+            f = ge.prepare_w4_gemm(s["X"], wp, s["scales"], prepacked=True, **kw)
             u = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], unfused=True, workspace=ws, **kw)
         ws = u._tensors[-1]  # one workspace shared by every rotation
         fused.append(f)

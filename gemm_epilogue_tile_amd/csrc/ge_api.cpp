@@ -106,8 +106,8 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
 // preconditions (shape, alignment) hold, the general kernel otherwise.
 hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     if (skinny_supported(p)) return launch_skinny(p, pl->cu_count, s);
-    if (p.w4_packed) return hipErrorInvalidValue;  // only the specialised kernels read the packed layout
     if (tile_supported(p)) return launch_tile(p, pl->cu_count, s);
+    if (p.w4_packed) return hipErrorInvalidValue;  // only the specialised kernels read the packed layout
     return launch_general(p, s);
 }
 
@@ -260,9 +260,10 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         if (pl.ldb < d.N / 2) return fail(GE_ERR_INVALID_ARG, "ldb < N/2 bytes");
         pl.ld_s = d.N;
         if (d.flags & GE_FLAG_W4_PREPACKED) {
-            if (d.M > 16 || d.N % 16 || d.K % 128 || pl.group > 128)
+            if (d.N % (d.M <= 16 ? 16 : 128) || d.K % 128 || pl.group > 128 || (d.M > 16 && pl.group != 128))
                 return fail(GE_ERR_UNSUPPORTED,
-                            "prepacked int4 weights need M <= 16, N %% 16 == 0, K %% 128 == 0, group <= 128");
+                            "prepacked int4 weights need K %% 128 == 0 and either M <= 16, N %% 16 == 0, group <= 128 "
+                            "or N %% 128 == 0, group == 128");
         }
     }
 
@@ -350,8 +351,9 @@ ge_status gemm_w4_run(const ge_plan *pl, const void *X, const uint8_t *Wq, const
     if (overlaps(scales, nS, D, nD)) return fail(GE_ERR_INVALID_ARG, "D overlaps the scales");
     if ((st = check_device(pl))) return st;
     const Problem p = make_problem(pl, X, Wq, nullptr, scales, C, bias, R, D);
-    if (p.w4_packed && !skinny_supported(p))
-        return fail(GE_ERR_ALIGN, "prepacked int4 path needs 16-byte aligned X and Wq and lda %% 8 == 0");
+    if (p.w4_packed && !skinny_supported(p) && !tile_supported(p))
+        return fail(GE_ERR_ALIGN, "prepacked int4 path needs 16-byte aligned X, Wq, D, bias, C, R and "
+                                  "leading dimensions that are multiples of 8");
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_w4_run launch");
 }
 

@@ -104,9 +104,12 @@ typedef int32_t ge_status;
  *   W4       a = BF16, b = U4X2, scale_type = BF16, d/bias/c/r in {F32, BF16},
  *            K % group == 0, N even, group in {32, 64, 128, 256},
  *            zero_point in [0, 15].
- *            With GE_FLAG_W4_PREPACKED additionally: M <= 16, N % 16 == 0,
- *            K % 128 == 0, group in {32, 64, 128}; the unfused entry points
- *            take raw weights and reject such plans.
+ *            With GE_FLAG_W4_PREPACKED additionally: K % 128 == 0, and
+ *            either M <= 16, N % 16 == 0, group in {32, 64, 128}, or N % 128
+ *            == 0, group == 128; the unfused entry points take raw weights
+ *            and reject such plans.
+ *            For M > 16 the product runs in fp16 (exact for |x| and
+ *            |8 * scale| inside the fp16 normal range, i.e. below 65504).
  */
 typedef struct ge_desc {
     int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */

@@ -342,8 +342,9 @@ def test_w4_prepacked_group_sizes(group):
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed group {group}")
 
 
-def test_w4_prepacked_lo_first_and_zero_point():
-    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=16, N=128, K=256)
+@pytest.mark.parametrize("M", [16, 96])
+def test_w4_prepacked_lo_first_and_zero_point(M):
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=128, K=256)
     inp = workloads.make_inputs(w, seed=7)
     ref = oracle.w4_gemm(inp["X"], inp["Wq"], inp["scales"], w.N, "bf16", zero_point=3, lo_first=True,
                          bias=inp["bias"])
@@ -372,3 +373,30 @@ def test_w4_prepacked_rejected_by_unfused_chain():
         X = torch.zeros((16, 256), dtype=torch.bfloat16, device=DEV)
         ge.w4_gemm_unfused(X, torch.zeros(256 * 128, dtype=torch.uint8, device=DEV),
                            torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV), prepacked=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 128, 128), (128, 256, 512), (200, 384, 1024), (512, 512, 2048)])
+def test_w4_prepacked_tile_path(M, N, K):
+    w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N)
+    p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
+    assert p.kernel.startswith("tile_w4")
+    assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
+
+
+def test_w4_prepacked_tile_one_hot_rows_bit_exact():
+    K, N, M = 512, 256, 160
+    Wq = workloads.uniform_bytes((K, N // 2), wid=103, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = np.arange(M) * 37 % K
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), ks] = 1.0
+    Wp = ge.w4_prepack(torch.from_numpy(Wq).to(DEV))
+    out = to_host(ge.w4_gemm(to_dev(workloads.f32_to_bf16_bits(X)), Wp, to_dev(scales), prepacked=True))
+    codes = oracle.w4_unpack(Wq, N).astype(np.int64)
+    assert np.array_equal(out, (codes[ks] - 8) * 2.0 ** -6)
+
+
+def test_w4_prepacked_tile_needs_group_128():
+    with pytest.raises(ge.GemmEpiError):
+        ge.plan(ge.KIND_W4, 64, 256, 512, b_type=ge.U4X2, group=64, prepacked=True)
