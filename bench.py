@@ -13,7 +13,7 @@ GEMM, W4A16 at M=16 and M=512) fused and unfused, and the CPU oracle timed
 on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--main-only]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -41,7 +41,22 @@ def _args():
     ap.add_argument("--main-only", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size in rows (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB fp32 device copy (y = -x) 5 times, the reference "
+                         "for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """Five launches of torch.neg over 2^28 fp32 values: each reads and writes exactly 1 GiB."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4,
+                      "launches": 5}), flush=True)
 
 
 # --------------------------------------------------------------------------
@@ -231,6 +246,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     import gemm_epilogue_tile_amd as ge
     ge.lib()  # fails loudly when the HIP library is missing
 
