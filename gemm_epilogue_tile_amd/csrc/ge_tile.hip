@@ -397,7 +397,8 @@ void tile_kernel(Problem p) {
 // The products are then exact in fp32 and no per-group rescaling of the
 // accumulators is needed.  Dequant per pair of codes: the codes are OR-ed into
 // the mantissa of fp16 1024 (giving 1024 + c), then a packed subtract of
-// 1024 + z and a packed multiply by s, both exact.  Scale groups of 128 rows.
+// 1024 + z and a packed multiply by s (exact for z = 8).  Scale groups of
+// 128 rows.
 //
 // A: direct loads into 4 LDS stages of 32 k, as in the bf16 tile kernel.
 // B: per 128-row group, the workgroup's 8 column tiles (8 KB, lane-major as
@@ -425,8 +426,9 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(const bf16x8 &x) {
 }
 
 // one packed dword of 8 codes -> fp16 B fragment (k in order), (c - z) * s:
-// (1024 + c) - (1024 + z) is an exact small integer, and its product with s
-// has at most 11 significant bits, so both packed steps are exact.
+// (1024 + c) - (1024 + z) is an exact small integer; with z = 8 it has at
+// most 3 significant bits, so its product with a bf16 scale (8 bits) is exact
+// in fp16.  Other zero points may round the product by half an fp16 ulp.
 __device__ __forceinline__ f16x8 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) {
     u32x4 r;
 #pragma unroll

@@ -108,8 +108,10 @@ typedef int32_t ge_status;
  *            either M <= 16, N % 16 == 0, group in {32, 64, 128}, or N % 128
  *            == 0, group == 128; the unfused entry points take raw weights
  *            and reject such plans.
- *            For M > 16 the product runs in fp16 (exact for |x| and
- *            |8 * scale| inside the fp16 normal range, i.e. below 65504).
+ *            For M > 16 the product runs in fp16: x and the dequantised
+ *            weights must lie in the fp16 range (|v| < 65504; below 2^-14
+ *            they lose precision).  The weights are exact for zero_point 8;
+ *            other zero points round them by at most 2^-12 relative.
  */
 typedef struct ge_desc {
     int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */
