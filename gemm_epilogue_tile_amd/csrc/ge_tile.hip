@@ -134,6 +134,127 @@ __device__ __forceinline__ void epi4(const EpiArgs &e, float v[4], int64_t m, in
     store4(e.D, e.d_type, m * e.ldd + n, v);
 }
 
+// Two horizontally adjacent 16x16 accumulator tiles x (columns c..c+15) and
+// y (c+16..c+31), in the fragment layout where lane row g = lane / 16 holds
+// columns 4g..4g+3 of its tile, become eight consecutive columns per lane:
+// lane row g ends up with columns c + 8g .. c + 8g + 7.  Two lane-row swaps
+// per register do it: rows 2,3 of x trade with rows 0,1 of y, then odd rows
+// of the first result trade with even rows of the second.
+// Inline assembly: each swap rewrites both of its registers, as the operands
+// state (this compiler's two-result swap builtins keep only the first).  The
+// inputs are taken through whole-vector bit casts (a bit cast of one vector
+// element reads element 0 with this compiler).
+__device__ __forceinline__ void pair_to_cols8(const f32x4 &x, const f32x4 &y, float v[8]) {
+    const u32x4 xu = __builtin_bit_cast(u32x4, x), yu = __builtin_bit_cast(u32x4, y);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t a = xu[e], b = yu[e];
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1"
+                     : "+v"(a), "+v"(b));
+        v[e] = __builtin_bit_cast(float, a);
+        v[4 + e] = __builtin_bit_cast(float, b);
+    }
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float v[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16lo(w[i]);
+        v[2 * i + 1] = bf16hi(w[i]);
+    }
+}
+
+// Buffer resource over a row-major bf16 matrix: rows below M, reads past it
+// give zeros and writes past it are dropped.  Absent operands get an empty
+// range, so their loads return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mat_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Epilogue of a wave's MT x NT grid of 16x16 tiles when D, C, R and bias are
+// all bf16 (the common case): each lane owns 8 consecutive columns per tile
+// pair, so every access is 16 bytes.  The C and R rows of tile row i + 2 are
+// fetched while tile row i is computed; the code has no branches, so the
+// memory waits count exactly (absent terms read zeros from empty buffers and
+// add nothing).  mrow: this lane's row in tile row 0; ncol: its first column
+// in tile pair 0 (tile pairs are 32 columns apart).  Needs the byte extent of
+// C, R and D below 2^31 (checked by the caller).
+template <int ACT, int MT, int NT>
+__device__ __forceinline__ void epilogue_bf16(const EpiArgs &e, f32x4 (&acc)[MT][NT], int M, int N, int mrow,
+                                              int ncol) {
+    constexpr int NP = NT / 2, DEPTH = 2;
+    static_assert(NT % 2 == 0, "tile pairs");
+    const bool has_c = e.flags & GE_FLAG_C, has_b = e.flags & GE_FLAG_BIAS, has_r = e.flags & GE_FLAG_RESIDUAL;
+    const auto rc = mat_rsrc(e.C, has_c ? ((int64_t)(M - 1) * e.ldc + N) * 2 : 0);
+    const auto rr = mat_rsrc(e.R, has_r ? ((int64_t)(M - 1) * e.ldr + N) * 2 : 0);
+    const auto rb = mat_rsrc(e.bias, has_b ? (int64_t)N * 2 : 0);
+    const auto rd = mat_rsrc(e.D, ((int64_t)(M - 1) * e.ldd + N) * 2);
+    const float beta = has_c ? e.beta : 0.0f;
+    u32x4 bias[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+        const int n = ncol + 32 * q;
+        bias[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, n < N ? n * 2 : (int)OOB, 0, 0);
+    }
+    u32x4 cv[DEPTH + 1][NP], rv[DEPTH + 1][NP];
+    auto fetch = [&](int i, u32x4 (&c)[NP], u32x4 (&r)[NP]) {
+        const int m = mrow + 16 * i;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int n = ncol + 32 * q;
+            const bool ok = m < M && n < N;
+            c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? (int)(((int64_t)m * e.ldc + n) * 2) : (int)OOB, 0, 0);
+            r[q] = __builtin_amdgcn_raw_buffer_load_b128(rr, ok ? (int)(((int64_t)m * e.ldr + n) * 2) : (int)OOB, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < DEPTH && i < MT; ++i) fetch(i, cv[i], rv[i]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        if (i + DEPTH < MT) fetch(i + DEPTH, cv[(i + DEPTH) % (DEPTH + 1)], rv[(i + DEPTH) % (DEPTH + 1)]);
+        const int m = mrow + 16 * i;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int n = ncol + 32 * q;
+            float v[8], c[8], b[8], r[8];
+            pair_to_cols8(acc[i][2 * q], acc[i][2 * q + 1], v);
+            bf16x8_to_f32(cv[i % (DEPTH + 1)][q], c);
+            bf16x8_to_f32(bias[q], b);
+            bf16x8_to_f32(rv[i % (DEPTH + 1)][q], r);
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = activate<ACT>(fmaf(beta, c[t], e.alpha * v[t]) + b[t]) + r[t];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
+            const bool ok = m < M && n < N;
+            __builtin_amdgcn_raw_buffer_store_b128(w, rd, ok ? (int)(((int64_t)m * e.ldd + n) * 2) : (int)OOB, 0, 0);
+        }
+    }
+}
+
+// SwiGLU store: silu(g) * u over the same 16-byte column groups.
+template <int MT, int NT>
+__device__ __forceinline__ void epilogue_swiglu(const EpiArgs &e, f32x4 (&g)[MT][NT], f32x4 (&u)[MT][NT], int M,
+                                                int N, int mrow, int ncol) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int m = mrow + 16 * i;
+#pragma unroll
+        for (int q = 0; q < NT / 2; ++q) {
+            const int n = ncol + 32 * q;
+            float vg[8], vu[8];
+            pair_to_cols8(g[i][2 * q], g[i][2 * q + 1], vg);
+            pair_to_cols8(u[i][2 * q], u[i][2 * q + 1], vu);
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                w[t] = pack_bf16x2(activate<GE_ACT_SILU>(vg[2 * t]) * vu[2 * t],
+                                   activate<GE_ACT_SILU>(vg[2 * t + 1]) * vu[2 * t + 1]);
+            if (m < M && n < N) *(u32x4 *)((uint16_t *)e.D + (int64_t)m * e.ldd + n) = w;
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 struct Cfg {
     static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -212,36 +333,50 @@ void tile_kernel(Problem p) {
         }
     }
 
-    // issue the direct loads of stage s (K offset s * 32) into LDS buffer s % T_NS
-    auto load_stage = [&](int s) {
+    // direct loads of one stage (K offset s * 32) into LDS buffer s % T_NS: the buffer
+    // resources are formed once per stage, the C::LOADS instructions issued one at a time
+    struct StageLoads {
+        i32x4 ra, rb[C::NB];
+        uint32_t adst, bdst[C::NB];
+        bool akin, bkin;
+    };
+    auto stage_loads = [&](int s) {
+        StageLoads L;
         const int k0 = s * T_BK;
         const int buf = s & (T_NS - 1);
-        {
-            const char *base = (const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2;
-            const i32x4 r = make_rsrc(base, ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
-            const bool kin = k0 + achunk * 8 < p.K;
-            const uint32_t dst = lds0 + buf * C::A_STAGE + wave * C::A_INSTR * 1024;
-#pragma unroll
-            for (int q = 0; q < C::A_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? a_off[q] : OOB);
-        }
+        L.ra = make_rsrc((const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2,
+                         ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
+        L.akin = k0 + achunk * 8 < p.K;
+        L.bkin = L.akin;
+        L.adst = lds0 + buf * C::A_STAGE + wave * C::A_INSTR * 1024;
 #pragma unroll
         for (int d = 0; d < C::NB; ++d) {
             const void *B = d == 0 ? p.B : p.B2;
-            const uint32_t dst = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE +
-                                 wave * C::B_INSTR * 1024;
-            if constexpr (B_NK) {
-                const char *base = (const char *)B + ((int64_t)n0 * p.ldb + k0) * 2;
-                const i32x4 r = make_rsrc(base, ((int64_t)(p.N - 1 - n0) * p.ldb + (p.K - k0)) * 2);
-                const bool kin = k0 + achunk * 8 < p.K;
-#pragma unroll
-                for (int q = 0; q < C::B_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? b_off[q] : OOB);
-            } else {
-                const char *base = (const char *)B + ((int64_t)k0 * p.ldb + n0) * 2;
-                const i32x4 r = make_rsrc(base, ((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
-#pragma unroll
-                for (int q = 0; q < C::B_INSTR; ++q) load_lds16(r, dst + q * 1024, b_off[q]);
-            }
+            L.bdst[d] = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE + wave * C::B_INSTR * 1024;
+            if constexpr (B_NK)
+                L.rb[d] = make_rsrc((const char *)B + ((int64_t)n0 * p.ldb + k0) * 2,
+                                    ((int64_t)(p.N - 1 - n0) * p.ldb + (p.K - k0)) * 2);
+            else
+                L.rb[d] = make_rsrc((const char *)B + ((int64_t)k0 * p.ldb + n0) * 2,
+                                    ((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
         }
+        return L;
+    };
+    auto issue_load = [&](const StageLoads &L, int q) {  // q < C::LOADS, compile-time after unrolling
+        if (q < C::A_INSTR) {
+            load_lds16(L.ra, L.adst + q * 1024, L.akin ? a_off[q] : OOB);
+        } else {
+            const int d = (q - C::A_INSTR) / C::B_INSTR, qq = (q - C::A_INSTR) % C::B_INSTR;
+            if constexpr (B_NK)
+                load_lds16(L.rb[d], L.bdst[d] + qq * 1024, L.bkin ? b_off[qq] : OOB);
+            else
+                load_lds16(L.rb[d], L.bdst[d] + qq * 1024, b_off[qq]);
+        }
+    };
+    auto load_stage = [&](int s) {
+        const StageLoads L = stage_loads(s);
+#pragma unroll
+        for (int q = 0; q < C::LOADS; ++q) issue_load(L, q);
     };
 
     // ---- fragment addresses (stage 0; other stages add a compile-time offset) ----
@@ -269,25 +404,35 @@ void tile_kernel(Problem p) {
     }
 
     bf16x8 fa[2][C::MT], fb[2][C::NB][C::NT];
+    const AS3 char *s3 = (const AS3 char *)smem;
+    auto read_a = [&](int buf, int i, bf16x8 &a) {
+        a = *(const AS3 bf16x8 *)(s3 + a_frag + buf * C::A_STAGE + i * 1024);
+    };
+    auto read_b = [&](int buf, int d, int j, bf16x8 &b) {
+        const int off = d * T_NS * C::B_STAGE + buf * C::B_STAGE;
+        if constexpr (B_NK) {
+            b = *(const AS3 bf16x8 *)(s3 + b_frag[j][0] + off);
+        } else {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][0] + off));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][1] + off));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            b = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+        }
+    };
+    // fragment read r of a stage: A fragments and B fragments alternate
+    constexpr int NRD = C::MT + C::NB * C::NT;
+    auto read_frag = [&](int buf, int r, bf16x8 (&a)[C::MT], bf16x8 (&b)[C::NB][C::NT]) {
+        const int ai = r / 2, bi = r / 2;  // interleave while both remain
+        if (r % 2 == 0 && ai < C::MT) {
+            read_a(buf, ai, a[ai]);
+        } else if (r % 2 == 1 && bi < C::NB * C::NT) {
+            read_b(buf, bi / C::NT, bi % C::NT, b[bi / C::NT][bi % C::NT]);
+        }
+    };
+    static_assert(C::MT == C::NB * C::NT, "fragment reads alternate A and B");
     auto read_frags = [&](int buf, bf16x8 (&a)[C::MT], bf16x8 (&b)[C::NB][C::NT]) {
-        const AS3 char *s3 = (const AS3 char *)smem;
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
-            a[i] = *(const AS3 bf16x8 *)(s3 + a_frag + buf * C::A_STAGE + i * 1024);
-#pragma unroll
-        for (int d = 0; d < C::NB; ++d)
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j) {
-                const int off = d * T_NS * C::B_STAGE + buf * C::B_STAGE;
-                if constexpr (B_NK) {
-                    b[d][j] = *(const AS3 bf16x8 *)(s3 + b_frag[j][0] + off);
-                } else {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][0] + off));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][1] + off));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    b[d][j] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                }
-            }
+        for (int r = 0; r < 2 * C::MT; ++r) read_frag(buf, r, a, b);
     };
 
     f32x4 acc[C::NB][C::MT][C::NT];
@@ -298,21 +443,35 @@ void tile_kernel(Problem p) {
 #pragma unroll
             for (int j = 0; j < C::NT; ++j) acc[d][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mfma_stage = [&](const bf16x8 (&a)[C::MT], const bf16x8 (&b)[C::NB][C::NT]) {
-#pragma unroll
-        for (int d = 0; d < C::NB; ++d)
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j)
-#pragma unroll
-                for (int i = 0; i < C::MT; ++i) mfma_bf16_acc(acc[d][i][j], b[d][j], a[i]);
-    };
-
     // LDS-only barrier: orders this workgroup's LDS traffic without waiting for prefetches
     auto lds_barrier = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
+
+    // One stage: the 64 MFMAs of stage s, with the next stage's fragment reads and the direct
+    // loads of stage s + T_NS spread between them so the matrix pipe never waits on a burst of
+    // LDS or memory instructions.  Reads go after MFMAs 0, 3, 6, ..., loads after 1, 4, 7, ...;
+    // an empty asm with a memory clobber pins each one to its slot.
+    constexpr int NMF = C::NB * C::NT * C::MT;
+    static_assert(3 * (2 * C::MT - 1) < NMF && 3 * (C::LOADS - 1) + 1 < NMF, "side-op slots");
+    auto stage = [&](const StageLoads &L, int nbuf, const bf16x8 (&a)[C::MT], const bf16x8 (&b)[C::NB][C::NT],
+                     bf16x8 (&na)[C::MT], bf16x8 (&nb)[C::NB][C::NT]) {
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            const int d = q / (C::NT * C::MT), j = (q / C::MT) % C::NT, i = q % C::MT;
+            mfma_bf16_acc(acc[d][i][j], b[d][j], a[i]);
+            if (q % 3 == 0 && q / 3 < 2 * C::MT) {
+                asm volatile("" ::: "memory");
+                read_frag(nbuf, q / 3, na, nb);
+                asm volatile("" ::: "memory");
+            } else if (q % 3 == 1 && q / 3 < C::LOADS) {
+                issue_load(L, q / 3);
+            }
+        }
+    };
+    (void)NRD;
 
     // wait until at most n of this wave's direct loads are outstanding
     // (vmcnt counts them in issue order; lgkm / exp counters left at their maximum)
@@ -335,9 +494,8 @@ void tile_kernel(Problem p) {
             // stage s+1 landed (own loads), visible to all; every wave is done reading stage s
             GE_WAIT_VM((T_NS - 2) * C::LOADS);
             lds_barrier();
-            load_stage(s + T_NS);                                  // into buffer b, three stages ahead
-            read_frags((b + 1) & (T_NS - 1), fa[(b + 1) & 1], fb[(b + 1) & 1]);  // stage s+1
-            mfma_stage(fa[b & 1], fb[b & 1]);                     // stage s
+            const StageLoads L = stage_loads(s + T_NS);  // into buffer b, three stages ahead
+            stage(L, (b + 1) & (T_NS - 1), fa[b & 1], fb[b & 1], fa[(b + 1) & 1], fb[(b + 1) & 1]);
         }
     }
 #undef GE_WAIT_VM
@@ -357,19 +515,19 @@ void tile_kernel(Problem p) {
     const EpiArgs &e = p.epi;
     const int mbase = m0 + wm * C::WTM + frow;
     const int nbase = n0 + wn * C::WTN + fgrp * 4;
+    auto small = [&](int64_t ld) { return ((int64_t)(p.M + 15) * ld + p.N) * 2 < (1ll << 31); };
+    const bool all_bf16 = e.d_type == GE_BF16 && small(e.ldd) &&
+                          (!(e.flags & GE_FLAG_C) || (e.c_type == GE_BF16 && small(e.ldc))) &&
+                          (!(e.flags & GE_FLAG_RESIDUAL) || (e.r_type == GE_BF16 && small(e.ldr))) &&
+                          (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
     if constexpr (DUAL) {
-#pragma unroll
-        for (int i = 0; i < C::MT; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NT; ++j) {
-                const int m = mbase + i * 16, n = nbase + j * 16;
-                if (m < p.M && n < p.N) {
-                    float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = activate<GE_ACT_SILU>(acc[0][i][j][r]) * acc[1][i][j][r];
-                    store4(e.D, e.d_type, (int64_t)m * e.ldd + n, v);
-                }
-            }
+        // SwiGLU outputs are bf16 (checked at plan time)
+        epilogue_swiglu(e, acc[0], acc[1], p.M, p.N, mbase, n0 + wn * C::WTN + fgrp * 8);
+    } else if (all_bf16) {
+        with_act(e.act, [&](auto ACTC) {
+            constexpr int ACT = decltype(ACTC)::value;
+            epilogue_bf16<ACT>(e, acc[0], p.M, p.N, mbase, n0 + wn * C::WTN + fgrp * 8);
+        });
     } else {
         with_act(e.act, [&](auto ACTC) {
             constexpr int ACT = decltype(ACTC)::value;
