@@ -65,8 +65,10 @@ __device__ __forceinline__ float activate(float t) {
     if constexpr (ACT == GE_ACT_RELU) {
         return fmaxf(t, 0.0f);
     } else if constexpr (ACT == GE_ACT_GELU_TANH) {
-        const float u2 = (2.0f * kSqrt2OverPi) * fmaf(kGeluCubic * t, t * t, t);
-        return t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-u2 * kLog2e));
+        // -2u log2(e) = t (a + b t^2): one exponent argument in three operations
+        constexpr float a = -2.0f * kSqrt2OverPi * kLog2e, b = a * kGeluCubic;
+        const float arg = t * fmaf(b, t * t, a);
+        return t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(arg));
     } else if constexpr (ACT == GE_ACT_SILU) {
         return t * fast_sigmoid(t);
     } else {

@@ -141,19 +141,26 @@ __device__ __forceinline__ void epi4(const EpiArgs &e, float v[4], int64_t m, in
 // per register do it: rows 2,3 of x trade with rows 0,1 of y, then odd rows
 // of the first result trade with even rows of the second.
 // Inline assembly: each swap rewrites both of its registers, as the operands
-// state (this compiler's two-result swap builtins keep only the first).  The
-// inputs are taken through whole-vector bit casts (a bit cast of one vector
-// element reads element 0 with this compiler).
+// state (this compiler's two-result swap builtins keep only the first).
 __device__ __forceinline__ void pair_to_cols8(const f32x4 &x, const f32x4 &y, float v[8]) {
+    // (scalar copies: neither vector elements nor single-element bit casts are used as asm or
+    // bit-cast operands, since this compiler reads element 0 for both)
     const u32x4 xu = __builtin_bit_cast(u32x4, x), yu = __builtin_bit_cast(u32x4, y);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        uint32_t a = xu[e], b = yu[e];
-        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1"
-                     : "+v"(a), "+v"(b));
-        v[e] = __builtin_bit_cast(float, a);
-        v[4 + e] = __builtin_bit_cast(float, b);
-    }
+    uint32_t a0 = xu[0], a1 = xu[1], a2 = xu[2], a3 = xu[3], b0 = yu[0], b1 = yu[1], b2 = yu[2], b3 = yu[3];
+    asm volatile("s_nop 1\n\t"
+                 "v_permlane32_swap_b32 %0, %4\n\tv_permlane32_swap_b32 %1, %5\n\t"
+                 "v_permlane32_swap_b32 %2, %6\n\tv_permlane32_swap_b32 %3, %7\n\t"
+                 "v_permlane16_swap_b32 %0, %4\n\tv_permlane16_swap_b32 %1, %5\n\t"
+                 "v_permlane16_swap_b32 %2, %6\n\tv_permlane16_swap_b32 %3, %7"
+                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+    v[0] = __builtin_bit_cast(float, a0);
+    v[1] = __builtin_bit_cast(float, a1);
+    v[2] = __builtin_bit_cast(float, a2);
+    v[3] = __builtin_bit_cast(float, a3);
+    v[4] = __builtin_bit_cast(float, b0);
+    v[5] = __builtin_bit_cast(float, b1);
+    v[6] = __builtin_bit_cast(float, b2);
+    v[7] = __builtin_bit_cast(float, b3);
 }
 
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float v[8]) {
@@ -179,23 +186,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mat_rsrc(const void *base, int
 // add nothing).  mrow: this lane's row in tile row 0; ncol: its first column
 // in tile pair 0 (tile pairs are 32 columns apart).  Needs the byte extent of
 // C, R and D below 2^31 (checked by the caller).
-template <int ACT, int MT, int NT>
+template <int ACT, bool HAS_C, int MT, int NT>
 __device__ __forceinline__ void epilogue_bf16(const EpiArgs &e, f32x4 (&acc)[MT][NT], int M, int N, int mrow,
                                               int ncol) {
     constexpr int NP = NT / 2, DEPTH = 2;
     static_assert(NT % 2 == 0, "tile pairs");
-    const bool has_c = e.flags & GE_FLAG_C, has_b = e.flags & GE_FLAG_BIAS, has_r = e.flags & GE_FLAG_RESIDUAL;
-    const auto rc = mat_rsrc(e.C, has_c ? ((int64_t)(M - 1) * e.ldc + N) * 2 : 0);
+    const bool has_b = e.flags & GE_FLAG_BIAS, has_r = e.flags & GE_FLAG_RESIDUAL;
+    const auto rc = mat_rsrc(e.C, HAS_C ? ((int64_t)(M - 1) * e.ldc + N) * 2 : 0);
     const auto rr = mat_rsrc(e.R, has_r ? ((int64_t)(M - 1) * e.ldr + N) * 2 : 0);
     const auto rb = mat_rsrc(e.bias, has_b ? (int64_t)N * 2 : 0);
     const auto rd = mat_rsrc(e.D, ((int64_t)(M - 1) * e.ldd + N) * 2);
-    const float beta = has_c ? e.beta : 0.0f;
-    u32x4 bias[NP];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-        const int n = ncol + 32 * q;
-        bias[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, n < N ? n * 2 : (int)OOB, 0, 0);
-    }
     u32x4 cv[DEPTH + 1][NP], rv[DEPTH + 1][NP];
     auto fetch = [&](int i, u32x4 (&c)[NP], u32x4 (&r)[NP]) {
         const int m = mrow + 16 * i;
@@ -203,12 +203,22 @@ __device__ __forceinline__ void epilogue_bf16(const EpiArgs &e, f32x4 (&acc)[MT]
         for (int q = 0; q < NP; ++q) {
             const int n = ncol + 32 * q;
             const bool ok = m < M && n < N;
-            c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? (int)(((int64_t)m * e.ldc + n) * 2) : (int)OOB, 0, 0);
+            if constexpr (HAS_C)
+                c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? (int)(((int64_t)m * e.ldc + n) * 2) : (int)OOB, 0, 0);
             r[q] = __builtin_amdgcn_raw_buffer_load_b128(rr, ok ? (int)(((int64_t)m * e.ldr + n) * 2) : (int)OOB, 0, 0);
         }
     };
+    u32x4 braw[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+        const int n = ncol + 32 * q;
+        braw[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, n < N ? n * 2 : (int)OOB, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < DEPTH && i < MT; ++i) fetch(i, cv[i], rv[i]);
+    float bias[NP][8];  // widened once
+#pragma unroll
+    for (int q = 0; q < NP; ++q) bf16x8_to_f32(braw[q], bias[q]);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         if (i + DEPTH < MT) fetch(i + DEPTH, cv[(i + DEPTH) % (DEPTH + 1)], rv[(i + DEPTH) % (DEPTH + 1)]);
@@ -216,14 +226,20 @@ __device__ __forceinline__ void epilogue_bf16(const EpiArgs &e, f32x4 (&acc)[MT]
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
             const int n = ncol + 32 * q;
-            float v[8], c[8], b[8], r[8];
+            float v[8], r[8];
             pair_to_cols8(acc[i][2 * q], acc[i][2 * q + 1], v);
-            bf16x8_to_f32(cv[i % (DEPTH + 1)][q], c);
-            bf16x8_to_f32(bias[q], b);
             bf16x8_to_f32(rv[i % (DEPTH + 1)][q], r);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = fmaf(e.alpha, v[t], bias[q][t]);
+            if constexpr (HAS_C) {
+                float c[8];
+                bf16x8_to_f32(cv[i % (DEPTH + 1)][q], c);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = fmaf(e.beta, c[t], v[t]);
+            }
             u32x4 w;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = activate<ACT>(fmaf(beta, c[t], e.alpha * v[t]) + b[t]) + r[t];
+            for (int t = 0; t < 8; ++t) v[t] = activate<ACT>(v[t]) + r[t];
 #pragma unroll
             for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
             const bool ok = m < M && n < N;
@@ -526,7 +542,10 @@ void tile_kernel(Problem p) {
     } else if (all_bf16) {
         with_act(e.act, [&](auto ACTC) {
             constexpr int ACT = decltype(ACTC)::value;
-            epilogue_bf16<ACT>(e, acc[0], p.M, p.N, mbase, n0 + wn * C::WTN + fgrp * 8);
+            if (e.flags & GE_FLAG_C)
+                epilogue_bf16<ACT, true>(e, acc[0], p.M, p.N, mbase, n0 + wn * C::WTN + fgrp * 8);
+            else
+                epilogue_bf16<ACT, false>(e, acc[0], p.M, p.N, mbase, n0 + wn * C::WTN + fgrp * 8);
         });
     } else {
         with_act(e.act, [&](auto ACTC) {
