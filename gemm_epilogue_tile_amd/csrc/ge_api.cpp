@@ -111,8 +111,8 @@ hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     return launch_general(p, s);
 }
 
-const char *fused_name(const Problem &p) {
-    if (skinny_supported(p)) return skinny_kernel_name(p);
+const char *fused_name(const Problem &p, int cu_count) {
+    if (skinny_supported(p)) return skinny_kernel_name(p, cu_count);
     if (tile_supported(p)) return tile_kernel_name(p);
     return "general_64x64";
 }
@@ -285,7 +285,7 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     // name of the fused kernel for aligned pointers
     Problem p = make_problem(&pl, (const void *)256, (const void *)256, (const void *)256, (const void *)256,
                              (const void *)256, (const void *)256, (const void *)256, (void *)256);
-    pl.kernel = fused_name(p);
+    pl.kernel = fused_name(p, pl.cu_count);
 
     ge_plan *h = new (std::nothrow) ge_plan(pl);
     if (!h) return fail(GE_ERR_INVALID_ARG, "out of host memory");

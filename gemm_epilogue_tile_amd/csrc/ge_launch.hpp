@@ -43,7 +43,7 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);
-const char *skinny_kernel_name(const Problem &p);
+const char *skinny_kernel_name(const Problem &p, int cu_count);
 
 // Elementwise kernels of the unfused chain.  All tensors dense [M, N] of the
 // given storage type unless noted.

@@ -50,8 +50,8 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return (x 
 // 8-column row chunks (16-byte accesses where aligned)
 // ---------------------------------------------------------------------------
 
-// red: [S_WAVES][MR][NC] fp32 partials in LDS (MR rows, NC columns)
-template <int MR, int NC>
+// red: [NWV][MR][NC] fp32 partials in LDS (MR rows, NC columns), NWV waves
+template <int MR, int NC, int NWV = S_WAVES>
 __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *red, int n0) {
     const EpiArgs &e = p.epi;
     constexpr int CH = NC / 8;  // 8-column chunks per row
@@ -64,7 +64,7 @@ __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *r
                         (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
     with_act(e.act, [&](auto ACTC) {
         constexpr int ACT = decltype(ACTC)::value;
-        for (int item = threadIdx.x; item < MR * CH; item += S_THREADS) {
+        for (int item = threadIdx.x; item < MR * CH; item += 64 * NWV) {
             const int r = item / CH, c = item % CH;
             const int m = r, n = n0 + c * 8;
             if (m >= p.M || n >= p.N) continue;
@@ -72,7 +72,7 @@ __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *r
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = 0.0f;
 #pragma unroll
-            for (int w = 0; w < S_WAVES; ++w) {
+            for (int w = 0; w < NWV; ++w) {
                 const f32x4 a = *(const f32x4 *)&red[(w * MR + r) * NC + c * 8];
                 const f32x4 b = *(const f32x4 *)&red[(w * MR + r) * NC + c * 8 + 4];
 #pragma unroll
@@ -96,10 +96,12 @@ __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *r
 // bf16 weights
 // ---------------------------------------------------------------------------
 
-// MT: 16-row tiles of X (M <= 16 MT).  WG: 128 columns, 8 waves splitting K.
-template <int MT>
+// MT: 16-row tiles of X (M <= 16 MT).  WG: NCH 8-column chunks (NCH <= 16,
+// one per lane of a 16-lane row; the remaining lanes idle), 8 waves splitting
+// K.  NCH is chosen per shape so that the workgroups fill the CUs evenly.
+template <int MT, int NCH>
 __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
-    constexpr int NC = 128;
+    constexpr int NC = 8 * NCH;
     constexpr int MR = 16 * MT;
     __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
 
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
     const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
 
     // W: lane -> rows 8 g + r of the block, 16-byte column chunk i (columns n0 + 8 i ..)
-    const bool nin = n0 + 8 * i < p.N;
+    const bool nin = i < NCH && n0 + 8 * i < p.N;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, ((int64_t)(p.K - 1) * p.ldb + p.N) * 2);
     // X: lane -> row mt*16 + i, k = 8 g .. 8 g + 7 of the block
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
@@ -169,14 +171,16 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
     }
 
     // partial tile -> LDS: lane (g, i) holds rows mt*16 + 4 g + e, columns 8 i + t
+    if (i < NCH) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            float *dst = &red[(wave * MR + mt * 16 + 4 * g + e4) * NC + 8 * i];
-            *(f32x4 *)dst = f32x4{acc[mt][0][e4], acc[mt][1][e4], acc[mt][2][e4], acc[mt][3][e4]};
-            *(f32x4 *)(dst + 4) = f32x4{acc[mt][4][e4], acc[mt][5][e4], acc[mt][6][e4], acc[mt][7][e4]};
-        }
+            for (int e4 = 0; e4 < 4; ++e4) {
+                float *dst = &red[(wave * MR + mt * 16 + 4 * g + e4) * NC + 8 * i];
+                *(f32x4 *)dst = f32x4{acc[mt][0][e4], acc[mt][1][e4], acc[mt][2][e4], acc[mt][3][e4]};
+                *(f32x4 *)(dst + 4) = f32x4{acc[mt][4][e4], acc[mt][5][e4], acc[mt][6][e4], acc[mt][7][e4]};
+            }
+    }
     __syncthreads();
     reduce_epilogue<MR, NC>(p, red, n0);
 }
@@ -196,13 +200,32 @@ __device__ __forceinline__ bf16x8 unpack_w4(uint32_t w) {
     return __builtin_bit_cast(bf16x8, f);
 }
 
-// NTW 16-column tiles per workgroup; 8 waves split the 128-row packing
+// NTW 16-column tiles per workgroup; W4_WAVES waves split the 128-row packing
 // groups.  SPG: 32-deep blocks per scale group (group size / 32 = 1, 2 or 4).
+// A wave takes its groups in rounds of RND: X, weights and scales of a whole
+// round are requested at once, in group order, so the wave computes group j
+// as soon as its bytes are in while the later groups are still arriving.  For
+// K = 8192 a round is the wave's entire share and a workgroup has all of its
+// weight bytes in flight at once.  Groups past the share read zeros.
+// Per group the sum of x * (c - z) is x * (128 + c) (one MFMA per 32-deep
+// block and tile) plus x * -(128 + z), which does not depend on the column and
+// is computed once for all tiles.
+#ifndef GE_W4_WAVES
+#define GE_W4_WAVES 8
+#endif
+#ifndef GE_W4_RND
+#define GE_W4_RND 4
+#endif
+constexpr int W4_WAVES = GE_W4_WAVES;
+constexpr int W4_THREADS = 64 * W4_WAVES;
+
 template <int NTW, int SPG>
-__global__ __launch_bounds__(S_THREADS) void skinny_w4_kernel(Problem p) {
+__global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
     constexpr int NC = 16 * NTW;
     constexpr int MR = 16;
-    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    constexpr int NSG = 4 / SPG;               // scale groups per 128-row packing group
+    constexpr int RND = SPG == 1 ? (GE_W4_RND + 1) / 2 : GE_W4_RND;  // groups per round (32-row groups carry 4 scales each)
+    __shared__ __attribute__((aligned(16))) float red[W4_WAVES * MR * NC];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -211,52 +234,66 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w4_kernel(Problem p) {
     const int n0 = nt0 * 16;
     const int ntiles = p.N / 16;
     const int ngroups = p.K / 128;
-    const int per = (ngroups + S_WAVES - 1) / S_WAVES;
+    const int per = (ngroups + W4_WAVES - 1) / W4_WAVES;
     const int g0 = wave * per, g1 = min(ngroups, g0 + per);
 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
-    const uint16_t *sc = (const uint16_t *)p.scales;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2);
 
     // constant fragment -(128 + zero point) (exact in bf16) for the zero-point correction
     const uint32_t nz = f32_to_bf16(-(128.0f + (float)p.zero_point));
     const uint32_t nz2 = nz | (nz << 16);
-    const bf16x8 neg136 = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
+    const bf16x8 negz = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
 
     f32x4 tot[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int gi = g0; gi < g1; ++gi) {
-        u32x4 w[NTW];
+    for (int base = g0; base < g1; base += RND) {
+        bf16x8 x[RND][4];
+        u32x4 w[RND][NTW];
+        uint16_t sraw[RND][NTW][NSG];
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const bool tin = nt0 + t < ntiles;
-            w[t] = bload16(rw, tin ? (uint32_t)((((int64_t)(nt0 + t) * ngroups + gi) * 64 + lane) * 16) : OOB);
+        for (int j = 0; j < RND; ++j) {
+            const int gi = base + j;
+            const bool gin = gi < g1;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int k = gi * 128 + kb * 32 + 8 * g;
+                const uint32_t off = (uint32_t)(((int64_t)i * p.lda + k) * 2);
+                x[j][kb] = __builtin_bit_cast(bf16x8, bload16(rx, (i < p.M && gin) ? off : OOB));
+            }
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const bool tin = gin && nt0 + t < ntiles;
+                w[j][t] = bload16(rw, tin ? (uint32_t)((((int64_t)(nt0 + t) * ngroups + gi) * 64 + lane) * 16) : OOB);
+                const int n = n0 + 16 * t + i;
+#pragma unroll
+                for (int sg = 0; sg < NSG; ++sg)
+                    sraw[j][t][sg] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rs, tin && n < p.N ? (int)(((int64_t)(gi * NSG + sg) * p.ld_s + n) * 2) : (int)OOB, 0, 0);
+            }
         }
-        bf16x8 x[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int k = gi * 128 + kb * 32 + 8 * g;
-            const uint32_t off = (uint32_t)(((int64_t)i * p.lda + k) * 2);
-            x[kb] = __builtin_bit_cast(bf16x8, bload16(rx, i < p.M ? off : OOB));
-        }
+        for (int j = 0; j < RND; ++j) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int n = n0 + 16 * t + i;
+            for (int sg = 0; sg < NSG; ++sg) {
+                f32x4 corr = f32x4{0.f, 0.f, 0.f, 0.f}, u[NTW];
 #pragma unroll
-            for (int sg = 0; sg < 4; sg += SPG) {
-                // sum over one scale group of x * (c - 8), then scale
-                f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < NTW; ++t) u[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = sg; kb < sg + SPG; ++kb) {
-                    u = mfma_bf16(x[kb], unpack_w4(w[t][kb]), u);
-                    u = mfma_bf16(x[kb], neg136, u);
+                for (int kb = sg * SPG; kb < (sg + 1) * SPG; ++kb) {
+                    corr = mfma_bf16(x[j][kb], negz, corr);
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) u[t] = mfma_bf16(x[j][kb], unpack_w4(w[j][t][kb]), u[t]);
                 }
-                const int grp = (gi * 128 + sg * 32) / (SPG * 32);
-                const float s = n < p.N ? bf16_to_f32(sc[(int64_t)grp * p.ld_s + n]) : 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) tot[t][q] = fmaf(s, u[q], tot[t][q]);
+                for (int t = 0; t < NTW; ++t) {
+                    const float sv = bf16_to_f32(sraw[j][t][sg]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) tot[t][q] = fmaf(sv, u[t][q] + corr[q], tot[t][q]);
+                }
             }
         }
     }
@@ -267,7 +304,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w4_kernel(Problem p) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) red[(wave * MR + 4 * g + e4) * NC + 16 * t + i] = tot[t][e4];
     __syncthreads();
-    reduce_epilogue<MR, NC>(p, red, n0);
+    reduce_epilogue<MR, NC, W4_WAVES>(p, red, n0);
 }
 
 // Prepack: raw [K, N/2] bytes (two codes per byte, order per lo_first) ->
@@ -331,29 +368,64 @@ bool skinny_supported(const Problem &p) {
     return b_bytes < (1ll << 31) && a_bytes < (1ll << 31);
 }
 
-const char *skinny_kernel_name(const Problem &p) {
-    if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
-    return p.M <= 16 ? "skinny_bf16_m16_128col" : "skinny_bf16_m32_128col";
+namespace {
+// 8-column chunks per bf16 workgroup: the choice that minimises the columns
+// the busiest CU streams, ceil(workgroups / CUs) * chunks (ties: wider).
+// Only 16 and 8 keep every workgroup's row segments on 128-byte boundaries;
+// 112- and 96-column blocks share cache lines between neighbours and measured
+// slower (the decode shape 16 x 28672 x 8192 went from 98 to 117 us).
+int bf16_chunks(int N, int cu_count) {
+    static const int opts[] = {16, 8};
+    int best = 16;
+    int64_t best_cost = -1;
+    for (int c : opts) {
+        const int64_t wgs = (N + 8 * c - 1) / (8 * c);
+        const int64_t cost = (wgs + cu_count - 1) / cu_count * c;
+        if (best_cost < 0 || cost < best_cost) best = c, best_cost = cost;
+    }
+    return best;
 }
 
-hipError_t launch_skinny(const Problem &p, int, hipStream_t s) {
+template <int MT>
+void launch_bf16(const Problem &p, int nch, hipStream_t s) {
+    const int blocks = (p.N + 8 * nch - 1) / (8 * nch);
+    switch (nch) {
+    case 14: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 14>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
+    case 12: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 12>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 8>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
+    default: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 16>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
+    }
+}
+}  // namespace
+
+const char *skinny_kernel_name(const Problem &p, int cu_count) {
+    if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
+    static const char *names[2][4] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_112col", "skinny_bf16_m16_96col",
+                                       "skinny_bf16_m16_64col"},
+                                      {"skinny_bf16_m32_128col", "skinny_bf16_m32_112col", "skinny_bf16_m32_96col",
+                                       "skinny_bf16_m32_64col"}};
+    const int c = bf16_chunks(p.N, cu_count);
+    return names[p.M > 16][c == 16 ? 0 : c == 14 ? 1 : c == 12 ? 2 : 3];
+}
+
+hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
     if (!skinny_supported(p)) return hipErrorInvalidValue;
     if (p.mode == MODE_W4) {
         constexpr int NTW = 2;
         const int blocks = (p.N / 16 + NTW - 1) / NTW;
         if (p.group == 32)
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 1>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 1>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
         else if (p.group == 64)
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
         else
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
         return hipGetLastError();
     }
-    const int blocks = (p.N + 127) / 128;
+    const int nch = bf16_chunks(p.N, cu_count > 0 ? cu_count : 256);
     if (p.M <= 16)
-        hipLaunchKernelGGL(skinny_bf16_kernel<1>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+        launch_bf16<1>(p, nch, s);
     else
-        hipLaunchKernelGGL(skinny_bf16_kernel<2>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+        launch_bf16<2>(p, nch, s);
     return hipGetLastError();
 }
 

@@ -302,7 +302,9 @@ def test_add_rmsnorm_in_place_residual():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 8), (3, 136, 96), (16, 1000, 1000), (16, 2048, 4096),
-                                   (17, 264, 520), (32, 512, 2048), (5, 4104, 136)])
+                                   (17, 264, 520), (32, 512, 2048), (5, 4104, 136),
+                                   # wide N: 128-column workgroups
+                                   (16, 32768, 64), (16, 28672, 96), (32, 28680, 64)])
 def test_skinny_bf16_bias_residual_gelu(M, N, K):
     w = workloads.WORKLOADS["skinny_decode"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N + K)
@@ -315,6 +317,8 @@ def test_skinny_bf16_bias_residual_gelu(M, N, K):
 def test_skinny_plan_picks_the_streaming_kernel():
     p = ge.plan(ge.KIND_GENERIC, 16, 28672, 8192, bias=True, R=True)
     assert p.kernel.startswith("skinny_bf16")
+    q16 = ge.plan(ge.KIND_GENERIC, 16, 4096, 8192, bias=True, R=True)
+    assert q16.kernel == "skinny_bf16_m16_64col"  # 64 workgroups of 64 columns beat 32 of 128
     q = ge.plan(ge.KIND_W4, 16, 8192, 8192, b_type=ge.U4X2, bias=True, prepacked=True)
     assert q.kernel.startswith("skinny_w4")
 
