@@ -211,6 +211,12 @@ class Prepared:
         if s != OK:
             raise GemmEpiError(s, self._where, lib().ge_last_error().decode())
 
+    def with_stream(self, stream=None) -> "Prepared":
+        """The same call bound to another stream (default: the current one), e.g.
+        the capture stream inside ``torch.cuda.graph``.  The runs allocate nothing
+        and never synchronise, so they can be captured into a HIP graph."""
+        return Prepared(self._fn, self._where, self._plan, self._tensors, self._args[:-1] + (_stream(stream),))
+
 
 _plan_cache: dict = {}
 

@@ -39,237 +39,8 @@
 namespace ge {
 namespace {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-#define AS3 __attribute__((address_space(3)))
+#include "ge_tile_common.hpp"
 
-constexpr int T_THREADS = 256;
-constexpr int T_BK = 32;   // K depth of one stage
-constexpr int T_NS = 4;    // LDS stages
-constexpr int GROUP_M = 4;
-constexpr uint32_t OOB = 0x80000000u;  // beyond any buffer this kernel builds (< 2^31 bytes)
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (base, size in bytes, stride 0): lanes whose offset is
-// at or past `bytes` read zeros.  The fields are wave-uniform.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
-    const uint32_t n = bytes > 0 ? (uint32_t)bytes : 0u;
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)n);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from memory straight into LDS at lds + 16 * lane.  Issued
-// as inline assembly so the compiler does not track it: its LDS writes are
-// ordered by the explicit vmcnt waits and barriers of the main loop.  (The
-// tracked builtin makes the compiler wait for every outstanding direct load
-// before any LDS read, which would undo the prefetch.)
-__device__ __forceinline__ void load_lds16(const i32x4 &r, uint32_t lds_addr, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(r) : "memory", "m0");
-}
-
-// [rows][32] tiles (64-byte rows): 16-byte chunk c of row r lives at c ^ ((r >> 1) & 3)
-__device__ __forceinline__ int swz_a(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
-// [32][BN] tiles: 16-byte chunk c of row k lives at c ^ ((k & 3) << 1)
-template <int BN>
-__device__ __forceinline__ int swz_b(int k, int chunk) { return k * (BN * 2) + ((chunk ^ ((k & 3) << 1)) << 4); }
-
-// 4 consecutive elements as fp32 (8-byte bf16 or 16-byte fp32 access)
-__device__ __forceinline__ void load4(const void *p, int32_t type, int64_t off, float v[4]) {
-    if (type == GE_BF16) {
-        const u32x2 w = *(const u32x2 *)((const uint16_t *)p + off);
-        v[0] = bf16lo(w[0]);
-        v[1] = bf16hi(w[0]);
-        v[2] = bf16lo(w[1]);
-        v[3] = bf16hi(w[1]);
-    } else {
-        const f32x4 a = *(const f32x4 *)((const float *)p + off);
-        v[0] = a[0];
-        v[1] = a[1];
-        v[2] = a[2];
-        v[3] = a[3];
-    }
-}
-
-__device__ __forceinline__ void store4(void *p, int32_t type, int64_t off, const float v[4]) {
-    if (type == GE_BF16) {
-        u32x2 w;
-        w[0] = pack_bf16x2(v[0], v[1]);
-        w[1] = pack_bf16x2(v[2], v[3]);
-        *(u32x2 *)((uint16_t *)p + off) = w;
-    } else {
-        *(f32x4 *)((float *)p + off) = f32x4{v[0], v[1], v[2], v[3]};
-    }
-}
-
-template <int ACT>
-__device__ __forceinline__ void epi4(const EpiArgs &e, float v[4], int64_t m, int64_t n) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= e.alpha;
-    if (e.flags & GE_FLAG_C) {
-        float c[4];
-        load4(e.C, e.c_type, m * e.ldc + n, c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = fmaf(e.beta, c[i], v[i]);
-    }
-    if (e.flags & GE_FLAG_BIAS) {
-        float b[4];
-        load4(e.bias, e.bias_type, n, b);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += b[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = activate<ACT>(v[i]);
-    if (e.flags & GE_FLAG_RESIDUAL) {
-        float r[4];
-        load4(e.R, e.r_type, m * e.ldr + n, r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += r[i];
-    }
-    store4(e.D, e.d_type, m * e.ldd + n, v);
-}
-
-// Two horizontally adjacent 16x16 accumulator tiles x (columns c..c+15) and
-// y (c+16..c+31), in the fragment layout where lane row g = lane / 16 holds
-// columns 4g..4g+3 of its tile, become eight consecutive columns per lane:
-// lane row g ends up with columns c + 8g .. c + 8g + 7.  Two lane-row swaps
-// per register do it: rows 2,3 of x trade with rows 0,1 of y, then odd rows
-// of the first result trade with even rows of the second.
-// Inline assembly: each swap rewrites both of its registers, as the operands
-// state (this compiler's two-result swap builtins keep only the first).
-__device__ __forceinline__ void pair_to_cols8(const f32x4 &x, const f32x4 &y, float v[8]) {
-    // (scalar copies: neither vector elements nor single-element bit casts are used as asm or
-    // bit-cast operands, since this compiler reads element 0 for both)
-    const u32x4 xu = __builtin_bit_cast(u32x4, x), yu = __builtin_bit_cast(u32x4, y);
-    uint32_t a0 = xu[0], a1 = xu[1], a2 = xu[2], a3 = xu[3], b0 = yu[0], b1 = yu[1], b2 = yu[2], b3 = yu[3];
-    asm volatile("s_nop 1\n\t"
-                 "v_permlane32_swap_b32 %0, %4\n\tv_permlane32_swap_b32 %1, %5\n\t"
-                 "v_permlane32_swap_b32 %2, %6\n\tv_permlane32_swap_b32 %3, %7\n\t"
-                 "v_permlane16_swap_b32 %0, %4\n\tv_permlane16_swap_b32 %1, %5\n\t"
-                 "v_permlane16_swap_b32 %2, %6\n\tv_permlane16_swap_b32 %3, %7"
-                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
-    v[0] = __builtin_bit_cast(float, a0);
-    v[1] = __builtin_bit_cast(float, a1);
-    v[2] = __builtin_bit_cast(float, a2);
-    v[3] = __builtin_bit_cast(float, a3);
-    v[4] = __builtin_bit_cast(float, b0);
-    v[5] = __builtin_bit_cast(float, b1);
-    v[6] = __builtin_bit_cast(float, b2);
-    v[7] = __builtin_bit_cast(float, b3);
-}
-
-__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float v[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16lo(w[i]);
-        v[2 * i + 1] = bf16hi(w[i]);
-    }
-}
-
-// Buffer resource over a row-major bf16 matrix: rows below M, reads past it
-// give zeros and writes past it are dropped.  Absent operands get an empty
-// range, so their loads return zeros without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mat_rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Epilogue of a wave's MT x NT grid of 16x16 tiles when D, C, R and bias are
-// all bf16 (the common case): each lane owns 8 consecutive columns per tile
-// pair, so every access is 16 bytes.  The C and R rows of tile row i + 2 are
-// fetched while tile row i is computed; the code has no branches, so the
-// memory waits count exactly (absent terms read zeros from empty buffers and
-// add nothing).  mrow: this lane's row in tile row 0; ncol: its first column
-// in tile pair 0 (tile pairs are 32 columns apart).  Needs the byte extent of
-// C, R and D below 2^31 (checked by the caller).
-template <int ACT, bool HAS_C, int MT, int NT>
-__device__ __forceinline__ void epilogue_bf16(const EpiArgs &e, f32x4 (&acc)[MT][NT], int M, int N, int mrow,
-                                              int ncol) {
-    constexpr int NP = NT / 2, DEPTH = 2;
-    static_assert(NT % 2 == 0, "tile pairs");
-    const bool has_b = e.flags & GE_FLAG_BIAS, has_r = e.flags & GE_FLAG_RESIDUAL;
-    const auto rc = mat_rsrc(e.C, HAS_C ? ((int64_t)(M - 1) * e.ldc + N) * 2 : 0);
-    const auto rr = mat_rsrc(e.R, has_r ? ((int64_t)(M - 1) * e.ldr + N) * 2 : 0);
-    const auto rb = mat_rsrc(e.bias, has_b ? (int64_t)N * 2 : 0);
-    const auto rd = mat_rsrc(e.D, ((int64_t)(M - 1) * e.ldd + N) * 2);
-    u32x4 cv[DEPTH + 1][NP], rv[DEPTH + 1][NP];
-    auto fetch = [&](int i, u32x4 (&c)[NP], u32x4 (&r)[NP]) {
-        const int m = mrow + 16 * i;
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            const int n = ncol + 32 * q;
-            const bool ok = m < M && n < N;
-            if constexpr (HAS_C)
-                c[q] = __builtin_amdgcn_raw_buffer_load_b128(rc, ok ? (int)(((int64_t)m * e.ldc + n) * 2) : (int)OOB, 0, 0);
-            r[q] = __builtin_amdgcn_raw_buffer_load_b128(rr, ok ? (int)(((int64_t)m * e.ldr + n) * 2) : (int)OOB, 0, 0);
-        }
-    };
-    u32x4 braw[NP];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-        const int n = ncol + 32 * q;
-        braw[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, n < N ? n * 2 : (int)OOB, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < DEPTH && i < MT; ++i) fetch(i, cv[i], rv[i]);
-    float bias[NP][8];  // widened once
-#pragma unroll
-    for (int q = 0; q < NP; ++q) bf16x8_to_f32(braw[q], bias[q]);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        if (i + DEPTH < MT) fetch(i + DEPTH, cv[(i + DEPTH) % (DEPTH + 1)], rv[(i + DEPTH) % (DEPTH + 1)]);
-        const int m = mrow + 16 * i;
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-            const int n = ncol + 32 * q;
-            float v[8], r[8];
-            pair_to_cols8(acc[i][2 * q], acc[i][2 * q + 1], v);
-            bf16x8_to_f32(rv[i % (DEPTH + 1)][q], r);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = fmaf(e.alpha, v[t], bias[q][t]);
-            if constexpr (HAS_C) {
-                float c[8];
-                bf16x8_to_f32(cv[i % (DEPTH + 1)][q], c);
-#pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = fmaf(e.beta, c[t], v[t]);
-            }
-            u32x4 w;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = activate<ACT>(v[t]) + r[t];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(v[2 * t], v[2 * t + 1]);
-            const bool ok = m < M && n < N;
-            __builtin_amdgcn_raw_buffer_store_b128(w, rd, ok ? (int)(((int64_t)m * e.ldd + n) * 2) : (int)OOB, 0, 0);
-        }
-    }
-}
-
-// SwiGLU store: silu(g) * u over the same 16-byte column groups.
-template <int MT, int NT>
-__device__ __forceinline__ void epilogue_swiglu(const EpiArgs &e, f32x4 (&g)[MT][NT], f32x4 (&u)[MT][NT], int M,
-                                                int N, int mrow, int ncol) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = mrow + 16 * i;
-#pragma unroll
-        for (int q = 0; q < NT / 2; ++q) {
-            const int n = ncol + 32 * q;
-            float vg[8], vu[8];
-            pair_to_cols8(g[i][2 * q], g[i][2 * q + 1], vg);
-            pair_to_cols8(u[i][2 * q], u[i][2 * q + 1], vu);
-            u32x4 w;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                w[t] = pack_bf16x2(activate<GE_ACT_SILU>(vg[2 * t]) * vu[2 * t],
-                                   activate<GE_ACT_SILU>(vg[2 * t + 1]) * vu[2 * t + 1]);
-            if (m < M && n < N) *(u32x4 *)((uint16_t *)e.D + (int64_t)m * e.ldd + n) = w;
-        }
-    }
-}
 
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 struct Cfg {
@@ -565,239 +336,6 @@ void tile_kernel(Problem p) {
 }
 
 
-// ---------------------------------------------------------------------------
-// int4 weights (prepacked), M > 16: 128 x 128 tiles, fp16 MFMA.
-//
-// (code - z) * s has at most 3 + 8 significant bits, so the dequantised
-// weight is exact in fp16 (for scales with |8 s| in the fp16 normal range);
-// the bf16 activations convert to fp16 exactly (for |x| in the fp16 range).
-// The products are then exact in fp32 and no per-group rescaling of the
-// accumulators is needed.  Dequant per pair of codes: the codes are OR-ed into
-// the mantissa of fp16 1024 (giving 1024 + c), then a packed subtract of
-// 1024 + z and a packed multiply by s (exact for z = 8).  Scale groups of
-// 128 rows.
-//
-// A: direct loads into 4 LDS stages of 32 k, as in the bf16 tile kernel.
-// B: per 128-row group, the workgroup's 8 column tiles (8 KB, lane-major as
-//    prepacked) go to one of two LDS group buffers by direct loads; each wave
-//    reads its 4 tiles' 16 bytes per lane once per group.
-// ---------------------------------------------------------------------------
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ void mfma_f16_acc(f32x4 &acc, const f16x8 &a, const f16x8 &b) {
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// bf16 x8 -> fp16 x8 (exact for values in the fp16 range)
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const bf16x8 &x) {
-    const u32x4 w = __builtin_bit_cast(u32x4, x);
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float lo = bf16lo(w[q]), hi = bf16hi(w[q]);
-        r[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-    }
-    return __builtin_bit_cast(f16x8, r);
-}
-
-// one packed dword of 8 codes -> fp16 B fragment (k in order), (c - z) * s:
-// (1024 + c) - (1024 + z) is an exact small integer; with z = 8 it has at
-// most 3 significant bits, so its product with a bf16 scale (8 bits) is exact
-// in fp16.  Other zero points may round the product by half an fp16 ulp.
-__device__ __forceinline__ f16x8 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) {
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t t = ((w >> (4 * q)) & 0x000f000fu) | 0x64006400u;  // fp16 1024 + c
-        const f16x2 v = (__builtin_bit_cast(f16x2, t) - z2) * s2;
-        r[q] = __builtin_bit_cast(uint32_t, v);
-    }
-    return __builtin_bit_cast(f16x8, r);
-}
-
-constexpr int W4_BM = 128, W4_BN = 128, W4_MT = 4, W4_NT = 4;
-constexpr int W4_A_STAGE = W4_BM * T_BK * 2;        // 8 KB
-constexpr int W4_A_INSTR = W4_A_STAGE / 1024 / 4;   // 2 per wave per stage
-constexpr int W4_B_GROUP = (W4_BN / 16) * 1024;     // 8 KB: 8 tiles x 64 lanes x 16 B
-constexpr int W4_B_INSTR = W4_B_GROUP / 1024 / 4;   // 2 per wave per group
-constexpr int W4_B_BASE = T_NS * W4_A_STAGE;        // 32 KB
-constexpr int W4_S_BASE = W4_B_BASE + 2 * W4_B_GROUP;  // scales: 2 group buffers x 4 waves x 1 KB
-constexpr int W4_S_GROUP = 4 * 1024;
-constexpr int W4_LDS = W4_S_BASE + 2 * W4_S_GROUP;  // 56 KB
-
-__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS)))
-void tile_w4_kernel(Problem p) {
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(AS3 void *)smem;
-    const AS3 char *s3 = (const AS3 char *)smem;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-
-    const int tiles_m = (p.M + W4_BM - 1) / W4_BM, tiles_n = p.N / W4_BN;
-    const int total = tiles_m * tiles_n;
-    int t = blockIdx.x;
-    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-    const int per_group = GROUP_M * tiles_n;
-    const int first_m = (t / per_group) * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (t % per_group) % gsize;
-    const int tn = (t % per_group) / gsize;
-    const int m0 = tm * W4_BM, n0 = tn * W4_BN;
-    const int ngroups = p.K / 128;
-
-    // A direct loads: [128][32] per stage, 16 rows x 4 chunks per instruction
-    const int arow_l = lane >> 2;
-    const int achunk = (lane & 3) ^ ((arow_l >> 1) & 3);
-    uint32_t a_off[W4_A_INSTR];
-#pragma unroll
-    for (int q = 0; q < W4_A_INSTR; ++q)
-        a_off[q] = (uint32_t)(((wave * W4_A_INSTR + q) * 16 + arow_l) * p.lda * 2) + achunk * 16;
-    auto load_a = [&](int s) {
-        const int k0 = s * T_BK;
-        const i32x4 r = make_rsrc((const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2,
-                                  ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
-        const bool kin = k0 + achunk * 8 < p.K;
-        const uint32_t dst = lds0 + (s & (T_NS - 1)) * W4_A_STAGE + wave * W4_A_INSTR * 1024;
-#pragma unroll
-        for (int q = 0; q < W4_A_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? a_off[q] : OOB);
-    };
-    // B direct loads: group gi of the workgroup's 8 column tiles (1 KB per tile and group), and
-    // the group's bf16 scales: wave w brings columns n0 + 32w .. n0 + 32w + 31 (lanes 0..3; the
-    // other lanes read out of range and fill the rest of the wave's 1 KB slot with zeros).
-    const i32x4 rb = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
-    const i32x4 rs = make_rsrc(p.scales, ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2);
-    auto load_b = [&](int gi) {
-        const bool gin = gi < ngroups;
-        const uint32_t dst = lds0 + W4_B_BASE + (gi & 1) * W4_B_GROUP + wave * W4_B_INSTR * 1024;
-#pragma unroll
-        for (int q = 0; q < W4_B_INSTR; ++q) {
-            const int nt = n0 / 16 + wave * W4_B_INSTR + q;
-            const uint32_t off = (uint32_t)(((nt * ngroups + gi) * 64 + lane) * 16);
-            load_lds16(rb, dst + q * 1024, gin ? off : OOB);
-        }
-        const uint32_t soff = (uint32_t)(((int64_t)gi * p.ld_s + n0 + wave * 32) * 2) + lane * 16;
-        load_lds16(rs, lds0 + W4_S_BASE + (gi & 1) * W4_S_GROUP + wave * 1024, gin && lane < 4 ? soff : OOB);
-    };
-
-    const int frow = lane & 15, fgrp = lane >> 4;
-    const int a_frag = swz_a(wm * 64 + frow, fgrp);
-    const uint32_t b_raw = W4_B_BASE + (wn * W4_NT) * 1024 + lane * 16;  // + group buffer
-
-    // fp16 scale pairs for this lane's 4 columns of one group (scale groups of 128 rows), from the
-    // group's LDS buffer: column c of the tile sits in wave c / 32's slot at byte 2 (c % 32)
-    auto scales_of = [&](int gb, f16x2 (&s2)[W4_NT]) {
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) {
-            const int c = (wn * W4_NT + j) * 16 + frow;
-            const uint16_t raw = *(const AS3 uint16_t *)(s3 + W4_S_BASE + gb * W4_S_GROUP + (c >> 5) * 1024 +
-                                                         (c & 31) * 2);
-            const _Float16 h = (_Float16)bf16_to_f32(raw);
-            s2[j] = f16x2{h, h};
-        }
-    };
-    const _Float16 zh = (_Float16)(1024.0f + (float)p.zero_point);
-    const f16x2 z2 = f16x2{zh, zh};
-
-    f32x4 acc[W4_MT][W4_NT];
-#pragma unroll
-    for (int i = 0; i < W4_MT; ++i)
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto lds_barrier = [&]() {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    };
-#define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
-    constexpr int LA = W4_A_INSTR, LB = W4_B_INSTR + 1;  // per wave: A loads per stage, B + scale loads per group
-
-    // issue order: B(g0), A(0), A(1), A(2), A(3); then per stage s: A(s+4), and at the first stage
-    // of a group also B(next group).  Waits below count the loads issued after the ones needed.
-    load_b(0);
-#pragma unroll
-    for (int s = 0; s < T_NS; ++s) load_a(s);
-    GE_WAIT_VM(3 * LA);  // A(0) and B(0) landed
-    lds_barrier();
-
-    bf16x8 fa[2][W4_MT];
-    u32x4 braw[W4_NT], braw_n[W4_NT];  // this group's / the next group's packed codes
-    f16x2 sc2[W4_NT], sc2_n[W4_NT];
-#pragma unroll
-    for (int i = 0; i < W4_MT; ++i) fa[0][i] = *(const AS3 bf16x8 *)(s3 + a_frag + i * 1024);
-#pragma unroll
-    for (int j = 0; j < W4_NT; ++j) braw[j] = *(const AS3 u32x4 *)(s3 + b_raw + j * 1024);
-    scales_of(0, sc2);
-
-    for (int gi = 0; gi < ngroups; ++gi) {
-        const int gb = gi & 1;
-#pragma unroll
-        for (int b = 0; b < T_NS; ++b) {
-            const int s = gi * T_NS + b;
-            // stage s+1 (and at b == 3 the next group's B) must have landed
-            if (b == 0) GE_WAIT_VM(2 * LA);
-            else if (b == 3) GE_WAIT_VM(2 * LA);
-            else GE_WAIT_VM(2 * LA + LB);
-            lds_barrier();
-            load_a(s + T_NS);
-            if (b == 0) load_b(gi + 1);
-            // next stage's fragments (the next group's raw B and scales at b == 3)
-            const int sn = (b + 1) & (T_NS - 1);
-#pragma unroll
-            for (int i = 0; i < W4_MT; ++i)
-                fa[(b + 1) & 1][i] = *(const AS3 bf16x8 *)(s3 + a_frag + sn * W4_A_STAGE + i * 1024);
-            if (b == 3) {
-#pragma unroll
-                for (int j = 0; j < W4_NT; ++j)
-                    braw_n[j] = *(const AS3 u32x4 *)(s3 + b_raw + (gb ^ 1) * W4_B_GROUP + j * 1024);
-                scales_of(gb ^ 1, sc2_n);
-            }
-            // this stage
-            f16x8 ah[W4_MT];
-#pragma unroll
-            for (int i = 0; i < W4_MT; ++i) ah[i] = bf16x8_to_f16x8(fa[b & 1][i]);
-#pragma unroll
-            for (int j = 0; j < W4_NT; ++j) {
-                const f16x8 bh = dequant_w4_f16(braw[j][b], sc2[j], z2);
-#pragma unroll
-                for (int i = 0; i < W4_MT; ++i) mfma_f16_acc(acc[i][j], bh, ah[i]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) {
-            braw[j] = braw_n[j];
-            sc2[j] = sc2_n[j];
-        }
-    }
-#undef GE_WAIT_VM
-    __builtin_amdgcn_s_waitcnt(0);
-    mfma_drain();
-#pragma unroll
-    for (int i = 0; i < W4_MT; ++i)
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) asm volatile("" : "+a"(acc[i][j]));
-
-    const EpiArgs &e = p.epi;
-    const int mbase = m0 + wm * 64 + frow;
-    const int nbase = n0 + wn * 64 + fgrp * 4;
-    with_act(e.act, [&](auto ACTC) {
-        constexpr int ACT = decltype(ACTC)::value;
-#pragma unroll
-        for (int i = 0; i < W4_MT; ++i)
-#pragma unroll
-            for (int j = 0; j < W4_NT; ++j) {
-                const int m = mbase + i * 16, n = nbase + j * 16;
-                if (m < p.M && n < p.N) {
-                    float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                    epi4<ACT>(e, v, m, n);
-                }
-            }
-    });
-}
-
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
 hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     using C = Cfg<BM, BN, WM, WN, DUAL, B_NK>;
@@ -813,30 +351,7 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
-
-bool epi_ok(const Problem &p) {
-    const EpiArgs &e = p.epi;
-    auto ok_mat = [](const void *q, int32_t type, int64_t ld) {
-        return al16(q) && ((ld * (type == GE_BF16 ? 2 : 4)) % 16) == 0;
-    };
-    if (!ok_mat(e.D, e.d_type, e.ldd)) return false;
-    if ((e.flags & GE_FLAG_C) && !ok_mat(e.C, e.c_type, e.ldc)) return false;
-    if ((e.flags & GE_FLAG_RESIDUAL) && !ok_mat(e.R, e.r_type, e.ldr)) return false;
-    if ((e.flags & GE_FLAG_BIAS) && !al16(e.bias)) return false;
-    return true;
-}
-
 }  // namespace
-
-bool tile_w4_supported(const Problem &p) {
-    if (p.mode != MODE_W4 || !p.w4_packed || p.M <= 16) return false;
-    if ((p.N % W4_BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
-    if (p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
-    if (((int64_t)(p.M - 1) * p.lda + p.K) * 2 >= (1ll << 31)) return false;
-    if ((int64_t)p.K * p.N / 2 >= (1ll << 31) || (int64_t)p.K / 128 * p.ld_s * 2 >= (1ll << 31)) return false;
-    return epi_ok(p);
-}
 
 bool tile_supported(const Problem &p) {
     if (p.mode == MODE_W4) return tile_w4_supported(p);
@@ -854,25 +369,14 @@ bool tile_supported(const Problem &p) {
 }
 
 const char *tile_kernel_name(const Problem &p) {
-    if (p.mode == MODE_W4) return "tile_w4_f16_128x128x32";
+    if (p.mode == MODE_W4) return tile_w4_kernel_name();
     if (p.mode == MODE_SWIGLU) return "tile_swiglu_256x128x32";
     return p.b_layout == GE_LAYOUT_NK ? "tile_nk_256x256x32" : "tile_kn_256x256x32";
 }
 
 hipError_t launch_tile(const Problem &p, int, hipStream_t s) {
     if (!tile_supported(p)) return hipErrorInvalidValue;
-    if (p.mode == MODE_W4) {
-        static bool attr_set = false;  // benign race: every caller sets the same value
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, W4_LDS);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
-        const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4_BN);
-        hipLaunchKernelGGL(tile_w4_kernel, dim3(tiles), dim3(T_THREADS), W4_LDS, s, p);
-        return hipGetLastError();
-    }
+    if (p.mode == MODE_W4) return launch_tile_w4(p, s);
     if (p.mode == MODE_SWIGLU) return launch_cfg<256, 128, 2, 2, true, false>(p, s);
     if (p.b_layout == GE_LAYOUT_NK) return launch_cfg<256, 256, 2, 2, false, true>(p, s);
     return launch_cfg<256, 256, 2, 2, false, false>(p, s);

@@ -1,0 +1,62 @@
+"""A decode chain of fused calls captured in a HIP graph and replayed (the
+runs allocate nothing and do not synchronise, so they are capture-safe).
+
+Every replay is checked against the eager result of the same inputs, with
+eager work and synchronisations between replays, and the inputs change
+between replays (the graph must read the current contents)."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_epilogue_tile_amd as ge
+import workloads
+from gpu_helpers import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain_inputs(seed):
+    g = torch.Generator().manual_seed(seed)
+    M, K, N1, N2, N3 = 16, 1024, 2048, 1024, 512
+    x = torch.randn(M, K, generator=g).bfloat16()
+    W1 = (torch.randn(K, N1, generator=g) / 32).bfloat16()
+    b1 = (torch.randn(N1, generator=g) * 0.1).bfloat16()
+    R1 = torch.randn(M, N1, generator=g).bfloat16()
+    Wq = torch.randint(0, 256, (N1, N2 // 2), generator=g, dtype=torch.uint8)
+    sc = workloads.f32_to_bf16_bits(np.full((N1 // 128, N2), 0.01, np.float32))
+    W3 = (torch.randn(N2, N3, generator=g) / 32).bfloat16()
+    return [t.to(DEV) for t in (x, W1, b1, R1, Wq)] + [torch.from_numpy(sc.view(np.int16)).to(DEV).view(torch.bfloat16), W3.to(DEV)]
+
+
+def _prepare(x, W1, b1, R1, Wp, sc, W3, h, y, z):
+    # h = gelu(x W1 + b1) + R1 ; y = h deq(Wq) ; z = silu(y W3)
+    return [ge.prepare_gemm_epilogue(x, W1, out=h, bias=b1, R=R1, act="gelu_tanh"),
+            ge.prepare_w4_gemm(h, Wp, sc, out=y, prepacked=True),
+            ge.prepare_gemm_epilogue(y, W3, out=z, act="silu")]
+
+
+def test_decode_chain_graph_replays_match_eager():
+    x, W1, b1, R1, Wq, sc, W3 = _chain_inputs(1)
+    Wp = ge.w4_prepack(Wq)
+    M, N1, N2, N3 = x.shape[0], W1.shape[1], sc.shape[1], W3.shape[1]
+    bufs_e = [torch.empty(M, n, dtype=torch.bfloat16, device=DEV) for n in (N1, N2, N3)]
+    bufs_g = [torch.empty(M, n, dtype=torch.bfloat16, device=DEV) for n in (N1, N2, N3)]
+    eager = _prepare(x, W1, b1, R1, Wp, sc, W3, *bufs_e)
+    graph_calls = _prepare(x, W1, b1, R1, Wp, sc, W3, *bufs_g)
+    for f in eager + graph_calls:   # plans and kernels set up before capture
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in graph_calls:
+            f.with_stream()()
+    for rep in range(4):
+        x.copy_(_chain_inputs(100 + rep)[0])   # new activations each step
+        for f in eager:
+            f()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for be, bg in zip(bufs_e, bufs_g):
+            assert torch.equal(be, bg), f"replay {rep} differs from the eager chain"
+        assert torch.isfinite(bufs_g[2].float()).all()
