@@ -12,19 +12,29 @@ namespace {
 // ---------------------------------------------------------------------------
 // int4 weights (prepacked), M > 16: 128 x 128 tiles, fp16 MFMA.
 //
-// (code - z) * s has at most 3 + 8 significant bits, so the dequantised
-// weight is exact in fp16 (for scales with |8 s| in the fp16 normal range);
-// the bf16 activations convert to fp16 exactly (for |x| in the fp16 range).
-// The products are then exact in fp32 and no per-group rescaling of the
-// accumulators is needed.  Dequant per pair of codes: the codes are OR-ed into
-// the mantissa of fp16 1024 (giving 1024 + c), then a packed subtract of
-// 1024 + z and a packed multiply by s (exact for z = 8).  Scale groups of
-// 128 rows.
+// (c - z) * s with z = 8 has at most 3 + 8 significant bits, so the
+// dequantised weight is exact in fp16 (scales in the fp16 normal range); bf16
+// activations convert to fp16 exactly (|x| in the fp16 range).  The products
+// are then exact in fp32 and the accumulators need no per-group rescaling.
 //
-// A: direct loads into 4 LDS stages of 32 k, as in the bf16 tile kernel.
-// B: per 128-row group, the workgroup's 8 column tiles (8 KB, lane-major as
-//    prepacked) go to one of two LDS group buffers by direct loads; each wave
-//    reads its 4 tiles' 16 bytes per lane once per group.
+// The conversions are shared by the workgroup: every 32-deep stage, each of
+// the 256 threads converts 16 activations (8 k of two rows) to fp16 and
+// dequantises 16 weight codes (one lane in each of two prepacked 16-column
+// tiles) and writes them to LDS in MFMA fragment order, so every element is
+// converted once per workgroup instead of once per wave that uses it.
+//
+// Pipeline, per stage s (unrolled by 8 = two 128-row scale groups): raw
+// activations of stage s + 6 and (every fourth stage) the raw codes and
+// scales of the group after next go straight to LDS by direct loads (their
+// waits are counted by hand); stage s + 2 is converted from the raw buffers
+// into LDS buffer (s + 2) % 2; the fragments of stage s + 1 are read from
+// buffer (s + 1) % 2; the 16 MFMAs of stage s run on the fragments read one
+// stage earlier.  The side work is spread between the MFMAs; one barrier per
+// stage.
+//
+// Dequant per pair of codes: the codes are OR-ed into the mantissa of fp16
+// 1024 (giving 1024 + c), then a packed subtract of 1024 + z and a packed
+// multiply by s.
 // ---------------------------------------------------------------------------
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -34,23 +44,17 @@ __device__ __forceinline__ void mfma_f16_acc(f32x4 &acc, const f16x8 &a, const f
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-// bf16 x8 -> fp16 x8 (exact for values in the fp16 range)
-__device__ __forceinline__ f16x8 bf16x8_to_f16x8(const bf16x8 &x) {
-    const u32x4 w = __builtin_bit_cast(u32x4, x);
+// 8 bf16 (one u32x4) -> 8 fp16 (exact for values in the fp16 range)
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 &w) {
     u32x4 r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float lo = bf16lo(w[q]), hi = bf16hi(w[q]);
-        r[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-    }
-    return __builtin_bit_cast(f16x8, r);
+    for (int q = 0; q < 4; ++q)
+        r[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(w[q]), bf16hi(w[q])));
+    return r;
 }
 
-// one packed dword of 8 codes -> fp16 B fragment (k in order), (c - z) * s:
-// (1024 + c) - (1024 + z) is an exact small integer; with z = 8 it has at
-// most 3 significant bits, so its product with a bf16 scale (8 bits) is exact
-// in fp16.  Other zero points may round the product by half an fp16 ulp.
-__device__ __forceinline__ f16x8 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) {
+// one packed dword of 8 codes -> 8 fp16 weights (k in order), (c - z) * s
+__device__ __forceinline__ u32x4 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) {
     u32x4 r;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -58,20 +62,37 @@ __device__ __forceinline__ f16x8 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) 
         const f16x2 v = (__builtin_bit_cast(f16x2, t) - z2) * s2;
         r[q] = __builtin_bit_cast(uint32_t, v);
     }
-    return __builtin_bit_cast(f16x8, r);
+    return r;
 }
 
 constexpr int W4_BM = 128, W4_BN = 128, W4_MT = 4, W4_NT = 4;
-constexpr int W4_A_STAGE = W4_BM * T_BK * 2;        // 8 KB
-constexpr int W4_A_INSTR = W4_A_STAGE / 1024 / 4;   // 2 per wave per stage
-constexpr int W4_B_GROUP = (W4_BN / 16) * 1024;     // 8 KB: 8 tiles x 64 lanes x 16 B
-constexpr int W4_B_INSTR = W4_B_GROUP / 1024 / 4;   // 2 per wave per group
-constexpr int W4_B_BASE = T_NS * W4_A_STAGE;        // 32 KB
-constexpr int W4_S_BASE = W4_B_BASE + 2 * W4_B_GROUP;  // scales: 2 group buffers x 4 waves x 1 KB
-constexpr int W4_S_GROUP = 4 * 1024;
-constexpr int W4_LDS = W4_S_BASE + 2 * W4_S_GROUP;  // 56 KB
+constexpr int W4_UNROLL = 8;                   // stages per loop trip (ring sizes divide it)
+constexpr int W4_AD = 6;                       // activation loads run this many stages ahead
+// LDS (bytes): raw bf16 activations, ring of 8 stages ([128][32], natural order); raw codes of two
+// groups (prepacked blocks of the 8 tiles); raw scales of two groups (one 1 KB slot per wave, the
+// wave's 32 columns in its first 64 bytes); converted fp16 A and B of two stages (fragment order)
+constexpr int W4_RAWA = 0, W4_RAWA_STAGE = W4_BM * 64;
+constexpr int W4_RAWB = W4_RAWA + W4_UNROLL * W4_RAWA_STAGE, W4_RAWB_GROUP = (W4_BN / 16) * 1024;
+constexpr int W4_RAWS = W4_RAWB + 2 * W4_RAWB_GROUP, W4_RAWS_GROUP = 4 * 1024;
+constexpr int W4_A16 = W4_RAWS + 2 * W4_RAWS_GROUP, W4_A16_STAGE = W4_BM * 64;
+constexpr int W4_B16 = W4_A16 + 2 * W4_A16_STAGE, W4_B16_STAGE = (W4_BN / 16) * 1024;
+constexpr int W4_LDS = W4_B16 + 2 * W4_B16_STAGE;  // 120 KB
 
-__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS)))
+// direct loads issued by each wave: 2 per stage (activations), 3 per group (codes, scales)
+constexpr int W4_LA = 2, W4_LB = 3;
+static_assert(W4_LA * 4 * 64 * 16 == W4_RAWA_STAGE, "four waves load one activation stage");
+// loads a wave may still have in flight at the top of stage u (mod 8) when everything issued up to
+// stage u - 4 must have landed: the activations of stages u-3 .. u-1 and the group loads among them
+// (issued at stages = 2 mod 4)
+constexpr int w4_inflight(int u) {
+    int n = 3 * W4_LA;
+    for (int k = 1; k <= 3; ++k)
+        if (((u - k) % 4 + 4) % 4 == 2) n += W4_LB;
+    return n;
+}
+static_assert(w4_inflight(0) == w4_inflight(1) && w4_inflight(1) == w4_inflight(3), "one group load among three stages");
+
+__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(1, 1)))
 void tile_w4_kernel(Problem p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(AS3 void *)smem;
@@ -90,60 +111,114 @@ void tile_w4_kernel(Problem p) {
     const int tm = first_m + (t % per_group) % gsize;
     const int tn = (t % per_group) / gsize;
     const int m0 = tm * W4_BM, n0 = tn * W4_BN;
-    const int ngroups = p.K / 128;
+    const int ngroups = p.K / 128, nst = p.K / T_BK;
 
-    // A direct loads: [128][32] per stage, 16 rows x 4 chunks per instruction
-    const int arow_l = lane >> 2;
-    const int achunk = (lane & 3) ^ ((arow_l >> 1) & 3);
-    uint32_t a_off[W4_A_INSTR];
+    // ---- direct loads (raw data into LDS) ----
+    // activations: wave w, instruction q -> rows 16 (2 w + q) + lane/4, 16-byte chunk lane % 4
+    const i32x4 rA = make_rsrc((const char *)p.A + (int64_t)m0 * p.lda * 2,
+                               ((int64_t)(p.M - 1 - m0) * p.lda + p.K) * 2);
+    uint32_t a_src[W4_LA];
 #pragma unroll
-    for (int q = 0; q < W4_A_INSTR; ++q)
-        a_off[q] = (uint32_t)(((wave * W4_A_INSTR + q) * 16 + arow_l) * p.lda * 2) + achunk * 16;
-    auto load_a = [&](int s) {
-        const int k0 = s * T_BK;
-        const i32x4 r = make_rsrc((const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2,
-                                  ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
-        const bool kin = k0 + achunk * 8 < p.K;
-        const uint32_t dst = lds0 + (s & (T_NS - 1)) * W4_A_STAGE + wave * W4_A_INSTR * 1024;
+    for (int q = 0; q < W4_LA; ++q) a_src[q] = (uint32_t)(((wave * W4_LA + q) * 16 + (lane >> 2)) * p.lda * 2 + (lane & 3) * 16);
+    auto load_a = [&](int d, int slot) {  // stage d (runtime) into ring slot d % 8 (compile-time)
+        const bool in = d < nst;
 #pragma unroll
-        for (int q = 0; q < W4_A_INSTR; ++q) load_lds16(r, dst + q * 1024, kin ? a_off[q] : OOB);
+        for (int q = 0; q < W4_LA; ++q)
+            load_lds16(rA, lds0 + W4_RAWA + slot * W4_RAWA_STAGE + (wave * W4_LA + q) * 1024,
+                       in ? a_src[q] + d * 64 : OOB);
     };
-    // B direct loads: group gi of the workgroup's 8 column tiles (1 KB per tile and group), and
-    // the group's bf16 scales: wave w brings columns n0 + 32w .. n0 + 32w + 31 (lanes 0..3; the
-    // other lanes read out of range and fill the rest of the wave's 1 KB slot with zeros).
-    const i32x4 rb = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
-    const i32x4 rs = make_rsrc(p.scales, ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2);
-    auto load_b = [&](int gi) {
-        const bool gin = gi < ngroups;
-        const uint32_t dst = lds0 + W4_B_BASE + (gi & 1) * W4_B_GROUP + wave * W4_B_INSTR * 1024;
+    // codes: wave w, instruction q -> tile 2 w + q (1 KB block of the group); scales: the wave's
+    // 32 columns (lanes 0..3; the other lanes read zeros into the rest of its 1 KB slot)
+    const i32x4 rB = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
+    const i32x4 rS = make_rsrc(p.scales, ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2);
+    auto load_b = [&](int g, int slot) {  // group g into ring slot g % 2
+        const bool in = g < ngroups;
 #pragma unroll
-        for (int q = 0; q < W4_B_INSTR; ++q) {
-            const int nt = n0 / 16 + wave * W4_B_INSTR + q;
-            const uint32_t off = (uint32_t)(((nt * ngroups + gi) * 64 + lane) * 16);
-            load_lds16(rb, dst + q * 1024, gin ? off : OOB);
+        for (int q = 0; q < 2; ++q) {
+            const int tt = wave * 2 + q;
+            load_lds16(rB, lds0 + W4_RAWB + slot * W4_RAWB_GROUP + tt * 1024,
+                       in ? (uint32_t)((((int64_t)(n0 / 16 + tt) * ngroups + g) * 64 + lane) * 16) : OOB);
         }
-        const uint32_t soff = (uint32_t)(((int64_t)gi * p.ld_s + n0 + wave * 32) * 2) + lane * 16;
-        load_lds16(rs, lds0 + W4_S_BASE + (gi & 1) * W4_S_GROUP + wave * 1024, gin && lane < 4 ? soff : OOB);
+        load_lds16(rS, lds0 + W4_RAWS + slot * W4_RAWS_GROUP + wave * 1024,
+                   in && lane < 4 ? (uint32_t)(((int64_t)g * p.ld_s + n0 + wave * 32) * 2) + lane * 16 : OOB);
     };
 
-    const int frow = lane & 15, fgrp = lane >> 4;
-    const int a_frag = swz_a(wm * 64 + frow, fgrp);
-    const uint32_t b_raw = W4_B_BASE + (wn * W4_NT) * 1024 + lane * 16;  // + group buffer
-
-    // fp16 scale pairs for this lane's 4 columns of one group (scale groups of 128 rows), from the
-    // group's LDS buffer: column c of the tile sits in wave c / 32's slot at byte 2 (c % 32)
-    auto scales_of = [&](int gb, f16x2 (&s2)[W4_NT]) {
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) {
-            const int c = (wn * W4_NT + j) * 16 + frow;
-            const uint16_t raw = *(const AS3 uint16_t *)(s3 + W4_S_BASE + gb * W4_S_GROUP + (c >> 5) * 1024 +
-                                                         (c & 31) * 2);
-            const _Float16 h = (_Float16)bf16_to_f32(raw);
-            s2[j] = f16x2{h, h};
-        }
-    };
+    // ---- per-thread conversion: activation chunk ca (8 k) of rows ra and ra + 64; code blocks
+    //      bi and bi + 256 (tile bi / 64, lane bi % 64) -- consecutive threads touch consecutive
+    //      16-byte LDS chunks, so every access is free of bank conflicts ----
+    const int ra = tid >> 2, ca = tid & 3;
+    const int a_src_lds = ra * 64 + ca * 16;
+    const int a_dst0 = swz_a(ra, ca), a_dst1 = swz_a(ra + 64, ca);
+    const int bi = tid;  // second block: bi + 256 (tile + 4, same lane)
+    const int sc_col = (bi >> 6) * 16 + (bi & 15);  // second block: sc_col + 64
     const _Float16 zh = (_Float16)(1024.0f + (float)p.zero_point);
     const f16x2 z2 = f16x2{zh, zh};
+    u32x4 craw[2];   // the two code blocks of the current group (read once per group)
+    f16x2 cs2[2];    // their scales
+    // conversion of one stage in 17 pieces, so that it can be spread between the MFMAs:
+    // piece 0 reads the raw activations (and at a group's first stage the codes and scales);
+    // pieces 1..8 convert one activation dword each (writing a 16-byte chunk after every
+    // fourth); pieces 9..16 dequantise one code pair each (writing a lane fragment after every
+    // fourth)
+    struct Raw {
+        u32x4 x[2];
+        u32x4 out;
+    };
+    auto convert_piece = [&](int dd, int k, Raw &r) {  // stage d, dd = d % 8 (compile-time)
+        const int buf = dd & 1, gs = (dd >> 2) & 1, q = dd & 3;
+        AS3 char *w3 = (AS3 char *)smem;
+        if (k == 0) {
+            r.x[0] = *(const AS3 u32x4 *)(s3 + W4_RAWA + dd * W4_RAWA_STAGE + a_src_lds);
+            r.x[1] = *(const AS3 u32x4 *)(s3 + W4_RAWA + dd * W4_RAWA_STAGE + a_src_lds + 64 * 64);
+            if (q == 0) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    craw[e] = *(const AS3 u32x4 *)(s3 + W4_RAWB + gs * W4_RAWB_GROUP + (bi + 256 * e) * 16);
+                    const int col = sc_col + 64 * e;
+                    const uint16_t sr =
+                        *(const AS3 uint16_t *)(s3 + W4_RAWS + gs * W4_RAWS_GROUP + (col >> 5) * 1024 + (col & 31) * 2);
+                    const _Float16 sh = (_Float16)bf16_to_f32(sr);
+                    cs2[e] = f16x2{sh, sh};
+                }
+            }
+        } else if (k <= 8) {
+            const int h = (k - 1) >> 2, w = (k - 1) & 3;  // activation row ra + 64 h, dword w
+            // (empty asm ties on the piece's input and output keep it between its two MFMAs)
+            uint32_t xin = r.x[h][w];
+            asm volatile("" : "+v"(xin));
+            uint32_t o = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(xin), bf16hi(xin)));
+            asm volatile("" : "+v"(o));
+            r.out[w] = o;
+            if (w == 3) *(AS3 u32x4 *)(w3 + W4_A16 + buf * W4_A16_STAGE + (h ? a_dst1 : a_dst0)) = r.out;
+        } else {
+            const int e = (k - 9) >> 2, w = (k - 9) & 3;  // code block e, pair w
+            uint32_t cin = craw[e][q];
+            asm volatile("" : "+v"(cin));
+            const uint32_t tt = ((cin >> (4 * w)) & 0x000f000fu) | 0x64006400u;  // fp16 1024 + c
+            uint32_t o = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, tt) - z2) * cs2[e]);
+            asm volatile("" : "+v"(o));
+            r.out[w] = o;
+            if (w == 3) *(AS3 u32x4 *)(w3 + W4_B16 + buf * W4_B16_STAGE + (bi + 256 * e) * 16) = r.out;
+        }
+    };
+    auto convert = [&](int dd) {
+        Raw r;
+#pragma unroll
+        for (int k = 0; k <= 16; ++k) convert_piece(dd, k, r);
+    };
+
+    // ---- fragments ----
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const int a_frag = W4_A16 + swz_a(wm * 64 + frow, fgrp);
+    const int b_frag = W4_B16 + (wn * W4_NT * 64 + lane) * 16;
+    f16x8 fa[2][W4_MT], fb[2][W4_NT];
+    auto read_frag = [&](int buf, int r) {  // read r of a stage in buffer buf: A and B fragments alternate
+        const int i = r >> 1;
+        if ((r & 1) == 0)
+            fa[buf][i] = *(const AS3 f16x8 *)(s3 + a_frag + buf * W4_A16_STAGE + i * 1024);
+        else
+            fb[buf][i] = *(const AS3 f16x8 *)(s3 + b_frag + buf * W4_B16_STAGE + i * 1024);
+    };
 
     f32x4 acc[W4_MT][W4_NT];
 #pragma unroll
@@ -157,63 +232,59 @@ void tile_w4_kernel(Problem p) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 #define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
-    constexpr int LA = W4_A_INSTR, LB = W4_B_INSTR + 1;  // per wave: A loads per stage, B + scale loads per group
 
-    // issue order: B(g0), A(0), A(1), A(2), A(3); then per stage s: A(s+4), and at the first stage
-    // of a group also B(next group).  Waits below count the loads issued after the ones needed.
-    load_b(0);
-#pragma unroll
-    for (int s = 0; s < T_NS; ++s) load_a(s);
-    GE_WAIT_VM(3 * LA);  // A(0) and B(0) landed
+    // prologue, in the order the loop would have issued it: activations of stage d at "stage" d - 6,
+    // group 0 at -6 and group 1 at -2 (after that stage's activations)
+    load_a(0, 0);
+    load_b(0, 0);
+    load_a(1, 1);
+    load_a(2, 2);
+    load_a(3, 3);
+    load_a(4, 4);
+    load_b(1, 1);
+    load_a(5, 5);
+    GE_WAIT_VM(4 * W4_LA + W4_LB);  // everything up to "stage" -5 (A0, B0, A1) landed
     lds_barrier();
+    convert(0);
+    convert(1);
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 2 * W4_MT; ++r) read_frag(0, r);
 
-    bf16x8 fa[2][W4_MT];
-    u32x4 braw[W4_NT], braw_n[W4_NT];  // this group's / the next group's packed codes
-    f16x2 sc2[W4_NT], sc2_n[W4_NT];
+    // main loop, stage s = s0 + u: wait for the loads of stage s - 4 and earlier, barrier, then the
+    // 16 MFMAs of stage s with, between them: the direct loads of stage s + 6 (and at u % 4 == 2 the
+    // group after next), the conversion of stage s + 2 and the fragment reads of stage s + 1
+    const int nsteps = (nst + W4_UNROLL - 1) / W4_UNROLL * W4_UNROLL;
+    for (int s0 = 0; s0 < nsteps; s0 += W4_UNROLL) {
 #pragma unroll
-    for (int i = 0; i < W4_MT; ++i) fa[0][i] = *(const AS3 bf16x8 *)(s3 + a_frag + i * 1024);
-#pragma unroll
-    for (int j = 0; j < W4_NT; ++j) braw[j] = *(const AS3 u32x4 *)(s3 + b_raw + j * 1024);
-    scales_of(0, sc2);
-
-    for (int gi = 0; gi < ngroups; ++gi) {
-        const int gb = gi & 1;
-#pragma unroll
-        for (int b = 0; b < T_NS; ++b) {
-            const int s = gi * T_NS + b;
-            // stage s+1 (and at b == 3 the next group's B) must have landed
-            if (b == 0) GE_WAIT_VM(2 * LA);
-            else if (b == 3) GE_WAIT_VM(2 * LA);
-            else GE_WAIT_VM(2 * LA + LB);
+        for (int u = 0; u < W4_UNROLL; ++u) {
+            const int s = s0 + u;
+            if ((u & 3) == 2)
+                GE_WAIT_VM(w4_inflight(2));
+            else
+                GE_WAIT_VM(w4_inflight(0));
             lds_barrier();
-            load_a(s + T_NS);
-            if (b == 0) load_b(gi + 1);
-            // next stage's fragments (the next group's raw B and scales at b == 3)
-            const int sn = (b + 1) & (T_NS - 1);
+            // side work after MFMA q: q = 0 direct loads and the raw reads of the conversion,
+            // q = 1..8 one fragment read each, q = 2..15 the conversion pieces (one or two each)
+            const int dd = (u + 2) & (W4_UNROLL - 1);
+            Raw raw;
 #pragma unroll
-            for (int i = 0; i < W4_MT; ++i)
-                fa[(b + 1) & 1][i] = *(const AS3 bf16x8 *)(s3 + a_frag + sn * W4_A_STAGE + i * 1024);
-            if (b == 3) {
+            for (int q = 0; q < W4_MT * W4_NT; ++q) {
+                const int i = q & (W4_MT - 1), j = q / W4_MT;
+                mfma_f16_acc(acc[i][j], fb[u & 1][j], fa[u & 1][i]);
+                asm volatile("" ::: "memory");
+                if (q == 0) {
+                    load_a(s + W4_AD, (u + W4_AD) & (W4_UNROLL - 1));
+                    // s0 is a multiple of 8, so the ring slots are compile-time
+                    if ((u & 3) == 2) load_b((s + 6) >> 2, ((u + 6) >> 2) & 1);
+                    convert_piece(dd, 0, raw);
+                }
+                if (q >= 1 && q <= 2 * W4_MT) read_frag((u + 1) & 1, q - 1);
 #pragma unroll
-                for (int j = 0; j < W4_NT; ++j)
-                    braw_n[j] = *(const AS3 u32x4 *)(s3 + b_raw + (gb ^ 1) * W4_B_GROUP + j * 1024);
-                scales_of(gb ^ 1, sc2_n);
+                for (int k = 1; k <= 16; ++k)
+                    if (q >= 2 && 2 + ((k - 1) * 14) / 16 == q) convert_piece(dd, k, raw);
+                asm volatile("" ::: "memory");
             }
-            // this stage
-            f16x8 ah[W4_MT];
-#pragma unroll
-            for (int i = 0; i < W4_MT; ++i) ah[i] = bf16x8_to_f16x8(fa[b & 1][i]);
-#pragma unroll
-            for (int j = 0; j < W4_NT; ++j) {
-                const f16x8 bh = dequant_w4_f16(braw[j][b], sc2[j], z2);
-#pragma unroll
-                for (int i = 0; i < W4_MT; ++i) mfma_f16_acc(acc[i][j], bh, ah[i]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < W4_NT; ++j) {
-            braw[j] = braw_n[j];
-            sc2[j] = sc2_n[j];
         }
     }
 #undef GE_WAIT_VM
@@ -261,7 +332,7 @@ bool tile_w4_supported(const Problem &p) {
     if ((p.N % W4_BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
     if (p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
     if (((int64_t)(p.M - 1) * p.lda + p.K) * 2 >= (1ll << 31)) return false;
-    if ((int64_t)p.K * p.N / 2 >= (1ll << 31) || (int64_t)p.K / 128 * p.ld_s * 2 >= (1ll << 31)) return false;
+    if ((int64_t)p.K * p.N / 2 >= (1ll << 31) || ((int64_t)(p.K / 128) * p.ld_s + p.N) * 2 >= (1ll << 31)) return false;
     return epi_ok(p);
 }
 
