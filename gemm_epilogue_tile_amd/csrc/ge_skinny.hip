@@ -29,6 +29,7 @@ namespace ge {
 namespace {
 
 constexpr int S_WAVES = 8;
+constexpr int SK_RING = 4;  // bf16 streaming: blocks in flight per wave
 constexpr int S_THREADS = 64 * S_WAVES;
 constexpr uint32_t OOB = 0x80000000u;
 
@@ -144,30 +145,41 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
         }
     };
 
-    u32x4 wcur[8], wnxt[8];
-    if (kb0 < kb1) load_w(kb0, wcur);
-    for (int kb = kb0; kb < kb1; ++kb) {
-        if (kb + 1 < kb1) load_w(kb + 1, wnxt);
-        bf16x8 x[MT];
-        load_x(kb, x);
-        // 8 rows x 8 columns -> 8 fragments (k-vectors of one column each)
+    // ring of SK_RING blocks: weights and activations of block kb + SK_RING - 1 are requested
+    // together while block kb is multiplied (loaded as a pair, so waiting for one block's
+    // activations never waits for a later block's weights); blocks past the wave's share read
+    // zeros and add nothing
+    u32x4 w[SK_RING][8];
+    bf16x8 xr[SK_RING][MT];
+    auto load_blk = [&](int kb, int slot) {
+        const bool in = kb < kb1;
+        load_w(in ? kb : nkb + 1, w[slot]);
+        load_x(in ? kb : nkb + 1, xr[slot]);
+    };
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-            u32x4 lo, hi;
+    for (int j = 0; j < SK_RING - 1; ++j) load_blk(kb0 + j, j);
+    for (int kb = kb0; kb < kb1; kb += SK_RING) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                lo[q] = pack_lo(wcur[2 * q][dw], wcur[2 * q + 1][dw]);
-                hi[q] = pack_hi(wcur[2 * q][dw], wcur[2 * q + 1][dw]);
-            }
-            const bf16x8 f0 = __builtin_bit_cast(bf16x8, lo), f1 = __builtin_bit_cast(bf16x8, hi);
+        for (int u = 0; u < SK_RING; ++u) {
+            load_blk(kb + u + SK_RING - 1, (u + SK_RING - 1) % SK_RING);
+            const u32x4 (&wc)[8] = w[u];
+            // 8 rows x 8 columns -> 8 fragments (k-vectors of one column each)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                acc[mt][2 * dw] = mfma_bf16(x[mt], f0, acc[mt][2 * dw]);
-                acc[mt][2 * dw + 1] = mfma_bf16(x[mt], f1, acc[mt][2 * dw + 1]);
+            for (int dw = 0; dw < 4; ++dw) {
+                u32x4 lo, hi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    lo[q] = pack_lo(wc[2 * q][dw], wc[2 * q + 1][dw]);
+                    hi[q] = pack_hi(wc[2 * q][dw], wc[2 * q + 1][dw]);
+                }
+                const bf16x8 f0 = __builtin_bit_cast(bf16x8, lo), f1 = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt][2 * dw] = mfma_bf16(xr[u][mt], f0, acc[mt][2 * dw]);
+                    acc[mt][2 * dw + 1] = mfma_bf16(xr[u][mt], f1, acc[mt][2 * dw + 1]);
+                }
             }
         }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) wcur[r] = wnxt[r];
     }
 
     // partial tile -> LDS: lane (g, i) holds rows mt*16 + 4 g + e, columns 8 i + t
@@ -389,23 +401,18 @@ int bf16_chunks(int N, int cu_count) {
 template <int MT>
 void launch_bf16(const Problem &p, int nch, hipStream_t s) {
     const int blocks = (p.N + 8 * nch - 1) / (8 * nch);
-    switch (nch) {
-    case 14: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 14>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
-    case 12: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 12>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 8>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
-    default: hipLaunchKernelGGL((skinny_bf16_kernel<MT, 16>), dim3(blocks), dim3(S_THREADS), 0, s, p); break;
-    }
+    if (nch == 8)
+        hipLaunchKernelGGL((skinny_bf16_kernel<MT, 8>), dim3(blocks), dim3(S_THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((skinny_bf16_kernel<MT, 16>), dim3(blocks), dim3(S_THREADS), 0, s, p);
 }
 }  // namespace
 
 const char *skinny_kernel_name(const Problem &p, int cu_count) {
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
-    static const char *names[2][4] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_112col", "skinny_bf16_m16_96col",
-                                       "skinny_bf16_m16_64col"},
-                                      {"skinny_bf16_m32_128col", "skinny_bf16_m32_112col", "skinny_bf16_m32_96col",
-                                       "skinny_bf16_m32_64col"}};
-    const int c = bf16_chunks(p.N, cu_count);
-    return names[p.M > 16][c == 16 ? 0 : c == 14 ? 1 : c == 12 ? 2 : 3];
+    static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
+                                      {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
+    return names[p.M > 16][bf16_chunks(p.N, cu_count) == 16 ? 0 : 1];
 }
 
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
