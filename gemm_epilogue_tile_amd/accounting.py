@@ -54,10 +54,10 @@ def work(w) -> dict:
         fused = x_b + 2 * w_b + out_b
         # gate GEMM, up GEMM, sigmoid(g), g * s, h * u
         unfused = 2 * (x_b + w_b + out_b) + 2 * out_b + 3 * out_b + 3 * out_b
-    elif w.kind == "w4":
+    elif w.kind in ("w4", "w8"):
         flops = 2.0 * M * N * K
         x_b = M * K * 2
-        wq_b = K * N // 2
+        wq_b = K * N // 2 if w.kind == "w4" else K * N
         s_b = (K // w.group) * N * 2
         fused = x_b + wq_b + s_b + epi_in + out_b
         # dequant writes bf16 W; the GEMM reads it back

@@ -70,6 +70,8 @@ def _load():
             lib.oracle_w4_unpack.restype = I
             lib.oracle_w4_dequant.argtypes = [I, I, P, P, I, L, I, I, P]
             lib.oracle_w4_dequant.restype = I
+            lib.oracle_w8_dequant.argtypes = [I, I, P, L, I, I, P, I, L, I, P]
+            lib.oracle_w8_dequant.restype = I
             lib.oracle_add_rmsnorm.argtypes = [I, I, P, I, P, I, P, I, D, P, P]
             lib.oracle_add_rmsnorm.restype = I
             lib.oracle_num_threads.argtypes = []
@@ -212,6 +214,33 @@ def w4_gemm(X, Wq, scales, N: int, dtype: str = "bf16", *, group=128, zero_point
                     act=act, R=R, r_dtype=dtype)
 
 
+W8_FORMATS = {"u8": 1, "fp8": 2}
+
+
+def w8_dequant(Wq, scales, fmt: str, *, group=128, zero_point=0, s_dtype="bf16") -> np.ndarray:
+    """Exact fp64 weights of 8-bit codes Wq [K, N]: (q - zero_point) * s (u8) or
+    e4m3(q) * s (fp8), s = scales[k // group][n]."""
+    lib = _load()
+    Wq = np.ascontiguousarray(Wq, dtype=np.uint8)
+    K, N = Wq.shape
+    scales = _as(scales, s_dtype)
+    if scales.shape != (K // group, N):
+        raise ValueError("scales must be [K/group, N]")
+    W = np.empty((K, N), dtype=np.float64)
+    _check(lib.oracle_w8_dequant(K, N, _ptr(Wq), N, W8_FORMATS[fmt], int(zero_point), _ptr(scales),
+                                 _DT[s_dtype], N, group, _ptr(W)), "w8 dequant")
+    return W
+
+
+def w8_gemm(X, Wq, scales, fmt: str, dtype: str = "bf16", *, group=128, zero_point=0, alpha=1.0, beta=0.0,
+            C=None, bias=None, act="none", R=None, s_dtype="bf16") -> np.ndarray:
+    """8-bit weight path: dequant pass, GEMM pass, then the epilogue passes."""
+    W = w8_dequant(Wq, scales, fmt, group=group, zero_point=zero_point, s_dtype=s_dtype)
+    acc = gemm(X, W, dtype, "f64")
+    return epilogue(acc, alpha=alpha, beta=beta, C=C, c_dtype=dtype, bias=bias, bias_dtype=dtype,
+                    act=act, R=R, r_dtype=dtype)
+
+
 def add_rmsnorm(a, x, w, dtype: str = "bf16", eps: float = 1e-6):
     """Residual add then RMSNorm per row: returns (resid, normed) in fp64."""
     lib = _load()
@@ -246,4 +275,8 @@ def reference(inputs: dict, rows=None) -> np.ndarray:
                        group=inputs["group"], zero_point=inputs["zero_point"],
                        alpha=inputs["alpha"], beta=inputs["beta"], C=sel("C"),
                        bias=inputs.get("bias"), act=inputs["act"], R=sel("R"))
+    if kind == "w8":
+        return w8_gemm(sel("X"), inputs["Wq"], inputs["scales"], inputs["fmt"], dt, group=inputs["group"],
+                       zero_point=inputs["zero_point"], alpha=inputs["alpha"], beta=inputs["beta"],
+                       C=sel("C"), bias=inputs.get("bias"), act=inputs["act"], R=sel("R"))
     raise ValueError(kind)

@@ -208,6 +208,46 @@ int oracle_w4_dequant(int K, int N, const uint8_t *codes, const void *scales, in
 }
 
 /*
+ * 8-bit weights (one code per byte, W stored [K, N] like dense B), the wider
+ * formats next to the pages' int4 loader ("Fusion Thinking", Pattern 3: codes
+ * dequantised with a per-group scale before the product):
+ *   fmt 1, unsigned 8-bit integer:  W[k][n] = (q - zero_point) * s[k / group][n]
+ *   fmt 2, OCP fp8 E4M3 ("fn": no infinities; S.1111.111 is NaN):
+ *          W[k][n] = value(q) * s[k / group][n], where for sign bit S, exponent
+ *          field E (4 bits, bias 7) and mantissa field F (3 bits)
+ *            E = 0:  (-1)^S * 2^-6 * F / 8         (subnormal)
+ *            E > 0:  (-1)^S * 2^(E - 7) * (1 + F / 8)
+ * Exact in fp64.
+ */
+static double or_fp8_e4m3(uint8_t q)
+{
+    const int sign = q >> 7, e = (q >> 3) & 15, f = q & 7;
+    double v;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)f / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+int oracle_w8_dequant(int K, int N, const uint8_t *Wq, int64_t ldq, int fmt, int zero_point,
+                      const void *scales, int s_dtype, int64_t lds, int group, double *W)
+{
+    if (group <= 0 || K % group || !or_dtype_ok(s_dtype) || (fmt != 1 && fmt != 2))
+        return -1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t q = Wq[k * ldq + n];
+            const double s = or_load(scales, s_dtype, (k / group) * lds + n);
+            const double v = fmt == 1 ? (double)q - (double)zero_point : or_fp8_e4m3(q);
+            W[k * N + n] = v * s;
+        }
+    return 0;
+}
+
+/*
  * Fused residual add + RMSNorm reference, one row at a time:
  *   r = a + x                  (stored to resid)
  *   rrms = 1 / sqrt(sum(r^2) / N + eps)

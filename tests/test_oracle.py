@@ -313,3 +313,62 @@ def test_w4_reference_equals_dense_bf16_gemm_on_dequantised_weights():
     W = oracle.w4_dequant(inp["Wq"], inp["scales"], w.N)
     ref = _bf16_values(inp["X"]) @ W + _bf16_values(inp["bias"])[None, :]
     assert np.max(np.abs(got - ref)) <= 1e-12 * (1 + np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# 8-bit weights: unsigned integer codes with a zero point, and OCP fp8 E4M3
+# ---------------------------------------------------------------------------
+
+def test_fp8_e4m3_decoder_matches_torch_for_every_code():
+    # torch's float8_e4m3fn is an independent implementation of the same format
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    W = oracle.w8_dequant(codes, np.ones((1, 256)), "fp8", group=1, s_dtype="f64")[0]
+    ref = torch.from_numpy(codes.reshape(-1).copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(W), np.isnan(ref))
+    assert np.array_equal(W[~np.isnan(W)], ref[~np.isnan(ref)])
+    fin = ~np.isnan(W)
+    assert np.array_equal(np.signbit(W[fin]), np.signbit(ref[fin]))
+
+
+def test_fp8_e4m3_anchor_values():
+    # format facts: largest finite 448 (0x7E), smallest normal 2^-6 (0x08), smallest
+    # subnormal 2^-9 (0x01), 1.0 = 0x38, -2.0 = 0xC0, S.1111.111 is NaN, 0x80 is -0
+    codes = np.array([[0x7E, 0x08, 0x01, 0x38, 0xC0, 0x7F, 0xFF, 0x80, 0x00, 0x3C]], dtype=np.uint8)
+    W = oracle.w8_dequant(codes, np.ones((1, codes.shape[1])), "fp8", group=1, s_dtype="f64")[0]
+    assert list(W[:5]) == [448.0, 2.0 ** -6, 2.0 ** -9, 1.0, -2.0]
+    assert np.isnan(W[5]) and np.isnan(W[6])
+    assert W[7] == 0.0 and np.signbit(W[7]) and W[8] == 0.0 and not np.signbit(W[8])
+    assert W[9] == 1.5
+    # positive finite codes are strictly increasing in value
+    pos = oracle.w8_dequant(np.arange(0x7F, dtype=np.uint8).reshape(1, -1), np.ones((1, 0x7F)), "fp8",
+                            group=1, s_dtype="f64")[0]
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_u8_dequant_hand_computed():
+    codes = np.array([[0, 1, 127, 128, 129, 255]], dtype=np.uint8)
+    W = oracle.w8_dequant(codes, np.full((1, 6), 0.25), "u8", group=1, zero_point=128, s_dtype="f64")[0]
+    assert list(W) == [-32.0, -31.75, -0.25, 0.0, 0.25, 31.75]
+
+
+@pytest.mark.parametrize("fmt,zp", [("u8", 128), ("u8", 3), ("fp8", 0)])
+def test_w8_gemm_matches_numpy_on_independently_decoded_weights(fmt, zp):
+    torch = pytest.importorskip("torch")
+    K, N, M, group = 96, 40, 5, 32
+    r = np.random.default_rng(11)
+    Wq = (workloads.fp8_codes((K, N), wid=90, tid=1) if fmt == "fp8"
+          else r.integers(0, 256, (K, N), dtype=np.uint8))
+    s = r.uniform(0.01, 0.02, (K // group, N))
+    X = r.standard_normal((M, K))
+    if fmt == "fp8":
+        vals = torch.from_numpy(Wq.reshape(-1).copy()).view(torch.float8_e4m3fn).float().numpy()
+        vals = vals.astype(np.float64).reshape(K, N)
+    else:
+        vals = Wq.astype(np.float64) - zp
+    W = vals * np.repeat(s, group, axis=0)
+    ref = X @ W
+    got = oracle.w8_gemm(X, Wq, s, fmt, "f64", group=group, zero_point=zp, s_dtype="f64")
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # and the dequant itself is exact
+    assert np.array_equal(oracle.w8_dequant(Wq, s, fmt, group=group, zero_point=zp, s_dtype="f64"), W)

@@ -91,7 +91,7 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 class Workload:
     name: str
     wid: int
-    kind: str            # "generic" | "swiglu" | "w4"
+    kind: str            # "generic" | "swiglu" | "w4" | "w8"
     M: int
     N: int
     K: int
@@ -104,6 +104,7 @@ class Workload:
     R: bool = False
     group: int = 128
     zero_point: int = 8
+    fmt: str = "u4"      # weight code format: u4 (packed pairs), u8, fp8 (OCP E4M3)
 
     def with_shape(self, M=None, N=None, K=None) -> "Workload":
         return dataclasses.replace(self, M=M or self.M, N=N or self.N, K=K or self.K)
@@ -124,7 +125,22 @@ WORKLOADS = {
     # W4A16 GEMM + bias, two batch sizes
     "w4a16_m16": Workload("w4a16_m16", 4, "w4", 16, 8192, 8192, "bf16", bias=True),
     "w4a16_m512": Workload("w4a16_m512", 5, "w4", 512, 8192, 8192, "bf16", bias=True),
+    # 8-bit weight formats on the same decode shape (beyond the five configurations)
+    "w8a16_u8_m16": Workload("w8a16_u8_m16", 6, "w8", 16, 8192, 8192, "bf16", bias=True, zero_point=128,
+                             fmt="u8"),
+    "w8a16_fp8_m16": Workload("w8a16_fp8_m16", 7, "w8", 16, 8192, 8192, "bf16", bias=True, zero_point=0,
+                              fmt="fp8"),
 }
+
+
+def fp8_codes(shape, *, wid, tid, seed=0) -> np.ndarray:
+    """E4M3 codes with random sign, exponent field 0..9 (so |value| < 4, subnormals
+    included, never NaN) and mantissa field 0..7."""
+    r = _rng(wid, tid, seed)
+    sign = r.integers(0, 2, size=shape, dtype=np.uint8)
+    e = r.integers(0, 10, size=shape, dtype=np.uint8)
+    f = r.integers(0, 8, size=shape, dtype=np.uint8)
+    return ((sign << 7) | (e << 3) | f).astype(np.uint8)
 
 
 def make_inputs(w: Workload, seed: int = 0) -> dict:
@@ -166,6 +182,21 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         out["X"] = normal((M, K), 1.0, dt, wid=wid, tid=0, seed=seed)
         out["Wq"] = uniform_bytes((K, N // 2), wid=wid, tid=1, seed=seed)
         out["scales"] = uniform((K // w.group, N), 0.005, 0.02, "bf16", wid=wid, tid=2, seed=seed)
+        if w.bias:
+            out["bias"] = normal((N,), 0.1, dt, wid=wid, tid=3, seed=seed)
+        if w.R:
+            out["R"] = normal((M, N), 1.0, dt, wid=wid, tid=4, seed=seed)
+    elif w.kind == "w8":
+        if K % w.group:
+            raise ValueError("w8 workload needs K % group == 0")
+        out["X"] = normal((M, K), 1.0, dt, wid=wid, tid=0, seed=seed)
+        if w.fmt == "fp8":
+            out["Wq"] = fp8_codes((K, N), wid=wid, tid=1, seed=seed)
+            out["scales"] = uniform((K // w.group, N), 0.005, 0.02, "bf16", wid=wid, tid=2, seed=seed)
+        else:
+            out["Wq"] = uniform_bytes((K, N), wid=wid, tid=1, seed=seed)
+            out["scales"] = uniform((K // w.group, N), 0.0003, 0.0012, "bf16", wid=wid, tid=2, seed=seed)
+        out["fmt"] = w.fmt
         if w.bias:
             out["bias"] = normal((N,), 0.1, dt, wid=wid, tid=3, seed=seed)
         if w.R:
