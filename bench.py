@@ -9,7 +9,8 @@ give the kernel's average duration for the roofline object.
 
 Also reported (same JSON line): the deliberately unfused chain of the same
 workload, the other workloads (tiny fp32, SwiGLU dual GEMM, 16-row decode
-GEMM, W4A16 at M=16 and M=512) fused and unfused, and the CPU oracle timed
+GEMM, W4A16 at M=16 and M=512) fused and unfused, the next steps (fused
+residual add + RMSNorm, 8-bit weight formats), and the CPU oracle timed
 on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--main-only]
@@ -145,13 +146,13 @@ def build_calls(name, w, inp):
     acc = accounting.work(w)
     d = {k: _dev(v) for k, v in inp.items() if hasattr(v, "dtype")}
     hbm = acc["bound"] == "hbm"
-    wkey = {"generic": "B", "swiglu": None, "w4": "Wq"}[w.kind]
+    wkey = {"generic": "B", "swiglu": None, "w4": "Wq", "w8": "Wq"}[w.kind]
     set_bytes = acc["bytes"]
     nrot = _rotations(set_bytes, hbm)
     sets = [d]
     for _ in range(nrot - 1):
         c = dict(d)
-        for k in (["Wg", "Wu"] if w.kind == "swiglu" else [wkey] + (["scales"] if w.kind == "w4" else [])):
+        for k in (["Wg", "Wu"] if w.kind == "swiglu" else [wkey] + (["scales"] if w.kind in ("w4", "w8") else [])):
             c[k] = d[k].clone()
         sets.append(c)
     out_dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -168,6 +169,10 @@ def build_calls(name, w, inp):
         elif w.kind == "swiglu":
             f = ge.prepare_swiglu(s["X"], s["Wg"], s["Wu"], out=o)
             u = ge.prepare_swiglu(s["X"], s["Wg"], s["Wu"], out=o, unfused=True, workspace=ws)
+        elif w.kind == "w8":
+            kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o, fmt=w.fmt)
+            f = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], **kw)
+            u = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], unfused=True, workspace=ws, **kw)
         else:
             kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o)
             # fused path: weights converted once to the kernel layout (a load-time step)
@@ -205,6 +210,29 @@ def measure(name, steps, warmup):
     r["mfma_frac"] = r["tflops"] / peak
     r["hbm_frac"] = r["gbps"] / PEAK_HBM_GBPS
     return r
+
+
+def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
+    """Fused residual add + RMSNorm over M x N bf16 rows (HBM-bound: reads a, x, w; writes the new
+    residual and the normalised rows), rotating over enough row sets to defeat the Infinity Cache."""
+    import torch
+    import gemm_epilogue_tile_amd as ge
+    g = torch.Generator(device="cuda").manual_seed(5)
+    set_bytes = 4 * M * N * 2
+    nrot = _rotations(set_bytes, True)
+    sets = []
+    for _ in range(nrot):
+        a = torch.randn(M, N, device="cuda", generator=g).bfloat16()
+        x = torch.randn(M, N, device="cuda", generator=g).bfloat16()
+        sets.append((a, x, torch.empty_like(a), torch.empty_like(a)))
+    w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).bfloat16()
+    calls = [(lambda a=a, x=x, r=r, o=o: ge.add_rmsnorm(a, x, w, resid=r, out=o)) for a, x, r, o in sets]
+    tot, per = time_launches(calls, steps, warmup)
+    kern = sum(per) / len(per)
+    byts = set_bytes + N * 2
+    return {"kernel": "add_rmsnorm", "M": M, "N": N, "bytes": byts, "rotations": nrot,
+            "kernel_ms_avg": round(kern, 4), "gbps": round(byts / (kern * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (kern * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 # --------------------------------------------------------------------------
@@ -319,6 +347,14 @@ def main():
     }
     if others:
         line["workloads"] = others
+        # a measured step beyond the fused GEMM: residual add + RMSNorm, fused in one kernel
+        nxt = {"add_rmsnorm_2048x4096": measure_add_rmsnorm(max(a.steps // 2, 10), max(a.warmup // 2, 3))}
+        # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
+        for name in ["w8a16_u8_m16", "w8a16_fp8_m16"]:
+            r = measure(name, max(a.steps // 2, 10), max(a.warmup // 2, 3))
+            torch.cuda.empty_cache()
+            nxt[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
+        line["next"] = nxt
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -18,7 +18,7 @@ __all__ = [
     "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
-    "w4_prepack",
+    "w4_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +26,7 @@ lib_path = os.path.join(_HERE, "libgemm_epi.so")
 
 # status codes, types, layouts, activations, kinds, flags (mirror gemm_epi.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_ALIGN = range(6)
-F32, BF16, U4X2 = 0, 1, 2
+F32, BF16, U4X2, U8, FP8E4M3 = 0, 1, 2, 3, 4
 LAYOUT_KN, LAYOUT_NK = 0, 1
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
@@ -327,49 +327,64 @@ def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, stream=None):
     return out
 
 
-def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked=False):
+WEIGHT_FORMATS = {"u4": U4X2, "u8": U8, "fp8": FP8E4M3}
+_DEFAULT_ZP = {"u4": 8, "u8": 128, "fp8": 0}
+
+
+def _zp(fmt, zero_point):
+    if fmt not in WEIGHT_FORMATS:
+        raise ValueError(f"weight format {fmt!r} not in {sorted(WEIGHT_FORMATS)}")
+    return _DEFAULT_ZP[fmt] if zero_point is None else zero_point
+
+
+def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked=False,
+             fmt="u4"):
     M, K = X.shape
     N = scales.shape[1]
-    return plan(KIND_W4, M, N, K, a_type=BF16, b_type=U4X2, d_type=_dtype_code(out),
+    return plan(KIND_W4, M, N, K, a_type=BF16, b_type=WEIGHT_FORMATS[fmt], d_type=_dtype_code(out),
                 c_type=_dtype_code(C) if C is not None else None,
                 bias_type=_dtype_code(bias) if bias is not None else None,
                 r_type=_dtype_code(R) if R is not None else None, lda=_ld(X),
                 ldb=_ld(Wq) if Wq.dim() == 2 else 0,
                 ldc=_ld(C) if C is not None else 0, ldd=_ld(out), ldr=_ld(R) if R is not None else 0,
                 alpha=alpha, beta=beta, act=act, bias=bias is not None, C=C is not None and beta != 0.0,
-                R=R is not None, group=group, zero_point=zero_point, lo_first=lo_first, prepacked=prepacked)
+                R=R is not None, group=group, zero_point=_zp(fmt, zero_point), lo_first=lo_first,
+                prepacked=prepacked)
 
 
 def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none", group=128,
-            zero_point=8, lo_first=False, prepacked=False, out=None, out_dtype=None, stream=None):
-    """D = act(alpha * X @ deq(Wq, scales) + beta * C + bias) + R with int4 weights (fused).
+            zero_point=None, lo_first=False, prepacked=False, out=None, out_dtype=None, stream=None, fmt="u4"):
+    """D = act(alpha * X @ deq(Wq, scales) + beta * C + bias) + R with quantised weights (fused).
 
-    ``prepacked``: Wq came from ``w4_prepack`` (kernel-native layout, same byte count)."""
+    ``fmt``: "u4" (packed pairs, Wq [K, N/2]), "u8" or "fp8" (E4M3; Wq [K, N] bytes).
+    ``zero_point``: default 8 (u4), 128 (u8), 0 (fp8).
+    ``prepacked``: int4 Wq came from ``w4_prepack`` (kernel-native layout, same byte count)."""
     out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
     _check(lib().gemm_w4_run(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R),
                              _ptr(out), _stream(stream)), "gemm_w4_run")
     return out
 
 
 def w4_gemm_unfused(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
-                    group=128, zero_point=8, lo_first=False, prepacked=False, out=None, out_dtype=None,
-                    workspace=None, stream=None):
+                    group=128, zero_point=None, lo_first=False, prepacked=False, out=None, out_dtype=None,
+                    workspace=None, stream=None, fmt="u4"):
     out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
     ws = workspace if workspace is not None else _workspace(p, X.device)
     _check(lib().gemm_w4_run_unfused(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias),
                                      _ptr(R), _ptr(out), _ptr(ws), _stream(stream)), "gemm_w4_run_unfused")
     return out
 
 
-def w4_dequant(Wq, scales, *, M=1, group=128, zero_point=8, lo_first=False, out=None, stream=None):
-    """bf16 W[k][n] = rne((code - zero_point) * s[k // group][n]) (the unfused chain's first step)."""
+def w4_dequant(Wq, scales, *, M=1, group=128, zero_point=None, lo_first=False, out=None, stream=None, fmt="u4"):
+    """bf16 W[k][n] = rne(value(code) * s[k // group][n]) (the unfused chain's first step)."""
     torch = _torch()
-    K, N = Wq.shape[0], Wq.shape[1] * 2
+    K = Wq.shape[0]
+    N = Wq.shape[1] * 2 if fmt == "u4" else Wq.shape[1]
     out = out if out is not None else torch.empty((K, N), dtype=torch.bfloat16, device=Wq.device)
-    p = plan(KIND_W4, M, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), group=group,
-             zero_point=zero_point, lo_first=lo_first)
+    p = plan(KIND_W4, M, N, K, a_type=BF16, b_type=WEIGHT_FORMATS[fmt], d_type=BF16, ldb=_ld(Wq), group=group,
+             zero_point=_zp(fmt, zero_point), lo_first=lo_first)
     _check(lib().gemm_w4_dequant_run(p.handle, _ptr(Wq), _ptr(scales), _ptr(out), _stream(stream)),
            "gemm_w4_dequant_run")
     return out
@@ -417,9 +432,9 @@ def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, stream=None
 
 
 def prepare_w4_gemm(X, Wq, scales, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
-                    group=128, zero_point=8, lo_first=False, prepacked=False, unfused=False, workspace=None,
-                    stream=None) -> Prepared:
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked)
+                    group=128, zero_point=None, lo_first=False, prepacked=False, unfused=False, workspace=None,
+                    stream=None, fmt="u4") -> Prepared:
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
     ts = [X, Wq, scales, C, bias, R, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, X.device)

@@ -55,6 +55,10 @@ struct ge_plan {
 
 namespace {
 
+int32_t wfmt_of(const ge_desc &d) {
+    return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
+}
+
 // Fill a Problem from a plan and the run's pointers.
 Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void *B2, const void *scales,
                      const void *C, const void *bias, const void *R, void *D) {
@@ -93,6 +97,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     e.act = pl->kind == GE_KIND_SWIGLU ? GE_ACT_NONE : d.act;
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
+    p.wfmt = wfmt_of(d);
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
         if (d.flags & GE_FLAG_BIAS) f |= GE_FLAG_BIAS;
@@ -247,9 +252,23 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             return fail(GE_ERR_UNSUPPORTED, "swiglu takes no extra epilogue");
         pl.ldb = d.ldb ? d.ldb : d.N;
         if (pl.ldb < d.N) return fail(GE_ERR_INVALID_ARG, "ldb < N");
+    } else if (d.b_type == GE_U8 || d.b_type == GE_FP8E4M3) {
+        if (d.a_type != GE_BF16 || d.scale_type != GE_BF16)
+            return fail(GE_ERR_UNSUPPORTED, "8-bit weights need bf16 X and bf16 scales");
+        if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "8-bit weights are [K, N]");
+        if (d.flags & (GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED))
+            return fail(GE_ERR_INVALID_ARG, "nibble order and prepacking apply to int4 weights only");
+        if (pl.group != 32 && pl.group != 64 && pl.group != 128 && pl.group != 256)
+            return fail(GE_ERR_UNSUPPORTED, "group size %d not in {32, 64, 128, 256}", pl.group);
+        if (d.K % pl.group) return fail(GE_ERR_INVALID_ARG, "K %% group != 0");
+        if (d.b_type == GE_U8 ? (d.zero_point < 0 || d.zero_point > 255) : d.zero_point != 0)
+            return fail(GE_ERR_INVALID_ARG, "zero_point must be in [0, 255] for u8 weights and 0 for fp8");
+        pl.ldb = d.ldb ? d.ldb : d.N;
+        if (pl.ldb < d.N) return fail(GE_ERR_INVALID_ARG, "ldb < N bytes");
+        pl.ld_s = d.N;
     } else {
         if (d.a_type != GE_BF16 || d.b_type != GE_U4X2 || d.scale_type != GE_BF16)
-            return fail(GE_ERR_UNSUPPORTED, "w4 needs bf16 X, U4X2 weights and bf16 scales");
+            return fail(GE_ERR_UNSUPPORTED, "w4 needs bf16 X, U4X2 / U8 / FP8E4M3 weights and bf16 scales");
         if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "w4 weights are [K, N/2]");
         if (d.N % 2) return fail(GE_ERR_INVALID_ARG, "w4 needs an even N");
         if (pl.group != 32 && pl.group != 64 && pl.group != 128 && pl.group != 256)
@@ -344,7 +363,7 @@ ge_status gemm_w4_run(const ge_plan *pl, const void *X, const uint8_t *Wq, const
     if (st) return st;
     const ge_desc &d = pl->d;
     const size_t nX = ((size_t)(d.M - 1) * pl->lda + d.K) * 2;
-    const size_t nW = (size_t)(d.K - 1) * pl->ldb + d.N / 2;
+    const size_t nW = (size_t)(d.K - 1) * pl->ldb + (d.b_type == GE_U4X2 ? d.N / 2 : d.N);
     if ((st = check_alias(pl, X, nX, Wq, nW, C, R, D))) return st;
     const size_t nS = (size_t)(d.K / pl->group) * d.N * 2;
     const size_t nD = ((size_t)(d.M - 1) * pl->ldd + d.N) * type_size(d.d_type);
@@ -508,7 +527,7 @@ ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *W
     void *T1 = (char *)T0 + mnb;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_w4_dequant(d.K, d.N, Wq, pl->ldb, scales, pl->ld_s, pl->group, d.zero_point,
-                                     (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, s);
+                                     (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, s, wfmt_of(d));
     if (!e) {
         ge_plan gp = *pl;
         gp.kind = GE_KIND_GENERIC;
@@ -531,7 +550,8 @@ ge_status gemm_w4_dequant_run(const ge_plan *pl, const uint8_t *Wq, const void *
     if ((st = check_device(pl))) return st;
     const ge_desc &d = pl->d;
     return hip_status(launch_w4_dequant(d.K, d.N, Wq, pl->ldb, scales, pl->ld_s, pl->group, d.zero_point,
-                                        (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, (hipStream_t)stream),
+                                        (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, W, (hipStream_t)stream,
+                                        wfmt_of(d)),
                       "gemm_w4_dequant_run");
 }
 
@@ -540,6 +560,7 @@ ge_status gemm_w4_prepack(const ge_plan *pl, const uint8_t *Wq, uint8_t *Wp, voi
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
     if (!Wq || !Wp) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     const ge_desc &d = pl->d;
+    if (d.b_type != GE_U4X2) return fail(GE_ERR_UNSUPPORTED, "prepacking applies to int4 weights");
     if (d.N % 16 || d.K % 128) return fail(GE_ERR_UNSUPPORTED, "prepack needs N %% 16 == 0 and K %% 128 == 0");
     if ((uintptr_t)Wp & 15) return fail(GE_ERR_ALIGN, "Wp must be 16-byte aligned");
     const size_t nq = (size_t)(d.K - 1) * pl->ldb + d.N / 2, np = (size_t)d.K * d.N / 2;

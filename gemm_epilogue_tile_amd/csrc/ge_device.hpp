@@ -37,6 +37,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, b);
 }
 
+// One OCP fp8 E4M3 code (low byte of q) -> fp32, exactly (NaN codes give
+// NaN).  The gfx950 conversion instruction implements this format; checked
+// for all 256 codes against the format's definition.
+__device__ __forceinline__ float fp8e4m3_to_f32(uint32_t q) { return __builtin_amdgcn_cvt_f32_fp8((int)q, 0); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xffffu);
 }

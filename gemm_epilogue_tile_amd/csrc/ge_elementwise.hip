@@ -163,11 +163,12 @@ __global__ __launch_bounds__(EW_THREADS) void k_mul(int64_t count, const void *X
     });
 }
 
-// W[k][n] = bf16((code - zp) * s[k / group][n]); 8 columns (4 bytes) per step
+// W[k][n] = bf16((code - zp) * s[k / group][n]) (or bf16(e4m3(q) * s) for fp8
+// codes); 8 columns per step
 __global__ __launch_bounds__(EW_THREADS) void k_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq,
                                                           int64_t ldq, const uint16_t *scales,
                                                           int64_t lds, int32_t group, int32_t zp,
-                                                          int32_t lo_first, uint16_t *W) {
+                                                          int32_t lo_first, uint16_t *W, int32_t wfmt) {
     const bool al = aligned16(W) && ((N & 7) == 0) && aligned16(scales) && ((lds & 7) == 0);
     for_chunks(K, N, [&](int64_t k, int64_t n, bool vec) {
         float w[8];
@@ -175,7 +176,10 @@ __global__ __launch_bounds__(EW_THREADS) void k_w4_dequant(int32_t K, int32_t N,
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t c = n + i;
-            if (c < N) {
+            if (c < N && wfmt != WFMT_U4) {
+                const uint8_t q = Wq[k * ldq + c];
+                w[i] = (wfmt == WFMT_U8 ? (float)((int)q - zp) : fp8e4m3_to_f32(q)) * bf16_to_f32(srow[c]);
+            } else if (c < N) {
                 const uint8_t b = Wq[k * ldq + (c >> 1)];
                 const bool even = (c & 1) == 0;
                 const int code = (even != (lo_first != 0)) ? (b >> 4) : (b & 0xF);
@@ -301,9 +305,9 @@ hipError_t launch_ew_mul(int64_t count, const void *X, const void *Z, void *Y, h
 
 hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
                              const void *scales, int64_t ld_s, int32_t group, int32_t zero_point,
-                             int32_t lo_first, void *W, hipStream_t s) {
+                             int32_t lo_first, void *W, hipStream_t s, int32_t wfmt) {
     hipLaunchKernelGGL(k_w4_dequant, ew_grid(K, N), dim3(EW_THREADS), 0, s, K, N, Wq, ldq,
-                       (const uint16_t *)scales, ld_s, group, zero_point, lo_first, (uint16_t *)W);
+                       (const uint16_t *)scales, ld_s, group, zero_point, lo_first, (uint16_t *)W, wfmt);
     return hipGetLastError();
 }
 

@@ -11,9 +11,10 @@
 // LDS with the reduction index contiguous; four waves in a 2 x 2 grid, each
 // owning 32 x 32 outputs = 2 x 2 MFMA tiles of 16 x 16.
 //   bf16 operands -> v_mfma_f32_16x16x32_bf16
-//   fp32 operands, and int4 weights -> v_mfma_f32_16x16x4f32 (the int4 path
-//   dequantises exactly: (code - zero_point) * scale has at most 12
-//   significant bits, so it is exact in fp32, and so are bf16 activations).
+//   fp32 operands, and quantised weights -> v_mfma_f32_16x16x4f32 (the
+//   weights dequantise exactly: (code - zero_point) * scale has at most 16
+//   significant bits for 4- and 8-bit codes, fp8 value * scale at most 12,
+//   so they are exact in fp32, and so are bf16 activations).
 
 #include "ge_launch.hpp"
 
@@ -27,10 +28,14 @@ constexpr int G_THREADS = 256;
 __device__ __forceinline__ float load_b(const Problem &p, const void *B, int k, int n) {
     if (k >= p.K || n >= p.N) return 0.0f;
     if (p.mode == MODE_W4) {
+        const float s = bf16_to_f32(((const uint16_t *)p.scales)[(int64_t)(k / p.group) * p.ld_s + n]);
+        if (p.wfmt != WFMT_U4) {  // one code per byte
+            const uint8_t q = ((const uint8_t *)B)[(int64_t)k * p.ldb + n];
+            return (p.wfmt == WFMT_U8 ? (float)((int)q - p.zero_point) : fp8e4m3_to_f32(q)) * s;
+        }
         const uint8_t byte = ((const uint8_t *)B)[(int64_t)k * p.ldb + (n >> 1)];
         const bool even = (n & 1) == 0;
         const int code = (even != (p.lo_first != 0)) ? (byte >> 4) : (byte & 0xF);
-        const float s = bf16_to_f32(((const uint16_t *)p.scales)[(int64_t)(k / p.group) * p.ld_s + n]);
         return (float)(code - p.zero_point) * s;
     }
     const int64_t off = p.b_layout == GE_LAYOUT_KN ? (int64_t)k * p.ldb + n : (int64_t)n * p.ldb + k;

@@ -10,6 +10,7 @@
 namespace ge {
 
 enum Mode : int32_t { MODE_GENERIC = 0, MODE_SWIGLU = 1, MODE_W4 = 2 };
+enum WFmt : int32_t { WFMT_U4 = 0, WFMT_U8 = 1, WFMT_FP8 = 2 };
 
 // A fully described product + epilogue, pointers included.
 struct Problem {
@@ -24,6 +25,7 @@ struct Problem {
     int64_t lda, ldb, ld_s;
     int32_t group, zero_point, lo_first;
     int32_t w4_packed;  // B holds int4 weights in the prepacked layout
+    int32_t wfmt;       // MODE_W4 code format: WFMT_U4 (packed pairs), WFMT_U8, WFMT_FP8
     EpiArgs epi;
 };
 
@@ -68,7 +70,7 @@ hipError_t launch_ew_copy(int64_t M, int64_t N, const void *X, int32_t x_type, v
                           int32_t y_type, int64_t ldy, hipStream_t s);
 hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
                              const void *scales, int64_t ld_s, int32_t group, int32_t zero_point,
-                             int32_t lo_first, void *W, hipStream_t s);
+                             int32_t lo_first, void *W, hipStream_t s, int32_t wfmt = WFMT_U4);
 
 // Fused residual add + RMSNorm (bf16 rows).
 hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,

@@ -319,6 +319,124 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
     reduce_epilogue<MR, NC, W4_WAVES>(p, red, n0);
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit weights (u8 with a zero point, or OCP fp8 E4M3), raw [K, N] bytes
+// ---------------------------------------------------------------------------
+
+// Same data path as the bf16 kernel (a lane reads 8 rows of an 8-column chunk
+// per 32-deep block, 8 bytes per row, and transposes 8 x 8 in registers), with
+// each row's bytes decoded to bf16 first: u8 as q - zero point (exact), fp8 by
+// the hardware E4M3 conversion (exact).  The per-group scales multiply fp32
+// partial sums: a wave's blocks start on a group boundary and every group's
+// partial is folded into the total with the 8 scales of the lane's columns.
+template <int WF>
+__global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
+    constexpr int NC = 128, MR = 16;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int n0 = blockIdx.x * NC;
+
+    const int nkb = p.K / 32, gb = p.group / 32;  // blocks, blocks per scale group
+    const int per = ((nkb + S_WAVES - 1) / S_WAVES + gb - 1) / gb * gb;
+    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+
+    const bool nin = n0 + 8 * i < p.N;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)(p.K - 1) * p.ldb + p.N);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2);
+    const float zp = (float)p.zero_point;
+
+    f32x4 acc[8], part[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x2 w[SK_RING][8];
+    bf16x8 xr[SK_RING];
+    u32x4 sr[SK_RING];  // scales of the block's group (8 columns of the lane)
+    auto load_blk = [&](int kb, int slot) {  // blocks past the wave's share read zeros
+        const bool in = kb < kb1;
+        const int k = kb * 32 + 8 * g;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t off = (uint32_t)((int64_t)(k + r) * p.ldb + n0 + 8 * i);
+            w[slot][r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, in && nin ? off : OOB, 0, 0));
+        }
+        const uint32_t xo = (uint32_t)(((int64_t)i * p.lda + k) * 2);
+        xr[slot] = __builtin_bit_cast(bf16x8, bload16(rx, in && i < p.M ? xo : OOB));
+        const uint32_t so = (uint32_t)(((int64_t)(kb / gb) * p.ld_s + n0 + 8 * i) * 2);
+        sr[slot] = bload16(rs, in && nin ? so : OOB);
+    };
+    // 8 codes (one row, 8 columns) -> 8 bf16 in 4 dwords
+    auto decode8 = [&](const u32x2 &c) {
+        u32x4 r;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (WF == WFMT_FP8) {
+                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], false);
+                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], true);
+                r[2 * h] = pack_bf16x2(a[0], a[1]);
+                r[2 * h + 1] = pack_bf16x2(b[0], b[1]);
+            } else {
+                r[2 * h] = pack_bf16x2((float)(c[h] & 0xffu) - zp, (float)((c[h] >> 8) & 0xffu) - zp);
+                r[2 * h + 1] = pack_bf16x2((float)((c[h] >> 16) & 0xffu) - zp, (float)(c[h] >> 24) - zp);
+            }
+        }
+        return r;
+    };
+    auto fold = [&](const u32x4 &s8) {  // total += scale * partial, per column
+        float sc[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sc[2 * q] = bf16lo(s8[q]);
+            sc[2 * q + 1] = bf16hi(s8[q]);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(sc[t], part[t][e], acc[t][e]);
+            part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < SK_RING - 1; ++j) load_blk(kb0 + j, j);
+    for (int kb = kb0; kb < kb1; kb += SK_RING) {
+#pragma unroll
+        for (int u = 0; u < SK_RING; ++u) {
+            load_blk(kb + u + SK_RING - 1, (u + SK_RING - 1) % SK_RING);
+            u32x4 wc[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) wc[r] = decode8(w[u][r]);
+#pragma unroll
+            for (int dw = 0; dw < 4; ++dw) {
+                u32x4 lo, hi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    lo[q] = pack_lo(wc[2 * q][dw], wc[2 * q + 1][dw]);
+                    hi[q] = pack_hi(wc[2 * q][dw], wc[2 * q + 1][dw]);
+                }
+                part[2 * dw] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, lo), part[2 * dw]);
+                part[2 * dw + 1] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, hi), part[2 * dw + 1]);
+            }
+            // last block of a scale group: kb - kb0 is a multiple of SK_RING and kb0 of gb
+            if (((kb - kb0 + u + 1) % gb) == 0) fold(sr[u]);
+        }
+    }
+
+    // partial tile -> LDS: lane (g, i) holds rows 4 g + e, columns 8 i + t
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+        float *dst = &red[(wave * MR + 4 * g + e4) * NC + 8 * i];
+        *(f32x4 *)dst = f32x4{acc[0][e4], acc[1][e4], acc[2][e4], acc[3][e4]};
+        *(f32x4 *)(dst + 4) = f32x4{acc[4][e4], acc[5][e4], acc[6][e4], acc[7][e4]};
+    }
+    __syncthreads();
+    reduce_epilogue<MR, NC>(p, red, n0);
+}
+
 // Prepack: raw [K, N/2] bytes (two codes per byte, order per lo_first) ->
 // per (16-column tile, 128-row group): 64 lanes x 16 bytes; lane l, dword kb
 // holds the 8 codes of column 16 tile + l % 16 at k = 128 group + 32 kb +
@@ -370,6 +488,12 @@ bool skinny_supported(const Problem &p) {
     if (p.ab_type != GE_BF16 || p.M > 32) return false;
     if (p.mode == MODE_SWIGLU) return false;
     if (!al16(p.A) || (p.lda & 7) || (p.K & 7)) return false;
+    if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
+        // 8-bit codes: 8-byte weight loads, 16-byte scale loads, 32-bit offsets
+        return p.M <= 16 && (p.K % 32) == 0 && (p.N % 8) == 0 && ((uintptr_t)p.B & 7) == 0 && (p.ldb % 8) == 0 &&
+               al16(p.scales) && (p.ld_s % 8) == 0 && (int64_t)p.K * p.ldb < (1ll << 31) &&
+               ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
+    }
     if (p.mode == MODE_W4) {
         return p.w4_packed && p.M <= 16 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
                (p.group == 32 || p.group == 64 || p.group == 128);
@@ -409,6 +533,8 @@ void launch_bf16(const Problem &p, int nch, hipStream_t s) {
 }  // namespace
 
 const char *skinny_kernel_name(const Problem &p, int cu_count) {
+    if (p.mode == MODE_W4 && p.wfmt == WFMT_U8) return "skinny_u8_m16_128col";
+    if (p.mode == MODE_W4 && p.wfmt == WFMT_FP8) return "skinny_fp8_m16_128col";
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
@@ -417,6 +543,14 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
 
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
     if (!skinny_supported(p)) return hipErrorInvalidValue;
+    if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
+        const int blocks = (p.N + 127) / 128;
+        if (p.wfmt == WFMT_FP8)
+            hipLaunchKernelGGL(skinny_w8_kernel<WFMT_FP8>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL(skinny_w8_kernel<WFMT_U8>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+        return hipGetLastError();
+    }
     if (p.mode == MODE_W4) {
         constexpr int NTW = 2;
         const int blocks = (p.N / 16 + NTW - 1) / NTW;

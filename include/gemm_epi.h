@@ -68,7 +68,9 @@ typedef int32_t ge_status;
 /* storage types */
 #define GE_F32 0
 #define GE_BF16 1
-#define GE_U4X2 2 /* two 4-bit codes per byte (packed int4 weights) */
+#define GE_U4X2 2     /* two 4-bit codes per byte (packed int4 weights) */
+#define GE_U8 3       /* one unsigned 8-bit code per byte (weights, with a zero point) */
+#define GE_FP8E4M3 4  /* one OCP fp8 E4M3 ("fn": no infinities) value per byte (weights) */
 
 /* layout of the second operand */
 #define GE_LAYOUT_KN 0 /* B[k][n] at B[k * ldb + n] */
@@ -94,7 +96,8 @@ typedef int32_t ge_status;
 
 /*
  * Problem descriptor.  Unused fields must be zero.  dtype fields take
- * GE_F32 / GE_BF16 (b_type may be GE_U4X2 for GE_KIND_W4).
+ * GE_F32 / GE_BF16 (b_type may be GE_U4X2, GE_U8 or GE_FP8E4M3 for
+ * GE_KIND_W4, the weight-only quantised kind).
  *
  * Supported combinations:
  *   GENERIC  a_type == b_type in {F32, BF16}; c/bias/r/d types in {F32, BF16};
@@ -112,6 +115,12 @@ typedef int32_t ge_status;
  *            weights must lie in the fp16 range (|v| < 65504; below 2^-14
  *            they lose precision).  The weights are exact for zero_point 8;
  *            other zero points round them by at most 2^-12 relative.
+ *   W4 with 8-bit codes: b = U8 (W = (q - zero_point) * s, zero_point in
+ *            [0, 255]) or FP8E4M3 (W = e4m3(q) * s, zero_point 0; NaN codes
+ *            give NaN), Wq [K, N] bytes with ldb >= N, scales [K/group, N]
+ *            bf16, group in {32, 64, 128, 256}, K % group == 0; flags
+ *            NIBBLE_LO_FIRST and W4_PREPACKED are invalid.  The dequantised
+ *            weights are exact in the product (bf16 / fp32 arithmetic).
  */
 typedef struct ge_desc {
     int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */
@@ -166,7 +175,8 @@ GE_API ge_status gemm_swiglu_run(const ge_plan *plan, const void *X, const void 
                           void *D, void *stream);
 
 /*
- * Fused W4A16 GEMM: the packed int4 weights are unpacked and dequantised
+ * Fused GEMM on weight-only quantised weights (packed int4, or 8-bit codes:
+ * u8 with a zero point, fp8 E4M3): the codes are decoded and dequantised
  * inside the K loop and never exist in memory as bf16 (page "Fusion
  * Thinking", Pattern 3).  D = act(alpha * X.deq(Wq, s) + beta*C + bias) + R.
  */

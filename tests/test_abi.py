@@ -116,6 +116,18 @@ def _plan_status(kind=ge.KIND_GENERIC, **kw):
     (dict(b_type=2, K=100), ge.KIND_W4, ge.ERR_INVALID_ARG),
     (dict(b_type=2, group_size=48), ge.KIND_W4, ge.ERR_UNSUPPORTED),
     (dict(b_type=2, zero_point=16), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=3, zero_point=256), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=3, zero_point=-1), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=4), ge.KIND_W4, ge.ERR_INVALID_ARG),  # fp8 codes take no zero point (default is 8)
+    (dict(b_type=3, flags=8), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=4, zero_point=0, flags=16), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=3, b_layout=1), ge.KIND_W4, ge.ERR_UNSUPPORTED),
+    (dict(b_type=3, group_size=48), ge.KIND_W4, ge.ERR_UNSUPPORTED),
+    (dict(b_type=4, zero_point=0, K=96, group_size=64), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=3, ldb=63), ge.KIND_W4, ge.ERR_INVALID_ARG),
+    (dict(b_type=3, a_type=0), ge.KIND_W4, ge.ERR_UNSUPPORTED),
+    (dict(b_type=3), ge.KIND_GENERIC, ge.ERR_UNSUPPORTED),
+    (dict(b_type=4), ge.KIND_SWIGLU, ge.ERR_UNSUPPORTED),
     (dict(), 9, ge.ERR_INVALID_ARG),
 ])
 def test_plan_rejects_bad_descriptors_before_any_device_call(kw, kind, want):
@@ -124,7 +136,8 @@ def test_plan_rejects_bad_descriptors_before_any_device_call(kw, kind, want):
 
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
 @pytest.mark.parametrize("kind,kw", [(ge.KIND_GENERIC, {}), (ge.KIND_SWIGLU, {}),
-                                     (ge.KIND_W4, dict(b_type=2))])
+                                     (ge.KIND_W4, dict(b_type=2)), (ge.KIND_W4, dict(b_type=3, ldb=64)),
+                                     (ge.KIND_W4, dict(b_type=4, zero_point=0, group_size=32))])
 def test_valid_plan_without_gpu_reports_no_device(kind, kw):
     assert _plan_status(kind, **kw) == ge.ERR_NO_DEVICE
     assert b"device" in ge.lib().ge_last_error()

@@ -27,13 +27,17 @@ def _run(name, inp):
     if inp["kind"] == "swiglu":
         return ge.swiglu(d["X"], d["Wg"], d["Wu"])
     Wq = torch.from_numpy(inp["Wq"]).to(DEV)
+    if inp["kind"] == "w8":
+        return ge.w4_gemm(d["X"], Wq, d["scales"], bias=d.get("bias"), group=inp["group"],
+                          zero_point=inp["zero_point"], fmt=inp["fmt"])
     packed = True  # the fused path takes prepacked weights, as in the benchmark
     return ge.w4_gemm(d["X"], ge.w4_prepack(Wq) if packed else Wq, d["scales"], bias=d.get("bias"),
                       group=inp["group"], zero_point=inp["zero_point"], prepacked=packed)
 
 
 @pytest.mark.parametrize("name,nrows", [("tiny_fp32", 64), ("square_bf16", 24), ("swiglu_8b", 8),
-                                        ("skinny_decode", 16), ("w4a16_m16", 16), ("w4a16_m512", 24)])
+                                        ("skinny_decode", 16), ("w4a16_m16", 16), ("w4a16_m512", 24),
+                                        ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16)])
 def test_full_size_sampled_rows(name, nrows):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)

@@ -1,0 +1,142 @@
+"""GPU parity of the 8-bit weight formats (unsigned codes with a zero point,
+OCP fp8 E4M3) against the oracle: the streaming kernel (M <= 16), the general
+kernel (larger M, ragged N), every group size and epilogue term, bit-exact
+decoding through one-hot activation rows, the dequantisation kernel, and the
+unfused chain."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_epilogue_tile_amd as ge
+import oracle
+import workloads
+from gpu_helpers import DEV, TOL_BF16, assert_close, dev_inputs, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+BASE = {"u8": workloads.WORKLOADS["w8a16_u8_m16"], "fp8": workloads.WORKLOADS["w8a16_fp8_m16"]}
+FMTS = ["u8", "fp8"]
+
+
+def _w8(inp, **kw):
+    d = dev_inputs(inp)
+    return ge.w4_gemm(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"], bias=d.get("bias"),
+                      C=d.get("C"), R=d.get("R"), alpha=inp["alpha"], beta=inp["beta"], act=inp["act"],
+                      group=inp["group"], zero_point=inp["zero_point"], fmt=inp["fmt"], **kw)
+
+
+def _plan_kernel(fmt, M, N, K, **kw):
+    return ge.plan(ge.KIND_W4, M, N, K, b_type=ge.WEIGHT_FORMATS[fmt], bias=True,
+                   zero_point=128 if fmt == "u8" else 0, **kw).kernel
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (16, 256, 512), (16, 1000, 1024), (7, 4104, 2048),
+                                   (16, 8192, 1024), (3, 13, 128), (33, 264, 384), (128, 512, 1024),
+                                   (200, 136, 640)])
+def test_w8_ragged(fmt, M, N, K):
+    w = BASE[fmt].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N + K)
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} {M}x{N}x{K}")
+
+
+def test_w8_plans_pick_the_streaming_kernel_for_small_M():
+    assert _plan_kernel("u8", 16, 8192, 8192) == "skinny_u8_m16_128col"
+    assert _plan_kernel("fp8", 1, 4096, 1024) == "skinny_fp8_m16_128col"
+    assert not _plan_kernel("u8", 17, 8192, 8192).startswith("skinny")
+    assert not _plan_kernel("fp8", 16, 13, 128).startswith("skinny")  # N % 8 != 0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [16, 40])
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+def test_w8_group_sizes(fmt, M, group):
+    w = dataclasses.replace(BASE[fmt], M=M, N=384, K=1024, group=group)
+    inp = workloads.make_inputs(w, seed=group + M)
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} M{M} group {group}")
+
+
+@pytest.mark.parametrize("M", [16, 40])
+@pytest.mark.parametrize("zp", [0, 77, 255])
+def test_u8_zero_points(M, zp):
+    w = dataclasses.replace(BASE["u8"], M=M, N=256, K=512, zero_point=zp)
+    inp = workloads.make_inputs(w, seed=zp)
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"u8 M{M} zp {zp}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [9, 64])
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh", "silu"])
+def test_w8_every_epilogue_term(fmt, M, act):
+    w = dataclasses.replace(BASE[fmt], M=M, N=520, K=256, alpha=0.75, beta=-0.5, act=act, C=True, R=True)
+    inp = workloads.make_inputs(w, seed=M)
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} M{M} {act}")
+
+
+def _non_nan_codes(shape, wid):
+    q = workloads.uniform_bytes(shape, wid=wid, tid=1)
+    q[(q & 0x7F) == 0x7F] = 0  # E4M3 has NaN at S.1111.111 only; every other code is finite
+    return q
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [16, 48])
+def test_w8_decode_bit_exact_with_one_hot_rows(fmt, M):
+    # X row m is one-hot at k_m and scales are 2^-6, so D[m][n] = value(code) * 2^-6 exactly:
+    # at most 9 significant bits for u8, 4 for fp8 (subnormals and 448 included)
+    K, N, zp = 1024, 512, (128 if fmt == "u8" else 0)
+    Wq = _non_nan_codes((K, N), 97) if fmt == "fp8" else workloads.uniform_bytes((K, N), wid=97, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = np.arange(M) * 37 % K
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), ks] = 1.0
+    out = to_host(ge.w4_gemm(to_dev(workloads.f32_to_bf16_bits(X)), torch.from_numpy(Wq).to(DEV),
+                             to_dev(scales), zero_point=zp, fmt=fmt))
+    ones = workloads.f32_to_bf16_bits(np.ones((K // 128, N), np.float32))
+    want = oracle.w8_dequant(Wq, ones, fmt, zero_point=zp)[ks] * 2.0 ** -6
+    assert np.array_equal(out, want)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_dequant_kernel_bit_exact(fmt):
+    K, N = 512, 392
+    w = dataclasses.replace(BASE[fmt], M=1, N=N, K=K, group=64)
+    inp = workloads.make_inputs(w, seed=11)
+    W = ge.w4_dequant(torch.from_numpy(inp["Wq"]).to(DEV), to_dev(inp["scales"]), group=64,
+                      zero_point=inp["zero_point"], fmt=fmt)
+    # code values carry <= 9 significant bits and scales 8: every product is exact in fp32
+    exact = oracle.w8_dequant(inp["Wq"], inp["scales"], fmt, group=64, zero_point=inp["zero_point"])
+    want = workloads.f32_to_bf16_bits(exact.astype(np.float32))
+    got = W.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", [16, 96])
+def test_unfused_w8_matches_oracle(fmt, M):
+    w = BASE[fmt].with_shape(M=M, N=512, K=1024)
+    inp = workloads.make_inputs(w, seed=15)
+    d = dev_inputs(inp)
+    out = to_host(ge.w4_gemm_unfused(d["X"], torch.from_numpy(inp["Wq"]).to(DEV), d["scales"],
+                                     bias=d["bias"], zero_point=inp["zero_point"], fmt=fmt))
+    ref = oracle.reference(inp)
+    # the chain rounds every dequantised weight to bf16: random error per product <= 2^-9 |x w|
+    X = workloads.bf16_bits_to_f32(inp["X"]).astype(np.float64)
+    W = oracle.w8_dequant(inp["Wq"], inp["scales"], fmt, zero_point=inp["zero_point"])
+    spread = np.sqrt((X ** 2) @ (W ** 2))
+    tol = TOL_BF16 * (1 + np.abs(ref)) + 6 * 2.0 ** -9 * spread / np.sqrt(3) + 2 * 2.0 ** -9 * np.abs(ref)
+    assert np.all(np.abs(out - ref) <= tol)
+
+
+def test_w8_strided_and_misaligned_weights_take_the_general_kernel():
+    # ldb > N and a weight pointer off the 8-byte grid: same values as the packed call
+    w = BASE["u8"].with_shape(M=16, N=256, K=512)
+    inp = workloads.make_inputs(w, seed=21)
+    d = dev_inputs(inp)
+    Wq = torch.from_numpy(inp["Wq"]).to(DEV)
+    big = torch.zeros((512, 256 + 40), dtype=torch.uint8, device=DEV)
+    big[:, 3:259] = Wq
+    out = ge.w4_gemm(d["X"], big[:, 3:259], d["scales"], bias=d["bias"], zero_point=128, fmt="u8")
+    assert_close(out, oracle.reference(inp), TOL_BF16, "u8 strided misaligned")

@@ -186,6 +186,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
             out["bias"] = normal((N,), 0.1, dt, wid=wid, tid=3, seed=seed)
         if w.R:
             out["R"] = normal((M, N), 1.0, dt, wid=wid, tid=4, seed=seed)
+        if w.C:
+            out["C"] = normal((M, N), 1.0, dt, wid=wid, tid=5, seed=seed)
     elif w.kind == "w8":
         if K % w.group:
             raise ValueError("w8 workload needs K % group == 0")
@@ -201,6 +203,8 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
             out["bias"] = normal((N,), 0.1, dt, wid=wid, tid=3, seed=seed)
         if w.R:
             out["R"] = normal((M, N), 1.0, dt, wid=wid, tid=4, seed=seed)
+        if w.C:
+            out["C"] = normal((M, N), 1.0, dt, wid=wid, tid=5, seed=seed)
     else:
         raise ValueError(w.kind)
     return out
