@@ -33,7 +33,7 @@ KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
 FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED = 1, 2, 4, 8, 16
 
 EXPORTS = [
-    "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_run",
+    "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_plan_scratch_bytes", "gemm_epi_run",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
     "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack",
     "ge_add_rmsnorm_run",
@@ -85,6 +85,8 @@ def lib():
             L.gemm_epi_plan_destroy.restype = I
             L.gemm_epi_plan_kernel.argtypes = [P]
             L.gemm_epi_plan_kernel.restype = ctypes.c_char_p
+            L.gemm_epi_plan_scratch_bytes.argtypes = [P]
+            L.gemm_epi_plan_scratch_bytes.restype = ctypes.c_size_t
             L.gemm_epi_run.argtypes = [P] * 8
             L.gemm_epi_run.restype = I
             L.gemm_swiglu_run.argtypes = [P] * 6
@@ -179,6 +181,11 @@ class Plan:
     @property
     def kernel(self) -> str:
         return lib().gemm_epi_plan_kernel(self.handle).decode()
+
+    @property
+    def scratch_bytes(self) -> int:
+        """Device scratch the plan owns (a plan with scratch runs on one stream at a time)."""
+        return int(lib().gemm_epi_plan_scratch_bytes(self.handle))
 
     def workspace_bytes(self) -> int:
         n = ctypes.c_size_t()

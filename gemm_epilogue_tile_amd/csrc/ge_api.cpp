@@ -51,6 +51,9 @@ struct ge_plan {
     int64_t lda, ldb, ldc, ldd, ldr, ld_s;
     int32_t group;
     const char *kernel;  // fused kernel chosen for aligned inputs
+    int32_t split;       // K splits of the 8-bit streaming kernel (1: none)
+    void *scratch;       // its device scratch (split tiles, then counters), or NULL
+    size_t scratch_bytes;
 };
 
 namespace {
@@ -98,6 +101,13 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
     p.wfmt = wfmt_of(d);
+    if (pl->scratch && pl->split > 1) {
+        p.split = pl->split;
+        p.split_ws = (float *)pl->scratch;
+        p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - (size_t)((d.N + 127) / 128) * 4);
+    } else {
+        p.split = 1;
+    }
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
         if (d.flags & GE_FLAG_BIAS) f |= GE_FLAG_BIAS;
@@ -306,18 +316,51 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
                              (const void *)256, (const void *)256, (const void *)256, (void *)256);
     pl.kernel = fused_name(p, pl.cu_count);
 
+    // the 8-bit streaming kernel splits K over workgroups when the column
+    // blocks alone do not fill the GPU; its scratch belongs to the plan
+    pl.split = 1;
+    pl.scratch = nullptr;
+    pl.scratch_bytes = 0;
+    if (kind == GE_KIND_W4 && p.wfmt != WFMT_U4 && skinny_supported(p)) {
+        const int split = w8_split(p, pl.cu_count);
+        const int64_t bytes = w8_split_scratch_bytes(p, split);
+        if (split > 1 && bytes > 0) {
+            hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);
+            if (e == hipSuccess) e = hipMemset(pl.scratch, 0, (size_t)bytes);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+            if (e != hipSuccess) {
+                if (pl.scratch) (void)hipFree(pl.scratch);
+                return hip_status(e, "allocating the plan's split-K scratch");
+            }
+            pl.split = split;
+            pl.scratch_bytes = (size_t)bytes;
+        }
+    }
+
     ge_plan *h = new (std::nothrow) ge_plan(pl);
-    if (!h) return fail(GE_ERR_INVALID_ARG, "out of host memory");
+    if (!h) {
+        if (pl.scratch) (void)hipFree(pl.scratch);
+        return fail(GE_ERR_INVALID_ARG, "out of host memory");
+    }
     *out = h;
     return ok();
 }
 
 ge_status gemm_epi_plan_destroy(ge_plan *plan) {
+    if (plan && plan->scratch) {
+        int cur = -1;
+        const bool have = hipGetDevice(&cur) == hipSuccess;
+        if (have && cur != plan->device) (void)hipSetDevice(plan->device);
+        (void)hipFree(plan->scratch);
+        if (have && cur != plan->device) (void)hipSetDevice(cur);
+    }
     delete plan;
     return ok();
 }
 
 const char *gemm_epi_plan_kernel(const ge_plan *plan) { return plan ? plan->kernel : ""; }
+
+size_t gemm_epi_plan_scratch_bytes(const ge_plan *plan) { return plan ? plan->scratch_bytes : 0; }
 
 ge_status gemm_epi_run(const ge_plan *pl, const void *A, const void *B, const void *C, const void *bias,
                        const void *R, void *D, void *stream) {

@@ -26,6 +26,11 @@ struct Problem {
     int32_t group, zero_point, lo_first;
     int32_t w4_packed;  // B holds int4 weights in the prepacked layout
     int32_t wfmt;       // MODE_W4 code format: WFMT_U4 (packed pairs), WFMT_U8, WFMT_FP8
+    // cross-workgroup K split of the 8-bit streaming kernel (split > 1): fp32
+    // tiles and per-column-block arrival counters, owned by the plan
+    int32_t split;
+    float *split_ws;
+    uint32_t *split_cnt;
     EpiArgs epi;
 };
 
@@ -51,6 +56,10 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 bool skinny_supported(const Problem &p);
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);
 const char *skinny_kernel_name(const Problem &p, int cu_count);
+// K splits of the 8-bit streaming kernel and the scratch bytes they need
+// (tiles, then counters that must start at zero; the kernel re-arms them).
+int w8_split(const Problem &p, int cu_count);
+int64_t w8_split_scratch_bytes(const Problem &p, int split);
 
 // Elementwise kernels of the unfused chain.  All tensors dense [M, N] of the
 // given storage type unless noted.

@@ -51,19 +51,36 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return (x 
 // 8-column row chunks (16-byte accesses where aligned)
 // ---------------------------------------------------------------------------
 
+// 16-byte epilogue accesses are possible (bf16 tensors, 16-byte aligned rows)
+__device__ __forceinline__ bool epi_vec_ok(const Problem &p) {
+    const EpiArgs &e = p.epi;
+    return ((p.N & 7) == 0) && (((uintptr_t)e.D & 15) == 0) && ((e.ldd & 7) == 0) &&
+           (!(e.flags & GE_FLAG_RESIDUAL) || ((((uintptr_t)e.R & 15) == 0) && ((e.ldr & 7) == 0))) &&
+           (!(e.flags & GE_FLAG_C) || ((((uintptr_t)e.C & 15) == 0) && ((e.ldc & 7) == 0))) &&
+           (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) && e.d_type == GE_BF16 &&
+           (!(e.flags & GE_FLAG_RESIDUAL) || e.r_type == GE_BF16) && (!(e.flags & GE_FLAG_C) || e.c_type == GE_BF16) &&
+           (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
+}
+
+// epilogue of the 8 accumulators of row m, columns n .. n + 7 (clipped at N)
+template <int ACT>
+__device__ __forceinline__ void finish_chunk(const Problem &p, bool vec_ok, int m, int n, const float v[8]) {
+    const EpiArgs &e = p.epi;
+    if (vec_ok && n + 8 <= p.N) {
+        epi_row8<ACT>(e, v, m, n);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (n + q < p.N) store_elem(e.D, e.d_type, (int64_t)m * e.ldd + n + q, epi_scalar<ACT>(e, v[q], m, n + q));
+    }
+}
+
 // red: [NWV][MR][NC] fp32 partials in LDS (MR rows, NC columns), NWV waves
 template <int MR, int NC, int NWV = S_WAVES>
 __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *red, int n0) {
-    const EpiArgs &e = p.epi;
     constexpr int CH = NC / 8;  // 8-column chunks per row
-    const bool vec_ok = ((p.N & 7) == 0) && (((uintptr_t)e.D & 15) == 0) && ((e.ldd & 7) == 0) &&
-                        (!(e.flags & GE_FLAG_RESIDUAL) || ((((uintptr_t)e.R & 15) == 0) && ((e.ldr & 7) == 0))) &&
-                        (!(e.flags & GE_FLAG_C) || ((((uintptr_t)e.C & 15) == 0) && ((e.ldc & 7) == 0))) &&
-                        (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) &&
-                        e.d_type == GE_BF16 && (!(e.flags & GE_FLAG_RESIDUAL) || e.r_type == GE_BF16) &&
-                        (!(e.flags & GE_FLAG_C) || e.c_type == GE_BF16) &&
-                        (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
-    with_act(e.act, [&](auto ACTC) {
+    const bool vec_ok = epi_vec_ok(p);
+    with_act(p.epi.act, [&](auto ACTC) {
         constexpr int ACT = decltype(ACTC)::value;
         for (int item = threadIdx.x; item < MR * CH; item += 64 * NWV) {
             const int r = item / CH, c = item % CH;
@@ -82,13 +99,7 @@ __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *r
                     v[4 + q] += b[q];
                 }
             }
-            if (vec_ok && n + 8 <= p.N) {
-                epi_row8<ACT>(e, v, m, n);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (n + q < p.N) store_elem(e.D, e.d_type, (int64_t)m * e.ldd + n + q, epi_scalar<ACT>(e, v[q], m, n + q));
-            }
+            finish_chunk<ACT>(p, vec_ok, m, n, v);
         }
     });
 }
@@ -323,70 +334,142 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
 // 8-bit weights (u8 with a zero point, or OCP fp8 E4M3), raw [K, N] bytes
 // ---------------------------------------------------------------------------
 
-// Same data path as the bf16 kernel (a lane reads 8 rows of an 8-column chunk
-// per 32-deep block, 8 bytes per row, and transposes 8 x 8 in registers), with
-// each row's bytes decoded to bf16 first: u8 as q - zero point (exact), fp8 by
-// the hardware E4M3 conversion (exact).  The per-group scales multiply fp32
-// partial sums: a wave's blocks start on a group boundary and every group's
-// partial is folded into the total with the 8 scales of the lane's columns.
-template <int WF>
+// Cross-workgroup K split.  The S workgroups of one column block each reduce
+// their waves' partials, write the [MR, NC] fp32 tile to the plan's scratch
+// ([S][column blocks][MR][NC]) and count themselves in; the last to arrive
+// sums the S tiles in split order (so the result does not depend on arrival
+// order), runs the epilogue and re-arms the counter for the next launch.
+// Launches that share one scratch buffer must not overlap.
+//
+// Tiles and counters are accessed only with device-scope (agent) atomic
+// loads and stores, which the hardware keeps coherent across the XCDs' L2
+// caches per access, so no fence has to write back or invalidate whole L2
+// caches (fences made the split slower than no split at all).  Ordering:
+// every wave waits until its tile stores have completed before the barrier,
+// the counter increment follows the barrier, and the last workgroup's tile
+// loads are issued only after the increment has returned (barrier and LDS
+// flag in between).
+template <int MR, int NC, int NS, int NWV = S_WAVES>
+__device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const float *red, int n0, int cb, int ks,
+                                                      int ncb, int *s_last) {
+    constexpr int CH = NC / 8;
+    float *mine = p.split_ws + ((int64_t)ks * ncb + cb) * (MR * NC);
+    for (int item = threadIdx.x; item < MR * CH; item += 64 * NWV) {
+        const int r = item / CH, c = item % CH;
+        f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            a += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8];
+            b += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8 + 4];
+        }
+        float *dst = mine + r * NC + c * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __hip_atomic_store(dst + q, a[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 4 + q, b[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(p.split_cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = prev == (uint32_t)(NS - 1);
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    const bool vec_ok = epi_vec_ok(p);
+    with_act(p.epi.act, [&](auto ACTC) {
+        constexpr int ACT = decltype(ACTC)::value;
+        for (int item = threadIdx.x; item < MR * CH; item += 64 * NWV) {
+            const int r = item / CH, c = item % CH;
+            const int m = r, n = n0 + c * 8;
+            if (m >= p.M || n >= p.N) continue;
+            // all NS tiles requested at once, then summed in split order
+            float tl[NS][8];
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const float *t = p.split_ws + ((int64_t)q * ncb + cb) * (MR * NC) + r * NC + c * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tl[q][e] = __hip_atomic_load(t + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += tl[q][e];
+            finish_chunk<ACT>(p, vec_ok, m, n, v);
+        }
+    });
+    if (threadIdx.x == 0) __hip_atomic_store(p.split_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A lane reads, per 32-deep block, 8 consecutive rows of one 8-column chunk
+// (8 bytes per row).  Each byte is converted once to fp32 (u8: the code
+// itself, 0..255; fp8: the hardware E4M3 conversion, both exact) and pairs of
+// rows of one column are packed into bf16 (exact), which forms the MFMA B
+// fragments of 8 k values per column directly, with no transpose.  The u8
+// zero point z enters as -z * sum(x) over the group, from one extra MFMA per
+// block against a fragment of ones.  Per-group scales multiply the fp32
+// partial sums: a wave's blocks start on a group boundary and each group's
+// partial is folded into the total with the scales of the lane's 8 columns.
+// Grid: column blocks x NS K-splits; 8 waves per workgroup split its K range.
+template <int WF, int NS>
 __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
+    constexpr bool SPLIT = NS > 1;
     constexpr int NC = 128, MR = 16;
     __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    __shared__ int s_last;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int n0 = blockIdx.x * NC;
+    const int ncb = (int)gridDim.x / NS;
+    const int cb = (int)blockIdx.x % ncb;
+    const int ks = (int)blockIdx.x / ncb;
+    const int n0 = cb * NC;
 
     const int nkb = p.K / 32, gb = p.group / 32;  // blocks, blocks per scale group
-    const int per = ((nkb + S_WAVES - 1) / S_WAVES + gb - 1) / gb * gb;
-    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+    const int nvw = NS * S_WAVES;                 // waves sharing K
+    const int per = ((nkb + nvw - 1) / nvw + gb - 1) / gb * gb;
+    const int kb0 = (ks * S_WAVES + wave) * per, kb1 = min(nkb, kb0 + per);
 
     const bool nin = n0 + 8 * i < p.N;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)(p.K - 1) * p.ldb + p.N);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2);
+    // lane parts of the offsets (OOB for lanes past N or M); block parts are uniform
+    const uint32_t vw = nin ? (uint32_t)(8 * g * p.ldb + n0 + 8 * i) : OOB;
+    const uint32_t vx = i < p.M ? (uint32_t)((i * p.lda + 8 * g) * 2) : OOB;
+    const uint32_t vs = nin ? (uint32_t)((n0 + 8 * i) * 2) : OOB;
+    const uint32_t blk_w = (uint32_t)(32 * p.ldb);
     const float zp = (float)p.zero_point;
 
-    f32x4 acc[8], part[8];
+    f32x4 acc[8], part[8], xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x2 w[SK_RING][8];
     bf16x8 xr[SK_RING];
-    u32x4 sr[SK_RING];  // scales of the block's group (8 columns of the lane)
-    auto load_blk = [&](int kb, int slot) {  // blocks past the wave's share read zeros
+    u32x4 sr[SK_RING];
+    // Blocks past the wave's share read zeros: their lane offsets become OOB
+    // and their uniform offsets 0, so no sum wraps past 2^32 (every in-range
+    // sum stays below 2^31, every OOB one between 2^31 and 2^32).
+    auto load_blk = [&](int kb, int slot) {
         const bool in = kb < kb1;
-        const int k = kb * 32 + 8 * g;
+        const uint32_t so = in ? (uint32_t)kb * blk_w : 0u;
+        const uint32_t lw = in ? vw : OOB;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const uint32_t off = (uint32_t)((int64_t)(k + r) * p.ldb + n0 + 8 * i);
-            w[slot][r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, in && nin ? off : OOB, 0, 0));
-        }
-        const uint32_t xo = (uint32_t)(((int64_t)i * p.lda + k) * 2);
-        xr[slot] = __builtin_bit_cast(bf16x8, bload16(rx, in && i < p.M ? xo : OOB));
-        const uint32_t so = (uint32_t)(((int64_t)(kb / gb) * p.ld_s + n0 + 8 * i) * 2);
-        sr[slot] = bload16(rs, in && nin ? so : OOB);
+        for (int r = 0; r < 8; ++r)
+            w[slot][r] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, lw, so + (uint32_t)(r * p.ldb), 0));
+        xr[slot] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? vx : OOB, in ? (uint32_t)kb * 64u : 0u, 0));
+        sr[slot] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, in ? vs : OOB,
+                                                         in ? (uint32_t)((kb / gb) * p.ld_s * 2) : 0u, 0));
     };
-    // 8 codes (one row, 8 columns) -> 8 bf16 in 4 dwords
-    auto decode8 = [&](const u32x2 &c) {
-        u32x4 r;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if constexpr (WF == WFMT_FP8) {
-                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], false);
-                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[h], true);
-                r[2 * h] = pack_bf16x2(a[0], a[1]);
-                r[2 * h + 1] = pack_bf16x2(b[0], b[1]);
-            } else {
-                r[2 * h] = pack_bf16x2((float)(c[h] & 0xffu) - zp, (float)((c[h] >> 8) & 0xffu) - zp);
-                r[2 * h + 1] = pack_bf16x2((float)((c[h] >> 16) & 0xffu) - zp, (float)(c[h] >> 24) - zp);
-            }
-        }
-        return r;
-    };
-    auto fold = [&](const u32x4 &s8) {  // total += scale * partial, per column
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    auto fold = [&](const u32x4 &s8) {  // total += scale * (partial - z * sum x), per column
         float sc[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -396,9 +479,40 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(sc[t], part[t][e], acc[t][e]);
+            for (int e = 0; e < 4; ++e) {
+                const float v = WF == WFMT_U8 ? fmaf(-zp, xs[e], part[t][e]) : part[t][e];
+                acc[t][e] = fmaf(sc[t], v, acc[t][e]);
+            }
             part[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        xs = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // one block: bytes -> fp32 -> bf16 fragments (column t: rows 0..7), 8 MFMAs
+    auto consume = [&](int slot) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {  // columns 4 hh .. 4 hh + 3
+            float f[8][4];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const uint32_t c = w[slot][r][hh];
+                if constexpr (WF == WFMT_FP8) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+                    f[r][0] = lo[0], f[r][1] = lo[1], f[r][2] = hi[0], f[r][3] = hi[1];
+                } else {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) f[r][b] = (float)((c >> (8 * b)) & 0xffu);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                u32x4 fr;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) fr[q] = pack_bf16x2(f[2 * q][b], f[2 * q + 1][b]);
+                part[4 * hh + b] = mfma_bf16(xr[slot], __builtin_bit_cast(bf16x8, fr), part[4 * hh + b]);
+            }
+        }
+        if constexpr (WF == WFMT_U8) xs = mfma_bf16(xr[slot], ones, xs);
     };
 
 #pragma unroll
@@ -407,20 +521,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
 #pragma unroll
         for (int u = 0; u < SK_RING; ++u) {
             load_blk(kb + u + SK_RING - 1, (u + SK_RING - 1) % SK_RING);
-            u32x4 wc[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) wc[r] = decode8(w[u][r]);
-#pragma unroll
-            for (int dw = 0; dw < 4; ++dw) {
-                u32x4 lo, hi;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    lo[q] = pack_lo(wc[2 * q][dw], wc[2 * q + 1][dw]);
-                    hi[q] = pack_hi(wc[2 * q][dw], wc[2 * q + 1][dw]);
-                }
-                part[2 * dw] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, lo), part[2 * dw]);
-                part[2 * dw + 1] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, hi), part[2 * dw + 1]);
-            }
+            consume(u);
             // last block of a scale group: kb - kb0 is a multiple of SK_RING and kb0 of gb
             if (((kb - kb0 + u + 1) % gb) == 0) fold(sr[u]);
         }
@@ -434,7 +535,10 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
         *(f32x4 *)(dst + 4) = f32x4{acc[4][e4], acc[5][e4], acc[6][e4], acc[7][e4]};
     }
     __syncthreads();
-    reduce_epilogue<MR, NC>(p, red, n0);
+    if constexpr (SPLIT)
+        split_reduce_epilogue<MR, NC, NS>(p, red, n0, cb, ks, ncb, &s_last);
+    else
+        reduce_epilogue<MR, NC>(p, red, n0);
 }
 
 // Prepack: raw [K, N/2] bytes (two codes per byte, order per lo_first) ->
@@ -532,9 +636,32 @@ void launch_bf16(const Problem &p, int nch, hipStream_t s) {
 }
 }  // namespace
 
+// K splits of the 8-bit kernel: the fewest (a power of two, at most 8) that
+// give every CU a workgroup, while each wave keeps at least one scale group.
+int w8_split(const Problem &p, int cu_count) {
+    if (p.mode != MODE_W4 || p.wfmt == WFMT_U4) return 1;
+    const int ncb = (p.N + 127) / 128, nkb = p.K / 32, gb = p.group / 32;
+    int s = 1;
+    while (s < 8 && (int64_t)ncb * s < cu_count && nkb / (2 * s * S_WAVES) >= gb) s *= 2;
+    return s;
+}
+
+int64_t w8_split_scratch_bytes(const Problem &p, int split) {
+    if (split <= 1) return 0;
+    const int64_t ncb = (p.N + 127) / 128;
+    return split * ncb * 16 * 128 * 4 + ncb * 4;
+}
+
 const char *skinny_kernel_name(const Problem &p, int cu_count) {
-    if (p.mode == MODE_W4 && p.wfmt == WFMT_U8) return "skinny_u8_m16_128col";
-    if (p.mode == MODE_W4 && p.wfmt == WFMT_FP8) return "skinny_fp8_m16_128col";
+    if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
+        static const char *names[2][4] = {
+            {"skinny_u8_m16_128col", "skinny_u8_m16_128col_split2", "skinny_u8_m16_128col_split4",
+             "skinny_u8_m16_128col_split8"},
+            {"skinny_fp8_m16_128col", "skinny_fp8_m16_128col_split2", "skinny_fp8_m16_128col_split4",
+             "skinny_fp8_m16_128col_split8"}};
+        const int s = w8_split(p, cu_count);
+        return names[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
+    }
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
@@ -544,11 +671,25 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
     if (!skinny_supported(p)) return hipErrorInvalidValue;
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
-        const int blocks = (p.N + 127) / 128;
+        const int ncb = (p.N + 127) / 128;
+        const int ns = (p.split_ws && p.split_cnt) ? p.split : 1;
+        if (ns != 1 && ns != 2 && ns != 4 && ns != 8) return hipErrorInvalidValue;
+        const dim3 grid(ncb * ns);
+        auto go = [&](auto WFC) {
+            constexpr int W = decltype(WFC)::value;
+            if (ns == 8)
+                hipLaunchKernelGGL((skinny_w8_kernel<W, 8>), grid, dim3(S_THREADS), 0, s, p);
+            else if (ns == 4)
+                hipLaunchKernelGGL((skinny_w8_kernel<W, 4>), grid, dim3(S_THREADS), 0, s, p);
+            else if (ns == 2)
+                hipLaunchKernelGGL((skinny_w8_kernel<W, 2>), grid, dim3(S_THREADS), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_w8_kernel<W, 1>), grid, dim3(S_THREADS), 0, s, p);
+        };
         if (p.wfmt == WFMT_FP8)
-            hipLaunchKernelGGL(skinny_w8_kernel<WFMT_FP8>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+            go(std::integral_constant<int, WFMT_FP8>{});
         else
-            hipLaunchKernelGGL(skinny_w8_kernel<WFMT_U8>, dim3(blocks), dim3(S_THREADS), 0, s, p);
+            go(std::integral_constant<int, WFMT_U8>{});
         return hipGetLastError();
     }
     if (p.mode == MODE_W4) {

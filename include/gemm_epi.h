@@ -39,7 +39,10 @@
  *     available from ge_last_error().
  *
  * Plans are immutable once made: one plan may be used from several threads
- * and streams at once.
+ * and streams at once, with one exception: a plan that owns device scratch
+ * (gemm_epi_plan_scratch_bytes() > 0; today only 8-bit weight plans with
+ * M <= 16 whose K is split over workgroups) must not run on two streams at
+ * once, since its launches share that scratch.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
@@ -145,13 +148,20 @@ GE_API void ge_desc_init(ge_desc *d);
  * Validate d for the given kind and choose a kernel instance.  On success
  * *out receives a library-owned plan that the caller releases with
  * gemm_epi_plan_destroy().  Queries the current device (architecture and
- * compute-unit count); allocates host memory only.
+ * compute-unit count); allocates host memory, and, for 8-bit weight plans
+ * with M <= 16 whose column blocks alone do not fill the GPU, a zeroed device
+ * scratch for the cross-workgroup K split (S * ceil(N/128) * 8 KiB of fp32
+ * tiles plus 4 * ceil(N/128) bytes of counters, S in {2, 4, 8}; this call
+ * then synchronises the device, so make plans outside graph capture).
  * Errors: INVALID_ARG (bad descriptor or null out), UNSUPPORTED, NO_DEVICE.
  */
 GE_API ge_status gemm_epi_plan(const ge_desc *d, int32_t kind, ge_plan **out);
 
-/* Release a plan (NULL is accepted). */
+/* Release a plan and its device scratch, if any (NULL is accepted). */
 GE_API ge_status gemm_epi_plan_destroy(ge_plan *plan);
+
+/* Bytes of device scratch the plan owns (0 for most plans; NULL gives 0). */
+GE_API size_t gemm_epi_plan_scratch_bytes(const ge_plan *plan);
 
 /* Name of the fused kernel instance a plan launches (static string). */
 GE_API const char *gemm_epi_plan_kernel(const ge_plan *plan);
