@@ -52,11 +52,15 @@ struct ge_plan {
     int32_t group;
     const char *kernel;  // fused kernel chosen for aligned inputs
     int32_t split;       // K splits of the 8-bit streaming kernel (1: none)
-    void *scratch;       // its device scratch (split tiles, then counters), or NULL
+    int32_t scratch_use; // what scratch holds: SCRATCH_NONE / SCRATCH_SPLIT / SCRATCH_A16
+    void *scratch;       // device scratch owned by the plan, or NULL
     size_t scratch_bytes;
 };
 
 namespace {
+
+// plan scratch: the 8-bit kernel's split tiles and counters, or the int4 tile kernel's fp16 copy of A
+enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_A16 = 2 };
 
 int32_t wfmt_of(const ge_desc &d) {
     return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
@@ -101,12 +105,13 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
     p.wfmt = wfmt_of(d);
-    if (pl->scratch && pl->split > 1) {
+    p.split = 1;
+    if (pl->scratch && pl->scratch_use == SCRATCH_SPLIT) {
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
         p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - (size_t)((d.N + 127) / 128) * 4);
-    } else {
-        p.split = 1;
+    } else if (pl->scratch && pl->scratch_use == SCRATCH_A16) {
+        p.A16 = pl->scratch;
     }
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
@@ -316,25 +321,37 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
                              (const void *)256, (const void *)256, (const void *)256, (void *)256);
     pl.kernel = fused_name(p, pl.cu_count);
 
-    // the 8-bit streaming kernel splits K over workgroups when the column
-    // blocks alone do not fill the GPU; its scratch belongs to the plan
+    // device scratch: the 8-bit streaming kernel splits K over workgroups when the column blocks
+    // alone do not fill the GPU; the int4 tile kernel reads an fp16 copy of A
     pl.split = 1;
+    pl.scratch_use = SCRATCH_NONE;
     pl.scratch = nullptr;
     pl.scratch_bytes = 0;
+    int64_t bytes = 0;
+    int32_t use = SCRATCH_NONE;
     if (kind == GE_KIND_W4 && p.wfmt != WFMT_U4 && skinny_supported(p)) {
         const int split = w8_split(p, pl.cu_count);
-        const int64_t bytes = w8_split_scratch_bytes(p, split);
-        if (split > 1 && bytes > 0) {
-            hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);
-            if (e == hipSuccess) e = hipMemset(pl.scratch, 0, (size_t)bytes);
-            if (e == hipSuccess) e = hipDeviceSynchronize();
-            if (e != hipSuccess) {
-                if (pl.scratch) (void)hipFree(pl.scratch);
-                return hip_status(e, "allocating the plan's split-K scratch");
-            }
+        if (split > 1) {
+            bytes = w8_split_scratch_bytes(p, split);
+            use = SCRATCH_SPLIT;
             pl.split = split;
-            pl.scratch_bytes = (size_t)bytes;
         }
+    } else if (kind == GE_KIND_W4 && p.wfmt == WFMT_U4 && !skinny_supported(p) && tile_w4_supported(p)) {
+        bytes = tile_w4_scratch_bytes(p);
+        use = SCRATCH_A16;
+    }
+    if (bytes > 0) {
+        hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);
+        if (e == hipSuccess) e = hipMemset(pl.scratch, 0, (size_t)bytes);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            if (pl.scratch) (void)hipFree(pl.scratch);
+            return hip_status(e, "allocating the plan's device scratch");
+        }
+        pl.scratch_use = use;
+        pl.scratch_bytes = (size_t)bytes;
+    } else {
+        pl.split = 1;
     }
 
     ge_plan *h = new (std::nothrow) ge_plan(pl);
