@@ -232,7 +232,11 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
          bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
          alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
          lo_first=False, prepacked=False) -> Plan:
-    """Build (or fetch from a cache) the plan of one problem descriptor."""
+    """Build (or fetch from a cache) the plan of one problem descriptor on the current device.
+
+    Calls with equal descriptors share one plan.  A plan that owns device scratch
+    (``Plan.scratch_bytes > 0``: 8-bit weights at M <= 16 with a K split, prepacked int4 weights
+    at M > 16) serves one stream at a time."""
     d = Desc()
     lib().ge_desc_init(ctypes.byref(d))
     d.M, d.N, d.K = M, N, K
@@ -249,7 +253,8 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
     d.flags = ((FLAG_BIAS if bias else 0) | (FLAG_C if C else 0) | (FLAG_RESIDUAL if R else 0)
                | (FLAG_NIBBLE_LO_FIRST if lo_first else 0) | (FLAG_W4_PREPACKED if prepacked else 0))
     d.group_size, d.zero_point = group, zero_point
-    key = (kind, bytes(d))
+    torch = _torch()
+    key = (kind, bytes(d), torch.cuda.current_device() if torch.cuda.is_available() else -1)
     p = _plan_cache.get(key)
     if p is None:
         p = Plan(d, kind)

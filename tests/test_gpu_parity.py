@@ -388,6 +388,22 @@ def test_w4_prepacked_tile_path(M, N, K):
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 
+def test_w4_tile_plan_scratch_is_rewritten_every_call():
+    # the int4 tile path converts X into the plan's fp16 scratch on every call: two calls on one
+    # plan with different X, each against the oracle, then the first X again, bitwise as before
+    M, N, K = 200, 384, 1024
+    w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
+    p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
+    assert p.kernel.startswith("tile_w4") and p.scratch_bytes == M * K * 2
+    a, b = workloads.make_inputs(w, seed=31), workloads.make_inputs(w, seed=32)
+    b["Wq"], b["scales"], b["bias"] = a["Wq"], a["scales"], a["bias"]
+    oa = _w4_packed(a)
+    ob = _w4_packed(b)
+    assert_close(oa, oracle.reference(a), TOL_BF16, "first X")
+    assert_close(ob, oracle.reference(b), TOL_BF16, "second X")
+    assert torch.equal(_w4_packed(a).view(torch.int16), oa.view(torch.int16))
+
+
 def test_w4_prepacked_tile_one_hot_rows_bit_exact():
     K, N, M = 512, 256, 160
     Wq = workloads.uniform_bytes((K, N // 2), wid=103, tid=1)
