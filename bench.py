@@ -3,9 +3,14 @@
 
 One step = one fused call of the headline workload: the 4096^3 bf16 GEMM
 with bias, tanh-GELU and residual add in the epilogue (fp32 accumulation,
-bf16 output).  W untimed warmup steps, then exactly K timed steps bracketed by
-device synchronisation; HIP events around every launch on the launch stream
-give the kernel's average duration for the roofline object.
+bf16 output).  W untimed warmup steps, then exactly K timed steps, back to
+back, between two HIP events on the launch stream and bracketed by device
+synchronisation; the region divided by K is the kernel's average duration for
+the roofline object (a kernel trace of the same command shows no gap between
+the launches).  The default warmup is long because the shader clock of a GPU
+that has just come out of idle settles over the first few hundred launches
+(at 4096^3: about 120 us per launch for the first hundred, 102 us from the
+third hundred on).
 
 Also reported (same JSON line): the deliberately unfused chain of the same
 workload, the other workloads (tiny fp32, SwiGLU dual GEMM, 16-row decode
@@ -13,7 +18,7 @@ GEMM, W4A16 at M=16 and M=512) fused and unfused, the next steps (fused
 residual add + RMSNorm, 8-bit weight formats), and the CPU oracle timed
 on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--main-only]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 400] [--main-only]
                        [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
@@ -37,8 +42,8 @@ MALL_BYTES = 256 << 20      # Infinity Cache: HBM-bound rows rotate past it
 def _args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--main-only", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size in rows (0 = auto)")
@@ -65,29 +70,26 @@ def calibrate_copy():
 # --------------------------------------------------------------------------
 
 def time_launches(fn_list, steps, warmup):
-    """Run fn_list[i % len] for warmup + steps iterations; return (total_ms, per_launch_ms list).
+    """Run fn_list[i % len] for warmup + steps iterations; return the timed region in ms.
 
-    Every timed launch is bracketed by its own pair of HIP events on the
-    current stream (the one the library launches on)."""
+    The timed calls run back to back between two HIP events recorded on the current stream
+    (the one the library launches on), bracketed by device synchronisation.  With no host
+    work or events between them, a kernel trace shows no gap between consecutive launches,
+    so the region divided by the number of calls is each call's duration on the GPU."""
     import torch
     s = torch.cuda.current_stream()
     n = len(fn_list)
     for i in range(warmup):
         fn_list[i % n]()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_all0.record(s)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
     for i in range(steps):
-        ev[i][0].record(s)
         fn_list[i % n]()
-        ev[i][1].record(s)
-    t_all1.record(s)
+    t1.record(s)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return t_all0.elapsed_time(t_all1), per
+    return t0.elapsed_time(t1)
 
 
 def graph_time(fn_list, steps, warmup):
@@ -109,11 +111,6 @@ def graph_time(fn_list, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / (reps * len(calls))
-
-
-def median(xs):
-    xs = sorted(xs)
-    return xs[len(xs) // 2]
 
 
 # --------------------------------------------------------------------------
@@ -191,14 +188,14 @@ def measure(name, steps, warmup):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     fused, unfused, meta = build_calls(name, w, inp)
-    tot_f, per_f = time_launches(fused, steps, warmup)
-    tot_u, per_u = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2))
-    fused_ms = tot_f / steps
-    kern_ms = sum(per_f) / len(per_f)
-    unfused_ms = tot_u / max(steps // 2, 5)
+    fused_ms = time_launches(fused, steps, warmup) / steps
+    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
+    # calls run back to back, so the per-call average is each call's GPU duration (one kernel for
+    # every fused call except int4 at M > 16, which is the activation pre-pass plus the tile kernel)
+    kern_ms = fused_ms
     r = dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
              flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"],
-             ms_per_step=fused_ms, kernel_ms_avg=kern_ms, kernel_ms_median=median(per_f),
+             ms_per_step=fused_ms, kernel_ms_avg=kern_ms,
              unfused_ms=unfused_ms, unfused_bytes=meta["unfused_bytes"],
              speedup_vs_unfused=unfused_ms / fused_ms)
     if meta["bound"] == "hbm":
@@ -227,8 +224,7 @@ def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
         sets.append((a, x, torch.empty_like(a), torch.empty_like(a)))
     w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).bfloat16()
     calls = [(lambda a=a, x=x, r=r, o=o: ge.add_rmsnorm(a, x, w, resid=r, out=o)) for a, x, r, o in sets]
-    tot, per = time_launches(calls, steps, warmup)
-    kern = sum(per) / len(per)
+    kern = time_launches(calls, steps, warmup) / steps
     byts = set_bytes + N * 2
     return {"kernel": "add_rmsnorm", "M": M, "N": N, "bytes": byts, "rotations": nrot,
             "kernel_ms_avg": round(kern, 4), "gbps": round(byts / (kern * 1e-3) / 1e9, 1),
