@@ -133,7 +133,7 @@ hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
 
 const char *fused_name(const Problem &p, int cu_count) {
     if (skinny_supported(p)) return skinny_kernel_name(p, cu_count);
-    if (tile_supported(p)) return tile_kernel_name(p);
+    if (tile_supported(p)) return tile_kernel_name(p, cu_count);
     return "general_64x64";
 }
 

@@ -43,7 +43,7 @@ hipError_t launch_general(const Problem &p, hipStream_t s);
 // the problem does not meet its preconditions (see tile_supported()).
 bool tile_supported(const Problem &p);
 hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s);
-const char *tile_kernel_name(const Problem &p);
+const char *tile_kernel_name(const Problem &p, int cu_count);
 
 // int4 tile kernel (prepacked weights, M > 16), dispatched through launch_tile.
 // It first converts A to fp16 into p.A16 (plan scratch of tile_w4_scratch_bytes).

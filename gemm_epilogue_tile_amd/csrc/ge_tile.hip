@@ -208,18 +208,21 @@ void tile_kernel(Problem p) {
     };
     // fragment read r of a stage: A fragments and B fragments alternate
     constexpr int NRD = C::MT + C::NB * C::NT;
+    // read r < NRD: A and B fragments interleave in proportion to their counts
+    constexpr int NBT = C::NB * C::NT;
     auto read_frag = [&](int buf, int r, bf16x8 (&a)[C::MT], bf16x8 (&b)[C::NB][C::NT]) {
-        const int ai = r / 2, bi = r / 2;  // interleave while both remain
-        if (r % 2 == 0 && ai < C::MT) {
-            read_a(buf, ai, a[ai]);
-        } else if (r % 2 == 1 && bi < C::NB * C::NT) {
+        // read r is an A read when ceil((r + 1) * MT / NRD) > ceil(r * MT / NRD) (read 0 is A)
+        const int a_before = (r * C::MT + NRD - 1) / NRD, a_after = ((r + 1) * C::MT + NRD - 1) / NRD;
+        if (a_after > a_before) {
+            read_a(buf, a_before, a[a_before]);
+        } else {
+            const int bi = r - a_before;
             read_b(buf, bi / C::NT, bi % C::NT, b[bi / C::NT][bi % C::NT]);
         }
     };
-    static_assert(C::MT == C::NB * C::NT, "fragment reads alternate A and B");
     auto read_frags = [&](int buf, bf16x8 (&a)[C::MT], bf16x8 (&b)[C::NB][C::NT]) {
 #pragma unroll
-        for (int r = 0; r < 2 * C::MT; ++r) read_frag(buf, r, a, b);
+        for (int r = 0; r < NRD; ++r) read_frag(buf, r, a, b);
     };
 
     f32x4 acc[C::NB][C::MT][C::NT];
@@ -242,23 +245,24 @@ void tile_kernel(Problem p) {
     // LDS or memory instructions.  Reads go after MFMAs 0, 3, 6, ..., loads after 1, 4, 7, ...;
     // an empty asm with a memory clobber pins each one to its slot.
     constexpr int NMF = C::NB * C::NT * C::MT;
-    static_assert(3 * (2 * C::MT - 1) < NMF && 3 * (C::LOADS - 1) + 1 < NMF, "side-op slots");
+    // side-op spacing: reads after MFMAs 0, SP, 2 SP, ..., loads after 1, SP + 1, ...
+    constexpr int SP = (3 * (NRD - 1) < NMF && 3 * (C::LOADS - 1) + 1 < NMF) ? 3 : 2;
+    static_assert(SP * (NRD - 1) < NMF && SP * (C::LOADS - 1) + 1 < NMF, "side-op slots");
     auto stage = [&](const StageLoads &L, int nbuf, const bf16x8 (&a)[C::MT], const bf16x8 (&b)[C::NB][C::NT],
                      bf16x8 (&na)[C::MT], bf16x8 (&nb)[C::NB][C::NT]) {
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int d = q / (C::NT * C::MT), j = (q / C::MT) % C::NT, i = q % C::MT;
             mfma_bf16_acc(acc[d][i][j], b[d][j], a[i]);
-            if (q % 3 == 0 && q / 3 < 2 * C::MT) {
+            if (q % SP == 0 && q / SP < NRD) {
                 asm volatile("" ::: "memory");
-                read_frag(nbuf, q / 3, na, nb);
+                read_frag(nbuf, q / SP, na, nb);
                 asm volatile("" ::: "memory");
-            } else if (q % 3 == 1 && q / 3 < C::LOADS) {
-                issue_load(L, q / 3);
+            } else if (q % SP == 1 && q / SP < C::LOADS) {
+                issue_load(L, q / SP);
             }
         }
     };
-    (void)NRD;
 
     // wait until at most n of this wave's direct loads are outstanding
     // (vmcnt counts them in issue order; lgkm / exp counters left at their maximum)
@@ -368,16 +372,48 @@ bool tile_supported(const Problem &p) {
     return epi_ok(p);
 }
 
-const char *tile_kernel_name(const Problem &p) {
+// SwiGLU tiles are 256 x 128.  When their count leaves the last round of workgroups
+// partly empty (2048 x 14336: 896 tiles = 3.5 rounds of 256 CUs), the columns of the
+// partial round are peeled off and run as 128 x 128 tiles, one full round of half-size
+// tiles: returns the 128-column blocks that stay in 256 x 128 tiles (all of them when
+// nothing is peeled).
+int swiglu_big_blocks(const Problem &p, int cu_count) {
+    const int tiles_m = (p.M + 255) / 256, ncb = (p.N + 127) / 128;
+    const int64_t total = (int64_t)tiles_m * ncb;
+    if (cu_count <= 0 || total <= cu_count || total % cu_count == 0) return ncb;
+    const int64_t full = total / cu_count * cu_count;
+    if (full % tiles_m) return ncb;
+    const int nb = (int)(full / tiles_m);
+    const int64_t small = (int64_t)((p.M + 127) / 128) * (ncb - nb);
+    return small <= cu_count ? nb : ncb;
+}
+
+const char *tile_kernel_name(const Problem &p, int cu_count) {
     if (p.mode == MODE_W4) return tile_w4_kernel_name();
-    if (p.mode == MODE_SWIGLU) return "tile_swiglu_256x128x32";
+    if (p.mode == MODE_SWIGLU)
+        return swiglu_big_blocks(p, cu_count) * 128 < p.N ? "tile_swiglu_256x128x32+128x128x32"
+                                                           : "tile_swiglu_256x128x32";
     return p.b_layout == GE_LAYOUT_NK ? "tile_nk_256x256x32" : "tile_kn_256x256x32";
 }
 
-hipError_t launch_tile(const Problem &p, int, hipStream_t s) {
+hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s) {
     if (!tile_supported(p)) return hipErrorInvalidValue;
     if (p.mode == MODE_W4) return launch_tile_w4(p, s);
-    if (p.mode == MODE_SWIGLU) return launch_cfg<256, 128, 2, 2, true, false>(p, s);
+    if (p.mode == MODE_SWIGLU) {
+        const int nb = swiglu_big_blocks(p, cu_count);
+        if (nb * 128 >= p.N) return launch_cfg<256, 128, 2, 2, true, false>(p, s);
+        // columns [0, 128 nb) in 256 x 128 tiles, the rest in 128 x 128 tiles
+        const int64_t off = (int64_t)nb * 128;
+        Problem big = p, rest = p;
+        big.N = (int32_t)off;
+        rest.N = p.N - (int32_t)off;
+        rest.B = (const uint16_t *)p.B + off;
+        rest.B2 = (const uint16_t *)p.B2 + off;
+        rest.epi.D = (uint16_t *)p.epi.D + off;
+        hipError_t e = launch_cfg<256, 128, 2, 2, true, false>(big, s);
+        if (e == hipSuccess) e = launch_cfg<128, 128, 2, 2, true, false>(rest, s);
+        return e;
+    }
     if (p.b_layout == GE_LAYOUT_NK) return launch_cfg<256, 256, 2, 2, false, true>(p, s);
     return launch_cfg<256, 256, 2, 2, false, false>(p, s);
 }

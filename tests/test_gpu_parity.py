@@ -155,6 +155,20 @@ def test_swiglu_ragged(M, N, K):
     assert_close(out, oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
 
 
+def test_swiglu_peeled_last_round():
+    # 2 x 136 tiles of 256 x 128 leave a partial round on 256 CUs: the last 8 column blocks run
+    # as 128 x 128 tiles in a second launch; every column is checked against the oracle
+    M, N, K = 512, 136 * 128, 256
+    p = ge.plan(ge.KIND_SWIGLU, M, N, K)
+    assert p.kernel == "tile_swiglu_256x128x32+128x128x32"
+    w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=7)
+    d = dev_inputs(inp)
+    assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, "swiglu peeled")
+    assert ge.plan(ge.KIND_SWIGLU, 2048, 14336, 4096).kernel == "tile_swiglu_256x128x32+128x128x32"
+    assert ge.plan(ge.KIND_SWIGLU, 2048, 16384, 4096).kernel == "tile_swiglu_256x128x32"  # 1024 tiles
+
+
 # --------------------------------------------------------------------------
 # W4A16
 # --------------------------------------------------------------------------
