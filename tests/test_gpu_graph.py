@@ -60,3 +60,60 @@ def test_decode_chain_graph_replays_match_eager():
         for be, bg in zip(bufs_e, bufs_g):
             assert torch.equal(be, bg), f"replay {rep} differs from the eager chain"
         assert torch.isfinite(bufs_g[2].float()).all()
+
+
+def _scratch_inputs(seed):
+    g = torch.Generator().manual_seed(seed)
+    x8 = torch.randn(16, 4096, generator=g).bfloat16()
+    x4 = torch.randn(256, 1024, generator=g).bfloat16()
+    xs = torch.randn(512, 256, generator=g).bfloat16()
+    return [t.to(DEV) for t in (x8, x4, xs)]
+
+
+def test_scratch_using_calls_replay_in_a_graph():
+    # calls whose plans own device scratch: the 8-bit K split (tile handoff, counters that re-arm
+    # themselves), the int4 tile path (activation pre-pass into scratch) and the SwiGLU launch
+    # whose partial last round is peeled into 128 x 128 tiles
+    g = torch.Generator().manual_seed(9)
+    x8, x4, xs = _scratch_inputs(2)
+    Wq8 = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
+    s8 = torch.full((32, 4096), 0.001).bfloat16().to(DEV)
+    Wp4 = ge.w4_prepack(torch.randint(0, 256, (1024, 512), generator=g, dtype=torch.uint8).to(DEV))
+    s4 = torch.full((8, 1024), 0.01).bfloat16().to(DEV)
+    Wg = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
+    Wu = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
+
+    def outs():
+        return [torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV),
+                torch.empty(256, 1024, dtype=torch.bfloat16, device=DEV),
+                torch.empty(512, 136 * 128, dtype=torch.bfloat16, device=DEV)]
+
+    def prepare(o):
+        return [ge.prepare_w4_gemm(x8, Wq8, s8, out=o[0], zero_point=128, fmt="u8"),
+                ge.prepare_w4_gemm(x4, Wp4, s4, out=o[1], prepacked=True),
+                ge.prepare_swiglu(xs, Wg, Wu, out=o[2])]
+
+    oe, og = outs(), outs()
+    eager, graph_calls = prepare(oe), prepare(og)
+    kernels = [f._plan.kernel for f in eager]
+    assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1].startswith("tile_w4")
+    assert kernels[2] == "tile_swiglu_256x128x32+128x128x32"
+    assert all(f._plan.scratch_bytes > 0 for f in eager[:2])
+    for f in eager + graph_calls:
+        f()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in graph_calls:
+            f.with_stream()()
+    for rep in range(4):
+        for dst, src in zip((x8, x4, xs), _scratch_inputs(200 + rep)):
+            dst.copy_(src)
+        for f in eager:
+            f()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for be, bg in zip(oe, og):
+            assert torch.equal(be, bg), f"replay {rep} differs from the eager calls"
+        assert all(torch.isfinite(t.float()).all() for t in og)
