@@ -14,7 +14,7 @@ namespace {
 
 constexpr int EW_THREADS = 256;
 
-__device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+__host__ __device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 // Walk an M x N index space in 8-column chunks: f(m, n, vec) where vec says the
 // whole chunk n..n+7 is inside the row.
@@ -248,6 +248,63 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm(int32_t M, int32_t N
     }
 }
 
+// Rows of at most 4096 bf16 elements: one wave per row, no LDS and no barrier.  Lane l owns
+// the 8-element chunks c * 64 + l (c < CH); every load of the row (a, x and w) is requested
+// before any is used, through buffer loads that read zeros past the row's end, and the
+// stores past the end are dropped the same way, so the row needs no branches.
+template <int CH>
+__global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int32_t N, const uint16_t *a,
+                                                                const uint16_t *x, const uint16_t *w,
+                                                                float eps, uint16_t *resid, uint16_t *out) {
+    const int lane = threadIdx.x & 63;
+    const int rows_per_block = EW_THREADS / 64;
+    const uint32_t row_bytes = (uint32_t)N * 2;
+    auto rsrc = [&](const void *base) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)row_bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rw = rsrc(w);
+    u32x4 vw[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        vw[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (c * 64 + lane) * 16, 0, 0));
+    for (int64_t m = (int64_t)blockIdx.x * rows_per_block + (threadIdx.x >> 6); m < M;
+         m += (int64_t)gridDim.x * rows_per_block) {
+        const __amdgpu_buffer_rsrc_t ra = rsrc(a + m * N), rx = rsrc(x + m * N);
+        u32x4 va[CH], vx[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            va[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (c * 64 + lane) * 16, 0, 0));
+            vx[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c * 64 + lane) * 16, 0, 0));
+        }
+        float r[CH][8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r[c][2 * q] = bf16lo(va[c][q]) + bf16lo(vx[c][q]);
+                r[c][2 * q + 1] = bf16hi(va[c][q]) + bf16hi(vx[c][q]);
+                ss = fmaf(r[c][2 * q], r[c][2 * q], ss);
+                ss = fmaf(r[c][2 * q + 1], r[c][2 * q + 1], ss);
+            }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        const float rrms = 1.0f / sqrtf(ss / (float)N + eps);
+        const __amdgpu_buffer_rsrc_t rr = rsrc(resid + m * N), ro = rsrc(out + m * N);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            u32x4 wr, wo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wr[q] = pack_bf16x2(r[c][2 * q], r[c][2 * q + 1]);
+                wo[q] = pack_bf16x2(r[c][2 * q] * rrms * bf16lo(vw[c][q]), r[c][2 * q + 1] * rrms * bf16hi(vw[c][q]));
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(wr, rr, (c * 64 + lane) * 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(wo, ro, (c * 64 + lane) * 16, 0, 0);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_ew_axpby(int64_t M, int64_t N, float alpha, const void *X, int32_t x_type,
@@ -313,6 +370,27 @@ hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 
 hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
                               float eps, void *resid, void *out, hipStream_t s) {
+    const bool al = aligned16(a) && aligned16(x) && aligned16(w) && aligned16(resid) && aligned16(out);
+    if (al && N % 8 == 0 && N <= 4096) {
+        const int rows = EW_THREADS / 64;
+        const unsigned blocks = (unsigned)((M + rows - 1) / rows < 65536 ? (M + rows - 1) / rows : 65536);
+        const int ch = (N + 511) / 512;
+        auto go = [&](auto CHC) {
+            constexpr int CH = decltype(CHC)::value;
+            hipLaunchKernelGGL(k_add_rmsnorm_wave<CH>, dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
+                               (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
+                               (uint16_t *)resid, (uint16_t *)out);
+        };
+        if (ch <= 1)
+            go(std::integral_constant<int, 1>{});
+        else if (ch <= 2)
+            go(std::integral_constant<int, 2>{});
+        else if (ch <= 4)
+            go(std::integral_constant<int, 4>{});
+        else
+            go(std::integral_constant<int, 8>{});
+        return hipGetLastError();
+    }
     const unsigned blocks = (unsigned)(M < 65536 ? M : 65536);
     hipLaunchKernelGGL(k_add_rmsnorm, dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
                        (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
