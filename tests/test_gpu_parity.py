@@ -289,7 +289,10 @@ def test_unfused_w4_matches_oracle():
 # fused residual add + RMSNorm
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N", [(1, 8), (4, 100), (16, 4096), (33, 8192), (7, 16384)])
+@pytest.mark.parametrize("M,N", [(1, 8), (4, 100), (16, 4096), (33, 8192), (7, 16384),
+                                 # one wave per row: ragged chunk counts, rows not a multiple of
+                                 # four, more rows than one launch of workgroups covers
+                                 (5, 1000), (9, 2056), (300000, 8)])
 def test_add_rmsnorm(M, N):
     a = workloads.normal((M, N), 1.0, "bf16", wid=100, tid=0, seed=N)
     x = workloads.normal((M, N), 1.0, "bf16", wid=100, tid=1, seed=N)
