@@ -40,9 +40,10 @@
  *
  * Plans are immutable once made: one plan may be used from several threads
  * and streams at once, with one exception: a plan that owns device scratch
- * (gemm_epi_plan_scratch_bytes() > 0; today only 8-bit weight plans with
- * M <= 16 whose K is split over workgroups) must not run on two streams at
- * once, since its launches share that scratch.
+ * (gemm_epi_plan_scratch_bytes() > 0: 8-bit weight plans with M <= 16 whose
+ * K is split over workgroups, and prepacked int4 plans with M > 16, which
+ * convert X to fp16 into it) must not run on two streams at once, since its
+ * launches share that scratch.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
@@ -148,11 +149,13 @@ GE_API void ge_desc_init(ge_desc *d);
  * Validate d for the given kind and choose a kernel instance.  On success
  * *out receives a library-owned plan that the caller releases with
  * gemm_epi_plan_destroy().  Queries the current device (architecture and
- * compute-unit count); allocates host memory, and, for 8-bit weight plans
- * with M <= 16 whose column blocks alone do not fill the GPU, a zeroed device
- * scratch for the cross-workgroup K split (S * ceil(N/128) * 8 KiB of fp32
- * tiles plus 4 * ceil(N/128) bytes of counters, S in {2, 4, 8}; this call
- * then synchronises the device, so make plans outside graph capture).
+ * compute-unit count); allocates host memory, and a zeroed device scratch
+ * for two kinds of plan: 8-bit weight plans with M <= 16 whose column blocks
+ * alone do not fill the GPU (the cross-workgroup K split: S * ceil(N/128) *
+ * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters, S in
+ * {2, 4, 8}), and prepacked int4 plans with M > 16 (the fp16 copy of X,
+ * M * K * 2 bytes).  Such a call synchronises the device, so make plans
+ * outside graph capture.
  * Errors: INVALID_ARG (bad descriptor or null out), UNSUPPORTED, NO_DEVICE.
  */
 GE_API ge_status gemm_epi_plan(const ge_desc *d, int32_t kind, ge_plan **out);
