@@ -171,3 +171,24 @@ def test_w8_split_repeat_calls_are_bitwise_identical(fmt):
     ref = {s: o for s, o in outs[:2]}
     for s, o in outs[2:]:
         assert torch.equal(o, ref[s])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_split_handoff_is_stable_over_many_calls(fmt):
+    # 300 back-to-back calls through the cross-workgroup handoff (device-scope loads and stores,
+    # counters re-armed by the last workgroup): every output bitwise equal to the first
+    w = BASE[fmt]
+    inp = workloads.make_inputs(w, seed=3)
+    d = dev_inputs(inp)
+    Wq = torch.from_numpy(inp["Wq"]).to(DEV)
+    outs = [torch.empty(w.M, w.N, dtype=torch.bfloat16, device=DEV) for _ in range(300)]
+    f = [ge.prepare_w4_gemm(d["X"], Wq, d["scales"], bias=d["bias"], out=o, zero_point=w.zero_point, fmt=fmt)
+         for o in outs]
+    assert f[0]._plan.kernel.endswith("_split4")
+    for g in f:
+        g()
+    torch.cuda.synchronize()
+    first = outs[0].view(torch.int16)
+    bad = [i for i, o in enumerate(outs) if not torch.equal(o.view(torch.int16), first)]
+    assert not bad, f"calls {bad[:10]} differ from the first"
+
