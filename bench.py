@@ -47,6 +47,9 @@ def _args():
     ap.add_argument("--main-only", action="store_true", help="only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size in rows (0 = auto)")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated workload names: run only their fused calls and print one JSON "
+                         "line each (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB fp32 device copy (y = -x) 5 times, the reference "
                          "for scaling HBM byte counters")
@@ -183,12 +186,16 @@ def build_calls(name, w, inp):
     return fused, unfused, dict(acc, kernel=kernel, rotations=nrot)
 
 
-def measure(name, steps, warmup):
+def measure(name, steps, warmup, unfused_chain=True):
     import workloads
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     fused, unfused, meta = build_calls(name, w, inp)
     fused_ms = time_launches(fused, steps, warmup) / steps
+    if not unfused_chain:
+        return dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
+                    flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"], ms_per_call=fused_ms,
+                    gbps=meta["bytes"] / (fused_ms * 1e-3) / 1e9, tflops=meta["flops"] / (fused_ms * 1e-3) / 1e12)
     unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
     # calls run back to back, so the per-call average is each call's GPU duration (one kernel for
     # every fused call except int4 at M > 16, which is the activation pre-pass plus the tile kernel)
@@ -251,9 +258,40 @@ def cpu_baseline(rows_req):
     oracle.reference(inp, rows=np.arange(rows))
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {rows} of 4096 output rows of the 4096x4096x4096 bf16 GELU+bias+residual "
-                      f"workload ({rows}x4096x4096 fp64 products + epilogue passes), {dt:.1f} s"}
+    r = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+         "sample": f"first {rows} of 4096 output rows of the 4096x4096x4096 bf16 GELU+bias+residual "
+                   f"workload ({rows}x4096x4096 fp64 products + epilogue passes), {dt:.1f} s",
+         "cpu_model": _cpu_model(), "affinity": len(os.sched_getaffinity(0))}
+    r["one_core_s"] = _one_core_times()
+    return r
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _one_core_times():
+    """The oracle on one thread (a child process with OMP_NUM_THREADS=1): the whole tiny fp32
+    configuration and the whole 16 x 28672 x 8192 decode configuration, in seconds."""
+    import subprocess
+    code = ("import json, sys, time; sys.path.insert(0, %r); import oracle, workloads; oracle.build(); out = {}\n"
+            "for name in ('tiny_fp32', 'skinny_decode'):\n"
+            "    inp = workloads.make_inputs(workloads.WORKLOADS[name]); t = time.perf_counter()\n"
+            "    oracle.reference(inp); out[name] = round(time.perf_counter() - t, 4)\n"
+            "print(json.dumps(out))") % ROOT
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+        return json.loads(res.stdout.strip().splitlines()[-1]) if res.returncode == 0 else None
+    except (subprocess.SubprocessError, IndexError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------------
@@ -303,6 +341,12 @@ def main():
         return
     import gemm_epilogue_tile_amd as ge
     ge.lib()  # fails loudly when the HIP library is missing
+    if a.workloads:
+        for name in a.workloads.split(","):
+            r = measure(name, a.steps, a.warmup, unfused_chain=False)
+            print(json.dumps({k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
+            torch.cuda.empty_cache()
+        return
 
     main_r = measure("square_bf16", a.steps, a.warmup)
     others = {}

@@ -341,19 +341,23 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
 // order), runs the epilogue and re-arms the counter for the next launch.
 // Launches that share one scratch buffer must not overlap.
 //
-// Tiles and counters are accessed only with device-scope (agent) atomic
-// loads and stores, which the hardware keeps coherent across the XCDs' L2
-// caches per access, so no fence has to write back or invalidate whole L2
-// caches (fences made the split slower than no split at all).  Ordering:
-// every wave waits until its tile stores have completed before the barrier,
-// the counter increment follows the barrier, and the last workgroup's tile
-// loads are issued only after the increment has returned (barrier and LDS
-// flag in between).
+// Tiles are written and read with 16-byte buffer accesses carrying the
+// device-scope cache policy (sc1: the access is coherent across the XCDs'
+// L2 caches, as a device-scope atomic access is), and the counters with
+// device-scope atomics, so no fence has to write back or invalidate whole L2
+// caches (fences made the split slower than no split at all; 4-byte atomic
+// stores of the tiles cost 8x their bytes in write traffic).  Ordering: every
+// wave waits until its tile stores have completed before the barrier, the
+// counter increment follows the barrier, and the last workgroup's tile loads
+// are issued only after the increment has returned (barrier and LDS flag in
+// between).
 template <int MR, int NC, int NS, int NWV = S_WAVES>
 __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const float *red, int n0, int cb, int ks,
                                                       int ncb, int *s_last) {
     constexpr int CH = NC / 8;
-    float *mine = p.split_ws + ((int64_t)ks * ncb + cb) * (MR * NC);
+    constexpr int SC1 = 16;  // cache policy operand: device scope
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.split_ws, (int64_t)NS * ncb * MR * NC * 4);
+    const uint32_t mine = (uint32_t)(((int64_t)ks * ncb + cb) * (MR * NC) * 4);
     for (int item = threadIdx.x; item < MR * CH; item += 64 * NWV) {
         const int r = item / CH, c = item % CH;
         f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
@@ -362,12 +366,9 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
             a += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8];
             b += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8 + 4];
         }
-        float *dst = mine + r * NC + c * 8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            __hip_atomic_store(dst + q, a[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(dst + 4 + q, b[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const uint32_t off = mine + (uint32_t)(r * NC + c * 8) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), rt, off, 0, SC1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rt, off + 16, 0, SC1);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile stores are complete
     __syncthreads();
@@ -385,18 +386,21 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
             const int m = r, n = n0 + c * 8;
             if (m >= p.M || n >= p.N) continue;
             // all NS tiles requested at once, then summed in split order
-            float tl[NS][8];
+            f32x4 tl[NS][2];
 #pragma unroll
             for (int q = 0; q < NS; ++q) {
-                const float *t = p.split_ws + ((int64_t)q * ncb + cb) * (MR * NC) + r * NC + c * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tl[q][e] = __hip_atomic_load(t + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t off = (uint32_t)((((int64_t)q * ncb + cb) * (MR * NC) + r * NC + c * 8) * 4);
+                tl[q][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, SC1));
+                tl[q][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16, 0, SC1));
             }
             float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q = 0; q < NS; ++q)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += tl[q][e];
+                for (int e = 0; e < 4; ++e) {
+                    v[e] += tl[q][0][e];
+                    v[4 + e] += tl[q][1][e];
+                }
             finish_chunk<ACT>(p, vec_ok, m, n, v);
         }
     });
