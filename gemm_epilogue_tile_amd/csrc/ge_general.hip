@@ -69,30 +69,36 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[d][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // the next K step's elements are loaded into registers while the current one is multiplied
+    // (A: thread -> row tid/4, 8 consecutive k; B: thread -> k row tid/8, 8 consecutive n)
+    constexpr int NBT = DUAL ? 2 : 1;
+    const int ar = tid >> 2, akc = (tid & 3) * 8;
+    const int bkr = tid >> 3, bnc = (tid & 7) * 8;
+    float ra[8], rb[NBT][8];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ra[i] = load_a(p, m0 + ar, k0 + akc + i);
+#pragma unroll
+        for (int d = 0; d < NBT; ++d) {
+            const void *B = d == 0 ? p.B : p.B2;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) rb[d][i] = load_b(p, B, k0 + bkr, n0 + bnc + i);
+        }
+    };
+    fetch(0);
     for (int k0 = 0; k0 < p.K; k0 += GB_K) {
-        // A tile: thread -> row tid/4, 8 consecutive k
-        {
-            const int r = tid >> 2, kc = (tid & 3) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (USE_BF16) As[ar][akc + i] = f32_to_bf16(ra[i]); else As[ar][akc + i] = ra[i];
+        }
+#pragma unroll
+        for (int d = 0; d < NBT; ++d)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float v = load_a(p, m0 + r, k0 + kc + i);
-                if constexpr (USE_BF16) As[r][kc + i] = f32_to_bf16(v); else As[r][kc + i] = v;
+                if constexpr (USE_BF16) Bs[d][bnc + i][bkr] = f32_to_bf16(rb[d][i]); else Bs[d][bnc + i][bkr] = rb[d][i];
             }
-        }
-        // B tile(s): thread -> k row tid/8, 8 consecutive n
-        {
-            const int kr = tid >> 3, nc = (tid & 7) * 8;
-#pragma unroll
-            for (int d = 0; d < (DUAL ? 2 : 1); ++d) {
-                const void *B = d == 0 ? p.B : p.B2;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float v = load_b(p, B, k0 + kr, n0 + nc + i);
-                    if constexpr (USE_BF16) Bs[d][nc + i][kr] = f32_to_bf16(v); else Bs[d][nc + i][kr] = v;
-                }
-            }
-        }
         __syncthreads();
+        if (k0 + GB_K < p.K) fetch(k0 + GB_K);
 
         if constexpr (USE_BF16) {
             const int kk = (lane >> 4) * 8;
