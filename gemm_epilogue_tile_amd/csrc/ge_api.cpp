@@ -59,8 +59,9 @@ struct ge_plan {
 
 namespace {
 
-// plan scratch: the 8-bit kernel's split tiles and counters, or the int4 tile kernel's fp16 copy of A
-enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_A16 = 2 };
+// plan scratch: the 8-bit kernel's split tiles and counters, the int4 tile kernel's fp16 copy
+// of A, or the stream-K decode kernel's tiles and counters
+enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_A16 = 2, SCRATCH_SK = 3 };
 
 int32_t wfmt_of(const ge_desc &d) {
     return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
@@ -105,12 +106,16 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
     p.wfmt = wfmt_of(d);
+    // scratch goes only to the kernel it was made for (unfused chains run copies of a plan
+    // with another kind)
     p.split = 1;
-    if (pl->scratch && pl->scratch_use == SCRATCH_SPLIT) {
+    const bool split_use = pl->scratch_use == SCRATCH_SPLIT && p.mode == MODE_W4;
+    const bool sk_use = pl->scratch_use == SCRATCH_SK && p.mode == MODE_GENERIC;
+    if (pl->scratch && (split_use || sk_use)) {
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
         p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - (size_t)((d.N + 127) / 128) * 4);
-    } else if (pl->scratch && pl->scratch_use == SCRATCH_A16) {
+    } else if (pl->scratch && pl->scratch_use == SCRATCH_A16 && p.mode == MODE_W4) {
         p.A16 = pl->scratch;
     }
     if (pl->kind != GE_KIND_SWIGLU) {
@@ -339,6 +344,13 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     } else if (kind == GE_KIND_W4 && p.wfmt == WFMT_U4 && !skinny_supported(p) && tile_w4_supported(p)) {
         bytes = tile_w4_scratch_bytes(p);
         use = SCRATCH_A16;
+    } else if (kind == GE_KIND_GENERIC && skinny_supported(p)) {
+        const int slots = bf16_sk_slots(p, pl.cu_count);
+        if (slots > 0) {
+            bytes = bf16_sk_scratch_bytes(p, slots);
+            use = SCRATCH_SK;
+            pl.split = slots;
+        }
     }
     if (bytes > 0) {
         hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);

@@ -64,6 +64,11 @@ const char *skinny_kernel_name(const Problem &p, int cu_count);
 // (tiles, then counters that must start at zero; the kernel re-arms them).
 int w8_split(const Problem &p, int cu_count);
 int64_t w8_split_scratch_bytes(const Problem &p, int split);
+// Stream-K bf16 decode kernel: tile slots per column block (0: the plain kernel) and the
+// scratch bytes they need (tiles, then counters that must start at zero).  It is launched
+// when p.split > 1 with p.split_ws / p.split_cnt set, on cu_count workgroups.
+int bf16_sk_slots(const Problem &p, int cu_count);
+int64_t bf16_sk_scratch_bytes(const Problem &p, int slots);
 
 // Elementwise kernels of the unfused chain.  All tensors dense [M, N] of the
 // given storage type unless noted.

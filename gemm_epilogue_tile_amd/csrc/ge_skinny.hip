@@ -111,32 +111,19 @@ __device__ __forceinline__ void reduce_epilogue(const Problem &p, const float *r
 // MT: 16-row tiles of X (M <= 16 MT).  WG: NCH 8-column chunks (NCH <= 16,
 // one per lane of a 16-lane row; the remaining lanes idle), 8 waves splitting
 // K.  NCH is chosen per shape so that the workgroups fill the CUs evenly.
+// One wave's share of a column block: 32-deep blocks [kb0, kb1) of the NC = 8 NCH columns
+// from n0, accumulated into acc (lane (g, i) holds rows mt*16 + 4 g + e, columns 8 i + t).
 template <int MT, int NCH>
-__global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
-    constexpr int NC = 8 * NCH;
-    constexpr int MR = 16 * MT;
-    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
-
+__device__ __forceinline__ void stream_bf16(const Problem &p, int n0, int kb0, int kb1, f32x4 (&acc)[MT][8]) {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int n0 = blockIdx.x * NC;
-
     const int nkb = (p.K + 31) / 32;
-    const int per = (nkb + S_WAVES - 1) / S_WAVES;
-    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
 
     // W: lane -> rows 8 g + r of the block, 16-byte column chunk i (columns n0 + 8 i ..)
     const bool nin = i < NCH && n0 + 8 * i < p.N;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, ((int64_t)(p.K - 1) * p.ldb + p.N) * 2);
     // X: lane -> row mt*16 + i, k = 8 g .. 8 g + 7 of the block
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
-
-    f32x4 acc[MT][8];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto load_w = [&](int kb, u32x4 (&w)[8]) {
         const int k = kb * 32 + 8 * g;
@@ -192,8 +179,14 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
             }
         }
     }
+}
 
-    // partial tile -> LDS: lane (g, i) holds rows mt*16 + 4 g + e, columns 8 i + t
+// partial tile of one wave -> LDS red[wave][MR][NC]
+template <int MT, int NCH>
+__device__ __forceinline__ void acc_to_lds(float *red, const f32x4 (&acc)[MT][8]) {
+    constexpr int NC = 8 * NCH, MR = 16 * MT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
     if (i < NCH) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -204,8 +197,135 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
                 *(f32x4 *)(dst + 4) = f32x4{acc[mt][4][e4], acc[mt][5][e4], acc[mt][6][e4], acc[mt][7][e4]};
             }
     }
+}
+
+template <int MT, int NCH>
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
+    constexpr int NC = 8 * NCH;
+    constexpr int MR = 16 * MT;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * NC;
+    const int nkb = (p.K + 31) / 32;
+    const int per = (nkb + S_WAVES - 1) / S_WAVES;
+    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16<MT, NCH>(p, n0, kb0, kb1, acc);
+    acc_to_lds<MT, NCH>(red, acc);
     __syncthreads();
     reduce_epilogue<MR, NC>(p, red, n0);
+}
+
+// Stream-K decode (bf16 weights, M <= 16, 128-column blocks): the (column block, 32-row
+// block) units are dealt to the G workgroups in equal contiguous ranges, so every CU streams
+// the same number of weight bytes even when the column blocks do not divide among the CUs
+// (16 x 28672: 224 blocks on 256 CUs).  A range covers whole column blocks or parts of at
+// most a few; a workgroup that holds only part of a block writes its partial tile to slot
+// (its index - the index of the block's first workgroup) of the block, counts its 32-row
+// blocks in, and the one that completes the count sums the slots in order and runs the
+// epilogue.  The handoff is the one of the 8-bit split (device-scope accesses, no fences).
+__device__ __forceinline__ int sk_owner(int64_t unit, int64_t U, int G) {
+    int w = (int)(unit * G / U);
+    while (w + 1 < G && U * (w + 1) / G <= unit) ++w;
+    while (w > 0 && U * w / G > unit) --w;
+    return w;
+}
+
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
+    constexpr int MT = 1, NCH = 16, NC = 128, MR = 16, CH = NC / 8, MAXS = 8;
+    constexpr int SC1 = 16;  // cache policy operand: device scope
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    __shared__ int s_last;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+    const int ncb = (p.N + NC - 1) / NC, nkb = (p.K + 31) / 32;
+    const int64_t U = (int64_t)ncb * nkb;
+    const int64_t u1 = U * (wg + 1) / G;
+    const int slots = p.split;  // tile slots per column block (plan scratch)
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.split_ws, (int64_t)ncb * slots * MR * NC * 4);
+
+    for (int64_t u = U * wg / G; u < u1;) {
+        const int cb = (int)(u / nkb), kbA = (int)(u % nkb);
+        const int kbB = (int)((u1 - u) < (int64_t)(nkb - kbA) ? kbA + (u1 - u) : nkb);
+        const int n0 = cb * NC;
+        const int per = (kbB - kbA + S_WAVES - 1) / S_WAVES;
+        const int k0 = min(kbB, kbA + wave * per), k1 = min(kbB, k0 + per);
+        f32x4 acc[MT][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        stream_bf16<MT, NCH>(p, n0, k0, k1, acc);
+        acc_to_lds<MT, NCH>(red, acc);
+        __syncthreads();
+        if (kbA == 0 && kbB == nkb) {
+            reduce_epilogue<MR, NC>(p, red, n0);
+        } else {
+            const int first = sk_owner((int64_t)cb * nkb, U, G);
+            const int nsl = sk_owner((int64_t)cb * nkb + nkb - 1, U, G) - first + 1;
+            const uint32_t mine = (uint32_t)(((int64_t)cb * slots + (wg - first)) * (MR * NC) * 4);
+            // this workgroup's partial tile: sum of its waves, 16-byte device-scope stores
+            for (int item = threadIdx.x; item < MR * CH; item += S_THREADS) {
+                const int r = item / CH, c = item % CH;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < S_WAVES; ++w) {
+                    a += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8];
+                    b += *(const f32x4 *)&red[(w * MR + r) * NC + c * 8 + 4];
+                }
+                const uint32_t off = mine + (uint32_t)(r * NC + c * 8) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), rt, off, 0, SC1);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rt, off + 16, 0, SC1);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile stores are complete
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const uint32_t add = (uint32_t)(kbB - kbA);
+                const uint32_t prev = __hip_atomic_fetch_add(p.split_cnt + cb, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_last = prev + add == (uint32_t)nkb;
+            }
+            __syncthreads();
+            if (s_last) {
+                const bool vec_ok = epi_vec_ok(p);
+                with_act(p.epi.act, [&](auto ACTC) {
+                    constexpr int ACT = decltype(ACTC)::value;
+                    for (int item = threadIdx.x; item < MR * CH; item += S_THREADS) {
+                        const int r = item / CH, c = item % CH;
+                        const int m = r, n = n0 + c * 8;
+                        if (m >= p.M || n >= p.N) continue;
+                        // every slot requested at once (slots past nsl read zeros), summed in slot order
+                        f32x4 tl[MAXS][2];
+#pragma unroll
+                        for (int q = 0; q < MAXS; ++q) {
+                            const uint32_t off =
+                                q < nsl ? (uint32_t)((((int64_t)cb * slots + q) * (MR * NC) + r * NC + c * 8) * 4) : OOB;
+                            tl[q][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, SC1));
+                            tl[q][1] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, q < nsl ? off + 16 : OOB, 0, SC1));
+                        }
+                        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int q = 0; q < MAXS; ++q)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                v[e] += tl[q][0][e];
+                                v[4 + e] += tl[q][1][e];
+                            }
+                        finish_chunk<ACT>(p, vec_ok, m, n, v);
+                    }
+                });
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(p.split_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();  // red and s_last are reused by the next range segment
+        u += kbB - kbA;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -656,6 +776,31 @@ int64_t w8_split_scratch_bytes(const Problem &p, int split) {
     return split * ncb * 16 * 128 * 4 + ncb * 4;
 }
 
+// Tile slots per column block of the stream-K decode kernel, or 0 for the plain kernel.
+// Stream-K is used where the plain kernel leaves CUs idle (its workgroups are not a multiple
+// of the CU count) and each workgroup's range is one piece of one column block (the ranges
+// divide the blocks evenly): a range that straddles two blocks streams two short segments
+// with a handoff each, which measured slower than idle CUs (16 x 28672 x 8192: 98 us against
+// 93 us for the plain kernel on 224 of 256 CUs).  At 16 x 8192 x 8192 it is a 4-way K split.
+int bf16_sk_slots(const Problem &p, int cu_count) {
+    if (p.mode != MODE_GENERIC || p.ab_type != GE_BF16 || p.M > 16 || cu_count <= 0) return 0;
+    const int nch = bf16_chunks(p.N, cu_count);
+    const int64_t plain = (p.N + 8 * nch - 1) / (8 * nch);
+    if (plain % cu_count == 0) return 0;
+    const int64_t ncb = (p.N + 127) / 128, nkb = (p.K + 31) / 32, U = ncb * nkb;
+    if (U % cu_count || U < 8ll * cu_count) return 0;
+    const int64_t per = U / cu_count;  // units per workgroup
+    if (per >= nkb || nkb % per) return 0;
+    const int64_t slots = nkb / per;
+    return slots >= 2 && slots <= 8 ? (int)slots : 0;
+}
+
+int64_t bf16_sk_scratch_bytes(const Problem &p, int slots) {
+    if (slots <= 0) return 0;
+    const int64_t ncb = (p.N + 127) / 128;
+    return ncb * slots * 16 * 128 * 4 + ncb * 4;
+}
+
 const char *skinny_kernel_name(const Problem &p, int cu_count) {
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
         static const char *names[2][4] = {
@@ -667,6 +812,7 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
         return names[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
+    if (bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
     return names[p.M > 16][bf16_chunks(p.N, cu_count) == 16 ? 0 : 1];
@@ -705,6 +851,10 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
             hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
         else
             hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+        return hipGetLastError();
+    }
+    if (p.mode == MODE_GENERIC && p.M <= 16 && p.split > 1 && p.split_ws && p.split_cnt) {
+        hipLaunchKernelGGL(skinny_bf16_sk_kernel, dim3(cu_count > 0 ? cu_count : 256), dim3(S_THREADS), 0, s, p);
         return hipGetLastError();
     }
     const int nch = bf16_chunks(p.N, cu_count > 0 ? cu_count : 256);

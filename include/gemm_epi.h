@@ -41,7 +41,8 @@
  * Plans are immutable once made: one plan may be used from several threads
  * and streams at once, with one exception: a plan that owns device scratch
  * (gemm_epi_plan_scratch_bytes() > 0: 8-bit weight plans with M <= 16 whose
- * K is split over workgroups, and prepacked int4 plans with M > 16, which
+ * K is split over workgroups, bf16 generic plans with M <= 16 whose K is
+ * split the same way (stream-K), and prepacked int4 plans with M > 16, which
  * convert X to fp16 into it) must not run on two streams at once, since its
  * launches share that scratch.
  */
@@ -150,10 +151,14 @@ GE_API void ge_desc_init(ge_desc *d);
  * *out receives a library-owned plan that the caller releases with
  * gemm_epi_plan_destroy().  Queries the current device (architecture and
  * compute-unit count); allocates host memory, and a zeroed device scratch
- * for two kinds of plan: 8-bit weight plans with M <= 16 whose column blocks
- * alone do not fill the GPU (the cross-workgroup K split: S * ceil(N/128) *
- * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters, S in
- * {2, 4, 8}), and prepacked int4 plans with M > 16 (the fp16 copy of X,
+ * for three kinds of plan: 8-bit weight plans with M <= 16 whose column
+ * blocks alone do not fill the GPU (the cross-workgroup K split: S *
+ * ceil(N/128) * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters,
+ * S in {2, 4, 8}); bf16 generic plans with M <= 16 whose column blocks leave
+ * CUs idle and whose (column block, 32-row K block) units divide evenly into
+ * one K piece of one column block per CU (stream-K: the same tiles and
+ * counters, S = pieces per block in {2..8}; e.g. 16 x 8192 x 8192 on 256
+ * CUs, S = 4); and prepacked int4 plans with M > 16 (the fp16 copy of X,
  * M * K * 2 bytes).  Such a call synchronises the device, so make plans
  * outside graph capture.
  * Errors: INVALID_ARG (bad descriptor or null out), UNSUPPORTED, NO_DEVICE.

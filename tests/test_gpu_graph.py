@@ -73,7 +73,7 @@ def _scratch_inputs(seed):
 def test_scratch_using_calls_replay_in_a_graph():
     # calls whose plans own device scratch: the 8-bit K split (tile handoff, counters that re-arm
     # themselves), the int4 tile path (activation pre-pass into scratch) and the SwiGLU launch
-    # whose partial last round is peeled into 128 x 128 tiles
+    # whose partial last round is peeled into 128 x 128 tiles, and the stream-K decode kernel
     g = torch.Generator().manual_seed(9)
     x8, x4, xs = _scratch_inputs(2)
     Wq8 = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
@@ -83,22 +83,29 @@ def test_scratch_using_calls_replay_in_a_graph():
     Wg = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
     Wu = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
 
+    xd = (torch.randn(16, 2048, generator=g)).bfloat16().to(DEV)
+    Wd = (torch.randn(2048, 4096, generator=g) / 16).bfloat16().to(DEV)
+    bd = (torch.randn(4096, generator=g) * 0.1).bfloat16().to(DEV)
+
     def outs():
         return [torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV),
                 torch.empty(256, 1024, dtype=torch.bfloat16, device=DEV),
-                torch.empty(512, 136 * 128, dtype=torch.bfloat16, device=DEV)]
+                torch.empty(512, 136 * 128, dtype=torch.bfloat16, device=DEV),
+                torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV)]
 
     def prepare(o):
         return [ge.prepare_w4_gemm(x8, Wq8, s8, out=o[0], zero_point=128, fmt="u8"),
                 ge.prepare_w4_gemm(x4, Wp4, s4, out=o[1], prepacked=True),
-                ge.prepare_swiglu(xs, Wg, Wu, out=o[2])]
+                ge.prepare_swiglu(xs, Wg, Wu, out=o[2]),
+                ge.prepare_gemm_epilogue(xd, Wd, bias=bd, out=o[3])]
 
     oe, og = outs(), outs()
     eager, graph_calls = prepare(oe), prepare(og)
     kernels = [f._plan.kernel for f in eager]
     assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1].startswith("tile_w4")
     assert kernels[2] == "tile_swiglu_256x128x32+128x128x32"
-    assert all(f._plan.scratch_bytes > 0 for f in eager[:2])
+    assert kernels[3] == "skinny_bf16_m16_128col_streamk"
+    assert all(f._plan.scratch_bytes > 0 for f in eager[:2] + eager[3:])
     for f in eager + graph_calls:
         f()
     torch.cuda.synchronize()

@@ -331,11 +331,49 @@ def test_skinny_bf16_bias_residual_gelu(M, N, K):
     assert_close(out, ref, TOL_BF16, f"skinny {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 2048), (7, 8104, 2040), (1, 4096, 4096)])
+def test_skinny_streamk_bias_residual_gelu(M, N, K):
+    # too few column blocks for the CUs: the (column block, 32-row block) units are dealt evenly to
+    # one workgroup per CU, each workgroup one K piece of one column block, partial tiles handed
+    # off through the plan's scratch (4 or 8 pieces per block here)
+    p = ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True, act="gelu_tanh")
+    assert p.kernel == "skinny_bf16_m16_128col_streamk" and p.scratch_bytes > 0
+    w = workloads.WORKLOADS["skinny_decode"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + K)
+    d = dev_inputs(inp)
+    out = ge.gemm_epilogue(d["A"], d["B"], bias=d["bias"], R=d["R"], act="gelu_tanh")
+    ref = oracle.gemm_epilogue(inp["A"], inp["B"], "bf16", bias=inp["bias"], act="gelu_tanh", R=inp["R"])
+    assert_close(out, ref, TOL_BF16, f"streamk {M}x{N}x{K}")
+
+
+def test_skinny_streamk_plan_and_repeat_calls():
+    p = ge.plan(ge.KIND_GENERIC, 16, 8192, 8192, bias=True, R=True)
+    # 64 column blocks x 256 row blocks over 256 workgroups: 64 units each, 4 workgroups per block
+    assert p.kernel == "skinny_bf16_m16_128col_streamk"
+    assert p.scratch_bytes == 64 * 4 * 16 * 128 * 4 + 64 * 4
+    # a range that would straddle two column blocks keeps the plain kernel
+    for N in (28672, 32768):
+        assert ge.plan(ge.KIND_GENERIC, 16, N, 8192, bias=True, R=True).kernel == "skinny_bf16_m16_128col"
+    w = workloads.WORKLOADS["skinny_decode"].with_shape(M=16, N=4096, K=2048)
+    inp = workloads.make_inputs(w, seed=4)
+    d = dev_inputs(inp)
+    outs = [torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV) for _ in range(200)]
+    for o in outs:
+        ge.gemm_epilogue(d["A"], d["B"], bias=d["bias"], R=d["R"], out=o)
+    torch.cuda.synchronize()
+    first = outs[0].view(torch.int16)
+    assert all(torch.equal(o.view(torch.int16), first) for o in outs[1:])
+    ref = oracle.gemm_epilogue(inp["A"], inp["B"], "bf16", bias=inp["bias"], R=inp["R"])
+    assert_close(outs[0], ref, TOL_BF16, "streamk 16x4096x2048")
+
+
 def test_skinny_plan_picks_the_streaming_kernel():
     p = ge.plan(ge.KIND_GENERIC, 16, 28672, 8192, bias=True, R=True)
     assert p.kernel.startswith("skinny_bf16")
-    q16 = ge.plan(ge.KIND_GENERIC, 16, 4096, 8192, bias=True, R=True)
+    q16 = ge.plan(ge.KIND_GENERIC, 16, 4096, 1024, bias=True, R=True)
     assert q16.kernel == "skinny_bf16_m16_64col"  # 64 workgroups of 64 columns beat 32 of 128
+    # at K = 8192 there is enough work to split each column block's K range over 8 workgroups
+    assert ge.plan(ge.KIND_GENERIC, 16, 4096, 8192, bias=True, R=True).kernel.endswith("_streamk")
     q = ge.plan(ge.KIND_W4, 16, 8192, 8192, b_type=ge.U4X2, bias=True, prepacked=True)
     assert q.kernel.startswith("skinny_w4")
 
