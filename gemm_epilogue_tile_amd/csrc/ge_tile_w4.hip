@@ -23,22 +23,33 @@ namespace {
 // streams the fp16 rows by direct loads straight into a ring of swizzled
 // fragment buffers, as the bf16 tile kernel does.
 //
-// Weights: every 32-deep stage, each of the 256 threads dequantises 16 codes
-// (one lane in each of two prepacked 16-column tiles) and writes them to LDS
-// in MFMA fragment order, so every code is converted once per workgroup
-// instead of once per wave that uses it.
+// Waves: the four waves sit side by side (wave w: all 128 rows, columns
+// n0 + 32 w .. + 31), so no two waves use the same weights.  Each wave loads
+// the codes of its two prepacked 16-column tiles and their 32 scales into a
+// private LDS slot by direct loads (no barrier: a wave reads back only what
+// it loaded itself), and every lane dequantises its own B fragments in
+// registers, straight from the 16 prepacked bytes its load delivered: 16
+// codes per lane per stage, each code converted once per workgroup, with no
+// round trip of fp16 weights through LDS.  Only the activations are shared
+// through LDS.  (Sharing dequantised fp16 fragments between 2 x 2 waves
+// through LDS took 92.5 us per call at 512 x 8192 x 8192; this layout 72.)
 //
 // Pipeline, per stage s (unrolled by 8 = two 128-row scale groups): the fp16
 // activations of stage s + 6 and (every fourth stage) the raw codes and
-// scales of the group after next go straight to LDS by direct loads (their
-// waits are counted by hand); the codes of stage s + 2 are dequantised into
-// LDS buffer (s + 2) % 2; the fragments of stage s + 1 are read; the 16 MFMAs
-// of stage s run on the fragments read one stage earlier.  The side work is
-// spread between the MFMAs; one barrier per stage.
+// scales of the group after next go straight to LDS by direct loads (waits
+// counted by hand; the stage's position sits in the buffer resource, so no
+// vector instruction computes an address); every fourth stage the codes and
+// scales of the next group are read into registers; the activation fragments
+// of stage s + 1 are read and its B fragments dequantised; the 16 MFMAs of
+// stage s run on the fragments prepared one stage earlier.  One barrier per
+// stage.
 //
-// Dequant per pair of codes: the codes are OR-ed into the mantissa of fp16
-// 1024 (giving 1024 + c), then a packed subtract of 1024 + z and a packed
-// multiply by s.
+// Dequant: a dword holds 8 codes, pair w (w = 0..3) at bits 4 w .. 4 w + 3 of
+// each 16-bit half.  Pairs at bits 0..3 are OR-ed into the mantissa of fp16
+// 1024 (ulp 1), pairs at bits 4..7 into that of fp16 64 (ulp 1/16), which
+// gives magic + c exactly either way with one v_and_or_b32 (pairs 2 and 3
+// after one shift by 8); then a packed subtract of magic + z and a packed
+// multiply by s.  13 instructions per 8 codes.
 // ---------------------------------------------------------------------------
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -57,29 +68,17 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 &w) {
     return r;
 }
 
-// one packed dword of 8 codes -> 8 fp16 weights (k in order), (c - z) * s
-__device__ __forceinline__ u32x4 dequant_w4_f16(uint32_t w, f16x2 s2, f16x2 z2) {
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t t = ((w >> (4 * q)) & 0x000f000fu) | 0x64006400u;  // fp16 1024 + c
-        const f16x2 v = (__builtin_bit_cast(f16x2, t) - z2) * s2;
-        r[q] = __builtin_bit_cast(uint32_t, v);
-    }
-    return r;
-}
-
-constexpr int W4_BM = 128, W4_BN = 128, W4_MT = 4, W4_NT = 4;
-constexpr int W4_UNROLL = 8;                   // stages per loop trip (ring sizes divide it)
-constexpr int W4_AD = 6;                       // activation loads run this many stages ahead
-// LDS (bytes): fp16 activations, ring of 8 stages ([128][32] in the swizzled fragment layout); raw
-// codes of two groups (prepacked blocks of the 8 tiles); raw scales of two groups (one 1 KB slot
-// per wave, the wave's 32 columns in its first 64 bytes); dequantised fp16 B of two stages
+constexpr int W4_BM = 128, W4_BN = 128;
+constexpr int W4_MT = 8, W4_NT = 2;          // 16x16 tiles per wave: 128 rows x 32 columns
+constexpr int W4_UNROLL = 8;                 // stages per loop trip (ring sizes divide it)
+constexpr int W4_AD = 6;                     // activation loads run this many stages ahead
+// LDS (bytes): fp16 activations, ring of 8 stages ([128][32] in the swizzled fragment layout);
+// per wave, the raw codes of two groups (its two prepacked 16-column tiles, 1 KB each) and the
+// raw scales of two groups (one 1 KB slot per group, the wave's 32 columns in its first 64 bytes)
 constexpr int W4_A16 = 0, W4_A16_STAGE = W4_BM * 64;
-constexpr int W4_RAWB = W4_A16 + W4_UNROLL * W4_A16_STAGE, W4_RAWB_GROUP = (W4_BN / 16) * 1024;
-constexpr int W4_RAWS = W4_RAWB + 2 * W4_RAWB_GROUP, W4_RAWS_GROUP = 4 * 1024;
-constexpr int W4_B16 = W4_RAWS + 2 * W4_RAWS_GROUP, W4_B16_STAGE = (W4_BN / 16) * 1024;
-constexpr int W4_LDS = W4_B16 + 2 * W4_B16_STAGE;  // 104 KB
+constexpr int W4_CODES = W4_A16 + W4_UNROLL * W4_A16_STAGE, W4_CODES_WAVE = 2 * 2 * 1024;
+constexpr int W4_SCALES = W4_CODES + 4 * W4_CODES_WAVE, W4_SCALES_WAVE = 2 * 1024;
+constexpr int W4_LDS = W4_SCALES + 4 * W4_SCALES_WAVE;  // 88 KB
 
 // direct loads issued by each wave: 2 per stage (activations), 3 per group (codes, scales)
 constexpr int W4_LA = 2, W4_LB = 3;
@@ -95,6 +94,17 @@ constexpr int w4_inflight(int u) {
 }
 static_assert(w4_inflight(0) == w4_inflight(1) && w4_inflight(1) == w4_inflight(3), "one group load among three stages");
 
+// buffer resource over [base, base + bytes), bytes already known to be in range (no 64-bit compare)
+__device__ __forceinline__ i32x4 rsrc32(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(1, 1)))
 void tile_w4_kernel(Problem p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -102,7 +112,6 @@ void tile_w4_kernel(Problem p) {
     const AS3 char *s3 = (const AS3 char *)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
 
     const int tiles_m = (p.M + W4_BM - 1) / W4_BM, tiles_n = p.N / W4_BN;
     const int total = tiles_m * tiles_n;
@@ -116,10 +125,13 @@ void tile_w4_kernel(Problem p) {
     const int m0 = tm * W4_BM, n0 = tn * W4_BN;
     const int ngroups = p.K / 128, nst = p.K / T_BK;
 
-    // ---- direct loads (into LDS) ----
-    // fp16 activations (dense [M][K] rows): wave w, instruction q -> rows 16 (2 w + q) + lane/4;
-    // LDS slot lane % 4 of the row holds logical chunk (lane % 4) ^ ((row >> 1) & 3)
-    const i32x4 rA = make_rsrc((const char *)p.A16 + (int64_t)m0 * p.K * 2, (int64_t)(p.M - m0) * p.K * 2);
+    // Direct loads.  The lane offsets are fixed; the stage's (or group's) position goes into the
+    // buffer resource (scalar arithmetic), whose range is empty past the end of K, so the loop
+    // spends no vector instructions on addresses.
+    // activations: wave w loads rows 32 w .. 32 w + 31 of each stage, lane l row l / 4 of 16, LDS
+    // slot l % 4 of the row holding logical chunk (l % 4) ^ ((row >> 1) & 3)
+    const char *a_base = (const char *)p.A16 + (int64_t)m0 * p.K * 2;
+    const int64_t a_bytes = (int64_t)(p.M - m0) * p.K * 2;
     uint32_t a_src[W4_LA];
 #pragma unroll
     for (int q = 0; q < W4_LA; ++q) {
@@ -127,91 +139,82 @@ void tile_w4_kernel(Problem p) {
         const int chunk = (lane & 3) ^ ((row_l >> 1) & 3);
         a_src[q] = (uint32_t)(((wave * W4_LA + q) * 16 + row_l) * p.K * 2 + chunk * 16);
     }
-    auto load_a = [&](int d, int slot) {  // stage d (runtime) into ring slot d % 8 (compile-time)
-        const bool in = d < nst;
+    auto load_a = [&](int d, int slot) {
+        const i32x4 r = rsrc32(a_base + d * 64, d < nst ? (uint32_t)(a_bytes - d * 64) : 0u);
 #pragma unroll
         for (int q = 0; q < W4_LA; ++q)
-            load_lds16(rA, lds0 + W4_A16 + slot * W4_A16_STAGE + (wave * W4_LA + q) * 1024,
-                       in ? a_src[q] + d * 64 : OOB);
+            load_lds16(r, lds0 + W4_A16 + slot * W4_A16_STAGE + (wave * W4_LA + q) * 1024, a_src[q]);
     };
-    // codes: wave w, instruction q -> tile 2 w + q (1 KB block of the group); scales: the wave's
-    // 32 columns (lanes 0..3; the other lanes read zeros into the rest of its 1 KB slot)
-    const i32x4 rB = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
-    const i32x4 rS = make_rsrc(p.scales, ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2);
-    auto load_b = [&](int g, int slot) {  // group g into ring slot g % 2
+    // codes of the wave's tiles 2 w, 2 w + 1 (group g: 1 KB at g KB into each tile's run) and
+    // their 32 scales (lanes 0..3) into the wave's slot
+    const int64_t b_bytes = (int64_t)p.K * p.N / 2, s_bytes = ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2;
+    uint32_t b_src[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) b_src[q] = (uint32_t)((((int64_t)(n0 / 16 + wave * 2 + q) * ngroups) * 64 + lane) * 16);
+    const uint32_t s_src = lane < 4 ? (uint32_t)((n0 + wave * 32) * 2 + lane * 16) : OOB;
+    const uint32_t codes_w = W4_CODES + wave * W4_CODES_WAVE, scales_w = W4_SCALES + wave * W4_SCALES_WAVE;
+    auto load_b = [&](int g, int slot) {
         const bool in = g < ngroups;
+        const i32x4 rb = rsrc32((const char *)p.B + (int64_t)g * 1024, in ? (uint32_t)(b_bytes - (int64_t)g * 1024) : 0u);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int tt = wave * 2 + q;
-            load_lds16(rB, lds0 + W4_RAWB + slot * W4_RAWB_GROUP + tt * 1024,
-                       in ? (uint32_t)((((int64_t)(n0 / 16 + tt) * ngroups + g) * 64 + lane) * 16) : OOB);
-        }
-        load_lds16(rS, lds0 + W4_RAWS + slot * W4_RAWS_GROUP + wave * 1024,
-                   in && lane < 4 ? (uint32_t)(((int64_t)g * p.ld_s + n0 + wave * 32) * 2) + lane * 16 : OOB);
+        for (int q = 0; q < 2; ++q) load_lds16(rb, lds0 + codes_w + slot * 2048 + q * 1024, b_src[q]);
+        const int64_t so = (int64_t)g * p.ld_s * 2;
+        const i32x4 rs = rsrc32((const char *)p.scales + so, in ? (uint32_t)(s_bytes - so) : 0u);
+        load_lds16(rs, lds0 + scales_w + slot * 1024, s_src);
     };
 
-    // ---- per-thread dequantisation: code blocks bi and bi + 256 (tile bi / 64, lane bi % 64);
-    //      consecutive threads touch consecutive 16-byte LDS chunks, free of bank conflicts ----
-    const int bi = tid;  // second block: bi + 256 (tile + 4, same lane)
-    const int sc_col = (bi >> 6) * 16 + (bi & 15);  // second block: sc_col + 64
-    const _Float16 zh = (_Float16)(1024.0f + (float)p.zero_point);
-    const f16x2 z2 = f16x2{zh, zh};
-    const uint32_t nib_mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
-    uint32_t f16_magic = 0x64006400u;
-    asm volatile("" : "+v"(f16_magic));
-    u32x4 craw[2];   // the two code blocks of the current group (read once per group)
-    f16x2 cs2[2];    // their scales
-    // dequantisation of one stage in 9 pieces, so that it can be spread between the MFMAs:
-    // piece 0 reads the codes and scales at a group's first stage; pieces 1..8 dequantise one
-    // code pair each (writing a lane fragment after every fourth)
-    u32x4 dq_out;
-    auto convert_piece = [&](int dd, int k) {  // stage d, dd = d % 8 (compile-time)
-        const int buf = dd & 1, gs = (dd >> 2) & 1, q = dd & 3;
-        AS3 char *w3 = (AS3 char *)smem;
-        if (k == 0) {
-            if (q == 0) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    craw[e] = *(const AS3 u32x4 *)(s3 + W4_RAWB + gs * W4_RAWB_GROUP + (bi + 256 * e) * 16);
-                    const int col = sc_col + 64 * e;
-                    const uint16_t sr =
-                        *(const AS3 uint16_t *)(s3 + W4_RAWS + gs * W4_RAWS_GROUP + (col >> 5) * 1024 + (col & 31) * 2);
-                    const _Float16 sh = (_Float16)bf16_to_f32(sr);
-                    cs2[e] = f16x2{sh, sh};
-                }
-            }
-        } else {
-            const int e = (k - 1) >> 2, w = (k - 1) & 3;  // code block e, pair w
-            // (empty asm ties on the piece's input and output keep it between its two MFMAs)
-            uint32_t cin = craw[e][q];
-            asm volatile("" : "+v"(cin));
-            // fp16 1024 + c: (codes & 0x000f000f) | 0x64006400 in one v_and_or_b32 (VOP3 takes no
-            // literals here, so the mask sits in an SGPR and the magic number in a VGPR)
-            uint32_t tt;
-            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(tt) : "v"(w ? cin >> (4 * w) : cin), "s"(nib_mask), "v"(f16_magic));
-            uint32_t o = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, tt) - z2) * cs2[e]);
-            asm volatile("" : "+v"(o));
-            dq_out[w] = o;
-            if (w == 3) *(AS3 u32x4 *)(w3 + W4_B16 + buf * W4_B16_STAGE + (bi + 256 * e) * 16) = dq_out;
-        }
-    };
-    auto convert = [&](int dd) {
-#pragma unroll
-        for (int k = 0; k <= 8; ++k) convert_piece(dd, k);
-    };
-
-    // ---- fragments ----
+    // a group's codes (lane's own 16 bytes of each tile) and scales (column 16 e + lane % 16)
     const int frow = lane & 15, fgrp = lane >> 4;
-    const int a_frag = W4_A16 + swz_a(wm * 64 + frow, fgrp);
-    const int b_frag = W4_B16 + (wn * W4_NT * 64 + lane) * 16;
-    f16x8 fa[2][W4_MT], fb[2][W4_NT];
-    // read r of stage d (dd = d % 8): A and B fragments alternate; registers d % 2
-    auto read_frag = [&](int dd, int r) {
-        const int i = r >> 1, buf = dd & 1;
-        if ((r & 1) == 0)
-            fa[buf][i] = *(const AS3 f16x8 *)(s3 + a_frag + dd * W4_A16_STAGE + i * 1024);
+    // code pairs at bits 0..3 (of each half) go into the mantissa of fp16 1024 (ulp 1), pairs at
+    // bits 4..7 into that of fp16 64 (ulp 1/16): both give magic + c exactly, with one v_and_or_b32
+    // and no shift for the latter
+    const _Float16 zl = (_Float16)(1024.0f + (float)p.zero_point), zh = (_Float16)(64.0f + (float)p.zero_point);
+    const f16x2 zlo2 = f16x2{zl, zl}, zhi2 = f16x2{zh, zh};
+    const uint32_t mask_lo = __builtin_amdgcn_readfirstlane(0x000f000fu);
+    const uint32_t mask_hi = __builtin_amdgcn_readfirstlane(0x00f000f0u);
+    uint32_t magic_lo = 0x64006400u, magic_hi = 0x54005400u;
+    asm volatile("" : "+v"(magic_lo), "+v"(magic_hi));
+    u32x4 craw[2][2];
+    f16x2 cs2[2][2];
+    auto read_group = [&](int gp) {  // ring slot gp = group parity (compile-time)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            craw[gp][e] = *(const AS3 u32x4 *)(s3 + codes_w + gp * 2048 + e * 1024 + lane * 16);
+            const uint16_t sr = *(const AS3 uint16_t *)(s3 + scales_w + gp * 1024 + (16 * e + frow) * 2);
+            const _Float16 sh = (_Float16)bf16_to_f32(sr);
+            cs2[gp][e] = f16x2{sh, sh};
+        }
+    };
+    // B fragments of stage d (dd = d % 8): piece k = 0..7 dequantises code pair k % 4 of tile k / 4
+    // (pair w holds the nibbles 4 w .. 4 w + 3 of each half of the dword; pairs 2, 3 after a shift by 8)
+    f16x8 fb[2][W4_NT];
+    u32x4 dq[W4_NT];
+    uint32_t csh[W4_NT];
+    auto dequant_piece = [&](int dd, int k) {
+        const int gp = (dd >> 2) & 1, q = dd & 3, e = k >> 2, w = k & 3;
+        uint32_t src;
+        if (w < 2) {
+            src = craw[gp][e][q];
+            asm volatile("" : "+v"(src));
+            if (w == 0) csh[e] = src >> 8;
+        } else {
+            src = csh[e];
+        }
+        uint32_t tt;
+        if (w & 1)
+            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(tt) : "v"(src), "s"(mask_hi), "v"(magic_hi));
         else
-            fb[buf][i] = *(const AS3 f16x8 *)(s3 + b_frag + buf * W4_B16_STAGE + i * 1024);
+            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(tt) : "v"(src), "s"(mask_lo), "v"(magic_lo));
+        uint32_t o = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, tt) - ((w & 1) ? zhi2 : zlo2)) * cs2[gp][e]);
+        asm volatile("" : "+v"(o));
+        dq[e][w] = o;
+        if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(f16x8, dq[e]);
+    };
+
+    const int a_frag = W4_A16 + swz_a(frow, fgrp);
+    f16x8 fa[2][W4_MT];
+    auto read_a = [&](int dd, int i) {
+        fa[dd & 1][i] = *(const AS3 f16x8 *)(s3 + a_frag + dd * W4_A16_STAGE + i * 1024);
     };
 
     f32x4 acc[W4_MT][W4_NT];
@@ -227,8 +230,8 @@ void tile_w4_kernel(Problem p) {
     };
 #define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 
-    // prologue, in the order the loop would have issued it: activations of stage d at "stage" d - 6,
-    // group 0 at -6 and group 1 at -2 (after that stage's activations)
+    // prologue (issue order and waits as in tile_w4_kernel): stage 0's activations, group 0 and
+    // stage 1's activations landed; group 0 read, stage 0's fragments read and dequantised
     load_a(0, 0);
     load_b(0, 0);
     load_a(1, 1);
@@ -237,17 +240,18 @@ void tile_w4_kernel(Problem p) {
     load_a(4, 4);
     load_b(1, 1);
     load_a(5, 5);
-    GE_WAIT_VM(4 * W4_LA + W4_LB);  // everything up to "stage" -5 (A0, B0, A1) landed
+    GE_WAIT_VM(4 * W4_LA + W4_LB);
     lds_barrier();
-    convert(0);
-    convert(1);
-    lds_barrier();
+    read_group(0);
 #pragma unroll
-    for (int r = 0; r < 2 * W4_MT; ++r) read_frag(0, r);
+    for (int i = 0; i < W4_MT; ++i) read_a(0, i);
+#pragma unroll
+    for (int k = 0; k < 2 * 4; ++k) dequant_piece(0, k);
 
-    // main loop, stage s = s0 + u: wait for the loads of stage s - 4 and earlier, barrier, then the
-    // 16 MFMAs of stage s with, between them: the direct loads of stage s + 6 (and at u % 4 == 2 the
-    // group after next), the dequantisation of stage s + 2 and the fragment reads of stage s + 1
+    // stage s = s0 + u: wait for the loads of stage s - 4 and earlier, barrier, then the 16 MFMAs
+    // of stage s with, between them: the direct loads of stage s + 6 (and at u % 4 == 2 the group
+    // after next), at u % 4 == 2 the read of the next group's codes, the activation fragments of
+    // stage s + 1 and its B fragments
     const int nsteps = (nst + W4_UNROLL - 1) / W4_UNROLL * W4_UNROLL;
     for (int s0 = 0; s0 < nsteps; s0 += W4_UNROLL) {
 #pragma unroll
@@ -258,9 +262,7 @@ void tile_w4_kernel(Problem p) {
             else
                 GE_WAIT_VM(w4_inflight(0));
             lds_barrier();
-            // side work after MFMA q: q = 0 direct loads and the code reads of the dequantisation,
-            // q = 1..8 one fragment read each, q = 2..15 the dequantisation pieces
-            const int dd = (u + 2) & (W4_UNROLL - 1);
+            const int dn = (u + 1) & (W4_UNROLL - 1);
 #pragma unroll
             for (int q = 0; q < W4_MT * W4_NT; ++q) {
                 const int i = q & (W4_MT - 1), j = q / W4_MT;
@@ -268,14 +270,13 @@ void tile_w4_kernel(Problem p) {
                 asm volatile("" ::: "memory");
                 if (q == 0) {
                     load_a(s + W4_AD, (u + W4_AD) & (W4_UNROLL - 1));
-                    // s0 is a multiple of 8, so the ring slots are compile-time
-                    if ((u & 3) == 2) load_b((s + 6) >> 2, ((u + 6) >> 2) & 1);
-                    convert_piece(dd, 0);
+                    if ((u & 3) == 2) {
+                        load_b((s + 6) >> 2, ((u + 6) >> 2) & 1);
+                        read_group(((u + 2) >> 2) & 1);  // group (s + 2) / 4, loaded at stage s - 4
+                    }
                 }
-                if (q >= 1 && q <= 2 * W4_MT) read_frag((u + 1) & (W4_UNROLL - 1), q - 1);
-#pragma unroll
-                for (int k = 1; k <= 8; ++k)
-                    if (q >= 2 && 2 + ((k - 1) * 14) / 8 == q) convert_piece(dd, k);
+                if (q >= 1 && q <= W4_MT) read_a(dn, q - 1);
+                if (q >= W4_MT) dequant_piece(dn, q - W4_MT);
                 asm volatile("" ::: "memory");
             }
         }
@@ -289,8 +290,8 @@ void tile_w4_kernel(Problem p) {
         for (int j = 0; j < W4_NT; ++j) asm volatile("" : "+a"(acc[i][j]));
 
     const EpiArgs &e = p.epi;
-    const int mbase = m0 + wm * 64 + frow;
-    const int nbase = n0 + wn * 64 + fgrp * 4;
+    const int mbase = m0 + frow;
+    const int nbase = n0 + wave * 32 + fgrp * 4;
     auto small = [&](int64_t ld) { return ((int64_t)(p.M + 15) * ld + p.N) * 2 < (1ll << 31); };
     const bool all_bf16 = e.d_type == GE_BF16 && small(e.ldd) &&
                           (!(e.flags & GE_FLAG_C) || (e.c_type == GE_BF16 && small(e.ldc))) &&
@@ -300,9 +301,9 @@ void tile_w4_kernel(Problem p) {
         constexpr int ACT = decltype(ACTC)::value;
         if (all_bf16) {
             if (e.flags & GE_FLAG_C)
-                epilogue_bf16<ACT, true>(e, acc, p.M, p.N, mbase, n0 + wn * 64 + fgrp * 8);
+                epilogue_bf16<ACT, true>(e, acc, p.M, p.N, mbase, n0 + wave * 32 + fgrp * 8);
             else
-                epilogue_bf16<ACT, false>(e, acc, p.M, p.N, mbase, n0 + wn * 64 + fgrp * 8);
+                epilogue_bf16<ACT, false>(e, acc, p.M, p.N, mbase, n0 + wave * 32 + fgrp * 8);
             return;
         }
 #pragma unroll
