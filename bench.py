@@ -164,7 +164,11 @@ def build_calls(name, w, inp):
         if w.kind == "generic":
             kw = dict(bias=s.get("bias"), C=s.get("C"), R=s.get("R"), alpha=w.alpha, beta=w.beta, act=w.act,
                       out=o)
-            f = ge.prepare_gemm_epilogue(s["A"], s["B"], **kw)
+            if w.M <= 16 and w.dtype == "bf16" and w.N % 128 == 0 and w.K % 32 == 0:
+                # decode shape: weights converted once to the streaming kernel's layout (a load-time step)
+                f = ge.prepare_gemm_epilogue(s["A"], ge.b_prepack(s["B"]), prepacked=True, **kw)
+            else:
+                f = ge.prepare_gemm_epilogue(s["A"], s["B"], **kw)
             u = ge.prepare_gemm_epilogue(s["A"], s["B"], unfused=True, workspace=ws, **kw)
         elif w.kind == "swiglu":
             f = ge.prepare_swiglu(s["X"], s["Wg"], s["Wu"], out=o)

@@ -18,7 +18,7 @@ __all__ = [
     "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
-    "w4_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS",
+    "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,12 +30,12 @@ F32, BF16, U4X2, U8, FP8E4M3 = 0, 1, 2, 3, 4
 LAYOUT_KN, LAYOUT_NK = 0, 1
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
-FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED = 1, 2, 4, 8, 16
+FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED, FLAG_B_PREPACKED = 1, 2, 4, 8, 16, 32
 
 EXPORTS = [
     "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_plan_scratch_bytes", "gemm_epi_run",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
-    "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack",
+    "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack", "gemm_b_prepack",
     "ge_add_rmsnorm_run",
     "ge_status_string", "ge_last_error", "ge_version",
 ]
@@ -105,6 +105,8 @@ def lib():
             L.gemm_w4_dequant_run.restype = I
             L.gemm_w4_prepack.argtypes = [P] * 4
             L.gemm_w4_prepack.restype = I
+            L.gemm_b_prepack.argtypes = [P] * 4
+            L.gemm_b_prepack.restype = I
             L.ge_add_rmsnorm_run.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
             L.ge_add_rmsnorm_run.restype = I
             L.ge_status_string.argtypes = [I]
@@ -231,7 +233,7 @@ _plan_cache: dict = {}
 def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=BF16, c_type=None,
          bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
          alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
-         lo_first=False, prepacked=False) -> Plan:
+         lo_first=False, prepacked=False, b_prepacked=False) -> Plan:
     """Build (or fetch from a cache) the plan of one problem descriptor on the current device.
 
     Calls with equal descriptors share one plan.  A plan that owns device scratch
@@ -251,7 +253,8 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
     d.alpha, d.beta = alpha, beta
     d.act = ACTS[act] if isinstance(act, str) else int(act)
     d.flags = ((FLAG_BIAS if bias else 0) | (FLAG_C if C else 0) | (FLAG_RESIDUAL if R else 0)
-               | (FLAG_NIBBLE_LO_FIRST if lo_first else 0) | (FLAG_W4_PREPACKED if prepacked else 0))
+               | (FLAG_NIBBLE_LO_FIRST if lo_first else 0) | (FLAG_W4_PREPACKED if prepacked else 0)
+               | (FLAG_B_PREPACKED if b_prepacked else 0))
     d.group_size, d.zero_point = group, zero_point
     torch = _torch()
     key = (kind, bytes(d), torch.cuda.current_device() if torch.cuda.is_available() else -1)
@@ -268,7 +271,7 @@ def _out(M, N, dtype, device, out):
     return _torch().empty((M, N), dtype=dtype, device=device)
 
 
-def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act):
+def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=False):
     M, K = A.shape
     N = B.shape[1] if b_layout == LAYOUT_KN else B.shape[0]
     return plan(KIND_GENERIC, M, N, K, a_type=_dtype_code(A), b_type=_dtype_code(B),
@@ -277,17 +280,19 @@ def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act):
                 r_type=_dtype_code(R) if R is not None else None, b_layout=b_layout,
                 lda=_ld(A), ldb=_ld(B), ldc=_ld(C) if C is not None else 0, ldd=_ld(out),
                 ldr=_ld(R) if R is not None else 0, alpha=alpha, beta=beta, act=act,
-                bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None)
+                bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None, b_prepacked=prepacked)
 
 
 def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
-                  b_layout="KN", out=None, out_dtype=None, stream=None):
-    """D = act(alpha * A @ B + beta * C + bias) + R on the GPU (fused kernel)."""
+                  b_layout="KN", out=None, out_dtype=None, stream=None, prepacked=False):
+    """D = act(alpha * A @ B + beta * C + bias) + R on the GPU (fused kernel).
+
+    ``prepacked``: B is the [K, N] tensor ``b_prepack`` returned (decode shapes, M <= 16)."""
     lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
     M = A.shape[0]
     N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]
     out = _out(M, N, out_dtype or A.dtype, A.device, out)
-    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked)
     _check(lib().gemm_epi_run(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
                               _stream(stream)), "gemm_epi_run")
     return out
@@ -417,10 +422,10 @@ def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
 
 
 def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
-                          b_layout="KN", unfused=False, workspace=None, stream=None) -> Prepared:
+                          b_layout="KN", unfused=False, workspace=None, stream=None, prepacked=False) -> Prepared:
     """Bind one fused (or unfused) generic call to fixed tensors and stream."""
     lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
-    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked)
     ts = [A, B, C, bias, R, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, A.device)
@@ -465,4 +470,15 @@ def w4_prepack(Wq, *, lo_first=False, out=None, stream=None):
     out = out if out is not None else torch.empty(K * N // 2, dtype=torch.uint8, device=Wq.device)
     p = plan(KIND_W4, 1, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), lo_first=lo_first)
     _check(lib().gemm_w4_prepack(p.handle, _ptr(Wq), _ptr(out), _stream(stream)), "gemm_w4_prepack")
+    return out
+
+
+def b_prepack(B, *, out=None, stream=None):
+    """bf16 weights [K, N] -> the prepacked decode layout (same bytes, one-time), returned as a
+    [K, N] tensor whose contents only the prepacked kernels read (``prepacked=True``)."""
+    torch = _torch()
+    K, N = B.shape
+    out = out if out is not None else torch.empty((K, N), dtype=torch.bfloat16, device=B.device)
+    p = plan(KIND_GENERIC, 1, N, K, a_type=BF16, b_type=BF16, d_type=BF16, ldb=_ld(B))
+    _check(lib().gemm_b_prepack(p.handle, _ptr(B), _ptr(out), _stream(stream)), "gemm_b_prepack")
     return out

@@ -105,6 +105,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     e.act = pl->kind == GE_KIND_SWIGLU ? GE_ACT_NONE : d.act;
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
+    p.b_packed = (pl->kind == GE_KIND_GENERIC && (d.flags & GE_FLAG_B_PREPACKED)) ? 1 : 0;
     p.wfmt = wfmt_of(d);
     // scratch goes only to the kernel it was made for (unfused chains run copies of a plan
     // with another kind)
@@ -132,7 +133,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
 hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     if (skinny_supported(p)) return launch_skinny(p, pl->cu_count, s);
     if (tile_supported(p)) return launch_tile(p, pl->cu_count, s);
-    if (p.w4_packed) return hipErrorInvalidValue;  // only the specialised kernels read the packed layout
+    if (p.w4_packed || p.b_packed) return hipErrorInvalidValue;  // only the specialised kernels read packed layouts
     return launch_general(p, s);
 }
 
@@ -230,8 +231,11 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         (int64_t)d.M * d.K >= (1ll << 31))
         return fail(GE_ERR_UNSUPPORTED, "matrix with 2^31 or more elements");
     if (d.act < GE_ACT_NONE || d.act > GE_ACT_SILU) return fail(GE_ERR_INVALID_ARG, "unknown activation %d", d.act);
-    if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED))
+    if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED |
+                    GE_FLAG_B_PREPACKED))
         return fail(GE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags);
+    if ((d.flags & GE_FLAG_B_PREPACKED) && kind != GE_KIND_GENERIC)
+        return fail(GE_ERR_INVALID_ARG, "B_PREPACKED applies to generic bf16 plans");
     if (d.b_layout != GE_LAYOUT_KN && d.b_layout != GE_LAYOUT_NK)
         return fail(GE_ERR_INVALID_ARG, "unknown b_layout %d", d.b_layout);
     if (!is_float_type(d.d_type)) return fail(GE_ERR_INVALID_ARG, "d_type must be F32 or BF16");
@@ -264,6 +268,10 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             return fail(GE_ERR_INVALID_ARG, "int4 flag on a dense product");
         pl.ldb = d.ldb ? d.ldb : (d.b_layout == GE_LAYOUT_KN ? d.N : d.K);
         if (pl.ldb < (d.b_layout == GE_LAYOUT_KN ? d.N : d.K)) return fail(GE_ERR_INVALID_ARG, "ldb too small");
+        if ((d.flags & GE_FLAG_B_PREPACKED) &&
+            (d.a_type != GE_BF16 || d.b_layout != GE_LAYOUT_KN || d.M > 16 || d.N % 128 || d.K % 32))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked bf16 weights need bf16 KN operands, M <= 16, N %% 128 == 0 "
+                                            "and K %% 32 == 0");
     } else if (kind == GE_KIND_SWIGLU) {
         if (d.a_type != GE_BF16 || d.b_type != GE_BF16 || d.d_type != GE_BF16)
             return fail(GE_ERR_UNSUPPORTED, "swiglu needs bf16 X, W and D");
@@ -401,11 +409,14 @@ ge_status gemm_epi_run(const ge_plan *pl, const void *A, const void *B, const vo
     const ge_desc &d = pl->d;
     const size_t es = type_size(d.a_type);
     const size_t nA = ((size_t)(d.M - 1) * pl->lda + d.K) * es;
-    const size_t nB = (d.b_layout == GE_LAYOUT_KN ? (size_t)(d.K - 1) * pl->ldb + d.N
-                                                  : (size_t)(d.N - 1) * pl->ldb + d.K) * es;
+    const size_t nB = (d.flags & GE_FLAG_B_PREPACKED) ? (size_t)d.K * d.N * es
+                      : (d.b_layout == GE_LAYOUT_KN ? (size_t)(d.K - 1) * pl->ldb + d.N
+                                                    : (size_t)(d.N - 1) * pl->ldb + d.K) * es;
     if ((st = check_alias(pl, A, nA, B, nB, C, R, D))) return st;
     if ((st = check_device(pl))) return st;
     const Problem p = make_problem(pl, A, B, nullptr, nullptr, C, bias, R, D);
+    if (p.b_packed && !skinny_supported(p))
+        return fail(GE_ERR_ALIGN, "prepacked bf16 path needs 16-byte aligned A and B and an lda that is a multiple of 8");
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_epi_run launch");
 }
 
@@ -545,6 +556,7 @@ ge_status gemm_epi_run_unfused(const ge_plan *pl, const void *A, const void *B, 
                                const void *bias, const void *R, void *D, void *ws, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (pl->d.flags & GE_FLAG_B_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw weights");
     if (!A || !B) return fail(GE_ERR_INVALID_ARG, "A or B is NULL");
     ge_status st = check_epi_ptrs(pl, C, bias, R, D);
     if (st || (st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
@@ -642,6 +654,23 @@ ge_status gemm_w4_prepack(const ge_plan *pl, const uint8_t *Wq, uint8_t *Wp, voi
     return hip_status(launch_w4_prepack(d.K, d.N, Wq, pl->ldb, (d.flags & GE_FLAG_NIBBLE_LO_FIRST) ? 1 : 0, Wp,
                                         (hipStream_t)stream),
                       "gemm_w4_prepack");
+}
+
+ge_status gemm_b_prepack(const ge_plan *pl, const void *B, void *Bp, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (!B || !Bp) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    const ge_desc &d = pl->d;
+    if (d.b_type != GE_BF16 || d.b_layout != GE_LAYOUT_KN)
+        return fail(GE_ERR_UNSUPPORTED, "prepacking applies to bf16 [K, N] weights");
+    if (d.N % 128 || d.K % 32) return fail(GE_ERR_UNSUPPORTED, "prepack needs N %% 128 == 0 and K %% 32 == 0");
+    if (((uintptr_t)Bp & 15) || ((uintptr_t)B & 1)) return fail(GE_ERR_ALIGN, "B must be 2-byte and Bp 16-byte aligned");
+    const size_t nb = ((size_t)(d.K - 1) * pl->ldb + d.N) * 2, np = (size_t)d.K * d.N * 2;
+    if (overlaps(B, nb, Bp, np)) return fail(GE_ERR_INVALID_ARG, "Bp overlaps B");
+    ge_status st;
+    if ((st = check_device(pl))) return st;
+    return hip_status(launch_b_prepack(d.K, d.N, (const uint16_t *)B, pl->ldb, (uint16_t *)Bp, (hipStream_t)stream),
+                      "gemm_b_prepack");
 }
 
 ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,

@@ -25,6 +25,7 @@ struct Problem {
     int64_t lda, ldb, ld_s;
     int32_t group, zero_point, lo_first;
     int32_t w4_packed;  // B holds int4 weights in the prepacked layout
+    int32_t b_packed;   // B holds bf16 weights in the prepacked decode layout (gemm_b_prepack)
     int32_t wfmt;       // MODE_W4 code format: WFMT_U4 (packed pairs), WFMT_U8, WFMT_FP8
     // cross-workgroup K split of the 8-bit streaming kernel (split > 1): fp32
     // tiles and per-column-block arrival counters, owned by the plan
@@ -55,6 +56,9 @@ const char *tile_w4_kernel_name();
 // One-time conversion of raw [K, N/2] int4 weights to the prepacked layout.
 hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,
                              hipStream_t s);
+
+// One-time conversion of raw [K, N] bf16 weights to the prepacked decode layout.
+hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s);
 
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);

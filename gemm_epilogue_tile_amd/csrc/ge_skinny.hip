@@ -222,6 +222,90 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
     reduce_epilogue<MR, NC>(p, red, n0);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 weights, prepacked (gemm_b_prepack), M <= 16
+// ---------------------------------------------------------------------------
+// Layout: per 128-column block and 32-deep K block, 8 KB: the B fragments of
+// the block's eight 16-column MFMA tiles, 1 KB each, lane l's 16 bytes
+// (column 16 t + l % 16, k = 8 (l / 16) .. + 7) at byte 16 l.  K blocks follow
+// each other, so a wave's share of a column block is one contiguous run, read
+// with 16-byte loads that are already MFMA fragments.  (The raw [K, N] layout
+// gives each wave 256-byte row pieces 2 N bytes apart, and a transpose.)
+// One workgroup per column block, 8 waves splitting K, a ring of SK_RING
+// blocks in flight per wave; the K partials are reduced in LDS and the shared
+// epilogue runs on 8-column row chunks.
+// Blocks kbA .. kbB - 1 of column block cb: wave w takes kbA + w, kbA + w + 8, ..., so at any time
+// the workgroup reads 8 consecutive 8 KB pieces (64 KB of contiguous memory); a ring of SK_RING
+// blocks in flight per wave, blocks past kbB read zeros and add nothing.  acc[t]: lane (g, i)
+// holds rows 4 g + e of column 16 t + i.
+__device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, int kbB, f32x4 (&acc)[8]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int nkb = p.K / 32;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc((const char *)p.B + (int64_t)cb * nkb * 8192, (int64_t)nkb * 8192);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+    const uint32_t xoff = (uint32_t)(((int64_t)i * p.lda + 8 * g) * 2);
+    const bool xin = i < p.M;
+    u32x4 w[SK_RING][8];
+    bf16x8 xr[SK_RING];
+    auto load_blk = [&](int kb, int slot) {
+        const bool in = kb < kbB;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) w[slot][t] = bload16(rw, in ? (uint32_t)(kb * 8192 + t * 1024 + lane * 16) : OOB);
+        xr[slot] = __builtin_bit_cast(bf16x8, bload16(rx, in && xin ? xoff + (uint32_t)kb * 64 : OOB));
+    };
+#pragma unroll
+    for (int j = 0; j < SK_RING - 1; ++j) load_blk(kbA + wave + S_WAVES * j, j);
+    for (int kb = kbA + wave; kb < kbB; kb += S_WAVES * SK_RING) {
+#pragma unroll
+        for (int u = 0; u < SK_RING; ++u) {
+            load_blk(kb + S_WAVES * (u + SK_RING - 1), (u + SK_RING - 1) % SK_RING);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, w[u][t]), acc[t]);
+        }
+    }
+}
+
+// partial tile of one wave (prepacked lane mapping) -> LDS red[wave][16][128]
+__device__ __forceinline__ void accp_to_lds(float *red, const f32x4 (&acc)[8]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) red[(wave * 16 + 4 * g + e4) * 128 + 16 * t + i] = acc[t][e4];
+}
+
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16p_kernel(Problem p) {
+    constexpr int NC = 128, MR = 16;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16p(p, blockIdx.x, 0, p.K / 32, acc);
+    accp_to_lds(red, acc);
+    __syncthreads();
+    reduce_epilogue<MR, NC>(p, red, blockIdx.x * NC);
+}
+
+// raw [K, N] bf16 (row stride ldb) -> the prepacked layout; item u writes the 16 bytes of lane
+// u % 64 of tile (u / 64) % 8 of piece u / 512 = cb * (K / 32) + kb, i.e. bytes 16 u .. 16 u + 15
+__global__ __launch_bounds__(256) void b_prepack_kernel(int32_t K, int32_t N, const uint16_t *B, int64_t ldb,
+                                                        uint16_t *Bp) {
+    const int64_t nkb = K / 32, total = (int64_t)(N / 128) * nkb * 512;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(u & 63), t = (int)((u >> 6) & 7);
+        const int64_t piece = u >> 9, kb = piece % nkb, cb = piece / nkb;
+        const int64_t n = cb * 128 + t * 16 + (l & 15), k = kb * 32 + 8 * (l >> 4);
+        u32x4 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            out[q] = (uint32_t)B[(k + 2 * q) * ldb + n] | ((uint32_t)B[(k + 2 * q + 1) * ldb + n] << 16);
+        *(u32x4 *)(Bp + u * 8) = out;
+    }
+}
+
 // Stream-K decode (bf16 weights, M <= 16, 128-column blocks): the (column block, 32-row
 // block) units are dealt to the G workgroups in equal contiguous ranges, so every CU streams
 // the same number of weight bytes even when the column blocks do not divide among the CUs
@@ -237,6 +321,7 @@ __device__ __forceinline__ int sk_owner(int64_t unit, int64_t U, int G) {
     return w;
 }
 
+template <bool PACKED>
 __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
     constexpr int MT = 1, NCH = 16, NC = 128, MR = 16, CH = NC / 8, MAXS = 8;
     constexpr int SC1 = 16;  // cache policy operand: device scope
@@ -260,8 +345,13 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
         f32x4 acc[MT][8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        stream_bf16<MT, NCH>(p, n0, k0, k1, acc);
-        acc_to_lds<MT, NCH>(red, acc);
+        if constexpr (PACKED) {
+            stream_bf16p(p, cb, kbA, kbB, acc[0]);
+            accp_to_lds(red, acc[0]);
+        } else {
+            stream_bf16<MT, NCH>(p, n0, k0, k1, acc);
+            acc_to_lds<MT, NCH>(red, acc);
+        }
         __syncthreads();
         if (kbA == 0 && kbB == nkb) {
             reduce_epilogue<MR, NC>(p, red, n0);
@@ -712,10 +802,21 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
     return hipGetLastError();
 }
 
+hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s) {
+    const int64_t total = (int64_t)(N / 128) * (K / 32) * 512;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(b_prepack_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s, K, N, B, ldb, Bp);
+    return hipGetLastError();
+}
+
 bool skinny_supported(const Problem &p) {
     if (p.ab_type != GE_BF16 || p.M > 32) return false;
     if (p.mode == MODE_SWIGLU) return false;
     if (!al16(p.A) || (p.lda & 7) || (p.K & 7)) return false;
+    if (p.b_packed)
+        return p.mode == MODE_GENERIC && p.M <= 16 && (p.N % 128) == 0 && (p.K % 32) == 0 && al16(p.B) &&
+               ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31) && (int64_t)p.K * 256 < (1ll << 31);
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
         // 8-bit codes: 8-byte weight loads, 16-byte scale loads, 32-bit offsets
         return p.M <= 16 && (p.K % 32) == 0 && (p.N % 8) == 0 && ((uintptr_t)p.B & 7) == 0 && (p.ldb % 8) == 0 &&
@@ -784,6 +885,17 @@ int64_t w8_split_scratch_bytes(const Problem &p, int split) {
 // 93 us for the plain kernel on 224 of 256 CUs).  At 16 x 8192 x 8192 it is a 4-way K split.
 int bf16_sk_slots(const Problem &p, int cu_count) {
     if (p.mode != MODE_GENERIC || p.ab_type != GE_BF16 || p.M > 16 || cu_count <= 0) return 0;
+    if (p.b_packed) {
+        // prepacked: every range is one contiguous run of memory.  Used when one workgroup per
+        // column block would leave at least half of the CUs idle (16 x 8192 x 8192: 29.5 us
+        // against 52 us), with at most 8 workgroups sharing a block.  With more blocks the
+        // plain kernel wins: at 16 x 28672 x 8192 (224 blocks on 256 CUs) 81.9 us against
+        // 90.4 us, the ranges' second segments and handoffs costing more than 32 idle CUs.
+        const int64_t ncb = p.N / 128, nkb = p.K / 32, U = ncb * nkb;
+        if (2 * ncb > cu_count || U < 8ll * cu_count) return 0;
+        const int64_t slots = (nkb + U / cu_count - 1) / (U / cu_count) + 1;
+        return slots <= 8 ? (int)slots : 0;
+    }
     const int nch = bf16_chunks(p.N, cu_count);
     const int64_t plain = (p.N + 8 * nch - 1) / (8 * nch);
     if (plain % cu_count == 0) return 0;
@@ -812,6 +924,8 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
         return names[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
+    if (p.b_packed)
+        return bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk" : "skinny_bf16_m16_128col_prepacked";
     if (bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
@@ -854,7 +968,15 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
         return hipGetLastError();
     }
     if (p.mode == MODE_GENERIC && p.M <= 16 && p.split > 1 && p.split_ws && p.split_cnt) {
-        hipLaunchKernelGGL(skinny_bf16_sk_kernel, dim3(cu_count > 0 ? cu_count : 256), dim3(S_THREADS), 0, s, p);
+        const dim3 grid(cu_count > 0 ? cu_count : 256);
+        if (p.b_packed)
+            hipLaunchKernelGGL(skinny_bf16_sk_kernel<true>, grid, dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL(skinny_bf16_sk_kernel<false>, grid, dim3(S_THREADS), 0, s, p);
+        return hipGetLastError();
+    }
+    if (p.b_packed) {
+        hipLaunchKernelGGL(skinny_bf16p_kernel, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
         return hipGetLastError();
     }
     const int nch = bf16_chunks(p.N, cu_count > 0 ? cu_count : 256);

@@ -98,6 +98,7 @@ typedef int32_t ge_status;
 #define GE_FLAG_RESIDUAL 4u        /* add R after the activation */
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
 #define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
+#define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 16: B is in the layout gemm_b_prepack writes */
 
 /*
  * Problem descriptor.  Unused fields must be zero.  dtype fields take
@@ -106,7 +107,10 @@ typedef int32_t ge_status;
  *
  * Supported combinations:
  *   GENERIC  a_type == b_type in {F32, BF16}; c/bias/r/d types in {F32, BF16};
- *            b_layout KN or NK; any act; any flags except NIBBLE_LO_FIRST.
+ *            b_layout KN or NK; any act; any flags except NIBBLE_LO_FIRST and
+ *            W4_PREPACKED.  With GE_FLAG_B_PREPACKED (a decode-time weight
+ *            layout): a = b = BF16, b_layout KN, M <= 16, N % 128 == 0,
+ *            K % 32 == 0; the unfused entry points reject such plans.
  *   SWIGLU   a, b, d = BF16, b_layout KN, act = NONE, alpha = 1, no flags
  *            other than none; Wg and Wu share ldb.
  *   W4       a = BF16, b = U4X2, scale_type = BF16, d/bias/c/r in {F32, BF16},
@@ -213,6 +217,23 @@ GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *
  * Wp that does not overlap Wq.  Asynchronous on the stream.
  */
 GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t *Wp, void *stream);
+
+/*
+ * One-time weight conversion for the prepacked bf16 decode kernel (M <= 16;
+ * the way a weight loader would store decode weights): reads B [K, N] bf16
+ * (row stride = the plan's ldb) and writes the same K*N*2 bytes to Bp in the
+ * kernel-native layout: for each 128-column block cb (outer) and 32-row K
+ * block kb (inner), 8 KiB holding the MFMA B fragments of the block's eight
+ * 16-column tiles t, 1 KiB each, lane l's 16 bytes at byte 16*l of tile t
+ * holding column 128*cb + 16*t + l%16 at k = 32*kb + 8*(l/16) + j, j = 0..7
+ * in order.  So each column block's K range is one contiguous run of memory
+ * and every 16-byte load is a finished fragment (no transpose in the
+ * kernel).  Any GENERIC bf16 KN plan of the same N, K and ldb serves (M and
+ * the epilogue are ignored).  Needs N % 128 == 0, K % 32 == 0, a 2-byte
+ * aligned B and a 16-byte aligned Bp that does not overlap B.  Asynchronous
+ * on the stream.
+ */
+GE_API ge_status gemm_b_prepack(const ge_plan *plan, const void *B, void *Bp, void *stream);
 
 /*
  * Deliberately unfused chains, for measurement only: the plain GEMM writes

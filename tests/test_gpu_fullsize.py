@@ -22,8 +22,10 @@ def _rows(M, n, seed):
 def _run(name, inp):
     d = dev_inputs(inp)
     if inp["kind"] == "generic":
-        return ge.gemm_epilogue(d["A"], d["B"], bias=d.get("bias"), C=d.get("C"), R=d.get("R"),
-                                alpha=inp["alpha"], beta=inp["beta"], act=inp["act"])
+        packed = name.endswith("+prepacked")  # decode weights in the prepacked layout, as in the benchmark
+        return ge.gemm_epilogue(d["A"], ge.b_prepack(d["B"]) if packed else d["B"], bias=d.get("bias"),
+                                C=d.get("C"), R=d.get("R"), alpha=inp["alpha"], beta=inp["beta"], act=inp["act"],
+                                prepacked=packed)
     if inp["kind"] == "swiglu":
         return ge.swiglu(d["X"], d["Wg"], d["Wu"])
     Wq = torch.from_numpy(inp["Wq"]).to(DEV)
@@ -36,10 +38,11 @@ def _run(name, inp):
 
 
 @pytest.mark.parametrize("name,nrows", [("tiny_fp32", 64), ("square_bf16", 24), ("swiglu_8b", 8),
-                                        ("skinny_decode", 16), ("w4a16_m16", 16), ("w4a16_m512", 24),
+                                        ("skinny_decode", 16), ("skinny_decode+prepacked", 16),
+                                        ("w4a16_m16", 16), ("w4a16_m512", 24),
                                         ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16)])
 def test_full_size_sampled_rows(name, nrows):
-    w = workloads.WORKLOADS[name]
+    w = workloads.WORKLOADS[name.split("+")[0]]
     inp = workloads.make_inputs(w)
     out = to_host(_run(name, inp))
     rows = _rows(w.M, nrows, seed=w.wid)
