@@ -280,3 +280,61 @@ def reference(inputs: dict, rows=None) -> np.ndarray:
                        zero_point=inputs["zero_point"], alpha=inputs["alpha"], beta=inputs["beta"],
                        C=sel("C"), bias=inputs.get("bias"), act=inputs["act"], R=sel("R"))
     raise ValueError(kind)
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding at operand load ("Fusion Thinking", Pattern 4)
+# --------------------------------------------------------------------------
+
+def _bf16_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _f32_to_bf16_rne(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even (finite values)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def rope(X, cos, sin, pos0: int = 0, interleaved: bool = False) -> np.ndarray:
+    """Rotary position embedding of the rows of X (bf16 bits, [..., S, D]; row s sits at position
+    pos0 + s), the rope(q, cos, sin) step of page "Fusion Thinking", Pattern 4.
+
+    cos, sin: float32 [P, D/2], row p holding cos(p theta_i), sin(p theta_i).  Pair i of a row is
+    (i, i + D/2) (rotate-half, the Llama layout) or (2i, 2i + 1) (``interleaved``), rotated by the
+    angle of its position:  x'_a = x_a cos - x_b sin,  x'_b = x_a sin + x_b cos.  Each product and
+    each sum is rounded to float32 (the precision the rotated operand is formed in), and the result
+    is stored as bf16 (RNE), as the unfused chain writes q' and k' before the product.
+    Returns bf16 bit patterns of X's shape."""
+    x = _bf16_to_f32(X)
+    S, D = x.shape[-2], x.shape[-1]
+    if D % 2:
+        raise ValueError("D must be even")
+    c = np.asarray(cos, dtype=np.float32)[pos0:pos0 + S]
+    s = np.asarray(sin, dtype=np.float32)[pos0:pos0 + S]
+    if c.shape != (S, D // 2) or s.shape != (S, D // 2):
+        raise ValueError("cos / sin tables do not cover the positions")
+    if interleaved:
+        a, b = x[..., 0::2], x[..., 1::2]
+    else:
+        a, b = x[..., :D // 2], x[..., D // 2:]
+    ya = np.subtract(np.multiply(a, c, dtype=np.float32), np.multiply(b, s, dtype=np.float32), dtype=np.float32)
+    yb = np.add(np.multiply(a, s, dtype=np.float32), np.multiply(b, c, dtype=np.float32), dtype=np.float32)
+    y = np.empty_like(x)
+    if interleaved:
+        y[..., 0::2], y[..., 1::2] = ya, yb
+    else:
+        y[..., :D // 2], y[..., D // 2:] = ya, yb
+    return _f32_to_bf16_rne(y)
+
+
+def rope_qk(Q, K, cos, sin, *, q_pos0: int = 0, k_pos0: int = 0, alpha: float = 1.0,
+            interleaved: bool = False, rotate: bool = True) -> np.ndarray:
+    """Scores S[b] = alpha * rope(Q[b]) @ rope(K[b])^T in fp64, as separate passes: the two
+    rotations, the product (fp64, index order), the scale.  Q [B, Sq, D], K [B, Sk, D] bf16 bits.
+    ``rotate=False`` gives the plain product of Q and K."""
+    Q = _as(Q, "bf16")
+    K = _as(K, "bf16")
+    q = rope(Q, cos, sin, q_pos0, interleaved) if rotate else Q
+    k = rope(K, cos, sin, k_pos0, interleaved) if rotate else K
+    return np.stack([epilogue(gemm(q[b], k[b], "bf16", "bf16", "NK"), alpha=alpha) for b in range(Q.shape[0])])

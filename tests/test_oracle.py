@@ -372,3 +372,85 @@ def test_w8_gemm_matches_numpy_on_independently_decoded_weights(fmt, zp):
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
     # and the dequant itself is exact
     assert np.array_equal(oracle.w8_dequant(Wq, s, fmt, group=group, zero_point=zp, s_dtype="f64"), W)
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding (page "Fusion Thinking", Pattern 4)
+# --------------------------------------------------------------------------
+
+def _b(x):
+    return workloads.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _f(bits):
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("interleaved,expect", [(False, [-3, -4, 1, 2]), (True, [-2, 1, -4, 3])])
+def test_rope_quarter_turn_hand_values(interleaved, expect):
+    # D = 4, angle pi/2 for both pairs (cos 0, sin 1): each pair (a, b) becomes (-b, a).
+    # rotate-half pairs (0, 2), (1, 3); interleaved pairs (0, 1), (2, 3)
+    cos, sin = np.zeros((1, 2), np.float32), np.ones((1, 2), np.float32)
+    got = _f(oracle.rope(_b([[1, 2, 3, 4]]), cos, sin, interleaved=interleaved))
+    assert got.tolist() == [expect]
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rope_with_zero_angles_is_the_identity(interleaved):
+    X = workloads.normal((3, 5, 64), 1.0, "bf16", wid=91, tid=0)
+    cos, sin = workloads.rope_tables(5, 64, 1.0e30)  # every angle rounds to 0 beyond i = 0
+    cos[:], sin[:] = 1.0, 0.0
+    assert np.array_equal(oracle.rope(X, cos, sin, interleaved=interleaved), X)
+
+
+def test_rope_is_multiplication_by_a_unit_complex_number():
+    # independent definition: (x_a + i x_b) * exp(i p theta_k), in complex128, against the oracle's
+    # fp32 evaluation stored as bf16 (within bf16 rounding of each component)
+    D, S, pos0 = 64, 9, 5
+    X = workloads.normal((S, D), 1.0, "bf16", wid=92, tid=0)
+    cos, sin = workloads.rope_tables(pos0 + S, D, 10000.0)
+    x = _f(X)
+    z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * (cos[pos0:].astype(np.float64) + 1j * sin[pos0:].astype(np.float64))
+    want = np.concatenate([z.real, z.imag], axis=1)
+    got = _f(oracle.rope(X, cos, sin, pos0))
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
+    # a rotation keeps each pair's length
+    n0 = x[:, :D // 2] ** 2 + x[:, D // 2:] ** 2
+    n1 = got[:, :D // 2] ** 2 + got[:, D // 2:] ** 2
+    assert np.allclose(n1, n0, rtol=2.0 ** -6, atol=1e-6)
+
+
+def test_rope_interleaved_is_rotate_half_with_columns_permuted():
+    D = 128
+    X = workloads.normal((2, 7, D), 1.0, "bf16", wid=93, tid=0)
+    cos, sin = workloads.rope_tables(10, D, 500000.0)
+    perm = np.empty(D, np.int64)
+    perm[0::2], perm[1::2] = np.arange(D // 2), np.arange(D // 2) + D // 2  # column 2i <- i, 2i+1 <- i + D/2
+    a = oracle.rope(np.ascontiguousarray(X[..., perm]), cos, sin, 3, interleaved=True)
+    b = oracle.rope(X, cos, sin, 3)[..., perm]
+    assert np.array_equal(a, b)
+
+
+def test_rope_scores_depend_only_on_the_relative_position():
+    # <rope(q, p + t), rope(k, p' + t)> = <rope(q, p), rope(k, p')> for exact rotations; here
+    # within the bf16 rounding of the rotated operands
+    w = workloads.ROPE_WORKLOADS["rope_qk_prefill"].with_shape(heads=2, Sq=16, Sk=24, D=64)
+    inp = workloads.make_rope_inputs(w)
+    cos, sin = workloads.rope_tables(200, 64, 10000.0)
+    s0 = oracle.rope_qk(inp["Q"], inp["K"], cos, sin, q_pos0=3, k_pos0=0, alpha=inp["alpha"])
+    s1 = oracle.rope_qk(inp["Q"], inp["K"], cos, sin, q_pos0=3 + 150, k_pos0=150, alpha=inp["alpha"])
+    assert np.max(np.abs(s1 - s0) / (1 + np.abs(s0))) < 2e-2
+    # and do change when only one side moves
+    s2 = oracle.rope_qk(inp["Q"], inp["K"], cos, sin, q_pos0=3 + 150, k_pos0=0, alpha=inp["alpha"])
+    assert np.max(np.abs(s2 - s0)) > 0.5
+
+
+def test_rope_qk_product_pass_matches_numpy():
+    w = workloads.ROPE_WORKLOADS["rope_qk_prefill"].with_shape(heads=3, Sq=20, Sk=33, D=128)
+    inp = workloads.make_rope_inputs(w)
+    S = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], alpha=0.5)
+    q = _f(oracle.rope(inp["Q"], inp["cos"], inp["sin"]))
+    k = _f(oracle.rope(inp["K"], inp["cos"], inp["sin"]))
+    assert np.allclose(S, 0.5 * np.einsum("bmd,bnd->bmn", q, k), rtol=1e-12, atol=1e-12)
+    plain = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], rotate=False)
+    assert np.allclose(plain, np.einsum("bmd,bnd->bmn", _f(inp["Q"]), _f(inp["K"])), rtol=1e-12, atol=1e-12)

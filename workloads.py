@@ -208,3 +208,48 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     else:
         raise ValueError(w.kind)
     return out
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding at operand load: scores S = alpha * rope(Q) rope(K)^T per head
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class RopeWorkload:
+    name: str
+    wid: int
+    heads: int
+    Sq: int
+    Sk: int
+    D: int
+    q_pos0: int = 0
+    k_pos0: int = 0
+    base: float = 500000.0   # Llama-3's rotary base
+    interleaved: bool = False
+    out: str = "f32"          # score storage type
+
+    def with_shape(self, **kw) -> "RopeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+ROPE_WORKLOADS = {
+    # prefill of one layer's attention scores, 32 heads of 128, 1024 queries x 1024 keys
+    "rope_qk_prefill": RopeWorkload("rope_qk_prefill", 8, 32, 1024, 1024, 128),
+}
+
+
+def rope_tables(P: int, D: int, base: float):
+    """cos, sin as float32 [P, D/2]: angle p * base^(-2i/D) for position p and pair i, computed in
+    float64 and rounded once (the tables are inputs of the rotation, as in rope(q, cos, sin))."""
+    i = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(P, dtype=np.float64)[:, None] * (base ** (-2.0 * i / D))[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_rope_inputs(w: RopeWorkload, seed: int = 0) -> dict:
+    """Q [heads, Sq, D], K [heads, Sk, D] ~N(0,1) as bf16 bits; the tables cover every position."""
+    Q = normal((w.heads, w.Sq, w.D), 1.0, "bf16", wid=w.wid, tid=0, seed=seed)
+    K = normal((w.heads, w.Sk, w.D), 1.0, "bf16", wid=w.wid, tid=1, seed=seed)
+    cos, sin = rope_tables(max(w.q_pos0 + w.Sq, w.k_pos0 + w.Sk), w.D, w.base)
+    return dict(Q=Q, K=K, cos=cos, sin=sin, q_pos0=w.q_pos0, k_pos0=w.k_pos0, interleaved=w.interleaved,
+                alpha=float(1.0 / np.sqrt(w.D)), out=w.out)
