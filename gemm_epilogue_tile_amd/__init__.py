@@ -18,7 +18,7 @@ __all__ = [
     "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
-    "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS",
+    "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTS = [
     "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_plan_scratch_bytes", "gemm_epi_run",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
     "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack", "gemm_b_prepack",
-    "ge_add_rmsnorm_run",
+    "ge_add_rmsnorm_run", "ge_rope_qk_run", "ge_rope_run",
     "ge_status_string", "ge_last_error", "ge_version",
 ]
 
@@ -109,6 +109,10 @@ def lib():
             L.gemm_b_prepack.restype = I
             L.ge_add_rmsnorm_run.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
             L.ge_add_rmsnorm_run.restype = I
+            L.ge_rope_qk_run.argtypes = [I, I, I, I, P, P, P, P, I, I, I, I, ctypes.c_float, I, P, P]
+            L.ge_rope_qk_run.restype = I
+            L.ge_rope_run.argtypes = [I, I, I, P, P, P, I, I, I, P, P]
+            L.ge_rope_run.restype = I
             L.ge_status_string.argtypes = [I]
             L.ge_status_string.restype = ctypes.c_char_p
             L.ge_last_error.argtypes = []
@@ -481,4 +485,30 @@ def b_prepack(B, *, out=None, stream=None):
     out = out if out is not None else torch.empty((K, N), dtype=torch.bfloat16, device=B.device)
     p = plan(KIND_GENERIC, 1, N, K, a_type=BF16, b_type=BF16, d_type=BF16, ldb=_ld(B))
     _check(lib().gemm_b_prepack(p.handle, _ptr(B), _ptr(out), _stream(stream)), "gemm_b_prepack")
+    return out
+
+
+def rope_qk(Q, K, cos=None, sin=None, *, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False, out=None,
+            out_dtype=None, stream=None):
+    """S[b] = alpha * rope(Q[b]) @ rope(K[b])^T with the rotation applied at tile load (one kernel).
+
+    Q [B, Sq, D], K [B, Sk, D] bf16; cos, sin float32 [P, D/2] (None: no rotation)."""
+    torch = _torch()
+    B, Sq, D = Q.shape
+    Sk = K.shape[1]
+    out = out if out is not None else torch.empty((B, Sq, Sk), dtype=out_dtype or torch.float32, device=Q.device)
+    n_pos = cos.shape[0] if cos is not None else 0
+    _check(lib().ge_rope_qk_run(B, Sq, Sk, D, _ptr(Q), _ptr(K), _ptr(cos), _ptr(sin), n_pos, q_pos0, k_pos0,
+                                1 if interleaved else 0, float(alpha), _dtype_code(out), _ptr(out), _stream(stream)),
+           "ge_rope_qk_run")
+    return out
+
+
+def rope(X, cos, sin, *, pos0=0, interleaved=False, out=None, stream=None):
+    """The rotation alone: rope(X) for X [B, S, D] bf16, row s at position pos0 + s."""
+    torch = _torch()
+    B, S, D = X.shape
+    out = out if out is not None else torch.empty_like(X)
+    _check(lib().ge_rope_run(B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, 1 if interleaved else 0,
+                             _ptr(out), _stream(stream)), "ge_rope_run")
     return out

@@ -673,6 +673,73 @@ ge_status gemm_b_prepack(const ge_plan *pl, const void *B, void *Bp, void *strea
                       "gemm_b_prepack");
 }
 
+namespace {
+ge_status rope_common(int32_t batch, int32_t D, const float *cosT, const float *sinT, int32_t n_pos) {
+    if (batch <= 0 || batch > 65535) return fail(GE_ERR_INVALID_ARG, "batch must be in [1, 65535]");
+    if (D != 64 && D != 128) return fail(GE_ERR_UNSUPPORTED, "head dimension %d not in {64, 128}", D);
+    if (!cosT || !sinT) return fail(GE_ERR_INVALID_ARG, "cos or sin is NULL");
+    if (((uintptr_t)cosT & 15) || ((uintptr_t)sinT & 15)) return fail(GE_ERR_ALIGN, "cos and sin must be 16-byte aligned");
+    if (n_pos <= 0) return fail(GE_ERR_INVALID_ARG, "n_pos must be positive");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        return fail(GE_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    return GE_OK;
+}
+}  // namespace
+
+ge_status ge_rope_qk_run(int32_t batch, int32_t Sq, int32_t Sk, int32_t D, const void *Q, const void *K,
+                         const float *cos_t, const float *sin_t, int32_t n_pos, int32_t q_pos0, int32_t k_pos0,
+                         int32_t interleaved, float alpha, int32_t s_type, void *S, void *stream) {
+    if (Sq <= 0 || Sk <= 0) return fail(GE_ERR_INVALID_ARG, "Sq and Sk must be positive");
+    if (!Q || !K || !S) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    if (s_type != GE_F32 && s_type != GE_BF16) return fail(GE_ERR_INVALID_ARG, "s_type must be F32 or BF16");
+    if (((uintptr_t)Q & 15) || ((uintptr_t)K & 15)) return fail(GE_ERR_ALIGN, "Q and K must be 16-byte aligned");
+    const bool rot = cos_t || sin_t;
+    ge_status st;
+    if (rot) {
+        if ((st = rope_common(batch, D, cos_t, sin_t, n_pos))) return st;
+        if (q_pos0 < 0 || k_pos0 < 0 || (int64_t)q_pos0 + Sq > n_pos || (int64_t)k_pos0 + Sk > n_pos)
+            return fail(GE_ERR_INVALID_ARG, "positions outside the cos / sin tables");
+    } else {
+        if (batch <= 0 || batch > 65535) return fail(GE_ERR_INVALID_ARG, "batch must be in [1, 65535]");
+        if (D != 64 && D != 128) return fail(GE_ERR_UNSUPPORTED, "head dimension %d not in {64, 128}", D);
+    }
+    const size_t nq = (size_t)batch * Sq * D * 2, nk = (size_t)batch * Sk * D * 2;
+    const size_t ns = (size_t)batch * Sq * Sk * (s_type == GE_F32 ? 4 : 2);
+    if (overlaps(S, ns, Q, nq) || overlaps(S, ns, K, nk)) return fail(GE_ERR_INVALID_ARG, "S overlaps Q or K");
+    RopeArgs a{};
+    a.batch = batch;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.D = D;
+    a.q_pos0 = q_pos0;
+    a.k_pos0 = k_pos0;
+    a.Q = (const uint16_t *)Q;
+    a.K = (const uint16_t *)K;
+    a.cos = rot ? cos_t : nullptr;
+    a.sin = rot ? sin_t : nullptr;
+    a.alpha = alpha;
+    a.S = S;
+    return hip_status(launch_rope_qk(a, interleaved != 0, s_type == GE_F32, (hipStream_t)stream), "ge_rope_qk_run");
+}
+
+ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const float *cos_t, const float *sin_t,
+                      int32_t n_pos, int32_t pos0, int32_t interleaved, void *Y, void *stream) {
+    if (S <= 0) return fail(GE_ERR_INVALID_ARG, "S must be positive");
+    if (!X || !Y) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    if (((uintptr_t)X & 15) || ((uintptr_t)Y & 15)) return fail(GE_ERR_ALIGN, "X and Y must be 16-byte aligned");
+    ge_status st;
+    if ((st = rope_common(batch, D, cos_t, sin_t, n_pos))) return st;
+    if (pos0 < 0 || (int64_t)pos0 + S > n_pos) return fail(GE_ERR_INVALID_ARG, "positions outside the cos / sin tables");
+    const size_t nb = (size_t)batch * S * D * 2;
+    if (overlaps(X, nb, Y, nb)) return fail(GE_ERR_INVALID_ARG, "Y overlaps X");
+    return hip_status(launch_rope(batch, S, D, (const uint16_t *)X, cos_t, sin_t, pos0, interleaved != 0,
+                                  (uint16_t *)Y, (hipStream_t)stream),
+                      "ge_rope_run");
+}
+
 ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,
                              void *resid, void *out, void *stream) {
     if (M <= 0 || N <= 0) return fail(GE_ERR_INVALID_ARG, "M and N must be positive");

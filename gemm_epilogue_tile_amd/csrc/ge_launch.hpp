@@ -60,6 +60,20 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 // One-time conversion of raw [K, N] bf16 weights to the prepacked decode layout.
 hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s);
 
+// Rotary position embedding at Q / K tile load, with the scores product as the consumer.
+struct RopeArgs {
+    int32_t batch, Sq, Sk, D;
+    int32_t q_pos0, k_pos0;
+    const uint16_t *Q, *K;      // [batch][Sq][D], [batch][Sk][D] bf16
+    const float *cos, *sin;     // [positions][D / 2]; NULL: no rotation
+    float alpha;
+    void *S;                    // [batch][Sq][Sk], fp32 or bf16
+};
+hipError_t launch_rope_qk(const RopeArgs &a, bool interleaved, bool f32out, hipStream_t s);
+// The rotation alone (the unfused chain's first step): X [batch * S][D] -> Y.
+hipError_t launch_rope(int32_t batch, int32_t S, int32_t D, const uint16_t *X, const float *cosT, const float *sinT,
+                       int32_t pos0, bool interleaved, uint16_t *Y, hipStream_t s);
+
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);

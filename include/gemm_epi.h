@@ -236,6 +236,40 @@ GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t
 GE_API ge_status gemm_b_prepack(const ge_plan *plan, const void *B, void *Bp, void *stream);
 
 /*
+ * Rotary position embedding applied as the Q and K tiles are loaded, with the
+ * attention scores product as the consumer (page "Fusion Thinking", Pattern
+ * 4: RoPE computed at Q-tile and K-tile load time instead of by two kernels
+ * that write q' and k' back to memory):
+ *   S[b, m, n] = alpha * sum_d rope(Q[b, m, :], q_pos0 + m)[d] * rope(K[b, n, :], k_pos0 + n)[d]
+ * Q [batch, Sq, D] and K [batch, Sk, D] bf16, dense, 16-byte aligned; cos and
+ * sin fp32 [n_pos, D/2] (row p: cos(p theta_i), sin(p theta_i)), 16-byte
+ * aligned, covering every position used; S [batch, Sq, Sk] of s_type (GE_F32
+ * or GE_BF16), dense, not overlapping Q or K.  Pair i of a row is (i, i + D/2)
+ * (rotate-half, the Llama layout), or (2i, 2i + 1) when interleaved != 0:
+ * x'_a = x_a cos - x_b sin, x'_b = x_a sin + x_b cos, each product and sum
+ * rounded to fp32 and x' rounded to bf16 (RNE), the values the unfused chain
+ * stores; the product is bf16 x bf16 with fp32 accumulation, alpha applied in
+ * fp32, one rounding to s_type.  cos == sin == NULL: no rotation (the plain
+ * product, the unfused chain's last step).  D in {64, 128}, batch <= 65535.
+ * Errors: INVALID_ARG (sizes, NULLs, positions outside the tables, overlap),
+ * UNSUPPORTED (D), ALIGN, NO_DEVICE, HIP.  Asynchronous on the stream.
+ */
+GE_API ge_status ge_rope_qk_run(int32_t batch, int32_t Sq, int32_t Sk, int32_t D, const void *Q, const void *K,
+                                const float *cos_t, const float *sin_t, int32_t n_pos, int32_t q_pos0,
+                                int32_t k_pos0, int32_t interleaved, float alpha, int32_t s_type, void *S,
+                                void *stream);
+
+/*
+ * The rotation alone (the unfused chain's first kernels, rope(q, cos, sin) of
+ * the same page): Y = rope(X) for X, Y [batch, S, D] bf16, row s of each batch
+ * at position pos0 + s, with the pairing and rounding of ge_rope_qk_run.  X
+ * and Y 16-byte aligned, not overlapping; cos, sin as above (required).
+ */
+GE_API ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const float *cos_t,
+                             const float *sin_t, int32_t n_pos, int32_t pos0, int32_t interleaved, void *Y,
+                             void *stream);
+
+/*
  * Deliberately unfused chains, for measurement only: the plain GEMM writes
  * its fp32-accumulated result to the workspace in the output type (bf16 or
  * fp32), then one elementwise kernel per epilogue step reads and writes

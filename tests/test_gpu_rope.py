@@ -1,0 +1,110 @@
+"""GPU parity of rotary position embedding at operand load (page "Fusion
+Thinking", Pattern 4): the standalone rotation bit-exact against the oracle,
+the fused scores kernel against the oracle on ragged shapes, both pairings,
+both output types and shifted positions, fused == unfused chain bitwise, and
+the requests the entry points must refuse."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_epilogue_tile_amd as ge
+import oracle
+import workloads
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RW = workloads.ROPE_WORKLOADS["rope_qk_prefill"]
+
+
+def _dev(inp):
+    return (to_dev(inp["Q"]), to_dev(inp["K"]), torch.from_numpy(inp["cos"]).to(DEV),
+            torch.from_numpy(inp["sin"]).to(DEV))
+
+
+def _bits(t):
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rotation_alone_is_bit_exact(D, interleaved):
+    w = RW.with_shape(heads=3, Sq=77, Sk=77, D=D, interleaved=interleaved)
+    inp = workloads.make_rope_inputs(w, seed=D)
+    Q, _, c, s = _dev(inp)
+    cos, sin = workloads.rope_tables(200, D, 500000.0)
+    got = _bits(ge.rope(Q, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), pos0=41,
+                        interleaved=interleaved))
+    assert np.array_equal(got, oracle.rope(inp["Q"], cos, sin, 41, interleaved))
+
+
+@pytest.mark.parametrize("H,Sq,Sk,D", [(1, 1, 1, 64), (2, 128, 128, 128), (3, 77, 200, 128), (2, 300, 131, 64),
+                                       (4, 1, 517, 128)])
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_fused_scores_match_the_oracle(H, Sq, Sk, D, interleaved):
+    w = RW.with_shape(heads=H, Sq=Sq, Sk=Sk, D=D, interleaved=interleaved, k_pos0=5, q_pos0=5 + Sk - Sq if Sk >= Sq else 5)
+    inp = workloads.make_rope_inputs(w, seed=H + Sq + Sk)
+    Q, K, c, s = _dev(inp)
+    out = ge.rope_qk(Q, K, c, s, q_pos0=w.q_pos0, k_pos0=w.k_pos0, alpha=inp["alpha"], interleaved=interleaved)
+    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], q_pos0=w.q_pos0, k_pos0=w.k_pos0,
+                         alpha=inp["alpha"], interleaved=interleaved)
+    assert_close(out, ref, TOL_F32, f"rope_qk {H}x{Sq}x{Sk}x{D} inter={interleaved}")
+
+
+def test_fused_scores_bf16_output():
+    w = RW.with_shape(heads=2, Sq=200, Sk=264, D=128)
+    inp = workloads.make_rope_inputs(w, seed=3)
+    Q, K, c, s = _dev(inp)
+    out = ge.rope_qk(Q, K, c, s, alpha=inp["alpha"], out_dtype=torch.bfloat16)
+    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], alpha=inp["alpha"])
+    assert_close(out, ref, TOL_BF16, "rope_qk bf16 out")
+
+
+def test_plain_product_without_tables():
+    w = RW.with_shape(heads=2, Sq=130, Sk=70, D=64)
+    inp = workloads.make_rope_inputs(w, seed=4)
+    Q, K, _, _ = _dev(inp)
+    out = ge.rope_qk(Q, K, alpha=0.25)
+    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], alpha=0.25, rotate=False)
+    assert_close(out, ref, TOL_F32, "plain product")
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_fused_equals_the_unfused_chain_bitwise(interleaved):
+    # rope(Q) and rope(K) written to memory, then the plain product: the same bf16 operands reach
+    # the same product code, so the scores agree bit for bit
+    w = RW.with_shape(heads=4, Sq=256, Sk=384, D=128, interleaved=interleaved, q_pos0=128)
+    inp = workloads.make_rope_inputs(w, seed=9)
+    Q, K, c, s = _dev(inp)
+    fused = ge.rope_qk(Q, K, c, s, q_pos0=128, alpha=inp["alpha"], interleaved=interleaved)
+    q2 = ge.rope(Q, c, s, pos0=128, interleaved=interleaved)
+    k2 = ge.rope(K, c, s, pos0=0, interleaved=interleaved)
+    unfused = ge.rope_qk(q2, k2, alpha=inp["alpha"])
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int32), unfused.view(torch.int32))
+
+
+def test_full_size_prefill_sampled_heads():
+    w = RW
+    inp = workloads.make_rope_inputs(w)
+    Q, K, c, s = _dev(inp)
+    out = ge.rope_qk(Q, K, c, s, alpha=inp["alpha"]).cpu().numpy().astype(np.float64)
+    heads = [0, 17, w.heads - 1]
+    ref = oracle.rope_qk(inp["Q"][heads], inp["K"][heads], inp["cos"], inp["sin"], alpha=inp["alpha"])
+    assert_close(out[heads], ref, TOL_F32, "rope_qk full size")
+    assert np.all(np.isfinite(out))
+
+
+def test_refusals():
+    Q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    cos = torch.zeros((8, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.rope_qk(Q, Q, cos, cos, q_pos0=1)  # position 8 is past the tables
+    assert e.value.status == ge.ERR_INVALID_ARG
+    Q96 = torch.zeros((1, 8, 96), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.rope_qk(Q96, Q96)
+    assert e.value.status == ge.ERR_UNSUPPORTED
+    with pytest.raises(ge.GemmEpiError):
+        ge.rope(Q, cos, cos, out=Q)  # Y overlaps X
