@@ -242,6 +242,42 @@ def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
             "hbm_frac": round(byts / (kern * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
+def measure_rope_qk(steps, warmup):
+    """Scores of one layer's attention prefill with the rotary embedding applied at Q / K tile load
+    (one kernel), against the unfused chain: rope(Q) and rope(K) written to memory, then the plain
+    product.  The fp32 scores dominate the bytes; two output buffers defeat the Infinity Cache."""
+    import numpy as np
+    import torch
+    import gemm_epilogue_tile_amd as ge
+    import workloads
+    w = workloads.ROPE_WORKLOADS["rope_qk_prefill"]
+    inp = workloads.make_rope_inputs(w)
+    Q, K = _dev(inp["Q"]), _dev(inp["K"])
+    cos, sin = torch.from_numpy(inp["cos"]).cuda(), torch.from_numpy(inp["sin"]).cuda()
+    outs = [torch.empty((w.heads, w.Sq, w.Sk), dtype=torch.float32, device="cuda") for _ in range(2)]
+    q2, k2 = torch.empty_like(Q), torch.empty_like(K)
+    kw = dict(alpha=inp["alpha"], q_pos0=w.q_pos0, k_pos0=w.k_pos0)
+    fused = [ge.prepare_rope_qk(Q, K, cos, sin, out=o, **kw) for o in outs]
+    rq = ge.prepare_rope(Q, cos, sin, out=q2, pos0=w.q_pos0)
+    rk = ge.prepare_rope(K, cos, sin, out=k2, pos0=w.k_pos0)
+    prods = [ge.prepare_rope_qk(q2, k2, out=o, alpha=inp["alpha"]) for o in outs]
+    unfused = [(lambda p=p: (rq(), rk(), p())) for p in prods]
+    fused_ms = time_launches(fused, steps, warmup) / steps
+    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
+    qk = Q.numel() * 2 + K.numel() * 2
+    tables = cos.numel() * 4 * 2
+    s_bytes = outs[0].numel() * 4
+    byts = qk + tables + s_bytes
+    flops = 2.0 * w.heads * w.Sq * w.Sk * w.D
+    return {"kernel": "rope_qk_128x128", "heads": w.heads, "Sq": w.Sq, "Sk": w.Sk, "D": w.D, "bound": "hbm",
+            "flops": flops, "bytes": byts, "rotations": 2, "kernel_ms_avg": round(fused_ms, 4),
+            "unfused_ms": round(unfused_ms, 4), "unfused_bytes": byts + 2 * qk + tables,
+            "speedup_vs_unfused": round(unfused_ms / fused_ms, 4),
+            "gbps": round(byts / (fused_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (fused_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "tflops": round(flops / (fused_ms * 1e-3) / 1e12, 2)}
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -393,6 +429,9 @@ def main():
         line["workloads"] = others
         # a measured step beyond the fused GEMM: residual add + RMSNorm, fused in one kernel
         nxt = {"add_rmsnorm_2048x4096": measure_add_rmsnorm(max(a.steps // 2, 10), max(a.warmup // 2, 3))}
+        # rotary embedding applied at Q / K tile load, the attention scores product as its consumer
+        nxt["rope_qk_prefill"] = measure_rope_qk(max(a.steps // 2, 10), max(a.warmup // 2, 3))
+        torch.cuda.empty_cache()
         # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
         for name in ["w8a16_u8_m16", "w8a16_fp8_m16"]:
             r = measure(name, max(a.steps // 2, 10), max(a.warmup // 2, 3))

@@ -18,7 +18,8 @@ __all__ = [
     "GemmEpiError", "Desc", "Plan", "lib", "lib_path", "plan", "gemm_epilogue", "swiglu", "w4_gemm",
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
-    "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope",
+    "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope", "prepare_rope_qk",
+    "prepare_rope",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -512,3 +513,20 @@ def rope(X, cos, sin, *, pos0=0, interleaved=False, out=None, stream=None):
     _check(lib().ge_rope_run(B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, 1 if interleaved else 0,
                              _ptr(out), _stream(stream)), "ge_rope_run")
     return out
+
+
+def prepare_rope_qk(Q, K, cos=None, sin=None, *, out, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False,
+                    stream=None) -> Prepared:
+    """``rope_qk`` bound to fixed tensors and stream (for timing loops and graph capture)."""
+    B, Sq, D = Q.shape
+    args = (B, Sq, K.shape[1], D, _ptr(Q), _ptr(K), _ptr(cos), _ptr(sin), cos.shape[0] if cos is not None else 0,
+            q_pos0, k_pos0, 1 if interleaved else 0, float(alpha), _dtype_code(out), _ptr(out), _stream(stream))
+    return Prepared(lib().ge_rope_qk_run, "ge_rope_qk_run", None, [Q, K, cos, sin, out], args)
+
+
+def prepare_rope(X, cos, sin, *, out, pos0=0, interleaved=False, stream=None) -> Prepared:
+    """``rope`` bound to fixed tensors and stream."""
+    B, S, D = X.shape
+    args = (B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, 1 if interleaved else 0, _ptr(out),
+            _stream(stream))
+    return Prepared(lib().ge_rope_run, "ge_rope_run", None, [X, cos, sin, out], args)
