@@ -4,8 +4,8 @@
 // Q-tile and K-tile load time instead of by two kernels that write q' and k'
 // back to memory just before the product reads them).
 //
-// One 256-thread workgroup per (head, 128-query tile, 128-key tile):
-//   1. both tiles are read from memory in 16-byte chunks, rotated in fp32
+// One 256-thread workgroup per (head, 128-query tile), walking the key tiles:
+//   1. the tiles are read from memory in 16-byte chunks, rotated in fp32
 //      (each product and each sum rounded to fp32, no contraction), rounded
 //      to bf16 (RNE) -- the values the unfused chain would have stored -- and
 //      written to LDS rows padded by 16 bytes, so that the MFMA fragment reads
@@ -14,6 +14,8 @@
 //      the head dimension, K' fragments as the first operand so that each
 //      lane holds four consecutive key columns of one query row;
 //   3. the scale alpha is applied in fp32 and S is stored once (fp32 or bf16).
+// The query tile is rotated once per workgroup; the next key tile's loads
+// are in flight while the current one is multiplied and its scores stored.
 // Pairs: (i, i + D/2) (rotate-half) or (2i, 2i + 1) (interleaved); the pair
 // rotates by the angle of the row's position p: cos and sin come from tables
 // [P][D/2], row p.
@@ -25,135 +27,184 @@ namespace {
 
 constexpr int RT = 128;  // query rows and key rows per tile
 
-// Rotate chunk c of one row.  Rotate-half: o0 = elements 8c .. 8c+7 (first half), o1 = the same
-// elements of the second half (D/2 + 8c ..), angles 8c .. 8c+7.  Interleaved: o0 = elements
-// 8c .. 8c+7, i.e. the pairs 4c .. 4c+3 with those angles (o1 unused).
+// Rotate chunk c of one row from registers.  Rotate-half: x[0] = elements 8c .. 8c+7 of the first
+// half, x[1] the same elements of the second half (D/2 + 8c ..), c4 / s4 the 8 angles 8c .. 8c+7;
+// o0, o1 the rotated chunks.  Interleaved: x[0] = elements 8c .. 8c+7, i.e. the pairs 4c .. 4c+3
+// with the 4 angles in c4[0] / s4[0]; o0 the rotated chunk.  Each product and each sum is rounded
+// to fp32 (no contraction), the result to bf16 (RNE).
 template <int D, bool INTER>
-__device__ __forceinline__ void rope_chunk(const uint16_t *xrow, const float *crow, const float *srow, int c,
-                                           u32x4 &o0, u32x4 &o1) {
+__device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const f32x4 *s4, u32x4 &o0, u32x4 &o1) {
 #pragma clang fp contract(off)
     if constexpr (INTER) {
-        const u32x4 v = *(const u32x4 *)(xrow + 8 * c);
-        const f32x4 cc = *(const f32x4 *)(crow + 4 * c), ss = *(const f32x4 *)(srow + 4 * c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float a = bf16lo(v[j]), b = bf16hi(v[j]);
-            const float ya = a * cc[j] - b * ss[j];
-            const float yb = a * ss[j] + b * cc[j];
+            const float a = bf16lo(x[0][j]), b = bf16hi(x[0][j]);
+            const float ya = a * c4[0][j] - b * s4[0][j];
+            const float yb = a * s4[0][j] + b * c4[0][j];
             o0[j] = pack_bf16x2(ya, yb);
         }
     } else {
-        const u32x4 lo = *(const u32x4 *)(xrow + 8 * c), hi = *(const u32x4 *)(xrow + D / 2 + 8 * c);
-        const f32x4 c0 = *(const f32x4 *)(crow + 8 * c), c1 = *(const f32x4 *)(crow + 8 * c + 4);
-        const f32x4 s0 = *(const f32x4 *)(srow + 8 * c), s1 = *(const f32x4 *)(srow + 8 * c + 4);
-        const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float a0 = bf16lo(lo[j]), a1 = bf16hi(lo[j]);  // first-half elements 8c + 2j, + 1
-            const float b0 = bf16lo(hi[j]), b1 = bf16hi(hi[j]);  // their partners in the second half
-            const float ya0 = a0 * cv[2 * j] - b0 * sv[2 * j];
-            const float yb0 = a0 * sv[2 * j] + b0 * cv[2 * j];
-            const float ya1 = a1 * cv[2 * j + 1] - b1 * sv[2 * j + 1];
-            const float yb1 = a1 * sv[2 * j + 1] + b1 * cv[2 * j + 1];
+            const float c0 = c4[j >> 1][(2 * j) & 3], c1 = c4[j >> 1][(2 * j + 1) & 3];
+            const float s0 = s4[j >> 1][(2 * j) & 3], s1 = s4[j >> 1][(2 * j + 1) & 3];
+            const float a0 = bf16lo(x[0][j]), a1 = bf16hi(x[0][j]);  // first-half elements 8c + 2j, + 1
+            const float b0 = bf16lo(x[1][j]), b1 = bf16hi(x[1][j]);  // their partners in the second half
+            const float ya0 = a0 * c0 - b0 * s0;
+            const float yb0 = a0 * s0 + b0 * c0;
+            const float ya1 = a1 * c1 - b1 * s1;
+            const float yb1 = a1 * s1 + b1 * c1;
             o0[j] = pack_bf16x2(ya0, ya1);
             o1[j] = pack_bf16x2(yb0, yb1);
         }
     }
 }
 
+// The same from memory: chunk c of the row at xrow with its position's table rows.
+template <int D, bool INTER>
+__device__ __forceinline__ void rope_chunk(const uint16_t *xrow, const float *crow, const float *srow, int c,
+                                           u32x4 &o0, u32x4 &o1) {
+    constexpr int NV = INTER ? 1 : 2, NT = INTER ? 1 : 2;
+    u32x4 x[NV];
+    f32x4 c4[NT], s4[NT];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[v] = *(const u32x4 *)(xrow + v * (D / 2) + 8 * c);
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        c4[q] = *(const f32x4 *)(crow + NT * 4 * c + 4 * q);
+        s4[q] = *(const f32x4 *)(srow + NT * 4 * c + 4 * q);
+    }
+    rope_regs<D, INTER>(x, c4, s4, o0, o1);
+}
+
 // chunks per row handled by one work item
 template <int D, bool INTER>
 constexpr int chunks_per_row() { return INTER ? D / 8 : D / 16; }
 
-// One 128-row tile of X (rows r0 .. r0 + 127 of a [rows][D] head, row r at position pos0 + r) into
-// LDS rows of LD elements, rotated when ROT; rows past the end are zeros.
+// One 128-row tile of X (rows r0 .. r0 + 127 of a [rows][D] head, row r at position pos0 + r): each
+// thread's chunks and their cos / sin requested into registers (rows past the end read nothing and
+// stage zeros), then rotated when ROT and written to LDS rows of D + 8 elements.
 template <int D, bool INTER, bool ROT>
-__device__ __forceinline__ void stage_tile(const uint16_t *X, int rows, int r0, int pos0, const float *cosT,
-                                           const float *sinT, uint16_t *dst) {
-    constexpr int LD = D + 8;
-    constexpr int CPR = ROT ? chunks_per_row<D, INTER>() : D / 8;
-    for (int it = threadIdx.x; it < RT * CPR; it += 256) {
-        const int r = it / CPR, c = it % CPR;
-        u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
-        const bool in = r0 + r < rows;
-        const uint16_t *xrow = X + (int64_t)(r0 + r) * D;
-        if constexpr (ROT) {
-            if (in) {
-                const int64_t p = pos0 + r0 + r;
-                rope_chunk<D, INTER>(xrow, cosT + p * (D / 2), sinT + p * (D / 2), c, o0, o1);
+struct TileRegs {
+    static constexpr int CPR = ROT ? chunks_per_row<D, INTER>() : D / 8;
+    static constexpr int ITEMS = RT * CPR / 256;               // per thread
+    static constexpr int NV = (ROT && !INTER) ? 2 : 1;         // 16-byte chunks of X per item
+    static constexpr int NT = ROT ? (INTER ? 1 : 2) : 1;       // 16-byte chunks of each table per item
+    static_assert(RT * CPR % 256 == 0, "items per thread");
+    u32x4 x[ITEMS][NV];
+    f32x4 c[ITEMS][NT], s[ITEMS][NT];
+
+    __device__ __forceinline__ void load(const uint16_t *X, int rows, int r0, int pos0, const float *cosT,
+                                         const float *sinT) {
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            const int it = threadIdx.x + 256 * u, r = it / CPR, ch = it % CPR;
+            const bool in = r0 + r < rows;
+            const uint16_t *xrow = X + (int64_t)(in ? r0 + r : 0) * D;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                x[u][v] = in ? *(const u32x4 *)(xrow + v * (D / 2) + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (ROT) {
+                const int64_t p = in ? pos0 + r0 + r : 0;
+#pragma unroll
+                for (int q = 0; q < NT; ++q) {
+                    c[u][q] = *(const f32x4 *)(cosT + p * (D / 2) + NT * 4 * ch + 4 * q);
+                    s[u][q] = *(const f32x4 *)(sinT + p * (D / 2) + NT * 4 * ch + 4 * q);
+                }
             }
-            if constexpr (INTER) {
-                *(u32x4 *)(dst + r * LD + 8 * c) = o0;
-            } else {
-                *(u32x4 *)(dst + r * LD + 8 * c) = o0;
-                *(u32x4 *)(dst + r * LD + D / 2 + 8 * c) = o1;
-            }
-        } else {
-            if (in) o0 = *(const u32x4 *)(xrow + 8 * c);
-            *(u32x4 *)(dst + r * LD + 8 * c) = o0;
         }
     }
-}
 
+    __device__ __forceinline__ void store(uint16_t *dst) const {
+        constexpr int LD = D + 8;
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            const int it = threadIdx.x + 256 * u, r = it / CPR, ch = it % CPR;
+            if constexpr (!ROT) {
+                *(u32x4 *)(dst + r * LD + 8 * ch) = x[u][0];
+            } else {
+                u32x4 o0, o1;
+                rope_regs<D, INTER>(x[u], c[u], s[u], o0, o1);
+                *(u32x4 *)(dst + r * LD + 8 * ch) = o0;
+                if constexpr (!INTER) *(u32x4 *)(dst + r * LD + D / 2 + 8 * ch) = o1;
+            }
+        }
+    }
+};
+
+// One workgroup per (head, 128-query tile): the query tile is rotated once into LDS; the key tiles
+// follow one another through two LDS buffers, the next one's chunks and tables requested into
+// registers before the current one is multiplied and its scores stored.
 template <int D, bool INTER, bool ROT, bool F32OUT>
 __global__ __launch_bounds__(256) void rope_qk_kernel(RopeArgs a) {
     constexpr int LD = D + 8;
     extern __shared__ __attribute__((aligned(16))) uint16_t rsm[];
-    uint16_t *qs = rsm, *ks = rsm + RT * LD;
-    const int b = blockIdx.z, m0 = blockIdx.y * RT, n0 = blockIdx.x * RT;
-    stage_tile<D, INTER, ROT>(a.Q + (int64_t)b * a.Sq * D, a.Sq, m0, a.q_pos0, a.cos, a.sin, qs);
-    stage_tile<D, INTER, ROT>(a.K + (int64_t)b * a.Sk * D, a.Sk, n0, a.k_pos0, a.cos, a.sin, ks);
-    __syncthreads();
+    uint16_t *qs = rsm;
+    const int b = blockIdx.y, m0 = blockIdx.x * RT;
+    const uint16_t *Kb = a.K + (int64_t)b * a.Sk * D;
+    const int ntiles = (a.Sk + RT - 1) / RT;
+
+    TileRegs<D, INTER, ROT> t;
+    t.load(a.Q + (int64_t)b * a.Sq * D, a.Sq, m0, a.q_pos0, a.cos, a.sin);
+    t.store(qs);
+    t.load(Kb, a.Sk, 0, a.k_pos0, a.cos, a.sin);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1, fr = lane & 15, fg = lane >> 4;
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        bf16x8 qa[4], kf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qa[i] = *(const bf16x8 *)(qs + (wm * 64 + 16 * i + fr) * LD + 32 * kk + 8 * fg);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kf[j] = *(const bf16x8 *)(ks + (wn * 64 + 16 * j + fr) * LD + 32 * kk + 8 * fg);
+    const bool vec = (a.Sk & 3) == 0;
+    for (int jt = 0; jt < ntiles; ++jt) {
+        uint16_t *ks = rsm + (1 + (jt & 1)) * RT * LD;
+        const int n0 = jt * RT;
+        t.store(ks);
+        if (jt + 1 < ntiles) t.load(Kb, a.Sk, n0 + RT, a.k_pos0, a.cos, a.sin);
+        __syncthreads();  // this key tile (and, first time, the query tile) visible; buffer jt-1 done with
+
+        f32x4 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(kf[j], qa[i], acc[i][j]);
-    }
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            bf16x8 qa[4], kf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qa[i] = *(const bf16x8 *)(qs + (wm * 64 + 16 * i + fr) * LD + 32 * kk + 8 * fg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kf[j] = *(const bf16x8 *)(ks + (wn * 64 + 16 * j + fr) * LD + 32 * kk + 8 * fg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(kf[j], qa[i], acc[i][j]);
+        }
 
-    // lane holds S[m][n .. n + 3], m = m0 + 64 wm + 16 i + fr, n = n0 + 64 wn + 16 j + 4 fg
-    const bool vec = (a.Sk & 3) == 0;
+        // lane holds S[m][n .. n + 3], m = m0 + 64 wm + 16 i + fr, n = n0 + 64 wn + 16 j + 4 fg
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 64 + 16 * i + fr;
-        if (m >= a.Sq) continue;
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wm * 64 + 16 * i + fr;
+            if (m >= a.Sq) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn * 64 + 16 * j + 4 * fg;
-            if (n >= a.Sk) continue;
-            float v[4];
+            for (int j = 0; j < 4; ++j) {
+                const int n = n0 + wn * 64 + 16 * j + 4 * fg;
+                if (n >= a.Sk) continue;
+                float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = a.alpha * acc[i][j][e];
-            const int64_t off = ((int64_t)b * a.Sq + m) * a.Sk + n;
-            if (vec && n + 4 <= a.Sk) {
-                if constexpr (F32OUT)
-                    *(f32x4 *)((float *)a.S + off) = f32x4{v[0], v[1], v[2], v[3]};
-                else
-                    *(u32x2 *)((uint16_t *)a.S + off) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            } else {
+                for (int e = 0; e < 4; ++e) v[e] = a.alpha * acc[i][j][e];
+                const int64_t off = ((int64_t)b * a.Sq + m) * a.Sk + n;
+                if (vec && n + 4 <= a.Sk) {
+                    if constexpr (F32OUT)
+                        *(f32x4 *)((float *)a.S + off) = f32x4{v[0], v[1], v[2], v[3]};
+                    else
+                        *(u32x2 *)((uint16_t *)a.S + off) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < a.Sk) {
-                        if constexpr (F32OUT)
-                            ((float *)a.S)[off + e] = v[e];
-                        else
-                            ((uint16_t *)a.S)[off + e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xffffu);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < a.Sk) {
+                            if constexpr (F32OUT)
+                                ((float *)a.S)[off + e] = v[e];
+                            else
+                                ((uint16_t *)a.S)[off + e] = (uint16_t)(pack_bf16x2(v[e], 0.0f) & 0xffffu);
+                        }
+                }
             }
         }
     }
@@ -179,14 +230,14 @@ __global__ __launch_bounds__(256) void rope_kernel(int64_t rows, int32_t S, cons
 template <int D, bool INTER, bool ROT, bool F32OUT>
 hipError_t go_qk(const RopeArgs &a, hipStream_t s) {
     auto k = rope_qk_kernel<D, INTER, ROT, F32OUT>;
-    constexpr int lds = 2 * RT * (D + 8) * 2;
+    constexpr int lds = 3 * RT * (D + 8) * 2;  // the query tile and two key tiles
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const dim3 grid((a.Sk + RT - 1) / RT, (a.Sq + RT - 1) / RT, a.batch);
+    const dim3 grid((a.Sq + RT - 1) / RT, a.batch);
     hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
