@@ -175,7 +175,11 @@ def build_calls(name, w, inp):
             u = ge.prepare_swiglu(s["X"], s["Wg"], s["Wu"], out=o, unfused=True, workspace=ws)
         elif w.kind == "w8":
             kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o, fmt=w.fmt)
-            f = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], **kw)
+            if w.M <= 16 and w.N % 128 == 0 and w.K % 32 == 0:
+                # decode shape: codes converted once to the streaming kernel's layout (a load-time step)
+                f = ge.prepare_w4_gemm(s["X"], ge.w4_prepack(s["Wq"], fmt=w.fmt), s["scales"], prepacked=True, **kw)
+            else:
+                f = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], **kw)
             u = ge.prepare_w4_gemm(s["X"], s["Wq"], s["scales"], unfused=True, workspace=ws, **kw)
         else:
             kw = dict(bias=s.get("bias"), group=w.group, zero_point=w.zero_point, out=o)

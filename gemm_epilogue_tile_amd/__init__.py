@@ -380,7 +380,7 @@ def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, ac
 
     ``fmt``: "u4" (packed pairs, Wq [K, N/2]), "u8" or "fp8" (E4M3; Wq [K, N] bytes).
     ``zero_point``: default 8 (u4), 128 (u8), 0 (fp8).
-    ``prepacked``: int4 Wq came from ``w4_prepack`` (kernel-native layout, same byte count)."""
+    ``prepacked``: Wq came from ``w4_prepack`` with the same ``fmt`` (kernel-native layout, same byte count)."""
     out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
     p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
     _check(lib().gemm_w4_run(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R),
@@ -468,12 +468,20 @@ def prepare_w4_gemm(X, Wq, scales, *, out, bias=None, C=None, R=None, alpha=1.0,
     return Prepared(lib().gemm_w4_run, "gemm_w4_run", p, ts, args)
 
 
-def w4_prepack(Wq, *, lo_first=False, out=None, stream=None):
-    """Raw packed int4 weights [K, N/2] -> the fused kernels' layout (same bytes, one-time)."""
+def w4_prepack(Wq, *, lo_first=False, fmt="u4", out=None, stream=None):
+    """Raw quantised weights -> the fused decode kernels' layout (same bytes, one-time).
+
+    ``fmt`` "u4": packed int4 [K, N/2]; "u8" / "fp8": 8-bit codes [K, N] (N % 128 == 0, M <= 16 plans)."""
     torch = _torch()
-    K, N = Wq.shape[0], Wq.shape[1] * 2
-    out = out if out is not None else torch.empty(K * N // 2, dtype=torch.uint8, device=Wq.device)
-    p = plan(KIND_W4, 1, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), lo_first=lo_first)
+    if fmt == "u4":
+        K, N = Wq.shape[0], Wq.shape[1] * 2
+        out = out if out is not None else torch.empty(K * N // 2, dtype=torch.uint8, device=Wq.device)
+        p = plan(KIND_W4, 1, N, K, a_type=BF16, b_type=U4X2, d_type=BF16, ldb=_ld(Wq), lo_first=lo_first)
+    else:
+        K, N = Wq.shape
+        out = out if out is not None else torch.empty(K * N, dtype=torch.uint8, device=Wq.device)
+        p = plan(KIND_W4, 1, N, K, a_type=BF16, b_type=WEIGHT_FORMATS[fmt], d_type=BF16, ldb=_ld(Wq), group=32,
+                 zero_point=_DEFAULT_ZP[fmt])
     _check(lib().gemm_w4_prepack(p.handle, _ptr(Wq), _ptr(out), _stream(stream)), "gemm_w4_prepack")
     return out
 

@@ -284,8 +284,9 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         if (d.a_type != GE_BF16 || d.scale_type != GE_BF16)
             return fail(GE_ERR_UNSUPPORTED, "8-bit weights need bf16 X and bf16 scales");
         if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "8-bit weights are [K, N]");
-        if (d.flags & (GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED))
-            return fail(GE_ERR_INVALID_ARG, "nibble order and prepacking apply to int4 weights only");
+        if (d.flags & GE_FLAG_NIBBLE_LO_FIRST) return fail(GE_ERR_INVALID_ARG, "nibble order applies to int4 weights only");
+        if ((d.flags & GE_FLAG_W4_PREPACKED) && (d.M > 16 || d.N % 128 || d.K % 32))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked 8-bit weights need M <= 16, N %% 128 == 0 and K %% 32 == 0");
         if (pl.group != 32 && pl.group != 64 && pl.group != 128 && pl.group != 256)
             return fail(GE_ERR_UNSUPPORTED, "group size %d not in {32, 64, 128, 256}", pl.group);
         if (d.K % pl.group) return fail(GE_ERR_INVALID_ARG, "K %% group != 0");
@@ -600,7 +601,7 @@ ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *W
                               const void *C, const void *bias, const void *R, void *D, void *ws, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
-    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw int4 weights");
+    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw (not prepacked) weights");
     if (!X || !Wq || !scales) return fail(GE_ERR_INVALID_ARG, "X, Wq or scales is NULL");
     ge_status st = check_epi_ptrs(pl, C, bias, R, D);
     if (st || (st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
@@ -628,7 +629,7 @@ ge_status gemm_w4_run_unfused(const ge_plan *pl, const void *X, const uint8_t *W
 ge_status gemm_w4_dequant_run(const ge_plan *pl, const uint8_t *Wq, const void *scales, void *W, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
-    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw int4 weights");
+    if (pl->d.flags & GE_FLAG_W4_PREPACKED) return fail(GE_ERR_UNSUPPORTED, "this entry point takes raw (not prepacked) weights");
     if (!Wq || !scales || !W) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     ge_status st;
     if ((st = check_device(pl))) return st;
@@ -644,7 +645,17 @@ ge_status gemm_w4_prepack(const ge_plan *pl, const uint8_t *Wq, uint8_t *Wp, voi
     if (pl->kind != GE_KIND_W4) return fail(GE_ERR_INVALID_ARG, "plan is not a w4 plan");
     if (!Wq || !Wp) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     const ge_desc &d = pl->d;
-    if (d.b_type != GE_U4X2) return fail(GE_ERR_UNSUPPORTED, "prepacking applies to int4 weights");
+    if (d.b_type == GE_U8 || d.b_type == GE_FP8E4M3) {
+        if (d.N % 128 || d.K % 32) return fail(GE_ERR_UNSUPPORTED, "8-bit prepack needs N %% 128 == 0 and K %% 32 == 0");
+        if (((uintptr_t)Wp & 15) || ((uintptr_t)Wq & 7) || (pl->ldb & 7))
+            return fail(GE_ERR_ALIGN, "8-bit prepack needs an 8-byte aligned Wq and ldb and a 16-byte aligned Wp");
+        const size_t nq8 = (size_t)(d.K - 1) * pl->ldb + d.N, np8 = (size_t)d.K * d.N;
+        if (overlaps(Wq, nq8, Wp, np8)) return fail(GE_ERR_INVALID_ARG, "Wp overlaps Wq");
+        ge_status st8;
+        if ((st8 = check_device(pl))) return st8;
+        return hip_status(launch_w8_prepack(d.K, d.N, Wq, pl->ldb, Wp, (hipStream_t)stream), "gemm_w4_prepack");
+    }
+    if (d.b_type != GE_U4X2) return fail(GE_ERR_UNSUPPORTED, "prepacking applies to int4 and 8-bit weights");
     if (d.N % 16 || d.K % 128) return fail(GE_ERR_UNSUPPORTED, "prepack needs N %% 16 == 0 and K %% 128 == 0");
     if ((uintptr_t)Wp & 15) return fail(GE_ERR_ALIGN, "Wp must be 16-byte aligned");
     const size_t nq = (size_t)(d.K - 1) * pl->ldb + d.N / 2, np = (size_t)d.K * d.N / 2;

@@ -57,6 +57,9 @@ const char *tile_w4_kernel_name();
 hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,
                              hipStream_t s);
 
+// One-time conversion of raw [K, N] 8-bit codes to the prepacked decode layout.
+hipError_t launch_w8_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, uint8_t *Wp, hipStream_t s);
+
 // One-time conversion of raw [K, N] bf16 weights to the prepacked decode layout.
 hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s);
 

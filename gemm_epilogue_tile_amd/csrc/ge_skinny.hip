@@ -648,14 +648,21 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
     const int kb0 = (ks * S_WAVES + wave) * per, kb1 = min(nkb, kb0 + per);
 
     const bool nin = n0 + 8 * i < p.N;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)(p.K - 1) * p.ldb + p.N);
+    // raw [K, N] codes: lane (g, i) reads rows 8 g + r of the block, bytes n0 + 8 i ..; prepacked
+    // (gemm_w4_prepack): the column block's run of 4 KB blocks, load r of a block being the 64 lanes'
+    // 8 bytes in lane order (512 contiguous bytes)
+    const bool packed = p.w4_packed != 0;
+    const __amdgpu_buffer_rsrc_t rw =
+        packed ? make_rsrc((const char *)p.B + (int64_t)cb * nkb * 4096, (int64_t)nkb * 4096)
+               : make_rsrc(p.B, (int64_t)(p.K - 1) * p.ldb + p.N);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2);
     // lane parts of the offsets (OOB for lanes past N or M); block parts are uniform
-    const uint32_t vw = nin ? (uint32_t)(8 * g * p.ldb + n0 + 8 * i) : OOB;
+    const uint32_t vw = packed ? (uint32_t)(lane * 8) : nin ? (uint32_t)(8 * g * p.ldb + n0 + 8 * i) : OOB;
     const uint32_t vx = i < p.M ? (uint32_t)((i * p.lda + 8 * g) * 2) : OOB;
     const uint32_t vs = nin ? (uint32_t)((n0 + 8 * i) * 2) : OOB;
-    const uint32_t blk_w = (uint32_t)(32 * p.ldb);
+    const uint32_t blk_w = packed ? 4096u : (uint32_t)(32 * p.ldb);
+    const uint32_t row_w = packed ? 512u : (uint32_t)p.ldb;
     const float zp = (float)p.zero_point;
 
     f32x4 acc[8], part[8], xs = {0.f, 0.f, 0.f, 0.f};
@@ -675,7 +682,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
             w[slot][r] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, lw, so + (uint32_t)(r * p.ldb), 0));
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, lw, so + (uint32_t)r * row_w, 0));
         xr[slot] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? vx : OOB, in ? (uint32_t)kb * 64u : 0u, 0));
         sr[slot] = __builtin_bit_cast(
@@ -810,6 +817,28 @@ hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb
     return hipGetLastError();
 }
 
+// raw [K, N] 8-bit codes (row stride ldq) -> the prepacked layout: piece u (8 bytes) is lane u % 64 of
+// load (u / 64) % 8 of 32-row block (u / 512) % (K / 32) of column block u / (512 K / 32), i.e. rows
+// 32 kb + 8 (lane / 16) + r, columns 128 cb + 8 (lane % 16) .. + 7
+__global__ __launch_bounds__(256) void w8_prepack_kernel(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
+                                                         uint8_t *Wp) {
+    const int64_t nkb = K / 32, total = (int64_t)(N / 128) * nkb * 512;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+        const int l = (int)(u & 63), r = (int)((u >> 6) & 7);
+        const int64_t blk = u >> 9, kb = blk % nkb, cb = blk / nkb;
+        const int64_t k = kb * 32 + 8 * (l >> 4) + r, n = cb * 128 + 8 * (l & 15);
+        *(u32x2 *)(Wp + u * 8) = *(const u32x2 *)(Wq + k * ldq + n);
+    }
+}
+
+hipError_t launch_w8_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, uint8_t *Wp, hipStream_t s) {
+    const int64_t total = (int64_t)(N / 128) * (K / 32) * 512;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(w8_prepack_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s, K, N, Wq, ldq, Wp);
+    return hipGetLastError();
+}
+
 bool skinny_supported(const Problem &p) {
     if (p.ab_type != GE_BF16 || p.M > 32) return false;
     if (p.mode == MODE_SWIGLU) return false;
@@ -819,6 +848,7 @@ bool skinny_supported(const Problem &p) {
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31) && (int64_t)p.K * 256 < (1ll << 31);
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
         // 8-bit codes: 8-byte weight loads, 16-byte scale loads, 32-bit offsets
+        if (p.w4_packed && ((p.N % 128) || !al16(p.B) || (int64_t)p.K * 128 >= (1ll << 31))) return false;
         return p.M <= 16 && (p.K % 32) == 0 && (p.N % 8) == 0 && ((uintptr_t)p.B & 7) == 0 && (p.ldb % 8) == 0 &&
                al16(p.scales) && (p.ld_s % 8) == 0 && (int64_t)p.K * p.ldb < (1ll << 31) &&
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
@@ -920,8 +950,13 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
              "skinny_u8_m16_128col_split8"},
             {"skinny_fp8_m16_128col", "skinny_fp8_m16_128col_split2", "skinny_fp8_m16_128col_split4",
              "skinny_fp8_m16_128col_split8"}};
+        static const char *packed_names[2][4] = {
+            {"skinny_u8_m16_128col_prepacked", "skinny_u8_m16_128col_split2_prepacked",
+             "skinny_u8_m16_128col_split4_prepacked", "skinny_u8_m16_128col_split8_prepacked"},
+            {"skinny_fp8_m16_128col_prepacked", "skinny_fp8_m16_128col_split2_prepacked",
+             "skinny_fp8_m16_128col_split4_prepacked", "skinny_fp8_m16_128col_split8_prepacked"}};
         const int s = w8_split(p, cu_count);
-        return names[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
+        return (p.w4_packed ? packed_names : names)[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
     if (p.b_packed)

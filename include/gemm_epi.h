@@ -127,9 +127,11 @@ typedef int32_t ge_status;
  *   W4 with 8-bit codes: b = U8 (W = (q - zero_point) * s, zero_point in
  *            [0, 255]) or FP8E4M3 (W = e4m3(q) * s, zero_point 0; NaN codes
  *            give NaN), Wq [K, N] bytes with ldb >= N, scales [K/group, N]
- *            bf16, group in {32, 64, 128, 256}, K % group == 0; flags
- *            NIBBLE_LO_FIRST and W4_PREPACKED are invalid.  The dequantised
- *            weights are exact in the product (bf16 / fp32 arithmetic).
+ *            bf16, group in {32, 64, 128, 256}, K % group == 0; flag
+ *            NIBBLE_LO_FIRST is invalid, W4_PREPACKED (Wq in the layout
+ *            gemm_w4_prepack writes for 8-bit codes) needs M <= 16,
+ *            N % 128 == 0 and K % 32 == 0.  The dequantised weights are exact
+ *            in the product (bf16 / fp32 arithmetic).
  */
 typedef struct ge_desc {
     int32_t M, N, K;         /* > 0; M * N and K * N below 2^31 */
@@ -215,6 +217,13 @@ GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *
  * 32*b + 8*(l/16) + j (b = 0..3, one dword per b; code j at bit
  * 4*(j/2) + 16*(j%2)).  Needs N % 16 == 0, K % 128 == 0 and a 16-byte aligned
  * Wp that does not overlap Wq.  Asynchronous on the stream.
+ * For a plan with 8-bit codes (b_type U8 or FP8E4M3) it reads Wq [K, N]
+ * bytes (row stride ldb, a multiple of 8, 8-byte aligned) and writes the K*N
+ * bytes in the layout the 8-bit decode kernel streams: for each 128-column
+ * block (outer) and 32-row K block (inner), 4 KiB holding 8 loads of 512
+ * bytes; load r holds, for lane l = 0..63 at byte 8*l, the codes of row
+ * 32*kb + 8*(l/16) + r, columns 128*cb + 8*(l%16) .. + 7.  Needs N % 128 == 0
+ * and K % 32 == 0.
  */
 GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t *Wp, void *stream);
 

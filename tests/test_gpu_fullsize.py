@@ -30,8 +30,10 @@ def _run(name, inp):
         return ge.swiglu(d["X"], d["Wg"], d["Wu"])
     Wq = torch.from_numpy(inp["Wq"]).to(DEV)
     if inp["kind"] == "w8":
-        return ge.w4_gemm(d["X"], Wq, d["scales"], bias=d.get("bias"), group=inp["group"],
-                          zero_point=inp["zero_point"], fmt=inp["fmt"])
+        packed = name.endswith("+prepacked")
+        return ge.w4_gemm(d["X"], ge.w4_prepack(Wq, fmt=inp["fmt"]) if packed else Wq, d["scales"],
+                          bias=d.get("bias"), group=inp["group"], zero_point=inp["zero_point"], fmt=inp["fmt"],
+                          prepacked=packed)
     packed = True  # the fused path takes prepacked weights, as in the benchmark
     return ge.w4_gemm(d["X"], ge.w4_prepack(Wq) if packed else Wq, d["scales"], bias=d.get("bias"),
                       group=inp["group"], zero_point=inp["zero_point"], prepacked=packed)
@@ -40,7 +42,8 @@ def _run(name, inp):
 @pytest.mark.parametrize("name,nrows", [("tiny_fp32", 64), ("square_bf16", 24), ("swiglu_8b", 8),
                                         ("skinny_decode", 16), ("skinny_decode+prepacked", 16),
                                         ("w4a16_m16", 16), ("w4a16_m512", 24),
-                                        ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16)])
+                                        ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16),
+                                        ("w8a16_u8_m16+prepacked", 16), ("w8a16_fp8_m16+prepacked", 16)])
 def test_full_size_sampled_rows(name, nrows):
     w = workloads.WORKLOADS[name.split("+")[0]]
     inp = workloads.make_inputs(w)

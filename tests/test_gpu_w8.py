@@ -192,3 +192,65 @@ def test_w8_split_handoff_is_stable_over_many_calls(fmt):
     bad = [i for i, o in enumerate(outs) if not torch.equal(o.view(torch.int16), first)]
     assert not bad, f"calls {bad[:10]} differ from the first"
 
+
+
+# ---------------------------------------------------------------------------
+# prepacked 8-bit codes (gemm_w4_prepack on an 8-bit plan)
+# ---------------------------------------------------------------------------
+
+def _host_prepack8(Wq: np.ndarray) -> np.ndarray:
+    """The documented layout, with numpy: block (cb, kb), load r, lane l holds row 32 kb + 8 (l // 16) + r,
+    columns 128 cb + 8 (l % 16) .. + 7."""
+    K, N = Wq.shape
+    v = Wq.reshape(K // 32, 4, 8, N // 128, 16, 8)  # kb, l//16, r, cb, l%16, byte
+    return np.ascontiguousarray(v.transpose(3, 0, 2, 1, 4, 5)).reshape(-1)  # cb, kb, r, l//16, l%16, byte
+
+
+def _w8_packed(inp, **kw):
+    d = dev_inputs(inp)
+    Wp = ge.w4_prepack(torch.from_numpy(inp["Wq"]).to(DEV), fmt=inp["fmt"])
+    return ge.w4_gemm(d["X"], Wp, d["scales"], bias=d.get("bias"), C=d.get("C"), R=d.get("R"), alpha=inp["alpha"],
+                      beta=inp["beta"], act=inp["act"], group=inp["group"], zero_point=inp["zero_point"],
+                      fmt=inp["fmt"], prepacked=True, **kw)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_prepack_layout_matches_the_documented_one(fmt):
+    K, N = 96, 384
+    Wq = workloads.uniform_bytes((K, N), wid=95, tid=1)
+    got = ge.w4_prepack(torch.from_numpy(Wq).to(DEV), fmt=fmt).cpu().numpy()
+    assert np.array_equal(got, _host_prepack8(Wq))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K,group", [(16, 8192, 4096, 128), (1, 128, 32, 32), (7, 1024, 2048, 64),
+                                         (16, 2048, 8192, 256), (13, 384, 1024, 32)])
+def test_w8_prepacked_matches_the_oracle(fmt, M, N, K, group):
+    w = dataclasses.replace(BASE[fmt], M=M, N=N, K=K, group=group)
+    inp = workloads.make_inputs(w, seed=M + N + group)
+    p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.WEIGHT_FORMATS[fmt], bias=True, group=group,
+                zero_point=inp["zero_point"], prepacked=True)
+    assert p.kernel.startswith(f"skinny_{fmt}_m16_128col")
+    for seed in (0, 1):  # two calls on one plan: the split counters re-arm themselves
+        if seed:
+            inp = workloads.make_inputs(w, seed=M + N + group + 100)
+        assert_close(_w8_packed(inp), oracle.reference(inp), TOL_BF16, f"{fmt} packed {M}x{N}x{K} g{group} #{seed}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_prepacked_every_epilogue_term(fmt):
+    w = dataclasses.replace(BASE[fmt], M=16, N=256, K=512, alpha=0.5, beta=-1.0, act="gelu_tanh", bias=True,
+                            C=True, R=True)
+    inp = workloads.make_inputs(w, seed=17)
+    assert_close(_w8_packed(inp), oracle.reference(inp), TOL_BF16, f"{fmt} packed b/c/r gelu")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_prepacked_refusals(fmt):
+    bt = ge.WEIGHT_FORMATS[fmt]
+    zp = 128 if fmt == "u8" else 0
+    for M, N, K in [(17, 256, 256), (16, 200, 256), (16, 256, 48)]:
+        with pytest.raises(ge.GemmEpiError):
+            ge.plan(ge.KIND_W4, M, N, K, b_type=bt, zero_point=zp, group=16 if K == 48 else 128, prepacked=True)
+    with pytest.raises(ge.GemmEpiError):
+        ge.w4_prepack(torch.zeros((64, 200), dtype=torch.uint8, device=DEV), fmt=fmt)
