@@ -124,3 +124,60 @@ def test_scratch_using_calls_replay_in_a_graph():
         for be, bg in zip(oe, og):
             assert torch.equal(be, bg), f"replay {rep} differs from the eager calls"
         assert all(torch.isfinite(t.float()).all() for t in og)
+
+
+def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
+    # prepacked bf16 decode (plain and stream-K, whose plan scratch holds self-re-arming counters),
+    # prepacked 8-bit codes with the K split, and the RoPE scores kernel, captured once and replayed
+    # with new activations each time; every replay bitwise equal to the eager calls
+    g = torch.Generator().manual_seed(13)
+
+    def acts(seed):
+        h = torch.Generator().manual_seed(seed)
+        return [t.bfloat16().to(DEV) for t in (torch.randn(16, 1024, generator=h), torch.randn(16, 256, generator=h),
+                                               torch.randn(16, 4096, generator=h),
+                                               torch.randn(2, 256, 128, generator=h),
+                                               torch.randn(2, 384, 128, generator=h))]
+
+    xs, xp, x8, Q, K = acts(3)
+    Ws = ge.b_prepack((torch.randn(1024, 8192, generator=g) / 32).bfloat16().to(DEV))
+    Wp = ge.b_prepack((torch.randn(256, 16512, generator=g) / 16).bfloat16().to(DEV))
+    Wq8 = ge.w4_prepack(torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV), fmt="u8")
+    s8 = torch.full((32, 4096), 0.001).bfloat16().to(DEV)
+    cos, sin = (torch.from_numpy(t).to(DEV) for t in workloads.rope_tables(384, 128, 500000.0))
+
+    def outs():
+        return [torch.empty(16, 8192, dtype=torch.bfloat16, device=DEV),
+                torch.empty(16, 16512, dtype=torch.bfloat16, device=DEV),
+                torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV),
+                torch.empty(2, 256, 384, dtype=torch.float32, device=DEV)]
+
+    def prepare(o):
+        return [ge.prepare_gemm_epilogue(xs, Ws, out=o[0], prepacked=True),
+                ge.prepare_gemm_epilogue(xp, Wp, out=o[1], prepacked=True),
+                ge.prepare_w4_gemm(x8, Wq8, s8, out=o[2], zero_point=128, fmt="u8", prepacked=True),
+                ge.prepare_rope_qk(Q, K, cos, sin, out=o[3], q_pos0=128, alpha=0.125)]
+
+    oe, og = outs(), outs()
+    eager, graph_calls = prepare(oe), prepare(og)
+    kernels = [f._plan.kernel for f in eager[:3]]
+    assert kernels == ["skinny_bf16_m16_prepacked_streamk", "skinny_bf16_m16_128col_prepacked",
+                       "skinny_u8_m16_128col_split4_prepacked"]
+    for f in eager + graph_calls:
+        f()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in graph_calls:
+            f.with_stream()()
+    for rep in range(4):
+        for dst, src in zip((xs, xp, x8, Q, K), acts(300 + rep)):
+            dst.copy_(src)
+        for f in eager:
+            f()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for be, bg in zip(oe, og):
+            assert torch.equal(be, bg), f"replay {rep} differs from the eager calls"
+        assert all(torch.isfinite(t.float()).all() for t in og)
