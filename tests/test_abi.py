@@ -180,3 +180,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ge, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ge.lib()
+
+
+@pytest.mark.skipif(_has_gpu(), reason="without a GPU every host-valid descriptor must stop at NO_DEVICE")
+def test_random_descriptors_get_a_documented_status_and_a_message():
+    # hypothesis-generated descriptors, garbage included: the planner never crashes, returns one of
+    # the documented statuses (no plan can be made without a GPU) and always leaves a message
+    hyp = pytest.importorskip("hypothesis")
+    st = hyp.strategies
+
+    @hyp.settings(max_examples=400, deadline=None, database=None)
+    @hyp.given(kind=st.integers(-1, 4), M=st.integers(-2, 70000), N=st.integers(-2, 70000), K=st.integers(-2, 70000),
+               a_type=st.integers(-1, 5), b_type=st.integers(-1, 5), c_type=st.integers(-1, 5),
+               d_type=st.integers(-1, 5), bias_type=st.integers(-1, 5), r_type=st.integers(-1, 5),
+               b_layout=st.integers(-1, 2), act=st.integers(-1, 5), flags=st.integers(0, 127),
+               group=st.sampled_from([0, 16, 32, 64, 100, 128, 256, 512]), zero_point=st.integers(-2, 300),
+               lda=st.sampled_from([0, 1, 7, 64, 4096, 100000]), ldb=st.sampled_from([0, 1, 7, 64, 4096, 100000]),
+               beta=st.sampled_from([0.0, 0.5]))
+    def check(kind, M, N, K, a_type, b_type, c_type, d_type, bias_type, r_type, b_layout, act, flags, group,
+              zero_point, lda, ldb, beta):
+        s = _plan_status(kind, M=M, N=N, K=K, a_type=a_type, b_type=b_type, c_type=c_type, d_type=d_type,
+                         bias_type=bias_type, r_type=r_type, b_layout=b_layout, act=act, flags=flags,
+                         group_size=group, zero_point=zero_point, lda=lda, ldb=ldb, beta=beta)
+        assert s in (ge.ERR_INVALID_ARG, ge.ERR_UNSUPPORTED, ge.ERR_NO_DEVICE, ge.ERR_ALIGN)
+        assert ge.lib().ge_last_error()
+
+    check()

@@ -38,6 +38,24 @@ def test_bf16_gelu_bias_residual_ragged(M, N, K):
     assert_close(_generic(inp), oracle.reference(inp), TOL_BF16, f"bf16 {M}x{N}x{K}")
 
 
+def _random_cases(n=32, seed=20261202):
+    rng = np.random.default_rng(seed)
+    acts, flag_sets = ["none", "relu", "gelu_tanh", "silu"], ["", "b", "c", "r", "bcr"]
+    return [(int(M), int(N), int(K), acts[c % 4], flag_sets[(c * 3) % 5])
+            for c, (M, N, K) in enumerate(rng.integers(1, 301, size=(n, 3)))]
+
+
+@pytest.mark.parametrize("M,N,K,act,flags", _random_cases())
+def test_random_ragged_shapes_through_the_generic_path(M, N, K, act, flags):
+    # seeded sweep over M, N, K in [1, 300] with every activation and epilogue term
+    import dataclasses
+    w = dataclasses.replace(SQ, M=M, N=N, K=K, alpha=0.75 if "c" in flags else 1.0,
+                            beta=-0.5 if "c" in flags else 0.0, act=act, bias="b" in flags, C="c" in flags,
+                            R="r" in flags)
+    inp = workloads.make_inputs(w, seed=M * 1000 + N)
+    assert_close(_generic(inp), oracle.reference(inp), TOL_BF16, f"random {M}x{N}x{K} {act}/{flags}")
+
+
 @pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh", "silu"])
 @pytest.mark.parametrize("flags", ["", "b", "c", "r", "bcr"])
 def test_bf16_every_activation_and_flag(act, flags):
