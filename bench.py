@@ -387,7 +387,10 @@ def main():
     ge.lib()  # fails loudly when the HIP library is missing
     if a.workloads:
         for name in a.workloads.split(","):
-            r = measure(name, a.steps, a.warmup, unfused_chain=False)
+            if name == "rope_qk_prefill":
+                r = dict(name=name, **measure_rope_qk(a.steps, a.warmup))
+            else:
+                r = measure(name, a.steps, a.warmup, unfused_chain=False)
             print(json.dumps({k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
             torch.cuda.empty_cache()
         return

@@ -132,7 +132,7 @@ struct TileRegs {
     }
 };
 
-// One workgroup per (head, 128-query tile): the query tile is rotated once into LDS; the key tiles
+// One workgroup per (head, 128-query tile), XCD-aware: the query tile is rotated once into LDS; the key tiles
 // follow one another through two LDS buffers, the next one's chunks and tables requested into
 // registers before the current one is multiplied and its scores stored.
 template <int D, bool INTER, bool ROT, bool F32OUT>
@@ -140,7 +140,13 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(RopeArgs a) {
     constexpr int LD = D + 8;
     extern __shared__ __attribute__((aligned(16))) uint16_t rsm[];
     uint16_t *qs = rsm;
-    const int b = blockIdx.y, m0 = blockIdx.x * RT;
+    // workgroup -> (head, query tile): consecutive ids land on different XCDs (round-robin), so ids
+    // are regrouped so that each XCD owns a contiguous run of (head, query tile) pairs, i.e. whole
+    // heads, whose key tiles its L2 then fetches once instead of once per query tile
+    const int nq = (a.Sq + RT - 1) / RT, total = nq * a.batch;
+    int pair = blockIdx.x;
+    if ((total & 7) == 0) pair = (pair & 7) * (total >> 3) + (pair >> 3);
+    const int b = pair / nq, m0 = (pair % nq) * RT;
     const uint16_t *Kb = a.K + (int64_t)b * a.Sk * D;
     const int ntiles = (a.Sk + RT - 1) / RT;
 
@@ -237,7 +243,7 @@ hipError_t go_qk(const RopeArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const dim3 grid((a.Sq + RT - 1) / RT, a.batch);
+    const dim3 grid((unsigned)(((a.Sq + RT - 1) / RT) * a.batch));
     hipLaunchKernelGGL(k, grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
