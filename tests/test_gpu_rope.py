@@ -40,7 +40,7 @@ def test_rotation_alone_is_bit_exact(D, interleaved):
 
 
 @pytest.mark.parametrize("H,Sq,Sk,D", [(1, 1, 1, 64), (2, 128, 128, 128), (3, 77, 200, 128), (2, 300, 131, 64),
-                                       (4, 1, 517, 128)])
+                                       (4, 1, 517, 128), (8, 129, 140, 64), (8, 384, 257, 128)])
 @pytest.mark.parametrize("interleaved", [False, True])
 def test_fused_scores_match_the_oracle(H, Sq, Sk, D, interleaved):
     w = RW.with_shape(heads=H, Sq=Sq, Sk=Sk, D=D, interleaved=interleaved, k_pos0=5, q_pos0=5 + Sk - Sq if Sk >= Sq else 5)
