@@ -855,7 +855,8 @@ bool skinny_supported(const Problem &p) {
     }
     if (p.mode == MODE_W4) {
         return p.w4_packed && p.M <= 16 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
-               (p.group == 32 || p.group == 64 || p.group == 128);
+               (p.group == 32 || p.group == 64 || p.group == 128) &&
+               ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
     }
     if (p.b_layout != GE_LAYOUT_KN || !al16(p.B) || (p.ldb & 7) || (p.N & 7)) return false;
     const int64_t b_bytes = ((int64_t)(p.K - 1) * p.ldb + p.N) * 2;

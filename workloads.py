@@ -70,6 +70,21 @@ def uniform(shape, lo, hi, dtype, *, wid, tid, seed=0):
     return _store(x, dtype)
 
 
+def lattice_bf16(rows: int, cols: int, *, seed: int = 0) -> np.ndarray:
+    """bf16 bits of ((17 i + 29 j + seed) mod 251 - 125) / 256 at row i, column j.
+
+    Deterministic, exact in bf16 (at most 7 significant bits), never periodic
+    along a row over fewer than 251 columns, and cheap at any size: for
+    matrices too large to draw element by element (several GiB)."""
+    table = f32_to_bf16_bits((np.arange(502, dtype=np.float32) % 251 - 125) / 256)
+    cj = ((29 * np.arange(cols, dtype=np.int64) + seed) % 251).astype(np.int16)
+    out = np.empty((rows, cols), dtype=np.uint16)
+    for r0 in range(0, rows, 512):
+        ri = ((17 * np.arange(r0, min(rows, r0 + 512), dtype=np.int64)) % 251).astype(np.int16)
+        np.take(table, ri[:, None] + cj[None, :], out=out[r0:r0 + len(ri)])
+    return out
+
+
 def uniform_bytes(shape, *, wid, tid, seed=0) -> np.ndarray:
     g = _rng(wid, tid, seed)
     return g.integers(0, 256, size=shape, dtype=np.uint8)
