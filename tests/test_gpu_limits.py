@@ -4,8 +4,10 @@ The streaming and tile kernels address each operand through 32-bit buffer
 offsets, so a plan sends a problem whose operand spans 2^31 bytes or more to
 the general kernel, which addresses memory with 64-bit offsets.  Here a decode
 product with an LM-head-sized weight (a 152064-token vocabulary: 16 x 152064
-x 8192 bf16, 2.3 GiB) takes that route, and one just under 2 GiB (16 x 131064
-x 8192) the streaming kernel;
+x 8192 bf16, 2.3 GiB) takes that route; the same weight prepacked runs on the
+prepacked streaming kernel, which rebases its range on each 128-column block;
+and one just under 2 GiB (16 x 131064 x 8192) runs on the raw-layout streaming
+kernel;
 output columns at both ends and in between are checked against the oracle,
 computed on the same columns."""
 import numpy as np
@@ -22,17 +24,22 @@ K = 8192
 WID = 20  # seed stream of these inputs
 
 
-@pytest.mark.parametrize("N,kernel", [(152064, "general_64x64"), (131064, "skinny_bf16_m16")])
-def test_weights_past_and_below_2gib(N, kernel):
+@pytest.mark.parametrize("N,prepacked,kernel", [(152064, False, "general_64x64"),
+                                                (152064, True, "skinny_bf16_m16_128col_prepacked"),
+                                                (131064, False, "skinny_bf16_m16")])
+def test_weights_past_and_below_2gib(N, prepacked, kernel):
     M = 16
-    assert (K * N * 2 >= 1 << 31) == (kernel == "general_64x64")
+    assert (K * N * 2 >= 1 << 31) == (N == 152064)
     A = workloads.normal((M, K), 1.0, "bf16", wid=WID, tid=0)
     B = workloads.lattice_bf16(K, N, seed=N)
     bias = workloads.normal((N,), 0.1, "bf16", wid=WID, tid=3)
     R = workloads.normal((M, N), 1.0, "bf16", wid=WID, tid=4)
-    assert ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True).kernel.startswith(kernel)
+    assert ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True, b_prepacked=prepacked).kernel.startswith(kernel)
     print(f"limits: 16x{N}x{K}, B {K * N * 2 / 2**30:.3f} GiB, kernel {kernel}", flush=True)
-    out = to_host(ge.gemm_epilogue(to_dev(A), to_dev(B), bias=to_dev(bias), R=to_dev(R)))
+    Bd = to_dev(B)
+    if prepacked:
+        Bd = ge.b_prepack(Bd)
+    out = to_host(ge.gemm_epilogue(to_dev(A), Bd, bias=to_dev(bias), R=to_dev(R), prepacked=prepacked))
     rng = np.random.default_rng(N)
     cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 256, N), rng.choice(N, 256, replace=False)]))
     ref = oracle.gemm_epilogue(A, np.ascontiguousarray(B[:, cols]), "bf16", bias=bias[cols],
