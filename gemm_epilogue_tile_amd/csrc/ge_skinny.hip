@@ -649,8 +649,8 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
 
     const bool nin = n0 + 8 * i < p.N;
     // raw [K, N] codes: lane (g, i) reads rows 8 g + r of the block, bytes n0 + 8 i ..; prepacked
-    // (gemm_w4_prepack): the column block's run of 4 KB blocks, load r of a block being the 64 lanes'
-    // 8 bytes in lane order (512 contiguous bytes)
+    // (gemm_w4_prepack): the column block's run of 4 KB blocks, rows r = 2q and 2q + 1 of a block
+    // being one 16-byte load per lane (1 KB contiguous over the 64 lanes)
     const bool packed = p.w4_packed != 0;
     const __amdgpu_buffer_rsrc_t rw =
         packed ? make_rsrc((const char *)p.B + (int64_t)cb * nkb * 4096, (int64_t)nkb * 4096)
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2);
     // lane parts of the offsets (OOB for lanes past N or M); block parts are uniform
-    const uint32_t vw = packed ? (uint32_t)(lane * 8) : nin ? (uint32_t)(8 * g * p.ldb + n0 + 8 * i) : OOB;
+    const uint32_t vw = packed ? (uint32_t)(lane * 16) : nin ? (uint32_t)(8 * g * p.ldb + n0 + 8 * i) : OOB;
     const uint32_t vx = i < p.M ? (uint32_t)((i * p.lda + 8 * g) * 2) : OOB;
     const uint32_t vs = nin ? (uint32_t)((n0 + 8 * i) * 2) : OOB;
     const uint32_t blk_w = packed ? 4096u : (uint32_t)(32 * p.ldb);
@@ -679,10 +679,20 @@ __global__ __launch_bounds__(S_THREADS) void skinny_w8_kernel(Problem p) {
         const bool in = kb < kb1;
         const uint32_t so = in ? (uint32_t)kb * blk_w : 0u;
         const uint32_t lw = in ? vw : OOB;
+        if (packed) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            w[slot][r] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, lw, so + (uint32_t)r * row_w, 0));
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, lw, so + (uint32_t)q * 1024u, 0));
+                w[slot][2 * q] = u32x2{v[0], v[1]};
+                w[slot][2 * q + 1] = u32x2{v[2], v[3]};
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                w[slot][r] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(rw, lw, so + (uint32_t)r * row_w, 0));
+        }
         xr[slot] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, in ? vx : OOB, in ? (uint32_t)kb * 64u : 0u, 0));
         sr[slot] = __builtin_bit_cast(
@@ -817,9 +827,10 @@ hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb
     return hipGetLastError();
 }
 
-// raw [K, N] 8-bit codes (row stride ldq) -> the prepacked layout: piece u (8 bytes) is lane u % 64 of
-// load (u / 64) % 8 of 32-row block (u / 512) % (K / 32) of column block u / (512 K / 32), i.e. rows
-// 32 kb + 8 (lane / 16) + r, columns 128 cb + 8 (lane % 16) .. + 7
+// raw [K, N] 8-bit codes (row stride ldq) -> the prepacked layout: the 8 bytes of lane l, row r
+// (0..7) of 32-row block kb of column block cb, i.e. row 32 kb + 8 (l / 16) + r, columns
+// 128 cb + 8 (l % 16) .. + 7, go to byte 1024 (r / 2) + 16 l + 8 (r % 2) of the block's 4 KB
+// (block index cb * K / 32 + kb), so one 16-byte load gives a lane rows 2q and 2q + 1
 __global__ __launch_bounds__(256) void w8_prepack_kernel(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq,
                                                          uint8_t *Wp) {
     const int64_t nkb = K / 32, total = (int64_t)(N / 128) * nkb * 512;
@@ -827,7 +838,7 @@ __global__ __launch_bounds__(256) void w8_prepack_kernel(int32_t K, int32_t N, c
         const int l = (int)(u & 63), r = (int)((u >> 6) & 7);
         const int64_t blk = u >> 9, kb = blk % nkb, cb = blk / nkb;
         const int64_t k = kb * 32 + 8 * (l >> 4) + r, n = cb * 128 + 8 * (l & 15);
-        *(u32x2 *)(Wp + u * 8) = *(const u32x2 *)(Wq + k * ldq + n);
+        *(u32x2 *)(Wp + blk * 4096 + (r >> 1) * 1024 + l * 16 + (r & 1) * 8) = *(const u32x2 *)(Wq + k * ldq + n);
     }
 }
 

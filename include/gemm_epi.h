@@ -220,10 +220,10 @@ GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *
  * For a plan with 8-bit codes (b_type U8 or FP8E4M3) it reads Wq [K, N]
  * bytes (row stride ldb, a multiple of 8, 8-byte aligned) and writes the K*N
  * bytes in the layout the 8-bit decode kernel streams: for each 128-column
- * block (outer) and 32-row K block (inner), 4 KiB holding 8 loads of 512
- * bytes; load r holds, for lane l = 0..63 at byte 8*l, the codes of row
- * 32*kb + 8*(l/16) + r, columns 128*cb + 8*(l%16) .. + 7.  Needs N % 128 == 0
- * and K % 32 == 0.
+ * block (outer) and 32-row K block (inner), 4 KiB holding 4 loads of 1 KiB;
+ * load q holds, for lane l = 0..63 at byte 16*l, the codes of rows
+ * 32*kb + 8*(l/16) + 2q and + 2q + 1 (8 bytes each, in that order), columns
+ * 128*cb + 8*(l%16) .. + 7.  Needs N % 128 == 0 and K % 32 == 0.
  */
 GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t *Wp, void *stream);
 

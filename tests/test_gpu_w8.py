@@ -199,11 +199,11 @@ def test_w8_split_handoff_is_stable_over_many_calls(fmt):
 # ---------------------------------------------------------------------------
 
 def _host_prepack8(Wq: np.ndarray) -> np.ndarray:
-    """The documented layout, with numpy: block (cb, kb), load r, lane l holds row 32 kb + 8 (l // 16) + r,
-    columns 128 cb + 8 (l % 16) .. + 7."""
+    """The documented layout, with numpy: block (cb, kb), load q, lane l holds rows 32 kb + 8 (l // 16)
+    + 2q and + 2q + 1 (8 bytes each), columns 128 cb + 8 (l % 16) .. + 7."""
     K, N = Wq.shape
-    v = Wq.reshape(K // 32, 4, 8, N // 128, 16, 8)  # kb, l//16, r, cb, l%16, byte
-    return np.ascontiguousarray(v.transpose(3, 0, 2, 1, 4, 5)).reshape(-1)  # cb, kb, r, l//16, l%16, byte
+    v = Wq.reshape(K // 32, 4, 4, 2, N // 128, 16, 8)  # kb, l//16, q, r%2, cb, l%16, byte
+    return np.ascontiguousarray(v.transpose(4, 0, 2, 1, 5, 3, 6)).reshape(-1)  # cb, kb, q, l//16, l%16, r%2, byte
 
 
 def _w8_packed(inp, **kw):
