@@ -119,9 +119,13 @@ __device__ __forceinline__ void stream_bf16(const Problem &p, int n0, int kb0, i
     const int g = lane >> 4, i = lane & 15;
     const int nkb = (p.K + 31) / 32;
 
-    // W: lane -> rows 8 g + r of the block, 16-byte column chunk i (columns n0 + 8 i ..)
+    // W: lane -> rows 8 g + r of the block, 16-byte column chunk i (columns n0 + 8 i ..).  The
+    // range starts at the wave's first row and column n0, so only the wave's share of W has to
+    // span less than 2^31 bytes (an empty share gets an empty range).
     const bool nin = i < NCH && n0 + 8 * i < p.N;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, ((int64_t)(p.K - 1) * p.ldb + p.N) * 2);
+    const int r0 = kb0 * 32, r1 = min(p.K, kb1 * 32);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc((const uint16_t *)p.B + ((int64_t)r0 * p.ldb + n0),
+                                                ((int64_t)(r1 - r0 - 1) * p.ldb + (p.N - n0)) * 2);
     // X: lane -> row mt*16 + i, k = 8 g .. 8 g + 7 of the block
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
 
@@ -129,8 +133,8 @@ __device__ __forceinline__ void stream_bf16(const Problem &p, int n0, int kb0, i
         const int k = kb * 32 + 8 * g;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const uint32_t off = (uint32_t)(((int64_t)(k + r) * p.ldb + n0 + 8 * i) * 2);
-            w[r] = bload16(rw, (nin && k + r < p.K) ? off : OOB);
+            const uint32_t off = (uint32_t)(((int64_t)(k + r - r0) * p.ldb + 8 * i) * 2);
+            w[r] = bload16(rw, (nin && k + r < r1 && k + r >= r0) ? off : OOB);
         }
     };
     auto load_x = [&](int kb, bf16x8 (&x)[MT]) {
@@ -870,7 +874,10 @@ bool skinny_supported(const Problem &p) {
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
     }
     if (p.b_layout != GE_LAYOUT_KN || !al16(p.B) || (p.ldb & 7) || (p.N & 7)) return false;
-    const int64_t b_bytes = ((int64_t)(p.K - 1) * p.ldb + p.N) * 2;
+    // the streaming loop addresses one wave's share of W at a time: at most ceil(K / 32 / 8)
+    // blocks of 32 rows (the plain kernel's share; the stream-K shares are no longer)
+    const int64_t share_rows = (int64_t)((p.K + 31) / 32 + S_WAVES - 1) / S_WAVES * 32;
+    const int64_t b_bytes = ((share_rows - 1) * p.ldb + p.N) * 2;
     const int64_t a_bytes = ((int64_t)(p.M - 1) * p.lda + p.K) * 2;
     return b_bytes < (1ll << 31) && a_bytes < (1ll << 31);
 }

@@ -1,13 +1,15 @@
 """GPU parity at operand sizes past the 32-bit offset range.
 
-The streaming and tile kernels address each operand through 32-bit buffer
-offsets, so a plan sends a problem whose operand spans 2^31 bytes or more to
-the general kernel, which addresses memory with 64-bit offsets.  Here a decode
-product with an LM-head-sized weight (a 152064-token vocabulary: 16 x 152064
-x 8192 bf16, 2.3 GiB) takes that route; the same weight prepacked runs on the
-prepacked streaming kernel, which rebases its range on each 128-column block;
-and one just under 2 GiB (16 x 131064 x 8192) runs on the raw-layout streaming
-kernel;
+The streaming and tile kernels address operands through 32-bit buffer
+offsets.  The decode kernels start a weight's range where a wave's (raw
+layout) or a column block's (prepacked layout) share begins, so only that
+share has to span less than 2^31 bytes; a problem no fast kernel can address
+runs on the general kernel, which uses 64-bit offsets.  Here a decode product
+with an LM-head-sized weight (a 152064-token vocabulary: 16 x 152064 x 8192
+bf16, 2.3 GiB) runs on the raw-layout and on the prepacked streaming kernel;
+one with an odd vocabulary (152063 columns, rows not 16-byte aligned) on the
+general kernel; and one just under 2 GiB (16 x 131064 x 8192) on the
+raw-layout streaming kernel;
 output columns at both ends and in between are checked against the oracle,
 computed on the same columns."""
 import numpy as np
@@ -24,12 +26,13 @@ K = 8192
 WID = 20  # seed stream of these inputs
 
 
-@pytest.mark.parametrize("N,prepacked,kernel", [(152064, False, "general_64x64"),
+@pytest.mark.parametrize("N,prepacked,kernel", [(152064, False, "skinny_bf16_m16"),
                                                 (152064, True, "skinny_bf16_m16_128col_prepacked"),
+                                                (152063, False, "general_64x64"),
                                                 (131064, False, "skinny_bf16_m16")])
 def test_weights_past_and_below_2gib(N, prepacked, kernel):
     M = 16
-    assert (K * N * 2 >= 1 << 31) == (N == 152064)
+    assert (K * N * 2 >= 1 << 31) == (N > 131064)
     A = workloads.normal((M, K), 1.0, "bf16", wid=WID, tid=0)
     B = workloads.lattice_bf16(K, N, seed=N)
     bias = workloads.normal((N,), 0.1, "bf16", wid=WID, tid=3)
