@@ -134,7 +134,7 @@ __device__ __forceinline__ void stream_bf16(const Problem &p, int n0, int kb0, i
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const uint32_t off = (uint32_t)(((int64_t)(k + r - r0) * p.ldb + 8 * i) * 2);
-            w[r] = bload16(rw, (nin && k + r < r1 && k + r >= r0) ? off : OOB);
+            w[r] = bload16(rw, (nin && k + r < r1) ? off : OOB);  // a wave reads rows >= r0 only
         }
     };
     auto load_x = [&](int kb, bf16x8 (&x)[MT]) {
