@@ -360,7 +360,7 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s) {
 bool tile_supported(const Problem &p) {
     if (p.mode == MODE_W4) return tile_w4_supported(p);
     if (p.ab_type != GE_BF16) return false;
-    if (p.M < 128) return false;
+    if (p.M <= 32) return false;  // the streaming kernels take M <= 32
     // buffer offsets are 31-bit: operands below 2 GiB
     const int64_t a_bytes = ((int64_t)(p.M - 1) * p.lda + p.K) * 2;
     const int64_t b_bytes = (p.b_layout == GE_LAYOUT_KN ? (int64_t)(p.K - 1) * p.ldb + p.N
@@ -388,11 +388,20 @@ int swiglu_big_blocks(const Problem &p, int cu_count) {
     return small <= cu_count ? nb : ncb;
 }
 
+// Plain products use 128 x 128 tiles when those fit in one round over the CUs (a few rows, or
+// few columns: 33..128 x 28672 and 512 x 8192 take 0.6-0.8x the time of 256 x 256 tiles, which
+// would leave half the CUs or more idle), and 256 x 256 tiles otherwise.
+static bool small_tiles(const Problem &p, int cu_count) {
+    const int64_t n128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+    return n128 <= (cu_count > 0 ? cu_count : 256);
+}
+
 const char *tile_kernel_name(const Problem &p, int cu_count) {
     if (p.mode == MODE_W4) return tile_w4_kernel_name();
     if (p.mode == MODE_SWIGLU)
         return swiglu_big_blocks(p, cu_count) * 128 < p.N ? "tile_swiglu_256x128x32+128x128x32"
                                                            : "tile_swiglu_256x128x32";
+    if (small_tiles(p, cu_count)) return p.b_layout == GE_LAYOUT_NK ? "tile_nk_128x128x32" : "tile_kn_128x128x32";
     return p.b_layout == GE_LAYOUT_NK ? "tile_nk_256x256x32" : "tile_kn_256x256x32";
 }
 
@@ -413,6 +422,10 @@ hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s) {
         hipError_t e = launch_cfg<256, 128, 2, 2, true, false>(big, s);
         if (e == hipSuccess) e = launch_cfg<128, 128, 2, 2, true, false>(rest, s);
         return e;
+    }
+    if (small_tiles(p, cu_count)) {
+        if (p.b_layout == GE_LAYOUT_NK) return launch_cfg<128, 128, 2, 2, false, true>(p, s);
+        return launch_cfg<128, 128, 2, 2, false, false>(p, s);
     }
     if (p.b_layout == GE_LAYOUT_NK) return launch_cfg<256, 256, 2, 2, false, true>(p, s);
     return launch_cfg<256, 256, 2, 2, false, false>(p, s);

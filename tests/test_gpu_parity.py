@@ -74,6 +74,25 @@ def test_fp32_operands_all_epilogue_terms(M, N, K):
     assert_close(_generic(inp), oracle.reference(inp), TOL_F32, f"fp32 {M}x{N}x{K}")
 
 
+# Plain products take 128 x 128 tiles when those fit in one round over the CUs, else 256 x 256
+# tiles; both sizes, both B layouts, ragged edges.
+@pytest.mark.parametrize("M,N,K,layout,kernel", [
+    (48, 28672, 256, "KN", "tile_kn_128x128x32"),      # batched decode rows: 224 tiles of 128
+    (100, 3000, 520, "NK", "tile_nk_128x128x32"),
+    (2100, 2056, 200, "KN", "tile_kn_256x256x32"),     # 289 tiles of 128 would take two rounds
+    (2100, 2056, 200, "NK", "tile_nk_256x256x32"),
+])
+def test_tile_size_choice_and_parity(M, N, K, layout, kernel):
+    w = SQ.with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N)
+    lay = ge.LAYOUT_KN if layout == "KN" else ge.LAYOUT_NK
+    assert ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True, act="gelu_tanh", b_layout=lay).kernel == kernel
+    d = dev_inputs(inp)
+    B = d["B"] if layout == "KN" else to_dev(np.ascontiguousarray(inp["B"].T))
+    out = ge.gemm_epilogue(d["A"], B, bias=d["bias"], R=d["R"], act="gelu_tanh", b_layout=layout)
+    assert_close(out, oracle.reference(inp), TOL_BF16, f"{kernel} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (100, 72, 200), (512, 512, 1024)])
 def test_nk_layout(M, N, K):
     w = SQ.with_shape(M=M, N=N, K=K)
