@@ -360,7 +360,8 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s) {
 bool tile_supported(const Problem &p) {
     if (p.mode == MODE_W4) return tile_w4_supported(p);
     if (p.ab_type != GE_BF16) return false;
-    if (p.M <= 32) return false;  // the streaming kernels take M <= 32
+    // the streaming kernels take plain products of M <= 32; SwiGLU has no streaming kernel
+    if (p.M <= 32 && p.mode != MODE_SWIGLU) return false;
     // buffer offsets are 31-bit: operands below 2 GiB
     const int64_t a_bytes = ((int64_t)(p.M - 1) * p.lda + p.K) * 2;
     const int64_t b_bytes = (p.b_layout == GE_LAYOUT_KN ? (int64_t)(p.K - 1) * p.ldb + p.N

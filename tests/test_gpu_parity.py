@@ -93,6 +93,16 @@ def test_tile_size_choice_and_parity(M, N, K, layout, kernel):
     assert_close(out, oracle.reference(inp), TOL_BF16, f"{kernel} {M}x{N}x{K}")
 
 
+# SwiGLU at decode sizes takes the tile kernel too (the streaming kernels have no dual form)
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 256), (16, 1000, 520), (31, 3000, 136)])
+def test_swiglu_few_rows_on_the_tile_kernel(M, N, K):
+    w = workloads.Workload("swiglu_rows", 2, "swiglu", M, N, K, "bf16")
+    inp = workloads.make_inputs(w, seed=M)
+    assert ge.plan(ge.KIND_SWIGLU, M, N, K).kernel.startswith("tile_swiglu"), M
+    d = dev_inputs(inp)
+    assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (100, 72, 200), (512, 512, 1024)])
 def test_nk_layout(M, N, K):
     w = SQ.with_shape(M=M, N=N, K=K)
