@@ -292,7 +292,7 @@ def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="
                   b_layout="KN", out=None, out_dtype=None, stream=None, prepacked=False):
     """D = act(alpha * A @ B + beta * C + bias) + R on the GPU (fused kernel).
 
-    ``prepacked``: B is the [K, N] tensor ``b_prepack`` returned (decode shapes, M <= 16)."""
+    ``prepacked``: B is the [K, N] tensor ``b_prepack`` returned (decode shapes, M <= 32)."""
     lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
     M = A.shape[0]
     N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]

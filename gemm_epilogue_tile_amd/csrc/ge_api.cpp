@@ -269,8 +269,8 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         pl.ldb = d.ldb ? d.ldb : (d.b_layout == GE_LAYOUT_KN ? d.N : d.K);
         if (pl.ldb < (d.b_layout == GE_LAYOUT_KN ? d.N : d.K)) return fail(GE_ERR_INVALID_ARG, "ldb too small");
         if ((d.flags & GE_FLAG_B_PREPACKED) &&
-            (d.a_type != GE_BF16 || d.b_layout != GE_LAYOUT_KN || d.M > 16 || d.N % 128 || d.K % 32))
-            return fail(GE_ERR_UNSUPPORTED, "prepacked bf16 weights need bf16 KN operands, M <= 16, N %% 128 == 0 "
+            (d.a_type != GE_BF16 || d.b_layout != GE_LAYOUT_KN || d.M > 32 || d.N % 128 || d.K % 32))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked bf16 weights need bf16 KN operands, M <= 32, N %% 128 == 0 "
                                             "and K %% 32 == 0");
     } else if (kind == GE_KIND_SWIGLU) {
         if (d.a_type != GE_BF16 || d.b_type != GE_BF16 || d.d_type != GE_BF16)

@@ -240,24 +240,28 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
 // epilogue runs on 8-column row chunks.
 // Blocks kbA .. kbB - 1 of column block cb: wave w takes kbA + w, kbA + w + 8, ..., so at any time
 // the workgroup reads 8 consecutive 8 KB pieces (64 KB of contiguous memory); a ring of SK_RING
-// blocks in flight per wave, blocks past kbB read zeros and add nothing.  acc[t]: lane (g, i)
-// holds rows 4 g + e of column 16 t + i.
-__device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, int kbB, f32x4 (&acc)[8]) {
+// blocks in flight per wave, blocks past kbB read zeros and add nothing.  acc[mt][t]: lane (g, i)
+// holds rows 16 mt + 4 g + e of column 16 t + i (MT 16-row tiles of X share each weight fragment).
+template <int MT>
+__device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, int kbB, f32x4 (&acc)[MT][8]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
     const int nkb = p.K / 32;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc((const char *)p.B + (int64_t)cb * nkb * 8192, (int64_t)nkb * 8192);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
-    const uint32_t xoff = (uint32_t)(((int64_t)i * p.lda + 8 * g) * 2);
-    const bool xin = i < p.M;
     u32x4 w[SK_RING][8];
-    bf16x8 xr[SK_RING];
+    bf16x8 xr[SK_RING][MT];
     auto load_blk = [&](int kb, int slot) {
         const bool in = kb < kbB;
 #pragma unroll
         for (int t = 0; t < 8; ++t) w[slot][t] = bload16(rw, in ? (uint32_t)(kb * 8192 + t * 1024 + lane * 16) : OOB);
-        xr[slot] = __builtin_bit_cast(bf16x8, bload16(rx, in && xin ? xoff + (uint32_t)kb * 64 : OOB));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + i;
+            const uint32_t xoff = (uint32_t)(((int64_t)m * p.lda + 8 * g) * 2);
+            xr[slot][mt] = __builtin_bit_cast(bf16x8, bload16(rx, in && m < p.M ? xoff + (uint32_t)kb * 64 : OOB));
+        }
     };
 #pragma unroll
     for (int j = 0; j < SK_RING - 1; ++j) load_blk(kbA + wave + S_WAVES * j, j);
@@ -266,29 +270,39 @@ __device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, 
         for (int u = 0; u < SK_RING; ++u) {
             load_blk(kb + S_WAVES * (u + SK_RING - 1), (u + SK_RING - 1) % SK_RING);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc[t] = mfma_bf16(xr[u], __builtin_bit_cast(bf16x8, w[u][t]), acc[t]);
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][t] = mfma_bf16(xr[u][mt], __builtin_bit_cast(bf16x8, w[u][t]), acc[mt][t]);
         }
     }
 }
 
-// partial tile of one wave (prepacked lane mapping) -> LDS red[wave][16][128]
-__device__ __forceinline__ void accp_to_lds(float *red, const f32x4 (&acc)[8]) {
+// partial tile of one wave (prepacked lane mapping) -> LDS red[wave][16 MT][128]
+template <int MT>
+__device__ __forceinline__ void accp_to_lds(float *red, const f32x4 (&acc)[MT][8]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) red[(wave * 16 + 4 * g + e4) * 128 + 16 * t + i] = acc[t][e4];
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                red[(wave * 16 * MT + 16 * mt + 4 * g + e4) * 128 + 16 * t + i] = acc[mt][t][e4];
 }
 
+template <int MT>
 __global__ __launch_bounds__(S_THREADS) void skinny_bf16p_kernel(Problem p) {
-    constexpr int NC = 128, MR = 16;
+    constexpr int NC = 128, MR = 16 * MT;
     __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
-    f32x4 acc[8];
+    f32x4 acc[MT][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_bf16p(p, blockIdx.x, 0, p.K / 32, acc);
-    accp_to_lds(red, acc);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16p<MT>(p, blockIdx.x, 0, p.K / 32, acc);
+    accp_to_lds<MT>(red, acc);
     __syncthreads();
     reduce_epilogue<MR, NC>(p, red, blockIdx.x * NC);
 }
@@ -350,8 +364,8 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (PACKED) {
-            stream_bf16p(p, cb, kbA, kbB, acc[0]);
-            accp_to_lds(red, acc[0]);
+            stream_bf16p<MT>(p, cb, kbA, kbB, acc);
+            accp_to_lds<MT>(red, acc);
         } else {
             stream_bf16<MT, NCH>(p, n0, k0, k1, acc);
             acc_to_lds<MT, NCH>(red, acc);
@@ -859,7 +873,7 @@ bool skinny_supported(const Problem &p) {
     if (p.mode == MODE_SWIGLU) return false;
     if (!al16(p.A) || (p.lda & 7) || (p.K & 7)) return false;
     if (p.b_packed)
-        return p.mode == MODE_GENERIC && p.M <= 16 && (p.N % 128) == 0 && (p.K % 32) == 0 && al16(p.B) &&
+        return p.mode == MODE_GENERIC && p.M <= 32 && (p.N % 128) == 0 && (p.K % 32) == 0 && al16(p.B) &&
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31) && (int64_t)p.K * 256 < (1ll << 31);
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
         // 8-bit codes: 8-byte weight loads, 16-byte scale loads, 32-bit offsets
@@ -979,7 +993,9 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
     }
     if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
     if (p.b_packed)
-        return bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk" : "skinny_bf16_m16_128col_prepacked";
+        return bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
+               : p.M <= 16                    ? "skinny_bf16_m16_128col_prepacked"
+                                              : "skinny_bf16_m32_128col_prepacked";
     if (bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
@@ -1030,7 +1046,10 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
         return hipGetLastError();
     }
     if (p.b_packed) {
-        hipLaunchKernelGGL(skinny_bf16p_kernel, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
+        if (p.M <= 16)
+            hipLaunchKernelGGL(skinny_bf16p_kernel<1>, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL(skinny_bf16p_kernel<2>, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
         return hipGetLastError();
     }
     const int nch = bf16_chunks(p.N, cu_count > 0 ? cu_count : 256);

@@ -98,7 +98,7 @@ typedef int32_t ge_status;
 #define GE_FLAG_RESIDUAL 4u        /* add R after the activation */
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
 #define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
-#define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 16: B is in the layout gemm_b_prepack writes */
+#define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 32: B is in the layout gemm_b_prepack writes */
 
 /*
  * Problem descriptor.  Unused fields must be zero.  dtype fields take
@@ -109,7 +109,7 @@ typedef int32_t ge_status;
  *   GENERIC  a_type == b_type in {F32, BF16}; c/bias/r/d types in {F32, BF16};
  *            b_layout KN or NK; any act; any flags except NIBBLE_LO_FIRST and
  *            W4_PREPACKED.  With GE_FLAG_B_PREPACKED (a decode-time weight
- *            layout): a = b = BF16, b_layout KN, M <= 16, N % 128 == 0,
+ *            layout): a = b = BF16, b_layout KN, M <= 32, N % 128 == 0,
  *            K % 32 == 0; the unfused entry points reject such plans.
  *   SWIGLU   a, b, d = BF16, b_layout KN, act = NONE, alpha = 1, no flags
  *            other than none; Wg and Wu share ldb.
@@ -228,7 +228,7 @@ GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *
 GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t *Wp, void *stream);
 
 /*
- * One-time weight conversion for the prepacked bf16 decode kernel (M <= 16;
+ * One-time weight conversion for the prepacked bf16 decode kernels (M <= 32;
  * the way a weight loader would store decode weights): reads B [K, N] bf16
  * (row stride = the plan's ldb) and writes the same K*N*2 bytes to Bp in the
  * kernel-native layout: for each 128-column block cb (outer) and 32-row K

@@ -123,7 +123,7 @@ def _plan_status(kind=ge.KIND_GENERIC, **kw):
     # prepacked 8-bit codes need M <= 16 and N % 128 == 0 (here M = 64, N = 64)
     (dict(b_type=4, zero_point=0, flags=16), ge.KIND_W4, ge.ERR_UNSUPPORTED),
     (dict(b_type=4, zero_point=0, flags=8), ge.KIND_W4, ge.ERR_INVALID_ARG),
-    (dict(flags=32, M=32, N=128), ge.KIND_GENERIC, ge.ERR_UNSUPPORTED),
+    (dict(flags=32, M=33, N=128), ge.KIND_GENERIC, ge.ERR_UNSUPPORTED),
     (dict(b_type=2, flags=32), ge.KIND_W4, ge.ERR_INVALID_ARG),
     (dict(b_type=3, b_layout=1), ge.KIND_W4, ge.ERR_UNSUPPORTED),
     (dict(b_type=3, group_size=48), ge.KIND_W4, ge.ERR_UNSUPPORTED),

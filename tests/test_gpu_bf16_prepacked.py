@@ -50,12 +50,14 @@ def test_prepack_reads_a_strided_source():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 32), (7, 256, 96), (16, 384, 1056), (13, 1024, 8192),
-                                   (16, 2048, 4096)])
+                                   (16, 2048, 4096), (17, 384, 1056), (29, 1024, 8192), (32, 28672, 512)])
 def test_prepacked_decode_ragged(M, N, K):
+    # M <= 16: one 16-row tile of X per weight fragment; 17 <= M <= 32: two
     w = DEC.with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N + K)
     p = ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True, b_prepacked=True)
-    assert p.kernel == "skinny_bf16_m16_128col_prepacked" and p.scratch_bytes == 0
+    want = "skinny_bf16_m16_128col_prepacked" if M <= 16 else "skinny_bf16_m32_128col_prepacked"
+    assert p.kernel == want and p.scratch_bytes == 0
     assert_close(_prepacked(inp), oracle.reference(inp), TOL_BF16, f"prepacked {M}x{N}x{K}")
 
 
@@ -112,7 +114,7 @@ def test_prepacked_matches_the_raw_layout_path():
     assert np.max(np.abs(raw - packed) / (1 + np.abs(raw))) <= TOL_BF16
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 128, 64), (16, 200, 64), (16, 128, 48)])
+@pytest.mark.parametrize("M,N,K", [(33, 128, 64), (16, 200, 64), (16, 128, 48)])
 def test_prepacked_plan_refuses_shapes_outside_the_layout(M, N, K):
     with pytest.raises(ge.GemmEpiError) as ei:
         ge.plan(ge.KIND_GENERIC, M, N, K, b_prepacked=True)
