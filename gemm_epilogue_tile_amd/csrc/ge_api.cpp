@@ -308,9 +308,9 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         if (pl.ldb < d.N / 2) return fail(GE_ERR_INVALID_ARG, "ldb < N/2 bytes");
         pl.ld_s = d.N;
         if (d.flags & GE_FLAG_W4_PREPACKED) {
-            if (d.N % (d.M <= 16 ? 16 : 128) || d.K % 128 || pl.group > 128 || (d.M > 16 && pl.group != 128))
+            if (d.N % (d.M <= 32 ? 16 : 128) || d.K % 128 || pl.group > 128 || (d.M > 32 && pl.group != 128))
                 return fail(GE_ERR_UNSUPPORTED,
-                            "prepacked int4 weights need K %% 128 == 0 and either M <= 16, N %% 16 == 0, group <= 128 "
+                            "prepacked int4 weights need K %% 128 == 0 and either M <= 32, N %% 16 == 0, group <= 128 "
                             "or N %% 128 == 0, group == 128");
         }
     }

@@ -470,12 +470,15 @@ __device__ __forceinline__ bf16x8 unpack_w4(uint32_t w) {
 constexpr int W4_WAVES = GE_W4_WAVES;
 constexpr int W4_THREADS = 64 * W4_WAVES;
 
-template <int NTW, int SPG>
+// MT 16-row tiles of X (M <= 16 MT) share each weight fragment; rounds shrink by MT so that the
+// activations in flight take the same registers.
+template <int NTW, int SPG, int MT>
 __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
     constexpr int NC = 16 * NTW;
-    constexpr int MR = 16;
+    constexpr int MR = 16 * MT;
     constexpr int NSG = 4 / SPG;               // scale groups per 128-row packing group
-    constexpr int RND = SPG == 1 ? (GE_W4_RND + 1) / 2 : GE_W4_RND;  // groups per round (32-row groups carry 4 scales each)
+    constexpr int RND0 = SPG == 1 ? (GE_W4_RND + 1) / 2 : GE_W4_RND;  // groups per round (32-row groups carry 4 scales each)
+    constexpr int RND = RND0 / MT > 0 ? RND0 / MT : 1;
     __shared__ __attribute__((aligned(16))) float red[W4_WAVES * MR * NC];
 
     const int lane = threadIdx.x & 63;
@@ -497,12 +500,14 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
     const uint32_t nz2 = nz | (nz << 16);
     const bf16x8 negz = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
 
-    f32x4 tot[NTW];
+    f32x4 tot[MT][NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) tot[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int base = g0; base < g1; base += RND) {
-        bf16x8 x[RND][4];
+        bf16x8 x[RND][MT][4];
         u32x4 w[RND][NTW];
         uint16_t sraw[RND][NTW][NSG];
 #pragma unroll
@@ -510,11 +515,13 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
             const int gi = base + j;
             const bool gin = gi < g1;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int k = gi * 128 + kb * 32 + 8 * g;
-                const uint32_t off = (uint32_t)(((int64_t)i * p.lda + k) * 2);
-                x[j][kb] = __builtin_bit_cast(bf16x8, bload16(rx, (i < p.M && gin) ? off : OOB));
-            }
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int k = gi * 128 + kb * 32 + 8 * g, m = 16 * mt + i;
+                    const uint32_t off = (uint32_t)(((int64_t)m * p.lda + k) * 2);
+                    x[j][mt][kb] = __builtin_bit_cast(bf16x8, bload16(rx, (m < p.M && gin) ? off : OOB));
+                }
 #pragma unroll
             for (int t = 0; t < NTW; ++t) {
                 const bool tin = gin && nt0 + t < ntiles;
@@ -530,30 +537,43 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
         for (int j = 0; j < RND; ++j) {
 #pragma unroll
             for (int sg = 0; sg < NSG; ++sg) {
-                f32x4 corr = f32x4{0.f, 0.f, 0.f, 0.f}, u[NTW];
+                f32x4 corr[MT], u[MT][NTW];
 #pragma unroll
-                for (int t = 0; t < NTW; ++t) u[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < MT; ++mt) {
+                    corr[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) u[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
                 for (int kb = sg * SPG; kb < (sg + 1) * SPG; ++kb) {
-                    corr = mfma_bf16(x[j][kb], negz, corr);
 #pragma unroll
-                    for (int t = 0; t < NTW; ++t) u[t] = mfma_bf16(x[j][kb], unpack_w4(w[j][t][kb]), u[t]);
+                    for (int mt = 0; mt < MT; ++mt) corr[mt] = mfma_bf16(x[j][mt][kb], negz, corr[mt]);
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) {
+                        const bf16x8 wf = unpack_w4(w[j][t][kb]);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) u[mt][t] = mfma_bf16(x[j][mt][kb], wf, u[mt][t]);
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
                     const float sv = bf16_to_f32(sraw[j][t][sg]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) tot[t][q] = fmaf(sv, u[t][q] + corr[q], tot[t][q]);
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) tot[mt][t][q] = fmaf(sv, u[mt][t][q] + corr[mt][q], tot[mt][t][q]);
                 }
             }
         }
     }
 
-    // partial tile -> LDS: lane (g, i) holds rows 4 g + e, column 16 t + i
+    // partial tile -> LDS: lane (g, i) holds rows 16 mt + 4 g + e, column 16 t + i
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) red[(wave * MR + 4 * g + e4) * NC + 16 * t + i] = tot[t][e4];
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) red[(wave * MR + 16 * mt + 4 * g + e4) * NC + 16 * t + i] = tot[mt][t][e4];
     __syncthreads();
     reduce_epilogue<MR, NC, W4_WAVES>(p, red, n0);
 }
@@ -883,7 +903,7 @@ bool skinny_supported(const Problem &p) {
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
     }
     if (p.mode == MODE_W4) {
-        return p.w4_packed && p.M <= 16 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
+        return p.w4_packed && p.M <= 32 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
                (p.group == 32 || p.group == 64 || p.group == 128) &&
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
     }
@@ -991,7 +1011,7 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
         const int s = w8_split(p, cu_count);
         return (p.w4_packed ? packed_names : names)[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
-    if (p.mode == MODE_W4) return "skinny_w4_m16_32col";
+    if (p.mode == MODE_W4) return p.M <= 16 ? "skinny_w4_m16_32col" : "skinny_w4_m32_32col";
     if (p.b_packed)
         return bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
                : p.M <= 16                    ? "skinny_bf16_m16_128col_prepacked"
@@ -1029,12 +1049,19 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
     if (p.mode == MODE_W4) {
         constexpr int NTW = 2;
         const int blocks = (p.N / 16 + NTW - 1) / NTW;
-        if (p.group == 32)
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 1>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
-        else if (p.group == 64)
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+        auto go = [&](auto MTC) {
+            constexpr int MT = decltype(MTC)::value;
+            if (p.group == 32)
+                hipLaunchKernelGGL((skinny_w4_kernel<NTW, 1, MT>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+            else if (p.group == 64)
+                hipLaunchKernelGGL((skinny_w4_kernel<NTW, 2, MT>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4, MT>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+        };
+        if (p.M <= 16)
+            go(std::integral_constant<int, 1>{});
         else
-            hipLaunchKernelGGL((skinny_w4_kernel<NTW, 4>), dim3(blocks), dim3(W4_THREADS), 0, s, p);
+            go(std::integral_constant<int, 2>{});
         return hipGetLastError();
     }
     if (p.mode == MODE_GENERIC && p.M <= 16 && p.split > 1 && p.split_ws && p.split_cnt) {

@@ -117,7 +117,7 @@ typedef int32_t ge_status;
  *            K % group == 0, N even, group in {32, 64, 128, 256},
  *            zero_point in [0, 15].
  *            With GE_FLAG_W4_PREPACKED additionally: K % 128 == 0, and
- *            either M <= 16, N % 16 == 0, group in {32, 64, 128}, or N % 128
+ *            either M <= 32, N % 16 == 0, group in {32, 64, 128}, or N % 128
  *            == 0, group == 128; the unfused entry points take raw weights
  *            and reject such plans.
  *            For M > 16 the product runs in fp16: x and the dequantised

@@ -433,10 +433,14 @@ def _w4_packed(inp, **kw):
                       zero_point=inp["zero_point"], prepacked=True, **kw)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (7, 256, 512), (16, 1008, 1024), (16, 4096, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (7, 256, 512), (16, 1008, 1024), (16, 4096, 2048),
+                                   (17, 1008, 1024), (25, 272, 512), (32, 4096, 2048)])
 def test_w4_prepacked_ragged(M, N, K):
+    # 17 <= M <= 32: two 16-row tiles of X per weight fragment
     w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
+    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel == \
+        ("skinny_w4_m16_32col" if M <= 16 else "skinny_w4_m32_32col")
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed {M}x{N}x{K}")
 
 
@@ -481,7 +485,7 @@ def test_w4_prepacked_rejected_by_unfused_chain():
                            torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV), prepacked=True)
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 128, 128), (128, 256, 512), (200, 384, 1024), (512, 512, 2048)])
+@pytest.mark.parametrize("M,N,K", [(33, 128, 128), (128, 256, 512), (200, 384, 1024), (512, 512, 2048)])
 def test_w4_prepacked_tile_path(M, N, K):
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
