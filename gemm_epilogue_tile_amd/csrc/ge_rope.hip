@@ -5,10 +5,10 @@
 // back to memory just before the product reads them).
 //
 // One 256-thread workgroup per (head, 128-query tile), walking the key tiles:
-//   1. the tiles are read from memory in 16-byte chunks, rotated in fp32
-//      (each product and each sum rounded to fp32, no contraction), rounded
-//      to bf16 (RNE) -- the values the unfused chain would have stored -- and
-//      written to LDS rows padded by 16 bytes, so that the MFMA fragment reads
+//   1. the tiles are read from memory in 16-byte chunks and rotated, each
+//      coordinate being the exact rotation rounded once to bf16 (RNE) -- the
+//      values the unfused chain would have stored -- and written to LDS rows
+//      padded by 16 bytes, so that the MFMA fragment reads
 //      of 16 rows hit 16 distinct bank groups;
 //   2. four waves (2 x 2, 64 x 64 each) run v_mfma_f32_16x16x32_bf16 over
 //      the head dimension, K' fragments as the first operand so that each
@@ -27,35 +27,122 @@ namespace {
 
 constexpr int RT = 128;  // query rows and key rows per tile
 
+// Rounding of a rotated coordinate.  The stored value is the exact rotation rounded once to bf16
+// (nearest, ties to even).  Fast path, in fp32: Kahan's difference of products, w = b t,
+// e = fma(b, t, -w) (exactly b t - w), f = fma(a, c, -+w), r = f -+ e, for x' = a c -+ b t.  Its error
+// is below 2 units in the last place of r (2^-23 |r|), so r rounds to the bf16 number the exact
+// value rounds to when r lies 4 or more of those units away from every point halfway between two
+// bf16 numbers (low 16 bits of r outside 0x7ffd .. 0x8003) and is neither tiny (|r| < 2^-100, where
+// underflow would void the bound) nor huge or not finite.  Other elements are redone by rot_exact.
+__device__ __forceinline__ bool rot_unsure(float r) {
+    const uint16_t lo = (uint16_t)__builtin_bit_cast(uint32_t, r);
+    const float m = __builtin_fabsf(r);
+    // 16-bit subtract and compare on the low half; !(m >= 2^-100 && m <= max) also catches NaN
+    return (uint16_t)(lo - (uint16_t)0x7ffd) <= (uint16_t)6 || !(m >= 0x1p-100f && m <= 0x1.fffffep127f);
+}
+
+__device__ __forceinline__ float rot_fast(float a, float c, float b, float t, bool neg, bool &slow) {
+    const float w = b * t;
+    const float e = __builtin_fmaf(b, t, -w);
+    const float r = neg ? __builtin_fmaf(a, c, -w) - e : __builtin_fmaf(a, c, w) + e;
+    slow |= rot_unsure(r);
+    return r;
+}
+
+// bf16 bits of a c -+ b t computed exactly: both products are exact in fp64 (8 and 24 significant
+// bits), their sum s is rounded once, and the TwoSum residual err (s + err is the exact value)
+// decides a tie that the fp64 rounding may have created.  The magnitude is scaled by a power of two
+// so that the bf16 spacing becomes 1 (2^-133 below 2^-126, the subnormal spacing).
+__device__ __noinline__ uint32_t rot_exact(float a, float c, float b, float t, bool neg) {
+    const double p = (double)a * (double)c;
+    const double q = neg ? -((double)b * (double)t) : (double)b * (double)t;
+    const double s = p + q;
+    const double bb = s - p;
+    const double err = (p - (s - bb)) + (q - bb);
+    const uint32_t sign = s < 0.0 ? 0x8000u : 0u;
+    if (s == 0.0) return (uint32_t)(__builtin_bit_cast(uint64_t, s) >> 48) & 0x8000u;
+    const double mag = __builtin_fabs(s);
+    int e2 = 0;
+    (void)__builtin_frexp(mag, &e2);  // 2^(e2 - 1) <= mag < 2^e2
+    const int sh = e2 - 8 > -133 ? e2 - 8 : -133;
+    const double v = __builtin_ldexp(mag, -sh);  // exact
+    const double fl = __builtin_floor(v);
+    const double frac = v - fl;                  // exact
+    bool up;
+    if (frac != 0.5)
+        up = frac > 0.5;
+    else if (err != 0.0)
+        up = (err > 0.0) == (s > 0.0);  // the exact magnitude lies above the halfway point
+    else
+        up = ((uint64_t)fl & 1u) != 0;  // exact tie: to even
+    const uint32_t f = (uint32_t)fl + (up ? 1u : 0u);
+    uint32_t mb = sh == -133 ? f : ((uint32_t)(e2 - 1 + 127) << 7) + (f - 128u);
+    if (mb > 0x7f80u) mb = 0x7f80u;  // beyond the largest bf16: infinity
+    return sign | mb;
+}
+
 // Rotate chunk c of one row from registers.  Rotate-half: x[0] = elements 8c .. 8c+7 of the first
 // half, x[1] the same elements of the second half (D/2 + 8c ..), c4 / s4 the 8 angles 8c .. 8c+7;
 // o0, o1 the rotated chunks.  Interleaved: x[0] = elements 8c .. 8c+7, i.e. the pairs 4c .. 4c+3
-// with the 4 angles in c4[0] / s4[0]; o0 the rotated chunk.  Each product and each sum is rounded
-// to fp32 (no contraction), the result to bf16 (RNE).
+// with the 4 angles in c4[0] / s4[0]; o0 the rotated chunk.  Every coordinate is the exact rotation
+// rounded once to bf16 (fast path above, flagged elements redone exactly).
 template <int D, bool INTER>
 __device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const f32x4 *s4, u32x4 &o0, u32x4 &o1) {
-#pragma clang fp contract(off)
+    // elements whose fast result is not certain (rare) are redone one by one, only in the lanes
+    // that hold them
+    auto fix = [](uint32_t o, int half, float r, float a, float c, float b, float t, bool neg) -> uint32_t {
+        if (rot_unsure(r)) {
+            const uint32_t v = rot_exact(a, c, b, t, neg);
+            o = half ? (o & 0xffffu) | (v << 16) : (o & 0xffff0000u) | v;
+        }
+        return o;
+    };
     if constexpr (INTER) {
+        bool slow = false;
+        float ya[4], yb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float a = bf16lo(x[0][j]), b = bf16hi(x[0][j]);
-            const float ya = a * c4[0][j] - b * s4[0][j];
-            const float yb = a * s4[0][j] + b * c4[0][j];
-            o0[j] = pack_bf16x2(ya, yb);
+            ya[j] = rot_fast(a, c4[0][j], b, s4[0][j], true, slow);
+            yb[j] = rot_fast(a, s4[0][j], b, c4[0][j], false, slow);
+            o0[j] = pack_bf16x2(ya[j], yb[j]);
+        }
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = bf16lo(x[0][j]), b = bf16hi(x[0][j]);
+                o0[j] = fix(o0[j], 0, ya[j], a, c4[0][j], b, s4[0][j], true);
+                o0[j] = fix(o0[j], 1, yb[j], a, s4[0][j], b, c4[0][j], false);
+            }
         }
     } else {
+        bool slow = false;
+        float ya[8], yb[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float c0 = c4[j >> 1][(2 * j) & 3], c1 = c4[j >> 1][(2 * j + 1) & 3];
             const float s0 = s4[j >> 1][(2 * j) & 3], s1 = s4[j >> 1][(2 * j + 1) & 3];
             const float a0 = bf16lo(x[0][j]), a1 = bf16hi(x[0][j]);  // first-half elements 8c + 2j, + 1
             const float b0 = bf16lo(x[1][j]), b1 = bf16hi(x[1][j]);  // their partners in the second half
-            const float ya0 = a0 * c0 - b0 * s0;
-            const float yb0 = a0 * s0 + b0 * c0;
-            const float ya1 = a1 * c1 - b1 * s1;
-            const float yb1 = a1 * s1 + b1 * c1;
-            o0[j] = pack_bf16x2(ya0, ya1);
-            o1[j] = pack_bf16x2(yb0, yb1);
+            ya[2 * j] = rot_fast(a0, c0, b0, s0, true, slow);
+            yb[2 * j] = rot_fast(a0, s0, b0, c0, false, slow);
+            ya[2 * j + 1] = rot_fast(a1, c1, b1, s1, true, slow);
+            yb[2 * j + 1] = rot_fast(a1, s1, b1, c1, false, slow);
+            o0[j] = pack_bf16x2(ya[2 * j], ya[2 * j + 1]);
+            o1[j] = pack_bf16x2(yb[2 * j], yb[2 * j + 1]);
+        }
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float c0 = c4[j >> 1][(2 * j) & 3], c1 = c4[j >> 1][(2 * j + 1) & 3];
+                const float s0 = s4[j >> 1][(2 * j) & 3], s1 = s4[j >> 1][(2 * j + 1) & 3];
+                const float a0 = bf16lo(x[0][j]), a1 = bf16hi(x[0][j]);
+                const float b0 = bf16lo(x[1][j]), b1 = bf16hi(x[1][j]);
+                o0[j] = fix(o0[j], 0, ya[2 * j], a0, c0, b0, s0, true);
+                o0[j] = fix(o0[j], 1, ya[2 * j + 1], a1, c1, b1, s1, true);
+                o1[j] = fix(o1[j], 0, yb[2 * j], a0, s0, b0, c0, false);
+                o1[j] = fix(o1[j], 1, yb[2 * j + 1], a1, s1, b1, c1, false);
+            }
         }
     }
 }

@@ -165,8 +165,10 @@ GE_API void ge_desc_init(ge_desc *d);
  * one K piece of one column block per CU (stream-K: the same tiles and
  * counters, S = pieces per block in {2..8}; e.g. 16 x 8192 x 8192 on 256
  * CUs, S = 4); and prepacked int4 plans with M > 16 (the fp16 copy of X,
- * M * K * 2 bytes).  Such a call synchronises the device, so make plans
- * outside graph capture.
+ * M * K * 2 bytes).  Such a call waits for the zeroing of its scratch on a
+ * stream of the library's own (the callers' streams keep running); device
+ * allocation is not allowed during graph capture, so make such plans before
+ * capturing (the call fails with GE_ERR_HIP and says so otherwise).
  * Errors: INVALID_ARG (bad descriptor or null out), UNSUPPORTED, NO_DEVICE.
  */
 GE_API ge_status gemm_epi_plan(const ge_desc *d, int32_t kind, ge_plan **out);
@@ -255,8 +257,8 @@ GE_API ge_status gemm_b_prepack(const ge_plan *plan, const void *B, void *Bp, vo
  * aligned, covering every position used; S [batch, Sq, Sk] of s_type (GE_F32
  * or GE_BF16), dense, not overlapping Q or K.  Pair i of a row is (i, i + D/2)
  * (rotate-half, the Llama layout), or (2i, 2i + 1) when interleaved != 0:
- * x'_a = x_a cos - x_b sin, x'_b = x_a sin + x_b cos, each product and sum
- * rounded to fp32 and x' rounded to bf16 (RNE), the values the unfused chain
+ * x'_a = x_a cos - x_b sin, x'_b = x_a sin + x_b cos, each x' being the exact
+ * rotated value rounded once to bf16 (RNE), the values the unfused chain
  * stores; the product is bf16 x bf16 with fp32 accumulation, alpha applied in
  * fp32, one rounding to s_type.  cos == sin == NULL: no rotation (the plain
  * product, the unfused chain's last step).  D in {64, 128}, batch <= 65535.

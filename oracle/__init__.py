@@ -290,10 +290,58 @@ def _bf16_to_f32(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _f32_to_bf16_rne(x) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest, ties to even (finite values)."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+def round_bf16(y) -> np.ndarray:
+    """float64 values -> bf16 bit patterns, round to nearest, ties to even (the storage step of a
+    bf16 result).  The value is scaled by a power of two so that the bf16 grid becomes the integers
+    (steps of 2^(e - 8) for |y| in [2^(e - 1), 2^e), 2^-133 below 2^-126, the subnormal spacing),
+    rounded with numpy's rint (half to even), and scaled back: every step is exact in float64.
+    Magnitudes beyond the largest bf16 become infinities."""
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(y)):
+        raise ValueError("round_bf16 takes finite values")
+    _, e = np.frexp(y)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(y / step) * step
+    with np.errstate(over="ignore"):
+        f = r.astype(np.float32)  # exact: r lies on the bf16 grid (or overflows to inf)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _round_sum_bf16(p, q) -> np.ndarray:
+    """bf16 bits of the exact value p + q (p, q float64 arrays holding exact products), rounded to
+    nearest, ties to even.  The float64 sum is exact or within 2^-53 of p + q; where that rounding
+    could decide the bf16 rounding (the sum lies within 2^-40 of a bf16 rounding point, in units of
+    the bf16 spacing), the element is recomputed with exact rational arithmetic."""
+    from fractions import Fraction
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    y = p + q
+    bits = round_bf16(y)
+    _, e = np.frexp(y)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    t = np.abs(y) / step
+    near = np.abs(t - np.floor(t) - 0.5) <= 2.0 ** -40
+    for idx in zip(*np.nonzero(near)):
+        exact = Fraction(float(p[idx])) + Fraction(float(q[idx]))
+        sgn = -1 if exact < 0 else 1
+        mag = abs(exact)
+        if mag == 0:
+            bits[idx] = 0
+            continue
+        # exponent of the exact value: 2^(ex - 1) <= mag < 2^ex
+        ex = mag.numerator.bit_length() - mag.denominator.bit_length()
+        while Fraction(2) ** ex <= mag:
+            ex += 1
+        while Fraction(2) ** (ex - 1) > mag:
+            ex -= 1
+        stp = Fraction(2) ** max(ex - 8, -133)
+        n = mag / stp
+        fl = n.numerator // n.denominator
+        rem = n - fl
+        up = rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1)
+        val = float((fl + up) * stp) * sgn
+        bits[idx] = round_bf16(np.array([val]))[0]
+    return bits
 
 
 def rope(X, cos, sin, pos0: int = 0, interleaved: bool = False) -> np.ndarray:
@@ -302,30 +350,30 @@ def rope(X, cos, sin, pos0: int = 0, interleaved: bool = False) -> np.ndarray:
 
     cos, sin: float32 [P, D/2], row p holding cos(p theta_i), sin(p theta_i).  Pair i of a row is
     (i, i + D/2) (rotate-half, the Llama layout) or (2i, 2i + 1) (``interleaved``), rotated by the
-    angle of its position:  x'_a = x_a cos - x_b sin,  x'_b = x_a sin + x_b cos.  Each product and
-    each sum is rounded to float32 (the precision the rotated operand is formed in), and the result
-    is stored as bf16 (RNE), as the unfused chain writes q' and k' before the product.
-    Returns bf16 bit patterns of X's shape."""
-    x = _bf16_to_f32(X)
+    angle of its position:  x'_a = x_a cos - x_b sin,  x'_b = x_a sin + x_b cos.  The plain
+    definition: the exact rotated value (each product of a bf16 and a float32 number is exact in
+    float64), stored as bf16 with one rounding to nearest, ties to even, as the unfused chain
+    writes q' and k' before the product.  Returns bf16 bit patterns of X's shape."""
+    x = _bf16_to_f32(X).astype(np.float64)
     S, D = x.shape[-2], x.shape[-1]
     if D % 2:
         raise ValueError("D must be even")
-    c = np.asarray(cos, dtype=np.float32)[pos0:pos0 + S]
-    s = np.asarray(sin, dtype=np.float32)[pos0:pos0 + S]
+    c = np.asarray(cos, dtype=np.float32)[pos0:pos0 + S].astype(np.float64)
+    s = np.asarray(sin, dtype=np.float32)[pos0:pos0 + S].astype(np.float64)
     if c.shape != (S, D // 2) or s.shape != (S, D // 2):
         raise ValueError("cos / sin tables do not cover the positions")
     if interleaved:
         a, b = x[..., 0::2], x[..., 1::2]
     else:
         a, b = x[..., :D // 2], x[..., D // 2:]
-    ya = np.subtract(np.multiply(a, c, dtype=np.float32), np.multiply(b, s, dtype=np.float32), dtype=np.float32)
-    yb = np.add(np.multiply(a, s, dtype=np.float32), np.multiply(b, c, dtype=np.float32), dtype=np.float32)
-    y = np.empty_like(x)
+    ya = _round_sum_bf16(a * c, -(b * s))
+    yb = _round_sum_bf16(a * s, b * c)
+    y = np.empty(x.shape, dtype=np.uint16)
     if interleaved:
         y[..., 0::2], y[..., 1::2] = ya, yb
     else:
         y[..., :D // 2], y[..., D // 2:] = ya, yb
-    return _f32_to_bf16_rne(y)
+    return y
 
 
 def rope_qk(Q, K, cos, sin, *, q_pos0: int = 0, k_pos0: int = 0, alpha: float = 1.0,

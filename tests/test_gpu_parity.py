@@ -350,6 +350,26 @@ def test_add_rmsnorm(M, N):
     assert_close(out, ro, TOL_BF16, "normed")
 
 
+@pytest.mark.parametrize("N", [4096, 1000, 8192])  # one wave per row; a workgroup per row (unaligned, long)
+@pytest.mark.parametrize("scale,eps", [(1e-3, 1e-6), (1.0, 4.0)])
+def test_add_rmsnorm_eps_changes_the_result(N, scale, eps):
+    # mean(r^2) of the same order as eps, so eps moves rrms by 18-60% and its placement (inside
+    # the root, added to the mean) is visible at the bf16 tolerance; row 0 is all zeros (finite
+    # only through eps)
+    M = 6
+    a = workloads.normal((M, N), scale, "bf16", wid=102, tid=0, seed=N)
+    x = workloads.normal((M, N), scale, "bf16", wid=102, tid=1, seed=N)
+    a[0] = 0
+    x[0] = 0
+    wt = workloads.normal((N,), 1.0, "bf16", wid=102, tid=2, seed=N)
+    resid, out = ge.add_rmsnorm(to_dev(a), to_dev(x), to_dev(wt), eps=eps)
+    rr, ro = oracle.add_rmsnorm(a, x, wt, "bf16", eps=eps)
+    _, ro_no_eps = oracle.add_rmsnorm(a[1:], x[1:], wt, "bf16", eps=0.0)
+    assert np.max(np.abs(ro[1:] - ro_no_eps) / (1 + np.abs(ro_no_eps))) > 0.1  # eps is not negligible here
+    assert_close(resid, rr, TOL_BF16, "resid")
+    assert_close(out, ro, TOL_BF16, f"normed eps={eps}")
+
+
 def test_add_rmsnorm_in_place_residual():
     M, N = 8, 2048
     a = workloads.normal((M, N), 1.0, "bf16", wid=101, tid=0)

@@ -39,6 +39,58 @@ def test_rotation_alone_is_bit_exact(D, interleaved):
     assert np.array_equal(got, oracle.rope(inp["Q"], cos, sin, 41, interleaved))
 
 
+def _tie_cases():
+    """(a, b, cos, sin) quadruples whose rotated values sit on, next to or far from points halfway
+    between two bf16 numbers, cancel, overflow, are subnormal or signed zeros."""
+    t = 2.0 ** -40
+    m = 1 + 2 ** -8  # halfway between 1 and 1 + 2^-7
+    cases = [(1.0, t, t, m), (1.0, t, m, t), (1.0, 0.0, m, 0.0), (1.0, 0.0, 1 + 3 * 2 ** -8, 0.0),
+             (1.0, 2.0 ** -30, m, 2.0 ** -30), (-1.0, t, m, -t), (3.0, 1.0, 1.0, 3.0), (1.5, 1.5, 0.5, 0.5),
+             (3.0e38, 3.0e38, 1.0, 0.5), (3.3e38, 1.0e38, 1.0, 0.1), (2.0 ** -130, 2.0 ** -131, 0.7, 0.3),
+             (2.0 ** -120, 2.0 ** -121, 0.7, 0.3), (-0.0, 0.0, 0.5, 0.5), (0.0, -0.0, 1.0, 0.0),
+             (1.0, 1.0, 0.70710677, 0.70710677), (2.0, 3.0, 0.6, 0.8)]
+    rng = np.random.default_rng(7)
+    while len(cases) < 64:
+        # products within 2^-20 of each other: heavy cancellation
+        a = float(workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(np.array([rng.normal()], np.float32)))[0])
+        c = float(np.float32(rng.uniform(0.1, 1)))
+        b = a
+        s_ = float(np.float32(c * (1 + rng.uniform(-2 ** -20, 2 ** -20))))
+        cases.append((a, b, c, s_))
+    return cases
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rotation_of_ties_overflow_subnormals_bit_exact(interleaved):
+    # 64 pairs, one per row (position), each with its own table entry: the kernel's fast fp32 path
+    # must flag every element it cannot round with certainty and redo it exactly
+    D = 128
+    cases = _tie_cases()
+    S = len(cases)
+    x = np.zeros((S, D), np.float32)
+    cos = np.full((S, D // 2), 0.5, np.float32)
+    sin = np.full((S, D // 2), 0.25, np.float32)
+    for r, (a, b, c, s_) in enumerate(cases):
+        for i in range(D // 2):  # every pair of the row carries the case, in a different pair slot too
+            ia, ib = (2 * i, 2 * i + 1) if interleaved else (i, i + D // 2)
+            x[r, ia], x[r, ib] = (a, b) if i % 2 == 0 else (b, a)
+            cos[r, i], sin[r, i] = (c, s_) if i % 3 else (s_, c)
+    X = workloads.f32_to_bf16_bits(x)[None]
+    Xd = to_dev(X)
+    got = _bits(ge.rope(Xd, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), interleaved=interleaved))
+    want = oracle.rope(X, cos, sin, 0, interleaved)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} mismatches, first at {tuple(b[0] for b in bad)}: gpu {got[bad][0]:#06x} oracle {want[bad][0]:#06x}"
+    # the fused scores kernel rotates the same way
+    ref_q = torch.from_numpy(want.view(np.int16)).to(DEV).view(torch.bfloat16)
+    fused = ge.rope_qk(Xd[:, :, :], Xd, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), alpha=1.0,
+                       interleaved=interleaved)
+    plain = ge.rope_qk(ref_q, ref_q, alpha=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(fused, posinf=1, neginf=-1).view(torch.int32),
+                       torch.nan_to_num(plain, posinf=1, neginf=-1).view(torch.int32))
+
+
 @pytest.mark.parametrize("H,Sq,Sk,D", [(1, 1, 1, 64), (2, 128, 128, 128), (3, 77, 200, 128), (2, 300, 131, 64),
                                        (4, 1, 517, 128), (8, 129, 140, 64), (8, 384, 257, 128)])
 @pytest.mark.parametrize("interleaved", [False, True])

@@ -273,6 +273,37 @@ def test_add_rmsnorm_constant_rows():
     assert np.array_equal(out, np.tile(w.astype(np.float64), (M, 1)))
 
 
+def test_add_rmsnorm_eps_inside_the_root():
+    # Pattern 1 of "Fusion Thinking": rrms = 1 / sqrt(mean(r^2) + eps).  r = 2 everywhere and
+    # eps = 12 give 1 / sqrt(4 + 12) = 1/4, so out = r / 4 * w = w / 2 exactly.  eps outside the
+    # root (1/2 + 12), eps dropped (1/2) or eps added to the sum instead of the mean
+    # (1 / sqrt((4 N + 12) / N)) all give another value.
+    M, N = 2, 10
+    a = np.full((M, N), 1.25, np.float32)
+    x = np.full((M, N), 0.75, np.float32)
+    w = np.linspace(-2, 2, N).astype(np.float32)
+    _, out = oracle.add_rmsnorm(a, x, w, "f32", eps=12.0)
+    assert np.array_equal(out, np.tile(w.astype(np.float64) / 2, (M, 1)))
+    # r = 1 and eps = 3: rrms = 1 / sqrt(1 + 3) = 1/2
+    one = np.full((1, N), 0.5, np.float32)
+    _, out = oracle.add_rmsnorm(one, one, w, "f32", eps=3.0)
+    assert np.array_equal(out[0], w.astype(np.float64) / 2)
+
+
+def test_add_rmsnorm_zero_row_is_finite_with_eps():
+    # a row of zeros: mean(r^2) = 0, so eps alone keeps the root nonzero: rrms = 1 / sqrt(1/4) = 2
+    # and out = 0 * 2 * w = 0 (a dropped eps would give 0 * inf = nan)
+    N = 16
+    z = np.zeros((3, N), np.float32)
+    w = np.linspace(1, 2, N).astype(np.float32)
+    resid, out = oracle.add_rmsnorm(z, z, w, "f32", eps=0.25)
+    assert np.array_equal(resid, np.zeros((3, N)))
+    assert np.array_equal(out, np.zeros((3, N)))
+    # eps = 0 on the same row has no finite answer
+    _, bad = oracle.add_rmsnorm(z, z, w, "f32", eps=0.0)
+    assert not np.any(np.isfinite(bad))
+
+
 def test_add_rmsnorm_unit_rms_after_normalisation():
     a = workloads.normal((4, 256), 1.0, "f32", wid=96, tid=0)
     x = workloads.normal((4, 256), 1.0, "f32", wid=96, tid=1)
@@ -404,8 +435,8 @@ def test_rope_with_zero_angles_is_the_identity(interleaved):
 
 
 def test_rope_is_multiplication_by_a_unit_complex_number():
-    # independent definition: (x_a + i x_b) * exp(i p theta_k), in complex128, against the oracle's
-    # fp32 evaluation stored as bf16 (within bf16 rounding of each component)
+    # independent definition: (x_a + i x_b) * exp(i p theta_k), in complex128; the stored result is
+    # within half a bf16 spacing of it (one rounding to nearest)
     D, S, pos0 = 64, 9, 5
     X = workloads.normal((S, D), 1.0, "bf16", wid=92, tid=0)
     cos, sin = workloads.rope_tables(pos0 + S, D, 10000.0)
@@ -413,11 +444,71 @@ def test_rope_is_multiplication_by_a_unit_complex_number():
     z = (x[:, :D // 2] + 1j * x[:, D // 2:]) * (cos[pos0:].astype(np.float64) + 1j * sin[pos0:].astype(np.float64))
     want = np.concatenate([z.real, z.imag], axis=1)
     got = _f(oracle.rope(X, cos, sin, pos0))
-    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
+    half_ulp = np.ldexp(1.0, np.floor(np.log2(np.abs(want))).astype(int) - 8)
+    assert np.all(np.abs(got - want) <= half_ulp * (1 + 1e-9))
     # a rotation keeps each pair's length
     n0 = x[:, :D // 2] ** 2 + x[:, D // 2:] ** 2
     n1 = got[:, :D // 2] ** 2 + got[:, D // 2:] ** 2
     assert np.allclose(n1, n0, rtol=2.0 ** -6, atol=1e-6)
+
+
+def _bf16_nearest_exact(v):
+    """bf16 bits of the Fraction v rounded to nearest, ties to even, by comparing exact distances
+    to the two bf16 neighbours (brute force; finite normal values)."""
+    from fractions import Fraction
+    if v == 0:
+        return 0
+    t = np.array([float(v)], np.float32).view(np.uint32)[0] >> 16  # a bf16 pattern within 2 steps of v
+    cands = [int(t) + d for d in range(-2, 3)]
+    vals = [Fraction(float(workloads.bf16_bits_to_f32(np.array([c], np.uint16))[0])) for c in cands]
+    dist = [abs(x - v) for x in vals]
+    best = min(dist)
+    ties = [c for c, d in zip(cands, dist) if d == best]
+    return min(ties, key=lambda c: c & 1)  # even mantissa wins a tie
+
+
+def _rope_exact(X, cos, sin, pos0=0):
+    """Rotate-half RoPE with exact rational arithmetic, element by element (tiny inputs only)."""
+    from fractions import Fraction
+    x = _f(X)
+    S, D = x.shape
+    out = np.empty((S, D), np.uint16)
+    for r in range(S):
+        for i in range(D // 2):
+            a, b = Fraction(float(x[r, i])), Fraction(float(x[r, i + D // 2]))
+            c, s = Fraction(float(cos[pos0 + r, i])), Fraction(float(sin[pos0 + r, i]))
+            out[r, i] = _bf16_nearest_exact(a * c - b * s)
+            out[r, i + D // 2] = _bf16_nearest_exact(a * s + b * c)
+    return out
+
+
+def test_rope_equals_exact_rational_rotation_rounded_once():
+    D, S, pos0 = 16, 6, 3
+    X = workloads.normal((S, D), 1.0, "bf16", wid=94, tid=0)
+    cos, sin = workloads.rope_tables(pos0 + S, D, 10000.0)
+    assert np.array_equal(oracle.rope(X, cos, sin, pos0), _rope_exact(X, cos, sin, pos0))
+
+
+def test_rope_ties_and_near_ties_round_on_the_exact_value():
+    # one row, D = 8 (pairs (i, i + 4)); each pair is built so that its exact rotated value sits on
+    # or next to a point halfway between two bf16 numbers:
+    #   pair 0: yb = 1 * (1 + 2^-8) + 2^-40 * 2^-40: just above the midpoint of 1 and 1 + 2^-7 ->
+    #           rounds up (float64 alone would round the sum onto the midpoint, then to even = 1)
+    #   pair 0: ya = 1 * 2^-40 - 2^-40 * (1 + 2^-8) ... small, exact in float64
+    #   pair 1: ya = 1 * (1 + 2^-8) - 2^-40 * 2^-40: just below that midpoint -> 1
+    #   pair 2: ya = 1 * (1 + 2^-8) - 0: exactly the midpoint -> ties to even -> 1
+    #   pair 3: ya = 1 * (1 + 3 * 2^-8) - 0: exactly a midpoint -> to even -> 1 + 2^-6
+    t = 2.0 ** -40
+    xa = np.array([1.0, 1.0, 1.0, 1.0], np.float32)
+    xb = np.array([t, t, 0.0, 0.0], np.float32)
+    cos = np.array([[t, 1 + 2 ** -8, 1 + 2 ** -8, 1 + 3 * 2 ** -8]], np.float32)
+    sin = np.array([[1 + 2 ** -8, t, 0.0, 0.0]], np.float32)
+    X = _b([np.concatenate([xa, xb])])
+    got = _f(oracle.rope(X, cos, sin))[0]
+    assert got[4] == 1 + 2 ** -7          # pair 0, yb
+    assert got[1] == 1.0                  # pair 1, ya
+    assert got[2] == 1.0 and got[3] == 1 + 2 ** -6
+    assert np.array_equal(oracle.rope(X, cos, sin), _rope_exact(X, cos, sin))
 
 
 def test_rope_interleaved_is_rotate_half_with_columns_permuted():
