@@ -1,18 +1,28 @@
 """A decode chain of fused calls captured in a HIP graph and replayed (the
 runs allocate nothing and do not synchronise, so they are capture-safe).
 
-Every replay is checked against the eager result of the same inputs, with
-eager work and synchronisations between replays, and the inputs change
-between replays (the graph must read the current contents)."""
+Every replay is checked against the oracle on the replay's own inputs (the
+bf16 or fp32 tolerance) and bitwise against the eager result of the same
+inputs, with eager work and synchronisations between replays; the inputs
+change between replays (the graph must read the current contents)."""
 import numpy as np
 import pytest
 import torch
 
 import gemm_epilogue_tile_amd as ge
+import oracle
 import workloads
-from gpu_helpers import DEV
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close
 
 pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    """host copy of a tensor: bf16 as uint16 bit patterns, other types as they are"""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
 
 
 def _chain_inputs(seed):
@@ -50,6 +60,7 @@ def test_decode_chain_graph_replays_match_eager():
     with torch.cuda.graph(g):
         for f in graph_calls:
             f.with_stream()()
+    W1n, b1n, R1n, Wqn, scn, W3n = (_np(t) for t in (W1, b1, R1, Wq, sc, W3))
     for rep in range(4):
         x.copy_(_chain_inputs(100 + rep)[0])   # new activations each step
         for f in eager:
@@ -59,7 +70,12 @@ def test_decode_chain_graph_replays_match_eager():
         torch.cuda.synchronize()
         for be, bg in zip(bufs_e, bufs_g):
             assert torch.equal(be, bg), f"replay {rep} differs from the eager chain"
-        assert torch.isfinite(bufs_g[2].float()).all()
+        # the oracle chain from the replay's inputs, each stage stored as bf16 like the chain's buffers
+        h = oracle.gemm_epilogue(_np(x), W1n, "bf16", bias=b1n, act="gelu_tanh", R=R1n)
+        y = oracle.w4_gemm(oracle.round_bf16(h), Wqn, scn, N2, "bf16")
+        z = oracle.gemm_epilogue(oracle.round_bf16(y), W3n, "bf16", act="silu")
+        for got, ref, name in zip(bufs_g, (h, y, z), ("h", "y", "z")):
+            assert_close(got, ref, TOL_BF16, f"replay {rep}: {name}")
 
 
 def _scratch_inputs(seed):
@@ -78,7 +94,8 @@ def test_scratch_using_calls_replay_in_a_graph():
     x8, x4, xs = _scratch_inputs(2)
     Wq8 = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
     s8 = torch.full((32, 4096), 0.001).bfloat16().to(DEV)
-    Wp4 = ge.w4_prepack(torch.randint(0, 256, (1024, 512), generator=g, dtype=torch.uint8).to(DEV))
+    Wq4 = torch.randint(0, 256, (1024, 512), generator=g, dtype=torch.uint8).to(DEV)
+    Wp4 = ge.w4_prepack(Wq4)
     s4 = torch.full((8, 1024), 0.01).bfloat16().to(DEV)
     Wg = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
     Wu = (torch.randn(256, 136 * 128, generator=g) / 16).bfloat16().to(DEV)
@@ -113,6 +130,7 @@ def test_scratch_using_calls_replay_in_a_graph():
     with torch.cuda.graph(graph):
         for f in graph_calls:
             f.with_stream()()
+    Wq4n = _np(Wq4)
     for rep in range(4):
         for dst, src in zip((x8, x4, xs), _scratch_inputs(200 + rep)):
             dst.copy_(src)
@@ -123,7 +141,12 @@ def test_scratch_using_calls_replay_in_a_graph():
         torch.cuda.synchronize()
         for be, bg in zip(oe, og):
             assert torch.equal(be, bg), f"replay {rep} differs from the eager calls"
-        assert all(torch.isfinite(t.float()).all() for t in og)
+        refs = [oracle.w8_gemm(_np(x8), _np(Wq8), _np(s8), "u8", "bf16", group=128, zero_point=128),
+                oracle.w4_gemm(_np(x4), Wq4n, _np(s4), 1024, "bf16"),
+                oracle.swiglu(_np(xs), _np(Wg), _np(Wu), "bf16"),
+                oracle.gemm_epilogue(_np(xd), _np(Wd), "bf16", bias=_np(bd))]
+        for got, ref, name in zip(og, refs, ("u8 split", "int4 tile", "swiglu", "stream-k")):
+            assert_close(got, ref, TOL_BF16, f"replay {rep}: {name}")
 
 
 def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
@@ -140,9 +163,10 @@ def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
                                                torch.randn(2, 384, 128, generator=h))]
 
     xs, xp, x8, Q, K = acts(3)
-    Ws = ge.b_prepack((torch.randn(1024, 8192, generator=g) / 32).bfloat16().to(DEV))
-    Wp = ge.b_prepack((torch.randn(256, 16512, generator=g) / 16).bfloat16().to(DEV))
-    Wq8 = ge.w4_prepack(torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV), fmt="u8")
+    Wsr = (torch.randn(1024, 8192, generator=g) / 32).bfloat16().to(DEV)
+    Wpr = (torch.randn(256, 16512, generator=g) / 16).bfloat16().to(DEV)
+    Wq8r = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
+    Ws, Wp, Wq8 = ge.b_prepack(Wsr), ge.b_prepack(Wpr), ge.w4_prepack(Wq8r, fmt="u8")
     s8 = torch.full((32, 4096), 0.001).bfloat16().to(DEV)
     cos, sin = (torch.from_numpy(t).to(DEV) for t in workloads.rope_tables(384, 128, 500000.0))
 
@@ -170,6 +194,7 @@ def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
     with torch.cuda.graph(graph):
         for f in graph_calls:
             f.with_stream()()
+    cosn, sinn = cos.cpu().numpy(), sin.cpu().numpy()
     for rep in range(4):
         for dst, src in zip((xs, xp, x8, Q, K), acts(300 + rep)):
             dst.copy_(src)
@@ -180,4 +205,10 @@ def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
         torch.cuda.synchronize()
         for be, bg in zip(oe, og):
             assert torch.equal(be, bg), f"replay {rep} differs from the eager calls"
-        assert all(torch.isfinite(t.float()).all() for t in og)
+        refs = [oracle.gemm_epilogue(_np(xs), _np(Wsr), "bf16"),
+                oracle.gemm_epilogue(_np(xp), _np(Wpr), "bf16"),
+                oracle.w8_gemm(_np(x8), _np(Wq8r), _np(s8), "u8", "bf16", group=128, zero_point=128)]
+        for got, ref, name in zip(og[:3], refs, ("bf16 stream-k", "bf16 prepacked", "u8 prepacked")):
+            assert_close(got, ref, TOL_BF16, f"replay {rep}: {name}")
+        sref = oracle.rope_qk(_np(Q), _np(K), cosn, sinn, q_pos0=128, alpha=0.125)
+        assert_close(og[3], sref, TOL_F32, f"replay {rep}: rope scores")
