@@ -7,10 +7,11 @@ bf16 output).  W untimed warmup steps, then exactly K timed steps, back to
 back, between two HIP events on the launch stream and bracketed by device
 synchronisation; the region divided by K is the kernel's average duration for
 the roofline object (a kernel trace of the same command shows no gap between
-the launches).  The default warmup is long because the shader clock of a GPU
-that has just come out of idle settles over the first few hundred launches
-(at 4096^3: about 120 us per launch for the first hundred, 102 us from the
-third hundred on).
+the launches).  The headline is timed last, right after the other rows: the
+shader clock of a GPU that has just come out of idle settles over the first
+tens of milliseconds of work (at 4096^3: about 120 us per launch for the
+first hundred launches, 102 us from the third hundred on), and the other rows
+are that much work.
 
 Also reported (same JSON line): the deliberately unfused chain of the same
 workload, the other workloads (tiny fp32, SwiGLU dual GEMM, 16-row decode
@@ -194,19 +195,24 @@ def build_calls(name, w, inp):
     return fused, unfused, dict(acc, kernel=kernel, rotations=nrot)
 
 
-def measure(name, steps, warmup, unfused_chain=True):
+def prepare(name):
+    """Inputs of one workload resident on the device and its calls prepared (nothing timed)."""
     import workloads
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     fused, unfused, meta = build_calls(name, w, inp)
+    return w, fused, unfused, meta
+
+
+def measure(name, steps, warmup, unfused_chain=True, prepared=None):
+    w, fused, unfused, meta = prepared if prepared is not None else prepare(name)
     fused_ms = time_launches(fused, steps, warmup) / steps
     if not unfused_chain:
         return dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
                     flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"], ms_per_call=fused_ms,
                     gbps=meta["bytes"] / (fused_ms * 1e-3) / 1e9, tflops=meta["flops"] / (fused_ms * 1e-3) / 1e12)
     unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
-    # calls run back to back, so the per-call average is each call's GPU duration (one kernel for
-    # every fused call except int4 at M > 16, which is the activation pre-pass plus the tile kernel)
+    # calls run back to back, so the per-call average is each call's GPU duration
     kern_ms = fused_ms
     r = dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
              flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"],
@@ -395,14 +401,31 @@ def main():
             torch.cuda.empty_cache()
         return
 
-    main_r = measure("square_bf16", a.steps, a.warmup)
-    others = {}
+    # The headline's inputs and calls are set up first; the other rows are measured next and the
+    # headline last, right after them, so that it is timed at the clock the GPU sustains under load
+    # rather than on a GPU that has just come out of idle (the first tens of milliseconds of
+    # launches run up to a quarter slower).
+    head = prepare("square_bf16")
+    others, nxt = {}, {}
     if not a.main_only:
+        # steps and warmups of the other rows: at least 50 each (they are short calls)
+        ks, ws = max(a.steps // 2, 50), max(a.warmup // 2, 50)
         for name in ["tiny_fp32", "swiglu_8b", "skinny_decode", "w4a16_m16", "w4a16_m512"]:
-            r = measure(name, max(a.steps // 2, 10), max(a.warmup // 2, 3))
+            r = measure(name, ks, ws)
             torch.cuda.empty_cache()
             others[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                             if k not in ("name",)}
+        # a measured step beyond the fused GEMM: residual add + RMSNorm, fused in one kernel
+        nxt["add_rmsnorm_2048x4096"] = measure_add_rmsnorm(ks, ws)
+        # rotary embedding applied at Q / K tile load, the attention scores product as its consumer
+        nxt["rope_qk_prefill"] = measure_rope_qk(ks, ws)
+        torch.cuda.empty_cache()
+        # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
+        for name in ["w8a16_u8_m16", "w8a16_fp8_m16"]:
+            r = measure(name, ks, ws)
+            torch.cuda.empty_cache()
+            nxt[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
+    main_r = measure("square_bf16", a.steps, a.warmup, prepared=head)
 
     achieved = main_r["tflops"]
     traffic = traffic_for(main_r["kernel"])
@@ -434,16 +457,6 @@ def main():
     }
     if others:
         line["workloads"] = others
-        # a measured step beyond the fused GEMM: residual add + RMSNorm, fused in one kernel
-        nxt = {"add_rmsnorm_2048x4096": measure_add_rmsnorm(max(a.steps // 2, 10), max(a.warmup // 2, 3))}
-        # rotary embedding applied at Q / K tile load, the attention scores product as its consumer
-        nxt["rope_qk_prefill"] = measure_rope_qk(max(a.steps // 2, 10), max(a.warmup // 2, 3))
-        torch.cuda.empty_cache()
-        # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
-        for name in ["w8a16_u8_m16", "w8a16_fp8_m16"]:
-            r = measure(name, max(a.steps // 2, 10), max(a.warmup // 2, 3))
-            torch.cuda.empty_cache()
-            nxt[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
         line["next"] = nxt
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.cpu_rows)

@@ -10,6 +10,7 @@ fallback path.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 import threading
@@ -228,22 +229,38 @@ class Prepared:
     def with_stream(self, stream=None) -> "Prepared":
         """The same call bound to another stream (default: the current one), e.g.
         the capture stream inside ``torch.cuda.graph``.  The runs allocate nothing
-        and never synchronise, so they can be captured into a HIP graph."""
+        and never synchronise, so they can be captured into a HIP graph.  The call
+        keeps its plan: when that plan owns device scratch, the two bindings must
+        not run at the same time (prepare the call again with ``stream=`` for that)."""
         return Prepared(self._fn, self._where, self._plan, self._tensors, self._args[:-1] + (_stream(stream),))
 
 
-_plan_cache: dict = {}
+# Plans by descriptor (and device).  A plan that owns device scratch serves one stream at a time,
+# so such plans are cached per stream as well; the cache keeps the most recently used plans only.
+_plan_cache: "collections.OrderedDict" = collections.OrderedDict()
+_PLAN_CACHE_MAX = 256
+_cache_lock = threading.Lock()
+
+
+def _stream_key(stream) -> int:
+    if stream is None:
+        return int(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
 
 
 def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=BF16, c_type=None,
          bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
          alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
-         lo_first=False, prepacked=False, b_prepacked=False) -> Plan:
+         lo_first=False, prepacked=False, b_prepacked=False, stream=None) -> Plan:
     """Build (or fetch from a cache) the plan of one problem descriptor on the current device.
 
-    Calls with equal descriptors share one plan.  A plan that owns device scratch
-    (``Plan.scratch_bytes > 0``: 8-bit weights at M <= 16 with a K split, prepacked int4 weights
-    at M > 16) serves one stream at a time."""
+    Calls with equal descriptors share one plan, except that a plan owning device scratch
+    (``Plan.scratch_bytes > 0``: bf16 decode shapes whose K is split over workgroups, 8-bit weights
+    at M <= 16 with a K split, prepacked int4 weights at M > 32) is made once per ``stream`` (default:
+    the current stream), since it must not run on two streams at once.  The cache holds the 256
+    most recently used plans."""
     d = Desc()
     lib().ge_desc_init(ctypes.byref(d))
     d.M, d.N, d.K = M, N, K
@@ -262,11 +279,19 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
                | (FLAG_B_PREPACKED if b_prepacked else 0))
     d.group_size, d.zero_point = group, zero_point
     torch = _torch()
-    key = (kind, bytes(d), torch.cuda.current_device() if torch.cuda.is_available() else -1)
-    p = _plan_cache.get(key)
-    if p is None:
-        p = Plan(d, kind)
-        _plan_cache[key] = p
+    base = (kind, bytes(d), torch.cuda.current_device() if torch.cuda.is_available() else -1)
+    skey = base + (_stream_key(stream),) if torch.cuda.is_available() else base + (0,)
+    with _cache_lock:
+        for key in (base, skey):
+            p = _plan_cache.get(key)
+            if p is not None:
+                _plan_cache.move_to_end(key)
+                return p
+    p = Plan(d, kind)
+    with _cache_lock:
+        _plan_cache[skey if p.scratch_bytes > 0 else base] = p
+        while len(_plan_cache) > _PLAN_CACHE_MAX:
+            _plan_cache.popitem(last=False)
     return p
 
 
@@ -276,7 +301,7 @@ def _out(M, N, dtype, device, out):
     return _torch().empty((M, N), dtype=dtype, device=device)
 
 
-def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=False):
+def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=False, stream=None):
     M, K = A.shape
     N = B.shape[1] if b_layout == LAYOUT_KN else B.shape[0]
     return plan(KIND_GENERIC, M, N, K, a_type=_dtype_code(A), b_type=_dtype_code(B),
@@ -285,7 +310,8 @@ def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=F
                 r_type=_dtype_code(R) if R is not None else None, b_layout=b_layout,
                 lda=_ld(A), ldb=_ld(B), ldc=_ld(C) if C is not None else 0, ldd=_ld(out),
                 ldr=_ld(R) if R is not None else 0, alpha=alpha, beta=beta, act=act,
-                bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None, b_prepacked=prepacked)
+                bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None, b_prepacked=prepacked,
+                stream=stream)
 
 
 def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
@@ -297,7 +323,7 @@ def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="
     M = A.shape[0]
     N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]
     out = _out(M, N, out_dtype or A.dtype, A.device, out)
-    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked, stream)
     _check(lib().gemm_epi_run(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
                               _stream(stream)), "gemm_epi_run")
     return out
@@ -310,7 +336,7 @@ def gemm_epilogue_unfused(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.
     M = A.shape[0]
     N = B.shape[1] if lay == LAYOUT_KN else B.shape[0]
     out = _out(M, N, out_dtype or A.dtype, A.device, out)
-    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, stream=stream)
     ws = workspace if workspace is not None else _workspace(p, A.device)
     _check(lib().gemm_epi_run_unfused(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
                                       _ptr(ws), _stream(stream)), "gemm_epi_run_unfused")
@@ -322,11 +348,11 @@ def _workspace(p: Plan, device):
     return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
 
 
-def _swiglu_plan(X, Wg, out):
+def _swiglu_plan(X, Wg, out, stream=None):
     M, K = X.shape
     N = Wg.shape[1]
     return plan(KIND_SWIGLU, M, N, K, a_type=BF16, b_type=BF16, d_type=BF16, lda=_ld(X), ldb=_ld(Wg),
-                ldd=_ld(out))
+                ldd=_ld(out), stream=stream)
 
 
 def swiglu(X, Wg, Wu, *, out=None, stream=None):
@@ -334,7 +360,7 @@ def swiglu(X, Wg, Wu, *, out=None, stream=None):
     if Wg.stride() != Wu.stride() or Wg.shape != Wu.shape:
         raise ValueError("Wg and Wu must have the same shape and strides")
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
-    p = _swiglu_plan(X, Wg, out)
+    p = _swiglu_plan(X, Wg, out, stream)
     _check(lib().gemm_swiglu_run(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream)),
            "gemm_swiglu_run")
     return out
@@ -342,7 +368,7 @@ def swiglu(X, Wg, Wu, *, out=None, stream=None):
 
 def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, stream=None):
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
-    p = _swiglu_plan(X, Wg, out)
+    p = _swiglu_plan(X, Wg, out, stream)
     ws = workspace if workspace is not None else _workspace(p, X.device)
     _check(lib().gemm_swiglu_run_unfused(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _ptr(ws),
                                          _stream(stream)), "gemm_swiglu_run_unfused")
@@ -360,7 +386,7 @@ def _zp(fmt, zero_point):
 
 
 def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked=False,
-             fmt="u4"):
+             fmt="u4", stream=None):
     M, K = X.shape
     N = scales.shape[1]
     return plan(KIND_W4, M, N, K, a_type=BF16, b_type=WEIGHT_FORMATS[fmt], d_type=_dtype_code(out),
@@ -371,7 +397,7 @@ def _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point
                 ldc=_ld(C) if C is not None else 0, ldd=_ld(out), ldr=_ld(R) if R is not None else 0,
                 alpha=alpha, beta=beta, act=act, bias=bias is not None, C=C is not None and beta != 0.0,
                 R=R is not None, group=group, zero_point=_zp(fmt, zero_point), lo_first=lo_first,
-                prepacked=prepacked)
+                prepacked=prepacked, stream=stream)
 
 
 def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none", group=128,
@@ -382,7 +408,8 @@ def w4_gemm(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, ac
     ``zero_point``: default 8 (u4), 128 (u8), 0 (fp8).
     ``prepacked``: Wq came from ``w4_prepack`` with the same ``fmt`` (kernel-native layout, same byte count)."""
     out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt,
+                 stream)
     _check(lib().gemm_w4_run(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias), _ptr(R),
                              _ptr(out), _stream(stream)), "gemm_w4_run")
     return out
@@ -392,7 +419,8 @@ def w4_gemm_unfused(X, Wq, scales, *, bias=None, C=None, R=None, alpha=1.0, beta
                     group=128, zero_point=None, lo_first=False, prepacked=False, out=None, out_dtype=None,
                     workspace=None, stream=None, fmt="u4"):
     out = _out(X.shape[0], scales.shape[1], out_dtype or X.dtype, X.device, out)
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt,
+                 stream)
     ws = workspace if workspace is not None else _workspace(p, X.device)
     _check(lib().gemm_w4_run_unfused(p.handle, _ptr(X), _ptr(Wq), _ptr(scales), _ptr(C), _ptr(bias),
                                      _ptr(R), _ptr(out), _ptr(ws), _stream(stream)), "gemm_w4_run_unfused")
@@ -430,7 +458,7 @@ def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, be
                           b_layout="KN", unfused=False, workspace=None, stream=None, prepacked=False) -> Prepared:
     """Bind one fused (or unfused) generic call to fixed tensors and stream."""
     lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
-    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked)
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked, stream)
     ts = [A, B, C, bias, R, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, A.device)
@@ -442,7 +470,7 @@ def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, be
 
 
 def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, stream=None) -> Prepared:
-    p = _swiglu_plan(X, Wg, out)
+    p = _swiglu_plan(X, Wg, out, stream)
     ts = [X, Wg, Wu, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, X.device)
@@ -456,7 +484,8 @@ def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, stream=None
 def prepare_w4_gemm(X, Wq, scales, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
                     group=128, zero_point=None, lo_first=False, prepacked=False, unfused=False, workspace=None,
                     stream=None, fmt="u4") -> Prepared:
-    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt)
+    p = _w4_plan(X, Wq, scales, C, bias, R, out, alpha, beta, act, group, zero_point, lo_first, prepacked, fmt,
+                 stream)
     ts = [X, Wq, scales, C, bias, R, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, X.device)

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -189,6 +190,26 @@ ge_status check_epi_ptrs(const ge_plan *pl, const void *C, const void *bias, con
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// One non-blocking stream per device, made on first use, for the library's own set-up work
+// (zeroing plan scratch): waiting for it does not wait for the callers' streams.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_init_mutex;
+hipStream_t g_init_stream[MAX_DEVICES];
+
+hipError_t init_stream(int dev, hipStream_t *out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_init_mutex);
+    if (!g_init_stream[dev]) {
+        hipError_t e = hipStreamCreateWithFlags(&g_init_stream[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            g_init_stream[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = g_init_stream[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,11 +384,23 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     }
     if (bytes > 0) {
         hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);
-        if (e == hipSuccess) e = hipMemset(pl.scratch, 0, (size_t)bytes);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
-            if (pl.scratch) (void)hipFree(pl.scratch);
-            return hip_status(e, "allocating the plan's device scratch");
+            pl.scratch = nullptr;
+            (void)hipGetLastError();
+            return fail(GE_ERR_HIP,
+                        "allocating the plan's %lld bytes of device scratch failed (%s); plans that own scratch "
+                        "must be made outside graph capture",
+                        (long long)bytes, hipGetErrorString(e));
+        }
+        // zeroed on a stream of the library's own, waiting for that stream alone (the callers'
+        // streams keep running)
+        hipStream_t zs = nullptr;
+        e = init_stream(dev, &zs);
+        if (e == hipSuccess) e = hipMemsetAsync(pl.scratch, 0, (size_t)bytes, zs);
+        if (e == hipSuccess) e = hipStreamSynchronize(zs);
+        if (e != hipSuccess) {
+            (void)hipFree(pl.scratch);
+            return hip_status(e, "zeroing the plan's device scratch");
         }
         pl.scratch_use = use;
         pl.scratch_bytes = (size_t)bytes;

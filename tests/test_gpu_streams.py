@@ -74,3 +74,36 @@ def test_call_is_ordered_by_its_stream():
     s.synchronize()
     want = dict(inp, A=other["A"])
     assert_close(out, oracle.reference(want), TOL_BF16, "stream order")
+
+
+@pytest.mark.parametrize("shape,kernel", [((16, 4096, 2048), "skinny_bf16_m16_128col_streamk"),
+                                          ((16, 8192, 4096), "skinny_bf16_m16_128col_streamk")])
+def test_scratch_owning_shape_on_two_streams_at_once(shape, kernel):
+    # the stream-K decode kernel hands partial tiles off through its plan's scratch: the same
+    # descriptor issued on two streams gets one plan (and scratch) per stream, so interleaved calls
+    # on both streams, with no synchronisation between them, each match the oracle
+    M, N, K = shape
+    _, i1 = _inputs(M, N, K, 35)
+    _, i2 = _inputs(M, N, K, 36)
+    B, bias, R = (to_dev(i1[k]) for k in ("B", "bias", "R"))
+    A1, A2 = to_dev(i1["A"]), to_dev(i2["A"])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    kw = dict(bias=True, R=True, act="gelu_tanh", lda=K, ldb=N, ldd=N, ldr=N)  # the descriptor gemm_epilogue makes
+    p1 = ge.plan(ge.KIND_GENERIC, M, N, K, stream=s1, **kw)
+    p2 = ge.plan(ge.KIND_GENERIC, M, N, K, stream=s2, **kw)
+    assert p1.kernel == kernel and p1.scratch_bytes > 0
+    assert p1 is not p2 and p1 is ge.plan(ge.KIND_GENERIC, M, N, K, stream=s1, **kw)
+    outs1 = [torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for _ in range(8)]
+    outs2 = [torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for _ in range(8)]
+    torch.cuda.synchronize()
+    for o1, o2 in zip(outs1, outs2):
+        ge.gemm_epilogue(A1, B, bias=bias, R=R, act="gelu_tanh", out=o1, stream=s1)
+        ge.gemm_epilogue(A2, B, bias=bias, R=R, act="gelu_tanh", out=o2, stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    ref1 = oracle.reference(i1)
+    ref2 = oracle.reference(dict(i1, A=i2["A"]))
+    for o in outs1:
+        assert_close(o, ref1, TOL_BF16, "stream 1")
+    for o in outs2:
+        assert_close(o, ref2, TOL_BF16, "stream 2")
