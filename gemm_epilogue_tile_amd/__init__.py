@@ -20,7 +20,7 @@ __all__ = [
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
     "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope", "prepare_rope_qk",
-    "prepare_rope",
+    "prepare_rope", "gemm_epilogue_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,9 +33,11 @@ LAYOUT_KN, LAYOUT_NK = 0, 1
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
 FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED, FLAG_B_PREPACKED = 1, 2, 4, 8, 16, 32
+FLAG_NO_SCRATCH = 64
 
 EXPORTS = [
     "ge_desc_init", "gemm_epi_plan", "gemm_epi_plan_destroy", "gemm_epi_plan_kernel", "gemm_epi_plan_scratch_bytes", "gemm_epi_run",
+    "gemm_epi_run_noalloc",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
     "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack", "gemm_b_prepack",
     "ge_add_rmsnorm_run", "ge_rope_qk_run", "ge_rope_run",
@@ -91,6 +93,8 @@ def lib():
             L.gemm_epi_plan_scratch_bytes.restype = ctypes.c_size_t
             L.gemm_epi_run.argtypes = [P] * 8
             L.gemm_epi_run.restype = I
+            L.gemm_epi_run_noalloc.argtypes = [P] * 8
+            L.gemm_epi_run_noalloc.restype = I
             L.gemm_swiglu_run.argtypes = [P] * 6
             L.gemm_swiglu_run.restype = I
             L.gemm_w4_run.argtypes = [P] * 9
@@ -253,14 +257,15 @@ def _stream_key(stream) -> int:
 def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=BF16, c_type=None,
          bias_type=None, r_type=None, b_layout=LAYOUT_KN, lda=0, ldb=0, ldc=0, ldd=0, ldr=0,
          alpha=1.0, beta=0.0, act="none", bias=False, C=False, R=False, group=128, zero_point=8,
-         lo_first=False, prepacked=False, b_prepacked=False, stream=None) -> Plan:
+         lo_first=False, prepacked=False, b_prepacked=False, no_scratch=False, stream=None) -> Plan:
     """Build (or fetch from a cache) the plan of one problem descriptor on the current device.
 
     Calls with equal descriptors share one plan, except that a plan owning device scratch
     (``Plan.scratch_bytes > 0``: bf16 decode shapes whose K is split over workgroups, 8-bit weights
     at M <= 16 with a K split, prepacked int4 weights at M > 32) is made once per ``stream`` (default:
-    the current stream), since it must not run on two streams at once.  The cache holds the 256
-    most recently used plans."""
+    the current stream), since it must not run on two streams at once.  ``no_scratch``: a plan that
+    allocates no device memory (for ``gemm_epilogue_noalloc``).  The cache holds the 256 most recently
+    used plans."""
     d = Desc()
     lib().ge_desc_init(ctypes.byref(d))
     d.M, d.N, d.K = M, N, K
@@ -276,7 +281,7 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
     d.act = ACTS[act] if isinstance(act, str) else int(act)
     d.flags = ((FLAG_BIAS if bias else 0) | (FLAG_C if C else 0) | (FLAG_RESIDUAL if R else 0)
                | (FLAG_NIBBLE_LO_FIRST if lo_first else 0) | (FLAG_W4_PREPACKED if prepacked else 0)
-               | (FLAG_B_PREPACKED if b_prepacked else 0))
+               | (FLAG_B_PREPACKED if b_prepacked else 0) | (FLAG_NO_SCRATCH if no_scratch else 0))
     d.group_size, d.zero_point = group, zero_point
     torch = _torch()
     base = (kind, bytes(d), torch.cuda.current_device() if torch.cuda.is_available() else -1)
@@ -301,7 +306,8 @@ def _out(M, N, dtype, device, out):
     return _torch().empty((M, N), dtype=dtype, device=device)
 
 
-def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=False, stream=None):
+def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=False, stream=None,
+                  no_scratch=False):
     M, K = A.shape
     N = B.shape[1] if b_layout == LAYOUT_KN else B.shape[0]
     return plan(KIND_GENERIC, M, N, K, a_type=_dtype_code(A), b_type=_dtype_code(B),
@@ -311,7 +317,7 @@ def _generic_plan(A, B, b_layout, C, bias, R, out, alpha, beta, act, prepacked=F
                 lda=_ld(A), ldb=_ld(B), ldc=_ld(C) if C is not None else 0, ldd=_ld(out),
                 ldr=_ld(R) if R is not None else 0, alpha=alpha, beta=beta, act=act,
                 bias=bias is not None, C=C is not None and beta != 0.0, R=R is not None, b_prepacked=prepacked,
-                stream=stream)
+                no_scratch=no_scratch, stream=stream)
 
 
 def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
@@ -326,6 +332,18 @@ def gemm_epilogue(A, B, *, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="
     p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked, stream)
     _check(lib().gemm_epi_run(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
                               _stream(stream)), "gemm_epi_run")
+    return out
+
+
+def gemm_epilogue_noalloc(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",
+                          b_layout="KN", stream=None, prepacked=False):
+    """``gemm_epilogue`` through ``gemm_epi_run_noalloc``: the plan allocates no device memory and the
+    run uses the library's static per-GPU scratch (calls that overlap on one GPU race).  ``out`` is
+    required, so the call allocates nothing either."""
+    lay = LAYOUT_KN if b_layout == "KN" else LAYOUT_NK
+    p = _generic_plan(A, B, lay, C, bias, R, out, alpha, beta, act, prepacked, stream, no_scratch=True)
+    _check(lib().gemm_epi_run_noalloc(p.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(bias), _ptr(R), _ptr(out),
+                                      _stream(stream)), "gemm_epi_run_noalloc")
     return out
 
 

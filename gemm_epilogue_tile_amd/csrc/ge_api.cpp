@@ -138,8 +138,8 @@ hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     return launch_general(p, s);
 }
 
-const char *fused_name(const Problem &p, int cu_count) {
-    if (skinny_supported(p)) return skinny_kernel_name(p, cu_count);
+const char *fused_name(const Problem &p, int cu_count, bool scratch = true) {
+    if (skinny_supported(p)) return skinny_kernel_name(p, cu_count, scratch);
     if (tile_supported(p)) return tile_kernel_name(p, cu_count);
     return "general_64x64";
 }
@@ -212,6 +212,46 @@ hipError_t init_stream(int dev, hipStream_t *out) {
 
 }  // namespace
 
+// Device scratch of gemm_epi_run_noalloc (for callers that cannot allocate): the stream-K decode
+// kernel's per-column-block arrival counters (first NOALLOC_COUNTER_BYTES, which must start at zero;
+// the kernel re-arms them) and its fp32 partial tiles (the rest).  Every GPU the library runs on
+// holds one copy until the process ends; host code uses only the address hipGetSymbolAddress returns
+// for the current device, never the array's name.
+#define NOALLOC_COUNTER_BYTES (64u << 10)
+#define NOALLOC_TILE_BYTES (8u << 20)
+static __device__ __align__(256) unsigned char scratch[NOALLOC_COUNTER_BYTES + NOALLOC_TILE_BYTES];
+
+namespace {
+
+void *g_scratch_ptr[MAX_DEVICES];  // device address of `scratch` per device (guarded by g_init_mutex)
+
+__global__ void zero_words_kernel(uint32_t *p, uint32_t n) {
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Address of this device's scratch; on the first call on a device its counters are cleared by a
+// kernel on the caller's stream (a kernel, not a memset, so that a graph capturing this call
+// replays correctly).
+ge_status noalloc_scratch(int dev, hipStream_t s, unsigned char **out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(GE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_init_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(GE_ERR_HIP, "hipGetSymbolAddress of the static scratch: %s", hipGetErrorString(e));
+        }
+        hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, s, (uint32_t *)ptr, NOALLOC_COUNTER_BYTES / 4);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_status(e, "clearing the static scratch");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = (unsigned char *)g_scratch_ptr[dev];
+    return GE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 void ge_desc_init(ge_desc *d) {
@@ -253,7 +293,7 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         return fail(GE_ERR_UNSUPPORTED, "matrix with 2^31 or more elements");
     if (d.act < GE_ACT_NONE || d.act > GE_ACT_SILU) return fail(GE_ERR_INVALID_ARG, "unknown activation %d", d.act);
     if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED |
-                    GE_FLAG_B_PREPACKED))
+                    GE_FLAG_B_PREPACKED | GE_FLAG_NO_SCRATCH))
         return fail(GE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags);
     if ((d.flags & GE_FLAG_B_PREPACKED) && kind != GE_KIND_GENERIC)
         return fail(GE_ERR_INVALID_ARG, "B_PREPACKED applies to generic bf16 plans");
@@ -382,6 +422,13 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             pl.split = slots;
         }
     }
+    if (bytes > 0 && (d.flags & GE_FLAG_NO_SCRATCH)) {
+        // no device memory: the variant of the kernel that needs none
+        if (use == SCRATCH_A16)
+            return fail(GE_ERR_UNSUPPORTED, "prepacked int4 weights with M > 32 need device scratch");
+        pl.kernel = fused_name(p, pl.cu_count, false);
+        bytes = 0;
+    }
     if (bytes > 0) {
         hipError_t e = hipMalloc(&pl.scratch, (size_t)bytes);
         if (e != hipSuccess) {
@@ -452,6 +499,47 @@ ge_status gemm_epi_run(const ge_plan *pl, const void *A, const void *B, const vo
     if (p.b_packed && !skinny_supported(p))
         return fail(GE_ERR_ALIGN, "prepacked bf16 path needs 16-byte aligned A and B and an lda that is a multiple of 8");
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_epi_run launch");
+}
+
+ge_status gemm_epi_run_noalloc(const ge_plan *pl, const void *A, const void *B, const void *C, const void *bias,
+                               const void *R, void *D, void *stream) {
+    if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
+    if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (!A || !B) return fail(GE_ERR_INVALID_ARG, "A or B is NULL");
+    ge_status st = check_epi_ptrs(pl, C, bias, R, D);
+    if (st) return st;
+    const ge_desc &d = pl->d;
+    const size_t es = type_size(d.a_type);
+    const size_t nA = ((size_t)(d.M - 1) * pl->lda + d.K) * es;
+    const size_t nB = (d.flags & GE_FLAG_B_PREPACKED) ? (size_t)d.K * d.N * es
+                      : (d.b_layout == GE_LAYOUT_KN ? (size_t)(d.K - 1) * pl->ldb + d.N
+                                                    : (size_t)(d.N - 1) * pl->ldb + d.K) * es;
+    if ((st = check_alias(pl, A, nA, B, nB, C, R, D))) return st;
+    if ((st = check_device(pl))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    Problem p = make_problem(pl, A, B, nullptr, nullptr, C, bias, R, D);
+    p.split = 1;
+    p.split_ws = nullptr;
+    p.split_cnt = nullptr;
+    if (p.b_packed && !skinny_supported(p))
+        return fail(GE_ERR_ALIGN, "prepacked bf16 path needs 16-byte aligned A and B and an lda that is a multiple of 8");
+    // the kernel a plan with scratch would launch, its tiles and counters in the static scratch
+    const int slots = skinny_supported(p) ? bf16_sk_slots(p, pl->cu_count) : 0;
+    if (slots > 0) {
+        const int64_t ncb = (d.N + 127) / 128;
+        const int64_t tiles = bf16_sk_scratch_bytes(p, slots) - ncb * 4;
+        if (ncb * 4 > (int64_t)NOALLOC_COUNTER_BYTES || tiles > (int64_t)NOALLOC_TILE_BYTES)
+            return fail(GE_ERR_UNSUPPORTED,
+                        "this shape needs %lld bytes of partial tiles and %lld counters; the static scratch holds "
+                        "%u bytes and %u counters",
+                        (long long)tiles, (long long)ncb, NOALLOC_TILE_BYTES, NOALLOC_COUNTER_BYTES / 4);
+        unsigned char *base = nullptr;
+        if ((st = noalloc_scratch(pl->device, s, &base))) return st;
+        p.split = slots;
+        p.split_cnt = (uint32_t *)base;
+        p.split_ws = (float *)(base + NOALLOC_COUNTER_BYTES);
+    }
+    return hip_status(launch_fused(pl, p, s), "gemm_epi_run_noalloc launch");
 }
 
 ge_status gemm_swiglu_run(const ge_plan *pl, const void *X, const void *Wg, const void *Wu, void *D,

@@ -80,7 +80,8 @@ hipError_t launch_rope(int32_t batch, int32_t S, int32_t D, const uint16_t *X, c
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);
-const char *skinny_kernel_name(const Problem &p, int cu_count);
+// scratch: the plan may own device scratch (false: the variants that need none)
+const char *skinny_kernel_name(const Problem &p, int cu_count, bool scratch = true);
 // K splits of the 8-bit streaming kernel and the scratch bytes they need
 // (tiles, then counters that must start at zero; the kernel re-arms them).
 int w8_split(const Problem &p, int cu_count);

@@ -996,7 +996,7 @@ int64_t bf16_sk_scratch_bytes(const Problem &p, int slots) {
     return ncb * slots * 16 * 128 * 4 + ncb * 4;
 }
 
-const char *skinny_kernel_name(const Problem &p, int cu_count) {
+const char *skinny_kernel_name(const Problem &p, int cu_count, bool scratch) {
     if (p.mode == MODE_W4 && p.wfmt != WFMT_U4) {
         static const char *names[2][4] = {
             {"skinny_u8_m16_128col", "skinny_u8_m16_128col_split2", "skinny_u8_m16_128col_split4",
@@ -1008,15 +1008,15 @@ const char *skinny_kernel_name(const Problem &p, int cu_count) {
              "skinny_u8_m16_128col_split4_prepacked", "skinny_u8_m16_128col_split8_prepacked"},
             {"skinny_fp8_m16_128col_prepacked", "skinny_fp8_m16_128col_split2_prepacked",
              "skinny_fp8_m16_128col_split4_prepacked", "skinny_fp8_m16_128col_split8_prepacked"}};
-        const int s = w8_split(p, cu_count);
+        const int s = scratch ? w8_split(p, cu_count) : 1;
         return (p.w4_packed ? packed_names : names)[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
     if (p.mode == MODE_W4) return p.M <= 16 ? "skinny_w4_m16_32col" : "skinny_w4_m32_32col";
     if (p.b_packed)
-        return bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
+        return scratch && bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
                : p.M <= 16                    ? "skinny_bf16_m16_128col_prepacked"
                                               : "skinny_bf16_m32_128col_prepacked";
-    if (bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
+    if (scratch && bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
     return names[p.M > 16][bf16_chunks(p.N, cu_count) == 16 ? 0 : 1];

@@ -99,6 +99,7 @@ typedef int32_t ge_status;
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
 #define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
 #define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 32: B is in the layout gemm_b_prepack writes */
+#define GE_FLAG_NO_SCRATCH 64u     /* the plan allocates no device memory (see gemm_epi_run_noalloc) */
 
 /*
  * Problem descriptor.  Unused fields must be zero.  dtype fields take
@@ -191,6 +192,26 @@ GE_API const char *gemm_epi_plan_kernel(const ge_plan *plan);
  */
 GE_API ge_status gemm_epi_run(const ge_plan *plan, const void *A, const void *B, const void *C,
                        const void *bias, const void *R, void *D, void *stream);
+
+/*
+ * gemm_epi_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as gemm_epi_run, and the same kernel that a
+ * plan owning scratch would launch; where that kernel needs device scratch
+ * (bf16 decode shapes, M <= 16, whose K is split over workgroups: partial
+ * fp32 tiles and per-column-block counters), it uses a static buffer that the
+ * library holds on each GPU until the process ends: 64 KiB of counters
+ * (16384 column blocks of 128) and 8 MiB of tiles; a shape that needs more
+ * returns GE_ERR_UNSUPPORTED.  The call allocates nothing and never
+ * synchronises; its first call on a GPU also queues a small kernel that
+ * clears the counters.  Every call on one GPU shares that buffer: calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads) race and give wrong results.  A plan made with GE_FLAG_NO_SCRATCH
+ * allocates no device memory, so neither making nor running it allocates
+ * (gemm_epi_run on such a plan launches the variant that needs no scratch).
+ */
+GE_API ge_status gemm_epi_run_noalloc(const ge_plan *plan, const void *A, const void *B, const void *C,
+                                      const void *bias, const void *R, void *D, void *stream);
 
 /*
  * Fused SwiGLU dual GEMM:  D = silu(X.Wg) * (X.Wu).  X is [M, K]; Wg and Wu

@@ -101,7 +101,7 @@ def _plan_status(kind=ge.KIND_GENERIC, **kw):
     (dict(M=0), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
     (dict(K=-1), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
     (dict(act=7), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
-    (dict(flags=64), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
+    (dict(flags=128), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
     (dict(b_layout=3), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
     (dict(lda=10), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
     (dict(ldd=5), ge.KIND_GENERIC, ge.ERR_INVALID_ARG),
@@ -151,6 +151,7 @@ def test_run_calls_reject_null_plan():
     L = ge.lib()
     p = ctypes.c_void_p(0)
     assert L.gemm_epi_run(p, None, None, None, None, None, None, None) == ge.ERR_INVALID_ARG
+    assert L.gemm_epi_run_noalloc(p, None, None, None, None, None, None, None) == ge.ERR_INVALID_ARG
     assert L.gemm_swiglu_run(p, None, None, None, None, None) == ge.ERR_INVALID_ARG
     assert L.gemm_w4_run(p, None, None, None, None, None, None, None, None) == ge.ERR_INVALID_ARG
     assert L.gemm_epi_run_unfused(p, *([None] * 8)) == ge.ERR_INVALID_ARG
