@@ -53,16 +53,16 @@ struct ge_plan {
     int32_t group;
     const char *kernel;  // fused kernel chosen for aligned inputs
     int32_t split;       // K splits of the 8-bit streaming kernel (1: none)
-    int32_t scratch_use; // what scratch holds: SCRATCH_NONE / SCRATCH_SPLIT / SCRATCH_A16
+    int32_t scratch_use; // what scratch holds: SCRATCH_NONE / SCRATCH_SPLIT / SCRATCH_SK
     void *scratch;       // device scratch owned by the plan, or NULL
     size_t scratch_bytes;
 };
 
 namespace {
 
-// plan scratch: the 8-bit kernel's split tiles and counters, the int4 tile kernel's fp16 copy
-// of A, or the stream-K decode kernel's tiles and counters
-enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_A16 = 2, SCRATCH_SK = 3 };
+// plan scratch: the 8-bit kernel's split tiles and counters, or the stream-K decode kernel's tiles
+// and counters
+enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_SK = 3 };
 
 int32_t wfmt_of(const ge_desc &d) {
     return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
@@ -117,8 +117,6 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
         p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - (size_t)((d.N + 127) / 128) * 4);
-    } else if (pl->scratch && pl->scratch_use == SCRATCH_A16 && p.mode == MODE_W4) {
-        p.A16 = pl->scratch;
     }
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
@@ -396,8 +394,8 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
                              (const void *)256, (const void *)256, (const void *)256, (void *)256);
     pl.kernel = fused_name(p, pl.cu_count);
 
-    // device scratch: the 8-bit streaming kernel splits K over workgroups when the column blocks
-    // alone do not fill the GPU; the int4 tile kernel reads an fp16 copy of A
+    // device scratch: the 8-bit and the bf16 streaming kernels split K over workgroups when the
+    // column blocks alone do not fill the GPU
     pl.split = 1;
     pl.scratch_use = SCRATCH_NONE;
     pl.scratch = nullptr;
@@ -411,9 +409,6 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             use = SCRATCH_SPLIT;
             pl.split = split;
         }
-    } else if (kind == GE_KIND_W4 && p.wfmt == WFMT_U4 && !skinny_supported(p) && tile_w4_supported(p)) {
-        bytes = tile_w4_scratch_bytes(p);
-        use = SCRATCH_A16;
     } else if (kind == GE_KIND_GENERIC && skinny_supported(p)) {
         const int slots = bf16_sk_slots(p, pl.cu_count);
         if (slots > 0) {
@@ -424,8 +419,6 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     }
     if (bytes > 0 && (d.flags & GE_FLAG_NO_SCRATCH)) {
         // no device memory: the variant of the kernel that needs none
-        if (use == SCRATCH_A16)
-            return fail(GE_ERR_UNSUPPORTED, "prepacked int4 weights with M > 32 need device scratch");
         pl.kernel = fused_name(p, pl.cu_count, false);
         bytes = 0;
     }

@@ -32,8 +32,6 @@ struct Problem {
     int32_t split;
     float *split_ws;
     uint32_t *split_cnt;
-    // fp16 copy of A for the int4 tile kernel (dense [M][K], plan scratch), or NULL
-    void *A16;
     EpiArgs epi;
 };
 
@@ -46,10 +44,8 @@ bool tile_supported(const Problem &p);
 hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s);
 const char *tile_kernel_name(const Problem &p, int cu_count);
 
-// int4 tile kernel (prepacked weights, M > 16), dispatched through launch_tile.
-// It first converts A to fp16 into p.A16 (plan scratch of tile_w4_scratch_bytes).
+// int4 tile kernel (prepacked weights, M > 32), dispatched through launch_tile.
 bool tile_w4_supported(const Problem &p);
-int64_t tile_w4_scratch_bytes(const Problem &p);
 hipError_t launch_tile_w4(const Problem &p, hipStream_t s);
 const char *tile_w4_kernel_name();
 

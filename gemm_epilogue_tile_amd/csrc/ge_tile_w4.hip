@@ -1,4 +1,4 @@
-// ge_tile_w4.hip -- int4 weights (prepacked), M > 16: MFMA tile kernel with
+// ge_tile_w4.hip -- int4 weights (prepacked), M > 32: MFMA tile kernel with
 // the dequantisation in the K-loop and the epilogue in the store path (page
 // "Fusion Thinking", Pattern 3: packed int4 codes, zero point, per-group
 // scales, dequantised in registers on the way into the product).
@@ -10,79 +10,68 @@ namespace {
 #include "ge_tile_common.hpp"
 
 // ---------------------------------------------------------------------------
-// int4 weights (prepacked), M > 16: 128 x 128 tiles, fp16 MFMA.
+// int4 weights (prepacked), M > 32: 64 x 128 tiles (two workgroups per CU), bf16 MFMA.
 //
-// (c - z) * s with z = 8 has at most 3 + 8 significant bits, so the
-// dequantised weight is exact in fp16 (scales in the fp16 normal range); bf16
-// activations convert to fp16 exactly (|x| in the fp16 range).  The products
-// are then exact in fp32 and the accumulators need no per-group rescaling.
+// Arithmetic, exact for every finite bf16 X and scale up to fp32 summation
+// order (no fp16 range or rounding anywhere).  A code c becomes the bf16 value
+// 128 + c by OR-ing it into the mantissa of 0x4300, so for 128-row group g
+//   sum_k x[m][k] (c[k][n] - z) s[g][n]
+//     = s[g][n] * U_g[m][n]  -  (128 + z) * Sx_g[m] * s[g][n],
+//   U_g[m][n] = sum_{k in g} x[m][k] (128 + c[k][n])   (bf16 MFMA, fp32),
+//   Sx_g[m]   = sum_{k in g} x[m][k].
+// The first term is accumulated group by group in fp32 registers (one fma per
+// output element per group).  The second term is a small product over the
+// groups, Sx (rows x groups) by s (groups x columns), run on the MFMA once per
+// 32 groups: -(128 + z) Sx is split exactly into three bf16 parts, the scales
+// are bf16 already, so each MFMA product is exact and the sum is fp32.
 //
-// Activations: a pre-pass converts X to fp16 once per call into the plan's
-// scratch (each element is used by all N / 128 column tiles, so converting
-// it in every workgroup was the kernel's largest cost); the tile kernel
-// streams the fp16 rows by direct loads straight into a ring of swizzled
-// fragment buffers, as the bf16 tile kernel does.
-//
-// Waves: the four waves sit side by side (wave w: all 128 rows, columns
+// Waves: the four waves sit side by side (wave w: all 64 rows, columns
 // n0 + 32 w .. + 31), so no two waves use the same weights.  Each wave loads
 // the codes of its two prepacked 16-column tiles and their 32 scales into a
 // private LDS slot by direct loads (no barrier: a wave reads back only what
-// it loaded itself), and every lane dequantises its own B fragments in
-// registers, straight from the 16 prepacked bytes its load delivered: 16
-// codes per lane per stage, each code converted once per workgroup, with no
-// round trip of fp16 weights through LDS.  Only the activations are shared
-// through LDS.  (Sharing dequantised fp16 fragments between 2 x 2 waves
-// through LDS took 92.5 us per call at 512 x 8192 x 8192; this layout 72.)
+// it loaded), and every lane turns its own 16 prepacked bytes into B
+// fragments in registers, 16 codes per lane per stage (7 instructions per 8
+// codes: three shifts and four v_and_or_b32).  The bf16 activations are
+// shared through LDS: direct loads from X (its own row stride) six stages
+// ahead into a ring of eight swizzled fragment buffers.  Wave w also sums
+// rows 16 w .. 16 w + 15 of every stage from that ring (v_dot2 against
+// ones), completes Sx_g at the group's last stage and writes its three bf16
+// parts to the correction buffer; one barrier per stage orders every LDS
+// hand-over.  Two workgroups share a CU, so one's vector work runs beside
+// the other's MFMAs.
 //
-// Pipeline, per stage s (unrolled by 8 = two 128-row scale groups): the fp16
-// activations of stage s + 6 and (every fourth stage) the raw codes and
-// scales of the group after next go straight to LDS by direct loads (waits
-// counted by hand; the stage's position sits in the buffer resource, so no
-// vector instruction computes an address); every fourth stage the codes and
-// scales of the next group are read into registers; the activation fragments
-// of stage s + 1 are read and its B fragments dequantised; the 16 MFMAs of
-// stage s run on the fragments prepared one stage earlier.  One barrier per
-// stage.
-//
-// Dequant: a dword holds 8 codes, pair w (w = 0..3) at bits 4 w .. 4 w + 3 of
-// each 16-bit half.  Pairs at bits 0..3 are OR-ed into the mantissa of fp16
-// 1024 (ulp 1), pairs at bits 4..7 into that of fp16 64 (ulp 1/16), which
-// gives magic + c exactly either way with one v_and_or_b32 (pairs 2 and 3
-// after one shift by 8); then a packed subtract of magic + z and a packed
-// multiply by s.  13 instructions per 8 codes.
+// Pipeline, per stage s (unrolled by 8 = two groups): at a group's first stage
+// the previous group's partial products are scaled into the accumulators and
+// the stage's MFMAs start new partials (zero C); every 32 groups (and at the
+// end) the correction product runs; the direct loads of stage s + 6 and
+// (every fourth stage) the codes and scales of the group after next are
+// issued; every fourth stage the next group's codes and scales are read into
+// registers; the activation fragments of stage s + 1 are read and its B
+// fragments made; the 16 MFMAs of stage s run on the fragments prepared one
+// stage earlier.
 // ---------------------------------------------------------------------------
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ void mfma_f16_acc(f32x4 &acc, const f16x8 &a, const f16x8 &b) {
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// 8 bf16 (one u32x4) -> 8 fp16 (exact for values in the fp16 range)
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4 &w) {
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        r[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(w[q]), bf16hi(w[q])));
-    return r;
-}
-
-constexpr int W4_BM = 128, W4_BN = 128;
-constexpr int W4_MT = 8, W4_NT = 2;          // 16x16 tiles per wave: 128 rows x 32 columns
+constexpr int W4_BM = 64, W4_BN = 128;
+constexpr int W4_MT = 4, W4_NT = 2;          // 16x16 tiles per wave: 64 rows x 32 columns
 constexpr int W4_UNROLL = 8;                 // stages per loop trip (ring sizes divide it)
 constexpr int W4_AD = 6;                     // activation loads run this many stages ahead
-// LDS (bytes): fp16 activations, ring of 8 stages ([128][32] in the swizzled fragment layout);
+constexpr int W4_CHUNK = 32;                 // groups per correction product (one MFMA k-step)
+static_assert(W4_MT * W4_NT == 8, "one dequantisation piece per MFMA of a stage");
+// LDS (bytes): bf16 activations, ring of 8 stages ([64][32] in the swizzled fragment layout);
 // per wave, the raw codes of two groups (its two prepacked 16-column tiles, 1 KB each) and the
-// raw scales of two groups (one 1 KB slot per group, the wave's 32 columns in its first 64 bytes)
-constexpr int W4_A16 = 0, W4_A16_STAGE = W4_BM * 64;
-constexpr int W4_CODES = W4_A16 + W4_UNROLL * W4_A16_STAGE, W4_CODES_WAVE = 2 * 2 * 1024;
+// raw scales of two groups (one 1 KB slot per group, the wave's 32 columns in its first 64 bytes);
+// the correction operands: three bf16 parts of -(128 + z) Sx, [part][m-tile][16 rows][32 groups],
+// and per wave the scales, [n-tile][16 columns][32 groups] (both 64-byte rows: fragment order)
+constexpr int W4_AS = 0, W4_AS_STAGE = W4_BM * 64;
+constexpr int W4_CODES = W4_AS + W4_UNROLL * W4_AS_STAGE, W4_CODES_WAVE = 2 * 2 * 1024;
 constexpr int W4_SCALES = W4_CODES + 4 * W4_CODES_WAVE, W4_SCALES_WAVE = 2 * 1024;
-constexpr int W4_LDS = W4_SCALES + 4 * W4_SCALES_WAVE;  // 88 KB
+constexpr int W4_CA = W4_SCALES + 4 * W4_SCALES_WAVE, W4_CA_BYTES = 3 * W4_MT * 1024;
+constexpr int W4_CB = W4_CA + W4_CA_BYTES, W4_CB_WAVE = W4_NT * 1024;
+constexpr int W4_LDS = W4_CB + 4 * W4_CB_WAVE;  // 76 KB: two workgroups per CU
 
 // direct loads issued by each wave: 2 per stage (activations), 3 per group (codes, scales)
-constexpr int W4_LA = 2, W4_LB = 3;
-static_assert(W4_LA * 4 * 64 * 16 == W4_A16_STAGE, "four waves load one activation stage");
+constexpr int W4_LA = 1, W4_LB = 3;
+static_assert(W4_LA * 4 * 64 * 16 == W4_AS_STAGE, "four waves load one activation stage");
 // loads a wave may still have in flight at the top of stage u (mod 8) when everything issued up to
 // stage u - 4 must have landed: the activations of stages u-3 .. u-1 and the group loads among them
 // (issued at stages = 2 mod 4)
@@ -105,11 +94,14 @@ __device__ __forceinline__ i32x4 rsrc32(const void *base, uint32_t bytes) {
     return r;
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(1, 1)))
+// fp32 -> bf16 bits, round to nearest even
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.0f) & 0xffffu; }
+
+__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(2, 2)))
 void tile_w4_kernel(Problem p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(AS3 void *)smem;
-    const AS3 char *s3 = (const AS3 char *)smem;
+    AS3 char *s3 = (AS3 char *)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -128,22 +120,22 @@ void tile_w4_kernel(Problem p) {
     // Direct loads.  The lane offsets are fixed; the stage's (or group's) position goes into the
     // buffer resource (scalar arithmetic), whose range is empty past the end of K, so the loop
     // spends no vector instructions on addresses.
-    // activations: wave w loads rows 32 w .. 32 w + 31 of each stage, lane l row l / 4 of 16, LDS
+    // activations: wave w loads rows 16 w .. 16 w + 15 of each stage, lane l row l / 4 of 16, LDS
     // slot l % 4 of the row holding logical chunk (l % 4) ^ ((row >> 1) & 3)
-    const char *a_base = (const char *)p.A16 + (int64_t)m0 * p.K * 2;
-    const int64_t a_bytes = (int64_t)(p.M - m0) * p.K * 2;
+    const char *a_base = (const char *)p.A + (int64_t)m0 * p.lda * 2;
+    const int64_t a_bytes = ((int64_t)(p.M - m0 - 1) * p.lda + p.K) * 2;
     uint32_t a_src[W4_LA];
 #pragma unroll
     for (int q = 0; q < W4_LA; ++q) {
         const int row_l = lane >> 2;
         const int chunk = (lane & 3) ^ ((row_l >> 1) & 3);
-        a_src[q] = (uint32_t)(((wave * W4_LA + q) * 16 + row_l) * p.K * 2 + chunk * 16);
+        a_src[q] = (uint32_t)((int64_t)((wave * W4_LA + q) * 16 + row_l) * p.lda * 2 + chunk * 16);
     }
     auto load_a = [&](int d, int slot) {
         const i32x4 r = rsrc32(a_base + d * 64, d < nst ? (uint32_t)(a_bytes - d * 64) : 0u);
 #pragma unroll
         for (int q = 0; q < W4_LA; ++q)
-            load_lds16(r, lds0 + W4_A16 + slot * W4_A16_STAGE + (wave * W4_LA + q) * 1024, a_src[q]);
+            load_lds16(r, lds0 + W4_AS + slot * W4_AS_STAGE + (wave * W4_LA + q) * 1024, a_src[q]);
     };
     // codes of the wave's tiles 2 w, 2 w + 1 (group g: 1 KB at g KB into each tile's run) and
     // their 32 scales (lanes 0..3) into the wave's slot
@@ -163,65 +155,128 @@ void tile_w4_kernel(Problem p) {
         load_lds16(rs, lds0 + scales_w + slot * 1024, s_src);
     };
 
-    // a group's codes (lane's own 16 bytes of each tile) and scales (column 16 e + lane % 16)
     const int frow = lane & 15, fgrp = lane >> 4;
-    // code pairs at bits 0..3 (of each half) go into the mantissa of fp16 1024 (ulp 1), pairs at
-    // bits 4..7 into that of fp16 64 (ulp 1/16): both give magic + c exactly, with one v_and_or_b32
-    // and no shift for the latter
-    const _Float16 zl = (_Float16)(1024.0f + (float)p.zero_point), zh = (_Float16)(64.0f + (float)p.zero_point);
-    const f16x2 zlo2 = f16x2{zl, zl}, zhi2 = f16x2{zh, zh};
-    const uint32_t mask_lo = __builtin_amdgcn_readfirstlane(0x000f000fu);
-    const uint32_t mask_hi = __builtin_amdgcn_readfirstlane(0x00f000f0u);
-    uint32_t magic_lo = 0x64006400u, magic_hi = 0x54005400u;
-    asm volatile("" : "+v"(magic_lo), "+v"(magic_hi));
-    u32x4 craw[2][2];
-    f16x2 cs2[2][2];
+    // a group's codes (the lane's own 16 bytes of each tile) and scales: the four columns
+    // 16 j + 4 fgrp .. + 3 of each tile (the accumulator layout, two bf16 per dword) and column
+    // 16 j + frow (the correction product's B fragment layout)
+    u32x4 craw[2][W4_NT];
+    u32x2 sacc[2][W4_NT];
+    uint32_t sfrag[2];
     auto read_group = [&](int gp) {  // ring slot gp = group parity (compile-time)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < W4_NT; ++e) {
             craw[gp][e] = *(const AS3 u32x4 *)(s3 + codes_w + gp * 2048 + e * 1024 + lane * 16);
-            const uint16_t sr = *(const AS3 uint16_t *)(s3 + scales_w + gp * 1024 + (16 * e + frow) * 2);
-            const _Float16 sh = (_Float16)bf16_to_f32(sr);
-            cs2[gp][e] = f16x2{sh, sh};
+            sacc[gp][e] = *(const AS3 u32x2 *)(s3 + scales_w + gp * 1024 + (16 * e + 4 * fgrp) * 2);
         }
+        const uint32_t lo = *(const AS3 uint16_t *)(s3 + scales_w + gp * 1024 + frow * 2);
+        const uint32_t hi = *(const AS3 uint16_t *)(s3 + scales_w + gp * 1024 + (16 + frow) * 2);
+        sfrag[gp] = lo | (hi << 16);
     };
-    // B fragments of stage d (dd = d % 8): piece k = 0..7 dequantises code pair k % 4 of tile k / 4
-    // (pair w holds the nibbles 4 w .. 4 w + 3 of each half of the dword; pairs 2, 3 after a shift by 8)
-    f16x8 fb[2][W4_NT];
+    // B fragments of stage d (dd = d % 8): piece k = 0..7 makes code pair k % 4 of tile k / 4 (pair
+    // w holds the nibbles 4 w .. 4 w + 3 of each half of the dword) into two bf16 128 + c
+    bf16x8 fb[2][W4_NT];
     u32x4 dq[W4_NT];
-    uint32_t csh[W4_NT];
+    // (src & mask) | magic in one v_and_or_b32: the mask in a scalar register and the magic in a
+    // vector one, since this instruction takes no literal operand
+    const uint32_t nib_mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
+    uint32_t magic = 0x43004300u;
+    asm volatile("" : "+v"(magic));
     auto dequant_piece = [&](int dd, int k) {
         const int gp = (dd >> 2) & 1, q = dd & 3, e = k >> 2, w = k & 3;
-        uint32_t src;
-        if (w < 2) {
-            src = craw[gp][e][q];
-            asm volatile("" : "+v"(src));
-            if (w == 0) csh[e] = src >> 8;
-        } else {
-            src = csh[e];
-        }
-        uint32_t tt;
-        if (w & 1)
-            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(tt) : "v"(src), "s"(mask_hi), "v"(magic_hi));
-        else
-            asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(tt) : "v"(src), "s"(mask_lo), "v"(magic_lo));
-        uint32_t o = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, tt) - ((w & 1) ? zhi2 : zlo2)) * cs2[gp][e]);
-        asm volatile("" : "+v"(o));
-        dq[e][w] = o;
-        if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(f16x8, dq[e]);
+        const uint32_t src = craw[gp][e][q] >> (4 * w);
+        uint32_t t;
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t) : "v"(src), "s"(nib_mask), "v"(magic));
+        dq[e][w] = t;
+        if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(bf16x8, dq[e]);
     };
 
-    const int a_frag = W4_A16 + swz_a(frow, fgrp);
-    f16x8 fa[2][W4_MT];
+    const int a_frag = W4_AS + swz_a(frow, fgrp);
+    bf16x8 fa[2][W4_MT];
     auto read_a = [&](int dd, int i) {
-        fa[dd & 1][i] = *(const AS3 f16x8 *)(s3 + a_frag + dd * W4_A16_STAGE + i * 1024);
+        fa[dd & 1][i] = *(const AS3 bf16x8 *)(s3 + a_frag + dd * W4_AS_STAGE + i * 1024);
     };
 
-    f32x4 acc[W4_MT][W4_NT];
+    f32x4 acc[W4_MT][W4_NT], U[W4_MT][W4_NT];
 #pragma unroll
     for (int i = 0; i < W4_MT; ++i)
 #pragma unroll
-        for (int j = 0; j < W4_NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < W4_NT; ++j) acc[i][j] = U[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // row sums: wave w sums rows 16 w .. 16 w + 15 of each stage straight from the LDS ring, lane l
+    // quarter l % 4 (16 of the row's 64 bytes, whatever logical chunk the swizzle put there) of row
+    // 16 w + l / 4, with v_dot2 against bf16 ones
+    const float cq = -(128.0f + (float)p.zero_point);
+    float rsum = 0.f;
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    const int rs_row = 16 * wave + (lane >> 2);
+    const uint32_t rs_addr = W4_AS + rs_row * 64 + (lane & 3) * 16;
+    // (requested first in a stage and summed last, so that its wait does not cover the stage's
+    // fragment reads, which are requested after it)
+    u32x4 rs_v;
+    auto row_read = [&](int dd) { rs_v = *(const AS3 u32x4 *)(s3 + rs_addr + dd * W4_AS_STAGE); };
+    auto row_sums = [&]() {
+        // scalar copies: this compiler reads element 0 for a bit cast of a vector element
+        const uint32_t w[4] = {rs_v[0], rs_v[1], rs_v[2], rs_v[3]};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones, rsum, false);
+    };
+    // group g complete: the four quarters of each row added, the three bf16 parts of -(128 + z)
+    // Sx_g written to the correction buffer (lanes 0, 1, 2 of a row's four write one each)
+    auto write_sx = [&](int g) {
+        const int gg = g % W4_CHUNK;
+        float t2 = rsum + __shfl_xor(rsum, 1);
+        t2 += __shfl_xor(t2, 2);
+        const float v = t2 * cq;
+        rsum = 0.f;
+        const uint32_t hi = bf16_bits(v);
+        const float r1 = v - __builtin_bit_cast(float, hi << 16);
+        const uint32_t mid = bf16_bits(r1);
+        const uint32_t lo = bf16_bits(r1 - __builtin_bit_cast(float, mid << 16));
+        const uint32_t at = W4_CA + (rs_row >> 4) * 1024 + (rs_row & 15) * 64 + gg * 2;
+        const int part = lane & 3;
+        if (part < 3) *(AS3 uint16_t *)(s3 + at + part * W4_MT * 1024) = (uint16_t)(part == 0 ? hi : part == 1 ? mid : lo);
+    };
+    // the wave's correction scales: lanes of k-octet 0 put column 16 j + frow of group g in place
+    const uint32_t cb_w = W4_CB + wave * W4_CB_WAVE;
+    auto write_sb = [&](int g, int gp) {
+        if (fgrp == 0) {
+            const int gg = g % W4_CHUNK;
+            *(AS3 uint16_t *)(s3 + cb_w + frow * 64 + gg * 2) = (uint16_t)(sfrag[gp] & 0xffffu);
+            *(AS3 uint16_t *)(s3 + cb_w + 1024 + frow * 64 + gg * 2) = (uint16_t)(sfrag[gp] >> 16);
+        }
+    };
+    // correction product of one chunk of groups: acc += Sx-parts (rows x groups) . s (groups x
+    // columns), then the wave clears what it wrote (after the next barrier)
+    auto correction = [&]() {
+        bf16x8 bfr[W4_NT];
+#pragma unroll
+        for (int j = 0; j < W4_NT; ++j) bfr[j] = *(const AS3 bf16x8 *)(s3 + cb_w + j * 1024 + frow * 64 + fgrp * 16);
+#pragma unroll
+        for (int part = 0; part < 3; ++part)
+#pragma unroll
+            for (int i = 0; i < W4_MT; ++i) {
+                const bf16x8 af = *(const AS3 bf16x8 *)(s3 + W4_CA + (part * W4_MT + i) * 1024 + frow * 64 + fgrp * 16);
+#pragma unroll
+                for (int j = 0; j < W4_NT; ++j) acc[i][j] = mfma_bf16(bfr[j], af, acc[i][j]);
+            }
+    };
+    auto clear_correction = [&]() {
+        // this wave's parts (m-tile w: 3 KB) and its scales (2 KB)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int part = 0; part < 3; ++part) *(AS3 u32x4 *)(s3 + W4_CA + (part * W4_MT + wave) * 1024 + lane * 16) = z;
+#pragma unroll
+        for (int j = 0; j < W4_NT; ++j) *(AS3 u32x4 *)(s3 + cb_w + j * 1024 + lane * 16) = z;
+    };
+    // previous group's partial products into the accumulators: acc += s[n] * U
+    auto apply_tile = [&](int gp, int i, int j) {
+        const float s0 = bf16lo(sacc[gp][j][0]), s1 = bf16hi(sacc[gp][j][0]);
+        const float s2 = bf16lo(sacc[gp][j][1]), s3f = bf16hi(sacc[gp][j][1]);
+        acc[i][j][0] = __builtin_fmaf(s0, U[i][j][0], acc[i][j][0]);
+        acc[i][j][1] = __builtin_fmaf(s1, U[i][j][1], acc[i][j][1]);
+        acc[i][j][2] = __builtin_fmaf(s2, U[i][j][2], acc[i][j][2]);
+        acc[i][j][3] = __builtin_fmaf(s3f, U[i][j][3], acc[i][j][3]);
+    };
 
     auto lds_barrier = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -230,8 +285,9 @@ void tile_w4_kernel(Problem p) {
     };
 #define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 
-    // prologue (issue order and waits as in tile_w4_kernel): stage 0's activations, group 0 and
-    // stage 1's activations landed; group 0 read, stage 0's fragments read and dequantised
+    // prologue: correction buffers cleared; stage 0's activations, group 0 and stage 1's
+    // activations landed; group 0 read, stage 0's fragments read and its B fragments made
+    clear_correction();
     load_a(0, 0);
     load_b(0, 0);
     load_a(1, 1);
@@ -249,9 +305,10 @@ void tile_w4_kernel(Problem p) {
     for (int k = 0; k < 2 * 4; ++k) dequant_piece(0, k);
 
     // stage s = s0 + u: wait for the loads of stage s - 4 and earlier, barrier, then the 16 MFMAs
-    // of stage s with, between them: the direct loads of stage s + 6 (and at u % 4 == 2 the group
-    // after next), at u % 4 == 2 the read of the next group's codes, the activation fragments of
-    // stage s + 1 and its B fragments
+    // of stage s with, between them: (first stage of a group) the previous group scaled into the
+    // accumulators, tile by tile; the direct loads of stage s + 6 (and at u % 4 == 2 the group
+    // after next), at u % 4 == 2 the read of the next group's codes and scales, the activation
+    // fragments of stage s + 1 and its B fragments
     const int nsteps = (nst + W4_UNROLL - 1) / W4_UNROLL * W4_UNROLL;
     for (int s0 = 0; s0 < nsteps; s0 += W4_UNROLL) {
 #pragma unroll
@@ -262,12 +319,21 @@ void tile_w4_kernel(Problem p) {
             else
                 GE_WAIT_VM(w4_inflight(0));
             lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
             const int dn = (u + 1) & (W4_UNROLL - 1);
+            const bool first = (u & 3) == 0;           // first stage of a group
+            const bool apply = first && s > 0;         // group s / 4 - 1 is complete
+            if (apply) write_sb(s / 4 - 1, ((u >> 2) + 1) & 1);
+            if (first && s > 0 && (s / 4) % W4_CHUNK == 0) correction();  // a chunk of groups is complete
+            // one barrier later every wave has read it, and the next chunk's first writes (end of
+            // this group's last stage) are still to come
+            if (u == 1 && s0 > 0 && s0 % (4 * W4_CHUNK) == 0) clear_correction();
 #pragma unroll
             for (int q = 0; q < W4_MT * W4_NT; ++q) {
                 const int i = q & (W4_MT - 1), j = q / W4_MT;
-                mfma_f16_acc(acc[i][j], fb[u & 1][j], fa[u & 1][i]);
-                asm volatile("" ::: "memory");
+                if (q == 0) row_read(u);
+                if (apply) apply_tile(((u >> 2) + 1) & 1, i, j);
+                U[i][j] = mfma_bf16(fb[u & 1][j], fa[u & 1][i], first ? f32x4{0.f, 0.f, 0.f, 0.f} : U[i][j]);
                 if (q == 0) {
                     load_a(s + W4_AD, (u + W4_AD) & (W4_UNROLL - 1));
                     if ((u & 3) == 2) {
@@ -275,19 +341,30 @@ void tile_w4_kernel(Problem p) {
                         read_group(((u + 2) >> 2) & 1);  // group (s + 2) / 4, loaded at stage s - 4
                     }
                 }
+                if (q == W4_MT * W4_NT - 1) row_sums();
                 if (q >= 1 && q <= W4_MT) read_a(dn, q - 1);
-                if (q >= W4_MT) dequant_piece(dn, q - W4_MT);
-                asm volatile("" ::: "memory");
+                dequant_piece(dn, q);  // 8 pieces: one per MFMA
+                // keep each MFMA with the work placed beside it (the scheduler would otherwise
+                // bunch the MFMAs and the reads and move them across the stage barriers)
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if ((u & 3) == 3) write_sx(s / 4);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #undef GE_WAIT_VM
     __builtin_amdgcn_s_waitcnt(0);
-    mfma_drain();
+    // the last group (stage nsteps - 4 .. nsteps - 1) and the last chunk's correction
+    {
+        const int g = nsteps / 4 - 1;  // odd: nsteps is a multiple of 8
+        write_sb(g, 1);
 #pragma unroll
-    for (int i = 0; i < W4_MT; ++i)
+        for (int i = 0; i < W4_MT; ++i)
 #pragma unroll
-        for (int j = 0; j < W4_NT; ++j) asm volatile("" : "+a"(acc[i][j]));
+            for (int j = 0; j < W4_NT; ++j) apply_tile(1, i, j);
+        lds_barrier();
+        correction();
+    }
 
     const EpiArgs &e = p.epi;
     const int mbase = m0 + frow;
@@ -319,34 +396,21 @@ void tile_w4_kernel(Problem p) {
     });
 }
 
-// X (bf16, [M][K] with row stride lda) -> dense fp16 [M][K]: exact for |x| in the fp16 normal range
-__global__ __launch_bounds__(256) void a16_convert_kernel(int32_t M, int32_t K, const uint16_t *A, int64_t lda,
-                                                          uint16_t *A16) {
-    const int64_t cpr = K / 8, chunks = (int64_t)M * cpr;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-        const int64_t m = c / cpr, kc = c - m * cpr;
-        const u32x4 w = *(const u32x4 *)(A + m * lda + kc * 8);
-        *(u32x4 *)(A16 + m * K + kc * 8) = bf16x8_to_f16x8(w);
-    }
-}
-
 }  // namespace
 
 bool tile_w4_supported(const Problem &p) {
     if (p.mode != MODE_W4 || !p.w4_packed || p.M <= 16) return false;
     if ((p.N % W4_BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
     if (p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
-    if ((int64_t)p.M * p.K * 2 >= (1ll << 31)) return false;  // the fp16 copy of X
+    if (((int64_t)(p.M - 1) * p.lda + p.K) * 2 >= (1ll << 31)) return false;  // X through 32-bit offsets
     if ((int64_t)p.K * p.N / 2 >= (1ll << 31) || ((int64_t)(p.K / 128) * p.ld_s + p.N) * 2 >= (1ll << 31)) return false;
     return epi_ok(p);
 }
 
-int64_t tile_w4_scratch_bytes(const Problem &p) { return (int64_t)p.M * p.K * 2; }
-
-const char *tile_w4_kernel_name() { return "tile_w4_f16_128x128x32"; }
+const char *tile_w4_kernel_name() { return "tile_w4_bf16_64x128x32"; }
 
 hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
-    if (!tile_w4_supported(p) || !p.A16) return hipErrorInvalidValue;
+    if (!tile_w4_supported(p)) return hipErrorInvalidValue;
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -354,10 +418,6 @@ hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t chunks = (int64_t)p.M * (p.K / 8);
-    const int cblocks = (int)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
-    hipLaunchKernelGGL(a16_convert_kernel, dim3(cblocks), dim3(256), 0, s, p.M, p.K, (const uint16_t *)p.A, p.lda,
-                       (uint16_t *)p.A16);
     const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4_BN);
     hipLaunchKernelGGL(tile_w4_kernel, dim3(tiles), dim3(T_THREADS), W4_LDS, s, p);
     return hipGetLastError();

@@ -41,10 +41,9 @@
  * Plans are immutable once made: one plan may be used from several threads
  * and streams at once, with one exception: a plan that owns device scratch
  * (gemm_epi_plan_scratch_bytes() > 0: 8-bit weight plans with M <= 16 whose
- * K is split over workgroups, bf16 generic plans with M <= 16 whose K is
- * split the same way (stream-K), and prepacked int4 plans with M > 16, which
- * convert X to fp16 into it) must not run on two streams at once, since its
- * launches share that scratch.
+ * K is split over workgroups, and bf16 generic plans with M <= 16 whose K is
+ * split the same way (stream-K)) must not run on two streams at once, since
+ * its launches share that scratch.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
@@ -121,10 +120,11 @@ typedef int32_t ge_status;
  *            either M <= 32, N % 16 == 0, group in {32, 64, 128}, or N % 128
  *            == 0, group == 128; the unfused entry points take raw weights
  *            and reject such plans.
- *            For M > 16 the product runs in fp16: x and the dequantised
- *            weights must lie in the fp16 range (|v| < 65504; below 2^-14
- *            they lose precision).  The weights are exact for zero_point 8;
- *            other zero points round them by at most 2^-12 relative.
+ *            The fused int4 kernels take every finite bf16 x and scale:
+ *            codes enter the products as exact bf16 integers, scales as
+ *            their exact bf16 values, and all sums (and the scaling of each
+ *            group's partial sums) are carried out in fp32; nothing passes
+ *            through fp16.
  *   W4 with 8-bit codes: b = U8 (W = (q - zero_point) * s, zero_point in
  *            [0, 255]) or FP8E4M3 (W = e4m3(q) * s, zero_point 0; NaN codes
  *            give NaN), Wq [K, N] bytes with ldb >= N, scales [K/group, N]
@@ -158,15 +158,14 @@ GE_API void ge_desc_init(ge_desc *d);
  * *out receives a library-owned plan that the caller releases with
  * gemm_epi_plan_destroy().  Queries the current device (architecture and
  * compute-unit count); allocates host memory, and a zeroed device scratch
- * for three kinds of plan: 8-bit weight plans with M <= 16 whose column
+ * for two kinds of plan: 8-bit weight plans with M <= 16 whose column
  * blocks alone do not fill the GPU (the cross-workgroup K split: S *
  * ceil(N/128) * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters,
  * S in {2, 4, 8}); bf16 generic plans with M <= 16 whose column blocks leave
  * CUs idle and whose (column block, 32-row K block) units divide evenly into
  * one K piece of one column block per CU (stream-K: the same tiles and
  * counters, S = pieces per block in {2..8}; e.g. 16 x 8192 x 8192 on 256
- * CUs, S = 4); and prepacked int4 plans with M > 16 (the fp16 copy of X,
- * M * K * 2 bytes).  Such a call waits for the zeroing of its scratch on a
+ * CUs, S = 4).  Such a call waits for the zeroing of its scratch on a
  * stream of the library's own (the callers' streams keep running); device
  * allocation is not allowed during graph capture, so make such plans before
  * capturing (the call fails with GE_ERR_HIP and says so otherwise).

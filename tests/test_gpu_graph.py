@@ -87,9 +87,10 @@ def _scratch_inputs(seed):
 
 
 def test_scratch_using_calls_replay_in_a_graph():
-    # calls whose plans own device scratch: the 8-bit K split (tile handoff, counters that re-arm
-    # themselves), the int4 tile path (activation pre-pass into scratch) and the SwiGLU launch
-    # whose partial last round is peeled into 128 x 128 tiles, and the stream-K decode kernel
+    # calls whose plans own device scratch (the 8-bit K split: tile handoff, counters that re-arm
+    # themselves; the stream-K decode kernel), the int4 tile kernel (per-group partial products and
+    # the correction product through LDS) and the SwiGLU launch whose partial last round is peeled
+    # into 128 x 128 tiles
     g = torch.Generator().manual_seed(9)
     x8, x4, xs = _scratch_inputs(2)
     Wq8 = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
@@ -122,7 +123,7 @@ def test_scratch_using_calls_replay_in_a_graph():
     assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1].startswith("tile_w4")
     assert kernels[2] == "tile_swiglu_256x128x32+128x128x32"
     assert kernels[3] == "skinny_bf16_m16_128col_streamk"
-    assert all(f._plan.scratch_bytes > 0 for f in eager[:2] + eager[3:])
+    assert eager[0]._plan.scratch_bytes > 0 and eager[3]._plan.scratch_bytes > 0
     for f in eager + graph_calls:
         f()
     torch.cuda.synchronize()

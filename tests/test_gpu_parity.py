@@ -464,15 +464,17 @@ def test_w4_prepacked_ragged(M, N, K):
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M", [16, 17, 32])
 @pytest.mark.parametrize("group", [32, 64])
-def test_w4_prepacked_group_sizes(group):
+def test_w4_prepacked_group_sizes(group, M):
+    # M 17 .. 32: each weight fragment feeds two 16-row tiles of X (the group-32 variant included)
     import dataclasses
-    w = dataclasses.replace(workloads.WORKLOADS["w4a16_m16"], M=16, N=256, K=512, group=group)
-    inp = workloads.make_inputs(w, seed=group)
+    w = dataclasses.replace(workloads.WORKLOADS["w4a16_m16"], M=M, N=256, K=512, group=group)
+    inp = workloads.make_inputs(w, seed=group + M)
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed group {group}")
 
 
-@pytest.mark.parametrize("M", [16, 96])
+@pytest.mark.parametrize("M", [16, 17, 32, 96])
 def test_w4_prepacked_lo_first_and_zero_point(M):
     w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=128, K=256)
     inp = workloads.make_inputs(w, seed=7)
@@ -482,8 +484,9 @@ def test_w4_prepacked_lo_first_and_zero_point(M):
     assert_close(_w4_packed(inp, lo_first=True), ref, TOL_BF16, "packed lo_first zp3")
 
 
-def test_w4_prepacked_one_hot_rows_bit_exact():
-    K, N, M = 1024, 512, 16
+@pytest.mark.parametrize("M", [16, 32])
+def test_w4_prepacked_one_hot_rows_bit_exact(M):
+    K, N = 1024, 512
     Wq = workloads.uniform_bytes((K, N // 2), wid=102, tid=1)
     scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
     ks = np.arange(M) * 61 % K
@@ -514,13 +517,14 @@ def test_w4_prepacked_tile_path(M, N, K):
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 
-def test_w4_tile_plan_scratch_is_rewritten_every_call():
-    # the int4 tile path converts X into the plan's fp16 scratch on every call: two calls on one
-    # plan with different X, each against the oracle, then the first X again, bitwise as before
+def test_w4_tile_plan_owns_no_scratch_and_repeats_bitwise():
+    # the int4 tile kernel reads X directly (bf16) and keeps its per-group partial products and the
+    # zero-point correction on chip: no plan scratch; a second X on the same plan, then the first
+    # again, bitwise as before
     M, N, K = 200, 384, 1024
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
-    assert p.kernel.startswith("tile_w4") and p.scratch_bytes == M * K * 2
+    assert p.kernel.startswith("tile_w4") and p.scratch_bytes == 0
     a, b = workloads.make_inputs(w, seed=31), workloads.make_inputs(w, seed=32)
     b["Wq"], b["scales"], b["bias"] = a["Wq"], a["scales"], a["bias"]
     oa = _w4_packed(a)
@@ -528,6 +532,57 @@ def test_w4_tile_plan_scratch_is_rewritten_every_call():
     assert_close(oa, oracle.reference(a), TOL_BF16, "first X")
     assert_close(ob, oracle.reference(b), TOL_BF16, "second X")
     assert torch.equal(_w4_packed(a).view(torch.int16), oa.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 128, 128), (64, 256, 8576), (100, 128, 4224), (65, 384, 12288)])
+def test_w4_tile_path_k_chunks(M, N, K):
+    # the zero-point correction product runs once per 32 groups: one group; 67 groups (two full
+    # chunks and a partial one, an odd group count); 33 groups; 96 groups
+    w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + K)
+    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel.startswith("tile_w4")
+    assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("xmag,smag", [(1e5, 0.01), (3e4, 0.01), (1e-6, 0.01), (1.0, 3e4), (1.0, 1e-7),
+                                       (1e-30, 1e20), (1e25, 1e-20)])
+def test_w4_tile_path_any_finite_range(xmag, smag):
+    # activations and scales far outside the fp16 range (or below its normal range): the tile
+    # kernel works in bf16 with fp32 accumulation, so every finite input gives the oracle's result
+    # within the bf16 tolerance; the sign pattern and magnitudes vary per element
+    M, N, K = 96, 256, 1024
+    w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=int(abs(np.log10(xmag * smag))) + 7)
+    x = workloads.bf16_bits_to_f32(inp["X"]).astype(np.float64) * xmag
+    sc = workloads.bf16_bits_to_f32(inp["scales"]).astype(np.float64) / 0.0125 * smag
+    inp["X"] = workloads.f32_to_bf16_bits(x.astype(np.float32))
+    inp["scales"] = workloads.f32_to_bf16_bits(sc.astype(np.float32))
+    inp["bias"] = None
+    ref = oracle.reference(inp)
+    out = to_host(_w4_packed(inp))
+    assert np.all(np.isfinite(out))
+    scale = np.max(np.abs(ref))
+    # compared on the scale of the result (bf16 tolerance relative to the largest output)
+    assert np.max(np.abs(out - ref)) <= 1e-2 * scale, (np.max(np.abs(out - ref)), scale)
+    assert_close(out / scale, ref / scale, TOL_BF16, f"x ~ {xmag}, s ~ {smag}")
+
+
+@pytest.mark.parametrize("M", [33, 96, 130])
+def test_w4_tile_path_one_hot_rows_bit_exact(M):
+    # one-hot rows of X select single codes: (128 + c) * 2^-6 from the product, -(128 + 8) * 2^-6 from
+    # the correction, both exact, so D = (c - 8) * 2^-6 exactly
+    K, N = 1024, 256
+    Wq = workloads.uniform_bytes((K, N // 2), wid=103, tid=1)
+    scales = workloads.f32_to_bf16_bits(np.full((K // 128, N), 2.0 ** -6, np.float32))
+    ks = np.arange(M) * 61 % K
+    X = np.zeros((M, K), np.float32)
+    X[np.arange(M), ks] = 1.0
+    p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, prepacked=True)
+    assert p.kernel.startswith("tile_w4")
+    Wp = ge.w4_prepack(torch.from_numpy(Wq).to(DEV))
+    out = to_host(ge.w4_gemm(to_dev(workloads.f32_to_bf16_bits(X)), Wp, to_dev(scales), prepacked=True))
+    codes = oracle.w4_unpack(Wq, N).astype(np.int64)
+    assert np.array_equal(out, (codes[ks] - 8) * 2.0 ** -6)
 
 
 def test_w4_prepacked_tile_one_hot_rows_bit_exact():
