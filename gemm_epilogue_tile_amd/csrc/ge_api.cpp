@@ -116,7 +116,8 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     if (pl->scratch && (split_use || sk_use)) {
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
-        p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - (size_t)((d.N + 127) / 128) * 4);
+        const size_t counters = split_use ? (size_t)split_counters(p) : (size_t)((d.N + 127) / 128);
+        p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - counters * 4);
     }
     if (pl->kind != GE_KIND_SWIGLU) {
         if ((d.flags & GE_FLAG_C) && d.beta != 0.0f) f |= GE_FLAG_C;
@@ -394,15 +395,15 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
                              (const void *)256, (const void *)256, (const void *)256, (void *)256);
     pl.kernel = fused_name(p, pl.cu_count);
 
-    // device scratch: the 8-bit and the bf16 streaming kernels split K over workgroups when the
-    // column blocks alone do not fill the GPU
+    // device scratch: the 8-bit, the int4 and the bf16 streaming kernels split K over
+    // workgroups when the column blocks alone do not fill the GPU
     pl.split = 1;
     pl.scratch_use = SCRATCH_NONE;
     pl.scratch = nullptr;
     pl.scratch_bytes = 0;
     int64_t bytes = 0;
     int32_t use = SCRATCH_NONE;
-    if (kind == GE_KIND_W4 && p.wfmt != WFMT_U4 && skinny_supported(p)) {
+    if (kind == GE_KIND_W4 && skinny_supported(p)) {
         const int split = w8_split(p, pl.cu_count);
         if (split > 1) {
             bytes = w8_split_scratch_bytes(p, split);

@@ -12,6 +12,19 @@ namespace ge {
 enum Mode : int32_t { MODE_GENERIC = 0, MODE_SWIGLU = 1, MODE_W4 = 2 };
 enum WFmt : int32_t { WFMT_U4 = 0, WFMT_U8 = 1, WFMT_FP8 = 2 };
 
+// Prepacked int4 layout (gemm_w4_prepack): 128-column blocks (outer), 128-row
+// groups, then the block's 16-column tiles (inner), one 1 KiB fragment each
+// (64 lanes x 16 bytes); the last block of a width that is not a multiple of
+// 128 holds the remaining tiles.  A block's groups are thus one contiguous run,
+// and its eight tiles of one group are 8 KiB in a row.  Byte offset of the
+// fragment of tile t, group g:
+constexpr int W4P_BLOCK_TILES = 8;
+__host__ __device__ inline int64_t w4p_frag_offset(int64_t t, int64_t g, int64_t ngroups, int64_t ntiles) {
+    const int64_t b = t / W4P_BLOCK_TILES;
+    const int64_t ntb = ntiles - W4P_BLOCK_TILES * b < W4P_BLOCK_TILES ? ntiles - W4P_BLOCK_TILES * b : W4P_BLOCK_TILES;
+    return (b * ngroups * W4P_BLOCK_TILES + g * ntb + t % W4P_BLOCK_TILES) * 1024;
+}
+
 // A fully described product + epilogue, pointers included.
 struct Problem {
     int32_t M, N, K;
@@ -78,10 +91,13 @@ bool skinny_supported(const Problem &p);
 hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s);
 // scratch: the plan may own device scratch (false: the variants that need none)
 const char *skinny_kernel_name(const Problem &p, int cu_count, bool scratch = true);
-// K splits of the 8-bit streaming kernel and the scratch bytes they need
-// (tiles, then counters that must start at zero; the kernel re-arms them).
+// K splits of the 8-bit and the 128-column int4 streaming kernels and the
+// scratch bytes they need (tiles, then counters that must start at zero; the
+// kernel re-arms them).
 int w8_split(const Problem &p, int cu_count);
 int64_t w8_split_scratch_bytes(const Problem &p, int split);
+// counters (column blocks) at the end of that scratch
+int split_counters(const Problem &p);
 // Stream-K bf16 decode kernel: tile slots per column block (0: the plain kernel) and the
 // scratch bytes they need (tiles, then counters that must start at zero).  It is launched
 // when p.split > 1 with p.split_ws / p.split_cnt set, on cu_count workgroups.

@@ -442,14 +442,27 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
 
 // Four bf16 pairs (a B fragment, k in order) from one packed dword of 8 codes:
 // pair q = (code at nibble q, code at nibble q + 4), each as bf16 128 + code.
-__device__ __forceinline__ bf16x8 unpack_w4(uint32_t w) {
-    u32x4 f;
-    f[0] = (w & 0x000f000fu) | 0x43004300u;
-    f[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-    f[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-    f[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
-    return __builtin_bit_cast(bf16x8, f);
-}
+// (w >> 4q) & 0x000f000f | 0x43004300 is one v_and_or_b32 per pair when the
+// mask sits in a scalar register and the magic in a vector one (that encoding
+// takes no literal operand; with both as literals the compiler spends an AND
+// and an OR): 7 instructions per 8 codes.  The two constants are hidden from
+// constant folding by empty asm statements; the arithmetic itself stays
+// ordinary code, so the compiler's hazard handling around the MFMAs that read
+// the result still applies.
+struct W4Unpack {
+    uint32_t mask, magic;
+    __device__ __forceinline__ W4Unpack() {
+        mask = 0x000f000fu;
+        magic = 0x43004300u;
+        asm volatile("" : "+s"(mask));
+        asm volatile("" : "+v"(magic));
+    }
+    __device__ __forceinline__ uint32_t pair(uint32_t src) const { return (src & mask) | magic; }
+    __device__ __forceinline__ bf16x8 operator()(uint32_t w) const {
+        const u32x4 f = {pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12)};
+        return __builtin_bit_cast(bf16x8, f);
+    }
+};
 
 // NTW 16-column tiles per workgroup; W4_WAVES waves split the 128-row packing
 // groups.  SPG: 32-deep blocks per scale group (group size / 32 = 1, 2 or 4).
@@ -499,6 +512,7 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
     const uint32_t nz = f32_to_bf16(-(128.0f + (float)p.zero_point));
     const uint32_t nz2 = nz | (nz << 16);
     const bf16x8 negz = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
+    const W4Unpack unpack_w4;
 
     f32x4 tot[MT][NTW];
 #pragma unroll
@@ -525,7 +539,7 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
 #pragma unroll
             for (int t = 0; t < NTW; ++t) {
                 const bool tin = gin && nt0 + t < ntiles;
-                w[j][t] = bload16(rw, tin ? (uint32_t)((((int64_t)(nt0 + t) * ngroups + gi) * 64 + lane) * 16) : OOB);
+                w[j][t] = bload16(rw, tin ? (uint32_t)(w4p_frag_offset(nt0 + t, gi, ngroups, ntiles) + lane * 16) : OOB);
                 const int n = n0 + 16 * t + i;
 #pragma unroll
                 for (int sg = 0; sg < NSG; ++sg)
@@ -653,6 +667,142 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
         }
     });
     if (threadIdx.x == 0) __hip_atomic_store(p.split_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+#ifndef GE_W4S_RING
+#define GE_W4S_RING 2
+#endif
+#ifndef GE_W4S_CODE_POLICY
+#define GE_W4S_CODE_POLICY 0
+#endif
+constexpr int W4S_RING = GE_W4S_RING;
+constexpr int W4S_CODE_POLICY = GE_W4S_CODE_POLICY;
+
+// int4 weights (prepacked, 128-row groups), M <= 16, K split over workgroups.
+// A workgroup owns one block of NTW prepacked 16-column tiles and 1/NS of K;
+// its 8 waves split that range by whole groups, and a wave streams its groups
+// through a ring of two: the codes (NTW x 16 bytes per lane), activations
+// (4 x 16 bytes) and scales of the group after next are requested as soon as
+// a group has been consumed.  With several groups per wave the requests of
+// the whole GPU reach memory in group order, so the dequantisation of the
+// first groups runs while later ones are still arriving instead of all of it
+// after the last byte (at 16 x 8192 x 8192: 64-column blocks, NS = 2, four
+// groups per wave).  Against 32-column workgroups over the whole of K, each
+// activation byte read from L2 serves twice as many weight bytes.
+// Per group and tile the sum of x * (c - z) is -(128 + z) * sum(x) (four MFMAs
+// against a constant fragment, computed first) plus x * (128 + c) (four
+// MFMAs accumulating onto it), times the tile's scales, into fp32 totals.
+template <int NTW, int NS, int NWV>
+__global__ __launch_bounds__(64 * NWV) void skinny_w4s_kernel(Problem p) {
+    static_assert(W4P_BLOCK_TILES % NTW == 0, "a workgroup's tiles lie in one block of the prepacked layout");
+    constexpr int NC = 16 * NTW, MR = 16;
+    constexpr bool SPLIT = NS > 1;
+    __shared__ __attribute__((aligned(16))) float red[NWV * MR * NC];
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int ncb = (int)gridDim.x / NS;
+    const int cb = (int)blockIdx.x % ncb;
+    const int ks = (int)blockIdx.x / ncb;
+    const int n0 = cb * NC, nt0 = cb * NTW;
+
+    const int ngroups = p.K / 128;
+    const int nvw = NS * NWV;
+    const int per = (ngroups + nvw - 1) / nvw;
+    const int g0 = (ks * NWV + wave) * per, g1 = min(ngroups, g0 + per);
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.B, (int64_t)p.K * p.N / 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scales, ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2);
+    // lane parts of the offsets; a group's part is uniform (groups past the wave's share read
+    // zeros: lane part OOB, uniform part 0)
+    const uint32_t vx = i < p.M ? (uint32_t)((i * p.lda + 8 * g) * 2) : OOB;
+    const uint32_t vw = (uint32_t)(lane * 16);
+    const uint32_t vs = (uint32_t)((n0 + i) * 2);
+    // the workgroup's first tile in its block of the prepacked layout (every block is whole)
+    const uint32_t blk = (uint32_t)(((int64_t)(nt0 / W4P_BLOCK_TILES) * ngroups * W4P_BLOCK_TILES +
+                                     nt0 % W4P_BLOCK_TILES) * 1024);
+
+    const uint32_t nz = f32_to_bf16(-(128.0f + (float)p.zero_point));
+    const uint32_t nz2 = nz | (nz << 16);
+    const bf16x8 negz = __builtin_bit_cast(bf16x8, u32x4{nz2, nz2, nz2, nz2});
+    const W4Unpack unpack_w4;
+
+    f32x4 tot[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) tot[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    bf16x8 x[W4S_RING][4];
+    u32x4 w[W4S_RING][NTW];
+    uint32_t sr[W4S_RING][NTW / 2];  // scales of columns 16 t + i, two per register
+    auto load = [&](int gi, int slot) {
+        const bool in = gi < g1;
+        const uint32_t lx = in ? vx : OOB, lw = in ? vw : OOB, ls = in ? vs : OOB;
+        // codes first: they come from memory, the activations mostly from L2
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+            w[slot][t] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rw, lw, in ? (uint32_t)(blk + gi * (W4P_BLOCK_TILES * 1024) + t * 1024) : 0u,
+                           W4S_CODE_POLICY));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            x[slot][kb] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, lx, in ? (uint32_t)(gi * 256 + kb * 64) : 0u, 0));
+        const uint32_t so = in ? (uint32_t)(gi * p.ld_s * 2) : 0u;
+#pragma unroll
+        for (int t = 0; t < NTW; t += 2) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, ls, so + t * 32, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, ls, so + t * 32 + 32, 0);
+            sr[slot][t / 2] = lo | (hi << 16);
+        }
+    };
+    auto consume = [&](int slot) {
+        f32x4 corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) corr = mfma_bf16(x[slot][kb], negz, corr);
+        f32x4 u[NTW];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t)
+                u[t] = mfma_bf16(x[slot][kb], unpack_w4(w[slot][t][kb]), kb == 0 ? corr : u[t]);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const float sv = (t & 1) ? bf16hi(sr[slot][t / 2]) : bf16lo(sr[slot][t / 2]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tot[t][q] = fmaf(sv, u[t][q], tot[t][q]);
+        }
+    };
+
+    // ring of W4S_RING groups: group j sits in slot j % W4S_RING
+    load(g0, 0);
+#pragma unroll
+    for (int u = 1; u < W4S_RING; ++u)
+        if (g0 + u < g1) load(g0 + u, u);
+    for (int j0 = g0; j0 < g1; j0 += W4S_RING) {
+#pragma unroll
+        for (int u = 0; u < W4S_RING; ++u) {
+            const int gi = j0 + u;
+            if (gi < g1) {
+                consume(u);
+                if (gi + W4S_RING < g1) load(gi + W4S_RING, u);
+            }
+        }
+    }
+
+    // partial tile -> LDS: lane (g, i) holds rows 4 g + e, column 16 t + i
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) red[(wave * MR + 4 * g + e4) * NC + 16 * t + i] = tot[t][e4];
+    __syncthreads();
+    if constexpr (SPLIT)
+        split_reduce_epilogue<MR, NC, NS, NWV>(p, red, n0, cb, ks, ncb, &s_last);
+    else
+        reduce_epilogue<MR, NC, NWV>(p, red, n0);
 }
 
 // A lane reads, per 32-deep block, 8 consecutive rows of one 8-column chunk
@@ -839,7 +989,7 @@ __global__ __launch_bounds__(256) void w4_prepack_kernel(int32_t K, int32_t N, c
             }
             out[kb] = d;
         }
-        *(u32x4 *)(Wp + ((nt * ngroups + gi) * 64 + l) * 16) = out;
+        *(u32x4 *)(Wp + w4p_frag_offset(nt, gi, ngroups, ntiles) + l * 16) = out;
     }
 }
 
@@ -903,9 +1053,11 @@ bool skinny_supported(const Problem &p) {
                ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
     }
     if (p.mode == MODE_W4) {
+        // codes, scales and activations through 32-bit buffer offsets
         return p.w4_packed && p.M <= 32 && (p.K % 128) == 0 && (p.N % 16) == 0 && al16(p.B) &&
                (p.group == 32 || p.group == 64 || p.group == 128) &&
-               ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31);
+               ((int64_t)(p.M - 1) * p.lda + p.K) * 2 < (1ll << 31) && (int64_t)p.K * p.N / 2 < (1ll << 31) &&
+               ((int64_t)(p.K / p.group - 1) * p.ld_s + p.N) * 2 < (1ll << 31);
     }
     if (p.b_layout != GE_LAYOUT_KN || !al16(p.B) || (p.ldb & 7) || (p.N & 7)) return false;
     // the streaming loop addresses one wave's share of W at a time: at most ceil(K / 32 / 8)
@@ -944,20 +1096,33 @@ void launch_bf16(const Problem &p, int nch, hipStream_t s) {
 }
 }  // namespace
 
-// K splits of the 8-bit kernel: the fewest (a power of two, at most 8) that
-// give every CU a workgroup, while each wave keeps at least one scale group.
+// The int4 decode kernel over 64-column blocks (prepacked 128-row groups, M <= 16).
+constexpr int W4S_NTW = 8, W4S_WAVES = 8, W4S_MAX_SPLIT = 8;
+bool w4s_ok(const Problem &p) {
+    return p.mode == MODE_W4 && p.wfmt == WFMT_U4 && p.w4_packed && p.group == 128 && p.M <= 16 &&
+           p.N % (16 * W4S_NTW) == 0;
+}
+
+// K splits of the 8-bit and the 128-column int4 kernels: the fewest (a power
+// of two, at most 8) that give every CU a workgroup, while each wave keeps at
+// least one scale group (int4: one 128-row group).
 int w8_split(const Problem &p, int cu_count) {
-    if (p.mode != MODE_W4 || p.wfmt == WFMT_U4) return 1;
-    const int ncb = (p.N + 127) / 128, nkb = p.K / 32, gb = p.group / 32;
+    if (p.mode != MODE_W4 || (p.wfmt == WFMT_U4 && !w4s_ok(p))) return 1;
+    const bool u4 = p.wfmt == WFMT_U4;
+    const int ncb = split_counters(p), nkb = p.K / 32, gb = u4 ? 4 : p.group / 32;
+    const int max_split = u4 ? W4S_MAX_SPLIT : 8, waves = u4 ? W4S_WAVES : S_WAVES;
     int s = 1;
-    while (s < 8 && (int64_t)ncb * s < cu_count && nkb / (2 * s * S_WAVES) >= gb) s *= 2;
+    while (s < max_split && (int64_t)ncb * s < cu_count && nkb / (2 * s * waves) >= gb) s *= 2;
     return s;
 }
 
+// column blocks of the split kernels: one counter and one [16][block width] fp32 tile per split each
+int split_counters(const Problem &p) { return w4s_ok(p) ? p.N / (16 * W4S_NTW) : (p.N + 127) / 128; }
+
 int64_t w8_split_scratch_bytes(const Problem &p, int split) {
     if (split <= 1) return 0;
-    const int64_t ncb = (p.N + 127) / 128;
-    return split * ncb * 16 * 128 * 4 + ncb * 4;
+    const int64_t ncb = split_counters(p), nc = w4s_ok(p) ? 16 * W4S_NTW : 128;
+    return split * ncb * 16 * nc * 4 + ncb * 4;
 }
 
 // Tile slots per column block of the stream-K decode kernel, or 0 for the plain kernel.
@@ -1011,7 +1176,16 @@ const char *skinny_kernel_name(const Problem &p, int cu_count, bool scratch) {
         const int s = scratch ? w8_split(p, cu_count) : 1;
         return (p.w4_packed ? packed_names : names)[p.wfmt == WFMT_FP8][s == 1 ? 0 : s == 2 ? 1 : s == 4 ? 2 : 3];
     }
-    if (p.mode == MODE_W4) return p.M <= 16 ? "skinny_w4_m16_32col" : "skinny_w4_m32_32col";
+    if (p.mode == MODE_W4) {
+        if (w4s_ok(p)) {
+            const int sp = w8_split(p, cu_count);
+            if (sp == 1) return "skinny_w4_m16_128col";
+            if (scratch)
+                return sp == 2 ? "skinny_w4_m16_128col_split2" : sp == 4 ? "skinny_w4_m16_128col_split4"
+                                                                    : "skinny_w4_m16_128col_split8";
+        }
+        return p.M <= 16 ? "skinny_w4_m16_32col" : "skinny_w4_m32_32col";
+    }
     if (p.b_packed)
         return scratch && bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
                : p.M <= 16                    ? "skinny_bf16_m16_128col_prepacked"
@@ -1045,6 +1219,25 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
         else
             go(std::integral_constant<int, WFMT_U8>{});
         return hipGetLastError();
+    }
+    if (p.mode == MODE_W4 && w4s_ok(p)) {
+        // the split the plan chose, with its scratch; without scratch the 32-column kernel
+        // below, unless the shape needs no split
+        const int ns = (p.split_ws && p.split_cnt) ? p.split : 1;
+        if (ns > 1 || w8_split(p, cu_count > 0 ? cu_count : 256) == 1) {
+            if (ns != 1 && ns != 2 && ns != 4 && ns != 8) return hipErrorInvalidValue;
+            const dim3 grid(split_counters(p) * ns);
+            const dim3 block(64 * W4S_WAVES);
+            if (ns == 8)
+                hipLaunchKernelGGL((skinny_w4s_kernel<W4S_NTW, 8, W4S_WAVES>), grid, block, 0, s, p);
+            else if (ns == 4)
+                hipLaunchKernelGGL((skinny_w4s_kernel<W4S_NTW, 4, W4S_WAVES>), grid, block, 0, s, p);
+            else if (ns == 2)
+                hipLaunchKernelGGL((skinny_w4s_kernel<W4S_NTW, 2, W4S_WAVES>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_w4s_kernel<W4S_NTW, 1, W4S_WAVES>), grid, block, 0, s, p);
+            return hipGetLastError();
+        }
     }
     if (p.mode == MODE_W4) {
         constexpr int NTW = 2;

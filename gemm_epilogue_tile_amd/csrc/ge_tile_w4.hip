@@ -142,12 +142,18 @@ void tile_w4_kernel(Problem p) {
     const int64_t b_bytes = (int64_t)p.K * p.N / 2, s_bytes = ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2;
     uint32_t b_src[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) b_src[q] = (uint32_t)((((int64_t)(n0 / 16 + wave * 2 + q) * ngroups) * 64 + lane) * 16);
+    for (int q = 0; q < 2; ++q) {
+        // tile tt of the prepacked layout's 128-column block n0 / 128 (N is a multiple of 128, so
+        // every block is whole): a group's eight tiles are 8 KiB in a row
+        const int tt = wave * 2 + q;
+        b_src[q] = (uint32_t)(((int64_t)(n0 / 128) * ngroups * W4P_BLOCK_TILES + tt) * 1024 + lane * 16);
+    }
     const uint32_t s_src = lane < 4 ? (uint32_t)((n0 + wave * 32) * 2 + lane * 16) : OOB;
     const uint32_t codes_w = W4_CODES + wave * W4_CODES_WAVE, scales_w = W4_SCALES + wave * W4_SCALES_WAVE;
     auto load_b = [&](int g, int slot) {
         const bool in = g < ngroups;
-        const i32x4 rb = rsrc32((const char *)p.B + (int64_t)g * 1024, in ? (uint32_t)(b_bytes - (int64_t)g * 1024) : 0u);
+        const int64_t go = (int64_t)g * W4P_BLOCK_TILES * 1024;
+        const i32x4 rb = rsrc32((const char *)p.B + go, in ? (uint32_t)(b_bytes - go) : 0u);
 #pragma unroll
         for (int q = 0; q < 2; ++q) load_lds16(rb, lds0 + codes_w + slot * 2048 + q * 1024, b_src[q]);
         const int64_t so = (int64_t)g * p.ld_s * 2;
@@ -177,16 +183,16 @@ void tile_w4_kernel(Problem p) {
     bf16x8 fb[2][W4_NT];
     u32x4 dq[W4_NT];
     // (src & mask) | magic in one v_and_or_b32: the mask in a scalar register and the magic in a
-    // vector one, since this instruction takes no literal operand
-    const uint32_t nib_mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
-    uint32_t magic = 0x43004300u;
+    // vector one, since this instruction takes no literal operand (the empty asm statements keep
+    // the compiler from folding them back into literals; the arithmetic stays ordinary code, so the
+    // compiler keeps track of the MFMAs still reading the registers it reuses)
+    uint32_t nib_mask = 0x000f000fu, magic = 0x43004300u;
+    asm volatile("" : "+s"(nib_mask));
     asm volatile("" : "+v"(magic));
     auto dequant_piece = [&](int dd, int k) {
         const int gp = (dd >> 2) & 1, q = dd & 3, e = k >> 2, w = k & 3;
         const uint32_t src = craw[gp][e][q] >> (4 * w);
-        uint32_t t;
-        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t) : "v"(src), "s"(nib_mask), "v"(magic));
-        dq[e][w] = t;
+        dq[e][w] = (src & nib_mask) | magic;
         if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(bf16x8, dq[e]);
     };
 

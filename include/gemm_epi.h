@@ -234,11 +234,15 @@ GE_API ge_status gemm_w4_run(const ge_plan *plan, const void *X, const uint8_t *
  * loader would store quantised weights): reads raw packed int4 weights Wq
  * [K, N/2] (nibble order from the plan's flags, row stride = the plan's ldb)
  * and writes the same K*N/2 bytes to Wp in the kernel-native layout: for each
- * 16-column tile (outer) and 128-row K group (inner), 64 lanes x 16 bytes,
- * lane l holding the codes of column 16*tile + l%16 for k = 128*group +
- * 32*b + 8*(l/16) + j (b = 0..3, one dword per b; code j at bit
- * 4*(j/2) + 16*(j%2)).  Needs N % 16 == 0, K % 128 == 0 and a 16-byte aligned
- * Wp that does not overlap Wq.  Asynchronous on the stream.
+ * 64-column block (outer), 128-row K group, and 16-column tile of the block
+ * (inner; the last block of an N that is not a multiple of 64 holds the
+ * remaining tiles), 1 KiB = 64 lanes x 16 bytes, lane l holding the codes of
+ * column 16*tile + l%16 for k = 128*group + 32*b + 8*(l/16) + j (b = 0..3,
+ * one dword per b; code j at bit 4*(j/2) + 16*(j%2)).  So the fragment of
+ * tile t and group g starts at byte 1024 * (4*ngroups*(t/4) + nt*g + t%4),
+ * nt being the number of tiles in t's block.  Needs N % 16 == 0, K % 128 == 0
+ * and a 16-byte aligned Wp that does not overlap Wq.  Asynchronous on the
+ * stream.
  * For a plan with 8-bit codes (b_type U8 or FP8E4M3) it reads Wq [K, N]
  * bytes (row stride ldb, a multiple of 8, 8-byte aligned) and writes the K*N
  * bytes in the layout the 8-bit decode kernel streams: for each 128-column

@@ -453,15 +453,38 @@ def _w4_packed(inp, **kw):
                       zero_point=inp["zero_point"], prepacked=True, **kw)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (7, 256, 512), (16, 1008, 1024), (16, 4096, 2048),
-                                   (17, 1008, 1024), (25, 272, 512), (32, 4096, 2048)])
-def test_w4_prepacked_ragged(M, N, K):
-    # 17 <= M <= 32: two 16-row tiles of X per weight fragment
+@pytest.mark.parametrize("M,N,K,kernel", [(1, 16, 128, "skinny_w4_m16_32col"), (7, 256, 512, "skinny_w4_m16_128col"),
+                                          (16, 1008, 1024, "skinny_w4_m16_32col"),
+                                          (16, 4096, 2048, "skinny_w4_m16_128col_split2"),
+                                          (17, 1008, 1024, "skinny_w4_m32_32col"), (25, 272, 512, "skinny_w4_m32_32col"),
+                                          (32, 4096, 2048, "skinny_w4_m32_32col")])
+def test_w4_prepacked_ragged(M, N, K, kernel):
+    # 17 <= M <= 32: two 16-row tiles of X per weight fragment; M <= 16 with N a multiple of 128:
+    # 128-column workgroups, K split over workgroups where the column blocks leave CUs idle
     w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
-    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel == \
-        ("skinny_w4_m16_32col" if M <= 16 else "skinny_w4_m32_32col")
+    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel == kernel
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 packed {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (16, 128, 1024, "skinny_w4_m16_128col"),           # one workgroup, one group per wave
+    (9, 640, 2944, "skinny_w4_m16_128col_split2"),     # 23 groups: a wave with one, waves with none
+    (3, 1024, 4096, "skinny_w4_m16_128col_split4"),    # one group per wave
+    (16, 2048, 16384, "skinny_w4_m16_128col_split8"),
+    (16, 128, 24576, "skinny_w4_m16_128col_split8"),   # three groups per wave
+])
+def test_w4_prepacked_128col_split(M, N, K, kernel):
+    w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + K)
+    pl = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
+    assert pl.kernel == kernel and (pl.scratch_bytes > 0) == ("split" in kernel)
+    ref = oracle.reference(inp)
+    for rep in range(3):  # the split counters re-arm themselves: repeated calls agree
+        assert_close(_w4_packed(inp), ref, TOL_BF16, f"w4 128col {M}x{N}x{K} call {rep}")
+    # a plan without device scratch takes the 32-column kernel
+    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True,
+                   no_scratch=True).kernel in ("skinny_w4_m16_32col", "skinny_w4_m16_128col")
 
 
 @pytest.mark.parametrize("M", [16, 17, 32])
@@ -482,6 +505,38 @@ def test_w4_prepacked_lo_first_and_zero_point(M):
                          bias=inp["bias"])
     inp["zero_point"] = 3
     assert_close(_w4_packed(inp, lo_first=True), ref, TOL_BF16, "packed lo_first zp3")
+
+
+def _host_w4_prepack(Wq: np.ndarray, N: int, lo_first: bool) -> np.ndarray:
+    """The documented int4 prepacked layout, built on the host from the unpacked codes: 128-column
+    blocks, then 128-row groups, then the block's 16-column tiles (the last block holds the
+    remaining tiles), each 64 lanes x 16 bytes; lane l, dword q holds the codes of column
+    16 t + l % 16 at k = 128 g + 32 q + 8 (l // 16) + j, code j at bit 4 (j // 2) + 16 (j % 2)."""
+    codes = oracle.w4_unpack(Wq, N, lo_first).astype(np.uint32)  # [K, N]
+    K = codes.shape[0]
+    ngroups, ntiles = K // 128, N // 16
+    out = np.zeros(K * N // 2, np.uint8)
+    lanes = np.arange(64)
+    shifts = np.array([4 * (j // 2) + 16 * (j % 2) for j in range(8)], np.uint32)
+    for t in range(ntiles):
+        b, nb = t // 8, min(8, ntiles - 8 * (t // 8))
+        for g in range(ngroups):
+            frag = np.zeros((64, 4), np.uint32)
+            for q in range(4):
+                ks = 128 * g + 32 * q + 8 * (lanes // 16)[:, None] + np.arange(8)[None, :]  # [64, 8]
+                c = codes[ks, (16 * t + lanes % 16)[:, None]]
+                frag[:, q] = np.bitwise_or.reduce(c << shifts[None, :], axis=1)
+            off = (b * ngroups * 8 + g * nb + t % 8) * 1024
+            out[off:off + 1024] = frag.view(np.uint8).reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("N,K,lo_first", [(256, 256, False), (48, 384, True), (400, 128, False)])
+def test_w4_prepack_layout_matches_the_documented_one(N, K, lo_first):
+    # N = 48 and 400: a last block of three and of one 16-column tiles
+    Wq = workloads.uniform_bytes((K, N // 2), wid=104, tid=N)
+    got = ge.w4_prepack(torch.from_numpy(Wq).to(DEV), lo_first=lo_first).cpu().numpy()
+    assert np.array_equal(got, _host_w4_prepack(Wq, N, lo_first))
 
 
 @pytest.mark.parametrize("M", [16, 32])
