@@ -795,8 +795,9 @@ ge_status gemm_b_prepack(const ge_plan *pl, const void *B, void *Bp, void *strea
     if (overlaps(B, nb, Bp, np)) return fail(GE_ERR_INVALID_ARG, "Bp overlaps B");
     ge_status st;
     if ((st = check_device(pl))) return st;
-    return hip_status(launch_b_prepack(d.K, d.N, (const uint16_t *)B, pl->ldb, (uint16_t *)Bp, (hipStream_t)stream),
-                      "gemm_b_prepack");
+    return hip_status(
+        launch_b_prepack(d.K, d.N, (const uint16_t *)B, pl->ldb, (uint16_t *)Bp, pl->cu_count, (hipStream_t)stream),
+        "gemm_b_prepack");
 }
 
 namespace {

@@ -70,7 +70,10 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 hipError_t launch_w8_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, uint8_t *Wp, hipStream_t s);
 
 // One-time conversion of raw [K, N] bf16 weights to the prepacked decode layout.
-hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s);
+hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, int cu_count,
+                            hipStream_t s);
+// 16-column tiles per block of the prepacked bf16 layout (7 or 8), a function of N and the CU count
+int bf16p_block_tiles(int N, int cu_count);
 
 // Rotary position embedding at Q / K tile load, with the scores product as the consumer.
 struct RopeArgs {

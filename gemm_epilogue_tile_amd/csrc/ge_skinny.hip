@@ -242,20 +242,21 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_kernel(Problem p) {
 // the workgroup reads 8 consecutive 8 KB pieces (64 KB of contiguous memory); a ring of SK_RING
 // blocks in flight per wave, blocks past kbB read zeros and add nothing.  acc[mt][t]: lane (g, i)
 // holds rows 16 mt + 4 g + e of column 16 t + i (MT 16-row tiles of X share each weight fragment).
-template <int MT>
-__device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, int kbB, f32x4 (&acc)[MT][8]) {
+template <int MT, int TB = 8>
+__device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, int kbB, f32x4 (&acc)[MT][TB]) {
+    constexpr int PIECE = TB * 1024;  // bytes of one 32-row piece of a block
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
     const int nkb = p.K / 32;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc((const char *)p.B + (int64_t)cb * nkb * 8192, (int64_t)nkb * 8192);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc((const char *)p.B + (int64_t)cb * nkb * PIECE, (int64_t)nkb * PIECE);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.A, ((int64_t)(p.M - 1) * p.lda + p.K) * 2);
-    u32x4 w[SK_RING][8];
+    u32x4 w[SK_RING][TB];
     bf16x8 xr[SK_RING][MT];
     auto load_blk = [&](int kb, int slot) {
         const bool in = kb < kbB;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) w[slot][t] = bload16(rw, in ? (uint32_t)(kb * 8192 + t * 1024 + lane * 16) : OOB);
+        for (int t = 0; t < TB; ++t) w[slot][t] = bload16(rw, in ? (uint32_t)(kb * PIECE + t * 1024 + lane * 16) : OOB);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = 16 * mt + i;
@@ -270,7 +271,7 @@ __device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, 
         for (int u = 0; u < SK_RING; ++u) {
             load_blk(kb + S_WAVES * (u + SK_RING - 1), (u + SK_RING - 1) % SK_RING);
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < TB; ++t)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     acc[mt][t] = mfma_bf16(xr[u][mt], __builtin_bit_cast(bf16x8, w[u][t]), acc[mt][t]);
@@ -278,44 +279,47 @@ __device__ __forceinline__ void stream_bf16p(const Problem &p, int cb, int kbA, 
     }
 }
 
-// partial tile of one wave (prepacked lane mapping) -> LDS red[wave][16 MT][128]
-template <int MT>
-__device__ __forceinline__ void accp_to_lds(float *red, const f32x4 (&acc)[MT][8]) {
+// partial tile of one wave (prepacked lane mapping) -> LDS red[wave][16 MT][16 TB]
+template <int MT, int TB = 8>
+__device__ __forceinline__ void accp_to_lds(float *red, const f32x4 (&acc)[MT][TB]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int t = 0; t < TB; ++t)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4)
-                red[(wave * 16 * MT + 16 * mt + 4 * g + e4) * 128 + 16 * t + i] = acc[mt][t][e4];
+                red[(wave * 16 * MT + 16 * mt + 4 * g + e4) * (16 * TB) + 16 * t + i] = acc[mt][t][e4];
 }
 
-template <int MT>
+// one workgroup per column block of TB 16-column tiles (128 or 112 columns)
+template <int MT, int TB>
 __global__ __launch_bounds__(S_THREADS) void skinny_bf16p_kernel(Problem p) {
-    constexpr int NC = 128, MR = 16 * MT;
+    constexpr int NC = 16 * TB, MR = 16 * MT;
     __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
-    f32x4 acc[MT][8];
+    f32x4 acc[MT][TB];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stream_bf16p<MT>(p, blockIdx.x, 0, p.K / 32, acc);
-    accp_to_lds<MT>(red, acc);
+        for (int t = 0; t < TB; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16p<MT, TB>(p, blockIdx.x, 0, p.K / 32, acc);
+    accp_to_lds<MT, TB>(red, acc);
     __syncthreads();
     reduce_epilogue<MR, NC>(p, red, blockIdx.x * NC);
 }
 
-// raw [K, N] bf16 (row stride ldb) -> the prepacked layout; item u writes the 16 bytes of lane
-// u % 64 of tile (u / 64) % 8 of piece u / 512 = cb * (K / 32) + kb, i.e. bytes 16 u .. 16 u + 15
+// raw [K, N] bf16 (row stride ldb) -> the prepacked layout of TB-tile blocks; item u writes the 16
+// bytes of lane u % 64 of tile (u / 64) % TB of piece u / (64 TB) = cb * (K / 32) + kb, i.e. bytes
+// 16 u .. 16 u + 15
+template <int TB>
 __global__ __launch_bounds__(256) void b_prepack_kernel(int32_t K, int32_t N, const uint16_t *B, int64_t ldb,
                                                         uint16_t *Bp) {
-    const int64_t nkb = K / 32, total = (int64_t)(N / 128) * nkb * 512;
+    const int64_t nkb = K / 32, total = (int64_t)(N / (16 * TB)) * nkb * 64 * TB;
     for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
-        const int l = (int)(u & 63), t = (int)((u >> 6) & 7);
-        const int64_t piece = u >> 9, kb = piece % nkb, cb = piece / nkb;
-        const int64_t n = cb * 128 + t * 16 + (l & 15), k = kb * 32 + 8 * (l >> 4);
+        const int l = (int)(u & 63), t = (int)((u >> 6) % TB);
+        const int64_t piece = (u >> 6) / TB, kb = piece % nkb, cb = piece / nkb;
+        const int64_t n = cb * 16 * TB + t * 16 + (l & 15), k = kb * 32 + 8 * (l >> 4);
         u32x4 out;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -1007,11 +1011,26 @@ hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
     return hipGetLastError();
 }
 
-hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, hipStream_t s) {
-    const int64_t total = (int64_t)(N / 128) * (K / 32) * 512;
+// 16-column tiles per block of the prepacked bf16 layout: 7 (112 columns) where that gives every
+// CU the same number of blocks and 128-column blocks do not (16 x 28672: 256 blocks of 112 against
+// 224 of 128 on 256 CUs), else 8
+int bf16p_block_tiles(int N, int cu_count) {
+    if (cu_count <= 0 || N % 112) return 8;
+    const bool even112 = (N / 112) % cu_count == 0, even128 = N % 128 == 0 && (N / 128) % cu_count == 0;
+    return even112 && !even128 ? 7 : 8;
+}
+
+hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, int cu_count,
+                            hipStream_t s) {
+    const int tb = bf16p_block_tiles(N, cu_count);
+    const int64_t total = (int64_t)(N / (16 * tb)) * (K / 32) * 64 * tb;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(b_prepack_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s, K, N, B, ldb, Bp);
+    const dim3 grid((unsigned)(blocks > 0 ? blocks : 1));
+    if (tb == 7)
+        hipLaunchKernelGGL(b_prepack_kernel<7>, grid, dim3(256), 0, s, K, N, B, ldb, Bp);
+    else
+        hipLaunchKernelGGL(b_prepack_kernel<8>, grid, dim3(256), 0, s, K, N, B, ldb, Bp);
     return hipGetLastError();
 }
 
@@ -1186,10 +1205,12 @@ const char *skinny_kernel_name(const Problem &p, int cu_count, bool scratch) {
         }
         return p.M <= 16 ? "skinny_w4_m16_32col" : "skinny_w4_m32_32col";
     }
-    if (p.b_packed)
-        return scratch && bf16_sk_slots(p, cu_count) > 0 ? "skinny_bf16_m16_prepacked_streamk"
-               : p.M <= 16                    ? "skinny_bf16_m16_128col_prepacked"
-                                              : "skinny_bf16_m32_128col_prepacked";
+    if (p.b_packed) {
+        if (scratch && bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_prepacked_streamk";
+        if (bf16p_block_tiles(p.N, cu_count) == 7)
+            return p.M <= 16 ? "skinny_bf16_m16_112col_prepacked" : "skinny_bf16_m32_112col_prepacked";
+        return p.M <= 16 ? "skinny_bf16_m16_128col_prepacked" : "skinny_bf16_m32_128col_prepacked";
+    }
     if (scratch && bf16_sk_slots(p, cu_count) > 0) return "skinny_bf16_m16_128col_streamk";
     static const char *names[2][2] = {{"skinny_bf16_m16_128col", "skinny_bf16_m16_64col"},
                                       {"skinny_bf16_m32_128col", "skinny_bf16_m32_64col"}};
@@ -1266,10 +1287,19 @@ hipError_t launch_skinny(const Problem &p, int cu_count, hipStream_t s) {
         return hipGetLastError();
     }
     if (p.b_packed) {
-        if (p.M <= 16)
-            hipLaunchKernelGGL(skinny_bf16p_kernel<1>, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
-        else
-            hipLaunchKernelGGL(skinny_bf16p_kernel<2>, dim3(p.N / 128), dim3(S_THREADS), 0, s, p);
+        const int tb = bf16p_block_tiles(p.N, cu_count);
+        const dim3 grid(p.N / (16 * tb));
+        if (tb == 7) {
+            if (p.M <= 16)
+                hipLaunchKernelGGL((skinny_bf16p_kernel<1, 7>), grid, dim3(S_THREADS), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_bf16p_kernel<2, 7>), grid, dim3(S_THREADS), 0, s, p);
+        } else {
+            if (p.M <= 16)
+                hipLaunchKernelGGL((skinny_bf16p_kernel<1, 8>), grid, dim3(S_THREADS), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_bf16p_kernel<2, 8>), grid, dim3(S_THREADS), 0, s, p);
+        }
         return hipGetLastError();
     }
     const int nch = bf16_chunks(p.N, cu_count > 0 ? cu_count : 256);

@@ -257,16 +257,20 @@ GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t
  * One-time weight conversion for the prepacked bf16 decode kernels (M <= 32;
  * the way a weight loader would store decode weights): reads B [K, N] bf16
  * (row stride = the plan's ldb) and writes the same K*N*2 bytes to Bp in the
- * kernel-native layout: for each 128-column block cb (outer) and 32-row K
- * block kb (inner), 8 KiB holding the MFMA B fragments of the block's eight
- * 16-column tiles t, 1 KiB each, lane l's 16 bytes at byte 16*l of tile t
- * holding column 128*cb + 16*t + l%16 at k = 32*kb + 8*(l/16) + j, j = 0..7
- * in order.  So each column block's K range is one contiguous run of memory
- * and every 16-byte load is a finished fragment (no transpose in the
- * kernel).  Any GENERIC bf16 KN plan of the same N, K and ldb serves (M and
- * the epilogue are ignored).  Needs N % 128 == 0, K % 32 == 0, a 2-byte
- * aligned B and a 16-byte aligned Bp that does not overlap B.  Asynchronous
- * on the stream.
+ * kernel-native layout: for each column block cb of T 16-column tiles
+ * (outer) and 32-row K block kb (inner), T KiB holding the MFMA B fragments
+ * of the block's tiles t, 1 KiB each, lane l's 16 bytes at byte 16*l of tile
+ * t holding column 16*T*cb + 16*t + l%16 at k = 32*kb + 8*(l/16) + j,
+ * j = 0..7 in order.  T is 8 (128-column blocks), or 7 where N / 112 is a
+ * multiple of the device's CU count and N / 128 is not (so that every CU
+ * streams the same number of blocks, e.g. N = 28672 on 256 CUs): the layout
+ * depends on N and on the device the plan was made on, which must be the
+ * device that runs it.  So each column block's K range is one contiguous
+ * run of memory and every 16-byte load is a finished fragment (no transpose
+ * in the kernel).  Any GENERIC bf16 KN plan of the same N, K and ldb serves
+ * (M and the epilogue are ignored).  Needs N % 128 == 0, K % 32 == 0, a
+ * 2-byte aligned B and a 16-byte aligned Bp that does not overlap B.
+ * Asynchronous on the stream.
  */
 GE_API ge_status gemm_b_prepack(const ge_plan *plan, const void *B, void *Bp, void *stream);
 

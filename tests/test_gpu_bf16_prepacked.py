@@ -18,11 +18,21 @@ pytestmark = pytest.mark.gpu
 DEC = workloads.WORKLOADS["skinny_decode"]
 
 
+def _block_tiles(N: int) -> int:
+    """Tiles per column block the header documents: 7 where N / 112 is a multiple of the CU count
+    and N / 128 is not, else 8."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    even112 = N % 112 == 0 and (N // 112) % cu == 0
+    even128 = N % 128 == 0 and (N // 128) % cu == 0
+    return 7 if even112 and not even128 else 8
+
+
 def _host_prepack(B: np.ndarray) -> np.ndarray:
     """The layout gemm_epi.h documents, written with numpy: piece (cb, kb), tile t, lane l holds
-    column 128 cb + 16 t + l % 16 at k = 32 kb + 8 (l // 16) + j, j = 0..7."""
+    column 16 T cb + 16 t + l % 16 at k = 32 kb + 8 (l // 16) + j, j = 0..7 (T tiles per block)."""
     K, N = B.shape
-    v = B.reshape(K // 32, 4, 8, N // 128, 8, 16)          # kb, l//16, j, cb, t, l%16
+    T = _block_tiles(N)
+    v = B.reshape(K // 32, 4, 8, N // (16 * T), T, 16)     # kb, l//16, j, cb, t, l%16
     v = v.transpose(3, 0, 4, 1, 5, 2)                       # cb, kb, t, l//16, l%16, j
     return np.ascontiguousarray(v).reshape(K, N)
 
@@ -34,8 +44,9 @@ def _prepacked(inp, **kw):
                             beta=inp["beta"], act=kw.pop("act", inp["act"]), prepacked=True, **kw)
 
 
-@pytest.mark.parametrize("K,N", [(32, 128), (96, 256), (1024, 384)])
+@pytest.mark.parametrize("K,N", [(32, 128), (96, 256), (1024, 384), (64, 28672)])
 def test_prepack_layout_matches_the_documented_one(K, N):
+    # N = 28672 on 256 CUs: 112-column blocks (256 of them, against 224 of 128 columns)
     B = workloads.f32_to_bf16_bits(np.random.default_rng(K + N).standard_normal((K, N)).astype(np.float32))
     got = ge.b_prepack(to_dev(B)).view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(got, _host_prepack(B))
@@ -50,13 +61,15 @@ def test_prepack_reads_a_strided_source():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 32), (7, 256, 96), (16, 384, 1056), (13, 1024, 8192),
-                                   (16, 2048, 4096), (17, 384, 1056), (29, 1024, 8192), (32, 28672, 512)])
+                                   (16, 2048, 4096), (17, 384, 1056), (29, 1024, 8192), (32, 28672, 512),
+                                   (16, 28672, 512), (5, 28672, 96)])
 def test_prepacked_decode_ragged(M, N, K):
     # M <= 16: one 16-row tile of X per weight fragment; 17 <= M <= 32: two
     w = DEC.with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N + K)
     p = ge.plan(ge.KIND_GENERIC, M, N, K, bias=True, R=True, b_prepacked=True)
-    want = "skinny_bf16_m16_128col_prepacked" if M <= 16 else "skinny_bf16_m32_128col_prepacked"
+    cols = 16 * _block_tiles(N)
+    want = f"skinny_bf16_m16_{cols}col_prepacked" if M <= 16 else f"skinny_bf16_m32_{cols}col_prepacked"
     assert p.kernel == want and p.scratch_bytes == 0
     assert_close(_prepacked(inp), oracle.reference(inp), TOL_BF16, f"prepacked {M}x{N}x{K}")
 
