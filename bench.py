@@ -421,7 +421,8 @@ def main():
         nxt["rope_qk_prefill"] = measure_rope_qk(ks, ws)
         torch.cuda.empty_cache()
         # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
-        for name in ["w8a16_u8_m16", "w8a16_fp8_m16"]:
+        # and on the W4A16 M=512 shape
+        for name in ["w8a16_u8_m16", "w8a16_fp8_m16", "w8a16_u8_m512", "w8a16_fp8_m512"]:
             r = measure(name, ks, ws)
             torch.cuda.empty_cache()
             nxt[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}

@@ -398,7 +398,7 @@ static bool small_tiles(const Problem &p, int cu_count) {
 }
 
 const char *tile_kernel_name(const Problem &p, int cu_count) {
-    if (p.mode == MODE_W4) return tile_w4_kernel_name();
+    if (p.mode == MODE_W4) return tile_w4_kernel_name(p);
     if (p.mode == MODE_SWIGLU)
         return swiglu_big_blocks(p, cu_count) * 128 < p.N ? "tile_swiglu_256x128x32+128x128x32"
                                                            : "tile_swiglu_256x128x32";

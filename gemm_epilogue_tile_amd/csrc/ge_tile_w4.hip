@@ -1,7 +1,8 @@
-// ge_tile_w4.hip -- int4 weights (prepacked), M > 32: MFMA tile kernel with
-// the dequantisation in the K-loop and the epilogue in the store path (page
-// "Fusion Thinking", Pattern 3: packed int4 codes, zero point, per-group
-// scales, dequantised in registers on the way into the product).
+// ge_tile_w4.hip -- quantised weights, M > 32 (int4 prepacked) or M > 16
+// (8-bit codes, raw layout): MFMA tile kernel with the dequantisation in the
+// K-loop and the epilogue in the store path (page "Fusion Thinking", Pattern
+// 3: packed int4 codes, zero point, per-group scales, dequantised in registers
+// on the way into the product; the same loader for INT8 / FP8 codes).
 
 #include "ge_launch.hpp"
 
@@ -19,6 +20,9 @@ namespace {
 //     = s[g][n] * U_g[m][n]  -  (128 + z) * Sx_g[m] * s[g][n],
 //   U_g[m][n] = sum_{k in g} x[m][k] (128 + c[k][n])   (bf16 MFMA, fp32),
 //   Sx_g[m]   = sum_{k in g} x[m][k].
+// 8-bit codes take the same scheme with the code's own value instead of
+// 128 + c: u8 codes 0..255 and fp8 E4M3 values are exact in bf16; for u8 the
+// correction is -z * Sx_g * s[g][n], for fp8 there is none.
 // The first term is accumulated group by group in fp32 registers (one fma per
 // output element per group).  The second term is a small product over the
 // groups, Sx (rows x groups) by s (groups x columns), run on the MFMA once per
@@ -39,6 +43,14 @@ namespace {
 // parts to the correction buffer; one barrier per stage orders every LDS
 // hand-over.  Two workgroups share a CU, so one's vector work runs beside
 // the other's MFMAs.
+//
+// 8-bit codes stream from the raw [K, N] layout instead: each stage, each wave
+// direct-loads its 32 columns x 32 rows (1 KB) three stages ahead into a
+// private ring of four slots, and reads its B fragments back with the
+// transposing LDS read ds_read_b64_tr_b8 (lane pairs name a 16-byte row, each
+// lane receives one column's 8 consecutive k), then converts the bytes to
+// bf16 (u8: one conversion per byte and one packing per pair; fp8: one
+// scaled conversion per pair).
 //
 // Pipeline, per stage s (unrolled by 8 = two groups): at a group's first stage
 // the previous group's partial products are scaled into the accumulators and
@@ -97,8 +109,17 @@ __device__ __forceinline__ i32x4 rsrc32(const void *base, uint32_t bytes) {
 // fp32 -> bf16 bits, round to nearest even
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.0f) & 0xffffu; }
 
+// 8-bit codes: loads a wave may still have in flight at the top of stage u (mod 8) when the codes of
+// stage u + 1 (issued last at stage u - 2) must have landed: the activations, scales (at stages = 2
+// mod 4) and codes of stage u - 1
+constexpr int w8_inflight(int u) { return 2 + (((u - 1) % 4 + 4) % 4 == 2 ? 1 : 0); }
+static_assert(w8_inflight(0) == 2 && w8_inflight(3) == 3, "scale loads at stages = 2 mod 4");
+
+template <int WF>
 __global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(2, 2)))
 void tile_w4_kernel(Problem p) {
+    constexpr bool U4 = WF == WFMT_U4, FP8 = WF == WFMT_FP8;
+    constexpr bool CORR = !FP8;  // a zero-point term (int4: -(128 + z); u8: -z)
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(AS3 void *)smem;
     AS3 char *s3 = (AS3 char *)smem;
@@ -137,9 +158,10 @@ void tile_w4_kernel(Problem p) {
         for (int q = 0; q < W4_LA; ++q)
             load_lds16(r, lds0 + W4_AS + slot * W4_AS_STAGE + (wave * W4_LA + q) * 1024, a_src[q]);
     };
-    // codes of the wave's tiles 2 w, 2 w + 1 (group g: 1 KB at g KB into each tile's run) and
-    // their 32 scales (lanes 0..3) into the wave's slot
-    const int64_t b_bytes = (int64_t)p.K * p.N / 2, s_bytes = ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2;
+    // int4: codes of the wave's tiles 2 w, 2 w + 1 and their 32 scales (lanes 0..3) into the wave's
+    // slot, once per group; 8-bit: the scales once per group, the codes once per stage
+    const int64_t b_bytes = U4 ? (int64_t)p.K * p.N / 2 : (int64_t)(p.K - 1) * p.ldb + p.N;
+    const int64_t s_bytes = ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2;
     uint32_t b_src[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -152,13 +174,23 @@ void tile_w4_kernel(Problem p) {
     const uint32_t codes_w = W4_CODES + wave * W4_CODES_WAVE, scales_w = W4_SCALES + wave * W4_SCALES_WAVE;
     auto load_b = [&](int g, int slot) {
         const bool in = g < ngroups;
-        const int64_t go = (int64_t)g * W4P_BLOCK_TILES * 1024;
-        const i32x4 rb = rsrc32((const char *)p.B + go, in ? (uint32_t)(b_bytes - go) : 0u);
+        if constexpr (U4) {
+            const int64_t go = (int64_t)g * W4P_BLOCK_TILES * 1024;
+            const i32x4 rb = rsrc32((const char *)p.B + go, in ? (uint32_t)(b_bytes - go) : 0u);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) load_lds16(rb, lds0 + codes_w + slot * 2048 + q * 1024, b_src[q]);
+            for (int q = 0; q < 2; ++q) load_lds16(rb, lds0 + codes_w + slot * 2048 + q * 1024, b_src[q]);
+        }
         const int64_t so = (int64_t)g * p.ld_s * 2;
         const i32x4 rs = rsrc32((const char *)p.scales + so, in ? (uint32_t)(s_bytes - so) : 0u);
         load_lds16(rs, lds0 + scales_w + slot * 1024, s_src);
+    };
+    // 8-bit codes of stage d (rows 32 d .. 32 d + 31, the wave's 32 columns): lane l loads row l / 2,
+    // bytes 16 (l % 2) .. + 15, into slot d % 4 of the wave's ring ([32 rows][32 bytes])
+    const uint32_t q_src = (uint32_t)((int64_t)(lane >> 1) * p.ldb + n0 + wave * 32 + (lane & 1) * 16);
+    auto load_q = [&](int d) {
+        const int64_t ro = (int64_t)d * 32 * p.ldb;
+        const i32x4 rq = rsrc32((const char *)p.B + ro, d < nst ? (uint32_t)(b_bytes - ro) : 0u);
+        load_lds16(rq, lds0 + codes_w + (d & 3) * 1024, q_src);
     };
 
     const int frow = lane & 15, fgrp = lane >> 4;
@@ -171,7 +203,7 @@ void tile_w4_kernel(Problem p) {
     auto read_group = [&](int gp) {  // ring slot gp = group parity (compile-time)
 #pragma unroll
         for (int e = 0; e < W4_NT; ++e) {
-            craw[gp][e] = *(const AS3 u32x4 *)(s3 + codes_w + gp * 2048 + e * 1024 + lane * 16);
+            if constexpr (U4) craw[gp][e] = *(const AS3 u32x4 *)(s3 + codes_w + gp * 2048 + e * 1024 + lane * 16);
             sacc[gp][e] = *(const AS3 u32x2 *)(s3 + scales_w + gp * 1024 + (16 * e + 4 * fgrp) * 2);
         }
         const uint32_t lo = *(const AS3 uint16_t *)(s3 + scales_w + gp * 1024 + frow * 2);
@@ -195,6 +227,39 @@ void tile_w4_kernel(Problem p) {
         dq[e][w] = (src & nib_mask) | magic;
         if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(bf16x8, dq[e]);
     };
+    // 8-bit: the B fragments of stage d from the wave's slot d % 4.  In each 16-lane group (k octet
+    // fgrp) lane pair 2 r, 2 r + 1 names row 8 fgrp + r, bytes 16 j .. 16 j + 15, and lane frow
+    // receives column 16 j + frow at k = 8 fgrp .. + 7 (byte order = k order)
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    v2i qraw[W4_NT];
+    const uint32_t q_frag = codes_w + (8 * fgrp + (frow >> 1)) * 32 + (frow & 1) * 8;
+    auto read_q = [&](int d) {
+#pragma unroll
+        for (int e = 0; e < W4_NT; ++e)
+            qraw[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 v2i *)(s3 + q_frag + (d & 3) * 1024 + e * 16));
+    };
+    // bytes -> bf16 fragment e of stage d (in two halves, h = 0, 1: one dword of 4 codes each)
+    auto convert_q = [&](int dd, int e, int h) {
+        const uint32_t w = (uint32_t)qraw[e][h];
+        if constexpr (FP8) {
+            dq[e][2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+            dq[e][2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+        } else {
+            dq[e][2 * h] = pack_bf16x2((float)(w & 0xffu), (float)((w >> 8) & 0xffu));
+            dq[e][2 * h + 1] = pack_bf16x2((float)((w >> 16) & 0xffu), (float)(w >> 24));
+        }
+        if (h == 1) fb[dd & 1][e] = __builtin_bit_cast(bf16x8, dq[e]);
+    };
+    // piece k = 0..7 of stage dd's B fragments: int4 one dequantisation piece; 8-bit pieces 3 .. 6
+    // convert the fragments read at piece 0 (a quarter each)
+    auto b_piece = [&](int dd, int k) {
+        if constexpr (U4) {
+            dequant_piece(dd, k);
+        } else {
+            if (k == 0) read_q(dd);
+            if (k >= 3 && k <= 6) convert_q(dd, (k - 3) >> 1, (k - 3) & 1);
+        }
+    };
 
     const int a_frag = W4_AS + swz_a(frow, fgrp);
     bf16x8 fa[2][W4_MT];
@@ -211,7 +276,7 @@ void tile_w4_kernel(Problem p) {
     // row sums: wave w sums rows 16 w .. 16 w + 15 of each stage straight from the LDS ring, lane l
     // quarter l % 4 (16 of the row's 64 bytes, whatever logical chunk the swizzle put there) of row
     // 16 w + l / 4, with v_dot2 against bf16 ones
-    const float cq = -(128.0f + (float)p.zero_point);
+    const float cq = U4 ? -(128.0f + (float)p.zero_point) : -(float)p.zero_point;
     float rsum = 0.f;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     const int rs_row = 16 * wave + (lane >> 2);
@@ -292,8 +357,9 @@ void tile_w4_kernel(Problem p) {
 #define GE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 
     // prologue: correction buffers cleared; stage 0's activations, group 0 and stage 1's
-    // activations landed; group 0 read, stage 0's fragments read and its B fragments made
-    clear_correction();
+    // activations landed (8-bit: also the codes of stages 0 .. 2, all of it); group 0 read, stage
+    // 0's fragments read and its B fragments made
+    if constexpr (CORR) clear_correction();
     load_a(0, 0);
     load_b(0, 0);
     load_a(1, 1);
@@ -302,13 +368,20 @@ void tile_w4_kernel(Problem p) {
     load_a(4, 4);
     load_b(1, 1);
     load_a(5, 5);
-    GE_WAIT_VM(4 * W4_LA + W4_LB);
+    if constexpr (U4) {
+        GE_WAIT_VM(4 * W4_LA + W4_LB);
+    } else {
+        load_q(0);
+        load_q(1);
+        load_q(2);
+        GE_WAIT_VM(0);
+    }
     lds_barrier();
     read_group(0);
 #pragma unroll
     for (int i = 0; i < W4_MT; ++i) read_a(0, i);
 #pragma unroll
-    for (int k = 0; k < 2 * 4; ++k) dequant_piece(0, k);
+    for (int k = 0; k < 2 * 4; ++k) b_piece(0, k);
 
     // stage s = s0 + u: wait for the loads of stage s - 4 and earlier, barrier, then the 16 MFMAs
     // of stage s with, between them: (first stage of a group) the previous group scaled into the
@@ -320,24 +393,31 @@ void tile_w4_kernel(Problem p) {
 #pragma unroll
         for (int u = 0; u < W4_UNROLL; ++u) {
             const int s = s0 + u;
-            if ((u & 3) == 2)
-                GE_WAIT_VM(w4_inflight(2));
-            else
-                GE_WAIT_VM(w4_inflight(0));
+            if constexpr (U4) {
+                if ((u & 3) == 2)
+                    GE_WAIT_VM(w4_inflight(2));
+                else
+                    GE_WAIT_VM(w4_inflight(0));
+            } else {
+                if ((u & 3) == 3)
+                    GE_WAIT_VM(w8_inflight(3));
+                else
+                    GE_WAIT_VM(w8_inflight(0));
+            }
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             const int dn = (u + 1) & (W4_UNROLL - 1);
             const bool first = (u & 3) == 0;           // first stage of a group
             const bool apply = first && s > 0;         // group s / 4 - 1 is complete
-            if (apply) write_sb(s / 4 - 1, ((u >> 2) + 1) & 1);
-            if (first && s > 0 && (s / 4) % W4_CHUNK == 0) correction();  // a chunk of groups is complete
+            if (CORR && apply) write_sb(s / 4 - 1, ((u >> 2) + 1) & 1);
+            if (CORR && first && s > 0 && (s / 4) % W4_CHUNK == 0) correction();  // a chunk of groups is complete
             // one barrier later every wave has read it, and the next chunk's first writes (end of
             // this group's last stage) are still to come
-            if (u == 1 && s0 > 0 && s0 % (4 * W4_CHUNK) == 0) clear_correction();
+            if (CORR && u == 1 && s0 > 0 && s0 % (4 * W4_CHUNK) == 0) clear_correction();
 #pragma unroll
             for (int q = 0; q < W4_MT * W4_NT; ++q) {
                 const int i = q & (W4_MT - 1), j = q / W4_MT;
-                if (q == 0) row_read(u);
+                if (CORR && q == 0) row_read(u);
                 if (apply) apply_tile(((u >> 2) + 1) & 1, i, j);
                 U[i][j] = mfma_bf16(fb[u & 1][j], fa[u & 1][i], first ? f32x4{0.f, 0.f, 0.f, 0.f} : U[i][j]);
                 if (q == 0) {
@@ -346,15 +426,16 @@ void tile_w4_kernel(Problem p) {
                         load_b((s + 6) >> 2, ((u + 6) >> 2) & 1);
                         read_group(((u + 2) >> 2) & 1);  // group (s + 2) / 4, loaded at stage s - 4
                     }
+                    if constexpr (!U4) load_q(s + 3);  // into the slot of stage s - 1, read at stage s - 2
                 }
-                if (q == W4_MT * W4_NT - 1) row_sums();
+                if (CORR && q == W4_MT * W4_NT - 1) row_sums();
                 if (q >= 1 && q <= W4_MT) read_a(dn, q - 1);
-                dequant_piece(dn, q);  // 8 pieces: one per MFMA
+                b_piece(dn, q);  // 8 pieces: one per MFMA
                 // keep each MFMA with the work placed beside it (the scheduler would otherwise
                 // bunch the MFMAs and the reads and move them across the stage barriers)
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if ((u & 3) == 3) write_sx(s / 4);
+            if (CORR && (u & 3) == 3) write_sx(s / 4);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -363,13 +444,15 @@ void tile_w4_kernel(Problem p) {
     // the last group (stage nsteps - 4 .. nsteps - 1) and the last chunk's correction
     {
         const int g = nsteps / 4 - 1;  // odd: nsteps is a multiple of 8
-        write_sb(g, 1);
+        if constexpr (CORR) write_sb(g, 1);
 #pragma unroll
         for (int i = 0; i < W4_MT; ++i)
 #pragma unroll
             for (int j = 0; j < W4_NT; ++j) apply_tile(1, i, j);
-        lds_barrier();
-        correction();
+        if constexpr (CORR) {
+            lds_barrier();
+            correction();
+        }
     }
 
     const EpiArgs &e = p.epi;
@@ -405,28 +488,43 @@ void tile_w4_kernel(Problem p) {
 }  // namespace
 
 bool tile_w4_supported(const Problem &p) {
-    if (p.mode != MODE_W4 || !p.w4_packed || p.M <= 16) return false;
+    if (p.mode != MODE_W4 || p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
     if ((p.N % W4_BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
-    if (p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
     if (((int64_t)(p.M - 1) * p.lda + p.K) * 2 >= (1ll << 31)) return false;  // X through 32-bit offsets
-    if ((int64_t)p.K * p.N / 2 >= (1ll << 31) || ((int64_t)(p.K / 128) * p.ld_s + p.N) * 2 >= (1ll << 31)) return false;
+    if (((int64_t)(p.K / 128) * p.ld_s + p.N) * 2 >= (1ll << 31)) return false;
+    if (p.wfmt == WFMT_U4) {
+        // prepacked int4, M > 32 (smaller M streams the weights)
+        if (!p.w4_packed || p.M <= 32 || (int64_t)p.K * p.N / 2 >= (1ll << 31)) return false;
+    } else {
+        // 8-bit codes in the raw [K, N] layout, M > 16: 16-byte rows pieces, 32-bit offsets
+        if (p.w4_packed || p.M <= 16 || (p.ldb & 15) || (int64_t)p.K * p.ldb >= (1ll << 31)) return false;
+    }
     return epi_ok(p);
 }
 
-const char *tile_w4_kernel_name() { return "tile_w4_bf16_64x128x32"; }
+const char *tile_w4_kernel_name(const Problem &p) {
+    return p.wfmt == WFMT_U4 ? "tile_w4_bf16_64x128x32" : p.wfmt == WFMT_U8 ? "tile_w8_u8_64x128x32" : "tile_w8_fp8_64x128x32";
+}
 
-hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
-    if (!tile_w4_supported(p)) return hipErrorInvalidValue;
+template <int WF>
+static hipError_t launch_wf(const Problem &p, hipStream_t s) {
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel<WF>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            W4_LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4_BN);
-    hipLaunchKernelGGL(tile_w4_kernel, dim3(tiles), dim3(T_THREADS), W4_LDS, s, p);
+    hipLaunchKernelGGL(tile_w4_kernel<WF>, dim3(tiles), dim3(T_THREADS), W4_LDS, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
+    if (!tile_w4_supported(p)) return hipErrorInvalidValue;
+    if (p.wfmt == WFMT_U8) return launch_wf<WFMT_U8>(p, s);
+    if (p.wfmt == WFMT_FP8) return launch_wf<WFMT_FP8>(p, s);
+    return launch_wf<WFMT_U4>(p, s);
 }
 
 }  // namespace ge

@@ -43,7 +43,8 @@ def _run(name, inp):
                                         ("skinny_decode", 16), ("skinny_decode+prepacked", 16),
                                         ("w4a16_m16", 16), ("w4a16_m512", 24),
                                         ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16),
-                                        ("w8a16_u8_m16+prepacked", 16), ("w8a16_fp8_m16+prepacked", 16)])
+                                        ("w8a16_u8_m16+prepacked", 16), ("w8a16_fp8_m16+prepacked", 16),
+                                        ("w8a16_u8_m512", 16), ("w8a16_fp8_m512", 16)])
 def test_full_size_sampled_rows(name, nrows):
     w = workloads.WORKLOADS[name.split("+")[0]]
     inp = workloads.make_inputs(w)

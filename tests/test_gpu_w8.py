@@ -50,6 +50,41 @@ def test_w8_plans_pick_the_streaming_kernel_for_small_M():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(17, 128, 128), (64, 256, 1024), (100, 384, 4224), (512, 1024, 2048)])
+def test_w8_tile_kernel(fmt, M, N, K):
+    # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes; K = 4224
+    # is 33 groups, not a whole number of the kernel's two-group loop trips
+    w = BASE[fmt].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=3 * M + K)
+    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x128x32"
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} tile {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("zp", [0, 77, 255])
+def test_w8_tile_u8_zero_points(zp):
+    w = dataclasses.replace(BASE["u8"], M=96, N=256, K=1024, zero_point=zp)
+    inp = workloads.make_inputs(w, seed=zp)
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"u8 tile zero point {zp}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_w8_tile_strided_operands(fmt):
+    # X with a row stride of K + 8 elements, codes with a row stride of N + 16 bytes
+    M, N, K = 80, 256, 512
+    w = BASE[fmt].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=11)
+    d = dev_inputs(inp)
+    Xf = torch.zeros((M, K + 8), dtype=torch.bfloat16, device=DEV)
+    Xf[:, :K] = d["X"]
+    Wf = torch.zeros((K, N + 16), dtype=torch.uint8, device=DEV)
+    Wf[:, :N] = torch.from_numpy(inp["Wq"]).to(DEV)
+    out = ge.w4_gemm(Xf[:, :K], Wf[:, :N], d["scales"], bias=d.get("bias"), group=inp["group"],
+                     zero_point=inp["zero_point"], fmt=fmt)
+    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x128x32"
+    assert_close(out, oracle.reference(inp), TOL_BF16, f"{fmt} tile strided")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M", [16, 40])
 @pytest.mark.parametrize("group", [32, 64, 128, 256])
 def test_w8_group_sizes(fmt, M, group):
@@ -82,7 +117,7 @@ def _non_nan_codes(shape, wid):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [16, 48])
+@pytest.mark.parametrize("M", [16, 48, 130])
 def test_w8_decode_bit_exact_with_one_hot_rows(fmt, M):
     # X row m is one-hot at k_m and scales are 2^-6, so D[m][n] = value(code) * 2^-6 exactly:
     # at most 9 significant bits for u8, 4 for fp8 (subnormals and 448 included)

@@ -145,6 +145,11 @@ WORKLOADS = {
                              fmt="u8"),
     "w8a16_fp8_m16": Workload("w8a16_fp8_m16", 7, "w8", 16, 8192, 8192, "bf16", bias=True, zero_point=0,
                               fmt="fp8"),
+    # and on the W4A16 M=512 shape
+    "w8a16_u8_m512": Workload("w8a16_u8_m512", 8, "w8", 512, 8192, 8192, "bf16", bias=True, zero_point=128,
+                              fmt="u8"),
+    "w8a16_fp8_m512": Workload("w8a16_fp8_m512", 9, "w8", 512, 8192, 8192, "bf16", bias=True, zero_point=0,
+                               fmt="fp8"),
 }
 
 
