@@ -277,7 +277,7 @@ void tile_w4_kernel(Problem p) {
     // quarter l % 4 (16 of the row's 64 bytes, whatever logical chunk the swizzle put there) of row
     // 16 w + l / 4, with v_dot2 against bf16 ones
     const float cq = U4 ? -(128.0f + (float)p.zero_point) : -(float)p.zero_point;
-    float rsum = 0.f;
+    float rsum = 0.f, rsum2 = 0.f;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
     const int rs_row = 16 * wave + (lane >> 2);
     const uint32_t rs_addr = W4_AS + rs_row * 64 + (lane & 3) * 16;
@@ -286,19 +286,25 @@ void tile_w4_kernel(Problem p) {
     u32x4 rs_v;
     auto row_read = [&](int dd) { rs_v = *(const AS3 u32x4 *)(s3 + rs_addr + dd * W4_AS_STAGE); };
     auto row_sums = [&]() {
-        // scalar copies: this compiler reads element 0 for a bit cast of a vector element
+        // scalar copies: this compiler reads element 0 for a bit cast of a vector element; two
+        // partial sums, so that the four dot products form two short chains
         const uint32_t w[4] = {rs_v[0], rs_v[1], rs_v[2], rs_v[3]};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones, rsum, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, rsum, false);
+        rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[1]), ones, rsum2, false);
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2]), ones, rsum, false);
+        rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[3]), ones, rsum2, false);
     };
-    // group g complete: the four quarters of each row added, the three bf16 parts of -(128 + z)
+    // group g complete: the four quarters of each row added (lane swaps within each group of four
+    // lanes through DPP quad permutations, no LDS round trip), the three bf16 parts of -(128 + z)
     // Sx_g written to the correction buffer (lanes 0, 1, 2 of a row's four write one each)
     auto write_sx = [&](int g) {
         const int gg = g % W4_CHUNK;
-        float t2 = rsum + __shfl_xor(rsum, 1);
-        t2 += __shfl_xor(t2, 2);
+        float t2 = rsum + rsum2;
+        t2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t2), 0xB1, 0xF, 0xF, false));
+        t2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t2), 0x4E, 0xF, 0xF, false));
         const float v = t2 * cq;
         rsum = 0.f;
+        rsum2 = 0.f;
         const uint32_t hi = bf16_bits(v);
         const float r1 = v - __builtin_bit_cast(float, hi << 16);
         const uint32_t mid = bf16_bits(r1);
