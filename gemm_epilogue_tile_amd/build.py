@@ -19,6 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libgemm_epi.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+DEBUG_LIB_NAME = "libgemm_epi_debug.so"
+DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)
 ARCH = "gfx950"
 
 
@@ -38,9 +40,9 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON_FLAGS
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, "debug" if debug else "", os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON_FLAGS + (["-DGE_DEBUG_SYNC"] if debug else [])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,24 +59,27 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every HIP source and link ``libgemm_epi.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, debug: bool = False) -> str:
+    """Compile every HIP source and link ``libgemm_epi.so`` (``debug``: the race-guard build
+    ``libgemm_epi_debug.so``, compiled with -DGE_DEBUG_SYNC); returns its path."""
+    os.makedirs(os.path.join(BUILD_DIR, "debug" if debug else ""), exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2) // 2), 8)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug), srcs))
+    lib_path, lib_name = (DEBUG_LIB_PATH, DEBUG_LIB_NAME) if debug else (LIB_PATH, LIB_NAME)
+    tmp = lib_path + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-           f"-Wl,-soname,{LIB_NAME}"] + objs
+           f"-Wl,-soname,{lib_name}"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug=True))

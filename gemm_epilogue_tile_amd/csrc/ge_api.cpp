@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -35,6 +36,12 @@ ge_status ok() {
 }
 
 ge_status hip_status(hipError_t e, const char *what) {
+#ifdef GE_DEBUG_SYNC
+    // race-guard build: every call completes on the device before it returns, so a kernel fault is
+    // reported by the call that launched it
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipGetLastError();
+#endif
     if (e == hipSuccess) return ok();
     return fail(GE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -59,6 +66,15 @@ struct ge_plan {
 };
 
 namespace {
+
+// GE_LOG=1 in the environment: each plan prints its kernel choice to stderr (read once)
+bool log_enabled() {
+    static const bool on = [] {
+        const char *v = std::getenv("GE_LOG");
+        return v && v[0] == '1';
+    }();
+    return on;
+}
 
 // plan scratch: the 8-bit kernel's split tiles and counters, or the stream-K decode kernel's tiles
 // and counters
@@ -455,6 +471,14 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         return fail(GE_ERR_INVALID_ARG, "out of host memory");
     }
     *out = h;
+    if (log_enabled()) {
+        static const char *kinds[] = {"generic", "swiglu", "w4"};
+        std::fprintf(stderr,
+                     "ge: plan kind=%s M=%d N=%d K=%d a=%d b=%d d=%d act=%d flags=0x%x group=%d -> kernel=%s "
+                     "split=%d scratch=%zu\n",
+                     kinds[kind], d.M, d.N, d.K, d.a_type, d.b_type, d.d_type, d.act, (unsigned)d.flags, pl.group,
+                     pl.kernel, pl.split, pl.scratch_bytes);
+    }
     return ok();
 }
 

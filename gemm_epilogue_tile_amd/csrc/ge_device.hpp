@@ -31,6 +31,27 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+// Race-guard build (-DGE_DEBUG_SYNC, libgemm_epi_debug.so): each pipeline stage of the tile
+// kernels also waits for all of its wave's outstanding memory operations and meets a full
+// workgroup barrier, and the cross-workgroup handoffs add device-scope fences.  The extra
+// ordering can only remove races, never add them, so the normal build's outputs must equal the
+// debug build's bit for bit; a difference points at a missing wait or barrier.
+#ifdef GE_DEBUG_SYNC
+#define GE_DEBUG_BARRIER()             \
+    do {                               \
+        __builtin_amdgcn_s_waitcnt(0); \
+        __syncthreads();               \
+    } while (0)
+#define GE_DEBUG_FENCE() __threadfence()
+#else
+#define GE_DEBUG_BARRIER() \
+    do {                   \
+    } while (0)
+#define GE_DEBUG_FENCE() \
+    do {                 \
+    } while (0)
+#endif
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 v = {lo, hi};
     bf16x2 b = __builtin_convertvector(v, bf16x2);

@@ -395,6 +395,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rt, off + 16, 0, SC1);
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile stores are complete
+            GE_DEBUG_FENCE();
             __syncthreads();
             if (threadIdx.x == 0) {
                 const uint32_t add = (uint32_t)(kbB - kbA);
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16_sk_kernel(Problem p) {
             }
             __syncthreads();
             if (s_last) {
+                GE_DEBUG_FENCE();
                 const bool vec_ok = epi_vec_ok(p);
                 with_act(p.epi.act, [&](auto ACTC) {
                     constexpr int ACT = decltype(ACTC)::value;
@@ -637,6 +639,7 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rt, off + 16, 0, SC1);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile stores are complete
+    GE_DEBUG_FENCE();
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(p.split_cnt + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -644,6 +647,7 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
     }
     __syncthreads();
     if (!*s_last) return;
+    GE_DEBUG_FENCE();
     const bool vec_ok = epi_vec_ok(p);
     with_act(p.epi.act, [&](auto ACTC) {
         constexpr int ACT = decltype(ACTC)::value;

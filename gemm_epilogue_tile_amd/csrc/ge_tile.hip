@@ -285,6 +285,7 @@ void tile_kernel(Problem p) {
             // stage s+1 landed (own loads), visible to all; every wave is done reading stage s
             GE_WAIT_VM((T_NS - 2) * C::LOADS);
             lds_barrier();
+            GE_DEBUG_BARRIER();
             const StageLoads L = stage_loads(s + T_NS);  // into buffer b, three stages ahead
             stage(L, (b + 1) & (T_NS - 1), fa[b & 1], fb[b & 1], fa[(b + 1) & 1], fb[(b + 1) & 1]);
         }

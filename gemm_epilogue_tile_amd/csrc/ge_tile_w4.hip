@@ -411,6 +411,7 @@ void tile_w4_kernel(Problem p) {
                     GE_WAIT_VM(w8_inflight(0));
             }
             lds_barrier();
+            GE_DEBUG_BARRIER();
             __builtin_amdgcn_sched_barrier(0);
             const int dn = (u + 1) & (W4_UNROLL - 1);
             const bool first = (u & 3) == 0;           // first stage of a group
