@@ -63,7 +63,7 @@ namespace {
 // stage earlier.
 // ---------------------------------------------------------------------------
 
-constexpr int W4_BM = 64, W4_BN = 128;
+constexpr int W4_BM = 64;
 constexpr int W4_MT = 4, W4_NT = 2;          // 16x16 tiles per wave: 64 rows x 32 columns
 constexpr int W4_UNROLL = 8;                 // stages per loop trip (ring sizes divide it)
 constexpr int W4_AD = 6;                     // activation loads run this many stages ahead
@@ -75,25 +75,42 @@ static_assert(W4_MT * W4_NT == 8, "one dequantisation piece per MFMA of a stage"
 // the correction operands: three bf16 parts of -(128 + z) Sx, [part][m-tile][16 rows][32 groups],
 // and per wave the scales, [n-tile][16 columns][32 groups] (both 64-byte rows: fragment order)
 constexpr int W4_AS = 0, W4_AS_STAGE = W4_BM * 64;
-constexpr int W4_CODES = W4_AS + W4_UNROLL * W4_AS_STAGE, W4_CODES_WAVE = 2 * 2 * 1024;
-constexpr int W4_SCALES = W4_CODES + 4 * W4_CODES_WAVE, W4_SCALES_WAVE = 2 * 1024;
-constexpr int W4_CA = W4_SCALES + 4 * W4_SCALES_WAVE, W4_CA_BYTES = 3 * W4_MT * 1024;
-constexpr int W4_CB = W4_CA + W4_CA_BYTES, W4_CB_WAVE = W4_NT * 1024;
-constexpr int W4_LDS = W4_CB + 4 * W4_CB_WAVE;  // 76 KB: two workgroups per CU
+constexpr int W4_CODES_WAVE = 2 * 2 * 1024, W4_SCALES_WAVE = 2 * 1024;
+constexpr int W4_CA_BYTES = 3 * W4_MT * 1024, W4_CB_WAVE = W4_NT * 1024;
+// NW waves side by side: a 64 x 32 NW tile.  NW = 4: 76 KB of LDS, two workgroups per CU; NW = 8:
+// 108 KB, one workgroup of 8 waves per CU, whose activation tile and row sums serve 256 columns
+// (half the activation loads and row sums per CU of two 4-wave workgroups)
+template <int NW>
+struct W4L {
+    static constexpr int BN = 32 * NW, THREADS = 64 * NW;
+    static constexpr int CODES = W4_AS + W4_UNROLL * W4_AS_STAGE;
+    static constexpr int SCALES = CODES + NW * W4_CODES_WAVE;
+    static constexpr int CA = SCALES + NW * W4_SCALES_WAVE;
+    static constexpr int CB = CA + W4_CA_BYTES;
+    static constexpr int LDS = CB + NW * W4_CB_WAVE;
+    static constexpr int RL = NW, RL_LOG = NW == 8 ? 3 : 2;  // lanes per row in the row sums (rows per wave: 64 / NW)
+};
 
-// direct loads issued by each wave: 2 per stage (activations), 3 per group (codes, scales)
-constexpr int W4_LA = 1, W4_LB = 3;
-static_assert(W4_LA * 4 * 64 * 16 == W4_AS_STAGE, "four waves load one activation stage");
+// direct loads issued by each wave: per group 3 (int4 codes, scales) or 1 (8-bit: scales); 4-wave
+// workgroups: one activation load per stage (stage s + 6 at stage s); 8-wave: one every other stage,
+// at even stages s, of the pair s + 6, s + 7 (waves 0-3 the first, 4-7 the second), so that every
+// wave of the workgroup issues the same sequence and the wait counts below hold for all of them
+constexpr int W4_LB = 3;
 // loads a wave may still have in flight at the top of stage u (mod 8) when everything issued up to
-// stage u - 4 must have landed: the activations of stages u-3 .. u-1 and the group loads among them
-// (issued at stages = 2 mod 4)
-constexpr int w4_inflight(int u) {
-    int n = 3 * W4_LA;
-    for (int k = 1; k <= 3; ++k)
-        if (((u - k) % 4 + 4) % 4 == 2) n += W4_LB;
+// stage u - 4 must have landed: the activations and the group loads (issued at stages = 2 mod 4) of
+// stages u-3 .. u-1
+constexpr int w4_inflight(int NW, int u) {
+    int n = 0;
+    for (int k = 1; k <= 3; ++k) {
+        const int t = ((u - k) % 8 + 8) % 8;
+        if (NW == 4 || (t & 1) == 0) n += 1;
+        if (t % 4 == 2) n += W4_LB;
+    }
     return n;
 }
-static_assert(w4_inflight(0) == w4_inflight(1) && w4_inflight(1) == w4_inflight(3), "one group load among three stages");
+static_assert(w4_inflight(4, 0) == 6 && w4_inflight(4, 3) == 6, "one group load among three stages");
+static_assert(w4_inflight(8, 0) == 4 && w4_inflight(8, 1) == 5 && w4_inflight(8, 2) == 1 && w4_inflight(8, 3) == 5 &&
+                  w4_inflight(8, 4) == w4_inflight(8, 0), "8 waves: activation pairs at even stages");
 
 // buffer resource over [base, base + bytes), bytes already known to be in range (no 64-bit compare)
 __device__ __forceinline__ i32x4 rsrc32(const void *base, uint32_t bytes) {
@@ -110,14 +127,20 @@ __device__ __forceinline__ i32x4 rsrc32(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16x2(x, 0.0f) & 0xffffu; }
 
 // 8-bit codes: loads a wave may still have in flight at the top of stage u (mod 8) when the codes of
-// stage u + 1 (issued last at stage u - 2) must have landed: the activations, scales (at stages = 2
-// mod 4) and codes of stage u - 1
-constexpr int w8_inflight(int u) { return 2 + (((u - 1) % 4 + 4) % 4 == 2 ? 1 : 0); }
-static_assert(w8_inflight(0) == 2 && w8_inflight(3) == 3, "scale loads at stages = 2 mod 4");
+// stage u + 1 (issued last at stage u - 2) must have landed: the activations (if the wave loaded
+// any), scales (at stages = 2 mod 4) and codes of stage u - 1
+constexpr int w8_inflight(int NW, int u) {
+    const int t = ((u - 1) % 8 + 8) % 8;
+    return (NW == 4 || (t & 1) == 0 ? 1 : 0) + (t % 4 == 2 ? 1 : 0) + 1;
+}
+static_assert(w8_inflight(4, 0) == 2 && w8_inflight(4, 3) == 3 && w8_inflight(8, 0) == 1 && w8_inflight(8, 1) == 2 &&
+                  w8_inflight(8, 3) == 3,
+              "scale loads at stages = 2 mod 4");
 
-template <int WF>
-__global__ __attribute__((amdgpu_flat_work_group_size(T_THREADS, T_THREADS), amdgpu_waves_per_eu(2, 2)))
+template <int WF, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void tile_w4_kernel(Problem p) {
+    using L = W4L<NW>;
     constexpr bool U4 = WF == WFMT_U4, FP8 = WF == WFMT_FP8;
     constexpr bool CORR = !FP8;  // a zero-point term (int4: -(128 + z); u8: -z)
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -126,7 +149,8 @@ void tile_w4_kernel(Problem p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int tiles_m = (p.M + W4_BM - 1) / W4_BM, tiles_n = p.N / W4_BN;
+    const int half = NW == 8 ? wave >> 2 : 0;  // 8 waves: which stage of a pair this wave loads
+    const int tiles_m = (p.M + W4_BM - 1) / W4_BM, tiles_n = p.N / L::BN;
     const int total = tiles_m * tiles_n;
     int t = blockIdx.x;
     if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
@@ -135,28 +159,22 @@ void tile_w4_kernel(Problem p) {
     const int gsize = min(tiles_m - first_m, GROUP_M);
     const int tm = first_m + (t % per_group) % gsize;
     const int tn = (t % per_group) / gsize;
-    const int m0 = tm * W4_BM, n0 = tn * W4_BN;
+    const int m0 = tm * W4_BM, n0 = tn * L::BN;
     const int ngroups = p.K / 128, nst = p.K / T_BK;
 
     // Direct loads.  The lane offsets are fixed; the stage's (or group's) position goes into the
     // buffer resource (scalar arithmetic), whose range is empty past the end of K, so the loop
     // spends no vector instructions on addresses.
-    // activations: wave w loads rows 16 w .. 16 w + 15 of each stage, lane l row l / 4 of 16, LDS
-    // slot l % 4 of the row holding logical chunk (l % 4) ^ ((row >> 1) & 3)
+    // activations: wave w (mod 4) loads rows 16 w .. 16 w + 15 of a stage, lane l row l / 4 of 16,
+    // LDS slot l % 4 of the row holding logical chunk (l % 4) ^ ((row >> 1) & 3)
     const char *a_base = (const char *)p.A + (int64_t)m0 * p.lda * 2;
     const int64_t a_bytes = ((int64_t)(p.M - m0 - 1) * p.lda + p.K) * 2;
-    uint32_t a_src[W4_LA];
-#pragma unroll
-    for (int q = 0; q < W4_LA; ++q) {
-        const int row_l = lane >> 2;
-        const int chunk = (lane & 3) ^ ((row_l >> 1) & 3);
-        a_src[q] = (uint32_t)((int64_t)((wave * W4_LA + q) * 16 + row_l) * p.lda * 2 + chunk * 16);
-    }
+    const int arow_l = lane >> 2;
+    const uint32_t a_src = (uint32_t)((int64_t)((wave & 3) * 16 + arow_l) * p.lda * 2 +
+                                      (((lane & 3) ^ ((arow_l >> 1) & 3)) * 16));
     auto load_a = [&](int d, int slot) {
         const i32x4 r = rsrc32(a_base + d * 64, d < nst ? (uint32_t)(a_bytes - d * 64) : 0u);
-#pragma unroll
-        for (int q = 0; q < W4_LA; ++q)
-            load_lds16(r, lds0 + W4_AS + slot * W4_AS_STAGE + (wave * W4_LA + q) * 1024, a_src[q]);
+        load_lds16(r, lds0 + W4_AS + slot * W4_AS_STAGE + (wave & 3) * 1024, a_src);
     };
     // int4: codes of the wave's tiles 2 w, 2 w + 1 and their 32 scales (lanes 0..3) into the wave's
     // slot, once per group; 8-bit: the scales once per group, the codes once per stage
@@ -165,13 +183,14 @@ void tile_w4_kernel(Problem p) {
     uint32_t b_src[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        // tile tt of the prepacked layout's 128-column block n0 / 128 (N is a multiple of 128, so
-        // every block is whole): a group's eight tiles are 8 KiB in a row
-        const int tt = wave * 2 + q;
-        b_src[q] = (uint32_t)(((int64_t)(n0 / 128) * ngroups * W4P_BLOCK_TILES + tt) * 1024 + lane * 16);
+        // tile tt of the prepacked layout (N is a multiple of 128, so every 128-column block is
+        // whole): a group's eight tiles of one block are 8 KiB in a row
+        const int tt = n0 / 16 + wave * 2 + q;
+        b_src[q] = (uint32_t)(((int64_t)(tt / W4P_BLOCK_TILES) * ngroups * W4P_BLOCK_TILES + tt % W4P_BLOCK_TILES) *
+                                  1024 + lane * 16);
     }
     const uint32_t s_src = lane < 4 ? (uint32_t)((n0 + wave * 32) * 2 + lane * 16) : OOB;
-    const uint32_t codes_w = W4_CODES + wave * W4_CODES_WAVE, scales_w = W4_SCALES + wave * W4_SCALES_WAVE;
+    const uint32_t codes_w = L::CODES + wave * W4_CODES_WAVE, scales_w = L::SCALES + wave * W4_SCALES_WAVE;
     auto load_b = [&](int g, int slot) {
         const bool in = g < ngroups;
         if constexpr (U4) {
@@ -279,20 +298,26 @@ void tile_w4_kernel(Problem p) {
     const float cq = U4 ? -(128.0f + (float)p.zero_point) : -(float)p.zero_point;
     float rsum = 0.f, rsum2 = 0.f;
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-    const int rs_row = 16 * wave + (lane >> 2);
-    const uint32_t rs_addr = W4_AS + rs_row * 64 + (lane & 3) * 16;
+    // (4 waves: 16 rows per wave, 4 lanes x 16 bytes per row; 8 waves: 8 rows, 8 lanes x 8 bytes)
+    constexpr int RB = 64 / L::RL;  // bytes of a row per lane
+    const int rs_row = (64 / NW) * wave + (lane >> L::RL_LOG);
+    const uint32_t rs_addr = W4_AS + rs_row * 64 + (lane & (L::RL - 1)) * RB;
     // (requested first in a stage and summed last, so that its wait does not cover the stage's
     // fragment reads, which are requested after it)
-    u32x4 rs_v;
-    auto row_read = [&](int dd) { rs_v = *(const AS3 u32x4 *)(s3 + rs_addr + dd * W4_AS_STAGE); };
+    using RV = std::conditional_t<NW == 4, u32x4, u32x2>;
+    RV rs_v;
+    auto row_read = [&](int dd) { rs_v = *(const AS3 RV *)(s3 + rs_addr + dd * W4_AS_STAGE); };
     auto row_sums = [&]() {
         // scalar copies: this compiler reads element 0 for a bit cast of a vector element; two
-        // partial sums, so that the four dot products form two short chains
-        const uint32_t w[4] = {rs_v[0], rs_v[1], rs_v[2], rs_v[3]};
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, rsum, false);
-        rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[1]), ones, rsum2, false);
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2]), ones, rsum, false);
-        rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[3]), ones, rsum2, false);
+        // partial sums, so that the dot products form two short chains
+        const uint32_t w0 = rs_v[0], w1 = rs_v[1];
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, rsum, false);
+        rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, rsum2, false);
+        if constexpr (NW == 4) {
+            const uint32_t w2 = rs_v[2], w3 = rs_v[3];
+            rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, rsum, false);
+            rsum2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, rsum2, false);
+        }
     };
     // group g complete: the four quarters of each row added (lane swaps within each group of four
     // lanes through DPP quad permutations, no LDS round trip), the three bf16 parts of -(128 + z)
@@ -302,6 +327,8 @@ void tile_w4_kernel(Problem p) {
         float t2 = rsum + rsum2;
         t2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t2), 0xB1, 0xF, 0xF, false));
         t2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t2), 0x4E, 0xF, 0xF, false));
+        if constexpr (NW == 8)  // the two quads of a row of eight lanes: half-row mirror
+            t2 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, t2), 0x141, 0xF, 0xF, false));
         const float v = t2 * cq;
         rsum = 0.f;
         rsum2 = 0.f;
@@ -309,12 +336,12 @@ void tile_w4_kernel(Problem p) {
         const float r1 = v - __builtin_bit_cast(float, hi << 16);
         const uint32_t mid = bf16_bits(r1);
         const uint32_t lo = bf16_bits(r1 - __builtin_bit_cast(float, mid << 16));
-        const uint32_t at = W4_CA + (rs_row >> 4) * 1024 + (rs_row & 15) * 64 + gg * 2;
-        const int part = lane & 3;
+        const uint32_t at = L::CA + (rs_row >> 4) * 1024 + (rs_row & 15) * 64 + gg * 2;
+        const int part = lane & (L::RL - 1);
         if (part < 3) *(AS3 uint16_t *)(s3 + at + part * W4_MT * 1024) = (uint16_t)(part == 0 ? hi : part == 1 ? mid : lo);
     };
     // the wave's correction scales: lanes of k-octet 0 put column 16 j + frow of group g in place
-    const uint32_t cb_w = W4_CB + wave * W4_CB_WAVE;
+    const uint32_t cb_w = L::CB + wave * W4_CB_WAVE;
     auto write_sb = [&](int g, int gp) {
         if (fgrp == 0) {
             const int gg = g % W4_CHUNK;
@@ -332,7 +359,7 @@ void tile_w4_kernel(Problem p) {
         for (int part = 0; part < 3; ++part)
 #pragma unroll
             for (int i = 0; i < W4_MT; ++i) {
-                const bf16x8 af = *(const AS3 bf16x8 *)(s3 + W4_CA + (part * W4_MT + i) * 1024 + frow * 64 + fgrp * 16);
+                const bf16x8 af = *(const AS3 bf16x8 *)(s3 + L::CA + (part * W4_MT + i) * 1024 + frow * 64 + fgrp * 16);
 #pragma unroll
                 for (int j = 0; j < W4_NT; ++j) acc[i][j] = mfma_bf16(bfr[j], af, acc[i][j]);
             }
@@ -340,8 +367,9 @@ void tile_w4_kernel(Problem p) {
     auto clear_correction = [&]() {
         // this wave's parts (m-tile w: 3 KB) and its scales (2 KB)
         const u32x4 z = {0u, 0u, 0u, 0u};
+        if (wave < 4)  // m-tile w's three parts (8 waves: waves 0-3)
 #pragma unroll
-        for (int part = 0; part < 3; ++part) *(AS3 u32x4 *)(s3 + W4_CA + (part * W4_MT + wave) * 1024 + lane * 16) = z;
+            for (int part = 0; part < 3; ++part) *(AS3 u32x4 *)(s3 + L::CA + (part * W4_MT + wave) * 1024 + lane * 16) = z;
 #pragma unroll
         for (int j = 0; j < W4_NT; ++j) *(AS3 u32x4 *)(s3 + cb_w + j * 1024 + lane * 16) = z;
     };
@@ -366,16 +394,26 @@ void tile_w4_kernel(Problem p) {
     // activations landed (8-bit: also the codes of stages 0 .. 2, all of it); group 0 read, stage
     // 0's fragments read and its B fragments made
     if constexpr (CORR) clear_correction();
-    load_a(0, 0);
-    load_b(0, 0);
-    load_a(1, 1);
-    load_a(2, 2);
-    load_a(3, 3);
-    load_a(4, 4);
-    load_b(1, 1);
-    load_a(5, 5);
+    // (the loads the loop's stages -6 .. -1 would have issued, in their order)
+    if constexpr (NW == 4) {
+        load_a(0, 0);
+        load_b(0, 0);
+        load_a(1, 1);
+        load_a(2, 2);
+        load_a(3, 3);
+        load_a(4, 4);
+        load_b(1, 1);
+        load_a(5, 5);
+    } else {
+        load_a(half, half);
+        load_b(0, 0);
+        load_a(2 + half, 2 + half);
+        load_a(4 + half, 4 + half);
+        load_b(1, 1);
+    }
     if constexpr (U4) {
-        GE_WAIT_VM(4 * W4_LA + W4_LB);
+        // after the activations of stages 0 and 1 come the later activation loads and one group's
+        GE_WAIT_VM(NW == 4 ? 4 + W4_LB : 2 + W4_LB);
     } else {
         load_q(0);
         load_q(1);
@@ -399,16 +437,25 @@ void tile_w4_kernel(Problem p) {
 #pragma unroll
         for (int u = 0; u < W4_UNROLL; ++u) {
             const int s = s0 + u;
+            // (each branch names its wait count as a constant)
             if constexpr (U4) {
-                if ((u & 3) == 2)
-                    GE_WAIT_VM(w4_inflight(2));
+                if ((u & 3) == 0)
+                    GE_WAIT_VM(w4_inflight(NW, 0));
+                else if ((u & 3) == 1)
+                    GE_WAIT_VM(w4_inflight(NW, 1));
+                else if ((u & 3) == 2)
+                    GE_WAIT_VM(w4_inflight(NW, 2));
                 else
-                    GE_WAIT_VM(w4_inflight(0));
+                    GE_WAIT_VM(w4_inflight(NW, 3));
             } else {
-                if ((u & 3) == 3)
-                    GE_WAIT_VM(w8_inflight(3));
+                if ((u & 3) == 0)
+                    GE_WAIT_VM(w8_inflight(NW, 0));
+                else if ((u & 3) == 1)
+                    GE_WAIT_VM(w8_inflight(NW, 1));
+                else if ((u & 3) == 2)
+                    GE_WAIT_VM(w8_inflight(NW, 2));
                 else
-                    GE_WAIT_VM(w8_inflight(0));
+                    GE_WAIT_VM(w8_inflight(NW, 3));
             }
             lds_barrier();
             GE_DEBUG_BARRIER();
@@ -428,7 +475,10 @@ void tile_w4_kernel(Problem p) {
                 if (apply) apply_tile(((u >> 2) + 1) & 1, i, j);
                 U[i][j] = mfma_bf16(fb[u & 1][j], fa[u & 1][i], first ? f32x4{0.f, 0.f, 0.f, 0.f} : U[i][j]);
                 if (q == 0) {
-                    load_a(s + W4_AD, (u + W4_AD) & (W4_UNROLL - 1));
+                    if constexpr (NW == 4)
+                        load_a(s + W4_AD, (u + W4_AD) & (W4_UNROLL - 1));
+                    else if ((u & 1) == 0)  // the pair s + 6, s + 7 (the slots of s - 2, s - 1)
+                        load_a(s + W4_AD + half, (u + W4_AD + half) & (W4_UNROLL - 1));
                     if ((u & 3) == 2) {
                         load_b((s + 6) >> 2, ((u + 6) >> 2) & 1);
                         read_group(((u + 2) >> 2) & 1);  // group (s + 2) / 4, loaded at stage s - 4
@@ -494,9 +544,12 @@ void tile_w4_kernel(Problem p) {
 
 }  // namespace
 
+// 8 waves (64 x 256 tiles) where N allows, else 4 (64 x 128)
+static int w4_waves(const Problem &p) { return p.N % W4L<8>::BN == 0 ? 8 : 4; }
+
 bool tile_w4_supported(const Problem &p) {
     if (p.mode != MODE_W4 || p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
-    if ((p.N % W4_BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
+    if ((p.N % W4L<4>::BN) || (p.K % 128) || (p.lda & 7) || !al16(p.A) || !al16(p.B)) return false;
     if (((int64_t)(p.M - 1) * p.lda + p.K) * 2 >= (1ll << 31)) return false;  // X through 32-bit offsets
     if (((int64_t)(p.K / 128) * p.ld_s + p.N) * 2 >= (1ll << 31)) return false;
     if (p.wfmt == WFMT_U4) {
@@ -510,28 +563,38 @@ bool tile_w4_supported(const Problem &p) {
 }
 
 const char *tile_w4_kernel_name(const Problem &p) {
-    return p.wfmt == WFMT_U4 ? "tile_w4_bf16_64x128x32" : p.wfmt == WFMT_U8 ? "tile_w8_u8_64x128x32" : "tile_w8_fp8_64x128x32";
+    const bool w8 = w4_waves(p) == 8;
+    switch (p.wfmt) {
+    case WFMT_U8: return w8 ? "tile_w8_u8_64x256x32" : "tile_w8_u8_64x128x32";
+    case WFMT_FP8: return w8 ? "tile_w8_fp8_64x256x32" : "tile_w8_fp8_64x128x32";
+    default: return w8 ? "tile_w4_bf16_64x256x32" : "tile_w4_bf16_64x128x32";
+    }
 }
 
-template <int WF>
+template <int WF, int NW>
 static hipError_t launch_wf(const Problem &p, hipStream_t s) {
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel<WF>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           W4_LDS);
+        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel<WF, NW>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, W4L<NW>::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4_BN);
-    hipLaunchKernelGGL(tile_w4_kernel<WF>, dim3(tiles), dim3(T_THREADS), W4_LDS, s, p);
+    const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4L<NW>::BN);
+    hipLaunchKernelGGL((tile_w4_kernel<WF, NW>), dim3(tiles), dim3(W4L<NW>::THREADS), W4L<NW>::LDS, s, p);
     return hipGetLastError();
+}
+
+template <int WF>
+static hipError_t launch_w(const Problem &p, hipStream_t s) {
+    return w4_waves(p) == 8 ? launch_wf<WF, 8>(p, s) : launch_wf<WF, 4>(p, s);
 }
 
 hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
     if (!tile_w4_supported(p)) return hipErrorInvalidValue;
-    if (p.wfmt == WFMT_U8) return launch_wf<WFMT_U8>(p, s);
-    if (p.wfmt == WFMT_FP8) return launch_wf<WFMT_FP8>(p, s);
-    return launch_wf<WFMT_U4>(p, s);
+    if (p.wfmt == WFMT_U8) return launch_w<WFMT_U8>(p, s);
+    if (p.wfmt == WFMT_FP8) return launch_w<WFMT_FP8>(p, s);
+    return launch_w<WFMT_U4>(p, s);
 }
 
 }  // namespace ge

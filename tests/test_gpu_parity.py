@@ -568,7 +568,8 @@ def test_w4_prepacked_tile_path(M, N, K):
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
     p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
-    assert p.kernel.startswith("tile_w4")
+    # 8 waves and 256 columns per workgroup where N % 256 == 0, else 4 waves and 128 columns
+    assert p.kernel == f"tile_w4_bf16_64x{256 if N % 256 == 0 else 128}x32"
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 

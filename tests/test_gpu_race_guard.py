@@ -59,4 +59,4 @@ def test_ge_log_prints_plan_decisions():
     lines = [l for l in r.stderr.splitlines() if l.startswith("ge: plan")]
     assert len(lines) == 2, r.stderr[-2000:]
     assert "kind=generic M=16 N=4096 K=8192" in lines[0] and "kernel=skinny_bf16_m16_128col_streamk" in lines[0]
-    assert "kind=w4 M=512 N=8192 K=8192" in lines[1] and "kernel=tile_w4_bf16_64x128x32" in lines[1]
+    assert "kind=w4 M=512 N=8192 K=8192" in lines[1] and "kernel=tile_w4_bf16_64x256x32" in lines[1]

@@ -52,11 +52,12 @@ def test_w8_plans_pick_the_streaming_kernel_for_small_M():
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(17, 128, 128), (64, 256, 1024), (100, 384, 4224), (512, 1024, 2048)])
 def test_w8_tile_kernel(fmt, M, N, K):
-    # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes; K = 4224
-    # is 33 groups, not a whole number of the kernel's two-group loop trips
+    # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes (8 waves,
+    # 256 columns per workgroup, where N % 256 == 0; else 4 waves, 128 columns); K = 4224 is 33
+    # groups, not a whole number of the kernel's two-group loop trips
     w = BASE[fmt].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=3 * M + K)
-    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x128x32"
+    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{256 if N % 256 == 0 else 128}x32"
     assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} tile {M}x{N}x{K}")
 
 
@@ -80,7 +81,7 @@ def test_w8_tile_strided_operands(fmt):
     Wf[:, :N] = torch.from_numpy(inp["Wq"]).to(DEV)
     out = ge.w4_gemm(Xf[:, :K], Wf[:, :N], d["scales"], bias=d.get("bias"), group=inp["group"],
                      zero_point=inp["zero_point"], fmt=fmt)
-    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x128x32"
+    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x256x32"
     assert_close(out, oracle.reference(inp), TOL_BF16, f"{fmt} tile strided")
 
 
