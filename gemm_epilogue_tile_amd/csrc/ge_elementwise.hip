@@ -248,6 +248,10 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm(int32_t M, int32_t N
     }
 }
 
+// cache policy of the row stores: non-temporal (each byte is written once per call; 2048x4096:
+// 13.7 -> 11.6-11.8 us; non-temporal loads of a and x as well measured 12.0-12.3 us)
+constexpr int EW_NT = 2;
+
 // Rows of at most 4096 bf16 elements: one wave per row, no LDS and no barrier.  Lane l owns
 // the 8-element chunks c * 64 + l (c < CH); every load of the row (a, x and w) is requested
 // before any is used, through buffer loads that read zeros past the row's end, and the
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int3
                 wr[q] = pack_bf16x2(r[c][2 * q], r[c][2 * q + 1]);
                 wo[q] = pack_bf16x2(r[c][2 * q] * rrms * bf16lo(vw[c][q]), r[c][2 * q + 1] * rrms * bf16hi(vw[c][q]));
             }
-            __builtin_amdgcn_raw_buffer_store_b128(wr, rr, (c * 64 + lane) * 16, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(wo, ro, (c * 64 + lane) * 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(wr, rr, (c * 64 + lane) * 16, 0, EW_NT);
+            __builtin_amdgcn_raw_buffer_store_b128(wo, ro, (c * 64 + lane) * 16, 0, EW_NT);
         }
     }
 }

@@ -14,7 +14,7 @@
 //   A in LDS        [BM][32] bf16, 16-byte chunk c of row r at c ^ ((r>>1)&3):
 //                   conflict-free 128-bit fragment reads.
 //   B in LDS        KN layout: [32][BN] as stored in memory, 16-byte chunk c of
-//                   row k at c ^ ((k&3)<<1); fragments come from the gfx950
+//                   row k at c ^ ((k&3)<<1) ^ (((k>>3)&1)<<3); fragments come from the gfx950
 //                   transposing read ds_read_b64_tr_b16, which turns four
 //                   rows x sixteen columns into one k-vector per column.
 //                   NK layout: [BN][32] like A.
@@ -114,39 +114,59 @@ void tile_kernel(Problem p) {
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q) {
             const int k = (wave * C::B_INSTR + q) * C::B_ROWS_PER_INSTR + krow_l;
-            const int chunk = slot ^ ((k & 3) << 1);
+            const int chunk = slot ^ swz_b_key(k);
             // columns past N read zeros (fixed per lane, so folded in once)
             b_off[q] = n0 + chunk * 8 < p.N ? (uint32_t)(k * p.ldb * 2) + chunk * 16 : OOB;
         }
     }
 
-    // direct loads of one stage (K offset s * 32) into LDS buffer s % T_NS: the buffer
-    // resources are formed once per stage, the C::LOADS instructions issued one at a time
+    // direct loads of one stage (K offset s * 32) into LDS buffer s % T_NS.  Stages are loaded in
+    // order, and the buffer resources of the next one are kept in scalar registers and advanced by
+    // one stage at a time: the base moves by the stage's step, the range shrinks by as much and stays
+    // at 0 once it is empty (a step beyond 2^31 - 1 bytes empties it at once: every operand is
+    // below 2 GiB).  No 64-bit multiply is left in the loop.
     struct StageLoads {
         i32x4 ra, rb[C::NB];
         uint32_t adst, bdst[C::NB];
         bool akin, bkin;
     };
-    auto stage_loads = [&](int s) {
+    auto rsrc_at = [](uint64_t a, int32_t range) {
+        i32x4 r;
+        r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+        r[2] = __builtin_amdgcn_readfirstlane(range);
+        r[3] = 0x00020000;
+        return r;
+    };
+    constexpr int32_t A_STEP = T_BK * 2;
+    const int64_t b_step64 = B_NK ? (int64_t)T_BK * 2 : (int64_t)T_BK * p.ldb * 2;
+    const int32_t b_step = b_step64 < 0x7fffffffll ? (int32_t)b_step64 : 0x7fffffff;
+    uint64_t a_ptr = (uint64_t)(uintptr_t)p.A + (uint64_t)((int64_t)m0 * p.lda * 2);
+    int32_t a_rng = (int32_t)(((int64_t)(p.M - 1 - m0) * p.lda + p.K) * 2);
+    uint64_t b_ptr[C::NB];
+#pragma unroll
+    for (int d = 0; d < C::NB; ++d)
+        b_ptr[d] = (uint64_t)(uintptr_t)(d == 0 ? p.B : p.B2) + (uint64_t)(B_NK ? (int64_t)n0 * p.ldb * 2 : (int64_t)n0 * 2);
+    int32_t b_rng = (int32_t)(B_NK ? ((int64_t)(p.N - 1 - n0) * p.ldb + p.K) * 2
+                                   : ((int64_t)(p.K - 1) * p.ldb + (p.N - n0)) * 2);
+    int k_next = 0;  // K offset of the next stage to load
+    auto stage_loads = [&](int s) {  // s: the next stage in load order
         StageLoads L;
-        const int k0 = s * T_BK;
         const int buf = s & (T_NS - 1);
-        L.ra = make_rsrc((const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2,
-                         ((int64_t)(p.M - 1 - m0) * p.lda + (p.K - k0)) * 2);
-        L.akin = k0 + achunk * 8 < p.K;
+        L.ra = rsrc_at(a_ptr, a_rng);
+        L.akin = k_next + achunk * 8 < p.K;
         L.bkin = L.akin;
         L.adst = lds0 + buf * C::A_STAGE + wave * C::A_INSTR * 1024;
 #pragma unroll
         for (int d = 0; d < C::NB; ++d) {
-            const void *B = d == 0 ? p.B : p.B2;
             L.bdst[d] = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE + wave * C::B_INSTR * 1024;
-            if constexpr (B_NK)
-                L.rb[d] = make_rsrc((const char *)B + ((int64_t)n0 * p.ldb + k0) * 2,
-                                    ((int64_t)(p.N - 1 - n0) * p.ldb + (p.K - k0)) * 2);
-            else
-                L.rb[d] = make_rsrc((const char *)B + ((int64_t)k0 * p.ldb + n0) * 2,
-                                    ((int64_t)(p.K - 1 - k0) * p.ldb + (p.N - n0)) * 2);
+            L.rb[d] = rsrc_at(b_ptr[d], b_rng);
+            b_ptr[d] += (uint64_t)b_step64;
         }
+        a_ptr += A_STEP;
+        a_rng = a_rng > A_STEP ? a_rng - A_STEP : 0;
+        b_rng = b_rng > b_step ? b_rng - b_step : 0;
+        k_next += T_BK;
         return L;
     };
     auto issue_load = [&](const StageLoads &L, int q) {  // q < C::LOADS, compile-time after unrolling

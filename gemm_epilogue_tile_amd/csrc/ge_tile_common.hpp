@@ -40,9 +40,13 @@ __device__ __forceinline__ void load_lds16(const i32x4 &r, uint32_t lds_addr, ui
 
 // [rows][32] tiles (64-byte rows): 16-byte chunk c of row r lives at c ^ ((r >> 1) & 3)
 __device__ __forceinline__ int swz_a(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
-// [32][BN] tiles: 16-byte chunk c of row k lives at c ^ ((k & 3) << 1)
+// [32][BN] tiles (BN >= 128): 16-byte chunk c of row k lives at c ^ swz_b_key(k).  The transposing
+// fragment read covers rows k0 .. k0 + 3 and k0 + 8 .. k0 + 11 in one half-wave: bits 0-1 of k spread
+// the first four rows over 8 chunks, bit 3 moves the other four to the next 8 (without it the two
+// sets share banks; 1.74 against 1.10 ns per read per CU in an LDS-bound probe).
+__device__ __forceinline__ int swz_b_key(int k) { return ((k & 3) << 1) ^ (((k >> 3) & 1) << 3); }
 template <int BN>
-__device__ __forceinline__ int swz_b(int k, int chunk) { return k * (BN * 2) + ((chunk ^ ((k & 3) << 1)) << 4); }
+__device__ __forceinline__ int swz_b(int k, int chunk) { return k * (BN * 2) + ((chunk ^ swz_b_key(k)) << 4); }
 
 // 4 consecutive elements as fp32 (8-byte bf16 or 16-byte fp32 access)
 __device__ __forceinline__ void load4(const void *p, int32_t type, int64_t off, float v[4]) {
