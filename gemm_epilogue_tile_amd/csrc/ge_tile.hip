@@ -48,18 +48,21 @@ struct Cfg {
     static constexpr int MT = WTM / 16, NT = WTN / 16;   // 16x16 MFMA tiles per wave
     static constexpr int NB = DUAL ? 2 : 1;
     static constexpr int A_STAGE = BM * T_BK * 2;        // bytes of one stage
+    static constexpr int A_PAIR = 2 * A_STAGE;           // A is staged two stages at a time: [BM][64]
     static constexpr int B_STAGE = BN * T_BK * 2;
-    static constexpr int B_BASE = T_NS * A_STAGE;        // LDS: all A stages, then all B stages
+    static constexpr int B_BASE = T_NS * A_STAGE;        // LDS: the two A pair buffers, then all B stages
     static constexpr int LDS = T_NS * (A_STAGE + NB * B_STAGE);
-    static constexpr int A_INSTR = A_STAGE / 1024 / 4;   // 1 KB direct loads per wave per stage
-    static constexpr int B_INSTR = B_STAGE / 1024 / 4;
-    static constexpr int LOADS = A_INSTR + NB * B_INSTR; // per wave per stage
+    static constexpr int AP_INSTR = A_PAIR / 1024 / 4;   // 1 KB direct loads per wave per A pair
+    static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // ... per wave per B stage
+    static constexpr int NBI = NB * B_INSTR;
+    static constexpr int LOADS = AP_INSTR + NBI;         // most loads a wave issues in one stage
     static constexpr int B_ROWS_PER_INSTR = 1024 / (BN * 2);  // KN: k rows one load instruction fills
     static_assert(WM * WN == 4, "four waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(A_INSTR >= 1 && B_INSTR >= 1 && A_INSTR * 4096 == A_STAGE && B_INSTR * 4096 == B_STAGE, "loads");
+    static_assert(T_NS == 4, "two A pairs: four stages");
+    static_assert(AP_INSTR >= 1 && B_INSTR >= 1 && AP_INSTR * 4096 == A_PAIR && B_INSTR * 4096 == B_STAGE, "loads");
     static_assert(B_NK || BN == 256 || BN == 128 || BN == 512, "KN row width");
-    static_assert((T_NS - 1) * A_STAGE + (MT - 1) * 1024 + 64 < 65536, "A fragment offsets fit the ds offset field");
+    static_assert(A_PAIR + (MT - 1) * 2048 + 128 < 65536, "A fragment offsets fit the ds offset field");
     static_assert((NB * T_NS - 1) * B_STAGE < 65536, "B stage offsets fit the ds offset field");
 };
 
@@ -89,23 +92,33 @@ void tile_kernel(Problem p) {
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- direct-load lane offsets (constant across stages; k advances in the resource base) ----
-    // A / B^T stage: [rows][32] = 16 rows x 4 chunks per 1 KB instruction; lane -> row lane/4,
-    // LDS slot lane%4, which holds logical chunk (lane%4) ^ ((row>>1)&3).
-    const int arow_l = lane >> 2;
-    const int achunk = (lane & 3) ^ ((arow_l >> 1) & 3);
-    uint32_t a_off[C::A_INSTR];
+    // A pair (stages 2t, 2t + 1): [BM][64] with 128-byte rows, so that every load fetches whole
+    // 128-byte lines (8 rows x 8 chunks per 1 KB instruction; 64-byte rows took two line requests
+    // per 128 bytes); lane -> row 8 i + lane/8 of instruction i, LDS slot lane%8, which holds
+    // logical chunk (lane%8) ^ ((row>>1)&7) (stage 2t: chunks 0-3, stage 2t + 1: chunks 4-7).  Bit
+    // 2 of that swizzle is the parity of i (AP_INSTR is even), so a lane's chunk takes two values.
+    const int arow_l = lane >> 3;
+    int achunk[2];
 #pragma unroll
-    for (int q = 0; q < C::A_INSTR; ++q) {
-        const int row = (wave * C::A_INSTR + q) * 16 + arow_l;
-        a_off[q] = (uint32_t)(row * p.lda * 2) + achunk * 16;
+    for (int e = 0; e < 2; ++e) achunk[e] = (lane & 7) ^ ((arow_l >> 1) & 7) ^ (4 * e);
+    static_assert(C::AP_INSTR % 2 == 0, "instruction parity");
+    uint32_t a_off[C::AP_INSTR];
+#pragma unroll
+    for (int q = 0; q < C::AP_INSTR; ++q) {
+        const int row = (wave * C::AP_INSTR + q) * 8 + arow_l;
+        a_off[q] = (uint32_t)(row * p.lda * 2) + ((lane & 7) ^ ((row >> 1) & 7)) * 16;
     }
-    // B stage: KN -> [32][BN], an instruction fills B_ROWS_PER_INSTR k rows; NK -> like A.
+    // B stage: KN -> [32][BN], an instruction fills B_ROWS_PER_INSTR k rows; NK -> [BN][32]:
+    // 16 rows x 4 chunks per 1 KB instruction, lane -> row lane/4, LDS slot lane%4, which holds
+    // logical chunk (lane%4) ^ ((row>>1)&3).
+    const int brow_l = lane >> 2;
+    const int bchunk = (lane & 3) ^ ((brow_l >> 1) & 3);
     uint32_t b_off[C::B_INSTR];
     if constexpr (B_NK) {
 #pragma unroll
         for (int q = 0; q < C::B_INSTR; ++q) {
-            const int row = (wave * C::B_INSTR + q) * 16 + arow_l;
-            b_off[q] = (uint32_t)(row * p.ldb * 2) + achunk * 16;
+            const int row = (wave * C::B_INSTR + q) * 16 + brow_l;
+            b_off[q] = (uint32_t)(row * p.ldb * 2) + bchunk * 16;
         }
     } else {
         constexpr int CPR = BN / 8;  // 16-byte chunks per k row
@@ -120,15 +133,21 @@ void tile_kernel(Problem p) {
         }
     }
 
-    // direct loads of one stage (K offset s * 32) into LDS buffer s % T_NS.  Stages are loaded in
-    // order, and the buffer resources of the next one are kept in scalar registers and advanced by
-    // one stage at a time: the base moves by the stage's step, the range shrinks by as much and stays
-    // at 0 once it is empty (a step beyond 2^31 - 1 bytes empties it at once: every operand is
-    // below 2 GiB).  No 64-bit multiply is left in the loop.
-    struct StageLoads {
-        i32x4 ra, rb[C::NB];
-        uint32_t adst, bdst[C::NB];
-        bool akin, bkin;
+    // Direct loads: B stage s (K offset 32 s) into B buffer s % T_NS; A pair t (K offset 64 t, the
+    // stages 2t and 2t + 1) into A pair buffer t % 2.  Both are loaded in order, and the buffer
+    // resources of the next B stage and the next A pair are kept in scalar registers and advanced
+    // one step at a time: the base moves by the step, the range shrinks by as much and stays at 0
+    // once it is empty (a step beyond 2^31 - 1 bytes empties it at once: every operand is below
+    // 2 GiB).  No 64-bit multiply is left in the loop.
+    struct BLoads {
+        i32x4 rb[C::NB];
+        uint32_t bdst[C::NB];
+        bool bkin;
+    };
+    struct ALoads {
+        i32x4 ra;
+        uint32_t adst;
+        bool akin[2];  // by instruction parity
     };
     auto rsrc_at = [](uint64_t a, int32_t range) {
         i32x4 r;
@@ -138,7 +157,7 @@ void tile_kernel(Problem p) {
         r[3] = 0x00020000;
         return r;
     };
-    constexpr int32_t A_STEP = T_BK * 2;
+    constexpr int32_t A_STEP = 2 * T_BK * 2;  // one pair
     const int64_t b_step64 = B_NK ? (int64_t)T_BK * 2 : (int64_t)T_BK * p.ldb * 2;
     const int32_t b_step = b_step64 < 0x7fffffffll ? (int32_t)b_step64 : 0x7fffffff;
     uint64_t a_ptr = (uint64_t)(uintptr_t)p.A + (uint64_t)((int64_t)m0 * p.lda * 2);
@@ -149,47 +168,61 @@ void tile_kernel(Problem p) {
         b_ptr[d] = (uint64_t)(uintptr_t)(d == 0 ? p.B : p.B2) + (uint64_t)(B_NK ? (int64_t)n0 * p.ldb * 2 : (int64_t)n0 * 2);
     int32_t b_rng = (int32_t)(B_NK ? ((int64_t)(p.N - 1 - n0) * p.ldb + p.K) * 2
                                    : ((int64_t)(p.K - 1) * p.ldb + (p.N - n0)) * 2);
-    int k_next = 0;  // K offset of the next stage to load
-    auto stage_loads = [&](int s) {  // s: the next stage in load order
-        StageLoads L;
+    int kb_next = 0, ka_next = 0;  // K offsets of the next B stage and the next A pair to load
+    auto b_loads = [&](int s) {  // s: the next B stage in load order
+        BLoads L;
         const int buf = s & (T_NS - 1);
-        L.ra = rsrc_at(a_ptr, a_rng);
-        L.akin = k_next + achunk * 8 < p.K;
-        L.bkin = L.akin;
-        L.adst = lds0 + buf * C::A_STAGE + wave * C::A_INSTR * 1024;
+        L.bkin = kb_next + bchunk * 8 < p.K;
 #pragma unroll
         for (int d = 0; d < C::NB; ++d) {
             L.bdst[d] = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE + wave * C::B_INSTR * 1024;
             L.rb[d] = rsrc_at(b_ptr[d], b_rng);
             b_ptr[d] += (uint64_t)b_step64;
         }
-        a_ptr += A_STEP;
-        a_rng = a_rng > A_STEP ? a_rng - A_STEP : 0;
         b_rng = b_rng > b_step ? b_rng - b_step : 0;
-        k_next += T_BK;
+        kb_next += T_BK;
         return L;
     };
-    auto issue_load = [&](const StageLoads &L, int q) {  // q < C::LOADS, compile-time after unrolling
-        if (q < C::A_INSTR) {
-            load_lds16(L.ra, L.adst + q * 1024, L.akin ? a_off[q] : OOB);
-        } else {
-            const int d = (q - C::A_INSTR) / C::B_INSTR, qq = (q - C::A_INSTR) % C::B_INSTR;
-            if constexpr (B_NK)
-                load_lds16(L.rb[d], L.bdst[d] + qq * 1024, L.bkin ? b_off[qq] : OOB);
-            else
-                load_lds16(L.rb[d], L.bdst[d] + qq * 1024, b_off[qq]);
-        }
+    auto a_loads = [&](int t) {  // t: the next A pair in load order
+        ALoads L;
+        L.ra = rsrc_at(a_ptr, a_rng);
+        L.akin[0] = ka_next + achunk[0] * 8 < p.K;
+        L.akin[1] = ka_next + achunk[1] * 8 < p.K;
+        L.adst = lds0 + (t & 1) * C::A_PAIR + wave * C::AP_INSTR * 1024;
+        a_ptr += A_STEP;
+        a_rng = a_rng > A_STEP ? a_rng - A_STEP : 0;
+        ka_next += 2 * T_BK;
+        return L;
     };
-    auto load_stage = [&](int s) {
-        const StageLoads L = stage_loads(s);
+    auto issue_a = [&](const ALoads &L, int q) { load_lds16(L.ra, L.adst + q * 1024, L.akin[q & 1] ? a_off[q] : OOB); };
+    auto issue_b = [&](const BLoads &L, int q) {
+        const int d = q / C::B_INSTR, qq = q % C::B_INSTR;
+        if constexpr (B_NK)
+            load_lds16(L.rb[d], L.bdst[d] + qq * 1024, L.bkin ? b_off[qq] : OOB);
+        else
+            load_lds16(L.rb[d], L.bdst[d] + qq * 1024, b_off[qq]);
+    };
+    auto load_a_pair = [&](int t) {
+        const ALoads L = a_loads(t);
 #pragma unroll
-        for (int q = 0; q < C::LOADS; ++q) issue_load(L, q);
+        for (int q = 0; q < C::AP_INSTR; ++q) issue_a(L, q);
+    };
+    auto load_b_stage = [&](int s) {
+        const BLoads L = b_loads(s);
+#pragma unroll
+        for (int q = 0; q < C::NBI; ++q) issue_b(L, q);
     };
 
     // ---- fragment addresses (stage 0; other stages add a compile-time offset) ----
     const int frow = lane & 15, fgrp = lane >> 4;
-    // A fragment i: rows wm*WTM + 16 i + frow, chunk fgrp (k = 8 fgrp .. 8 fgrp + 7)
-    const int a_frag = swz_a(wm * C::WTM + frow, fgrp);
+    // A fragment i of stage 2t + h: rows wm*WTM + 16 i + frow of pair buffer t % 2, logical chunk
+    // 4 h + fgrp (k = 8 fgrp .. 8 fgrp + 7 of the stage); rows 16 apart share the swizzle
+    int a_frag[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = wm * C::WTM + frow;
+        a_frag[h] = row * 128 + (((4 * h + fgrp) ^ ((row >> 1) & 7)) << 4);
+    }
     // B fragment j:
     //   NK: like A;
     //   KN: two transposing reads r = 0, 1: lane (g, jj) points at k = 8 g + 4 r + jj/4 and
@@ -213,7 +246,7 @@ void tile_kernel(Problem p) {
     bf16x8 fa[2][C::MT], fb[2][C::NB][C::NT];
     const AS3 char *s3 = (const AS3 char *)smem;
     auto read_a = [&](int buf, int i, bf16x8 &a) {
-        a = *(const AS3 bf16x8 *)(s3 + a_frag + buf * C::A_STAGE + i * 1024);
+        a = *(const AS3 bf16x8 *)(s3 + a_frag[buf & 1] + (buf >> 1) * C::A_PAIR + i * 2048);
     };
     auto read_b = [&](int buf, int d, int j, bf16x8 &b) {
         const int off = d * T_NS * C::B_STAGE + buf * C::B_STAGE;
@@ -261,15 +294,17 @@ void tile_kernel(Problem p) {
     };
 
     // One stage: the 64 MFMAs of stage s, with the next stage's fragment reads and the direct
-    // loads of stage s + T_NS spread between them so the matrix pipe never waits on a burst of
-    // LDS or memory instructions.  Reads go after MFMAs 0, 3, 6, ..., loads after 1, 4, 7, ...;
-    // an empty asm with a memory clobber pins each one to its slot.
+    // loads issued in this stage (odd s: A pair (s + 3) / 2; every s: B stage s + T_NS) spread
+    // between them so the matrix pipe never waits on a burst of LDS or memory instructions.
+    // Reads go after MFMAs 0, 3, 6, ..., loads after 1, 4, 7, ...; an empty asm with a memory
+    // clobber pins each one to its slot.
     constexpr int NMF = C::NB * C::NT * C::MT;
     // side-op spacing: reads after MFMAs 0, SP, 2 SP, ..., loads after 1, SP + 1, ...
     constexpr int SP = (3 * (NRD - 1) < NMF && 3 * (C::LOADS - 1) + 1 < NMF) ? 3 : 2;
     static_assert(SP * (NRD - 1) < NMF && SP * (C::LOADS - 1) + 1 < NMF, "side-op slots");
-    auto stage = [&](const StageLoads &L, int nbuf, const bf16x8 (&a)[C::MT], const bf16x8 (&b)[C::NB][C::NT],
-                     bf16x8 (&na)[C::MT], bf16x8 (&nb)[C::NB][C::NT]) {
+    auto stage = [&](bool with_a, const ALoads &LA, const BLoads &LB, int nbuf, const bf16x8 (&a)[C::MT],
+                     const bf16x8 (&b)[C::NB][C::NT], bf16x8 (&na)[C::MT], bf16x8 (&nb)[C::NB][C::NT]) {
+        const int nload = with_a ? C::LOADS : C::NBI;
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int d = q / (C::NT * C::MT), j = (q / C::MT) % C::NT, i = q % C::MT;
@@ -278,8 +313,12 @@ void tile_kernel(Problem p) {
                 asm volatile("" ::: "memory");
                 read_frag(nbuf, q / SP, na, nb);
                 asm volatile("" ::: "memory");
-            } else if (q % SP == 1 && q / SP < C::LOADS) {
-                issue_load(L, q / SP);
+            } else if (q % SP == 1 && q / SP < nload) {
+                const int l = q / SP;  // A pair loads first, then the B stage's
+                if (with_a && l < C::AP_INSTR)
+                    issue_a(LA, l);
+                else
+                    issue_b(LB, with_a ? l - C::AP_INSTR : l);
             }
         }
     };
@@ -291,10 +330,16 @@ void tile_kernel(Problem p) {
     const int nk = (p.K + T_BK - 1) / T_BK;
     const int nsteps = (nk + T_NS - 1) / T_NS * T_NS;  // whole rounds of T_NS stages (extra stages read zeros)
 
-    // prologue: stages 0..3 in flight, stage 0 landed, its fragments read
-#pragma unroll
-    for (int s = 0; s < T_NS; ++s) load_stage(s);
-    GE_WAIT_VM((T_NS - 1) * C::LOADS);
+    // Load order: stage s issues (odd s) A pair (s + 3) / 2, then B stage s + 4.  The prologue
+    // issues what stages -4 .. -1 would have (B 0, A pair 0, B 1, B 2, A pair 1, B 3), waits for
+    // B 0 and A pair 0 and reads stage 0's fragments.
+    load_b_stage(0);
+    load_a_pair(0);
+    load_b_stage(1);
+    load_b_stage(2);
+    load_a_pair(1);
+    load_b_stage(3);
+    GE_WAIT_VM(3 * C::NBI + C::AP_INSTR);
     lds_barrier();
     read_frags(0, fa[0], fb[0]);
 
@@ -302,12 +347,20 @@ void tile_kernel(Problem p) {
 #pragma unroll
         for (int b = 0; b < T_NS; ++b) {
             const int s = s0 + b;
-            // stage s+1 landed (own loads), visible to all; every wave is done reading stage s
-            GE_WAIT_VM((T_NS - 2) * C::LOADS);
+            // stage s+1 landed (own loads), visible to all; every wave is done reading stage s.  Still
+            // in flight may be what stages s-2 and s-1 issued after stage s+1's loads: the B stages
+            // s+2 and s+3 and, for even s, the A pair of stages s+2 and s+3 (issued by stage s-1)
+            if (b & 1)
+                GE_WAIT_VM(2 * C::NBI);
+            else
+                GE_WAIT_VM(2 * C::NBI + C::AP_INSTR);
             lds_barrier();
             GE_DEBUG_BARRIER();
-            const StageLoads L = stage_loads(s + T_NS);  // into buffer b, three stages ahead
-            stage(L, (b + 1) & (T_NS - 1), fa[b & 1], fb[b & 1], fa[(b + 1) & 1], fb[(b + 1) & 1]);
+            // odd s: A pair (s + 3) / 2 into the pair buffer of stages s - 1, s (read by now)
+            ALoads LA{};
+            if (b & 1) LA = a_loads((s + 3) >> 1);
+            const BLoads LB = b_loads(s + T_NS);  // into buffer b, three stages ahead
+            stage((b & 1) != 0, LA, LB, (b + 1) & (T_NS - 1), fa[b & 1], fb[b & 1], fa[(b + 1) & 1], fb[(b + 1) & 1]);
         }
     }
 #undef GE_WAIT_VM
