@@ -203,13 +203,20 @@ void tile_w4_kernel(Problem p) {
         const i32x4 rs = rsrc32((const char *)p.scales + so, in ? (uint32_t)(s_bytes - so) : 0u);
         load_lds16(rs, lds0 + scales_w + slot * 1024, s_src);
     };
-    // 8-bit codes of stage d (rows 32 d .. 32 d + 31, the wave's 32 columns): lane l loads row l / 2,
-    // bytes 16 (l % 2) .. + 15, into slot d % 4 of the wave's ring ([32 rows][32 bytes])
-    const uint32_t q_src = (uint32_t)((int64_t)(lane >> 1) * p.ldb + n0 + wave * 32 + (lane & 1) * 16);
+    // 8-bit codes of stage d (rows 32 d .. 32 d + 31, the workgroup's BN columns) go to slot d % 4 of
+    // a ring the waves share: [32 rows][BN bytes], 16-byte chunk c of row r at c ^ q_swz(r), so that
+    // the transposing reads of 16 rows hit distinct banks.  Wave w loads rows 1024 / BN of them, whole
+    // 128-byte lines (a wave's own 32 columns are a quarter line per row: four times the line
+    // requests); lane l row l / (BN / 16) of those, slot l % (BN / 16).  A wave reads other waves'
+    // codes, after the stage barrier that follows every wave's wait for them.
+    constexpr int QCH = L::BN / 16, Q_STAGE = 32 * L::BN;
+    auto q_swz = [](int r) { return NW == 8 ? (r & 15) : ((r >> 1) & 7); };
+    const int q_row = (1024 / L::BN) * wave + lane / QCH;
+    const uint32_t q_src = (uint32_t)((int64_t)q_row * p.ldb + n0 + (((lane % QCH) ^ q_swz(q_row)) * 16));
     auto load_q = [&](int d) {
         const int64_t ro = (int64_t)d * 32 * p.ldb;
         const i32x4 rq = rsrc32((const char *)p.B + ro, d < nst ? (uint32_t)(b_bytes - ro) : 0u);
-        load_lds16(rq, lds0 + codes_w + (d & 3) * 1024, q_src);
+        load_lds16(rq, lds0 + L::CODES + (d & 3) * Q_STAGE + wave * 1024, q_src);
     };
 
     const int frow = lane & 15, fgrp = lane >> 4;
@@ -246,16 +253,22 @@ void tile_w4_kernel(Problem p) {
         dq[e][w] = (src & nib_mask) | magic;
         if (w == 3) fb[dd & 1][e] = __builtin_bit_cast(bf16x8, dq[e]);
     };
-    // 8-bit: the B fragments of stage d from the wave's slot d % 4.  In each 16-lane group (k octet
-    // fgrp) lane pair 2 r, 2 r + 1 names row 8 fgrp + r, bytes 16 j .. 16 j + 15, and lane frow
+    // 8-bit: the B fragments of stage d from slot d % 4 of the shared ring (the wave's column blocks
+    // 2 w + j, j = 0, 1).  In each 16-lane group (k octet fgrp) lane pair 2 r, 2 r + 1 names row
+    // 8 fgrp + r, the 16 bytes of block 2 w + j (wherever the swizzle put them), and lane frow
     // receives column 16 j + frow at k = 8 fgrp .. + 7 (byte order = k order)
     typedef int v2i __attribute__((ext_vector_type(2)));
     v2i qraw[W4_NT];
-    const uint32_t q_frag = codes_w + (8 * fgrp + (frow >> 1)) * 32 + (frow & 1) * 8;
+    uint32_t q_frag[W4_NT];
+#pragma unroll
+    for (int e = 0; e < W4_NT; ++e) {
+        const int r = 8 * fgrp + (frow >> 1);
+        q_frag[e] = L::CODES + r * L::BN + (((2 * wave + e) ^ q_swz(r)) * 16) + (frow & 1) * 8;
+    }
     auto read_q = [&](int d) {
 #pragma unroll
         for (int e = 0; e < W4_NT; ++e)
-            qraw[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 v2i *)(s3 + q_frag + (d & 3) * 1024 + e * 16));
+            qraw[e] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((AS3 v2i *)(s3 + q_frag[e] + (d & 3) * Q_STAGE));
     };
     // bytes -> bf16 fragment e of stage d (in two halves, h = 0, 1: one dword of 4 codes each)
     auto convert_q = [&](int dd, int e, int h) {
