@@ -55,7 +55,9 @@ struct Cfg {
     static constexpr int AP_INSTR = A_PAIR / 1024 / 4;   // 1 KB direct loads per wave per A pair
     static constexpr int B_INSTR = B_STAGE / 1024 / 4;   // ... per wave per B stage
     static constexpr int NBI = NB * B_INSTR;
-    static constexpr int LOADS = AP_INSTR + NBI;         // most loads a wave issues in one stage
+    static constexpr int B_PAIR = 2 * B_STAGE;           // NK: B staged two stages at a time, like A
+    static constexpr int BP_INSTR = B_PAIR / 1024 / 4;
+    static constexpr int LOADS = AP_INSTR + (B_NK ? BP_INSTR : NBI);  // most loads a wave issues in one stage
     static constexpr int B_ROWS_PER_INSTR = 1024 / (BN * 2);  // KN: k rows one load instruction fills
     static_assert(WM * WN == 4, "four waves");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
@@ -64,6 +66,7 @@ struct Cfg {
     static_assert(B_NK || BN == 256 || BN == 128 || BN == 512, "KN row width");
     static_assert(A_PAIR + (MT - 1) * 2048 + 128 < 65536, "A fragment offsets fit the ds offset field");
     static_assert((NB * T_NS - 1) * B_STAGE < 65536, "B stage offsets fit the ds offset field");
+    static_assert(!B_NK || (NB == 1 && B_PAIR + (NT - 1) * 2048 + 128 < 65536), "NK B fragment offsets");
 };
 
 template <int BM, int BN, int WM, int WN, bool DUAL, bool B_NK>
@@ -112,17 +115,14 @@ void tile_kernel(Problem p) {
         const int row = (wave * C::AP_INSTR + q) * 8 + arow_l;
         a_off[q] = (uint32_t)(row * p.lda * 2) + ((lane & 7) ^ ((row >> 1) & 7)) * 16;
     }
-    // B stage: KN -> [32][BN], an instruction fills B_ROWS_PER_INSTR k rows; NK -> [BN][32]:
-    // 16 rows x 4 chunks per 1 KB instruction, lane -> row lane/4, LDS slot lane%4, which holds
-    // logical chunk (lane%4) ^ ((row>>1)&3).
-    const int brow_l = lane >> 2;
-    const int bchunk = (lane & 3) ^ ((brow_l >> 1) & 3);
-    uint32_t b_off[C::B_INSTR];
+    // B: KN -> one stage [32][BN] at a time, an instruction fills B_ROWS_PER_INSTR k rows; NK -> B^T
+    // is staged in pairs exactly like A ([BN][64], the same lane mapping and swizzle).
+    uint32_t b_off[B_NK ? C::BP_INSTR : C::B_INSTR];
     if constexpr (B_NK) {
 #pragma unroll
-        for (int q = 0; q < C::B_INSTR; ++q) {
-            const int row = (wave * C::B_INSTR + q) * 16 + brow_l;
-            b_off[q] = (uint32_t)(row * p.ldb * 2) + bchunk * 16;
+        for (int q = 0; q < C::BP_INSTR; ++q) {
+            const int row = (wave * C::BP_INSTR + q) * 8 + arow_l;
+            b_off[q] = (uint32_t)(row * p.ldb * 2) + ((lane & 7) ^ ((row >> 1) & 7)) * 16;
         }
     } else {
         constexpr int CPR = BN / 8;  // 16-byte chunks per k row
@@ -146,7 +146,7 @@ void tile_kernel(Problem p) {
     struct BLoads {
         i32x4 rb[C::NB];
         uint32_t bdst[C::NB];
-        bool bkin;
+        bool bkin[2];  // NK: by instruction parity
     };
     struct ALoads {
         i32x4 ra;
@@ -162,7 +162,7 @@ void tile_kernel(Problem p) {
         return r;
     };
     constexpr int32_t A_STEP = 2 * T_BK * 2;  // one pair
-    const int64_t b_step64 = B_NK ? (int64_t)T_BK * 2 : (int64_t)T_BK * p.ldb * 2;
+    const int64_t b_step64 = B_NK ? (int64_t)2 * T_BK * 2 : (int64_t)T_BK * p.ldb * 2;  // NK: one pair
     const int32_t b_step = b_step64 < 0x7fffffffll ? (int32_t)b_step64 : 0x7fffffff;
     uint64_t a_ptr = (uint64_t)(uintptr_t)p.A + (uint64_t)((int64_t)m0 * p.lda * 2);
     int32_t a_rng = (int32_t)(((int64_t)(p.M - 1 - m0) * p.lda + p.K) * 2);
@@ -173,18 +173,26 @@ void tile_kernel(Problem p) {
     int32_t b_rng = (int32_t)(B_NK ? ((int64_t)(p.N - 1 - n0) * p.ldb + p.K) * 2
                                    : ((int64_t)(p.K - 1) * p.ldb + (p.N - n0)) * 2);
     int kb_next = 0, ka_next = 0;  // K offsets of the next B stage and the next A pair to load
-    auto b_loads = [&](int s) {  // s: the next B stage in load order
+    auto b_loads = [&](int s) {  // s: the next B stage (NK: pair) in load order
         BLoads L;
         const int buf = s & (T_NS - 1);
-        L.bkin = kb_next + bchunk * 8 < p.K;
+        if constexpr (B_NK) {
+            L.bkin[0] = kb_next + achunk[0] * 8 < p.K;
+            L.bkin[1] = kb_next + achunk[1] * 8 < p.K;
+            L.bdst[0] = lds0 + C::B_BASE + (s & 1) * C::B_PAIR + wave * C::BP_INSTR * 1024;
+            L.rb[0] = rsrc_at(b_ptr[0], b_rng);
+            b_ptr[0] += (uint64_t)b_step64;
+            kb_next += 2 * T_BK;
+        } else {
 #pragma unroll
-        for (int d = 0; d < C::NB; ++d) {
-            L.bdst[d] = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE + wave * C::B_INSTR * 1024;
-            L.rb[d] = rsrc_at(b_ptr[d], b_rng);
-            b_ptr[d] += (uint64_t)b_step64;
+            for (int d = 0; d < C::NB; ++d) {
+                L.bdst[d] = lds0 + C::B_BASE + d * T_NS * C::B_STAGE + buf * C::B_STAGE + wave * C::B_INSTR * 1024;
+                L.rb[d] = rsrc_at(b_ptr[d], b_rng);
+                b_ptr[d] += (uint64_t)b_step64;
+            }
+            kb_next += T_BK;
         }
         b_rng = b_rng > b_step ? b_rng - b_step : 0;
-        kb_next += T_BK;
         return L;
     };
     auto a_loads = [&](int t) {  // t: the next A pair in load order
@@ -200,21 +208,23 @@ void tile_kernel(Problem p) {
     };
     auto issue_a = [&](const ALoads &L, int q) { load_lds16(L.ra, L.adst + q * 1024, L.akin[q & 1] ? a_off[q] : OOB); };
     auto issue_b = [&](const BLoads &L, int q) {
-        const int d = q / C::B_INSTR, qq = q % C::B_INSTR;
-        if constexpr (B_NK)
-            load_lds16(L.rb[d], L.bdst[d] + qq * 1024, L.bkin ? b_off[qq] : OOB);
-        else
+        if constexpr (B_NK) {
+            load_lds16(L.rb[0], L.bdst[0] + q * 1024, L.bkin[q & 1] ? b_off[q] : OOB);
+        } else {
+            const int d = q / C::B_INSTR, qq = q % C::B_INSTR;
             load_lds16(L.rb[d], L.bdst[d] + qq * 1024, b_off[qq]);
+        }
     };
     auto load_a_pair = [&](int t) {
         const ALoads L = a_loads(t);
 #pragma unroll
         for (int q = 0; q < C::AP_INSTR; ++q) issue_a(L, q);
     };
+    constexpr int NBL = B_NK ? C::BP_INSTR : C::NBI;  // B loads per load step (NK: per pair)
     auto load_b_stage = [&](int s) {
         const BLoads L = b_loads(s);
 #pragma unroll
-        for (int q = 0; q < C::NBI; ++q) issue_b(L, q);
+        for (int q = 0; q < NBL; ++q) issue_b(L, q);
     };
 
     // ---- fragment addresses (stage 0; other stages add a compile-time offset) ----
@@ -235,8 +245,13 @@ void tile_kernel(Problem p) {
 #pragma unroll
     for (int j = 0; j < C::NT; ++j) {
         if constexpr (B_NK) {
-            b_frag[j][0] = C::B_BASE + swz_a(wn * C::WTN + j * 16 + frow, fgrp);
-            b_frag[j][1] = 0;
+            // like A: row wn*WTN + 16 j + frow of the pair buffer, logical chunk 4 h + fgrp (h: the
+            // stage's half, 0 / 1 in b_frag[j][h])
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = wn * C::WTN + j * 16 + frow;
+                b_frag[j][h] = C::B_BASE + row * 128 + (((4 * h + fgrp) ^ ((row >> 1) & 7)) << 4);
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -255,7 +270,7 @@ void tile_kernel(Problem p) {
     auto read_b = [&](int buf, int d, int j, bf16x8 &b) {
         const int off = d * T_NS * C::B_STAGE + buf * C::B_STAGE;
         if constexpr (B_NK) {
-            b = *(const AS3 bf16x8 *)(s3 + b_frag[j][0] + off);
+            b = *(const AS3 bf16x8 *)(s3 + b_frag[j][buf & 1] + (buf >> 1) * C::B_PAIR);
         } else {
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][0] + off));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 i16x4 *)(s3 + b_frag[j][1] + off));
@@ -306,9 +321,10 @@ void tile_kernel(Problem p) {
     // side-op spacing: reads after MFMAs 0, SP, 2 SP, ..., loads after 1, SP + 1, ...
     constexpr int SP = (3 * (NRD - 1) < NMF && 3 * (C::LOADS - 1) + 1 < NMF) ? 3 : 2;
     static_assert(SP * (NRD - 1) < NMF && SP * (C::LOADS - 1) + 1 < NMF, "side-op slots");
+    // (NK: odd stages issue the A pair and the B pair, even stages nothing)
     auto stage = [&](bool with_a, const ALoads &LA, const BLoads &LB, int nbuf, const bf16x8 (&a)[C::MT],
                      const bf16x8 (&b)[C::NB][C::NT], bf16x8 (&na)[C::MT], bf16x8 (&nb)[C::NB][C::NT]) {
-        const int nload = with_a ? C::LOADS : C::NBI;
+        const int nload = with_a ? C::LOADS : (B_NK ? 0 : C::NBI);
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int d = q / (C::NT * C::MT), j = (q / C::MT) % C::NT, i = q % C::MT;
@@ -334,16 +350,25 @@ void tile_kernel(Problem p) {
     const int nk = (p.K + T_BK - 1) / T_BK;
     const int nsteps = (nk + T_NS - 1) / T_NS * T_NS;  // whole rounds of T_NS stages (extra stages read zeros)
 
-    // Load order: stage s issues (odd s) A pair (s + 3) / 2, then B stage s + 4.  The prologue
-    // issues what stages -4 .. -1 would have (B 0, A pair 0, B 1, B 2, A pair 1, B 3), waits for
-    // B 0 and A pair 0 and reads stage 0's fragments.
-    load_b_stage(0);
-    load_a_pair(0);
-    load_b_stage(1);
-    load_b_stage(2);
-    load_a_pair(1);
-    load_b_stage(3);
-    GE_WAIT_VM(3 * C::NBI + C::AP_INSTR);
+    // Load order: stage s issues (odd s) A pair (s + 3) / 2, then B stage s + 4 (NK: odd s only, the
+    // B pair (s + 3) / 2).  The prologue issues what stages -4 .. -1 would have (B 0, A pair 0, B 1,
+    // B 2, A pair 1, B 3; NK: A pair 0, B pair 0, A pair 1, B pair 1), waits for stage 0's loads and
+    // reads its fragments.
+    if constexpr (B_NK) {
+        load_a_pair(0);
+        load_b_stage(0);
+        load_a_pair(1);
+        load_b_stage(1);
+        GE_WAIT_VM(C::AP_INSTR + C::BP_INSTR);
+    } else {
+        load_b_stage(0);
+        load_a_pair(0);
+        load_b_stage(1);
+        load_b_stage(2);
+        load_a_pair(1);
+        load_b_stage(3);
+        GE_WAIT_VM(3 * C::NBI + C::AP_INSTR);
+    }
     lds_barrier();
     read_frags(0, fa[0], fb[0]);
 
@@ -353,17 +378,31 @@ void tile_kernel(Problem p) {
             const int s = s0 + b;
             // stage s+1 landed (own loads), visible to all; every wave is done reading stage s.  Still
             // in flight may be what stages s-2 and s-1 issued after stage s+1's loads: the B stages
-            // s+2 and s+3 and, for even s, the A pair of stages s+2 and s+3 (issued by stage s-1)
-            if (b & 1)
-                GE_WAIT_VM(2 * C::NBI);
-            else
-                GE_WAIT_VM(2 * C::NBI + C::AP_INSTR);
+            // s+2 and s+3 and, for even s, the A pair of stages s+2 and s+3 (issued by stage s-1).
+            // NK: for even s the A and B pairs of stages s+2 and s+3, for odd s nothing.
+            if constexpr (B_NK) {
+                if (b & 1)
+                    GE_WAIT_VM(0);
+                else
+                    GE_WAIT_VM(C::AP_INSTR + C::BP_INSTR);
+            } else {
+                if (b & 1)
+                    GE_WAIT_VM(2 * C::NBI);
+                else
+                    GE_WAIT_VM(2 * C::NBI + C::AP_INSTR);
+            }
             lds_barrier();
             GE_DEBUG_BARRIER();
-            // odd s: A pair (s + 3) / 2 into the pair buffer of stages s - 1, s (read by now)
+            // odd s: A pair (s + 3) / 2 into the pair buffer of stages s - 1, s (read by now); NK: the
+            // B pair as well
             ALoads LA{};
+            BLoads LB{};
             if (b & 1) LA = a_loads((s + 3) >> 1);
-            const BLoads LB = b_loads(s + T_NS);  // into buffer b, three stages ahead
+            if constexpr (B_NK) {
+                if (b & 1) LB = b_loads((s + 3) >> 1);
+            } else {
+                LB = b_loads(s + T_NS);  // into buffer b, three stages ahead
+            }
             stage((b & 1) != 0, LA, LB, (b + 1) & (T_NS - 1), fa[b & 1], fb[b & 1], fa[(b + 1) & 1], fb[(b + 1) & 1]);
         }
     }
