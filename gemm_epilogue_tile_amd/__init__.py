@@ -30,6 +30,7 @@ lib_path = os.path.join(_HERE, "libgemm_epi.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_HIP, ERR_ALIGN = range(6)
 F32, BF16, U4X2, U8, FP8E4M3 = 0, 1, 2, 3, 4
 LAYOUT_KN, LAYOUT_NK = 0, 1
+ROPE_INTERLEAVED, ROPE_EXACT = 1, 2
 ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 KIND_GENERIC, KIND_SWIGLU, KIND_W4 = 0, 1, 2
 FLAG_BIAS, FLAG_C, FLAG_RESIDUAL, FLAG_NIBBLE_LO_FIRST, FLAG_W4_PREPACKED, FLAG_B_PREPACKED = 1, 2, 4, 8, 16, 32
@@ -544,44 +545,50 @@ def b_prepack(B, *, out=None, stream=None):
     return out
 
 
-def rope_qk(Q, K, cos=None, sin=None, *, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False, out=None,
+def _rope_flags(interleaved, exact):
+    return (ROPE_INTERLEAVED if interleaved else 0) | (ROPE_EXACT if exact else 0)
+
+
+def rope_qk(Q, K, cos=None, sin=None, *, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False, exact=False, out=None,
             out_dtype=None, stream=None):
     """S[b] = alpha * rope(Q[b]) @ rope(K[b])^T with the rotation applied at tile load (one kernel).
 
-    Q [B, Sq, D], K [B, Sk, D] bf16; cos, sin float32 [P, D/2] (None: no rotation)."""
+    Q [B, Sq, D], K [B, Sk, D] bf16; cos, sin float32 [P, D/2] (None: no rotation).  exact: each rotated
+    coordinate is the exact rotation rounded once to bf16 (else fp32, within one bf16 unit of it)."""
     torch = _torch()
     B, Sq, D = Q.shape
     Sk = K.shape[1]
     out = out if out is not None else torch.empty((B, Sq, Sk), dtype=out_dtype or torch.float32, device=Q.device)
     n_pos = cos.shape[0] if cos is not None else 0
     _check(lib().ge_rope_qk_run(B, Sq, Sk, D, _ptr(Q), _ptr(K), _ptr(cos), _ptr(sin), n_pos, q_pos0, k_pos0,
-                                1 if interleaved else 0, float(alpha), _dtype_code(out), _ptr(out), _stream(stream)),
+                                _rope_flags(interleaved, exact), float(alpha), _dtype_code(out), _ptr(out), _stream(stream)),
            "ge_rope_qk_run")
     return out
 
 
-def rope(X, cos, sin, *, pos0=0, interleaved=False, out=None, stream=None):
-    """The rotation alone: rope(X) for X [B, S, D] bf16, row s at position pos0 + s."""
+def rope(X, cos, sin, *, pos0=0, interleaved=False, exact=False, out=None, stream=None):
+    """The rotation alone: rope(X) for X [B, S, D] bf16, row s at position pos0 + s (``exact`` as in
+    ``rope_qk``)."""
     torch = _torch()
     B, S, D = X.shape
     out = out if out is not None else torch.empty_like(X)
-    _check(lib().ge_rope_run(B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, 1 if interleaved else 0,
+    _check(lib().ge_rope_run(B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, _rope_flags(interleaved, exact),
                              _ptr(out), _stream(stream)), "ge_rope_run")
     return out
 
 
-def prepare_rope_qk(Q, K, cos=None, sin=None, *, out, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False,
+def prepare_rope_qk(Q, K, cos=None, sin=None, *, out, q_pos0=0, k_pos0=0, alpha=1.0, interleaved=False, exact=False,
                     stream=None) -> Prepared:
     """``rope_qk`` bound to fixed tensors and stream (for timing loops and graph capture)."""
     B, Sq, D = Q.shape
     args = (B, Sq, K.shape[1], D, _ptr(Q), _ptr(K), _ptr(cos), _ptr(sin), cos.shape[0] if cos is not None else 0,
-            q_pos0, k_pos0, 1 if interleaved else 0, float(alpha), _dtype_code(out), _ptr(out), _stream(stream))
+            q_pos0, k_pos0, _rope_flags(interleaved, exact), float(alpha), _dtype_code(out), _ptr(out), _stream(stream))
     return Prepared(lib().ge_rope_qk_run, "ge_rope_qk_run", None, [Q, K, cos, sin, out], args)
 
 
-def prepare_rope(X, cos, sin, *, out, pos0=0, interleaved=False, stream=None) -> Prepared:
+def prepare_rope(X, cos, sin, *, out, pos0=0, interleaved=False, exact=False, stream=None) -> Prepared:
     """``rope`` bound to fixed tensors and stream."""
     B, S, D = X.shape
-    args = (B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, 1 if interleaved else 0, _ptr(out),
+    args = (B, S, D, _ptr(X), _ptr(cos), _ptr(sin), cos.shape[0], pos0, _rope_flags(interleaved, exact), _ptr(out),
             _stream(stream))
     return Prepared(lib().ge_rope_run, "ge_rope_run", None, [X, cos, sin, out], args)

@@ -842,8 +842,9 @@ ge_status rope_common(int32_t batch, int32_t D, const float *cosT, const float *
 
 ge_status ge_rope_qk_run(int32_t batch, int32_t Sq, int32_t Sk, int32_t D, const void *Q, const void *K,
                          const float *cos_t, const float *sin_t, int32_t n_pos, int32_t q_pos0, int32_t k_pos0,
-                         int32_t interleaved, float alpha, int32_t s_type, void *S, void *stream) {
+                         int32_t flags, float alpha, int32_t s_type, void *S, void *stream) {
     if (Sq <= 0 || Sk <= 0) return fail(GE_ERR_INVALID_ARG, "Sq and Sk must be positive");
+    if (flags & ~(GE_ROPE_INTERLEAVED | GE_ROPE_EXACT)) return fail(GE_ERR_INVALID_ARG, "unknown rope flag bits");
     if (!Q || !K || !S) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     if (s_type != GE_F32 && s_type != GE_BF16) return fail(GE_ERR_INVALID_ARG, "s_type must be F32 or BF16");
     if (((uintptr_t)Q & 15) || ((uintptr_t)K & 15)) return fail(GE_ERR_ALIGN, "Q and K must be 16-byte aligned");
@@ -873,12 +874,15 @@ ge_status ge_rope_qk_run(int32_t batch, int32_t Sq, int32_t Sk, int32_t D, const
     a.sin = rot ? sin_t : nullptr;
     a.alpha = alpha;
     a.S = S;
-    return hip_status(launch_rope_qk(a, interleaved != 0, s_type == GE_F32, (hipStream_t)stream), "ge_rope_qk_run");
+    return hip_status(launch_rope_qk(a, (flags & GE_ROPE_INTERLEAVED) != 0, s_type == GE_F32, (flags & GE_ROPE_EXACT) != 0,
+                                     (hipStream_t)stream),
+                      "ge_rope_qk_run");
 }
 
 ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const float *cos_t, const float *sin_t,
-                      int32_t n_pos, int32_t pos0, int32_t interleaved, void *Y, void *stream) {
+                      int32_t n_pos, int32_t pos0, int32_t flags, void *Y, void *stream) {
     if (S <= 0) return fail(GE_ERR_INVALID_ARG, "S must be positive");
+    if (flags & ~(GE_ROPE_INTERLEAVED | GE_ROPE_EXACT)) return fail(GE_ERR_INVALID_ARG, "unknown rope flag bits");
     if (!X || !Y) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     if (((uintptr_t)X & 15) || ((uintptr_t)Y & 15)) return fail(GE_ERR_ALIGN, "X and Y must be 16-byte aligned");
     ge_status st;
@@ -886,8 +890,8 @@ ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const 
     if (pos0 < 0 || (int64_t)pos0 + S > n_pos) return fail(GE_ERR_INVALID_ARG, "positions outside the cos / sin tables");
     const size_t nb = (size_t)batch * S * D * 2;
     if (overlaps(X, nb, Y, nb)) return fail(GE_ERR_INVALID_ARG, "Y overlaps X");
-    return hip_status(launch_rope(batch, S, D, (const uint16_t *)X, cos_t, sin_t, pos0, interleaved != 0,
-                                  (uint16_t *)Y, (hipStream_t)stream),
+    return hip_status(launch_rope(batch, S, D, (const uint16_t *)X, cos_t, sin_t, pos0, (flags & GE_ROPE_INTERLEAVED) != 0,
+                                  (flags & GE_ROPE_EXACT) != 0, (uint16_t *)Y, (hipStream_t)stream),
                       "ge_rope_run");
 }
 

@@ -85,10 +85,12 @@ struct RopeArgs {
     float alpha;
     void *S;                    // [batch][Sq][Sk], fp32 or bf16
 };
-hipError_t launch_rope_qk(const RopeArgs &a, bool interleaved, bool f32out, hipStream_t s);
+// exact: each rotated coordinate is the exact rotation rounded once (else fp32 with one fused
+// multiply-add, within one bf16 unit of it)
+hipError_t launch_rope_qk(const RopeArgs &a, bool interleaved, bool f32out, bool exact, hipStream_t s);
 // The rotation alone (the unfused chain's first step): X [batch * S][D] -> Y.
 hipError_t launch_rope(int32_t batch, int32_t S, int32_t D, const uint16_t *X, const float *cosT, const float *sinT,
-                       int32_t pos0, bool interleaved, uint16_t *Y, hipStream_t s);
+                       int32_t pos0, bool interleaved, bool exact, uint16_t *Y, hipStream_t s);
 
 // Small-M weight-streaming kernel (decode shapes).
 bool skinny_supported(const Problem &p);

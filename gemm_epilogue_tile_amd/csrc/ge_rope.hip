@@ -5,9 +5,10 @@
 // back to memory just before the product reads them).
 //
 // One 256-thread workgroup per (head, 128-query tile), walking the key tiles:
-//   1. the tiles are read from memory in 16-byte chunks and rotated, each
-//      coordinate being the exact rotation rounded once to bf16 (RNE) -- the
-//      values the unfused chain would have stored -- and written to LDS rows
+//   1. the tiles are read from memory in 16-byte chunks and rotated -- the
+//      values the unfused chain would have stored, each coordinate in fp32
+//      (one product and one fused multiply-add) rounded to bf16 (RNE), or
+//      (EX) the exact rotation rounded once -- and written to LDS rows
 //      padded by 16 bytes, so that the MFMA fragment reads
 //      of 16 rows hit 16 distinct bank groups;
 //   2. four waves (2 x 2, 64 x 64 each) run v_mfma_f32_16x16x32_bf16 over
@@ -41,12 +42,23 @@ __device__ __forceinline__ bool rot_unsure(float r) {
     return (uint16_t)(lo - (uint16_t)0x7ffd) <= (uint16_t)6 || !(m >= 0x1p-100f && m <= 0x1.fffffep127f);
 }
 
+// EX: the fast path of the exact rounding above.  Otherwise one rounded product and one fused
+// multiply-add, r = fma(a, c, -+ rn(b t)): |r - (a c -+ b t)| <= 2^-24 (|b t| + |r|), so after the
+// rounding to bf16 the value is within one bf16 unit of the exactly rounded one, or, where the two
+// products cancel, within 2^-23 (|a c| + |b t|) of the exact rotation (a quarter of the exact
+// rounding's cost: the rotation of every key tile for every query tile is the fused kernel's main
+// vector work).
+template <bool EX>
 __device__ __forceinline__ float rot_fast(float a, float c, float b, float t, bool neg, bool &slow) {
-    const float w = b * t;
-    const float e = __builtin_fmaf(b, t, -w);
-    const float r = neg ? __builtin_fmaf(a, c, -w) - e : __builtin_fmaf(a, c, w) + e;
-    slow |= rot_unsure(r);
-    return r;
+    if constexpr (EX) {
+        const float w = b * t;
+        const float e = __builtin_fmaf(b, t, -w);
+        const float r = neg ? __builtin_fmaf(a, c, -w) - e : __builtin_fmaf(a, c, w) + e;
+        slow |= rot_unsure(r);
+        return r;
+    } else {
+        return neg ? __builtin_fmaf(a, c, -(b * t)) : __builtin_fmaf(a, c, b * t);
+    }
 }
 
 // bf16 bits of a c -+ b t computed exactly: both products are exact in fp64 (8 and 24 significant
@@ -86,7 +98,7 @@ __device__ __noinline__ uint32_t rot_exact(float a, float c, float b, float t, b
 // o0, o1 the rotated chunks.  Interleaved: x[0] = elements 8c .. 8c+7, i.e. the pairs 4c .. 4c+3
 // with the 4 angles in c4[0] / s4[0]; o0 the rotated chunk.  Every coordinate is the exact rotation
 // rounded once to bf16 (fast path above, flagged elements redone exactly).
-template <int D, bool INTER>
+template <int D, bool INTER, bool EX>
 __device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const f32x4 *s4, u32x4 &o0, u32x4 &o1) {
     // elements whose fast result is not certain (rare) are redone one by one, only in the lanes
     // that hold them
@@ -103,8 +115,8 @@ __device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float a = bf16lo(x[0][j]), b = bf16hi(x[0][j]);
-            ya[j] = rot_fast(a, c4[0][j], b, s4[0][j], true, slow);
-            yb[j] = rot_fast(a, s4[0][j], b, c4[0][j], false, slow);
+            ya[j] = rot_fast<EX>(a, c4[0][j], b, s4[0][j], true, slow);
+            yb[j] = rot_fast<EX>(a, s4[0][j], b, c4[0][j], false, slow);
             o0[j] = pack_bf16x2(ya[j], yb[j]);
         }
         if (__builtin_expect(slow, 0)) {
@@ -124,10 +136,10 @@ __device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const
             const float s0 = s4[j >> 1][(2 * j) & 3], s1 = s4[j >> 1][(2 * j + 1) & 3];
             const float a0 = bf16lo(x[0][j]), a1 = bf16hi(x[0][j]);  // first-half elements 8c + 2j, + 1
             const float b0 = bf16lo(x[1][j]), b1 = bf16hi(x[1][j]);  // their partners in the second half
-            ya[2 * j] = rot_fast(a0, c0, b0, s0, true, slow);
-            yb[2 * j] = rot_fast(a0, s0, b0, c0, false, slow);
-            ya[2 * j + 1] = rot_fast(a1, c1, b1, s1, true, slow);
-            yb[2 * j + 1] = rot_fast(a1, s1, b1, c1, false, slow);
+            ya[2 * j] = rot_fast<EX>(a0, c0, b0, s0, true, slow);
+            yb[2 * j] = rot_fast<EX>(a0, s0, b0, c0, false, slow);
+            ya[2 * j + 1] = rot_fast<EX>(a1, c1, b1, s1, true, slow);
+            yb[2 * j + 1] = rot_fast<EX>(a1, s1, b1, c1, false, slow);
             o0[j] = pack_bf16x2(ya[2 * j], ya[2 * j + 1]);
             o1[j] = pack_bf16x2(yb[2 * j], yb[2 * j + 1]);
         }
@@ -148,7 +160,7 @@ __device__ __forceinline__ void rope_regs(const u32x4 *x, const f32x4 *c4, const
 }
 
 // The same from memory: chunk c of the row at xrow with its position's table rows.
-template <int D, bool INTER>
+template <int D, bool INTER, bool EX>
 __device__ __forceinline__ void rope_chunk(const uint16_t *xrow, const float *crow, const float *srow, int c,
                                            u32x4 &o0, u32x4 &o1) {
     constexpr int NV = INTER ? 1 : 2, NT = INTER ? 1 : 2;
@@ -161,7 +173,7 @@ __device__ __forceinline__ void rope_chunk(const uint16_t *xrow, const float *cr
         c4[q] = *(const f32x4 *)(crow + NT * 4 * c + 4 * q);
         s4[q] = *(const f32x4 *)(srow + NT * 4 * c + 4 * q);
     }
-    rope_regs<D, INTER>(x, c4, s4, o0, o1);
+    rope_regs<D, INTER, EX>(x, c4, s4, o0, o1);
 }
 
 // chunks per row handled by one work item
@@ -171,7 +183,7 @@ constexpr int chunks_per_row() { return INTER ? D / 8 : D / 16; }
 // One 128-row tile of X (rows r0 .. r0 + 127 of a [rows][D] head, row r at position pos0 + r): each
 // thread's chunks and their cos / sin requested into registers (rows past the end read nothing and
 // stage zeros), then rotated when ROT and written to LDS rows of D + 8 elements.
-template <int D, bool INTER, bool ROT>
+template <int D, bool INTER, bool ROT, bool EX>
 struct TileRegs {
     static constexpr int CPR = ROT ? chunks_per_row<D, INTER>() : D / 8;
     static constexpr int ITEMS = RT * CPR / 256;               // per thread
@@ -211,7 +223,7 @@ struct TileRegs {
                 *(u32x4 *)(dst + r * LD + 8 * ch) = x[u][0];
             } else {
                 u32x4 o0, o1;
-                rope_regs<D, INTER>(x[u], c[u], s[u], o0, o1);
+                rope_regs<D, INTER, EX>(x[u], c[u], s[u], o0, o1);
                 *(u32x4 *)(dst + r * LD + 8 * ch) = o0;
                 if constexpr (!INTER) *(u32x4 *)(dst + r * LD + D / 2 + 8 * ch) = o1;
             }
@@ -222,7 +234,7 @@ struct TileRegs {
 // One workgroup per (head, 128-query tile), XCD-aware: the query tile is rotated once into LDS; the key tiles
 // follow one another through two LDS buffers, the next one's chunks and tables requested into
 // registers before the current one is multiplied and its scores stored.
-template <int D, bool INTER, bool ROT, bool F32OUT>
+template <int D, bool INTER, bool ROT, bool F32OUT, bool EX>
 __global__ __launch_bounds__(256) void rope_qk_kernel(RopeArgs a) {
     constexpr int LD = D + 8;
     extern __shared__ __attribute__((aligned(16))) uint16_t rsm[];
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(RopeArgs a) {
     const uint16_t *Kb = a.K + (int64_t)b * a.Sk * D;
     const int ntiles = (a.Sk + RT - 1) / RT;
 
-    TileRegs<D, INTER, ROT> t;
+    TileRegs<D, INTER, ROT, EX> t;
     t.load(a.Q + (int64_t)b * a.Sq * D, a.Sq, m0, a.q_pos0, a.cos, a.sin);
     t.store(qs);
     t.load(Kb, a.Sk, 0, a.k_pos0, a.cos, a.sin);
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(256) void rope_qk_kernel(RopeArgs a) {
 }
 
 // the rotation alone: X [batch * S][D] -> Y, row r at position pos0 + r % S
-template <int D, bool INTER>
+template <int D, bool INTER, bool EX>
 __global__ __launch_bounds__(256) void rope_kernel(int64_t rows, int32_t S, const uint16_t *X, const float *cosT,
                                                    const float *sinT, int32_t pos0, uint16_t *Y) {
     constexpr int CPR = chunks_per_row<D, INTER>();
@@ -314,15 +326,15 @@ __global__ __launch_bounds__(256) void rope_kernel(int64_t rows, int32_t S, cons
         const int c = (int)(it % CPR);
         const int64_t p = pos0 + r % S;
         u32x4 o0, o1;
-        rope_chunk<D, INTER>(X + r * D, cosT + p * (D / 2), sinT + p * (D / 2), c, o0, o1);
+        rope_chunk<D, INTER, EX>(X + r * D, cosT + p * (D / 2), sinT + p * (D / 2), c, o0, o1);
         *(u32x4 *)(Y + r * D + 8 * c) = o0;
         if constexpr (!INTER) *(u32x4 *)(Y + r * D + D / 2 + 8 * c) = o1;
     }
 }
 
-template <int D, bool INTER, bool ROT, bool F32OUT>
+template <int D, bool INTER, bool ROT, bool F32OUT, bool EX>
 hipError_t go_qk(const RopeArgs &a, hipStream_t s) {
-    auto k = rope_qk_kernel<D, INTER, ROT, F32OUT>;
+    auto k = rope_qk_kernel<D, INTER, ROT, F32OUT, EX>;
     constexpr int lds = 3 * RT * (D + 8) * 2;  // the query tile and two key tiles
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
@@ -335,24 +347,24 @@ hipError_t go_qk(const RopeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool EX>
 hipError_t qk_for_d(const RopeArgs &a, bool inter, bool rot, bool f32out, hipStream_t s) {
-    if (!rot) return f32out ? go_qk<D, false, false, true>(a, s) : go_qk<D, false, false, false>(a, s);
-    if (inter) return f32out ? go_qk<D, true, true, true>(a, s) : go_qk<D, true, true, false>(a, s);
-    return f32out ? go_qk<D, false, true, true>(a, s) : go_qk<D, false, true, false>(a, s);
+    if (!rot) return f32out ? go_qk<D, false, false, true, false>(a, s) : go_qk<D, false, false, false, false>(a, s);
+    if (inter) return f32out ? go_qk<D, true, true, true, EX>(a, s) : go_qk<D, true, true, false, EX>(a, s);
+    return f32out ? go_qk<D, false, true, true, EX>(a, s) : go_qk<D, false, true, false, EX>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_rope_qk(const RopeArgs &a, bool interleaved, bool f32out, hipStream_t s) {
+hipError_t launch_rope_qk(const RopeArgs &a, bool interleaved, bool f32out, bool exact, hipStream_t s) {
     const bool rot = a.cos != nullptr;
-    if (a.D == 64) return qk_for_d<64>(a, interleaved, rot, f32out, s);
-    if (a.D == 128) return qk_for_d<128>(a, interleaved, rot, f32out, s);
+    if (a.D == 64) return exact ? qk_for_d<64, true>(a, interleaved, rot, f32out, s) : qk_for_d<64, false>(a, interleaved, rot, f32out, s);
+    if (a.D == 128) return exact ? qk_for_d<128, true>(a, interleaved, rot, f32out, s) : qk_for_d<128, false>(a, interleaved, rot, f32out, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_rope(int32_t batch, int32_t S, int32_t D, const uint16_t *X, const float *cosT, const float *sinT,
-                       int32_t pos0, bool interleaved, uint16_t *Y, hipStream_t s) {
+                       int32_t pos0, bool interleaved, bool exact, uint16_t *Y, hipStream_t s) {
     const int64_t rows = (int64_t)batch * S;
     const int64_t items = rows * (interleaved ? D / 8 : D / 16);
     const int blocks = (int)((items + 255) / 256 < 8192 ? (items + 255) / 256 : 8192);
@@ -360,8 +372,13 @@ hipError_t launch_rope(int32_t batch, int32_t S, int32_t D, const uint16_t *X, c
         hipLaunchKernelGGL(kern, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s, rows, S, X, cosT, sinT, pos0, Y);
         return hipGetLastError();
     };
-    if (D == 64) return interleaved ? go(rope_kernel<64, true>) : go(rope_kernel<64, false>);
-    if (D == 128) return interleaved ? go(rope_kernel<128, true>) : go(rope_kernel<128, false>);
+    if (exact) {
+        if (D == 64) return interleaved ? go(rope_kernel<64, true, true>) : go(rope_kernel<64, false, true>);
+        if (D == 128) return interleaved ? go(rope_kernel<128, true, true>) : go(rope_kernel<128, false, true>);
+    } else {
+        if (D == 64) return interleaved ? go(rope_kernel<64, true, false>) : go(rope_kernel<64, false, false>);
+        if (D == 128) return interleaved ? go(rope_kernel<128, true, false>) : go(rope_kernel<128, false, false>);
+    }
     return hipErrorInvalidValue;
 }
 

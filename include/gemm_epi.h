@@ -98,6 +98,10 @@ typedef int32_t ge_status;
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
 #define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
 #define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 32: B is in the layout gemm_b_prepack writes */
+
+/* rope flags (ge_rope_qk_run, ge_rope_run) */
+#define GE_ROPE_INTERLEAVED 1 /* pair i is (2i, 2i + 1); else (i, i + D/2), rotate-half */
+#define GE_ROPE_EXACT 2       /* each rotated coordinate is the exact rotation rounded once to bf16 */
 #define GE_FLAG_NO_SCRATCH 64u     /* the plan allocates no device memory (see gemm_epi_run_noalloc) */
 
 /*
@@ -284,28 +288,35 @@ GE_API ge_status gemm_b_prepack(const ge_plan *plan, const void *B, void *Bp, vo
  * sin fp32 [n_pos, D/2] (row p: cos(p theta_i), sin(p theta_i)), 16-byte
  * aligned, covering every position used; S [batch, Sq, Sk] of s_type (GE_F32
  * or GE_BF16), dense, not overlapping Q or K.  Pair i of a row is (i, i + D/2)
- * (rotate-half, the Llama layout), or (2i, 2i + 1) when interleaved != 0:
- * x'_a = x_a cos - x_b sin, x'_b = x_a sin + x_b cos, each x' being the exact
- * rotated value rounded once to bf16 (RNE), the values the unfused chain
- * stores; the product is bf16 x bf16 with fp32 accumulation, alpha applied in
- * fp32, one rounding to s_type.  cos == sin == NULL: no rotation (the plain
- * product, the unfused chain's last step).  D in {64, 128}, batch <= 65535.
- * Errors: INVALID_ARG (sizes, NULLs, positions outside the tables, overlap),
- * UNSUPPORTED (D), ALIGN, NO_DEVICE, HIP.  Asynchronous on the stream.
+ * (rotate-half, the Llama layout), or (2i, 2i + 1) with GE_ROPE_INTERLEAVED in
+ * flags: x'_a = x_a cos - x_b sin, x'_b = x_a sin + x_b cos, the values the
+ * unfused chain stores (bf16, RNE).  With GE_ROPE_EXACT each x' is the exact
+ * rotated value rounded once; without it each is computed in fp32 (one rounded
+ * product, one fused multiply-add) and rounded to bf16: within one bf16 unit of
+ * the exactly rounded value, or within 2^-23 (|x_a cos| + |x_b sin|) of the
+ * exact rotation where the two products cancel (the exact rounding costs about
+ * a third more time here: the key tiles are rotated once per query tile).  The
+ * product is bf16 x bf16 with fp32 accumulation, alpha applied in fp32, one
+ * rounding to s_type.  cos == sin == NULL: no rotation (the plain product, the
+ * unfused chain's last step).  D in {64, 128}, batch <= 65535.
+ * Errors: INVALID_ARG (sizes, NULLs, positions outside the tables, overlap,
+ * unknown flag bits), UNSUPPORTED (D), ALIGN, NO_DEVICE, HIP.  Asynchronous on
+ * the stream.
  */
 GE_API ge_status ge_rope_qk_run(int32_t batch, int32_t Sq, int32_t Sk, int32_t D, const void *Q, const void *K,
                                 const float *cos_t, const float *sin_t, int32_t n_pos, int32_t q_pos0,
-                                int32_t k_pos0, int32_t interleaved, float alpha, int32_t s_type, void *S,
+                                int32_t k_pos0, int32_t flags, float alpha, int32_t s_type, void *S,
                                 void *stream);
 
 /*
  * The rotation alone (the unfused chain's first kernels, rope(q, cos, sin) of
  * the same page): Y = rope(X) for X, Y [batch, S, D] bf16, row s of each batch
- * at position pos0 + s, with the pairing and rounding of ge_rope_qk_run.  X
- * and Y 16-byte aligned, not overlapping; cos, sin as above (required).
+ * at position pos0 + s, with the pairing and rounding of ge_rope_qk_run (the
+ * same flags).  X and Y 16-byte aligned, not overlapping; cos, sin as above
+ * (required).
  */
 GE_API ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const float *cos_t,
-                             const float *sin_t, int32_t n_pos, int32_t pos0, int32_t interleaved, void *Y,
+                             const float *sin_t, int32_t n_pos, int32_t pos0, int32_t flags, void *Y,
                              void *stream);
 
 /*

@@ -1,8 +1,10 @@
 """GPU parity of rotary position embedding at operand load (page "Fusion
-Thinking", Pattern 4): the standalone rotation bit-exact against the oracle,
-the fused scores kernel against the oracle on ragged shapes, both pairings,
-both output types and shifted positions, fused == unfused chain bitwise, and
-the requests the entry points must refuse."""
+Thinking", Pattern 4): the standalone rotation against the oracle -- bit-exact
+with the exact rounding (ties, near ties, cancellation, overflow, subnormals,
+signed zeros), within its stated bound with the default fp32 rounding -- the
+fused scores kernel against the oracle on ragged shapes, both pairings, both
+output types and shifted positions, fused == unfused chain bitwise in both
+roundings, and the requests the entry points must refuse."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +37,72 @@ def test_rotation_alone_is_bit_exact(D, interleaved):
     Q, _, c, s = _dev(inp)
     cos, sin = workloads.rope_tables(200, D, 500000.0)
     got = _bits(ge.rope(Q, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), pos0=41,
-                        interleaved=interleaved))
+                        interleaved=interleaved, exact=True))
     assert np.array_equal(got, oracle.rope(inp["Q"], cos, sin, 41, interleaved))
+
+
+def _fast_bound(X, cos, sin, pos0, interleaved):
+    """Per output element, what the default fp32 rounding may differ by from the exactly rounded
+    value: one bf16 unit of it, or 2^-22 (|a| + |b|) max(|cos|, |sin|) where the two products
+    cancel (a, b: the pair the element belongs to)."""
+    x = workloads.bf16_bits_to_f32(X).astype(np.float64)
+    S, D = x.shape[-2], x.shape[-1]
+    c = cos[pos0:pos0 + S].astype(np.float64)
+    t = sin[pos0:pos0 + S].astype(np.float64)
+    if interleaved:
+        a, b = x[..., 0::2], x[..., 1::2]
+    else:
+        a, b = x[..., :D // 2], x[..., D // 2:]
+    m = (np.abs(a) + np.abs(b)) * np.maximum(np.abs(c), np.abs(t)) * 2.0 ** -22
+    out = np.empty_like(x)
+    if interleaved:
+        out[..., 0::2], out[..., 1::2] = m, m
+    else:
+        out[..., :D // 2], out[..., D // 2:] = m, m
+    return out
+
+
+def _assert_scores_fast(out, inp, q_pos0, k_pos0, interleaved, what):
+    """Scores of the default rounding against the oracle's (exactly rounded operands): each rotated
+    operand element may be off by d = max(one bf16 unit, the cancellation term of _fast_bound), so
+    |S - S_ref| <= alpha (dQ |K'|^T + |Q'| dK^T + dQ dK^T), plus the fp32 product's own tolerance."""
+    alpha = inp["alpha"]
+    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], q_pos0=q_pos0, k_pos0=k_pos0, alpha=alpha,
+                         interleaved=interleaved)
+    g = out.float().cpu().numpy().astype(np.float64) if isinstance(out, torch.Tensor) else out
+    bound = np.zeros_like(ref)
+    for b in range(ref.shape[0]):
+        ops = []
+        for X, p0 in ((inp["Q"][b:b + 1], q_pos0), (inp["K"][b:b + 1], k_pos0)):
+            xr = workloads.bf16_bits_to_f32(oracle.rope(X, inp["cos"], inp["sin"], p0, interleaved))[0].astype(np.float64)
+            d = np.maximum(np.ldexp(1.0, np.frexp(np.abs(xr))[1] - 8),
+                           _fast_bound(X, inp["cos"], inp["sin"], p0, interleaved)[0])
+            ops.append((np.abs(xr), d))
+        (aq, dq), (ak, dk) = ops
+        bound[b] = abs(alpha) * (dq @ ak.T + aq @ dk.T + dq @ dk.T)
+    err = np.abs(g - ref)
+    ok = err <= bound + TOL_F32 * (1 + np.abs(ref))
+    i = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(ok), f"{what}: err {err[i]:.3e} > bound {bound[i]:.3e} at {i}"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rotation_alone_default_rounding_within_bound(D, interleaved):
+    w = RW.with_shape(heads=3, Sq=77, Sk=77, D=D, interleaved=interleaved)
+    inp = workloads.make_rope_inputs(w, seed=D + 1)
+    Q, _, c, s = _dev(inp)
+    cos, sin = workloads.rope_tables(200, D, 500000.0)
+    got = _bits(ge.rope(Q, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), pos0=41,
+                        interleaved=interleaved))
+    want = oracle.rope(inp["Q"], cos, sin, 41, interleaved)
+    g = workloads.bf16_bits_to_f32(got).astype(np.float64)
+    e = workloads.bf16_bits_to_f32(want).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(e))[1] - 8)  # one bf16 unit at the exact value
+    err = np.abs(g - e)
+    assert np.all((err <= ulp) | (err <= _fast_bound(inp["Q"], cos, sin, 41, interleaved))), np.max(err)
+    # and nearly every element is the exactly rounded one
+    assert np.mean(got != want) < 0.01
 
 
 def _tie_cases():
@@ -77,14 +143,15 @@ def test_rotation_of_ties_overflow_subnormals_bit_exact(interleaved):
             cos[r, i], sin[r, i] = (c, s_) if i % 3 else (s_, c)
     X = workloads.f32_to_bf16_bits(x)[None]
     Xd = to_dev(X)
-    got = _bits(ge.rope(Xd, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), interleaved=interleaved))
+    got = _bits(ge.rope(Xd, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), interleaved=interleaved,
+                        exact=True))
     want = oracle.rope(X, cos, sin, 0, interleaved)
     bad = np.nonzero(got != want)
     assert bad[0].size == 0, f"{bad[0].size} mismatches, first at {tuple(b[0] for b in bad)}: gpu {got[bad][0]:#06x} oracle {want[bad][0]:#06x}"
     # the fused scores kernel rotates the same way
     ref_q = torch.from_numpy(want.view(np.int16)).to(DEV).view(torch.bfloat16)
     fused = ge.rope_qk(Xd[:, :, :], Xd, torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV), alpha=1.0,
-                       interleaved=interleaved)
+                       interleaved=interleaved, exact=True)
     plain = ge.rope_qk(ref_q, ref_q, alpha=1.0)
     torch.cuda.synchronize()
     assert torch.equal(torch.nan_to_num(fused, posinf=1, neginf=-1).view(torch.int32),
@@ -99,9 +166,18 @@ def test_fused_scores_match_the_oracle(H, Sq, Sk, D, interleaved):
     inp = workloads.make_rope_inputs(w, seed=H + Sq + Sk)
     Q, K, c, s = _dev(inp)
     out = ge.rope_qk(Q, K, c, s, q_pos0=w.q_pos0, k_pos0=w.k_pos0, alpha=inp["alpha"], interleaved=interleaved)
-    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], q_pos0=w.q_pos0, k_pos0=w.k_pos0,
-                         alpha=inp["alpha"], interleaved=interleaved)
-    assert_close(out, ref, TOL_F32, f"rope_qk {H}x{Sq}x{Sk}x{D} inter={interleaved}")
+    _assert_scores_fast(out, inp, w.q_pos0, w.k_pos0, interleaved, f"rope_qk {H}x{Sq}x{Sk}x{D} inter={interleaved}")
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_fused_scores_exact_rounding_match_the_oracle(interleaved):
+    w = RW.with_shape(heads=3, Sq=77, Sk=200, D=128, interleaved=interleaved, q_pos0=9, k_pos0=5)
+    inp = workloads.make_rope_inputs(w, seed=13)
+    Q, K, c, s = _dev(inp)
+    out = ge.rope_qk(Q, K, c, s, q_pos0=9, k_pos0=5, alpha=inp["alpha"], interleaved=interleaved, exact=True)
+    ref = oracle.rope_qk(inp["Q"], inp["K"], inp["cos"], inp["sin"], q_pos0=9, k_pos0=5, alpha=inp["alpha"],
+                         interleaved=interleaved)
+    assert_close(out, ref, TOL_F32, f"rope_qk exact inter={interleaved}")
 
 
 def test_fused_scores_bf16_output():
@@ -123,15 +199,16 @@ def test_plain_product_without_tables():
 
 
 @pytest.mark.parametrize("interleaved", [False, True])
-def test_fused_equals_the_unfused_chain_bitwise(interleaved):
+@pytest.mark.parametrize("exact", [False, True])
+def test_fused_equals_the_unfused_chain_bitwise(interleaved, exact):
     # rope(Q) and rope(K) written to memory, then the plain product: the same bf16 operands reach
-    # the same product code, so the scores agree bit for bit
+    # the same product code, so the scores agree bit for bit (in either rounding)
     w = RW.with_shape(heads=4, Sq=256, Sk=384, D=128, interleaved=interleaved, q_pos0=128)
     inp = workloads.make_rope_inputs(w, seed=9)
     Q, K, c, s = _dev(inp)
-    fused = ge.rope_qk(Q, K, c, s, q_pos0=128, alpha=inp["alpha"], interleaved=interleaved)
-    q2 = ge.rope(Q, c, s, pos0=128, interleaved=interleaved)
-    k2 = ge.rope(K, c, s, pos0=0, interleaved=interleaved)
+    fused = ge.rope_qk(Q, K, c, s, q_pos0=128, alpha=inp["alpha"], interleaved=interleaved, exact=exact)
+    q2 = ge.rope(Q, c, s, pos0=128, interleaved=interleaved, exact=exact)
+    k2 = ge.rope(K, c, s, pos0=0, interleaved=interleaved, exact=exact)
     unfused = ge.rope_qk(q2, k2, alpha=inp["alpha"])
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int32), unfused.view(torch.int32))
@@ -143,8 +220,8 @@ def test_full_size_prefill_sampled_heads():
     Q, K, c, s = _dev(inp)
     out = ge.rope_qk(Q, K, c, s, alpha=inp["alpha"]).cpu().numpy().astype(np.float64)
     heads = [0, 17, w.heads - 1]
-    ref = oracle.rope_qk(inp["Q"][heads], inp["K"][heads], inp["cos"], inp["sin"], alpha=inp["alpha"])
-    assert_close(out[heads], ref, TOL_F32, "rope_qk full size")
+    sub = dict(inp, Q=inp["Q"][heads], K=inp["K"][heads])
+    _assert_scores_fast(out[heads], sub, w.q_pos0, w.k_pos0, w.interleaved, "rope_qk full size")
     assert np.all(np.isfinite(out))
 
 
@@ -160,3 +237,7 @@ def test_refusals():
     assert e.value.status == ge.ERR_UNSUPPORTED
     with pytest.raises(ge.GemmEpiError):
         ge.rope(Q, cos, cos, out=Q)  # Y overlaps X
+    out = torch.empty((1, 8, 8), dtype=torch.float32, device=DEV)
+    st = ge.lib().ge_rope_qk_run(1, 8, 8, 128, ge._ptr(Q), ge._ptr(Q), ge._ptr(cos), ge._ptr(cos), 8, 0, 0, 4, 1.0,
+                                 ge.F32, ge._ptr(out), None)
+    assert st == ge.ERR_INVALID_ARG  # unknown flag bit
