@@ -60,8 +60,8 @@ const char *tile_kernel_name(const Problem &p, int cu_count);
 // Quantised-weight tile kernel (prepacked int4 with M > 32, or raw 8-bit codes with M > 16),
 // dispatched through launch_tile.
 bool tile_w4_supported(const Problem &p);
-hipError_t launch_tile_w4(const Problem &p, hipStream_t s);
-const char *tile_w4_kernel_name(const Problem &p);
+hipError_t launch_tile_w4(const Problem &p, int cu_count, hipStream_t s);
+const char *tile_w4_kernel_name(const Problem &p, int cu_count);
 
 // One-time conversion of raw [K, N/2] int4 weights to the prepacked layout.
 hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,

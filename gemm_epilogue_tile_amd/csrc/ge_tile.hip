@@ -515,7 +515,7 @@ static bool small_tiles(const Problem &p, int cu_count) {
 }
 
 const char *tile_kernel_name(const Problem &p, int cu_count) {
-    if (p.mode == MODE_W4) return tile_w4_kernel_name(p);
+    if (p.mode == MODE_W4) return tile_w4_kernel_name(p, cu_count);
     if (p.mode == MODE_SWIGLU)
         return swiglu_big_blocks(p, cu_count) * 128 < p.N ? "tile_swiglu_256x128x32+128x128x32"
                                                            : "tile_swiglu_256x128x32";
@@ -525,7 +525,7 @@ const char *tile_kernel_name(const Problem &p, int cu_count) {
 
 hipError_t launch_tile(const Problem &p, int cu_count, hipStream_t s) {
     if (!tile_supported(p)) return hipErrorInvalidValue;
-    if (p.mode == MODE_W4) return launch_tile_w4(p, s);
+    if (p.mode == MODE_W4) return launch_tile_w4(p, cu_count, s);
     if (p.mode == MODE_SWIGLU) {
         const int nb = swiglu_big_blocks(p, cu_count);
         if (nb * 128 >= p.N) return launch_cfg<256, 128, 2, 2, true, false>(p, s);

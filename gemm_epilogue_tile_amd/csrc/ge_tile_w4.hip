@@ -557,8 +557,14 @@ void tile_w4_kernel(Problem p) {
 
 }  // namespace
 
-// 8 waves (64 x 256 tiles) where N allows, else 4 (64 x 128)
-static int w4_waves(const Problem &p) { return p.N % W4L<8>::BN == 0 ? 8 : 4; }
+// 8 waves (64 x 256 tiles) where N allows and the tiles still fill the CUs, else 4 (64 x 128).  A
+// workgroup's time is set by its own K loop (the loop is latency-bound), not by how many run: at
+// 8192 x 8192, 33-256 rows take 79-80 us in 64 x 256 tiles (32-128 workgroups) against 61-62 us
+// in 64 x 128 tiles; 512 rows 81 us against 85 us.
+static int w4_waves(const Problem &p, int cu_count) {
+    const int64_t tiles = (int64_t)((p.M + W4_BM - 1) / W4_BM) * (p.N / W4L<8>::BN);
+    return p.N % W4L<8>::BN == 0 && tiles >= cu_count ? 8 : 4;
+}
 
 bool tile_w4_supported(const Problem &p) {
     if (p.mode != MODE_W4 || p.group != 128 || !al16(p.scales) || (p.ld_s & 7)) return false;
@@ -575,8 +581,8 @@ bool tile_w4_supported(const Problem &p) {
     return epi_ok(p);
 }
 
-const char *tile_w4_kernel_name(const Problem &p) {
-    const bool w8 = w4_waves(p) == 8;
+const char *tile_w4_kernel_name(const Problem &p, int cu_count) {
+    const bool w8 = w4_waves(p, cu_count) == 8;
     switch (p.wfmt) {
     case WFMT_U8: return w8 ? "tile_w8_u8_64x256x32" : "tile_w8_u8_64x128x32";
     case WFMT_FP8: return w8 ? "tile_w8_fp8_64x256x32" : "tile_w8_fp8_64x128x32";
@@ -599,15 +605,15 @@ static hipError_t launch_wf(const Problem &p, hipStream_t s) {
 }
 
 template <int WF>
-static hipError_t launch_w(const Problem &p, hipStream_t s) {
-    return w4_waves(p) == 8 ? launch_wf<WF, 8>(p, s) : launch_wf<WF, 4>(p, s);
+static hipError_t launch_w(const Problem &p, int cu_count, hipStream_t s) {
+    return w4_waves(p, cu_count) == 8 ? launch_wf<WF, 8>(p, s) : launch_wf<WF, 4>(p, s);
 }
 
-hipError_t launch_tile_w4(const Problem &p, hipStream_t s) {
+hipError_t launch_tile_w4(const Problem &p, int cu_count, hipStream_t s) {
     if (!tile_w4_supported(p)) return hipErrorInvalidValue;
-    if (p.wfmt == WFMT_U8) return launch_w<WFMT_U8>(p, s);
-    if (p.wfmt == WFMT_FP8) return launch_w<WFMT_FP8>(p, s);
-    return launch_w<WFMT_U4>(p, s);
+    if (p.wfmt == WFMT_U8) return launch_w<WFMT_U8>(p, cu_count, s);
+    if (p.wfmt == WFMT_FP8) return launch_w<WFMT_FP8>(p, cu_count, s);
+    return launch_w<WFMT_U4>(p, cu_count, s);
 }
 
 }  // namespace ge

@@ -49,3 +49,10 @@ def dev_inputs(inp: dict) -> dict:
         if isinstance(v, np.ndarray):
             out[k] = to_dev(v)
     return out
+
+
+def w4_tile_cols(M, N):
+    """Columns per workgroup of the quantised tile kernel: 256 (8 waves) where N % 256 == 0 and its
+    64 x 256 tiles still give every CU one, else 128 (4 waves)."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return 256 if N % 256 == 0 and (M + 63) // 64 * (N // 256) >= cu else 128

@@ -181,7 +181,7 @@ def test_prepacked_decode_and_rope_calls_replay_in_a_graph():
         return [ge.prepare_gemm_epilogue(xs, Ws, out=o[0], prepacked=True),
                 ge.prepare_gemm_epilogue(xp, Wp, out=o[1], prepacked=True),
                 ge.prepare_w4_gemm(x8, Wq8, s8, out=o[2], zero_point=128, fmt="u8", prepacked=True),
-                ge.prepare_rope_qk(Q, K, cos, sin, out=o[3], q_pos0=128, alpha=0.125)]
+                ge.prepare_rope_qk(Q, K, cos, sin, out=o[3], q_pos0=128, alpha=0.125, exact=True)]
 
     oe, og = outs(), outs()
     eager, graph_calls = prepare(oe), prepare(og)

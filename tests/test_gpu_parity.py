@@ -8,7 +8,7 @@ import torch
 import gemm_epilogue_tile_amd as ge
 import oracle
 import workloads
-from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, dev_inputs, to_dev, to_host
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols
 
 pytestmark = pytest.mark.gpu
 
@@ -563,13 +563,14 @@ def test_w4_prepacked_rejected_by_unfused_chain():
                            torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV), prepacked=True)
 
 
-@pytest.mark.parametrize("M,N,K", [(33, 128, 128), (128, 256, 512), (200, 384, 1024), (512, 512, 2048)])
+@pytest.mark.parametrize("M,N,K", [(33, 128, 128), (128, 256, 512), (200, 384, 1024), (512, 512, 2048),
+                                   (100, 32768, 256), (130, 22016, 384)])
 def test_w4_prepacked_tile_path(M, N, K):
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
     p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
-    # 8 waves and 256 columns per workgroup where N % 256 == 0, else 4 waves and 128 columns
-    assert p.kernel == f"tile_w4_bf16_64x{256 if N % 256 == 0 else 128}x32"
+    # 8 waves and 256 columns per workgroup where those tiles fill the CUs, else 4 waves and 128
+    assert p.kernel == f"tile_w4_bf16_64x{w4_tile_cols(M, N)}x32"
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 

@@ -12,7 +12,7 @@ import torch
 import gemm_epilogue_tile_amd as ge
 import oracle
 import workloads
-from gpu_helpers import DEV, TOL_BF16, assert_close, dev_inputs, to_dev, to_host
+from gpu_helpers import DEV, TOL_BF16, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols
 
 pytestmark = pytest.mark.gpu
 
@@ -52,13 +52,23 @@ def test_w8_plans_pick_the_streaming_kernel_for_small_M():
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(17, 128, 128), (64, 256, 1024), (100, 384, 4224), (512, 1024, 2048)])
 def test_w8_tile_kernel(fmt, M, N, K):
-    # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes (8 waves,
-    # 256 columns per workgroup, where N % 256 == 0; else 4 waves, 128 columns); K = 4224 is 33
-    # groups, not a whole number of the kernel's two-group loop trips
+    # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes (4 waves,
+    # 128 columns per workgroup at these sizes); K = 4224 is 33 groups, not a whole number of the
+    # kernel's two-group loop trips
     w = BASE[fmt].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=3 * M + K)
-    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{256 if N % 256 == 0 else 128}x32"
+    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
     assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} tile {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(100, 32768, 256), (130, 22016, 384)])
+def test_w8_tile_kernel_eight_waves(fmt, M, N, K):
+    # enough 64 x 256 tiles for every CU: the 8-wave workgroups, ragged M (two and three row tiles)
+    w = BASE[fmt].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + K)
+    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
+    assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} 8-wave tile {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("zp", [0, 77, 255])
@@ -81,7 +91,7 @@ def test_w8_tile_strided_operands(fmt):
     Wf[:, :N] = torch.from_numpy(inp["Wq"]).to(DEV)
     out = ge.w4_gemm(Xf[:, :K], Wf[:, :N], d["scales"], bias=d.get("bias"), group=inp["group"],
                      zero_point=inp["zero_point"], fmt=fmt)
-    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x256x32"
+    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
     assert_close(out, oracle.reference(inp), TOL_BF16, f"{fmt} tile strided")
 
 
