@@ -60,7 +60,7 @@ struct ge_plan {
     int32_t group;
     const char *kernel;  // fused kernel chosen for aligned inputs
     int32_t split;       // K splits of the 8-bit streaming kernel (1: none)
-    int32_t scratch_use; // what scratch holds: SCRATCH_NONE / SCRATCH_SPLIT / SCRATCH_SK
+    int32_t scratch_use; // what scratch holds: SCRATCH_NONE / SCRATCH_SPLIT / SCRATCH_SK / SCRATCH_TILE_SPLIT
     void *scratch;       // device scratch owned by the plan, or NULL
     size_t scratch_bytes;
 };
@@ -78,7 +78,7 @@ bool log_enabled() {
 
 // plan scratch: the 8-bit kernel's split tiles and counters, or the stream-K decode kernel's tiles
 // and counters
-enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_SK = 3 };
+enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_SK = 3, SCRATCH_TILE_SPLIT = 4 };
 
 int32_t wfmt_of(const ge_desc &d) {
     return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
@@ -128,11 +128,14 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     // with another kind)
     p.split = 1;
     const bool split_use = pl->scratch_use == SCRATCH_SPLIT && p.mode == MODE_W4;
+    const bool tsplit_use = pl->scratch_use == SCRATCH_TILE_SPLIT && p.mode == MODE_W4;
     const bool sk_use = pl->scratch_use == SCRATCH_SK && p.mode == MODE_GENERIC;
-    if (pl->scratch && (split_use || sk_use)) {
+    if (pl->scratch && (split_use || tsplit_use || sk_use)) {
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
-        const size_t counters = split_use ? (size_t)split_counters(p) : (size_t)((d.N + 127) / 128);
+        const size_t counters = split_use    ? (size_t)split_counters(p)
+                                : tsplit_use ? (size_t)tile_w4_split_counters(p)
+                                             : (size_t)((d.N + 127) / 128);
         p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - counters * 4);
     }
     if (pl->kind != GE_KIND_SWIGLU) {
@@ -426,6 +429,13 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             use = SCRATCH_SPLIT;
             pl.split = split;
         }
+    } else if (kind == GE_KIND_W4 && tile_supported(p)) {
+        const int split = tile_w4_split(p, pl.cu_count);
+        if (split > 1) {
+            bytes = tile_w4_split_scratch_bytes(p, split);
+            use = SCRATCH_TILE_SPLIT;
+            pl.split = split;
+        }
     } else if (kind == GE_KIND_GENERIC && skinny_supported(p)) {
         const int slots = bf16_sk_slots(p, pl.cu_count);
         if (slots > 0) {
@@ -461,6 +471,11 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         }
         pl.scratch_use = use;
         pl.scratch_bytes = (size_t)bytes;
+        if (use == SCRATCH_TILE_SPLIT) {  // the split kernel's name
+            Problem q = p;
+            q.split = pl.split;
+            pl.kernel = fused_name(q, pl.cu_count);
+        }
     } else {
         pl.split = 1;
     }

@@ -63,6 +63,14 @@ bool tile_w4_supported(const Problem &p);
 hipError_t launch_tile_w4(const Problem &p, int cu_count, hipStream_t s);
 const char *tile_w4_kernel_name(const Problem &p, int cu_count);
 
+// K split of the quantised tile kernel when its tiles do not fill the CUs (1: none), the scratch
+// bytes it needs (partial tiles, then one counter per tile that must start at zero; the kernel
+// re-arms them) and the number of those counters.  The kernel runs split when p.split > 1 with
+// p.split_ws / p.split_cnt set.
+int tile_w4_split(const Problem &p, int cu_count);
+int64_t tile_w4_split_scratch_bytes(const Problem &p, int split);
+int tile_w4_split_counters(const Problem &p);
+
 // One-time conversion of raw [K, N/2] int4 weights to the prepacked layout.
 hipError_t launch_w4_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ldq, int32_t lo_first, uint8_t *Wp,
                              hipStream_t s);

@@ -137,7 +137,10 @@ static_assert(w8_inflight(4, 0) == 2 && w8_inflight(4, 3) == 3 && w8_inflight(8,
                   w8_inflight(8, 3) == 3,
               "scale loads at stages = 2 mod 4");
 
-template <int WF, int NW>
+// SPLIT: the grid is tiles x p.split K slices (p.split divides K / 128); each workgroup writes its
+// fp32 partial tile to p.split_ws and counts itself in on the tile's counter in p.split_cnt; the last
+// to arrive sums the slices in slice order (deterministic), runs the epilogue and re-arms the counter.
+template <int WF, int NW, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void tile_w4_kernel(Problem p) {
     using L = W4L<NW>;
@@ -152,23 +155,30 @@ void tile_w4_kernel(Problem p) {
     const int half = NW == 8 ? wave >> 2 : 0;  // 8 waves: which stage of a pair this wave loads
     const int tiles_m = (p.M + W4_BM - 1) / W4_BM, tiles_n = p.N / L::BN;
     const int total = tiles_m * tiles_n;
+    const int nsplit = SPLIT ? p.split : 1, grid = total * nsplit;
     int t = blockIdx.x;
-    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+    if ((grid & 7) == 0) t = (t & 7) * (grid >> 3) + (t >> 3);
+    const int ks = t / total;  // K slice
+    t %= total;
     const int per_group = GROUP_M * tiles_n;
     const int first_m = (t / per_group) * GROUP_M;
     const int gsize = min(tiles_m - first_m, GROUP_M);
     const int tm = first_m + (t % per_group) % gsize;
     const int tn = (t % per_group) / gsize;
     const int m0 = tm * W4_BM, n0 = tn * L::BN;
-    const int ngroups = p.K / 128, nst = p.K / T_BK;
+    // K slice ks: groups g0 .. g0 + ngroups - 1 of the ngt groups of K (the whole K without a split)
+    const int ngt = p.K / 128;
+    const int ngroups = ngt / nsplit, nst = 4 * ngroups;
+    const int g0 = ks * ngroups;
+    const int64_t k0 = (int64_t)g0 * 128;
 
     // Direct loads.  The lane offsets are fixed; the stage's (or group's) position goes into the
     // buffer resource (scalar arithmetic), whose range is empty past the end of K, so the loop
     // spends no vector instructions on addresses.
     // activations: wave w (mod 4) loads rows 16 w .. 16 w + 15 of a stage, lane l row l / 4 of 16,
     // LDS slot l % 4 of the row holding logical chunk (l % 4) ^ ((row >> 1) & 3)
-    const char *a_base = (const char *)p.A + (int64_t)m0 * p.lda * 2;
-    const int64_t a_bytes = ((int64_t)(p.M - m0 - 1) * p.lda + p.K) * 2;
+    const char *a_base = (const char *)p.A + ((int64_t)m0 * p.lda + k0) * 2;
+    const int64_t a_bytes = ((int64_t)(p.M - m0 - 1) * p.lda + p.K - k0) * 2;
     const int arow_l = lane >> 2;
     const uint32_t a_src = (uint32_t)((int64_t)((wave & 3) * 16 + arow_l) * p.lda * 2 +
                                       (((lane & 3) ^ ((arow_l >> 1) & 3)) * 16));
@@ -179,14 +189,14 @@ void tile_w4_kernel(Problem p) {
     // int4: codes of the wave's tiles 2 w, 2 w + 1 and their 32 scales (lanes 0..3) into the wave's
     // slot, once per group; 8-bit: the scales once per group, the codes once per stage
     const int64_t b_bytes = U4 ? (int64_t)p.K * p.N / 2 : (int64_t)(p.K - 1) * p.ldb + p.N;
-    const int64_t s_bytes = ((int64_t)(ngroups - 1) * p.ld_s + p.N) * 2;
+    const int64_t s_bytes = ((int64_t)(ngt - 1) * p.ld_s + p.N) * 2;
     uint32_t b_src[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         // tile tt of the prepacked layout (N is a multiple of 128, so every 128-column block is
         // whole): a group's eight tiles of one block are 8 KiB in a row
         const int tt = n0 / 16 + wave * 2 + q;
-        b_src[q] = (uint32_t)(((int64_t)(tt / W4P_BLOCK_TILES) * ngroups * W4P_BLOCK_TILES + tt % W4P_BLOCK_TILES) *
+        b_src[q] = (uint32_t)(((int64_t)(tt / W4P_BLOCK_TILES) * ngt * W4P_BLOCK_TILES + tt % W4P_BLOCK_TILES) *
                                   1024 + lane * 16);
     }
     const uint32_t s_src = lane < 4 ? (uint32_t)((n0 + wave * 32) * 2 + lane * 16) : OOB;
@@ -194,12 +204,12 @@ void tile_w4_kernel(Problem p) {
     auto load_b = [&](int g, int slot) {
         const bool in = g < ngroups;
         if constexpr (U4) {
-            const int64_t go = (int64_t)g * W4P_BLOCK_TILES * 1024;
+            const int64_t go = (int64_t)(g0 + g) * W4P_BLOCK_TILES * 1024;
             const i32x4 rb = rsrc32((const char *)p.B + go, in ? (uint32_t)(b_bytes - go) : 0u);
 #pragma unroll
             for (int q = 0; q < 2; ++q) load_lds16(rb, lds0 + codes_w + slot * 2048 + q * 1024, b_src[q]);
         }
-        const int64_t so = (int64_t)g * p.ld_s * 2;
+        const int64_t so = (int64_t)(g0 + g) * p.ld_s * 2;
         const i32x4 rs = rsrc32((const char *)p.scales + so, in ? (uint32_t)(s_bytes - so) : 0u);
         load_lds16(rs, lds0 + scales_w + slot * 1024, s_src);
     };
@@ -214,7 +224,7 @@ void tile_w4_kernel(Problem p) {
     const int q_row = (1024 / L::BN) * wave + lane / QCH;
     const uint32_t q_src = (uint32_t)((int64_t)q_row * p.ldb + n0 + (((lane % QCH) ^ q_swz(q_row)) * 16));
     auto load_q = [&](int d) {
-        const int64_t ro = (int64_t)d * 32 * p.ldb;
+        const int64_t ro = (int64_t)(4 * g0 + d) * 32 * p.ldb;
         const i32x4 rq = rsrc32((const char *)p.B + ro, d < nst ? (uint32_t)(b_bytes - ro) : 0u);
         load_lds16(rq, lds0 + L::CODES + (d & 3) * Q_STAGE + wave * 1024, q_src);
     };
@@ -525,6 +535,56 @@ void tile_w4_kernel(Problem p) {
         }
     }
 
+    if constexpr (SPLIT) {
+        // partial tile -> slot (ks, t) of the scratch, lane-major (each lane's accumulators 16 bytes
+        // apart over the lanes, so the last workgroup's lane reads back exactly what the same lane of
+        // every slice wrote); device-scope cache policy on the stores and loads, a device-scope
+        // counter per tile
+        constexpr int SC1 = 16;
+        constexpr uint32_t PT = NW * W4_MT * W4_NT * 1024;  // bytes of one partial tile
+        __shared__ int s_last;
+        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)p.split_ws, (short)0, (int)((uint32_t)grid * PT), 0x00020000);
+        const uint32_t lane_off = (uint32_t)(wave * W4_MT * W4_NT * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < W4_MT; ++i)
+#pragma unroll
+            for (int j = 0; j < W4_NT; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rt,
+                                                       (uint32_t)(ks * total + t) * PT + lane_off +
+                                                           (uint32_t)(i * W4_NT + j) * 1024,
+                                                       0, SC1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are complete
+        GE_DEBUG_FENCE();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(p.split_cnt + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (uint32_t)(nsplit - 1);
+        }
+        __syncthreads();
+        if (!s_last) return;
+        GE_DEBUG_FENCE();
+#pragma unroll
+        for (int i = 0; i < W4_MT; ++i)
+#pragma unroll
+            for (int j = 0; j < W4_NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < nsplit; ++q) {  // slice order
+            f32x4 part[W4_MT][W4_NT];
+#pragma unroll
+            for (int i = 0; i < W4_MT; ++i)
+#pragma unroll
+                for (int j = 0; j < W4_NT; ++j)
+                    part[i][j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rt, (uint32_t)(q * total + t) * PT + lane_off + (uint32_t)(i * W4_NT + j) * 1024, 0, SC1));
+#pragma unroll
+            for (int i = 0; i < W4_MT; ++i)
+#pragma unroll
+                for (int j = 0; j < W4_NT; ++j) acc[i][j] += part[i][j];
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(p.split_cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     const EpiArgs &e = p.epi;
     const int mbase = m0 + frow;
     const int nbase = n0 + wave * 32 + fgrp * 4;
@@ -581,7 +641,39 @@ bool tile_w4_supported(const Problem &p) {
     return epi_ok(p);
 }
 
+// K split for too few tiles (33-256 rows): 64 x 128 tiles x S slices, S the largest of 2, 4, 8 that
+// keeps tiles x S within the CU count, divides the K / 128 groups and leaves each slice 2 or more
+static int tiles4(const Problem &p) { return ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4L<4>::BN); }
+
+int tile_w4_split(const Problem &p, int cu_count) {
+    if (!tile_w4_supported(p) || cu_count <= 0) return 1;
+    const int tiles = tiles4(p), ngt = p.K / 128;
+    int s = 1;
+    for (int c = 2; c <= 8; c *= 2)
+        if ((int64_t)tiles * c <= cu_count && ngt % c == 0 && ngt / c >= 2) s = c;
+    // 32-bit scratch offsets
+    while (s > 1 && (int64_t)tiles * s * (4 * W4_MT * W4_NT * 1024) >= (1ll << 31)) s /= 2;
+    return s;
+}
+
+int tile_w4_split_counters(const Problem &p) { return tiles4(p); }
+
+int64_t tile_w4_split_scratch_bytes(const Problem &p, int split) {
+    if (split <= 1) return 0;
+    return (int64_t)tiles4(p) * split * (4 * W4_MT * W4_NT * 1024) + (int64_t)tiles4(p) * 4;
+}
+
+static bool use_split(const Problem &p) { return p.split > 1 && p.split_ws && p.split_cnt; }
+
 const char *tile_w4_kernel_name(const Problem &p, int cu_count) {
+    if (p.split > 1) {  // (named from the plan's choice, before its scratch exists)
+        static const char *names[3][4] = {
+            {"tile_w4_bf16_64x128x32_split2", "tile_w4_bf16_64x128x32_split4", "tile_w4_bf16_64x128x32_split8", ""},
+            {"tile_w8_u8_64x128x32_split2", "tile_w8_u8_64x128x32_split4", "tile_w8_u8_64x128x32_split8", ""},
+            {"tile_w8_fp8_64x128x32_split2", "tile_w8_fp8_64x128x32_split4", "tile_w8_fp8_64x128x32_split8", ""}};
+        const int si = p.split == 2 ? 0 : p.split == 4 ? 1 : p.split == 8 ? 2 : 3;
+        return names[p.wfmt == WFMT_U8 ? 1 : p.wfmt == WFMT_FP8 ? 2 : 0][si];
+    }
     const bool w8 = w4_waves(p, cu_count) == 8;
     switch (p.wfmt) {
     case WFMT_U8: return w8 ? "tile_w8_u8_64x256x32" : "tile_w8_u8_64x128x32";
@@ -590,23 +682,27 @@ const char *tile_w4_kernel_name(const Problem &p, int cu_count) {
     }
 }
 
-template <int WF, int NW>
+template <int WF, int NW, bool SPLIT>
 static hipError_t launch_wf(const Problem &p, hipStream_t s) {
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel<WF, NW>,
+        hipError_t e = hipFuncSetAttribute((const void *)tile_w4_kernel<WF, NW, SPLIT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, W4L<NW>::LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4L<NW>::BN);
-    hipLaunchKernelGGL((tile_w4_kernel<WF, NW>), dim3(tiles), dim3(W4L<NW>::THREADS), W4L<NW>::LDS, s, p);
+    const int tiles = ((p.M + W4_BM - 1) / W4_BM) * (p.N / W4L<NW>::BN) * (SPLIT ? p.split : 1);
+    hipLaunchKernelGGL((tile_w4_kernel<WF, NW, SPLIT>), dim3(tiles), dim3(W4L<NW>::THREADS), W4L<NW>::LDS, s, p);
     return hipGetLastError();
 }
 
 template <int WF>
 static hipError_t launch_w(const Problem &p, int cu_count, hipStream_t s) {
-    return w4_waves(p, cu_count) == 8 ? launch_wf<WF, 8>(p, s) : launch_wf<WF, 4>(p, s);
+    if (use_split(p)) {
+        if ((p.K / 128) % p.split || p.split > 8) return hipErrorInvalidValue;
+        return launch_wf<WF, 4, true>(p, s);
+    }
+    return w4_waves(p, cu_count) == 8 ? launch_wf<WF, 8, false>(p, s) : launch_wf<WF, 4, false>(p, s);
 }
 
 hipError_t launch_tile_w4(const Problem &p, int cu_count, hipStream_t s) {

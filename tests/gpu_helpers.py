@@ -56,3 +56,18 @@ def w4_tile_cols(M, N):
     64 x 256 tiles still give every CU one, else 128 (4 waves)."""
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     return 256 if N % 256 == 0 and (M + 63) // 64 * (N // 256) >= cu else 128
+
+
+def w4_tile_kernel(fmt, M, N, K):
+    """Kernel name the plan gives the quantised tile path: split over K (64 x 128 tiles x S slices,
+    S in 2, 4, 8 dividing the K / 128 groups with 2 or more per slice) when the tiles do not fill
+    the CUs, else w4_tile_cols."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    prefix = {"u4": "tile_w4_bf16", "u8": "tile_w8_u8", "fp8": "tile_w8_fp8"}[fmt]
+    tiles, ngt, s = (M + 63) // 64 * (N // 128), K // 128, 1
+    for c in (2, 4, 8):
+        if tiles * c <= cu and ngt % c == 0 and ngt // c >= 2:
+            s = c
+    if s > 1:
+        return f"{prefix}_64x128x32_split{s}"
+    return f"{prefix}_64x{w4_tile_cols(M, N)}x32"

@@ -47,7 +47,8 @@ def run_cases(ge, torch):
         "decode_streamk": gemm("decode_streamk", 16, 4096, 8192, 4),
         "decode_prepacked": gemm("decode_prepacked", 16, 4096, 2048, 5, prepack=True),
         "w4_decode_split": w4(16, 8192, 2048, 6),
-        "w4_tile": w4(96, 1024, 1024, 7),
+        "w4_tile": w4(96, 1024, 1024, 7),  # split over K (4 slices)
+        "w4_tile_8wave": w4(100, 32768, 256, 11),  # enough 64 x 256 tiles for every CU: no split
         "w8_u8_split": w8("u8", 16, 4096, 4096, 8),
         "w8_u8_tile": w8("u8", 128, 1024, 1024, 9),
         "w8_fp8_tile": w8("fp8", 128, 1024, 1024, 10),

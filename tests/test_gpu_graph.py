@@ -120,10 +120,10 @@ def test_scratch_using_calls_replay_in_a_graph():
     oe, og = outs(), outs()
     eager, graph_calls = prepare(oe), prepare(og)
     kernels = [f._plan.kernel for f in eager]
-    assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1].startswith("tile_w4")
+    assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1] == "tile_w4_bf16_64x128x32_split4"
     assert kernels[2] == "tile_swiglu_256x128x32+128x128x32"
     assert kernels[3] == "skinny_bf16_m16_128col_streamk"
-    assert eager[0]._plan.scratch_bytes > 0 and eager[3]._plan.scratch_bytes > 0
+    assert eager[0]._plan.scratch_bytes > 0 and eager[1]._plan.scratch_bytes > 0 and eager[3]._plan.scratch_bytes > 0
     for f in eager + graph_calls:
         f()
     torch.cuda.synchronize()

@@ -8,7 +8,7 @@ import torch
 import gemm_epilogue_tile_amd as ge
 import oracle
 import workloads
-from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols, w4_tile_kernel
 
 pytestmark = pytest.mark.gpu
 
@@ -569,19 +569,22 @@ def test_w4_prepacked_tile_path(M, N, K):
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N)
     p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
-    # 8 waves and 256 columns per workgroup where those tiles fill the CUs, else 4 waves and 128
-    assert p.kernel == f"tile_w4_bf16_64x{w4_tile_cols(M, N)}x32"
+    # 8 waves and 256 columns per workgroup where those tiles fill the CUs, else 4 waves and 128,
+    # split over K where the 64 x 128 tiles leave CUs idle and the groups allow
+    assert p.kernel == w4_tile_kernel("u4", M, N, K)
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 
-def test_w4_tile_plan_owns_no_scratch_and_repeats_bitwise():
+@pytest.mark.parametrize("M,N,K", [(200, 384, 1024), (512, 8192, 1024)])
+def test_w4_tile_plan_scratch_and_repeats_bitwise(M, N, K):
     # the int4 tile kernel reads X directly (bf16) and keeps its per-group partial products and the
-    # zero-point correction on chip: no plan scratch; a second X on the same plan, then the first
-    # again, bitwise as before
-    M, N, K = 200, 384, 1024
+    # zero-point correction on chip; only the K split (12 tiles of 64 x 128 here) owns plan scratch:
+    # partial tiles and per-tile counters that the kernel re-arms.  A second X on the same plan,
+    # then the first again, bitwise as before (the slices are summed in a fixed order)
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     p = ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True)
-    assert p.kernel.startswith("tile_w4") and p.scratch_bytes == 0
+    assert p.kernel == w4_tile_kernel("u4", M, N, K)
+    assert (p.scratch_bytes > 0) == ("split" in p.kernel)
     a, b = workloads.make_inputs(w, seed=31), workloads.make_inputs(w, seed=32)
     b["Wq"], b["scales"], b["bias"] = a["Wq"], a["scales"], a["bias"]
     oa = _w4_packed(a)
@@ -597,7 +600,7 @@ def test_w4_tile_path_k_chunks(M, N, K):
     # chunks and a partial one, an odd group count); 33 groups; 96 groups
     w = workloads.WORKLOADS["w4a16_m512"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + K)
-    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel.startswith("tile_w4")
+    assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True, prepacked=True).kernel == w4_tile_kernel("u4", M, N, K)
     assert_close(_w4_packed(inp), oracle.reference(inp), TOL_BF16, f"w4 tile {M}x{N}x{K}")
 
 

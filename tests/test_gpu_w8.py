@@ -12,7 +12,7 @@ import torch
 import gemm_epilogue_tile_amd as ge
 import oracle
 import workloads
-from gpu_helpers import DEV, TOL_BF16, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols
+from gpu_helpers import DEV, TOL_BF16, assert_close, dev_inputs, to_dev, to_host, w4_tile_cols, w4_tile_kernel
 
 pytestmark = pytest.mark.gpu
 
@@ -53,11 +53,11 @@ def test_w8_plans_pick_the_streaming_kernel_for_small_M():
 @pytest.mark.parametrize("M,N,K", [(17, 128, 128), (64, 256, 1024), (100, 384, 4224), (512, 1024, 2048)])
 def test_w8_tile_kernel(fmt, M, N, K):
     # M > 16 with N % 128 == 0, K % 128 == 0 and 128-row groups: the tile kernel on raw codes (4 waves,
-    # 128 columns per workgroup at these sizes); K = 4224 is 33 groups, not a whole number of the
-    # kernel's two-group loop trips
+    # 128 columns per workgroup at these sizes, split over K where the groups allow); K = 4224 is 33
+    # groups, not a whole number of the kernel's two-group loop trips
     w = BASE[fmt].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=3 * M + K)
-    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
+    assert _plan_kernel(fmt, M, N, K) == w4_tile_kernel(fmt, M, N, K)
     assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} tile {M}x{N}x{K}")
 
 
@@ -67,7 +67,7 @@ def test_w8_tile_kernel_eight_waves(fmt, M, N, K):
     # enough 64 x 256 tiles for every CU: the 8-wave workgroups, ragged M (two and three row tiles)
     w = BASE[fmt].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + K)
-    assert _plan_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
+    assert _plan_kernel(fmt, M, N, K) == w4_tile_kernel(fmt, M, N, K) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
     assert_close(_w8(inp), oracle.reference(inp), TOL_BF16, f"{fmt} 8-wave tile {M}x{N}x{K}")
 
 
@@ -91,7 +91,7 @@ def test_w8_tile_strided_operands(fmt):
     Wf[:, :N] = torch.from_numpy(inp["Wq"]).to(DEV)
     out = ge.w4_gemm(Xf[:, :K], Wf[:, :N], d["scales"], bias=d.get("bias"), group=inp["group"],
                      zero_point=inp["zero_point"], fmt=fmt)
-    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == f"tile_w8_{fmt}_64x{w4_tile_cols(M, N)}x32"
+    assert _plan_kernel(fmt, M, N, K, lda=K + 8, ldb=N + 16) == w4_tile_kernel(fmt, M, N, K)
     assert_close(out, oracle.reference(inp), TOL_BF16, f"{fmt} tile strided")
 
 
@@ -196,8 +196,12 @@ def test_w8_split_plans_own_scratch():
     assert p.scratch_bytes == 4 * 64 * 16 * 128 * 4 + 64 * 4
     q = ge.plan(ge.KIND_W4, 16, 28672, 8192, b_type=ge.FP8E4M3, bias=True, zero_point=0)
     assert q.kernel == "skinny_fp8_m16_128col_split2"
+    # 40 rows take the tile kernel: 64 tiles of 64 x 128 split 4 ways over K, 4 x 64 partial tiles of
+    # 4 waves x 8 fragments of 1 KiB and 64 counters
     r = ge.plan(ge.KIND_W4, 40, 8192, 8192, b_type=ge.U8, bias=True, zero_point=128)
-    assert r.scratch_bytes == 0
+    assert r.kernel == w4_tile_kernel("u8", 40, 8192, 8192)
+    if r.kernel.endswith("split4"):
+        assert r.scratch_bytes == 4 * 64 * 4 * 8 * 1024 + 64 * 4
 
 
 @pytest.mark.parametrize("fmt", FMTS)
