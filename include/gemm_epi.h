@@ -40,10 +40,11 @@
  *
  * Plans are immutable once made: one plan may be used from several threads
  * and streams at once, with one exception: a plan that owns device scratch
- * (gemm_epi_plan_scratch_bytes() > 0: 8-bit weight plans with M <= 16 whose
- * K is split over workgroups, and bf16 generic plans with M <= 16 whose K is
- * split the same way (stream-K)) must not run on two streams at once, since
- * its launches share that scratch.
+ * (gemm_epi_plan_scratch_bytes() > 0: quantised-weight plans whose K is split
+ * over workgroups -- M <= 16 streaming, or the tile kernel at M > 16 (8-bit)
+ * or M > 32 (int4) when its tiles leave CUs idle -- and bf16 generic plans
+ * with M <= 16 whose K is split the same way (stream-K)) must not run on two
+ * streams at once, since its launches share that scratch.
  */
 #ifndef GEMM_EPI_H
 #define GEMM_EPI_H
@@ -162,10 +163,14 @@ GE_API void ge_desc_init(ge_desc *d);
  * *out receives a library-owned plan that the caller releases with
  * gemm_epi_plan_destroy().  Queries the current device (architecture and
  * compute-unit count); allocates host memory, and a zeroed device scratch
- * for two kinds of plan: 8-bit weight plans with M <= 16 whose column
- * blocks alone do not fill the GPU (the cross-workgroup K split: S *
- * ceil(N/128) * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters,
- * S in {2, 4, 8}); bf16 generic plans with M <= 16 whose column blocks leave
+ * for these plans: quantised-weight plans with M <= 16 whose column blocks
+ * alone do not fill the GPU (the cross-workgroup K split: S * ceil(N/128) *
+ * 8 KiB of fp32 tiles plus 4 * ceil(N/128) bytes of counters, S in {2, 4,
+ * 8}); quantised-weight plans on the tile kernel (prepacked int4 with M > 32,
+ * 8-bit with M > 16) whose 64 x 128 tiles leave CUs idle (K split S ways, S
+ * in {2, 4, 8} dividing K / 128 with 2 or more groups per slice: S * tiles *
+ * 32 KiB of fp32 partial tiles plus 4 * tiles bytes of counters, tiles =
+ * ceil(M / 64) * N / 128); bf16 generic plans with M <= 16 whose column blocks leave
  * CUs idle and whose (column block, 32-row K block) units divide evenly into
  * one K piece of one column block per CU (stream-K: the same tiles and
  * counters, S = pieces per block in {2..8}; e.g. 16 x 8192 x 8192 on 256
