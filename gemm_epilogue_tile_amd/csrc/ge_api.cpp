@@ -153,13 +153,13 @@ hipError_t launch_fused(const ge_plan *pl, const Problem &p, hipStream_t s) {
     if (skinny_supported(p)) return launch_skinny(p, pl->cu_count, s);
     if (tile_supported(p)) return launch_tile(p, pl->cu_count, s);
     if (p.w4_packed || p.b_packed) return hipErrorInvalidValue;  // only the specialised kernels read packed layouts
-    return launch_general(p, s);
+    return launch_general(p, pl->cu_count, s);
 }
 
 const char *fused_name(const Problem &p, int cu_count, bool scratch = true) {
     if (skinny_supported(p)) return skinny_kernel_name(p, cu_count, scratch);
     if (tile_supported(p)) return tile_kernel_name(p, cu_count);
-    return "general_64x64";
+    return general_kernel_name(p, cu_count);
 }
 
 ge_status check_device(const ge_plan *pl) {

@@ -8,9 +8,10 @@
 // branch).  It is the slow, simple path; the large-tile and skinny kernels
 // take the shapes that matter for speed.
 //
-// Tile: 64 x 64 outputs per 256-thread workgroup, 32-deep K steps staged in
-// LDS with the reduction index contiguous; four waves in a 2 x 2 grid, each
-// owning 32 x 32 outputs = 2 x 2 MFMA tiles of 16 x 16.
+// Tile: T x T outputs per 256-thread workgroup (T = 64, or 32 when 64 x 64
+// tiles would leave most CUs idle), 32-deep K steps staged in LDS with the
+// reduction index contiguous; four waves in a 2 x 2 grid, each owning
+// T/2 x T/2 outputs = MFMA tiles of 16 x 16.
 //   bf16 operands -> v_mfma_f32_16x16x32_bf16
 //   fp32 operands, and quantised weights -> v_mfma_f32_16x16x4f32 (the
 //   weights dequantise exactly: (code - zero_point) * scale has at most 16
@@ -22,7 +23,7 @@
 namespace ge {
 namespace {
 
-constexpr int GB_M = 64, GB_N = 64, GB_K = 32;
+constexpr int GB_K = 32;
 constexpr int G_THREADS = 256;
 
 // Raw bits of element i of a bf16 (T = uint16_t, zero-extended) or fp32 (T = float) array, with
@@ -44,62 +45,108 @@ __device__ __forceinline__ float raw_value(uint32_t bits, bool bf16, bool ok) {
 
 // USE_BF16: operands staged as bf16 and multiplied with the bf16 MFMA;
 // otherwise staged as fp32 and multiplied with the fp32 MFMA.
-template <bool USE_BF16, bool DUAL>
+template <bool USE_BF16, bool DUAL, int T>
 __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
+    static_assert(T == 32 || T == 64, "tile size");
     constexpr int PADK = USE_BF16 ? GB_K + 8 : GB_K + 1;
+    constexpr int W = T / 2, MT = W / 16;  // wave tile W x W, MT x MT MFMA tiles
+    constexpr int E = T / 8;               // A and B elements per thread per K step
     using S = typename std::conditional<USE_BF16, uint16_t, float>::type;
-    __shared__ __attribute__((aligned(16))) S As[GB_M][PADK];
-    __shared__ __attribute__((aligned(16))) S Bs[DUAL ? 2 : 1][GB_N][PADK];
+    __shared__ __attribute__((aligned(16))) S As[T][PADK];
+    __shared__ __attribute__((aligned(16))) S Bs[DUAL ? 2 : 1][T][PADK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * GB_M, n0 = blockIdx.x * GB_N;
+    const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
 
-    f32x4 acc[2][2][2];
+    f32x4 acc[2][MT][MT];
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[d][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < MT; ++j) acc[d][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The epilogue's operands (C, R, bias) do not depend on the product: they are requested
+    // first, so their latency overlaps the K loop.  Fragment layout: lane l, element r of tile
+    // (i, j) is row 16 i + 4 (l / 16) + r, column 16 j + l % 16 of the wave's W x W.
+    const EpiArgs &e = p.epi;
+    const bool hc = !DUAL && (e.flags & GE_FLAG_C), hb = !DUAL && (e.flags & GE_FLAG_BIAS);
+    const bool hr = !DUAL && (e.flags & GE_FLAG_RESIDUAL);
+    auto row_of = [&](int i, int r) { return m0 + wm * W + i * 16 + (lane >> 4) * 4 + r; };
+    auto col_of = [&](int j) { return n0 + wn * W + j * 16 + (lane & 15); };
+    // raw bits; em bit 4 (MT i + j) + r: output in range
+    uint32_t cv[MT][MT][4], rv[MT][MT][4], bv[MT], em = 0;
+    auto load_mat = [&](auto tag, const void *P, int64_t ld, uint32_t (&out)[MT][MT][4]) {
+        using TT = decltype(tag);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < MT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = row_of(i, r), n = col_of(j);
+                    out[i][j][r] = ld_raw<TT>(P, (int64_t)m * ld + n, m < p.M && n < p.N);
+                }
+    };
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                em |= (uint32_t)(row_of(i, r) < p.M && col_of(j) < p.N) << (4 * (MT * i + j) + r);
+    if (hc) {
+        if (e.c_type == GE_BF16) load_mat(uint16_t{}, e.C, e.ldc, cv); else load_mat(float{}, e.C, e.ldc, cv);
+    }
+    if (hr) {
+        if (e.r_type == GE_BF16) load_mat(uint16_t{}, e.R, e.ldr, rv); else load_mat(float{}, e.R, e.ldr, rv);
+    }
+    if (hb) {
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            const int n = col_of(j);
+            bv[j] = e.bias_type == GE_BF16 ? ld_raw<uint16_t>(e.bias, n, n < p.N) : ld_raw<float>(e.bias, n, n < p.N);
+        }
+    }
 
     // K steps are fetched into registers two ahead of the step being multiplied, as raw bits with
     // an in-range mask (bit i: A element i; bit 8 + 8 d + i: element i of B operand d)
-    // (A: thread -> row tid/4, 8 consecutive k; B: thread -> k row tid/8, 8 consecutive n)
+    // (A: thread -> one row, E consecutive k; B: thread -> k row tid / 8, E consecutive n)
     constexpr int NBT = DUAL ? 2 : 1;
-    const int ar = tid >> 2, akc = (tid & 3) * 8;
-    const int bkr = tid >> 3, bnc = (tid & 7) * 8;
+    const int ar = tid / (GB_K / E), akc = (tid % (GB_K / E)) * E;
+    const int bkr = tid >> 3, bnc = (tid & 7) * E;
     const bool quant = p.mode == MODE_W4, a16 = p.ab_type == GE_BF16;
     const bool kn = p.b_layout == GE_LAYOUT_KN;
-    uint32_t ra[2][8], rb[2][NBT][8], rsc[2][8], okm[2];
+    uint32_t ra[2][E], rb[2][NBT][E], rsc[2][E], okm[2];
     auto fetch = [&](int k0, auto SLOT) {
         constexpr int sl = decltype(SLOT)::value;
         uint32_t mask = 0;
         auto fetch_a = [&](auto tag) {
-            using T = decltype(tag);
+            using ET = decltype(tag);
             const int m = m0 + ar;
             const int64_t row = (int64_t)m * p.lda;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < E; ++i) {
                 const int k = k0 + akc + i;
                 const bool ok = m < p.M && k < p.K;
                 mask |= (uint32_t)ok << i;
-                ra[sl][i] = ld_raw<T>(p.A, row + k, ok);
+                ra[sl][i] = ld_raw<ET>(p.A, row + k, ok);
             }
         };
         auto fetch_b = [&](auto tag) {
-            using T = decltype(tag);
+            using ET = decltype(tag);
             const int k = k0 + bkr;
 #pragma unroll
             for (int d = 0; d < NBT; ++d) {
                 const void *B = d == 0 ? p.B : p.B2;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < E; ++i) {
                     const int n = n0 + bnc + i;
                     const bool ok = k < p.K && n < p.N;
                     mask |= (uint32_t)ok << (8 + 8 * d + i);
-                    rb[sl][d][i] = ld_raw<T>(B, kn ? (int64_t)k * p.ldb + n : (int64_t)n * p.ldb + k, ok);
+                    rb[sl][d][i] = ld_raw<ET>(B, kn ? (int64_t)k * p.ldb + n : (int64_t)n * p.ldb + k, ok);
                 }
             }
         };
@@ -111,7 +158,7 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
             const int64_t crow = (int64_t)(kok ? k : 0) * p.ldb;
             const bool u4 = p.wfmt == WFMT_U4;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < E; ++i) {
                 const int n = n0 + bnc + i;
                 const bool ok = kok && n < p.N;
                 const int nn = ok ? n : 0;
@@ -137,7 +184,7 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
         constexpr int sl = decltype(SLOT)::value;
         const uint32_t mask = okm[sl];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < E; ++i) {
             const bool ok = (mask >> i) & 1;
             if constexpr (USE_BF16) As[ar][akc + i] = ok ? (uint16_t)ra[sl][i] : (uint16_t)0;
             else As[ar][akc + i] = raw_value(ra[sl][i], a16, ok);
@@ -146,14 +193,14 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
 #pragma unroll
             for (int d = 0; d < NBT; ++d)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < E; ++i) {
                     const bool ok = (mask >> (8 + 8 * d + i)) & 1;
                     Bs[d][bnc + i][bkr] = ok ? (uint16_t)rb[sl][d][i] : (uint16_t)0;
                 }
         } else if (!DUAL && quant) {
             const bool u4 = p.wfmt == WFMT_U4, u8 = p.wfmt == WFMT_U8;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < E; ++i) {
                 const bool ok = (mask >> (8 + i)) & 1;
                 const uint32_t byte = rb[sl][0][i];
                 float w;
@@ -171,7 +218,7 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
 #pragma unroll
             for (int d = 0; d < NBT; ++d)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < E; ++i) {
                     const bool ok = (mask >> (8 + 8 * d + i)) & 1;
                     Bs[d][bnc + i][bkr] = raw_value(rb[sl][d][i], a16, ok);
                 }
@@ -186,32 +233,32 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
 
         if constexpr (USE_BF16) {
             const int kk = (lane >> 4) * 8;
-            bf16x8 af[2];
+            bf16x8 af[MT];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *(const bf16x8 *)&As[wm * 32 + i * 16 + (lane & 15)][kk];
+            for (int i = 0; i < MT; ++i)
+                af[i] = *(const bf16x8 *)&As[wm * W + i * 16 + (lane & 15)][kk];
 #pragma unroll
             for (int d = 0; d < (DUAL ? 2 : 1); ++d)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const bf16x8 bfr = *(const bf16x8 *)&Bs[d][wn * 32 + j * 16 + (lane & 15)][kk];
+                for (int j = 0; j < MT; ++j) {
+                    const bf16x8 bfr = *(const bf16x8 *)&Bs[d][wn * W + j * 16 + (lane & 15)][kk];
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) acc[d][i][j] = mfma_bf16(af[i], bfr, acc[d][i][j]);
+                    for (int i = 0; i < MT; ++i) acc[d][i][j] = mfma_bf16(af[i], bfr, acc[d][i][j]);
                 }
         } else {
 #pragma unroll
             for (int ks = 0; ks < GB_K; ks += 4) {
                 const int kk = ks + (lane >> 4);
-                float af[2];
+                float af[MT];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) af[i] = As[wm * 32 + i * 16 + (lane & 15)][kk];
+                for (int i = 0; i < MT; ++i) af[i] = As[wm * W + i * 16 + (lane & 15)][kk];
 #pragma unroll
                 for (int d = 0; d < (DUAL ? 2 : 1); ++d)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const float bv = Bs[d][wn * 32 + j * 16 + (lane & 15)][kk];
+                    for (int j = 0; j < MT; ++j) {
+                        const float bf = Bs[d][wn * W + j * 16 + (lane & 15)][kk];
 #pragma unroll
-                        for (int i = 0; i < 2; ++i) acc[d][i][j] = mfma_f32(af[i], bv, acc[d][i][j]);
+                        for (int i = 0; i < MT; ++i) acc[d][i][j] = mfma_f32(af[i], bf, acc[d][i][j]);
                     }
             }
         }
@@ -227,56 +274,17 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
         if (k0 + GB_K < p.K) step(k0 + GB_K, Slot1{});
     }
 
-    // epilogue from the MFMA fragment layout: lane l, element r of tile (i, j) is row
-    // 16 i + 4 (l / 16) + r, column 16 j + l % 16 of the wave's 32 x 32.  Every operand the
-    // epilogue reads is requested first (branch-free), then each element is finished and stored.
-    const EpiArgs &e = p.epi;
-    const bool hc = !DUAL && (e.flags & GE_FLAG_C), hb = !DUAL && (e.flags & GE_FLAG_BIAS);
-    const bool hr = !DUAL && (e.flags & GE_FLAG_RESIDUAL);
-    auto row_of = [&](int i, int r) { return m0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r; };
-    auto col_of = [&](int j) { return n0 + wn * 32 + j * 16 + (lane & 15); };
-    uint32_t cv[2][2][4], rv[2][2][4], bv[2], em = 0;  // raw bits; em bit 4 (2 i + j) + r: in range
-    auto load_mat = [&](auto tag, const void *P, int64_t ld, uint32_t (&out)[2][2][4]) {
-        using T = decltype(tag);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = row_of(i, r), n = col_of(j);
-                    out[i][j][r] = ld_raw<T>(P, (int64_t)m * ld + n, m < p.M && n < p.N);
-                }
-    };
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) em |= (uint32_t)(row_of(i, r) < p.M && col_of(j) < p.N) << (8 * i + 4 * j + r);
-    if (hc) {
-        if (e.c_type == GE_BF16) load_mat(uint16_t{}, e.C, e.ldc, cv); else load_mat(float{}, e.C, e.ldc, cv);
-    }
-    if (hr) {
-        if (e.r_type == GE_BF16) load_mat(uint16_t{}, e.R, e.ldr, rv); else load_mat(float{}, e.R, e.ldr, rv);
-    }
-    if (hb) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = col_of(j);
-            bv[j] = e.bias_type == GE_BF16 ? ld_raw<uint16_t>(e.bias, n, n < p.N) : ld_raw<float>(e.bias, n, n < p.N);
-        }
-    }
+    // epilogue: each in-range element finished in fp32 and stored
     with_act(DUAL ? GE_ACT_NONE : e.act, [&](auto ACTC) {
         constexpr int ACT = decltype(ACTC)::value;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < MT; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = row_of(i, r), n = col_of(j);
-                    if ((em >> (8 * i + 4 * j + r)) & 1) {
+                    if ((em >> (4 * (MT * i + j) + r)) & 1) {
                         float v;
                         if constexpr (DUAL) {
                             const float g = acc[0][i][j][r], u = acc[1][i][j][r];
@@ -297,19 +305,35 @@ __global__ __launch_bounds__(G_THREADS) void general_kernel(Problem p) {
 
 }  // namespace
 
-hipError_t launch_general(const Problem &p, hipStream_t s) {
-    const dim3 grid((p.N + GB_N - 1) / GB_N, (p.M + GB_M - 1) / GB_M);
+// 32 x 32 tiles when 64 x 64 ones would fill fewer than half the CUs (small problems: four times
+// the workgroups, each a quarter of the MFMA work per K step), 64 x 64 otherwise
+int general_tile(const Problem &p, int cu_count) {
+    const int64_t tiles64 = (int64_t)((p.M + 63) / 64) * ((p.N + 63) / 64);
+    return 2 * tiles64 < cu_count ? 32 : 64;
+}
+
+const char *general_kernel_name(const Problem &p, int cu_count) {
+    return general_tile(p, cu_count) == 32 ? "general_32x32" : "general_64x64";
+}
+
+template <int T>
+static hipError_t launch_general_t(const Problem &p, hipStream_t s) {
+    const dim3 grid((p.N + T - 1) / T, (p.M + T - 1) / T);
     const bool bf16 = p.ab_type == GE_BF16 && p.mode != MODE_W4;
     const bool dual = p.mode == MODE_SWIGLU;
     if (bf16 && dual)
-        hipLaunchKernelGGL((general_kernel<true, true>), grid, dim3(G_THREADS), 0, s, p);
+        hipLaunchKernelGGL((general_kernel<true, true, T>), grid, dim3(G_THREADS), 0, s, p);
     else if (bf16)
-        hipLaunchKernelGGL((general_kernel<true, false>), grid, dim3(G_THREADS), 0, s, p);
+        hipLaunchKernelGGL((general_kernel<true, false, T>), grid, dim3(G_THREADS), 0, s, p);
     else if (dual)
-        hipLaunchKernelGGL((general_kernel<false, true>), grid, dim3(G_THREADS), 0, s, p);
+        hipLaunchKernelGGL((general_kernel<false, true, T>), grid, dim3(G_THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((general_kernel<false, false>), grid, dim3(G_THREADS), 0, s, p);
+        hipLaunchKernelGGL((general_kernel<false, false, T>), grid, dim3(G_THREADS), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_general(const Problem &p, int cu_count, hipStream_t s) {
+    return general_tile(p, cu_count) == 32 ? launch_general_t<32>(p, s) : launch_general_t<64>(p, s);
 }
 
 }  // namespace ge

@@ -49,7 +49,9 @@ struct Problem {
 };
 
 // Fallback tile kernel: any shape, stride and alignment.
-hipError_t launch_general(const Problem &p, hipStream_t s);
+hipError_t launch_general(const Problem &p, int cu_count, hipStream_t s);
+int general_tile(const Problem &p, int cu_count);  // 32 or 64
+const char *general_kernel_name(const Problem &p, int cu_count);
 
 // Large-tile bf16 MFMA kernel (M large).  Returns hipErrorInvalidValue when
 // the problem does not meet its preconditions (see tile_supported()).

@@ -154,6 +154,50 @@ def test_misaligned_pointers_take_the_general_kernel():
     assert_close(out, oracle.reference(inp), TOL_BF16, "misaligned")
 
 
+# The general kernel takes 32 x 32 tiles when 64 x 64 ones would fill fewer than half of the 256
+# CUs, 64 x 64 tiles otherwise; both sizes against the oracle, for fp32 operands, misaligned bf16
+# operands (which the tile kernels refuse), the dual product and raw int4 weights.
+@pytest.mark.parametrize("case,M,N,K,tile", [
+    ("f32", 64, 64, 128, 32),       # the tiny config's shape: one 64 x 64 tile, four of 32 x 32
+    ("f32", 300, 200, 70, 32),      # 5 x 4 tiles of 64
+    ("f32", 700, 1200, 96, 64),     # 11 x 19 = 209 tiles of 64
+    ("bf16_misaligned", 70, 90, 101, 32),
+    ("bf16_misaligned", 700, 1200, 101, 64),
+    ("swiglu_k_ragged", 100, 300, 100, 32),
+    ("swiglu_k_ragged", 900, 1100, 100, 64),
+    ("w4_raw", 40, 256, 256, 32),
+    ("w4_raw", 600, 1024, 256, 64),
+])
+def test_general_tile_size_choice_and_parity(case, M, N, K, tile):
+    name = f"general_{tile}x{tile}"
+    if case == "f32":
+        w = workloads.WORKLOADS["tiny_fp32"].with_shape(M=M, N=N, K=K)
+        inp = workloads.make_inputs(w, seed=M + K)
+        assert ge.plan(ge.KIND_GENERIC, M, N, K, a_type=ge.F32, b_type=ge.F32, d_type=ge.F32, c_type=ge.F32,
+                       bias_type=ge.F32, bias=True, C=True, beta=0.5, act="relu").kernel == name
+        assert_close(_generic(inp), oracle.reference(inp), TOL_F32, f"f32 {M}x{N}x{K}")
+    elif case == "bf16_misaligned":
+        w = SQ.with_shape(M=M, N=N, K=K)
+        inp = workloads.make_inputs(w, seed=M + 1)
+        d = dev_inputs(inp)
+        flatA = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+        flatA[1:] = d["A"].reshape(-1)
+        A = flatA[1:].view(M, K)
+        out = ge.gemm_epilogue(A, d["B"], bias=d["bias"], R=d["R"], act="gelu_tanh")
+        assert_close(out, oracle.reference(inp), TOL_BF16, f"misaligned {M}x{N}x{K}")
+    elif case == "swiglu_k_ragged":
+        assert ge.plan(ge.KIND_SWIGLU, M, N, K).kernel == name
+        w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
+        inp = workloads.make_inputs(w, seed=M + N)
+        d = dev_inputs(inp)
+        assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
+    else:
+        assert ge.plan(ge.KIND_W4, M, N, K, b_type=ge.U4X2, bias=True).kernel == name
+        w = workloads.WORKLOADS["w4a16_m16"].with_shape(M=M, N=N, K=K)
+        inp = workloads.make_inputs(w, seed=M + K)
+        assert_close(_w4(inp), oracle.reference(inp), TOL_BF16, f"w4 raw {M}x{N}x{K}")
+
+
 def test_output_aliases_residual():
     w = SQ.with_shape(M=128, N=128, K=256)
     inp = workloads.make_inputs(w, seed=10)
