@@ -244,12 +244,18 @@ def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
         x = torch.randn(M, N, device="cuda", generator=g).bfloat16()
         sets.append((a, x, torch.empty_like(a), torch.empty_like(a)))
     w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).bfloat16()
-    calls = [(lambda a=a, x=x, r=r, o=o: ge.add_rmsnorm(a, x, w, resid=r, out=o)) for a, x, r, o in sets]
+    calls = [ge.prepare_add_rmsnorm(a, x, w, resid=r, out=o) for a, x, r, o in sets]
     kern = time_launches(calls, steps, warmup) / steps
+    # the unfused chain: an add kernel (reads a, x; writes resid), then the RMSNorm kernel (reads
+    # resid, w; writes out)
+    ucalls = [ge.prepare_add_rmsnorm(a, x, w, resid=r, out=o, unfused=True) for a, x, r, o in sets]
+    unf = time_launches(ucalls, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
     byts = set_bytes + N * 2
+    ubyts = 5 * M * N * 2 + N * 2
     return {"kernel": "add_rmsnorm", "M": M, "N": N, "bytes": byts, "rotations": nrot,
             "kernel_ms_avg": round(kern, 4), "gbps": round(byts / (kern * 1e-3) / 1e9, 1),
-            "hbm_frac": round(byts / (kern * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+            "hbm_frac": round(byts / (kern * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "unfused_ms": round(unf, 4), "unfused_bytes": ubyts, "speedup_vs_unfused": round(unf / kern, 4)}
 
 
 def measure_rope_qk(steps, warmup):

@@ -41,7 +41,7 @@ EXPORTS = [
     "gemm_epi_run_noalloc",
     "gemm_swiglu_run", "gemm_w4_run", "gemm_epi_unfused_workspace_bytes", "gemm_epi_run_unfused",
     "gemm_swiglu_run_unfused", "gemm_w4_run_unfused", "gemm_w4_dequant_run", "gemm_w4_prepack", "gemm_b_prepack",
-    "ge_add_rmsnorm_run", "ge_rope_qk_run", "ge_rope_run",
+    "ge_add_rmsnorm_run", "ge_add_rmsnorm_run_unfused", "ge_rope_qk_run", "ge_rope_run",
     "ge_status_string", "ge_last_error", "ge_version",
 ]
 
@@ -116,6 +116,8 @@ def lib():
             L.gemm_b_prepack.restype = I
             L.ge_add_rmsnorm_run.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
             L.ge_add_rmsnorm_run.restype = I
+            L.ge_add_rmsnorm_run_unfused.argtypes = [I, I, P, P, P, ctypes.c_float, P, P, P]
+            L.ge_add_rmsnorm_run_unfused.restype = I
             L.ge_rope_qk_run.argtypes = [I, I, I, I, P, P, P, P, I, I, I, I, ctypes.c_float, I, P, P]
             L.ge_rope_qk_run.restype = I
             L.ge_rope_run.argtypes = [I, I, I, P, P, P, I, I, I, P, P]
@@ -459,8 +461,7 @@ def w4_dequant(Wq, scales, *, M=1, group=128, zero_point=None, lo_first=False, o
     return out
 
 
-def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
-    """resid = a + x; out = resid * rsqrt(mean(resid^2) + eps) * w (fused row kernel, bf16)."""
+def _add_rmsnorm_args(a, x, w, eps, resid, out, stream):
     torch = _torch()
     M, N = a.shape
     resid = resid if resid is not None else torch.empty_like(a)
@@ -468,9 +469,28 @@ def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
     for t in (a, x, resid, out):
         if not t.is_contiguous() or t.dtype != torch.bfloat16:
             raise ValueError("add_rmsnorm takes dense bf16 rows")
-    _check(lib().ge_add_rmsnorm_run(M, N, _ptr(a), _ptr(x), _ptr(w), float(eps), _ptr(resid), _ptr(out),
-                                    _stream(stream)), "ge_add_rmsnorm_run")
+    return resid, out, (M, N, _ptr(a), _ptr(x), _ptr(w), float(eps), _ptr(resid), _ptr(out), _stream(stream))
+
+
+def add_rmsnorm(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
+    """resid = a + x; out = resid * rsqrt(mean(resid^2) + eps) * w (fused row kernel, bf16)."""
+    resid, out, args = _add_rmsnorm_args(a, x, w, eps, resid, out, stream)
+    _check(lib().ge_add_rmsnorm_run(*args), "ge_add_rmsnorm_run")
     return resid, out
+
+
+def add_rmsnorm_unfused(a, x, w, *, eps=1e-6, resid=None, out=None, stream=None):
+    """The same step as two kernels (add, then RMSNorm over the stored bf16 residual); measurement only."""
+    resid, out, args = _add_rmsnorm_args(a, x, w, eps, resid, out, stream)
+    _check(lib().ge_add_rmsnorm_run_unfused(*args), "ge_add_rmsnorm_run_unfused")
+    return resid, out
+
+
+def prepare_add_rmsnorm(a, x, w, *, resid, out, eps=1e-6, unfused=False, stream=None) -> Prepared:
+    """``add_rmsnorm`` (or its unfused chain) bound to fixed tensors and stream."""
+    resid, out, args = _add_rmsnorm_args(a, x, w, eps, resid, out, stream)
+    name = "ge_add_rmsnorm_run_unfused" if unfused else "ge_add_rmsnorm_run"
+    return Prepared(getattr(lib(), name), name, None, [a, x, w, resid, out], args)
 
 
 def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, beta=0.0, act="none",

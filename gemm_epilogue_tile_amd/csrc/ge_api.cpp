@@ -910,8 +910,8 @@ ge_status ge_rope_run(int32_t batch, int32_t S, int32_t D, const void *X, const 
                       "ge_rope_run");
 }
 
-ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,
-                             void *resid, void *out, void *stream) {
+static ge_status add_rmsnorm_common(bool fused, int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                                    float eps, void *resid, void *out, void *stream) {
     if (M <= 0 || N <= 0) return fail(GE_ERR_INVALID_ARG, "M and N must be positive");
     if (N > 16384) return fail(GE_ERR_UNSUPPORTED, "rows longer than 16384 elements");
     if (!a || !x || !w || !resid || !out) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
@@ -926,8 +926,21 @@ ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x,
         (void)hipGetLastError();
         return fail(GE_ERR_NO_DEVICE, "no HIP device visible");
     }
-    return hip_status(launch_add_rmsnorm(M, N, a, x, w, eps, resid, out, (hipStream_t)stream),
-                      "ge_add_rmsnorm_run");
+    if (fused)
+        return hip_status(launch_add_rmsnorm(M, N, a, x, w, eps, resid, out, (hipStream_t)stream),
+                          "ge_add_rmsnorm_run");
+    return hip_status(launch_add_rmsnorm_unfused(M, N, a, x, w, eps, resid, out, (hipStream_t)stream),
+                      "ge_add_rmsnorm_run_unfused");
+}
+
+ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,
+                             void *resid, void *out, void *stream) {
+    return add_rmsnorm_common(true, M, N, a, x, w, eps, resid, out, stream);
+}
+
+ge_status ge_add_rmsnorm_run_unfused(int32_t M, int32_t N, const void *a, const void *x, const void *w, float eps,
+                                     void *resid, void *out, void *stream) {
+    return add_rmsnorm_common(false, M, N, a, x, w, eps, resid, out, stream);
 }
 
 }  // extern "C"

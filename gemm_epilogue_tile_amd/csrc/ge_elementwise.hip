@@ -199,11 +199,14 @@ __global__ __launch_bounds__(EW_THREADS) void k_w4_dequant(int32_t K, int32_t N,
 // same thread writes resid at that position, so resid may alias a or x.
 constexpr int RMS_MAX_CHUNKS = 8;
 
+// ADD = false: the RMSNorm alone, over rows of a (x and resid unused), the second kernel of the
+// unfused chain.
+template <bool ADD>
 __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm(int32_t M, int32_t N, const uint16_t *a,
                                                            const uint16_t *x, const uint16_t *w,
                                                            float eps, uint16_t *resid, uint16_t *out) {
     __shared__ float red[EW_THREADS / 64];
-    const bool al = aligned16(a) && aligned16(x) && aligned16(w) && aligned16(resid) &&
+    const bool al = aligned16(a) && (!ADD || (aligned16(x) && aligned16(resid))) && aligned16(w) &&
                     aligned16(out) && (N & 7) == 0;
     for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
         float r[RMS_MAX_CHUNKS][8];
@@ -213,15 +216,16 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm(int32_t M, int32_t N
             const int64_t n = ((int64_t)c * EW_THREADS + threadIdx.x) * 8;
             if (n < N) {
                 const bool vec = n + 8 <= N;
-                float vx[8];
                 rd(a, GE_BF16, N, m, n, N, vec, al, r[c]);
-                rd(x, GE_BF16, N, m, n, N, vec, al, vx);
+                if constexpr (ADD) {
+                    float vx[8];
+                    rd(x, GE_BF16, N, m, n, N, vec, al, vx);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    r[c][i] += vx[i];
-                    ss = fmaf(r[c][i], r[c][i], ss);
+                    for (int i = 0; i < 8; ++i) r[c][i] += vx[i];
+                    wr(resid, GE_BF16, N, m, n, N, vec, al, r[c]);
                 }
-                wr(resid, GE_BF16, N, m, n, N, vec, al, r[c]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(r[c][i], r[c][i], ss);
             }
         }
 #pragma unroll
@@ -256,7 +260,7 @@ constexpr int EW_NT = 2;
 // the 8-element chunks c * 64 + l (c < CH); every load of the row (a, x and w) is requested
 // before any is used, through buffer loads that read zeros past the row's end, and the
 // stores past the end are dropped the same way, so the row needs no branches.
-template <int CH>
+template <int CH, bool ADD>
 __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int32_t N, const uint16_t *a,
                                                                 const uint16_t *x, const uint16_t *w,
                                                                 float eps, uint16_t *resid, uint16_t *out) {
@@ -273,12 +277,16 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int3
         vw[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (c * 64 + lane) * 16, 0, 0));
     for (int64_t m = (int64_t)blockIdx.x * rows_per_block + (threadIdx.x >> 6); m < M;
          m += (int64_t)gridDim.x * rows_per_block) {
-        const __amdgpu_buffer_rsrc_t ra = rsrc(a + m * N), rx = rsrc(x + m * N);
+        const __amdgpu_buffer_rsrc_t ra = rsrc(a + m * N);
         u32x4 va[CH], vx[CH];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
+        for (int c = 0; c < CH; ++c)
             va[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, (c * 64 + lane) * 16, 0, 0));
-            vx[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c * 64 + lane) * 16, 0, 0));
+        if constexpr (ADD) {
+            const __amdgpu_buffer_rsrc_t rx = rsrc(x + m * N);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                vx[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c * 64 + lane) * 16, 0, 0));
         }
         float r[CH][8];
         float ss = 0.0f;
@@ -286,15 +294,19 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int3
         for (int c = 0; c < CH; ++c)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                r[c][2 * q] = bf16lo(va[c][q]) + bf16lo(vx[c][q]);
-                r[c][2 * q + 1] = bf16hi(va[c][q]) + bf16hi(vx[c][q]);
+                r[c][2 * q] = bf16lo(va[c][q]);
+                r[c][2 * q + 1] = bf16hi(va[c][q]);
+                if constexpr (ADD) {
+                    r[c][2 * q] += bf16lo(vx[c][q]);
+                    r[c][2 * q + 1] += bf16hi(vx[c][q]);
+                }
                 ss = fmaf(r[c][2 * q], r[c][2 * q], ss);
                 ss = fmaf(r[c][2 * q + 1], r[c][2 * q + 1], ss);
             }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
         const float rrms = 1.0f / sqrtf(ss / (float)N + eps);
-        const __amdgpu_buffer_rsrc_t rr = rsrc(resid + m * N), ro = rsrc(out + m * N);
+        const __amdgpu_buffer_rsrc_t ro = rsrc(out + m * N);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             u32x4 wr, wo;
@@ -303,7 +315,8 @@ __global__ __launch_bounds__(EW_THREADS) void k_add_rmsnorm_wave(int32_t M, int3
                 wr[q] = pack_bf16x2(r[c][2 * q], r[c][2 * q + 1]);
                 wo[q] = pack_bf16x2(r[c][2 * q] * rrms * bf16lo(vw[c][q]), r[c][2 * q + 1] * rrms * bf16hi(vw[c][q]));
             }
-            __builtin_amdgcn_raw_buffer_store_b128(wr, rr, (c * 64 + lane) * 16, 0, EW_NT);
+            if constexpr (ADD)
+                __builtin_amdgcn_raw_buffer_store_b128(wr, rsrc(resid + m * N), (c * 64 + lane) * 16, 0, EW_NT);
             __builtin_amdgcn_raw_buffer_store_b128(wo, ro, (c * 64 + lane) * 16, 0, EW_NT);
         }
     }
@@ -372,18 +385,24 @@ hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
     return hipGetLastError();
 }
 
-hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
-                              float eps, void *resid, void *out, hipStream_t s) {
-    const bool al = aligned16(a) && aligned16(x) && aligned16(w) && aligned16(resid) && aligned16(out);
+// add = false: the RMSNorm alone over the rows of a (x and resid unused)
+static hipError_t launch_rmsnorm_rows(bool add, int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                                      float eps, void *resid, void *out, hipStream_t s) {
+    const bool al = aligned16(a) && (!add || (aligned16(x) && aligned16(resid))) && aligned16(w) && aligned16(out);
+    auto with_add = [&](auto F) {
+        if (add) F(std::true_type{}); else F(std::false_type{});
+    };
     if (al && N % 8 == 0 && N <= 4096) {
         const int rows = EW_THREADS / 64;
         const unsigned blocks = (unsigned)((M + rows - 1) / rows < 65536 ? (M + rows - 1) / rows : 65536);
         const int ch = (N + 511) / 512;
         auto go = [&](auto CHC) {
             constexpr int CH = decltype(CHC)::value;
-            hipLaunchKernelGGL(k_add_rmsnorm_wave<CH>, dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
-                               (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
-                               (uint16_t *)resid, (uint16_t *)out);
+            with_add([&](auto ADDC) {
+                hipLaunchKernelGGL((k_add_rmsnorm_wave<CH, decltype(ADDC)::value>), dim3(blocks), dim3(EW_THREADS), 0,
+                                   s, M, N, (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
+                                   (uint16_t *)resid, (uint16_t *)out);
+            });
         };
         if (ch <= 1)
             go(std::integral_constant<int, 1>{});
@@ -396,10 +415,26 @@ hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)(M < 65536 ? M : 65536);
-    hipLaunchKernelGGL(k_add_rmsnorm, dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
-                       (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps,
-                       (uint16_t *)resid, (uint16_t *)out);
+    with_add([&](auto ADDC) {
+        hipLaunchKernelGGL((k_add_rmsnorm<decltype(ADDC)::value>), dim3(blocks), dim3(EW_THREADS), 0, s, M, N,
+                           (const uint16_t *)a, (const uint16_t *)x, (const uint16_t *)w, eps, (uint16_t *)resid,
+                           (uint16_t *)out);
+    });
     return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                              float eps, void *resid, void *out, hipStream_t s) {
+    return launch_rmsnorm_rows(true, M, N, a, x, w, eps, resid, out, s);
+}
+
+// The same step unfused, for measurement: resid = bf16(a + x) by the elementwise add kernel, then
+// the RMSNorm kernel over the stored (bf16) resid.
+hipError_t launch_add_rmsnorm_unfused(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                                      float eps, void *resid, void *out, hipStream_t s) {
+    const hipError_t e = launch_ew_add(M, N, a, GE_BF16, x, GE_BF16, N, resid, GE_BF16, N, s);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm_rows(false, M, N, resid, nullptr, w, eps, nullptr, out, s);
 }
 
 }  // namespace ge

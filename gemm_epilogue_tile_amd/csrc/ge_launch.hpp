@@ -143,5 +143,8 @@ hipError_t launch_w4_dequant(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 // Fused residual add + RMSNorm (bf16 rows).
 hipError_t launch_add_rmsnorm(int32_t M, int32_t N, const void *a, const void *x, const void *w,
                               float eps, void *resid, void *out, hipStream_t s);
+// The same step as two kernels (add, then RMSNorm over the stored residual), for measurement.
+hipError_t launch_add_rmsnorm_unfused(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                                      float eps, void *resid, void *out, hipStream_t s);
 
 }  // namespace ge

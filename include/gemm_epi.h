@@ -360,6 +360,18 @@ GE_API ge_status gemm_w4_dequant_run(const ge_plan *plan, const uint8_t *Wq, con
 GE_API ge_status ge_add_rmsnorm_run(int32_t M, int32_t N, const void *a, const void *x, const void *w,
                              float eps, void *resid, void *out, void *stream);
 
+/*
+ * The same step deliberately unfused, for measurement only (page "Fusion
+ * Thinking", Pattern 1: the separate add and normalisation kernels that the
+ * fused one replaces): one elementwise kernel writes resid = bf16(a + x),
+ * then a second one reads the stored resid back and writes out = resid /
+ * sqrt(mean(resid^2) + eps) * w, so the norm is taken over the rounded
+ * residual.  Same arguments, checks, aliasing rules and status codes as
+ * ge_add_rmsnorm_run; resid is written before it is read, on the same stream.
+ */
+GE_API ge_status ge_add_rmsnorm_run_unfused(int32_t M, int32_t N, const void *a, const void *x, const void *w,
+                                     float eps, void *resid, void *out, void *stream);
+
 /* Static text for a status code. */
 GE_API const char *ge_status_string(ge_status s);
 

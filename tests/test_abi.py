@@ -163,17 +163,19 @@ def test_run_calls_reject_null_plan():
     assert L.gemm_epi_plan_destroy(p) == 0  # NULL is accepted
 
 
-def test_add_rmsnorm_argument_checks():
-    L = ge.lib()
+@pytest.mark.parametrize("fn", ["ge_add_rmsnorm_run", "ge_add_rmsnorm_run_unfused"])
+def test_add_rmsnorm_argument_checks(fn):
+    run = getattr(ge.lib(), fn)
     f = ctypes.c_float(1e-6)
     a = ctypes.c_void_p(4096)
-    assert L.ge_add_rmsnorm_run(0, 16, a, a, a, f, ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20), None) \
-        == ge.ERR_INVALID_ARG
-    assert L.ge_add_rmsnorm_run(1, 1 << 15, a, a, a, f, ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20), None) \
-        == ge.ERR_UNSUPPORTED
-    assert L.ge_add_rmsnorm_run(2, 16, a, None, a, f, a, ctypes.c_void_p(1 << 20), None) == ge.ERR_INVALID_ARG
+    assert run(0, 16, a, a, a, f, ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20), None) == ge.ERR_INVALID_ARG
+    assert run(1, 1 << 15, a, a, a, f, ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20), None) == ge.ERR_UNSUPPORTED
+    assert run(2, 16, a, None, a, f, a, ctypes.c_void_p(1 << 20), None) == ge.ERR_INVALID_ARG
     # out overlapping the input
-    assert L.ge_add_rmsnorm_run(2, 16, a, a, a, f, a, a, None) == ge.ERR_INVALID_ARG
+    assert run(2, 16, a, a, a, f, a, a, None) == ge.ERR_INVALID_ARG
+    # negative eps
+    assert run(2, 16, a, a, a, ctypes.c_float(-1.0), ctypes.c_void_p(8192), ctypes.c_void_p(1 << 20), None) \
+        == ge.ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

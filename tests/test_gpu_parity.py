@@ -425,6 +425,25 @@ def test_add_rmsnorm_in_place_residual():
     assert_close(ad, rr, TOL_BF16, "resid in place")
 
 
+# the same step unfused (measurement only): add kernel, then the RMSNorm over the stored residual,
+# on both row kernels (one wave per row: aligned rows of at most 4096; a workgroup per row otherwise)
+@pytest.mark.parametrize("M,N,eps", [(4, 100, 1e-6), (16, 4096, 1e-6), (33, 8192, 1e-6), (5, 1000, 1e-6),
+                                     (300000, 8, 1e-6), (6, 4096, 4.0), (6, 8192, 4.0)])
+def test_add_rmsnorm_unfused(M, N, eps):
+    a = workloads.normal((M, N), 1.0, "bf16", wid=103, tid=0, seed=N)
+    x = workloads.normal((M, N), 1.0, "bf16", wid=103, tid=1, seed=N)
+    wt = workloads.normal((N,), 1.0, "bf16", wid=103, tid=2, seed=N)
+    ad, xd, wd = to_dev(a), to_dev(x), to_dev(wt)
+    resid, out = ge.add_rmsnorm_unfused(ad, xd, wd, eps=eps)
+    fresid, _ = ge.add_rmsnorm(ad, xd, wd, eps=eps)
+    rr, ro = oracle.add_rmsnorm(a, x, wt, "bf16", eps=eps)
+    assert torch.equal(resid, fresid), "both paths store bf16(a + x)"
+    assert_close(resid, rr, TOL_BF16, "resid")
+    # the norm is taken over the rounded residual: one more bf16 rounding than the fused kernel,
+    # far inside the tolerance
+    assert_close(out, ro, TOL_BF16, f"normed unfused eps={eps}")
+
+
 # --------------------------------------------------------------------------
 # small-M weight-streaming kernels
 # --------------------------------------------------------------------------
