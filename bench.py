@@ -11,7 +11,8 @@ the launches).  The headline is timed last, right after the other rows: the
 shader clock of a GPU that has just come out of idle settles over the first
 tens of milliseconds of work (at 4096^3: about 120 us per launch for the
 first hundred launches, 102 us from the third hundred on), and the other rows
-are that much work.
+are that much work.  Before the other rows, 400 untimed headline calls settle
+the clock for them as well.
 
 Also reported (same JSON line): the deliberately unfused chain of the same
 workload, the other workloads (tiny fp32, SwiGLU dual GEMM, 16-row decode
@@ -73,8 +74,15 @@ def calibrate_copy():
 # timing
 # --------------------------------------------------------------------------
 
-def time_launches(fn_list, steps, warmup):
+# untimed work each secondary row runs before it is timed, at the least: after a memory-bound row
+# the shader clock takes tens of milliseconds to climb back for an MFMA-bound one (512-row int4:
+# about 97 us per launch over its first 25 launches, 86 us from the 200th on)
+ROW_WARM_MS = 30.0
+
+
+def time_launches(fn_list, steps, warmup, min_warm_ms=0.0):
     """Run fn_list[i % len] for warmup + steps iterations; return the timed region in ms.
+    With min_warm_ms, the untimed calls go on until that much time has passed as well.
 
     The timed calls run back to back between two HIP events recorded on the current stream
     (the one the library launches on), bracketed by device synchronisation.  With no host
@@ -86,6 +94,13 @@ def time_launches(fn_list, steps, warmup):
     for i in range(warmup):
         fn_list[i % n]()
     torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        t_start, i = time.perf_counter(), warmup
+        while (time.perf_counter() - t_start) * 1e3 < min_warm_ms:
+            for _ in range(8):
+                fn_list[i % n]()
+                i += 1
+            torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(s)
@@ -204,14 +219,14 @@ def prepare(name):
     return w, fused, unfused, meta
 
 
-def measure(name, steps, warmup, unfused_chain=True, prepared=None):
+def measure(name, steps, warmup, unfused_chain=True, prepared=None, min_warm_ms=0.0):
     w, fused, unfused, meta = prepared if prepared is not None else prepare(name)
-    fused_ms = time_launches(fused, steps, warmup) / steps
+    fused_ms = time_launches(fused, steps, warmup, min_warm_ms) / steps
     if not unfused_chain:
         return dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
                     flops=meta["flops"], bytes=meta["bytes"], rotations=meta["rotations"], ms_per_call=fused_ms,
                     gbps=meta["bytes"] / (fused_ms * 1e-3) / 1e9, tflops=meta["flops"] / (fused_ms * 1e-3) / 1e12)
-    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
+    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2), min_warm_ms) / max(steps // 2, 5)
     # calls run back to back, so the per-call average is each call's GPU duration
     kern_ms = fused_ms
     r = dict(name=name, kernel=meta["kernel"], M=w.M, N=w.N, K=w.K, bound=meta["bound"],
@@ -230,7 +245,7 @@ def measure(name, steps, warmup, unfused_chain=True, prepared=None):
     return r
 
 
-def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
+def measure_add_rmsnorm(steps, warmup, M=2048, N=4096, min_warm_ms=ROW_WARM_MS):
     """Fused residual add + RMSNorm over M x N bf16 rows (HBM-bound: reads a, x, w; writes the new
     residual and the normalised rows), rotating over enough row sets to defeat the Infinity Cache."""
     import torch
@@ -245,11 +260,11 @@ def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
         sets.append((a, x, torch.empty_like(a), torch.empty_like(a)))
     w = (1 + 0.1 * torch.randn(N, device="cuda", generator=g)).bfloat16()
     calls = [ge.prepare_add_rmsnorm(a, x, w, resid=r, out=o) for a, x, r, o in sets]
-    kern = time_launches(calls, steps, warmup) / steps
+    kern = time_launches(calls, steps, warmup, min_warm_ms) / steps
     # the unfused chain: an add kernel (reads a, x; writes resid), then the RMSNorm kernel (reads
     # resid, w; writes out)
     ucalls = [ge.prepare_add_rmsnorm(a, x, w, resid=r, out=o, unfused=True) for a, x, r, o in sets]
-    unf = time_launches(ucalls, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
+    unf = time_launches(ucalls, max(steps // 2, 5), max(warmup // 2, 2), min_warm_ms) / max(steps // 2, 5)
     byts = set_bytes + N * 2
     ubyts = 5 * M * N * 2 + N * 2
     return {"kernel": "add_rmsnorm", "M": M, "N": N, "bytes": byts, "rotations": nrot,
@@ -258,7 +273,7 @@ def measure_add_rmsnorm(steps, warmup, M=2048, N=4096):
             "unfused_ms": round(unf, 4), "unfused_bytes": ubyts, "speedup_vs_unfused": round(unf / kern, 4)}
 
 
-def measure_rope_qk(steps, warmup):
+def measure_rope_qk(steps, warmup, min_warm_ms=ROW_WARM_MS):
     """Scores of one layer's attention prefill with the rotary embedding applied at Q / K tile load
     (one kernel), against the unfused chain: rope(Q) and rope(K) written to memory, then the plain
     product.  The fp32 scores dominate the bytes; two output buffers defeat the Infinity Cache."""
@@ -278,8 +293,8 @@ def measure_rope_qk(steps, warmup):
     rk = ge.prepare_rope(K, cos, sin, out=k2, pos0=w.k_pos0)
     prods = [ge.prepare_rope_qk(q2, k2, out=o, alpha=inp["alpha"]) for o in outs]
     unfused = [(lambda p=p: (rq(), rk(), p())) for p in prods]
-    fused_ms = time_launches(fused, steps, warmup) / steps
-    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2)) / max(steps // 2, 5)
+    fused_ms = time_launches(fused, steps, warmup, min_warm_ms) / steps
+    unfused_ms = time_launches(unfused, max(steps // 2, 5), max(warmup // 2, 2), min_warm_ms) / max(steps // 2, 5)
     qk = Q.numel() * 2 + K.numel() * 2
     tables = cos.numel() * 4 * 2
     s_bytes = outs[0].numel() * 4
@@ -414,10 +429,15 @@ def main():
     head = prepare("square_bf16")
     others, nxt = {}, {}
     if not a.main_only:
+        # untimed: the headline's own calls for about 40 ms, so that the first rows below are timed on
+        # a settled clock too
+        for i in range(400):
+            head[1][i % len(head[1])]()
+        torch.cuda.synchronize()
         # steps and warmups of the other rows: at least 50 each (they are short calls)
         ks, ws = max(a.steps // 2, 50), max(a.warmup // 2, 50)
         for name in ["tiny_fp32", "swiglu_8b", "skinny_decode", "w4a16_m16", "w4a16_m512"]:
-            r = measure(name, ks, ws)
+            r = measure(name, ks, ws, min_warm_ms=ROW_WARM_MS)
             torch.cuda.empty_cache()
             others[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
                             if k not in ("name",)}
@@ -429,7 +449,7 @@ def main():
         # 8-bit weight formats (unsigned codes with a zero point, OCP fp8 E4M3) on the decode shape
         # and on the W4A16 M=512 shape
         for name in ["w8a16_u8_m16", "w8a16_fp8_m16", "w8a16_u8_m512", "w8a16_fp8_m512"]:
-            r = measure(name, ks, ws)
+            r = measure(name, ks, ws, min_warm_ms=ROW_WARM_MS)
             torch.cuda.empty_cache()
             nxt[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if k != "name"}
     main_r = measure("square_bf16", a.steps, a.warmup, prepared=head)
