@@ -20,7 +20,7 @@ __all__ = [
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
     "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope", "prepare_rope_qk",
-    "prepare_rope", "gemm_epilogue_noalloc",
+    "prepare_rope", "gemm_epilogue_noalloc", "add_rmsnorm_unfused", "prepare_add_rmsnorm",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -369,27 +369,31 @@ def _workspace(p: Plan, device):
     return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
 
 
-def _swiglu_plan(X, Wg, out, stream=None):
+def _swiglu_plan(X, Wg, out, stream=None, prepacked=False):
     M, K = X.shape
     N = Wg.shape[1]
     return plan(KIND_SWIGLU, M, N, K, a_type=BF16, b_type=BF16, d_type=BF16, lda=_ld(X), ldb=_ld(Wg),
-                ldd=_ld(out), stream=stream)
+                ldd=_ld(out), b_prepacked=prepacked, stream=stream)
 
 
-def swiglu(X, Wg, Wu, *, out=None, stream=None):
-    """D = silu(X @ Wg) * (X @ Wu) (fused dual GEMM)."""
+def swiglu(X, Wg, Wu, *, out=None, prepacked=False, stream=None):
+    """D = silu(X @ Wg) * (X @ Wu) (fused dual GEMM).
+
+    ``prepacked``: Wg and Wu were converted by ``b_prepack`` (M <= 32, N % 128 == 0, K % 32 == 0): the
+    two weights stream through the prepacked decode kernel, the gate product's silu kept in fp32 in
+    the plan's scratch and applied in the up product's epilogue."""
     if Wg.stride() != Wu.stride() or Wg.shape != Wu.shape:
         raise ValueError("Wg and Wu must have the same shape and strides")
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
-    p = _swiglu_plan(X, Wg, out, stream)
+    p = _swiglu_plan(X, Wg, out, stream, prepacked)
     _check(lib().gemm_swiglu_run(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream)),
            "gemm_swiglu_run")
     return out
 
 
-def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, stream=None):
+def swiglu_unfused(X, Wg, Wu, *, out=None, workspace=None, prepacked=False, stream=None):
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
-    p = _swiglu_plan(X, Wg, out, stream)
+    p = _swiglu_plan(X, Wg, out, stream, prepacked)
     ws = workspace if workspace is not None else _workspace(p, X.device)
     _check(lib().gemm_swiglu_run_unfused(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _ptr(ws),
                                          _stream(stream)), "gemm_swiglu_run_unfused")
@@ -508,8 +512,8 @@ def prepare_gemm_epilogue(A, B, *, out, bias=None, C=None, R=None, alpha=1.0, be
     return Prepared(lib().gemm_epi_run, "gemm_epi_run", p, ts, args)
 
 
-def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, stream=None) -> Prepared:
-    p = _swiglu_plan(X, Wg, out, stream)
+def prepare_swiglu(X, Wg, Wu, *, out, unfused=False, workspace=None, prepacked=False, stream=None) -> Prepared:
+    p = _swiglu_plan(X, Wg, out, stream, prepacked)
     ts = [X, Wg, Wu, out]
     if unfused:
         ws = workspace if workspace is not None else _workspace(p, X.device)

@@ -78,7 +78,7 @@ bool log_enabled() {
 
 // plan scratch: the 8-bit kernel's split tiles and counters, or the stream-K decode kernel's tiles
 // and counters
-enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_SK = 3, SCRATCH_TILE_SPLIT = 4 };
+enum { SCRATCH_NONE = 0, SCRATCH_SPLIT = 1, SCRATCH_SK = 3, SCRATCH_TILE_SPLIT = 4, SCRATCH_SWIGLU = 5 };
 
 int32_t wfmt_of(const ge_desc &d) {
     return d.b_type == GE_U8 ? WFMT_U8 : d.b_type == GE_FP8E4M3 ? WFMT_FP8 : WFMT_U4;
@@ -162,6 +162,45 @@ const char *fused_name(const Problem &p, int cu_count, bool scratch = true) {
     return general_kernel_name(p, cu_count);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// SwiGLU on prepacked weights (M <= 32): two passes of the prepacked decode kernel.  Pass 1 writes
+// S = silu(X Wg) in fp32 to the front of the plan's scratch; pass 2 computes D = S * (X Wu), the
+// gate applied in its epilogue.  Both run under a generic copy of the plan whose scratch is the
+// rest (the decode kernel's stream-K tiles and counters, when the column blocks leave CUs idle).
+size_t swiglu_gate_bytes(const ge_desc &d) { return align256((size_t)d.M * d.N * 4); }
+
+ge_plan swiglu_pass_plan(const ge_plan *pl) {
+    ge_plan gp = *pl;
+    gp.kind = GE_KIND_GENERIC;
+    gp.d.flags = GE_FLAG_B_PREPACKED;
+    gp.d.b_layout = GE_LAYOUT_KN;
+    const size_t sb = swiglu_gate_bytes(pl->d);
+    const bool sk = pl->scratch && pl->scratch_bytes > sb;
+    gp.scratch = sk ? (char *)pl->scratch + sb : nullptr;
+    gp.scratch_bytes = sk ? pl->scratch_bytes - sb : 0;
+    gp.scratch_use = sk ? SCRATCH_SK : SCRATCH_NONE;
+    return gp;
+}
+
+// the two passes' problems (S: the gate buffer, fp32 [M, N])
+void swiglu_pass_problems(const ge_plan *gp, const void *X, const void *Wg, const void *Wu, float *S, void *D,
+                          Problem &p1, Problem &p2) {
+    const ge_desc &d = gp->d;
+    p1 = make_problem(gp, X, Wg, nullptr, nullptr, nullptr, nullptr, nullptr, S);
+    p1.epi.alpha = 1.0f;
+    p1.epi.flags = 0;
+    p1.epi.act = GE_ACT_SILU;
+    p1.epi.d_type = GE_F32;
+    p1.epi.ldd = d.N;
+    p2 = make_problem(gp, X, Wu, nullptr, nullptr, nullptr, nullptr, nullptr, D);
+    p2.epi.alpha = 1.0f;
+    p2.epi.act = GE_ACT_NONE;
+    p2.epi.flags = EPI_GATE;
+    p2.epi.G = S;
+    p2.epi.ldg = d.N;
+}
+
 ge_status check_device(const ge_plan *pl) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
@@ -206,7 +245,6 @@ ge_status check_epi_ptrs(const ge_plan *pl, const void *C, const void *bias, con
     return GE_OK;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // One non-blocking stream per device, made on first use, for the library's own set-up work
 // (zeroing plan scratch): waiting for it does not wait for the callers' streams.
@@ -313,8 +351,8 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
     if (d.flags & ~(GE_FLAG_BIAS | GE_FLAG_C | GE_FLAG_RESIDUAL | GE_FLAG_NIBBLE_LO_FIRST | GE_FLAG_W4_PREPACKED |
                     GE_FLAG_B_PREPACKED | GE_FLAG_NO_SCRATCH))
         return fail(GE_ERR_INVALID_ARG, "unknown flag bits 0x%x", d.flags);
-    if ((d.flags & GE_FLAG_B_PREPACKED) && kind != GE_KIND_GENERIC)
-        return fail(GE_ERR_INVALID_ARG, "B_PREPACKED applies to generic bf16 plans");
+    if ((d.flags & GE_FLAG_B_PREPACKED) && kind != GE_KIND_GENERIC && kind != GE_KIND_SWIGLU)
+        return fail(GE_ERR_INVALID_ARG, "B_PREPACKED applies to generic and swiglu bf16 plans");
     if (d.b_layout != GE_LAYOUT_KN && d.b_layout != GE_LAYOUT_NK)
         return fail(GE_ERR_INVALID_ARG, "unknown b_layout %d", d.b_layout);
     if (!is_float_type(d.d_type)) return fail(GE_ERR_INVALID_ARG, "d_type must be F32 or BF16");
@@ -355,10 +393,13 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         if (d.a_type != GE_BF16 || d.b_type != GE_BF16 || d.d_type != GE_BF16)
             return fail(GE_ERR_UNSUPPORTED, "swiglu needs bf16 X, W and D");
         if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "swiglu needs KN weights");
-        if (d.act != GE_ACT_NONE || d.flags != 0 || d.alpha != 1.0f)
+        if (d.act != GE_ACT_NONE || (d.flags & ~GE_FLAG_B_PREPACKED) || d.alpha != 1.0f)
             return fail(GE_ERR_UNSUPPORTED, "swiglu takes no extra epilogue");
         pl.ldb = d.ldb ? d.ldb : d.N;
         if (pl.ldb < d.N) return fail(GE_ERR_INVALID_ARG, "ldb < N");
+        if ((d.flags & GE_FLAG_B_PREPACKED) && (d.M > 32 || d.N % 128 || d.K % 32 || pl.ldb != d.N))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked swiglu weights need M <= 32, N %% 128 == 0, K %% 32 == 0 and "
+                                            "dense weights");
     } else if (d.b_type == GE_U8 || d.b_type == GE_FP8E4M3) {
         if (d.a_type != GE_BF16 || d.scale_type != GE_BF16)
             return fail(GE_ERR_UNSUPPORTED, "8-bit weights need bf16 X and bf16 scales");
@@ -443,6 +484,16 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             use = SCRATCH_SK;
             pl.split = slots;
         }
+    } else if (kind == GE_KIND_SWIGLU && (d.flags & GE_FLAG_B_PREPACKED)) {
+        // the gate buffer, then the decode kernel's stream-K scratch when it takes one
+        const ge_plan gp = swiglu_pass_plan(&pl);
+        const Problem q = make_problem(&gp, (const void *)256, (const void *)256, nullptr, nullptr, nullptr, nullptr,
+                                       nullptr, (void *)256);
+        const int slots = bf16_sk_slots(q, pl.cu_count);
+        bytes = (int64_t)swiglu_gate_bytes(d) + (slots > 0 ? bf16_sk_scratch_bytes(q, slots) : 0);
+        use = SCRATCH_SWIGLU;
+        pl.split = slots > 0 ? slots : 1;
+        pl.kernel = slots > 0 ? "skinny_bf16_prepacked_swiglu_sk" : "skinny_bf16_prepacked_swiglu";
     }
     if (bytes > 0 && (d.flags & GE_FLAG_NO_SCRATCH)) {
         // no device memory: the variant of the kernel that needs none
@@ -588,6 +639,18 @@ ge_status gemm_swiglu_run(const ge_plan *pl, const void *X, const void *Wg, cons
         return fail(GE_ERR_INVALID_ARG, "D overlaps an input");
     ge_status st;
     if ((st = check_device(pl))) return st;
+    if (d.flags & GE_FLAG_B_PREPACKED) {
+        if (!pl->scratch || pl->scratch_use != SCRATCH_SWIGLU)
+            return fail(GE_ERR_INVALID_ARG, "prepacked swiglu plan has no gate buffer");
+        const ge_plan gp = swiglu_pass_plan(pl);
+        Problem p1, p2;
+        swiglu_pass_problems(&gp, X, Wg, Wu, (float *)pl->scratch, D, p1, p2);
+        if (!skinny_supported(p1) || !skinny_supported(p2))
+            return fail(GE_ERR_ALIGN, "prepacked swiglu needs 16-byte aligned X, Wg and Wu and an lda that is a multiple of 8");
+        hipError_t e = launch_fused(&gp, p1, (hipStream_t)stream);
+        if (e == hipSuccess) e = launch_fused(&gp, p2, (hipStream_t)stream);
+        return hip_status(e, "gemm_swiglu_run launch (prepacked)");
+    }
     const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_swiglu_run launch");
 }

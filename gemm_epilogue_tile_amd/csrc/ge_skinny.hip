@@ -66,7 +66,8 @@ __device__ __forceinline__ bool epi_vec_ok(const Problem &p) {
     return ((p.N & 7) == 0) && (((uintptr_t)e.D & 15) == 0) && ((e.ldd & 7) == 0) &&
            (!(e.flags & GE_FLAG_RESIDUAL) || ((((uintptr_t)e.R & 15) == 0) && ((e.ldr & 7) == 0))) &&
            (!(e.flags & GE_FLAG_C) || ((((uintptr_t)e.C & 15) == 0) && ((e.ldc & 7) == 0))) &&
-           (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) && e.d_type == GE_BF16 &&
+           (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) &&
+           (!(e.flags & EPI_GATE) || ((((uintptr_t)e.G & 15) == 0) && ((e.ldg & 7) == 0))) &&
            (!(e.flags & GE_FLAG_RESIDUAL) || e.r_type == GE_BF16) && (!(e.flags & GE_FLAG_C) || e.c_type == GE_BF16) &&
            (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
 }

@@ -98,7 +98,7 @@ typedef int32_t ge_status;
 #define GE_FLAG_RESIDUAL 4u        /* add R after the activation */
 #define GE_FLAG_NIBBLE_LO_FIRST 8u /* W4: low nibble is the even column */
 #define GE_FLAG_W4_PREPACKED 16u   /* W4: Wq is in the layout gemm_w4_prepack writes */
-#define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16, M <= 32: B is in the layout gemm_b_prepack writes */
+#define GE_FLAG_B_PREPACKED 32u    /* GENERIC bf16 or SWIGLU, M <= 32: B (Wg, Wu) in the layout gemm_b_prepack writes */
 
 /* rope flags (ge_rope_qk_run, ge_rope_run) */
 #define GE_ROPE_INTERLEAVED 1 /* pair i is (2i, 2i + 1); else (i, i + D/2), rotate-half */
@@ -225,6 +225,15 @@ GE_API ge_status gemm_epi_run_noalloc(const ge_plan *plan, const void *A, const 
  * Fused SwiGLU dual GEMM:  D = silu(X.Wg) * (X.Wu).  X is [M, K]; Wg and Wu
  * are [K, N] with the plan's ldb.  Each X tile is read once and feeds both
  * products (page "Fusion Thinking", Pattern 2, Level 2).
+ *
+ * A SwiGLU plan made with GE_FLAG_B_PREPACKED (M <= 32, N % 128 == 0,
+ * K % 32 == 0, dense weights) takes Wg and Wu each converted by
+ * gemm_b_prepack, and streams them through the prepacked decode kernel in
+ * two passes: silu(X.Wg) is kept in fp32 in the plan's device scratch
+ * (M * N * 4 bytes, plus the decode kernel's split tiles when the column
+ * blocks leave CUs idle) and multiplied in the epilogue of X.Wu.  The plan
+ * owns that scratch, so calls on one plan must not overlap in time; X, Wg
+ * and Wu must be 16-byte aligned (GE_ERR_ALIGN otherwise).
  */
 GE_API ge_status gemm_swiglu_run(const ge_plan *plan, const void *X, const void *Wg, const void *Wu,
                           void *D, void *stream);

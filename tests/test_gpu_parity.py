@@ -103,6 +103,40 @@ def test_swiglu_few_rows_on_the_tile_kernel(M, N, K):
     assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
 
 
+# SwiGLU at decode sizes on prepacked weights: silu(X Wg) through the prepacked decode kernel into
+# the plan's fp32 scratch, then X Wu with that gate in its epilogue (stream-K at M <= 16 when the
+# column blocks leave CUs idle, the plain prepacked kernel otherwise)
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (16, 14336, 4096), (5, 1024, 256), (32, 2048, 512),
+                                   (17, 384, 96)])
+def test_swiglu_prepacked_decode(M, N, K):
+    w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
+    inp = workloads.make_inputs(w, seed=M + N + K)
+    d = dev_inputs(inp)
+    pl = ge.plan(ge.KIND_SWIGLU, M, N, K, b_prepacked=True)
+    assert pl.kernel.startswith("skinny_bf16_prepacked_swiglu"), pl.kernel
+    assert pl.scratch_bytes >= M * N * 4
+    Wgp, Wup = ge.b_prepack(d["Wg"]), ge.b_prepack(d["Wu"])
+    out = ge.swiglu(d["X"], Wgp, Wup, prepacked=True)
+    ref = oracle.reference(inp)
+    assert_close(out, ref, TOL_BF16, f"swiglu prepacked {M}x{N}x{K} ({pl.kernel})")
+    again = ge.swiglu(d["X"], Wgp, Wup, prepacked=True)
+    assert torch.equal(out, again), "repeat calls must agree bitwise"
+    # the unfused chain reads the same prepacked weights through the prepacked decode kernel
+    assert_close(ge.swiglu_unfused(d["X"], Wgp, Wup, prepacked=True), ref, TOL_BF16, "swiglu prepacked unfused")
+
+
+def test_swiglu_prepacked_refusals():
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.plan(ge.KIND_SWIGLU, 33, 1024, 256, b_prepacked=True)
+    assert e.value.status == ge.ERR_UNSUPPORTED
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.plan(ge.KIND_SWIGLU, 16, 1000, 256, b_prepacked=True)
+    assert e.value.status == ge.ERR_UNSUPPORTED
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.plan(ge.KIND_SWIGLU, 16, 1024, 256, b_prepacked=True, ldb=1152)
+    assert e.value.status == ge.ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (100, 72, 200), (512, 512, 1024)])
 def test_nk_layout(M, N, K):
     w = SQ.with_shape(M=M, N=N, K=K)
