@@ -20,7 +20,7 @@ __all__ = [
     "gemm_epilogue_unfused", "swiglu_unfused", "w4_gemm_unfused", "w4_dequant", "add_rmsnorm",
     "F32", "BF16", "U4X2", "ACTS", "Prepared", "prepare_gemm_epilogue", "prepare_swiglu", "prepare_w4_gemm",
     "w4_prepack", "b_prepack", "U8", "FP8E4M3", "WEIGHT_FORMATS", "rope_qk", "rope", "prepare_rope_qk",
-    "prepare_rope", "gemm_epilogue_noalloc", "add_rmsnorm_unfused", "prepare_add_rmsnorm",
+    "prepare_rope", "gemm_epilogue_noalloc", "add_rmsnorm_unfused", "prepare_add_rmsnorm", "swiglu_prepack",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -379,9 +379,10 @@ def _swiglu_plan(X, Wg, out, stream=None, prepacked=False):
 def swiglu(X, Wg, Wu, *, out=None, prepacked=False, stream=None):
     """D = silu(X @ Wg) * (X @ Wu) (fused dual GEMM).
 
-    ``prepacked``: Wg and Wu were converted by ``b_prepack`` (M <= 32, N % 128 == 0, K % 32 == 0): the
-    two weights stream through the prepacked decode kernel, the gate product's silu kept in fp32 in
-    the plan's scratch and applied in the up product's epilogue."""
+    ``prepacked``: Wg and Wu were converted by ``swiglu_prepack`` (M <= 32, N % 128 == 0, K % 32 == 0):
+    each column block of the gate and of the up weight streams on a workgroup of its own through the
+    prepacked decode loop, and the second of the two to finish combines silu(gate) * up for the
+    block (fp32 tiles in the plan's scratch)."""
     if Wg.stride() != Wu.stride() or Wg.shape != Wu.shape:
         raise ValueError("Wg and Wu must have the same shape and strides")
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
@@ -567,6 +568,23 @@ def b_prepack(B, *, out=None, stream=None):
     p = plan(KIND_GENERIC, 1, N, K, a_type=BF16, b_type=BF16, d_type=BF16, ldb=_ld(B))
     _check(lib().gemm_b_prepack(p.handle, _ptr(B), _ptr(out), _stream(stream)), "gemm_b_prepack")
     return out
+
+
+def swiglu_prepack(Wg, Wu, *, stream=None):
+    """SwiGLU weights [K, N] (bf16) -> the prepacked layout ``swiglu(..., prepacked=True)`` reads
+    (one-time): the decode layout of ``b_prepack`` with the column-block width chosen so that the
+    gate and up blocks, one workgroup each, fill the GPU."""
+    torch = _torch()
+    if Wg.shape != Wu.shape:
+        raise ValueError("Wg and Wu must have the same shape")
+    K, N = Wg.shape
+    outs = []
+    for W in (Wg, Wu):
+        out = torch.empty((K, N), dtype=torch.bfloat16, device=W.device)
+        p = plan(KIND_SWIGLU, 1, N, K, a_type=BF16, b_type=BF16, d_type=BF16, ldb=_ld(W))
+        _check(lib().gemm_b_prepack(p.handle, _ptr(W), _ptr(out), _stream(stream)), "gemm_b_prepack")
+        outs.append(out)
+    return tuple(outs)
 
 
 def _rope_flags(interleaved, exact):

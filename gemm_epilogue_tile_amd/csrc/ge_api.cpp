@@ -122,7 +122,7 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     e.act = pl->kind == GE_KIND_SWIGLU ? GE_ACT_NONE : d.act;
     uint32_t f = 0;
     p.w4_packed = (pl->kind == GE_KIND_W4 && (d.flags & GE_FLAG_W4_PREPACKED)) ? 1 : 0;
-    p.b_packed = (pl->kind == GE_KIND_GENERIC && (d.flags & GE_FLAG_B_PREPACKED)) ? 1 : 0;
+    p.b_packed = ((pl->kind == GE_KIND_GENERIC || pl->kind == GE_KIND_SWIGLU) && (d.flags & GE_FLAG_B_PREPACKED)) ? 1 : 0;
     p.wfmt = wfmt_of(d);
     // scratch goes only to the kernel it was made for (unfused chains run copies of a plan
     // with another kind)
@@ -130,6 +130,13 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     const bool split_use = pl->scratch_use == SCRATCH_SPLIT && p.mode == MODE_W4;
     const bool tsplit_use = pl->scratch_use == SCRATCH_TILE_SPLIT && p.mode == MODE_W4;
     const bool sk_use = pl->scratch_use == SCRATCH_SK && p.mode == MODE_GENERIC;
+    if (pl->scratch && pl->scratch_use == SCRATCH_SWIGLU && p.mode == MODE_SWIGLU) {
+        // the gate / up tile pairs of the prepacked SwiGLU kernel, then one counter per column block
+        const int64_t ncb = d.N / (16 * swiglu_block_tiles(d.N, pl->cu_count));
+        p.split = 2;
+        p.split_ws = (float *)pl->scratch;
+        p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - ncb * 4);
+    }
     if (pl->scratch && (split_use || tsplit_use || sk_use)) {
         p.split = pl->split;
         p.split_ws = (float *)pl->scratch;
@@ -163,43 +170,6 @@ const char *fused_name(const Problem &p, int cu_count, bool scratch = true) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// SwiGLU on prepacked weights (M <= 32): two passes of the prepacked decode kernel.  Pass 1 writes
-// S = silu(X Wg) in fp32 to the front of the plan's scratch; pass 2 computes D = S * (X Wu), the
-// gate applied in its epilogue.  Both run under a generic copy of the plan whose scratch is the
-// rest (the decode kernel's stream-K tiles and counters, when the column blocks leave CUs idle).
-size_t swiglu_gate_bytes(const ge_desc &d) { return align256((size_t)d.M * d.N * 4); }
-
-ge_plan swiglu_pass_plan(const ge_plan *pl) {
-    ge_plan gp = *pl;
-    gp.kind = GE_KIND_GENERIC;
-    gp.d.flags = GE_FLAG_B_PREPACKED;
-    gp.d.b_layout = GE_LAYOUT_KN;
-    const size_t sb = swiglu_gate_bytes(pl->d);
-    const bool sk = pl->scratch && pl->scratch_bytes > sb;
-    gp.scratch = sk ? (char *)pl->scratch + sb : nullptr;
-    gp.scratch_bytes = sk ? pl->scratch_bytes - sb : 0;
-    gp.scratch_use = sk ? SCRATCH_SK : SCRATCH_NONE;
-    return gp;
-}
-
-// the two passes' problems (S: the gate buffer, fp32 [M, N])
-void swiglu_pass_problems(const ge_plan *gp, const void *X, const void *Wg, const void *Wu, float *S, void *D,
-                          Problem &p1, Problem &p2) {
-    const ge_desc &d = gp->d;
-    p1 = make_problem(gp, X, Wg, nullptr, nullptr, nullptr, nullptr, nullptr, S);
-    p1.epi.alpha = 1.0f;
-    p1.epi.flags = 0;
-    p1.epi.act = GE_ACT_SILU;
-    p1.epi.d_type = GE_F32;
-    p1.epi.ldd = d.N;
-    p2 = make_problem(gp, X, Wu, nullptr, nullptr, nullptr, nullptr, nullptr, D);
-    p2.epi.alpha = 1.0f;
-    p2.epi.act = GE_ACT_NONE;
-    p2.epi.flags = EPI_GATE;
-    p2.epi.G = S;
-    p2.epi.ldg = d.N;
-}
 
 ge_status check_device(const ge_plan *pl) {
     int dev = -1;
@@ -485,15 +455,10 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
             pl.split = slots;
         }
     } else if (kind == GE_KIND_SWIGLU && (d.flags & GE_FLAG_B_PREPACKED)) {
-        // the gate buffer, then the decode kernel's stream-K scratch when it takes one
-        const ge_plan gp = swiglu_pass_plan(&pl);
-        const Problem q = make_problem(&gp, (const void *)256, (const void *)256, nullptr, nullptr, nullptr, nullptr,
-                                       nullptr, (void *)256);
-        const int slots = bf16_sk_slots(q, pl.cu_count);
-        bytes = (int64_t)swiglu_gate_bytes(d) + (slots > 0 ? bf16_sk_scratch_bytes(q, slots) : 0);
+        bytes = swiglu_prepacked_scratch_bytes(d.M, d.N, pl.cu_count);
         use = SCRATCH_SWIGLU;
-        pl.split = slots > 0 ? slots : 1;
-        pl.kernel = slots > 0 ? "skinny_bf16_prepacked_swiglu_sk" : "skinny_bf16_prepacked_swiglu";
+        pl.split = 2;
+        pl.kernel = swiglu_prepacked_name(d.N, pl.cu_count);
     }
     if (bytes > 0 && (d.flags & GE_FLAG_NO_SCRATCH)) {
         // no device memory: the variant of the kernel that needs none
@@ -641,15 +606,13 @@ ge_status gemm_swiglu_run(const ge_plan *pl, const void *X, const void *Wg, cons
     if ((st = check_device(pl))) return st;
     if (d.flags & GE_FLAG_B_PREPACKED) {
         if (!pl->scratch || pl->scratch_use != SCRATCH_SWIGLU)
-            return fail(GE_ERR_INVALID_ARG, "prepacked swiglu plan has no gate buffer");
-        const ge_plan gp = swiglu_pass_plan(pl);
-        Problem p1, p2;
-        swiglu_pass_problems(&gp, X, Wg, Wu, (float *)pl->scratch, D, p1, p2);
-        if (!skinny_supported(p1) || !skinny_supported(p2))
+            return fail(GE_ERR_INVALID_ARG, "prepacked swiglu plan has no scratch");
+        if (((uintptr_t)X & 15) || (pl->lda & 7) || ((uintptr_t)Wg & 15) || ((uintptr_t)Wu & 15))
             return fail(GE_ERR_ALIGN, "prepacked swiglu needs 16-byte aligned X, Wg and Wu and an lda that is a multiple of 8");
-        hipError_t e = launch_fused(&gp, p1, (hipStream_t)stream);
-        if (e == hipSuccess) e = launch_fused(&gp, p2, (hipStream_t)stream);
-        return hip_status(e, "gemm_swiglu_run launch (prepacked)");
+        if (nX >= (1ull << 31) || (int64_t)d.K * 256 >= (1ll << 31))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked swiglu addresses X and each weight block with 32-bit offsets");
+        const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
+        return hip_status(launch_swiglu_prepacked(p, pl->cu_count, (hipStream_t)stream), "gemm_swiglu_run launch (prepacked)");
     }
     const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_swiglu_run launch");
@@ -793,6 +756,8 @@ ge_status gemm_swiglu_run_unfused(const ge_plan *pl, const void *X, const void *
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
     if (pl->kind != GE_KIND_SWIGLU) return fail(GE_ERR_INVALID_ARG, "plan is not a swiglu plan");
     if (!X || !Wg || !Wu || !D) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
+    if (pl->d.flags & GE_FLAG_B_PREPACKED)
+        return fail(GE_ERR_UNSUPPORTED, "the unfused swiglu chain reads the raw [K, N] weights");
     ge_status st;
     if ((st = check_ws(pl, ws)) || (st = check_device(pl))) return st;
     const ge_desc &d = pl->d;
@@ -886,7 +851,8 @@ ge_status gemm_w4_prepack(const ge_plan *pl, const uint8_t *Wq, uint8_t *Wp, voi
 
 ge_status gemm_b_prepack(const ge_plan *pl, const void *B, void *Bp, void *stream) {
     if (!pl) return fail(GE_ERR_INVALID_ARG, "plan is NULL");
-    if (pl->kind != GE_KIND_GENERIC) return fail(GE_ERR_INVALID_ARG, "plan is not a generic plan");
+    if (pl->kind != GE_KIND_GENERIC && pl->kind != GE_KIND_SWIGLU)
+        return fail(GE_ERR_INVALID_ARG, "plan is not a generic or swiglu plan");
     if (!B || !Bp) return fail(GE_ERR_INVALID_ARG, "NULL pointer");
     const ge_desc &d = pl->d;
     if (d.b_type != GE_BF16 || d.b_layout != GE_LAYOUT_KN)
@@ -898,7 +864,8 @@ ge_status gemm_b_prepack(const ge_plan *pl, const void *B, void *Bp, void *strea
     ge_status st;
     if ((st = check_device(pl))) return st;
     return hip_status(
-        launch_b_prepack(d.K, d.N, (const uint16_t *)B, pl->ldb, (uint16_t *)Bp, pl->cu_count, (hipStream_t)stream),
+        launch_b_prepack(d.K, d.N, (const uint16_t *)B, pl->ldb, (uint16_t *)Bp, pl->cu_count, (hipStream_t)stream,
+                         pl->kind == GE_KIND_SWIGLU ? swiglu_block_tiles(d.N, pl->cu_count) : 0),
         "gemm_b_prepack");
 }
 

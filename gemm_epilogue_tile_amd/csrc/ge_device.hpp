@@ -112,15 +112,11 @@ struct EpiArgs {
     const void *bias;
     const void *R;
     void *D;
-    const float *G;  // EPI_GATE: fp32 [M, N] gate, row stride ldg
-    int64_t ldc, ldr, ldd, ldg;
+    int64_t ldc, ldr, ldd;
     int32_t c_type, bias_type, r_type, d_type;
     int32_t act;
-    uint32_t flags;  // GE_FLAG_BIAS / GE_FLAG_C (only when beta != 0) / GE_FLAG_RESIDUAL / EPI_GATE
+    uint32_t flags;  // GE_FLAG_BIAS / GE_FLAG_C (only when beta != 0) / GE_FLAG_RESIDUAL
 };
-// internal epilogue term of the streaming (decode) kernels: the result is multiplied by G[m][n]
-// (the second pass of SwiGLU on prepacked weights: G = silu(x Wg) from the first pass)
-constexpr uint32_t EPI_GATE = 1u << 16;
 
 __device__ __forceinline__ float load_elem(const void *p, int32_t type, int64_t i) {
     return type == GE_BF16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
@@ -141,7 +137,6 @@ __device__ __forceinline__ float epi_scalar(const EpiArgs &e, float acc, int64_t
     if (e.flags & GE_FLAG_BIAS) t += load_elem(e.bias, e.bias_type, n);
     float u = activate<ACT>(t);
     if (e.flags & GE_FLAG_RESIDUAL) u += load_elem(e.R, e.r_type, m * e.ldr + n);
-    if (e.flags & EPI_GATE) u *= e.G[m * e.ldg + n];
     return u;
 }
 
@@ -210,12 +205,6 @@ __device__ __forceinline__ void epi_row8(const EpiArgs &e, const float acc[8], i
         load8(e.R, e.r_type, m * e.ldr + n, r);
 #pragma unroll
         for (int i = 0; i < 8; ++i) t[i] += r[i];
-    }
-    if (e.flags & EPI_GATE) {
-        float g[8];
-        load8(e.G, GE_F32, m * e.ldg + n, g);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] *= g[i];
     }
     store8(e.D, e.d_type, m * e.ldd + n, t);
 }

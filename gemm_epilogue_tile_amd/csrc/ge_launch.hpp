@@ -82,7 +82,14 @@ hipError_t launch_w8_prepack(int32_t K, int32_t N, const uint8_t *Wq, int64_t ld
 
 // One-time conversion of raw [K, N] bf16 weights to the prepacked decode layout.
 hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, int cu_count,
-                            hipStream_t s);
+                            hipStream_t s, int tb_override = 0);
+// SwiGLU on prepacked weights (M <= 32): gate and up column blocks on workgroup pairs; the block
+// width (the layout gemm_b_prepack writes for a SwiGLU plan), the plan scratch (the pairs' fp32
+// tiles, then one counter per block) and the kernel's name
+int swiglu_block_tiles(int N, int cu_count);
+int64_t swiglu_prepacked_scratch_bytes(int M, int N, int cu_count);
+const char *swiglu_prepacked_name(int N, int cu_count);
+hipError_t launch_swiglu_prepacked(const Problem &p, int cu_count, hipStream_t s);
 // 16-column tiles per block of the prepacked bf16 layout (7 or 8), a function of N and the CU count
 int bf16p_block_tiles(int N, int cu_count);
 

@@ -66,8 +66,7 @@ __device__ __forceinline__ bool epi_vec_ok(const Problem &p) {
     return ((p.N & 7) == 0) && (((uintptr_t)e.D & 15) == 0) && ((e.ldd & 7) == 0) &&
            (!(e.flags & GE_FLAG_RESIDUAL) || ((((uintptr_t)e.R & 15) == 0) && ((e.ldr & 7) == 0))) &&
            (!(e.flags & GE_FLAG_C) || ((((uintptr_t)e.C & 15) == 0) && ((e.ldc & 7) == 0))) &&
-           (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) &&
-           (!(e.flags & EPI_GATE) || ((((uintptr_t)e.G & 15) == 0) && ((e.ldg & 7) == 0))) &&
+           (!(e.flags & GE_FLAG_BIAS) || (((uintptr_t)e.bias & 15) == 0)) && e.d_type == GE_BF16 &&
            (!(e.flags & GE_FLAG_RESIDUAL) || e.r_type == GE_BF16) && (!(e.flags & GE_FLAG_C) || e.c_type == GE_BF16) &&
            (!(e.flags & GE_FLAG_BIAS) || e.bias_type == GE_BF16);
 }
@@ -629,9 +628,12 @@ __global__ __launch_bounds__(W4_THREADS) void skinny_w4_kernel(Problem p) {
 // counter increment follows the barrier, and the last workgroup's tile loads
 // are issued only after the increment has returned (barrier and LDS flag in
 // between).
-template <int MR, int NC, int NS, int NWV = S_WAVES>
+// SWI (NS = 2): the two tiles are the gate and the up product of one column block, combined as
+// silu(gate) * up instead of summed
+template <int MR, int NC, int NS, int NWV = S_WAVES, bool SWI = false>
 __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const float *red, int n0, int cb, int ks,
                                                       int ncb, int *s_last) {
+    static_assert(!SWI || NS == 2, "gate and up");
     constexpr int CH = NC / 8;
     constexpr int SC1 = 16;  // cache policy operand: device scope
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.split_ws, (int64_t)NS * ncb * MR * NC * 4);
@@ -674,17 +676,49 @@ __device__ __forceinline__ void split_reduce_epilogue(const Problem &p, const fl
                 tl[q][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16, 0, SC1));
             }
             float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < NS; ++q)
+            if constexpr (SWI) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    v[e] += tl[q][0][e];
-                    v[4 + e] += tl[q][1][e];
+                    v[e] = activate<GE_ACT_SILU>(tl[0][0][e]) * tl[1][0][e];
+                    v[4 + e] = activate<GE_ACT_SILU>(tl[0][1][e]) * tl[1][1][e];
                 }
+            } else {
+#pragma unroll
+                for (int q = 0; q < NS; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] += tl[q][0][e];
+                        v[4 + e] += tl[q][1][e];
+                    }
+            }
             finish_chunk<ACT>(p, vec_ok, m, n, v);
         }
     });
     if (threadIdx.x == 0) __hip_atomic_store(p.split_cnt + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// SwiGLU on prepacked weights, M <= 32: workgroup 2 cb + h streams column block cb of W_gate
+// (h = 0) or of W_up (h = 1, p.B2) through the prepacked decode loop; of the two, the one that
+// arrives second combines silu(gate) * up into the block's output (page "Fusion Thinking",
+// Pattern 2: the dual product's epilogue; here the two products of a block run on two CUs side by
+// side, so that the 2 N / NC workgroups fill the GPU at decode sizes)
+template <int MT, int TB>
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16p_swiglu_kernel(Problem p) {
+    constexpr int NC = 16 * TB, MR = 16 * MT;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    __shared__ int s_last;
+    const int h = blockIdx.x & 1, cb = blockIdx.x >> 1, ncb = gridDim.x >> 1;
+    Problem q = p;
+    if (h) q.B = p.B2;
+    f32x4 acc[MT][TB];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16p<MT, TB>(q, cb, 0, p.K / 32, acc);
+    accp_to_lds<MT, TB>(red, acc);
+    __syncthreads();
+    split_reduce_epilogue<MR, NC, 2, S_WAVES, true>(p, red, cb * NC, cb, h, ncb, &s_last);
 }
 
 #ifndef GE_W4S_RING
@@ -1034,9 +1068,46 @@ int bf16p_block_tiles(int N, int cu_count) {
     return even112 && !even128 ? 7 : 8;
 }
 
+// SwiGLU pairs on prepacked weights: the block width that makes the 2 N / (16 TB) workgroups fill
+// the CUs (112-column blocks only where N is a multiple of 112)
+int swiglu_block_tiles(int N, int cu_count) {
+    if (cu_count <= 0 || N % 112) return 8;
+    const bool even112 = (2 * (N / 112)) % cu_count == 0, even128 = N % 128 == 0 && (2 * (N / 128)) % cu_count == 0;
+    return even112 && !even128 ? 7 : 8;
+}
+
+int64_t swiglu_prepacked_scratch_bytes(int M, int N, int cu_count) {
+    const int tb = swiglu_block_tiles(N, cu_count);
+    const int64_t ncb = N / (16 * tb), mr = M <= 16 ? 16 : 32;
+    return 2 * ncb * mr * 16 * tb * 4 + ncb * 4;
+}
+
+const char *swiglu_prepacked_name(int N, int cu_count) {
+    return swiglu_block_tiles(N, cu_count) == 7 ? "skinny_bf16p_swiglu_112col_pairs" : "skinny_bf16p_swiglu_128col_pairs";
+}
+
+// p: mode SWIGLU, B / B2 the prepacked gate and up weights, split_ws / split_cnt the plan's scratch
+hipError_t launch_swiglu_prepacked(const Problem &p, int cu_count, hipStream_t s) {
+    if (!p.split_ws || !p.split_cnt || p.M > 32) return hipErrorInvalidValue;
+    const int tb = swiglu_block_tiles(p.N, cu_count);
+    const dim3 grid(2 * (p.N / (16 * tb)));
+    if (tb == 7) {
+        if (p.M <= 16)
+            hipLaunchKernelGGL((skinny_bf16p_swiglu_kernel<1, 7>), grid, dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_bf16p_swiglu_kernel<2, 7>), grid, dim3(S_THREADS), 0, s, p);
+    } else {
+        if (p.M <= 16)
+            hipLaunchKernelGGL((skinny_bf16p_swiglu_kernel<1, 8>), grid, dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_bf16p_swiglu_kernel<2, 8>), grid, dim3(S_THREADS), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_b_prepack(int32_t K, int32_t N, const uint16_t *B, int64_t ldb, uint16_t *Bp, int cu_count,
-                            hipStream_t s) {
-    const int tb = bf16p_block_tiles(N, cu_count);
+                            hipStream_t s, int tb_override) {
+    const int tb = tb_override ? tb_override : bf16p_block_tiles(N, cu_count);
     const int64_t total = (int64_t)(N / (16 * tb)) * (K / 32) * 64 * tb;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;

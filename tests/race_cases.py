@@ -35,10 +35,13 @@ def run_cases(ge, torch):
         return ge.w4_gemm(to_dev(inp["X"]), torch.from_numpy(inp["Wq"]).to(dev), to_dev(inp["scales"]),
                           bias=to_dev(inp["bias"]), zero_point=inp["zero_point"], fmt=fmt)
 
-    def swiglu(M, N, K, seed):
+    def swiglu(M, N, K, seed, prepacked=False):
         w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
         inp = workloads.make_inputs(w, seed=seed)
-        return ge.swiglu(to_dev(inp["X"]), to_dev(inp["Wg"]), to_dev(inp["Wu"]))
+        Wg, Wu = to_dev(inp["Wg"]), to_dev(inp["Wu"])
+        if prepacked:
+            Wg, Wu = ge.swiglu_prepack(Wg, Wu)
+        return ge.swiglu(to_dev(inp["X"]), Wg, Wu, prepacked=prepacked)
 
     out = {
         "tile_128": gemm("tile_128", 512, 768, 1024, 1),
@@ -52,6 +55,7 @@ def run_cases(ge, torch):
         "w8_u8_split": w8("u8", 16, 4096, 4096, 8),
         "w8_u8_tile": w8("u8", 128, 1024, 1024, 9),
         "w8_fp8_tile": w8("fp8", 128, 1024, 1024, 10),
+        "swiglu_prepacked_pairs": swiglu(16, 14336, 512, 12, prepacked=True),  # gate / up block pairs
     }
     torch.cuda.synchronize()
     return {k: v.view(torch.int16).cpu().numpy() for k, v in out.items()}

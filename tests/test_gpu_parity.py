@@ -103,37 +103,36 @@ def test_swiglu_few_rows_on_the_tile_kernel(M, N, K):
     assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
 
 
-# SwiGLU at decode sizes on prepacked weights: silu(X Wg) through the prepacked decode kernel into
-# the plan's fp32 scratch, then X Wu with that gate in its epilogue (stream-K at M <= 16 when the
-# column blocks leave CUs idle, the plain prepacked kernel otherwise)
-@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (16, 14336, 4096), (5, 1024, 256), (32, 2048, 512),
-                                   (17, 384, 96)])
-def test_swiglu_prepacked_decode(M, N, K):
+# SwiGLU at decode sizes on prepacked weights: each column block of W_gate and of W_up streams on a
+# workgroup of its own through the prepacked decode loop; the second of a pair to finish combines
+# silu(gate) * up (112-column blocks where 2 N / 112 fills the CUs, 128 otherwise)
+@pytest.mark.parametrize("M,N,K,cols", [(1, 14336, 4096, 112), (16, 14336, 4096, 112), (5, 1024, 256, 128),
+                                        (32, 2048, 512, 128), (17, 384, 96, 128), (16, 28672, 128, 112)])
+def test_swiglu_prepacked_decode(M, N, K, cols):
     w = workloads.WORKLOADS["swiglu_8b"].with_shape(M=M, N=N, K=K)
     inp = workloads.make_inputs(w, seed=M + N + K)
     d = dev_inputs(inp)
     pl = ge.plan(ge.KIND_SWIGLU, M, N, K, b_prepacked=True)
-    assert pl.kernel.startswith("skinny_bf16_prepacked_swiglu"), pl.kernel
-    assert pl.scratch_bytes >= M * N * 4
-    Wgp, Wup = ge.b_prepack(d["Wg"]), ge.b_prepack(d["Wu"])
+    assert pl.kernel == f"skinny_bf16p_swiglu_{cols}col_pairs", pl.kernel
+    ncb = N // cols
+    assert pl.scratch_bytes == 2 * ncb * (16 if M <= 16 else 32) * cols * 4 + ncb * 4
+    Wgp, Wup = ge.swiglu_prepack(d["Wg"], d["Wu"])
     out = ge.swiglu(d["X"], Wgp, Wup, prepacked=True)
-    ref = oracle.reference(inp)
-    assert_close(out, ref, TOL_BF16, f"swiglu prepacked {M}x{N}x{K} ({pl.kernel})")
+    assert_close(out, oracle.reference(inp), TOL_BF16, f"swiglu prepacked {M}x{N}x{K} ({pl.kernel})")
     again = ge.swiglu(d["X"], Wgp, Wup, prepacked=True)
     assert torch.equal(out, again), "repeat calls must agree bitwise"
-    # the unfused chain reads the same prepacked weights through the prepacked decode kernel
-    assert_close(ge.swiglu_unfused(d["X"], Wgp, Wup, prepacked=True), ref, TOL_BF16, "swiglu prepacked unfused")
 
 
 def test_swiglu_prepacked_refusals():
+    for M, N, ldb in [(33, 1024, 0), (16, 1000, 0), (16, 1024, 1152)]:
+        with pytest.raises(ge.GemmEpiError) as e:
+            ge.plan(ge.KIND_SWIGLU, M, N, 256, b_prepacked=True, ldb=ldb)
+        assert e.value.status == ge.ERR_UNSUPPORTED, (M, N, ldb)
+    # the unfused chain reads raw weights
+    X = torch.zeros(4, 256, dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros(256, 1024, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ge.GemmEpiError) as e:
-        ge.plan(ge.KIND_SWIGLU, 33, 1024, 256, b_prepacked=True)
-    assert e.value.status == ge.ERR_UNSUPPORTED
-    with pytest.raises(ge.GemmEpiError) as e:
-        ge.plan(ge.KIND_SWIGLU, 16, 1000, 256, b_prepacked=True)
-    assert e.value.status == ge.ERR_UNSUPPORTED
-    with pytest.raises(ge.GemmEpiError) as e:
-        ge.plan(ge.KIND_SWIGLU, 16, 1024, 256, b_prepacked=True, ldb=1152)
+        ge.swiglu_unfused(X, W, W, prepacked=True)
     assert e.value.status == ge.ERR_UNSUPPORTED
 
 
