@@ -83,16 +83,18 @@ def _scratch_inputs(seed):
     x8 = torch.randn(16, 4096, generator=g).bfloat16()
     x4 = torch.randn(256, 1024, generator=g).bfloat16()
     xs = torch.randn(512, 256, generator=g).bfloat16()
-    return [t.to(DEV) for t in (x8, x4, xs)]
+    xw = torch.randn(16, 512, generator=g).bfloat16()
+    return [t.to(DEV) for t in (x8, x4, xs, xw)]
 
 
 def test_scratch_using_calls_replay_in_a_graph():
     # calls whose plans own device scratch (the 8-bit K split: tile handoff, counters that re-arm
     # themselves; the stream-K decode kernel), the int4 tile kernel (per-group partial products and
-    # the correction product through LDS) and the SwiGLU launch whose partial last round is peeled
-    # into 128 x 128 tiles
+    # the correction product through LDS), the SwiGLU launch whose partial last round is peeled
+    # into 128 x 128 tiles, and SwiGLU on prepacked weights (gate / up workgroup pairs, per-block
+    # counters that re-arm themselves)
     g = torch.Generator().manual_seed(9)
-    x8, x4, xs = _scratch_inputs(2)
+    x8, x4, xs, xw = _scratch_inputs(2)
     Wq8 = torch.randint(0, 256, (4096, 4096), generator=g, dtype=torch.uint8).to(DEV)
     s8 = torch.full((32, 4096), 0.001).bfloat16().to(DEV)
     Wq4 = torch.randint(0, 256, (1024, 512), generator=g, dtype=torch.uint8).to(DEV)
@@ -104,18 +106,23 @@ def test_scratch_using_calls_replay_in_a_graph():
     xd = (torch.randn(16, 2048, generator=g)).bfloat16().to(DEV)
     Wd = (torch.randn(2048, 4096, generator=g) / 16).bfloat16().to(DEV)
     bd = (torch.randn(4096, generator=g) * 0.1).bfloat16().to(DEV)
+    Wgd = (torch.randn(512, 14336, generator=g) / 16).bfloat16().to(DEV)
+    Wud = (torch.randn(512, 14336, generator=g) / 16).bfloat16().to(DEV)
+    Wgp, Wup = ge.swiglu_prepack(Wgd, Wud)
 
     def outs():
         return [torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV),
                 torch.empty(256, 1024, dtype=torch.bfloat16, device=DEV),
                 torch.empty(512, 136 * 128, dtype=torch.bfloat16, device=DEV),
-                torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV)]
+                torch.empty(16, 4096, dtype=torch.bfloat16, device=DEV),
+                torch.empty(16, 14336, dtype=torch.bfloat16, device=DEV)]
 
     def prepare(o):
         return [ge.prepare_w4_gemm(x8, Wq8, s8, out=o[0], zero_point=128, fmt="u8"),
                 ge.prepare_w4_gemm(x4, Wp4, s4, out=o[1], prepacked=True),
                 ge.prepare_swiglu(xs, Wg, Wu, out=o[2]),
-                ge.prepare_gemm_epilogue(xd, Wd, bias=bd, out=o[3])]
+                ge.prepare_gemm_epilogue(xd, Wd, bias=bd, out=o[3]),
+                ge.prepare_swiglu(xw, Wgp, Wup, out=o[4], prepacked=True)]
 
     oe, og = outs(), outs()
     eager, graph_calls = prepare(oe), prepare(og)
@@ -123,7 +130,8 @@ def test_scratch_using_calls_replay_in_a_graph():
     assert kernels[0] == "skinny_u8_m16_128col_split4" and kernels[1] == "tile_w4_bf16_64x128x32_split4"
     assert kernels[2] == "tile_swiglu_256x128x32+128x128x32"
     assert kernels[3] == "skinny_bf16_m16_128col_streamk"
-    assert eager[0]._plan.scratch_bytes > 0 and eager[1]._plan.scratch_bytes > 0 and eager[3]._plan.scratch_bytes > 0
+    assert kernels[4] == "skinny_bf16p_swiglu_112col_pairs"
+    assert all(eager[i]._plan.scratch_bytes > 0 for i in (0, 1, 3, 4))
     for f in eager + graph_calls:
         f()
     torch.cuda.synchronize()
@@ -133,7 +141,7 @@ def test_scratch_using_calls_replay_in_a_graph():
             f.with_stream()()
     Wq4n = _np(Wq4)
     for rep in range(4):
-        for dst, src in zip((x8, x4, xs), _scratch_inputs(200 + rep)):
+        for dst, src in zip((x8, x4, xs, xw), _scratch_inputs(200 + rep)):
             dst.copy_(src)
         for f in eager:
             f()
@@ -145,8 +153,9 @@ def test_scratch_using_calls_replay_in_a_graph():
         refs = [oracle.w8_gemm(_np(x8), _np(Wq8), _np(s8), "u8", "bf16", group=128, zero_point=128),
                 oracle.w4_gemm(_np(x4), Wq4n, _np(s4), 1024, "bf16"),
                 oracle.swiglu(_np(xs), _np(Wg), _np(Wu), "bf16"),
-                oracle.gemm_epilogue(_np(xd), _np(Wd), "bf16", bias=_np(bd))]
-        for got, ref, name in zip(og, refs, ("u8 split", "int4 tile", "swiglu", "stream-k")):
+                oracle.gemm_epilogue(_np(xd), _np(Wd), "bf16", bias=_np(bd)),
+                oracle.swiglu(_np(xw), _np(Wgd), _np(Wud), "bf16")]
+        for got, ref, name in zip(og, refs, ("u8 split", "int4 tile", "swiglu", "stream-k", "swiglu prepacked")):
             assert_close(got, ref, TOL_BF16, f"replay {rep}: {name}")
 
 
