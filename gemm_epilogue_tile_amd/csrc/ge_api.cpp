@@ -131,8 +131,8 @@ Problem make_problem(const ge_plan *pl, const void *A, const void *B, const void
     const bool tsplit_use = pl->scratch_use == SCRATCH_TILE_SPLIT && p.mode == MODE_W4;
     const bool sk_use = pl->scratch_use == SCRATCH_SK && p.mode == MODE_GENERIC;
     if (pl->scratch && pl->scratch_use == SCRATCH_SWIGLU && p.mode == MODE_SWIGLU) {
-        // the gate / up tile pairs of the prepacked SwiGLU kernel, then one counter per column block
-        const int64_t ncb = d.N / (16 * swiglu_block_tiles(d.N, pl->cu_count));
+        // the gate / up tile pairs of the SwiGLU decode kernels, then one counter per column block
+        const int64_t ncb = swiglu_pair_blocks(d.N, pl->cu_count, p.b_packed != 0);
         p.split = 2;
         p.split_ws = (float *)pl->scratch;
         p.split_cnt = (uint32_t *)((char *)pl->scratch + pl->scratch_bytes - ncb * 4);
@@ -459,6 +459,12 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         use = SCRATCH_SWIGLU;
         pl.split = 2;
         pl.kernel = swiglu_prepacked_name(d.N, pl.cu_count);
+    } else if (kind == GE_KIND_SWIGLU && swiglu_raw_supported(p)) {
+        // decode sizes on raw weights: the gate / up workgroup pairs over the raw layout
+        bytes = swiglu_raw_scratch_bytes(d.M, d.N, pl.cu_count);
+        use = SCRATCH_SWIGLU;
+        pl.split = 2;
+        pl.kernel = swiglu_raw_name(d.N, pl.cu_count);
     }
     if (bytes > 0 && (d.flags & GE_FLAG_NO_SCRATCH)) {
         // no device memory: the variant of the kernel that needs none
@@ -614,7 +620,13 @@ ge_status gemm_swiglu_run(const ge_plan *pl, const void *X, const void *Wg, cons
         const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
         return hip_status(launch_swiglu_prepacked(p, pl->cu_count, (hipStream_t)stream), "gemm_swiglu_run launch (prepacked)");
     }
-    const Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
+    Problem p = make_problem(pl, X, Wg, Wu, nullptr, nullptr, nullptr, nullptr, D);
+    if (pl->scratch_use == SCRATCH_SWIGLU && swiglu_raw_supported(p))
+        return hip_status(launch_swiglu_raw(p, pl->cu_count, (hipStream_t)stream), "gemm_swiglu_run launch (pairs)");
+    // the tile or general kernel (also when these pointers do not suit the pairs)
+    p.split = 1;
+    p.split_ws = nullptr;
+    p.split_cnt = nullptr;
     return hip_status(launch_fused(pl, p, (hipStream_t)stream), "gemm_swiglu_run launch");
 }
 

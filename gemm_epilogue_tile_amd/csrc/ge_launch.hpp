@@ -90,6 +90,12 @@ int swiglu_block_tiles(int N, int cu_count);
 int64_t swiglu_prepacked_scratch_bytes(int M, int N, int cu_count);
 const char *swiglu_prepacked_name(int N, int cu_count);
 hipError_t launch_swiglu_prepacked(const Problem &p, int cu_count, hipStream_t s);
+// the same pairs on raw [K, N] weights (M <= 32, when the raw decode kernel takes both weights)
+bool swiglu_raw_supported(const Problem &p);
+int64_t swiglu_raw_scratch_bytes(int M, int N, int cu_count);
+const char *swiglu_raw_name(int N, int cu_count);
+int64_t swiglu_pair_blocks(int N, int cu_count, bool prepacked);  // column blocks (one counter each)
+hipError_t launch_swiglu_raw(const Problem &p, int cu_count, hipStream_t s);
 // 16-column tiles per block of the prepacked bf16 layout (7 or 8), a function of N and the CU count
 int bf16p_block_tiles(int N, int cu_count);
 

@@ -721,6 +721,31 @@ __global__ __launch_bounds__(S_THREADS) void skinny_bf16p_swiglu_kernel(Problem 
     split_reduce_epilogue<MR, NC, 2, S_WAVES, true>(p, red, cb * NC, cb, h, ncb, &s_last);
 }
 
+// The same pairs on raw [K, N] weights (row stride ldb): workgroup 2 cb + h streams the NC = 8 NCH
+// columns from cb * NC of W_gate (h = 0) or W_up (h = 1) like the raw decode kernel
+template <int MT, int NCH>
+__global__ __launch_bounds__(S_THREADS) void skinny_bf16_swiglu_kernel(Problem p) {
+    constexpr int NC = 8 * NCH, MR = 16 * MT;
+    __shared__ __attribute__((aligned(16))) float red[S_WAVES * MR * NC];
+    __shared__ int s_last;
+    const int h = blockIdx.x & 1, cb = blockIdx.x >> 1, ncb = gridDim.x >> 1;
+    Problem q = p;
+    if (h) q.B = p.B2;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nkb = (p.K + 31) / 32;
+    const int per = (nkb + S_WAVES - 1) / S_WAVES;
+    const int kb0 = wave * per, kb1 = min(nkb, kb0 + per);
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stream_bf16<MT, NCH>(q, cb * NC, kb0, kb1, acc);
+    acc_to_lds<MT, NCH>(red, acc);
+    __syncthreads();
+    split_reduce_epilogue<MR, NC, 2, S_WAVES, true>(p, red, cb * NC, cb, h, ncb, &s_last);
+}
+
 #ifndef GE_W4S_RING
 #define GE_W4S_RING 2
 #endif
@@ -1102,6 +1127,56 @@ hipError_t launch_swiglu_prepacked(const Problem &p, int cu_count, hipStream_t s
         else
             hipLaunchKernelGGL((skinny_bf16p_swiglu_kernel<2, 8>), grid, dim3(S_THREADS), 0, s, p);
     }
+    return hipGetLastError();
+}
+
+namespace {
+int bf16_chunks(int N, int cu_count);
+}
+
+// raw weights: 8-column chunks per workgroup (8 or 16) for 2 N columns' worth of workgroups
+int swiglu_raw_chunks(int N, int cu_count) { return bf16_chunks(2 * N, cu_count > 0 ? cu_count : 256); }
+
+int64_t swiglu_raw_scratch_bytes(int M, int N, int cu_count) {
+    const int nch = swiglu_raw_chunks(N, cu_count);
+    const int64_t ncb = (N + 8 * nch - 1) / (8 * nch), mr = M <= 16 ? 16 : 32;
+    return 2 * ncb * mr * 8 * nch * 4 + ncb * 4;
+}
+
+int64_t swiglu_pair_blocks(int N, int cu_count, bool prepacked) {
+    if (prepacked) return N / (16 * swiglu_block_tiles(N, cu_count));
+    const int nch = swiglu_raw_chunks(N, cu_count);
+    return (N + 8 * nch - 1) / (8 * nch);
+}
+
+const char *swiglu_raw_name(int N, int cu_count) {
+    return swiglu_raw_chunks(N, cu_count) == 8 ? "skinny_bf16_swiglu_64col_pairs" : "skinny_bf16_swiglu_128col_pairs";
+}
+
+// whether the raw pairs can read these operands (the raw decode kernel's conditions, for both weights)
+bool swiglu_raw_supported(const Problem &p) {
+    Problem g = p, u = p;
+    g.mode = u.mode = MODE_GENERIC;
+    u.B = p.B2;
+    g.b_packed = u.b_packed = 0;
+    return p.M <= 32 && skinny_supported(g) && skinny_supported(u);
+}
+
+hipError_t launch_swiglu_raw(const Problem &p, int cu_count, hipStream_t s) {
+    if (!p.split_ws || !p.split_cnt || p.M > 32) return hipErrorInvalidValue;
+    const int nch = swiglu_raw_chunks(p.N, cu_count);
+    const dim3 grid(2 * ((p.N + 8 * nch - 1) / (8 * nch)));
+    auto go = [&](auto MTC) {
+        constexpr int MT = decltype(MTC)::value;
+        if (nch == 8)
+            hipLaunchKernelGGL((skinny_bf16_swiglu_kernel<MT, 8>), grid, dim3(S_THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_bf16_swiglu_kernel<MT, 16>), grid, dim3(S_THREADS), 0, s, p);
+    };
+    if (p.M <= 16)
+        go(std::integral_constant<int, 1>{});
+    else
+        go(std::integral_constant<int, 2>{});
     return hipGetLastError();
 }
 

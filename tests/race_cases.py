@@ -56,6 +56,7 @@ def run_cases(ge, torch):
         "w8_u8_tile": w8("u8", 128, 1024, 1024, 9),
         "w8_fp8_tile": w8("fp8", 128, 1024, 1024, 10),
         "swiglu_prepacked_pairs": swiglu(16, 14336, 512, 12, prepacked=True),  # gate / up block pairs
+        "swiglu_raw_pairs": swiglu(16, 14336, 512, 13),
     }
     torch.cuda.synchronize()
     return {k: v.view(torch.int16).cpu().numpy() for k, v in out.items()}

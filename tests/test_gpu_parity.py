@@ -93,14 +93,40 @@ def test_tile_size_choice_and_parity(M, N, K, layout, kernel):
     assert_close(out, oracle.reference(inp), TOL_BF16, f"{kernel} {M}x{N}x{K}")
 
 
-# SwiGLU at decode sizes takes the tile kernel too (the streaming kernels have no dual form)
-@pytest.mark.parametrize("M,N,K", [(1, 14336, 256), (16, 1000, 520), (31, 3000, 136)])
-def test_swiglu_few_rows_on_the_tile_kernel(M, N, K):
+# SwiGLU at decode sizes (M <= 32) on raw weights: gate / up workgroup pairs over the raw decode loop
+# (128- or 64-column blocks); shapes the raw decode kernel cannot read (N % 8 != 0) take the tile or
+# general kernel
+@pytest.mark.parametrize("M,N,K,kernel", [(1, 14336, 256, "skinny_bf16_swiglu_128col_pairs"),
+                                          (16, 1000, 520, "skinny_bf16_swiglu_64col_pairs"),
+                                          (31, 3000, 136, "skinny_bf16_swiglu_64col_pairs"),
+                                          (8, 1001, 256, None)])
+def test_swiglu_few_rows(M, N, K, kernel):
     w = workloads.Workload("swiglu_rows", 2, "swiglu", M, N, K, "bf16")
     inp = workloads.make_inputs(w, seed=M)
-    assert ge.plan(ge.KIND_SWIGLU, M, N, K).kernel.startswith("tile_swiglu"), M
+    pl = ge.plan(ge.KIND_SWIGLU, M, N, K)
+    if kernel is not None:
+        assert pl.kernel == kernel, pl.kernel
+        assert pl.scratch_bytes > 0
+    else:
+        assert not pl.kernel.startswith("skinny"), pl.kernel
     d = dev_inputs(inp)
-    assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
+    out = ge.swiglu(d["X"], d["Wg"], d["Wu"])
+    assert_close(out, oracle.reference(inp), TOL_BF16, f"swiglu {M}x{N}x{K}")
+    assert torch.equal(out, ge.swiglu(d["X"], d["Wg"], d["Wu"])), "repeat calls must agree bitwise"
+
+
+def test_swiglu_pairs_fall_back_on_misaligned_operands():
+    # X one element off 16-byte alignment: the plan's pairs cannot read it, the call takes the tile
+    # or general kernel instead, same results within the tolerance
+    M, N, K = 16, 1024, 256
+    w = workloads.Workload("swiglu_rows", 2, "swiglu", M, N, K, "bf16")
+    inp = workloads.make_inputs(w, seed=3)
+    d = dev_inputs(inp)
+    flat = torch.zeros(M * K + 1, dtype=torch.bfloat16, device=DEV)
+    flat[1:] = d["X"].reshape(-1)
+    X = flat[1:].view(M, K)
+    assert X.data_ptr() % 16 != 0
+    assert_close(ge.swiglu(X, d["Wg"], d["Wu"]), oracle.reference(inp), TOL_BF16, "swiglu misaligned X")
 
 
 # SwiGLU at decode sizes on prepacked weights: each column block of W_gate and of W_up streams on a
