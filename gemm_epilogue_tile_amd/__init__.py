@@ -265,7 +265,8 @@ def plan(kind: int, M: int, N: int, K: int, *, a_type=BF16, b_type=None, d_type=
 
     Calls with equal descriptors share one plan, except that a plan owning device scratch
     (``Plan.scratch_bytes > 0``: bf16 decode shapes whose K is split over workgroups, quantised weights
-    with a K split: at M <= 16, or on the tile kernel when its tiles leave CUs idle) is made once per
+    with a K split: at M <= 16, or on the tile kernel when its tiles leave CUs idle; SwiGLU at M <= 32,
+    whose gate and up blocks run on workgroup pairs) is made once per
     ``stream`` (default: the current stream), since it must not run on two streams at once.
     ``no_scratch``: a plan that allocates no device memory (for ``gemm_epilogue_noalloc``).  The cache
     holds the 256 most recently used plans."""

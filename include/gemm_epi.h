@@ -226,14 +226,19 @@ GE_API ge_status gemm_epi_run_noalloc(const ge_plan *plan, const void *A, const 
  * are [K, N] with the plan's ldb.  Each X tile is read once and feeds both
  * products (page "Fusion Thinking", Pattern 2, Level 2).
  *
+ * At M <= 32 each column block of Wg and of Wu streams on a workgroup of
+ * its own through the decode loop, and the second of the two to finish
+ * combines silu(gate) * up for the block: the pair's fp32 tiles and a
+ * counter per block live in device scratch that the plan owns, so calls on
+ * one such plan must not overlap in time.  Raw weights take this route when
+ * the raw decode loop can read them (N % 8 == 0, 16-byte aligned X, Wg, Wu,
+ * lda and ldb multiples of 8; otherwise the tile or general kernel runs).
  * A SwiGLU plan made with GE_FLAG_B_PREPACKED (M <= 32, N % 128 == 0,
  * K % 32 == 0, dense weights) takes Wg and Wu each converted by
- * gemm_b_prepack, and streams them through the prepacked decode kernel in
- * two passes: silu(X.Wg) is kept in fp32 in the plan's device scratch
- * (M * N * 4 bytes, plus the decode kernel's split tiles when the column
- * blocks leave CUs idle) and multiplied in the epilogue of X.Wu.  The plan
- * owns that scratch, so calls on one plan must not overlap in time; X, Wg
- * and Wu must be 16-byte aligned (GE_ERR_ALIGN otherwise).
+ * gemm_b_prepack on a SwiGLU plan of the same N and K (that layout's column
+ * blocks are sized so that the pairs fill the GPU); X, Wg and Wu must then
+ * be 16-byte aligned (GE_ERR_ALIGN otherwise), and the unfused chain is
+ * refused (it reads raw weights).
  */
 GE_API ge_status gemm_swiglu_run(const ge_plan *plan, const void *X, const void *Wg, const void *Wu,
                           void *D, void *stream);
@@ -286,7 +291,11 @@ GE_API ge_status gemm_w4_prepack(const ge_plan *plan, const uint8_t *Wq, uint8_t
  * device that runs it.  So each column block's K range is one contiguous
  * run of memory and every 16-byte load is a finished fragment (no transpose
  * in the kernel).  Any GENERIC bf16 KN plan of the same N, K and ldb serves
- * (M and the epilogue are ignored).  Needs N % 128 == 0, K % 32 == 0, a
+ * (M and the epilogue are ignored).  On a SWIGLU plan, T is chosen the same
+ * way for 2 N columns (the gate and the up blocks together: T = 7 where
+ * N % 112 == 0 and 2 N / 112 is a multiple of the CU count while 2 N / 128
+ * is not, e.g. N = 14336 on 256 CUs), and the result serves the SwiGLU
+ * plans made with GE_FLAG_B_PREPACKED.  Needs N % 128 == 0, K % 32 == 0, a
  * 2-byte aligned B and a 16-byte aligned Bp that does not overlap B.
  * Asynchronous on the stream.
  */
