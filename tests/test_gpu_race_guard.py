@@ -1,5 +1,6 @@
-"""The race-guard build against the normal one (an extra ordering check the
-SURVEY's race-detection row describes): every case of race_cases.py is run with
+"""The race-guard build against the normal one (an extra ordering check: the
+debug library adds waits, barriers and fences, which can only remove races):
+every case of race_cases.py is run with
 libgemm_epi.so here and with libgemm_epi_debug.so in a child process, and the
 outputs must agree bit for bit."""
 import os
