@@ -150,6 +150,8 @@ WORKLOADS = {
                               fmt="u8"),
     "w8a16_fp8_m512": Workload("w8a16_fp8_m512", 9, "w8", 512, 8192, 8192, "bf16", bias=True, zero_point=0,
                                fmt="fp8"),
+    # the SwiGLU MLP shape at 16 rows (decode), beyond the five configurations
+    "swiglu_decode": Workload("swiglu_decode", 11, "swiglu", 16, 14336, 4096, "bf16"),
 }
 
 
