@@ -370,24 +370,25 @@ def _workspace(p: Plan, device):
     return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
 
 
-def _swiglu_plan(X, Wg, out, stream=None, prepacked=False):
+def _swiglu_plan(X, Wg, out, stream=None, prepacked=False, no_scratch=False):
     M, K = X.shape
     N = Wg.shape[1]
     return plan(KIND_SWIGLU, M, N, K, a_type=BF16, b_type=BF16, d_type=BF16, lda=_ld(X), ldb=_ld(Wg),
-                ldd=_ld(out), b_prepacked=prepacked, stream=stream)
+                ldd=_ld(out), b_prepacked=prepacked, no_scratch=no_scratch, stream=stream)
 
 
-def swiglu(X, Wg, Wu, *, out=None, prepacked=False, stream=None):
+def swiglu(X, Wg, Wu, *, out=None, prepacked=False, no_scratch=False, stream=None):
     """D = silu(X @ Wg) * (X @ Wu) (fused dual GEMM).
 
     ``prepacked``: Wg and Wu were converted by ``swiglu_prepack`` (M <= 32, N % 128 == 0, K % 32 == 0):
     each column block of the gate and of the up weight streams on a workgroup of its own through the
     prepacked decode loop, and the second of the two to finish combines silu(gate) * up for the
-    block (fp32 tiles in the plan's scratch)."""
+    block (fp32 tiles in the plan's scratch).  ``no_scratch``: a plan that allocates no device memory
+    (raw weights only: the tile kernel at every M)."""
     if Wg.stride() != Wu.stride() or Wg.shape != Wu.shape:
         raise ValueError("Wg and Wu must have the same shape and strides")
     out = _out(X.shape[0], Wg.shape[1], X.dtype, X.device, out)
-    p = _swiglu_plan(X, Wg, out, stream, prepacked)
+    p = _swiglu_plan(X, Wg, out, stream, prepacked, no_scratch)
     _check(lib().gemm_swiglu_run(p.handle, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream)),
            "gemm_swiglu_run")
     return out

@@ -363,8 +363,10 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         if (d.a_type != GE_BF16 || d.b_type != GE_BF16 || d.d_type != GE_BF16)
             return fail(GE_ERR_UNSUPPORTED, "swiglu needs bf16 X, W and D");
         if (d.b_layout != GE_LAYOUT_KN) return fail(GE_ERR_UNSUPPORTED, "swiglu needs KN weights");
-        if (d.act != GE_ACT_NONE || (d.flags & ~GE_FLAG_B_PREPACKED) || d.alpha != 1.0f)
+        if (d.act != GE_ACT_NONE || (d.flags & ~(GE_FLAG_B_PREPACKED | GE_FLAG_NO_SCRATCH)) || d.alpha != 1.0f)
             return fail(GE_ERR_UNSUPPORTED, "swiglu takes no extra epilogue");
+        if ((d.flags & GE_FLAG_B_PREPACKED) && (d.flags & GE_FLAG_NO_SCRATCH))
+            return fail(GE_ERR_UNSUPPORTED, "prepacked swiglu needs the plan's scratch");
         pl.ldb = d.ldb ? d.ldb : d.N;
         if (pl.ldb < d.N) return fail(GE_ERR_INVALID_ARG, "ldb < N");
         if ((d.flags & GE_FLAG_B_PREPACKED) && (d.M > 32 || d.N % 128 || d.K % 32 || pl.ldb != d.N))
@@ -459,7 +461,7 @@ ge_status gemm_epi_plan(const ge_desc *dp, int32_t kind, ge_plan **out) {
         use = SCRATCH_SWIGLU;
         pl.split = 2;
         pl.kernel = swiglu_prepacked_name(d.N, pl.cu_count);
-    } else if (kind == GE_KIND_SWIGLU && swiglu_raw_supported(p)) {
+    } else if (kind == GE_KIND_SWIGLU && !(d.flags & GE_FLAG_NO_SCRATCH) && swiglu_raw_supported(p)) {
         // decode sizes on raw weights: the gate / up workgroup pairs over the raw layout
         bytes = swiglu_raw_scratch_bytes(d.M, d.N, pl.cu_count);
         use = SCRATCH_SWIGLU;

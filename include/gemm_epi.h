@@ -232,7 +232,9 @@ GE_API ge_status gemm_epi_run_noalloc(const ge_plan *plan, const void *A, const 
  * counter per block live in device scratch that the plan owns, so calls on
  * one such plan must not overlap in time.  Raw weights take this route when
  * the raw decode loop can read them (N % 8 == 0, 16-byte aligned X, Wg, Wu,
- * lda and ldb multiples of 8; otherwise the tile or general kernel runs).
+ * lda and ldb multiples of 8; otherwise the tile or general kernel runs),
+ * unless the plan is made with GE_FLAG_NO_SCRATCH: then it allocates nothing
+ * and runs the tile kernel.
  * A SwiGLU plan made with GE_FLAG_B_PREPACKED (M <= 32, N % 128 == 0,
  * K % 32 == 0, dense weights) takes Wg and Wu each converted by
  * gemm_b_prepack on a SwiGLU plan of the same N and K (that layout's column

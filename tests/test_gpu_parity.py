@@ -115,6 +115,21 @@ def test_swiglu_few_rows(M, N, K, kernel):
     assert torch.equal(out, ge.swiglu(d["X"], d["Wg"], d["Wu"])), "repeat calls must agree bitwise"
 
 
+def test_swiglu_few_rows_without_scratch():
+    # a plan that may not allocate keeps the tile kernel; prepacked weights need the pairs' scratch
+    M, N, K = 16, 1024, 256
+    pl = ge.plan(ge.KIND_SWIGLU, M, N, K, no_scratch=True)
+    assert pl.scratch_bytes == 0 and pl.kernel.startswith("tile_swiglu"), pl.kernel
+    w = workloads.Workload("swiglu_rows", 2, "swiglu", M, N, K, "bf16")
+    inp = workloads.make_inputs(w, seed=4)
+    d = dev_inputs(inp)
+    assert_close(ge.swiglu(d["X"], d["Wg"], d["Wu"], no_scratch=True), oracle.reference(inp), TOL_BF16,
+                 "swiglu without scratch")
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.plan(ge.KIND_SWIGLU, M, N, K, b_prepacked=True, no_scratch=True)
+    assert e.value.status == ge.ERR_UNSUPPORTED
+
+
 def test_swiglu_pairs_fall_back_on_misaligned_operands():
     # X one element off 16-byte alignment: the plan's pairs cannot read it, the call takes the tile
     # or general kernel instead, same results within the tolerance
