@@ -27,6 +27,8 @@ def _run(name, inp):
                                 C=d.get("C"), R=d.get("R"), alpha=inp["alpha"], beta=inp["beta"], act=inp["act"],
                                 prepacked=packed)
     if inp["kind"] == "swiglu":
+        if name.endswith("+prepacked"):  # decode rows on prepacked weights, as in the benchmark
+            return ge.swiglu(d["X"], *ge.swiglu_prepack(d["Wg"], d["Wu"]), prepacked=True)
         return ge.swiglu(d["X"], d["Wg"], d["Wu"])
     Wq = torch.from_numpy(inp["Wq"]).to(DEV)
     if inp["kind"] == "w8":
@@ -40,6 +42,7 @@ def _run(name, inp):
 
 
 @pytest.mark.parametrize("name,nrows", [("tiny_fp32", 64), ("square_bf16", 24), ("swiglu_8b", 8),
+                                        ("swiglu_decode", 16), ("swiglu_decode+prepacked", 16),
                                         ("skinny_decode", 16), ("skinny_decode+prepacked", 16),
                                         ("w4a16_m16", 16), ("w4a16_m512", 24),
                                         ("w8a16_u8_m16", 16), ("w8a16_fp8_m16", 16),
