@@ -420,6 +420,8 @@ def main():
         for name in a.workloads.split(","):
             if name == "rope_qk_prefill":
                 r = dict(name=name, **measure_rope_qk(a.steps, a.warmup))
+            elif name == "add_rmsnorm_2048x4096":
+                r = dict(name=name, **measure_add_rmsnorm(a.steps, a.warmup))
             else:
                 r = measure(name, a.steps, a.warmup, unfused_chain=False)
             print(json.dumps({k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
