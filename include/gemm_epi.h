@@ -43,7 +43,8 @@
  * (gemm_epi_plan_scratch_bytes() > 0: quantised-weight plans whose K is split
  * over workgroups -- M <= 16 streaming, or the tile kernel at M > 16 (8-bit)
  * or M > 32 (int4) when its tiles leave CUs idle -- and bf16 generic plans
- * with M <= 16 whose K is split the same way (stream-K)) must not run on two
+ * with M <= 16 whose K is split the same way (stream-K), and SwiGLU plans
+ * with M <= 32 on the gate / up workgroup pairs) must not run on two
  * streams at once, since its launches share that scratch.
  */
 #ifndef GEMM_EPI_H
@@ -174,7 +175,10 @@ GE_API void ge_desc_init(ge_desc *d);
  * CUs idle and whose (column block, 32-row K block) units divide evenly into
  * one K piece of one column block per CU (stream-K: the same tiles and
  * counters, S = pieces per block in {2..8}; e.g. 16 x 8192 x 8192 on 256
- * CUs, S = 4).  Such a call waits for the zeroing of its scratch on a
+ * CUs, S = 4); SwiGLU plans with M <= 32 that take the gate / up
+ * workgroup pairs (prepacked weights, or raw weights without
+ * GE_FLAG_NO_SCRATCH: two fp32 tiles of 16 or 32 rows per column block plus
+ * 4 bytes of counter per block).  Such a call waits for the zeroing of its scratch on a
  * stream of the library's own (the callers' streams keep running); device
  * allocation is not allowed during graph capture, so make such plans before
  * capturing (the call fails with GE_ERR_HIP and says so otherwise).
